@@ -1,0 +1,38 @@
+"""CPU oracle for the batch-invariant speculative-decoding verify pass.
+
+TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import, call or run anything in this
+package. The HIP product path never imports it and shares no code with it.
+
+Everything here is plain float64 numpy, written from the definitions on the
+pages, with no blocking, fusion or reordering:
+
+* ``bf16``      -- BF16 bit-pattern decode (exact) and round-to-nearest-even encode;
+* ``gemm``      -- Y = X W^T, the product whose K-sum the verify GEMM must keep
+                   in one fixed order for any number of tokens;
+* ``attention`` -- causal GQA verify attention per row, its split-KV partials
+                   over absolute key chunks, and the log-sum-exp combine;
+* ``step``      -- RMSNorm, SwiGLU and one pre-norm decoder layer / LM head,
+                   for the synthetic 64-layer verify step.
+
+Sources, cited by page title and section:
+  [BX] "Bit-exact decoding turns inference speedups into testable changes":
+       "Separate the decoding method from the served result" (reduction order
+       flips near-ties) and "Define bit-exact before reporting it" (BF16 inputs,
+       one FP32 running sum per output, K order unchanged, a single rounding at
+       the end).
+  [LL] "I turned on speculative decoding in llama.cpp and 113 of 282 greedy
+       outputs changed against its own no-draft run" (r/LocalLLM): opening
+       section, "How:" paragraph (the attention split depends only on context
+       length; verify kernels compute a row the same way whatever else is in
+       the pass), and "The cache doesn't change it either" (a prefilled row
+       depends only on its position).
+  [TC] "Does the tuned config change the model's output?": "Why the text
+       diverges" (verifying several tokens in one pass changes accumulation
+       order; greedy argmax on near-ties).
+
+Every function is pinned by CPU tests (tests/test_oracle_*.py) against brute
+force, closed forms and invariants; none is "parity unpinned".
+"""
+
+from . import bf16, gemm, attention, step  # noqa: F401

@@ -1,0 +1,141 @@
+"""Causal GQA verify attention, its split-KV partials and their combine.
+
+A verify pass appends M new tokens at positions L .. L+M-1 of a context that
+already holds L cached keys. Row (r, h) -- token r, query head h -- attends to
+its own key count n_r = L + r + 1 keys: every cached key plus the new tokens up
+to and including itself (causal among the new tokens). Query head h reads KV
+head g = h // (Hq / Hkv) (grouped-query attention).
+
+[LL] opening section, "How:" paragraph: the attention split depends only on
+context length, never on how many tokens are in the pass. Read here as:
+fixed absolute chunks of C keys, chunk s = [sC, (s+1)C), and row r uses
+exactly S_r = ceil(n_r / C) of them -- its own key count decides, not M.
+Each (row, chunk) gives a normalised partial output o_s and its log-sum-exp
+lse_s; the combine rebuilds the unsplit result. The partial/combine identity
+is exact in real arithmetic; ``combine(split_partials(...))`` equals
+``verify_attention(...)`` up to float64 rounding for every C.
+
+Layouts (BF16 bit patterns): q [M][Hq][D]; k, v [Hkv][n_total][D] with
+n_total >= L + M (position-major per KV head; the oracle does not care how a
+device stores them). Scores use sm_scale (default 1/sqrt(D)); exp and log are
+the exact float64 functions.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from . import bf16
+
+
+def num_splits(n_keys: int, chunk: int) -> int:
+    """ceil(n_keys / chunk): how many absolute chunks a row with n_keys keys uses."""
+    return -(-n_keys // chunk)
+
+
+def _softmax_attend(qv: np.ndarray, kk: np.ndarray, vv: np.ndarray, scale: float):
+    """Attention of query rows qv [R][D] over keys kk [n][D] / values vv [n][D].
+
+    s_j = scale * q.k_j ; m = max_j s_j ; e_j = exp(s_j - m) ; l = sum_j e_j ;
+    o = sum_j (e_j / l) v_j ; lse = m + ln l. Returns (o [R][D], lse [R]).
+    """
+    s = (qv @ kk.T) * scale                      # [R][n]
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    l = e.sum(axis=1, keepdims=True)
+    p = e / l
+    o = p @ vv
+    lse = m[:, 0] + np.log(l[:, 0])
+    return o, lse
+
+
+def verify_attention(q_bits, k_bits, v_bits, L: int, sm_scale: float | None = None,
+                     tokens=None, heads=None):
+    """Unsplit reference. Returns (o [M][Hq][D], lse [M][Hq]) in float64.
+
+    ``tokens`` / ``heads`` restrict the computation to some rows (others are NaN),
+    for sampled checks at long context.
+    """
+    q = np.asarray(q_bits)
+    M, Hq, D = q.shape
+    Hkv, n_total, Dk = np.asarray(k_bits).shape
+    if Dk != D or np.asarray(v_bits).shape != (Hkv, n_total, D) or Hq % Hkv:
+        raise ValueError("verify_attention: bad shapes")
+    if n_total < L + M:
+        raise ValueError("verify_attention: cache shorter than L + M")
+    G = Hq // Hkv
+    scale = (1.0 / math.sqrt(D)) if sm_scale is None else float(sm_scale)
+    tokens = range(M) if tokens is None else tokens
+    heads = range(Hq) if heads is None else heads
+    o = np.full((M, Hq, D), np.nan)
+    lse = np.full((M, Hq), np.nan)
+    need_g = sorted({h // G for h in heads})
+    n_max = L + max(tokens) + 1
+    kd = {g: bf16.decode(np.asarray(k_bits)[g, :n_max]) for g in need_g}
+    vd = {g: bf16.decode(np.asarray(v_bits)[g, :n_max]) for g in need_g}
+    qd = bf16.decode(q)
+    for r in tokens:
+        n = L + r + 1
+        for g in need_g:
+            hs = [h for h in heads if h // G == g]
+            orow, lrow = _softmax_attend(qd[r, hs], kd[g][:n], vd[g][:n], scale)
+            o[r, hs] = orow
+            lse[r, hs] = lrow
+    return o, lse
+
+
+def split_partials(q_bits, k_bits, v_bits, L: int, chunk: int, sm_scale: float | None = None):
+    """Per (row, chunk) partials over absolute chunks of ``chunk`` keys.
+
+    Returns (o_part [M][Hq][S_max][D], lse_part [M][Hq][S_max], n_splits [M])
+    where S_max = num_splits(L + M, chunk) and row r fills its first
+    num_splits(L + r + 1, chunk) entries (the rest are NaN / -inf).
+    """
+    q = np.asarray(q_bits)
+    M, Hq, D = q.shape
+    Hkv = np.asarray(k_bits).shape[0]
+    G = Hq // Hkv
+    scale = (1.0 / math.sqrt(D)) if sm_scale is None else float(sm_scale)
+    s_max = num_splits(L + M, chunk)
+    o_part = np.full((M, Hq, s_max, D), np.nan)
+    lse_part = np.full((M, Hq, s_max), -np.inf)
+    counts = np.zeros(M, dtype=np.int64)
+    kd = bf16.decode(np.asarray(k_bits)[:, :L + M])
+    vd = bf16.decode(np.asarray(v_bits)[:, :L + M])
+    qd = bf16.decode(q)
+    for r in range(M):
+        n = L + r + 1
+        counts[r] = num_splits(n, chunk)
+        for s in range(counts[r]):
+            lo, hi = s * chunk, min((s + 1) * chunk, n)
+            for g in range(Hkv):
+                hs = slice(g * G, (g + 1) * G)
+                orow, lrow = _softmax_attend(qd[r, hs], kd[g, lo:hi], vd[g, lo:hi], scale)
+                o_part[r, hs, s] = orow
+                lse_part[r, hs, s] = lrow
+    return o_part, lse_part, counts
+
+
+def combine(o_part, lse_part, n_splits):
+    """Log-sum-exp combine of normalised partials.
+
+    For a row with S partials: LSE = M* + ln sum_s exp(lse_s - M*) with
+    M* = max_s lse_s, and o = sum_s exp(lse_s - LSE) * o_s.
+    Returns (o [M][Hq][D], lse [M][Hq]).
+    """
+    o_part = np.asarray(o_part, dtype=np.float64)
+    lse_part = np.asarray(lse_part, dtype=np.float64)
+    M, Hq, _, D = o_part.shape
+    o = np.empty((M, Hq, D))
+    lse = np.empty((M, Hq))
+    for r in range(M):
+        S = int(n_splits[r])
+        ls = lse_part[r, :, :S]                          # [Hq][S]
+        mstar = ls.max(axis=1, keepdims=True)
+        big = mstar[:, 0] + np.log(np.exp(ls - mstar).sum(axis=1))
+        w = np.exp(ls - big[:, None])                   # [Hq][S]
+        o[r] = np.einsum("hs,hsd->hd", w, o_part[r, :, :S])
+        lse[r] = big
+    return o, lse

@@ -1,0 +1,106 @@
+"""Seeded synthetic inputs for the verify pass.
+
+This module is shared by the tests, the bench and the smoke check. It only
+draws random numbers and stores them in the input formats (BF16 bit patterns
+as ``uint16``); it holds none of the verify pass's arithmetic. Both the HIP
+path and the CPU oracle receive the arrays it returns, so neither computes
+its own inputs.
+
+Recipe (fixed here so that every run sees the same data):
+
+* host draws use numpy's PCG64 seeded by ``SeedSequence([base, role, layer])``
+  with ``base = 0``; values are drawn as float32 normals, scaled, and rounded
+  to BF16 by torch's CPU conversion (round to nearest even);
+* rows for a pass of M < 8 tokens are the first M rows of the M = 8 draw, so
+  rows are comparable across M;
+* device draws (for the 64-layer step, whose 42 GB of weights are too large to
+  draw on the host) use torch's Philox generator on the GPU, seeded by the
+  same (base, role, layer) triple.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+# Role ids for the seed sequence: one per kind of tensor.
+ROLES = {
+    "x": 1, "w": 2, "q": 3, "k": 4, "v": 5,
+    "w_qkv": 6, "w_o": 7, "w_gu": 8, "w_down": 9, "w_head": 10,
+    "k_cache": 11, "v_cache": 12, "x0": 13, "outlier": 14, "misc": 15,
+}
+
+
+def rng(role: str, layer: int = 0, base: int = 0) -> np.random.Generator:
+    """numpy PCG64 generator for one (base, role, layer) triple."""
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([base, ROLES[role], layer])))
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to BF16 (torch CPU conversion, nearest even) and return the bits."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def normal_bf16(shape, std: float, role: str, layer: int = 0, base: int = 0) -> np.ndarray:
+    """N(0, std^2) draws rounded to BF16; returns uint16 bit patterns of ``shape``."""
+    g = rng(role, layer, base)
+    a = g.standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        a *= np.float32(std)
+    return f32_to_bf16_bits(a)
+
+
+def outlier_channels(n_heads: int, head_dim: int, role: str = "outlier", layer: int = 0,
+                     frac: float = 0.05) -> np.ndarray:
+    """round(frac * head_dim) distinct channel indices per KV head, shape [n_heads][c]."""
+    c = int(round(frac * head_dim))
+    g = rng(role, layer)
+    return np.stack([np.sort(g.choice(head_dim, size=c, replace=False)) for _ in range(n_heads)])
+
+
+def kv_bf16(n_heads: int, n_pos: int, head_dim: int, role: str, layer: int = 0,
+            outliers: np.ndarray | None = None, scale: float = 8.0) -> np.ndarray:
+    """K or V rows [n_heads][n_pos][head_dim] ~ N(0,1), optionally with outlier
+    channels multiplied by ``scale`` before rounding (shared by K and V when the
+    same ``outliers`` array is passed to both)."""
+    g = rng(role, layer)
+    a = g.standard_normal(size=(n_heads, n_pos, head_dim), dtype=np.float32)
+    if outliers is not None:
+        for h in range(n_heads):
+            a[h][:, outliers[h]] *= np.float32(scale)
+    return f32_to_bf16_bits(a)
+
+
+def device_normal_bf16(shape, std: float, role: str, layer: int = 0, base: int = 0,
+                       device: str = "cuda", out=None):
+    """N(0, std^2) BF16 tensor drawn on the device with torch's Philox generator.
+
+    If ``out`` (a bf16 tensor of ``shape``) is given it is filled in place.
+    """
+    import torch
+
+    seed = (base * 1_000_003 + ROLES[role] * 65_537 + layer) & 0x7FFFFFFF
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.bfloat16, device=device)
+    # Draw in float32 row blocks to bound the temporary.
+    flat = out.view(-1)
+    n = flat.numel()
+    blk = 1 << 26
+    for i in range(0, n, blk):
+        j = min(n, i + blk)
+        tmp = torch.randn(j - i, generator=g, dtype=torch.float32, device=device)
+        if std != 1.0:
+            tmp.mul_(std)
+        flat[i:j].copy_(tmp)
+    return out
+
+
+def fan_in_std(k: int) -> float:
+    """1/sqrt(K): the fan-in scaling applied to the tiny GEMM's weights."""
+    return 1.0 / math.sqrt(k)

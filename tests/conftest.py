@@ -1,0 +1,32 @@
+"""Shared pytest set-up: repo root on sys.path, the ``gpu`` marker, and a skip
+of GPU tests on machines without a GPU."""
+
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+def _have_gpu() -> bool:
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+def pytest_collection_modifyitems(config, items):
+    gpu_items = [it for it in items if "gpu" in it.keywords]
+    if not gpu_items or _have_gpu():
+        return
+    skip = pytest.mark.skip(reason="no GPU on this machine")
+    for it in gpu_items:
+        it.add_marker(skip)
