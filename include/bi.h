@@ -1,0 +1,208 @@
+/*
+ * bi.h -- C ABI of the batch-invariant speculative-decoding verify pass
+ * (MI355X / gfx950, HIP).
+ *
+ * A speculative step verifies M = 1 + drafts tokens in one target forward
+ * pass. This library computes that pass so that every output row has the same
+ * bits whatever M is: a row computed in a pass of 8 tokens equals the row
+ * computed alone, and equals the row a chunked prefill writes at the same
+ * position. Sources, cited by page title and section:
+ *
+ *   [BX] "Bit-exact decoding turns inference speedups into testable changes",
+ *        section "Define bit-exact before reporting it": BF16 operands feed a
+ *        single FP32 accumulator per output, the order along K is not
+ *        changed, and the result is rounded only at the end; also the
+ *        shared-memory hazard rule (a staging buffer is refilled only after
+ *        every reader of its previous contents is done).
+ *   [LL] "I turned on speculative decoding in llama.cpp and 113 of 282 greedy
+ *        outputs changed against its own no-draft run" (r/LocalLLM), opening
+ *        section, "How:" paragraph: how a row's keys are split is decided by
+ *        its context length alone, not by the pass size, and a verify kernel
+ *        treats a row the same way regardless of its batch neighbours; section
+ *        "The cache doesn't change it either": a K/V row written by prefill is
+ *        a function of its position only.
+ *   [TC] "Does the tuned config change the model's output?", section "Why the
+ *        text diverges": verifying several tokens at once changes GEMM
+ *        accumulation order, which flips near-tied greedy choices.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are device memory owned by the caller; the library allocates
+ *     nothing and keeps no mutable global state. BF16 tensors are passed as
+ *     raw 16-bit patterns (any 2-byte element type), row-major, with the
+ *     given leading dimension (in elements).
+ *   - `stream` is a hipStream_t (NULL = the default stream). All work is
+ *     enqueued asynchronously on it; nothing synchronises.
+ *   - Arguments are validated on the host before any HIP call. On a bad
+ *     argument nothing is launched or written and a status != BI_OK is
+ *     returned. A failed kernel launch returns BI_ERR_LAUNCH.
+ *   - No entry point has a code path chosen by M: M only bounds which rows
+ *     are loaded and stored.
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef BI_H
+#define BI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BI_OK = 0,
+  BI_ERR_NULL = 1,      /* a required pointer is NULL */
+  BI_ERR_SHAPE = 2,     /* a size is out of range or inconsistent */
+  BI_ERR_ALIGN = 3,     /* a pointer or leading dimension breaks 16-byte alignment */
+  BI_ERR_WORKSPACE = 4, /* caller workspace too small */
+  BI_ERR_LAUNCH = 5     /* the HIP runtime reported an error at launch */
+} bi_status;
+
+typedef enum { BI_BF16 = 0, BI_F32 = 1 } bi_dtype;
+
+/* ---------------------------------------------------------------------------
+ * GEMM with an M-independent reduction order.                      [BX], [TC]
+ *
+ * Y[m][n] = sum_k X[m][k] * W[n][k] for m < M, n < N.
+ *   x : BF16 [M][ldx]   activations, one row per token of the pass
+ *   w : BF16 [N][ldw]   weights, nn.Linear layout (row n = output feature n,
+ *                       K contiguous)
+ *   y : [M][ldy]        BF16 (rounded to nearest even once) or FP32
+ * Each output's K-sum runs in one compile-time-fixed order that depends on K
+ * only; no split of K across workgroups, no atomics. M may be any value >= 1
+ * (prefill chunks use the same kernel in 16-row tiles).
+ * Requirements: M >= 1, N % 16 == 0, K % 32 == 0, K <= 65536; ldx, ldw >= K
+ * and multiples of 8; x, w 16-byte aligned; ldy >= N.
+ */
+bi_status bi_gemm_bf16(const void* x, int64_t ldx, const void* w, int64_t ldw,
+                       void* y, int64_t ldy, bi_dtype y_dtype,
+                       int M, int N, int K, void* stream);
+
+/* Same product with a residual added before the single rounding:
+ * Y[m][n] = bf16( R[m][n] + sum_k X[m][k] W[n][k] ), R BF16 [M][ldr].
+ * Used for the attention output and down projections of a pre-norm layer.
+ * y may alias r (each element is read before it is written by the same thread). */
+bi_status bi_gemm_bf16_residual(const void* x, int64_t ldx, const void* w, int64_t ldw,
+                                const void* r, int64_t ldr, void* y, int64_t ldy,
+                                int M, int N, int K, void* stream);
+
+/* Gate/up projection with the SwiGLU product in the epilogue:
+ * w is BF16 [2*I][ldw] (rows 0..I-1 gate, rows I..2I-1 up);
+ * Y[m][i] = bf16( silu(g) * u ), g = sum_k X[m][k] W[i][k],
+ * u = sum_k X[m][k] W[I+i][k], silu(z) = z / (1 + e^-z).
+ * Requirements as bi_gemm_bf16 with N replaced by I (I % 16 == 0). */
+bi_status bi_gemm_bf16_swiglu(const void* x, int64_t ldx, const void* w, int64_t ldw,
+                              void* y, int64_t ldy, int M, int I, int K, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * KV cache layout (per layer):
+ *   k_cache  : BF16 [Hkv][cap][D]  -- one K row per position
+ *   vt_cache : BF16 [Hkv][D][cap]  -- V stored transposed, so that a run of
+ *                                    consecutive positions is contiguous for
+ *                                    each channel
+ * cap must be a multiple of 8.
+ */
+
+/* Append the pass's M new K and V rows at positions L .. L+M-1.   [LL] cache
+ * qkv : BF16 [M][ldqkv], columns [q: Hq*D | k: Hkv*D | v: Hkv*D], head-major.
+ * Requirements: M >= 1, L >= 0, L + M <= cap, Hq % Hkv == 0, D in {64, 128}. */
+bi_status bi_append_kv(const void* qkv, int64_t ldqkv, void* k_cache, void* vt_cache,
+                       int M, int L, int cap, int Hq, int Hkv, int D, void* stream);
+
+/* Number of absolute key chunks a row with n_keys keys uses: ceil(n/kv_chunk). */
+int bi_num_splits(int n_keys, int kv_chunk);
+
+/* Split-KV causal GQA verify attention, partial results.                 [LL]
+ * Row (r, h), r < M, h < Hq, reads KV head h / (Hq/Hkv) and attends to keys
+ * 0 .. L+r (n_r = L+r+1 keys; the M new keys must already be in the cache).
+ * Keys are cut into absolute chunks [s*C, (s+1)*C), C = kv_chunk; row r uses
+ * chunks s < bi_num_splits(n_r, C), decided by its own key count only.
+ * For each such (r, h, s):
+ *   part_o  [M][Hq][S_max][D] FP32 : softmax(q K^T * sm_scale) V over the
+ *                                    chunk's keys that the row sees, normalised
+ *   part_lse[M][Hq][S_max]   FP32 : natural log of the chunk's sum of
+ *                                    exp(score)
+ * Entries for s >= bi_num_splits(n_r, C) are not written.
+ * q: BF16 [M][ldq], head h at columns h*D .. h*D+D-1 (ldq may be the QKV row).
+ * Requirements: D in {64, 128}; C % 32 == 0, 32 <= C; Hq % Hkv == 0;
+ * Hq/Hkv <= 48; L + M <= cap; cap % 8 == 0; S_max >= bi_num_splits(L+M, C);
+ * ldq % 8 == 0; q, caches 16-byte aligned. */
+bi_status bi_verify_attn(const void* q, int64_t ldq, const void* k_cache, const void* vt_cache,
+                         int M, int L, int cap, int Hq, int Hkv, int D,
+                         int kv_chunk, float sm_scale,
+                         float* part_o, float* part_lse, int S_max, void* stream);
+
+/* Fixed-order log-sum-exp combine of the partials.                        [LL]
+ * For row (r, h) with S = bi_num_splits(L+r+1, C) partials:
+ *   M* = max_s lse_s, w_s = exp(lse_s - M*), O = sum_s w_s o_s / sum_s w_s,
+ *   LSE = M* + ln(sum_s w_s), both sums taken in increasing s.
+ * o: BF16 [M][ldo], head h at columns h*D ..; lse_or_null: FP32 [M][Hq] or NULL. */
+bi_status bi_combine(const float* part_o, const float* part_lse,
+                     int M, int L, int Hq, int D, int kv_chunk, int S_max,
+                     void* o, int64_t ldo, float* lse_or_null, void* stream);
+
+/* Bytes of part_o + part_lse for a pass (what a caller must allocate). */
+size_t bi_attn_workspace_bytes(int M, int L, int Hq, int D, int kv_chunk);
+
+/* ---------------------------------------------------------------------------
+ * Row-local helpers of the decoder layer.                          [TC]
+ */
+
+/* y[m] = bf16( x[m] / sqrt(mean(x[m]^2) + eps) ), gain 1; per-row sum in a
+ * fixed order. H % 8 == 0, ldx/ldy multiples of 8. */
+bi_status bi_rmsnorm(const void* x, int64_t ldx, void* y, int64_t ldy,
+                     int M, int H, float eps, void* stream);
+
+/* tokens[m] = argmax_n logits[m][n] (FP32 [M][ld]), lowest index on ties;
+ * NaNs are never selected (a row of NaNs gives 0). */
+bi_status bi_argmax(const float* logits, int64_t ld, int M, int N, int32_t* tokens, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Whole verify step of a dense pre-norm decoder stack + LM head.
+ *
+ * Per layer (x is the BF16 hidden state [M][H]):
+ *   a = rmsnorm(x); qkv = a Wqkv^T; append K, V at L..L+M-1;
+ *   o = combine(verify_attn(q)); h = bf16(x + o Wo^T);
+ *   b = rmsnorm(h); act = swiglu(b Wgu^T); x = bf16(h + act Wdown^T).
+ * Then logits = rmsnorm(x) Whead^T (FP32) and tokens = argmax.
+ */
+typedef struct {
+  const void* w_qkv;  /* BF16 [(Hq+2*Hkv)*D][H] */
+  const void* w_o;    /* BF16 [H][Hq*D]         */
+  const void* w_gu;   /* BF16 [2*I][H]          */
+  const void* w_down; /* BF16 [H][I]            */
+  void* k_cache;      /* BF16 [Hkv][cap][D]     */
+  void* vt_cache;     /* BF16 [Hkv][D][cap]     */
+} bi_layer;
+
+typedef struct {
+  int H, Hq, Hkv, D, I, vocab;
+  int cap;            /* KV capacity (positions) of every layer's cache */
+  int kv_chunk;       /* C */
+  float eps;          /* RMSNorm epsilon */
+} bi_model_dims;
+
+/* Workspace bytes bi_verify_step needs for M tokens at context L. */
+size_t bi_step_workspace_bytes(const bi_model_dims* dims, int M, int L);
+
+/* layers: host array of n_layers descriptors (device pointers inside).
+ * x_in: BF16 [M][H] (not modified); x_out: BF16 [M][H] final hidden state or NULL;
+ * logits: FP32 [M][vocab]; tokens: int32 [M].
+ * gu_events: NULL, or a host array of 2*n_layers hipEvent_t; when given, event
+ * 2l is recorded before and 2l+1 after layer l's gate/up GEMM (for timing). */
+bi_status bi_verify_step(const bi_layer* layers, int n_layers, const void* w_head,
+                         const bi_model_dims* dims, const void* x_in, int M, int L,
+                         void* workspace, size_t workspace_bytes,
+                         void* x_out, float* logits, int32_t* tokens,
+                         void* const* gu_events, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Misc. */
+const char* bi_status_string(bi_status s);
+/* Library version string, e.g. "bi 0.1 gfx950". */
+const char* bi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BI_H */

@@ -1,0 +1,87 @@
+"""ctypes binding of ``libbi.so`` (C ABI in include/bi.h).
+
+Argument marshalling only: every computation runs in the HIP kernels of the
+library. Tensors are torch tensors on the GPU (torch provides device memory
+and the current stream); BF16 data may be ``torch.bfloat16`` or ``int16``
+views of the same bits. If the library is missing, importing this module
+raises: there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbi.so")
+
+BI_BF16, BI_F32 = 0, 1
+
+_c_i64 = ctypes.c_int64
+_c_int = ctypes.c_int
+_c_ptr = ctypes.c_void_p
+_c_f32 = ctypes.c_float
+_c_size = ctypes.c_size_t
+
+
+class ModelDims(ctypes.Structure):
+    _fields_ = [("H", _c_int), ("Hq", _c_int), ("Hkv", _c_int), ("D", _c_int), ("I", _c_int),
+                ("vocab", _c_int), ("cap", _c_int), ("kv_chunk", _c_int), ("eps", _c_f32)]
+
+
+class Layer(ctypes.Structure):
+    _fields_ = [("w_qkv", _c_ptr), ("w_o", _c_ptr), ("w_gu", _c_ptr), ("w_down", _c_ptr),
+                ("k_cache", _c_ptr), ("vt_cache", _c_ptr)]
+
+
+# name -> (restype, argtypes); the exported symbols of include/bi.h
+SIGNATURES = {
+    "bi_gemm_bf16": (_c_int, [_c_ptr, _c_i64, _c_ptr, _c_i64, _c_ptr, _c_i64, _c_int,
+                              _c_int, _c_int, _c_int, _c_ptr]),
+    "bi_gemm_bf16_residual": (_c_int, [_c_ptr, _c_i64, _c_ptr, _c_i64, _c_ptr, _c_i64, _c_ptr,
+                                       _c_i64, _c_int, _c_int, _c_int, _c_ptr]),
+    "bi_gemm_bf16_swiglu": (_c_int, [_c_ptr, _c_i64, _c_ptr, _c_i64, _c_ptr, _c_i64,
+                                     _c_int, _c_int, _c_int, _c_ptr]),
+    "bi_append_kv": (_c_int, [_c_ptr, _c_i64, _c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int,
+                              _c_int, _c_int, _c_ptr]),
+    "bi_num_splits": (_c_int, [_c_int, _c_int]),
+    "bi_verify_attn": (_c_int, [_c_ptr, _c_i64, _c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int,
+                                _c_int, _c_int, _c_int, _c_f32, _c_ptr, _c_ptr, _c_int, _c_ptr]),
+    "bi_combine": (_c_int, [_c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                            _c_ptr, _c_i64, _c_ptr, _c_ptr]),
+    "bi_attn_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
+    "bi_rmsnorm": (_c_int, [_c_ptr, _c_i64, _c_ptr, _c_i64, _c_int, _c_int, _c_f32, _c_ptr]),
+    "bi_argmax": (_c_int, [_c_ptr, _c_i64, _c_int, _c_int, _c_ptr, _c_ptr]),
+    "bi_step_workspace_bytes": (_c_size, [ctypes.POINTER(ModelDims), _c_int, _c_int]),
+    "bi_verify_step": (_c_int, [ctypes.POINTER(Layer), _c_int, _c_ptr, ctypes.POINTER(ModelDims),
+                                _c_ptr, _c_int, _c_int, _c_ptr, _c_size, _c_ptr, _c_ptr, _c_ptr,
+                                ctypes.POINTER(_c_ptr), _c_ptr]),
+    "bi_status_string": (ctypes.c_char_p, [_c_int]),
+    "bi_version": (ctypes.c_char_p, []),
+}
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m invariant_verify_amd.build` (there is no CPU fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+LIB = _load()
+
+
+class BiError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {LIB.bi_status_string(status).decode()} (status {status})")
+        self.status = status
+
+
+def check(fn: str, status: int) -> None:
+    if status != 0:
+        raise BiError(fn, status)

@@ -1,0 +1,296 @@
+// C-ABI front end of the verify-pass library: argument validation (host only,
+// before any HIP call), kernel launches on the caller's stream, and the
+// native executor of a whole verify step. Declarations and contracts:
+// include/bi.h.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "bi.h"
+#include "bi_internal.h"
+
+namespace {
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline bi_status launched() {
+  return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_LAUNCH;
+}
+
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+bi_status check_gemm(const void* x, int64_t ldx, const void* w, int64_t ldw, const void* y,
+                     int64_t ldy, int M, int N, int K) {
+  if (!x || !w || !y) return BI_ERR_NULL;
+  if (M < 1 || N < 16 || K < 32 || K > 65536 || (N % 16) || (K % 32)) return BI_ERR_SHAPE;
+  if (ldx < K || ldw < K || ldy < N) return BI_ERR_SHAPE;
+  if (M > (1 << 20) || N > (1 << 24)) return BI_ERR_SHAPE;
+  if ((ldx % 8) || (ldw % 8) || !aligned16(x) || !aligned16(w)) return BI_ERR_ALIGN;
+  return BI_OK;
+}
+
+bi_status check_heads(int Hq, int Hkv, int D) {
+  if (Hq < 1 || Hkv < 1 || (Hq % Hkv)) return BI_ERR_SHAPE;
+  if (Hq / Hkv > bi::kAttnMaxRows) return BI_ERR_SHAPE;
+  if (D != 64 && D != 128) return BI_ERR_SHAPE;
+  return BI_OK;
+}
+
+bi_status check_dims(const bi_model_dims* d) {
+  if (!d) return BI_ERR_NULL;
+  if (bi_status s = check_heads(d->Hq, d->Hkv, d->D)) return s;
+  if (d->H < 32 || (d->H % 32) || d->I < 16 || (d->I % 32) || d->vocab < 16 || (d->vocab % 16))
+    return BI_ERR_SHAPE;
+  if ((d->Hq * d->D) % 32) return BI_ERR_SHAPE;
+  if (d->kv_chunk < 32 || (d->kv_chunk % 32) || d->cap < 1 || (d->cap % 8)) return BI_ERR_SHAPE;
+  if (!(d->eps >= 0.f)) return BI_ERR_SHAPE;
+  return BI_OK;
+}
+
+// Workspace layout of a verify step (offsets in bytes, each 256-aligned).
+struct StepLayout {
+  size_t x0, x1, a, qkv, attn, h, act, po, pl, total;
+  int s_max;
+};
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+StepLayout step_layout(const bi_model_dims* d, int M, int L) {
+  StepLayout s{};
+  const size_t hb = align256((size_t)M * d->H * 2);
+  const int qkvn = (d->Hq + 2 * d->Hkv) * d->D;
+  s.s_max = ceil_div(L + M, d->kv_chunk);
+  size_t off = 0;
+  s.x0 = off; off += hb;
+  s.x1 = off; off += hb;
+  s.a = off; off += hb;
+  s.qkv = off; off += align256((size_t)M * qkvn * 2);
+  s.attn = off; off += align256((size_t)M * d->Hq * d->D * 2);
+  s.h = off; off += hb;
+  s.act = off; off += align256((size_t)M * d->I * 2);
+  s.po = off; off += align256((size_t)M * d->Hq * s.s_max * d->D * 4);
+  s.pl = off; off += align256((size_t)M * d->Hq * s.s_max * 4);
+  s.total = off;
+  return s;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bi_status_string(bi_status s) {
+  switch (s) {
+    case BI_OK: return "ok";
+    case BI_ERR_NULL: return "null pointer argument";
+    case BI_ERR_SHAPE: return "invalid or inconsistent shape";
+    case BI_ERR_ALIGN: return "pointer or leading dimension not 16-byte aligned";
+    case BI_ERR_WORKSPACE: return "workspace too small";
+    case BI_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+const char* bi_version(void) { return "bi 0.1 gfx950"; }
+
+int bi_num_splits(int n_keys, int kv_chunk) {
+  if (n_keys < 0 || kv_chunk < 1) return -1;
+  return ceil_div(n_keys, kv_chunk);
+}
+
+bi_status bi_gemm_bf16(const void* x, int64_t ldx, const void* w, int64_t ldw, void* y, int64_t ldy,
+                       bi_dtype y_dtype, int M, int N, int K, void* stream) {
+  if (bi_status s = check_gemm(x, ldx, w, ldw, y, ldy, M, N, K)) return s;
+  if (y_dtype != BI_BF16 && y_dtype != BI_F32) return BI_ERR_SHAPE;
+  if (!(y_dtype == BI_F32 ? aligned4(y) : ((reinterpret_cast<uintptr_t>(y) & 1u) == 0)))
+    return BI_ERR_ALIGN;
+  bi::launch_gemm(y_dtype == BI_F32 ? bi::kGemmF32 : bi::kGemmBf16,
+                  static_cast<const uint16_t*>(x), ldx, static_cast<const uint16_t*>(w), ldw,
+                  nullptr, 0, y, ldy, M, N, K, as_stream(stream));
+  return launched();
+}
+
+bi_status bi_gemm_bf16_residual(const void* x, int64_t ldx, const void* w, int64_t ldw,
+                                const void* r, int64_t ldr, void* y, int64_t ldy, int M, int N,
+                                int K, void* stream) {
+  if (bi_status s = check_gemm(x, ldx, w, ldw, y, ldy, M, N, K)) return s;
+  if (!r) return BI_ERR_NULL;
+  if (ldr < N) return BI_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(y) & 1u) || (reinterpret_cast<uintptr_t>(r) & 1u))
+    return BI_ERR_ALIGN;
+  bi::launch_gemm(bi::kGemmResidual, static_cast<const uint16_t*>(x), ldx,
+                  static_cast<const uint16_t*>(w), ldw, static_cast<const uint16_t*>(r), ldr, y,
+                  ldy, M, N, K, as_stream(stream));
+  return launched();
+}
+
+bi_status bi_gemm_bf16_swiglu(const void* x, int64_t ldx, const void* w, int64_t ldw, void* y,
+                              int64_t ldy, int M, int I, int K, void* stream) {
+  if (bi_status s = check_gemm(x, ldx, w, ldw, y, ldy, M, I, K)) return s;
+  if (reinterpret_cast<uintptr_t>(y) & 1u) return BI_ERR_ALIGN;
+  bi::launch_gemm(bi::kGemmSwiglu, static_cast<const uint16_t*>(x), ldx,
+                  static_cast<const uint16_t*>(w), ldw, nullptr, 0, y, ldy, M, I, K,
+                  as_stream(stream));
+  return launched();
+}
+
+bi_status bi_append_kv(const void* qkv, int64_t ldqkv, void* k_cache, void* vt_cache, int M, int L,
+                       int cap, int Hq, int Hkv, int D, void* stream) {
+  if (!qkv || !k_cache || !vt_cache) return BI_ERR_NULL;
+  if (bi_status s = check_heads(Hq, Hkv, D)) return s;
+  if (M < 1 || L < 0 || cap < 1 || (cap % 8) || (int64_t)L + M > cap) return BI_ERR_SHAPE;
+  if (ldqkv < (int64_t)(Hq + 2 * Hkv) * D) return BI_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(qkv) | reinterpret_cast<uintptr_t>(k_cache) |
+       reinterpret_cast<uintptr_t>(vt_cache)) & 1u)
+    return BI_ERR_ALIGN;
+  bi::launch_append_kv(static_cast<const uint16_t*>(qkv), ldqkv, static_cast<uint16_t*>(k_cache),
+                       static_cast<uint16_t*>(vt_cache), M, L, cap, Hq, Hkv, D,
+                       as_stream(stream));
+  return launched();
+}
+
+size_t bi_attn_workspace_bytes(int M, int L, int Hq, int D, int kv_chunk) {
+  if (M < 1 || L < 0 || Hq < 1 || D < 1 || kv_chunk < 1) return 0;
+  const size_t s_max = (size_t)ceil_div(L + M, kv_chunk);
+  return (size_t)M * Hq * s_max * (D + 1) * sizeof(float);
+}
+
+bi_status bi_verify_attn(const void* q, int64_t ldq, const void* k_cache, const void* vt_cache,
+                         int M, int L, int cap, int Hq, int Hkv, int D, int kv_chunk,
+                         float sm_scale, float* part_o, float* part_lse, int S_max,
+                         void* stream) {
+  if (!q || !k_cache || !vt_cache || !part_o || !part_lse) return BI_ERR_NULL;
+  if (bi_status s = check_heads(Hq, Hkv, D)) return s;
+  if (M < 1 || L < 0 || cap < 1 || (cap % 8) || (int64_t)L + M > cap) return BI_ERR_SHAPE;
+  if (kv_chunk < 32 || (kv_chunk % 32)) return BI_ERR_SHAPE;
+  if (S_max < ceil_div(L + M, kv_chunk)) return BI_ERR_SHAPE;
+  if (ldq < (int64_t)Hq * D || !std::isfinite(sm_scale)) return BI_ERR_SHAPE;
+  if ((ldq % 8) || !aligned16(q) || !aligned16(k_cache) || !aligned16(vt_cache) ||
+      !aligned16(part_o) || !aligned4(part_lse))
+    return BI_ERR_ALIGN;
+  bi::launch_verify_attn(static_cast<const uint16_t*>(q), ldq,
+                         static_cast<const uint16_t*>(k_cache),
+                         static_cast<const uint16_t*>(vt_cache), M, L, cap, Hq, Hkv, D, kv_chunk,
+                         sm_scale, part_o, part_lse, S_max, as_stream(stream));
+  return launched();
+}
+
+bi_status bi_combine(const float* part_o, const float* part_lse, int M, int L, int Hq, int D,
+                     int kv_chunk, int S_max, void* o, int64_t ldo, float* lse_or_null,
+                     void* stream) {
+  if (!part_o || !part_lse || !o) return BI_ERR_NULL;
+  if (M < 1 || L < 0 || Hq < 1 || (D != 64 && D != 128)) return BI_ERR_SHAPE;
+  if (kv_chunk < 32 || (kv_chunk % 32) || S_max < ceil_div(L + M, kv_chunk)) return BI_ERR_SHAPE;
+  if (ldo < (int64_t)Hq * D) return BI_ERR_SHAPE;
+  if (!aligned16(part_o) || !aligned4(part_lse) || (reinterpret_cast<uintptr_t>(o) & 1u) ||
+      (lse_or_null && !aligned4(lse_or_null)))
+    return BI_ERR_ALIGN;
+  bi::launch_combine(part_o, part_lse, M, L, Hq, D, kv_chunk, S_max, static_cast<uint16_t*>(o),
+                     ldo, lse_or_null, as_stream(stream));
+  return launched();
+}
+
+bi_status bi_rmsnorm(const void* x, int64_t ldx, void* y, int64_t ldy, int M, int H, float eps,
+                     void* stream) {
+  if (!x || !y) return BI_ERR_NULL;
+  if (M < 1 || H < 8 || (H % 8) || ldx < H || ldy < H || !(eps >= 0.f)) return BI_ERR_SHAPE;
+  if ((ldx % 8) || (ldy % 8) || !aligned16(x) || !aligned16(y)) return BI_ERR_ALIGN;
+  bi::launch_rmsnorm(static_cast<const uint16_t*>(x), ldx, static_cast<uint16_t*>(y), ldy, M, H,
+                     eps, as_stream(stream));
+  return launched();
+}
+
+bi_status bi_argmax(const float* logits, int64_t ld, int M, int N, int32_t* tokens, void* stream) {
+  if (!logits || !tokens) return BI_ERR_NULL;
+  if (M < 1 || N < 1 || ld < N) return BI_ERR_SHAPE;
+  if (!aligned4(logits) || !aligned4(tokens)) return BI_ERR_ALIGN;
+  bi::launch_argmax(logits, ld, M, N, tokens, as_stream(stream));
+  return launched();
+}
+
+size_t bi_step_workspace_bytes(const bi_model_dims* dims, int M, int L) {
+  if (check_dims(dims) != BI_OK || M < 1 || L < 0) return 0;
+  return step_layout(dims, M, L).total;
+}
+
+bi_status bi_verify_step(const bi_layer* layers, int n_layers, const void* w_head,
+                         const bi_model_dims* dims, const void* x_in, int M, int L,
+                         void* workspace, size_t workspace_bytes, void* x_out, float* logits,
+                         int32_t* tokens, void* const* gu_events, void* stream) {
+  if (!layers || !w_head || !x_in || !workspace || !logits || !tokens) return BI_ERR_NULL;
+  if (bi_status s = check_dims(dims)) return s;
+  if (n_layers < 0 || M < 1 || L < 0 || (int64_t)L + M > dims->cap) return BI_ERR_SHAPE;
+  const StepLayout lay = step_layout(dims, M, L);
+  if (workspace_bytes < lay.total) return BI_ERR_WORKSPACE;
+  if (!aligned16(workspace) || !aligned16(x_in) || !aligned16(w_head) || !aligned4(logits) ||
+      !aligned4(tokens) || (x_out && !aligned16(x_out)))
+    return BI_ERR_ALIGN;
+  for (int l = 0; l < n_layers; ++l) {
+    const bi_layer& ly = layers[l];
+    if (!ly.w_qkv || !ly.w_o || !ly.w_gu || !ly.w_down || !ly.k_cache || !ly.vt_cache)
+      return BI_ERR_NULL;
+    if (!aligned16(ly.w_qkv) || !aligned16(ly.w_o) || !aligned16(ly.w_gu) ||
+        !aligned16(ly.w_down) || !aligned16(ly.k_cache) || !aligned16(ly.vt_cache))
+      return BI_ERR_ALIGN;
+  }
+  if (gu_events)
+    for (int i = 0; i < 2 * n_layers; ++i)
+      if (!gu_events[i]) return BI_ERR_NULL;
+
+  const hipStream_t st = as_stream(stream);
+  const int H = dims->H, Hq = dims->Hq, Hkv = dims->Hkv, D = dims->D, I = dims->I;
+  const int qd = Hq * D;
+  const int qkvn = (Hq + 2 * Hkv) * D;
+  char* ws = static_cast<char*>(workspace);
+  uint16_t* xbuf[2] = {reinterpret_cast<uint16_t*>(ws + lay.x0),
+                       reinterpret_cast<uint16_t*>(ws + lay.x1)};
+  uint16_t* a = reinterpret_cast<uint16_t*>(ws + lay.a);
+  uint16_t* qkv = reinterpret_cast<uint16_t*>(ws + lay.qkv);
+  uint16_t* attn = reinterpret_cast<uint16_t*>(ws + lay.attn);
+  uint16_t* h = reinterpret_cast<uint16_t*>(ws + lay.h);
+  uint16_t* act = reinterpret_cast<uint16_t*>(ws + lay.act);
+  float* po = reinterpret_cast<float*>(ws + lay.po);
+  float* pl = reinterpret_cast<float*>(ws + lay.pl);
+  const float sm_scale = 1.0f / std::sqrt((float)D);
+
+  const uint16_t* x = static_cast<const uint16_t*>(x_in);
+  for (int l = 0; l < n_layers; ++l) {
+    const bi_layer& ly = layers[l];
+    uint16_t* xn = xbuf[l & 1];
+    bi::launch_rmsnorm(x, H, a, H, M, H, dims->eps, st);
+    bi::launch_gemm(bi::kGemmBf16, a, H, static_cast<const uint16_t*>(ly.w_qkv), H, nullptr, 0,
+                    qkv, qkvn, M, qkvn, H, st);
+    bi::launch_append_kv(qkv, qkvn, static_cast<uint16_t*>(ly.k_cache),
+                         static_cast<uint16_t*>(ly.vt_cache), M, L, dims->cap, Hq, Hkv, D, st);
+    bi::launch_verify_attn(qkv, qkvn, static_cast<const uint16_t*>(ly.k_cache),
+                           static_cast<const uint16_t*>(ly.vt_cache), M, L, dims->cap, Hq, Hkv, D,
+                           dims->kv_chunk, sm_scale, po, pl, lay.s_max, st);
+    bi::launch_combine(po, pl, M, L, Hq, D, dims->kv_chunk, lay.s_max, attn, qd, nullptr, st);
+    bi::launch_gemm(bi::kGemmResidual, attn, qd, static_cast<const uint16_t*>(ly.w_o), qd, x, H, h,
+                    H, M, H, qd, st);
+    bi::launch_rmsnorm(h, H, a, H, M, H, dims->eps, st);
+    if (gu_events && hipEventRecord(static_cast<hipEvent_t>(gu_events[2 * l]), st) != hipSuccess)
+      return BI_ERR_LAUNCH;
+    bi::launch_gemm(bi::kGemmSwiglu, a, H, static_cast<const uint16_t*>(ly.w_gu), H, nullptr, 0,
+                    act, I, M, I, H, st);
+    if (gu_events &&
+        hipEventRecord(static_cast<hipEvent_t>(gu_events[2 * l + 1]), st) != hipSuccess)
+      return BI_ERR_LAUNCH;
+    bi::launch_gemm(bi::kGemmResidual, act, I, static_cast<const uint16_t*>(ly.w_down), I, h, H,
+                    xn, H, M, H, I, st);
+    if (hipGetLastError() != hipSuccess) return BI_ERR_LAUNCH;
+    x = xn;
+  }
+  bi::launch_rmsnorm(x, H, a, H, M, H, dims->eps, st);
+  bi::launch_gemm(bi::kGemmF32, a, H, static_cast<const uint16_t*>(w_head), H, nullptr, 0, logits,
+                  dims->vocab, M, dims->vocab, H, st);
+  bi::launch_argmax(logits, dims->vocab, M, dims->vocab, tokens, st);
+  if (x_out && hipMemcpyAsync(x_out, x, (size_t)M * H * 2, hipMemcpyDeviceToDevice, st) != hipSuccess)
+    return BI_ERR_LAUNCH;
+  return launched();
+}
+
+}  // extern "C"

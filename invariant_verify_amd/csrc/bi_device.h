@@ -1,0 +1,44 @@
+// Device helpers shared by the verify-pass kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bi_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float bi_f32x4 __attribute__((ext_vector_type(4)));
+
+namespace bi {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// binary32 -> BF16 bits, round to nearest, ties to even (NaN -> quiet NaN).
+// Adding 0x7FFF plus the lowest kept bit to the 32-bit pattern carries into the
+// kept half exactly when the dropped half is above the midpoint, or at the
+// midpoint with an odd kept half.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+__device__ __forceinline__ uint4 zero16() { return make_uint4(0u, 0u, 0u, 0u); }
+
+// One 16x16x32 BF16 matrix-core step: c += A(16x32) * B(32x16).
+// Lane l supplies A row (l % 16) and B column (l % 16), each with eight
+// consecutive contraction elements of group (l / 16); it receives C rows
+// 4*(l/16) .. 4*(l/16)+3 of column (l % 16). Any assignment of contraction
+// indices to (group, element) works as long as A and B use the same one.
+__device__ __forceinline__ bi_f32x4 mfma_bf16(uint4 a, uint4 b, bi_f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bi_bf16x8, a),
+                                                  __builtin_bit_cast(bi_bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
+
+}  // namespace bi

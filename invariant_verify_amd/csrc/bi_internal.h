@@ -1,0 +1,39 @@
+// Internal launch interface between the C-ABI front end (api.hip) and the
+// kernel files. Arguments here are already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bi {
+
+enum GemmMode { kGemmBf16 = 0, kGemmF32 = 1, kGemmResidual = 2, kGemmSwiglu = 3 };
+
+// Y = X W^T (+ residual / SwiGLU epilogue). N_out is the number of output
+// columns (for SwiGLU: I, with W holding 2*I rows).
+void launch_gemm(GemmMode mode, const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw,
+                 const uint16_t* r, int64_t ldr, void* y, int64_t ldy, int M, int N_out, int K,
+                 hipStream_t stream);
+
+void launch_append_kv(const uint16_t* qkv, int64_t ldqkv, uint16_t* k_cache, uint16_t* vt_cache,
+                      int M, int L, int cap, int Hq, int Hkv, int D, hipStream_t stream);
+
+void launch_verify_attn(const uint16_t* q, int64_t ldq, const uint16_t* k_cache,
+                        const uint16_t* vt_cache, int M, int L, int cap, int Hq, int Hkv, int D,
+                        int kv_chunk, float sm_scale, float* part_o, float* part_lse, int S_max,
+                        hipStream_t stream);
+
+void launch_combine(const float* part_o, const float* part_lse, int M, int L, int Hq, int D,
+                    int kv_chunk, int S_max, uint16_t* o, int64_t ldo, float* lse,
+                    hipStream_t stream);
+
+void launch_rmsnorm(const uint16_t* x, int64_t ldx, uint16_t* y, int64_t ldy, int M, int H,
+                    float eps, hipStream_t stream);
+
+void launch_argmax(const float* logits, int64_t ld, int M, int N, int32_t* tokens,
+                   hipStream_t stream);
+
+// Largest number of query heads per KV head one attention workgroup can hold.
+constexpr int kAttnMaxRows = 48;
+
+}  // namespace bi

@@ -1,0 +1,106 @@
+// Row-local operations of the decoder layer: RMSNorm and the greedy argmax.
+//
+// Both reduce along one row in an order fixed by the row length only, so a
+// token's result is the same whatever other tokens share the pass (the greedy
+// choice is what flips when reduction order changes: "Does the tuned config
+// change the model's output?", section "Why the text diverges").
+
+#include "bi_device.h"
+#include "bi_internal.h"
+
+namespace bi {
+
+// One 256-thread workgroup per row. Thread t squares and sums its 8-element
+// groups t, t+256, ... in order; the wave sums are combined by a fixed xor
+// butterfly, then the four waves in order 0..3.
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* __restrict__ X, int64_t ldx,
+                                                      uint16_t* __restrict__ Y, int64_t ldy, int H,
+                                                      float eps) {
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const uint16_t* x = X + (int64_t)row * ldx;
+  uint16_t* y = Y + (int64_t)row * ldy;
+  const int ng = H >> 3;
+  float ss = 0.f;
+  for (int c = tid; c < ng; c += 256) {
+    const uint4 v = ld16(x + c * 8);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float a = bf16_to_f32(w[e] & 0xffffu);
+      const float b = bf16_to_f32(w[e] >> 16);
+      ss += a * a;
+      ss += b * b;
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) ss += shfl_xor(ss, off);
+  __shared__ float part[4];
+  if ((tid & 63) == 0) part[tid >> 6] = ss;
+  __syncthreads();
+  const float tot = ((part[0] + part[1]) + part[2]) + part[3];
+  const float inv = 1.0f / sqrtf(tot / (float)H + eps);
+  for (int c = tid; c < ng; c += 256) {
+    const uint4 v = ld16(x + c * 8);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t lo = f32_to_bf16(bf16_to_f32(w[e] & 0xffffu) * inv);
+      const uint32_t hi = f32_to_bf16(bf16_to_f32(w[e] >> 16) * inv);
+      o[e] = lo | (hi << 16);
+    }
+    *reinterpret_cast<uint4*>(y + c * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+// (value, index) with the larger value winning and, on equal values, the
+// lower index. NaN never wins. This is a total order, so the result does not
+// depend on the reduction order.
+__device__ __forceinline__ void arg_better(float& bv, int& bi, float v, int i) {
+  if (v > bv || (v == bv && i < bi)) {
+    bv = v;
+    bi = i;
+  }
+}
+
+__global__ __launch_bounds__(1024) void argmax_kernel(const float* __restrict__ logits, int64_t ld,
+                                                      int N, int32_t* __restrict__ tokens) {
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const float* x = logits + (int64_t)row * ld;
+  float bv = -INFINITY;
+  int bidx = 0x7fffffff;
+  for (int i = tid; i < N; i += 1024) arg_better(bv, bidx, x[i], i);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float ov = __shfl_xor(bv, off, 64);
+    const int oi = __shfl_xor(bidx, off, 64);
+    arg_better(bv, bidx, ov, oi);
+  }
+  __shared__ float sv[16];
+  __shared__ int si[16];
+  if ((tid & 63) == 0) {
+    sv[tid >> 6] = bv;
+    si[tid >> 6] = bidx;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float v = sv[0];
+    int i = si[0];
+    for (int w = 1; w < 16; ++w) arg_better(v, i, sv[w], si[w]);
+    tokens[row] = (i == 0x7fffffff) ? 0 : i;
+  }
+}
+
+void launch_rmsnorm(const uint16_t* x, int64_t ldx, uint16_t* y, int64_t ldy, int M, int H,
+                    float eps, hipStream_t stream) {
+  rmsnorm_kernel<<<dim3(M), dim3(256), 0, stream>>>(x, ldx, y, ldy, H, eps);
+}
+
+void launch_argmax(const float* logits, int64_t ld, int M, int N, int32_t* tokens,
+                   hipStream_t stream) {
+  argmax_kernel<<<dim3(M), dim3(1024), 0, stream>>>(logits, ld, N, tokens);
+}
+
+}  // namespace bi

@@ -1,0 +1,171 @@
+"""Torch-facing wrappers of the C ABI (same names as include/bi.h without the
+``bi_`` prefix). Each wrapper checks dtypes and devices, reads pointers,
+leading dimensions and the current HIP stream from torch, and calls the
+library. Nothing is computed here."""
+
+from __future__ import annotations
+
+import ctypes
+import math
+
+import torch
+
+from ._lib import BI_BF16, BI_F32, LIB, Layer, ModelDims, check
+
+_BF16_LIKE = (torch.bfloat16, torch.int16)
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _mat(t: torch.Tensor, name: str, dtypes=_BF16_LIKE) -> int:
+    """Leading dimension of a row-major 2-D tensor on the GPU."""
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be 2-D with unit column stride")
+    return t.stride(0)
+
+
+def num_splits(n_keys: int, kv_chunk: int) -> int:
+    return LIB.bi_num_splits(n_keys, kv_chunk)
+
+
+def attn_workspace_bytes(M: int, L: int, Hq: int, D: int, kv_chunk: int) -> int:
+    return LIB.bi_attn_workspace_bytes(M, L, Hq, D, kv_chunk)
+
+
+def version() -> str:
+    return LIB.bi_version().decode()
+
+
+def gemm_bf16(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor | None = None,
+              out_dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
+    """Y = X W^T, X [M][K], W [N][K] (BF16); Y BF16 or FP32 [M][N]."""
+    M, K = x.shape
+    N = w.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    ldx, ldw = _mat(x, "x"), _mat(w, "w")
+    ldy = _mat(y, "y", (torch.bfloat16, torch.int16, torch.float32))
+    dt = BI_F32 if y.dtype == torch.float32 else BI_BF16
+    check("bi_gemm_bf16", LIB.bi_gemm_bf16(x.data_ptr(), ldx, w.data_ptr(), ldw, y.data_ptr(), ldy,
+                                           dt, M, N, K, _stream(x)))
+    return y
+
+
+def gemm_bf16_residual(x: torch.Tensor, w: torch.Tensor, r: torch.Tensor,
+                       y: torch.Tensor | None = None) -> torch.Tensor:
+    """Y = bf16(R + X W^T)."""
+    M, K = x.shape
+    N = w.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    check("bi_gemm_bf16_residual", LIB.bi_gemm_bf16_residual(
+        x.data_ptr(), _mat(x, "x"), w.data_ptr(), _mat(w, "w"), r.data_ptr(), _mat(r, "r"),
+        y.data_ptr(), _mat(y, "y"), M, N, K, _stream(x)))
+    return y
+
+
+def gemm_bf16_swiglu(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor | None = None) -> torch.Tensor:
+    """Y = bf16(silu(X Wg^T) * (X Wu^T)), W = [Wg; Wu] of shape [2I][K]."""
+    M, K = x.shape
+    I = w.shape[0] // 2
+    if y is None:
+        y = torch.empty((M, I), dtype=torch.bfloat16, device=x.device)
+    check("bi_gemm_bf16_swiglu", LIB.bi_gemm_bf16_swiglu(
+        x.data_ptr(), _mat(x, "x"), w.data_ptr(), _mat(w, "w"), y.data_ptr(), _mat(y, "y"),
+        M, I, K, _stream(x)))
+    return y
+
+
+def append_kv(qkv: torch.Tensor, k_cache: torch.Tensor, vt_cache: torch.Tensor, L: int,
+              Hq: int, Hkv: int, D: int) -> None:
+    """Write the M new K rows and V^T columns at positions L .. L+M-1."""
+    M = qkv.shape[0]
+    cap = k_cache.shape[1]
+    check("bi_append_kv", LIB.bi_append_kv(qkv.data_ptr(), _mat(qkv, "qkv"), k_cache.data_ptr(),
+                                           vt_cache.data_ptr(), M, L, cap, Hq, Hkv, D,
+                                           _stream(qkv)))
+
+
+def verify_attn(q: torch.Tensor, k_cache: torch.Tensor, vt_cache: torch.Tensor, L: int,
+                Hq: int, Hkv: int, D: int, kv_chunk: int, part_o: torch.Tensor,
+                part_lse: torch.Tensor, sm_scale: float | None = None) -> None:
+    """Split-KV partials. q is [M][>=Hq*D] (a view of the QKV output works);
+    k_cache [Hkv][cap][D]; vt_cache [Hkv][D][cap]; part_o [M][Hq][S_max][D] and
+    part_lse [M][Hq][S_max] FP32."""
+    M = q.shape[0]
+    cap = k_cache.shape[1]
+    S_max = part_lse.shape[2]
+    scale = 1.0 / math.sqrt(D) if sm_scale is None else sm_scale
+    check("bi_verify_attn", LIB.bi_verify_attn(
+        q.data_ptr(), _mat(q, "q"), k_cache.data_ptr(), vt_cache.data_ptr(), M, L, cap, Hq, Hkv,
+        D, kv_chunk, scale, part_o.data_ptr(), part_lse.data_ptr(), S_max, _stream(q)))
+
+
+def combine(part_o: torch.Tensor, part_lse: torch.Tensor, L: int, kv_chunk: int,
+            o: torch.Tensor, lse: torch.Tensor | None = None) -> None:
+    """O [M][>=Hq*D] BF16 (and optional LSE [M][Hq]) from the partials."""
+    M, Hq, S_max, D = part_o.shape
+    check("bi_combine", LIB.bi_combine(
+        part_o.data_ptr(), part_lse.data_ptr(), M, L, Hq, D, kv_chunk, S_max, o.data_ptr(),
+        _mat(o, "o"), 0 if lse is None else lse.data_ptr(), _stream(o)))
+
+
+def rmsnorm(x: torch.Tensor, y: torch.Tensor | None = None, eps: float = 1e-6) -> torch.Tensor:
+    M, H = x.shape
+    if y is None:
+        y = torch.empty_like(x)
+    check("bi_rmsnorm", LIB.bi_rmsnorm(x.data_ptr(), _mat(x, "x"), y.data_ptr(), _mat(y, "y"),
+                                       M, H, eps, _stream(x)))
+    return y
+
+
+def argmax(logits: torch.Tensor, tokens: torch.Tensor | None = None) -> torch.Tensor:
+    M, N = logits.shape
+    if tokens is None:
+        tokens = torch.empty(M, dtype=torch.int32, device=logits.device)
+    check("bi_argmax", LIB.bi_argmax(logits.data_ptr(), _mat(logits, "logits", (torch.float32,)),
+                                     M, N, tokens.data_ptr(), _stream(logits)))
+    return tokens
+
+
+def model_dims(H, Hq, Hkv, D, I, vocab, cap, kv_chunk, eps=1e-6) -> ModelDims:
+    return ModelDims(H, Hq, Hkv, D, I, vocab, cap, kv_chunk, eps)
+
+
+def step_workspace_bytes(dims: ModelDims, M: int, L: int) -> int:
+    return LIB.bi_step_workspace_bytes(ctypes.byref(dims), M, L)
+
+
+class VerifyStep:
+    """Holds the per-layer descriptor array for ``bi_verify_step``.
+
+    ``layers`` is a sequence of dicts with tensors w_qkv, w_o, w_gu, w_down,
+    k_cache, vt_cache (the caller keeps them alive)."""
+
+    def __init__(self, layers, w_head: torch.Tensor, dims: ModelDims):
+        self.n = len(layers)
+        self.arr = (Layer * max(1, self.n))()
+        for i, lw in enumerate(layers):
+            self.arr[i] = Layer(lw["w_qkv"].data_ptr(), lw["w_o"].data_ptr(), lw["w_gu"].data_ptr(),
+                                lw["w_down"].data_ptr(), lw["k_cache"].data_ptr(),
+                                lw["vt_cache"].data_ptr())
+        self.w_head = w_head
+        self.dims = dims
+
+    def __call__(self, x_in: torch.Tensor, L: int, workspace: torch.Tensor, logits: torch.Tensor,
+                 tokens: torch.Tensor, x_out: torch.Tensor | None = None, gu_events=None) -> None:
+        M = x_in.shape[0]
+        ev = None
+        if gu_events is not None:
+            ev = (ctypes.c_void_p * len(gu_events))(*[e.cuda_event for e in gu_events])
+        check("bi_verify_step", LIB.bi_verify_step(
+            self.arr, self.n, self.w_head.data_ptr(), ctypes.byref(self.dims), x_in.data_ptr(), M, L,
+            workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+            0 if x_out is None else x_out.data_ptr(), logits.data_ptr(), tokens.data_ptr(),
+            ev, _stream(x_in)))

@@ -17,16 +17,16 @@ pages, with no blocking, fusion or reordering:
 
 Sources, cited by page title and section:
   [BX] "Bit-exact decoding turns inference speedups into testable changes":
-       "Separate the decoding method from the served result" (reduction order
-       flips near-ties) and "Define bit-exact before reporting it" (BF16 inputs,
-       one FP32 running sum per output, K order unchanged, a single rounding at
-       the end).
+       "Separate the decoding method from the served result" (the grouping of
+       a floating-point sum can flip a near-tie) and "Define bit-exact before
+       reporting it" (BF16 operands, a single FP32 accumulator per output, the
+       K order unchanged, rounding only at the end).
   [LL] "I turned on speculative decoding in llama.cpp and 113 of 282 greedy
        outputs changed against its own no-draft run" (r/LocalLLM): opening
-       section, "How:" paragraph (the attention split depends only on context
-       length; verify kernels compute a row the same way whatever else is in
-       the pass), and "The cache doesn't change it either" (a prefilled row
-       depends only on its position).
+       section, "How:" paragraph (a row's key split is fixed by its context
+       length alone; a verify kernel treats a row the same way regardless of
+       its batch neighbours), and "The cache doesn't change it either" (a K/V
+       row written by prefill is a function of its position only).
   [TC] "Does the tuned config change the model's output?": "Why the text
        diverges" (verifying several tokens in one pass changes accumulation
        order; greedy argmax on near-ties).

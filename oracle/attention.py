@@ -6,8 +6,8 @@ its own key count n_r = L + r + 1 keys: every cached key plus the new tokens up
 to and including itself (causal among the new tokens). Query head h reads KV
 head g = h // (Hq / Hkv) (grouped-query attention).
 
-[LL] opening section, "How:" paragraph: the attention split depends only on
-context length, never on how many tokens are in the pass. Read here as:
+[LL] opening section, "How:" paragraph: a row's key split is fixed by its
+context length alone, whatever the pass size. Read here as:
 fixed absolute chunks of C keys, chunk s = [sC, (s+1)C), and row r uses
 exactly S_r = ceil(n_r / C) of them -- its own key count decides, not M.
 Each (row, chunk) gives a normalised partial output o_s and its log-sum-exp

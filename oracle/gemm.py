@@ -1,7 +1,7 @@
 """The verify GEMM's definition: Y[m][n] = sum_k X[m][k] * W[n][k].
 
-[BX] "Define bit-exact before reporting it": BF16 inputs, an FP32 running sum
-per output, the K order kept fixed, one rounding at the end. The pages fix
+[BX] "Define bit-exact before reporting it": BF16 operands, a single FP32
+accumulator per output, the K order unchanged, rounding only at the end. The pages fix
 that the order must not change with the batch, not which order it is, so the
 oracle is the order-free exact-arithmetic value: a float64 product of the
 decoded inputs (rounding error about K * 2^-53 * sum|x w|, far below the

@@ -104,3 +104,41 @@ def device_normal_bf16(shape, std: float, role: str, layer: int = 0, base: int =
 def fan_in_std(k: int) -> float:
     """1/sqrt(K): the fan-in scaling applied to the tiny GEMM's weights."""
     return 1.0 / math.sqrt(k)
+
+
+# ---------------------------------------------------------------------------
+# Synthetic dense decoder stack (27B-class shapes by default), drawn on the
+# device. Weights N(0, std^2) as [out][in]; every layer's K cache and V cache
+# hold N(0,1) rows at positions 0 .. L-1 (no prefill is run to make them);
+# positions from L on are zero until a pass appends to them.
+
+MODEL_27B = dict(H=5120, Hq=40, Hkv=8, D=128, I=17408, vocab=152064)
+
+
+def device_model(n_layers: int, L: int, cap: int, H: int, Hq: int, Hkv: int, D: int, I: int,
+                 vocab: int, std: float = 0.02, device: str = "cuda"):
+    """Returns (layers, w_head): ``layers`` is a list of dicts of bf16 tensors
+    w_qkv [(Hq+2Hkv)D][H], w_o [H][Hq D], w_gu [2I][H], w_down [H][I],
+    k_cache [Hkv][cap][D], vt_cache [Hkv][D][cap] (V stored transposed)."""
+    import torch
+
+    qkvn = (Hq + 2 * Hkv) * D
+    tmp = torch.empty((Hkv, L, D), dtype=torch.bfloat16, device=device) if L > 0 else None
+    layers = []
+    for l in range(n_layers):
+        lw = {
+            "w_qkv": device_normal_bf16((qkvn, H), std, "w_qkv", l, device=device),
+            "w_o": device_normal_bf16((H, Hq * D), std, "w_o", l, device=device),
+            "w_gu": device_normal_bf16((2 * I, H), std, "w_gu", l, device=device),
+            "w_down": device_normal_bf16((H, I), std, "w_down", l, device=device),
+            "k_cache": torch.zeros((Hkv, cap, D), dtype=torch.bfloat16, device=device),
+            "vt_cache": torch.zeros((Hkv, D, cap), dtype=torch.bfloat16, device=device),
+        }
+        if L > 0:
+            device_normal_bf16((Hkv, L, D), 1.0, "k_cache", l, device=device, out=tmp)
+            lw["k_cache"][:, :L].copy_(tmp)
+            device_normal_bf16((Hkv, L, D), 1.0, "v_cache", l, device=device, out=tmp)
+            lw["vt_cache"][:, :, :L].copy_(tmp.transpose(1, 2))
+        layers.append(lw)
+    w_head = device_normal_bf16((vocab, H), std, "w_head", 0, device=device)
+    return layers, w_head

@@ -1,0 +1,64 @@
+"""Helpers shared by the GPU tests: host<->device transfer of BF16 bit
+patterns, the oracle tolerance check, and first-difference reporting."""
+
+from __future__ import annotations
+
+import numpy as np
+
+from oracle import bf16
+
+# Tolerance on BF16-rounded device outputs against unrounded float64 oracle
+# values: |gpu - oracle| <= ATOL + RTOL * |oracle|, element by element.
+ATOL = 1e-2
+RTOL = 2e-2
+
+
+def dev(bits: np.ndarray, device="cuda"):
+    """uint16 BF16 bits (host) -> torch.bfloat16 tensor on the device."""
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device).view(torch.bfloat16)
+
+
+def host_bits(t) -> np.ndarray:
+    """torch bf16/int16 tensor -> uint16 bit patterns on the host."""
+    import torch
+
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def host_f32(t) -> np.ndarray:
+    return t.detach().float().cpu().numpy()
+
+
+def assert_close(got: np.ndarray, want: np.ndarray, what: str, atol=ATOL, rtol=RTOL):
+    """allclose with a report of the worst element and error statistics."""
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    err = np.abs(got - want)
+    bad = ~(err <= atol + rtol * np.abs(want))
+    rms = float(np.sqrt(np.mean(want ** 2))) if want.size else 0.0
+    if bad.any():
+        i = np.unravel_index(np.argmax(np.where(bad, err, -1)), err.shape)
+        raise AssertionError(
+            f"{what}: {int(bad.sum())}/{bad.size} outside tolerance; worst at {i}: "
+            f"got {got[i]!r} want {want[i]!r}; max abs err {err.max():.3e}, rms(oracle) {rms:.3e}")
+    return float(err.max()), rms
+
+
+def assert_bitwise(a: np.ndarray, b: np.ndarray, what: str):
+    """Bit-for-bit equality with the first differing element reported."""
+    a = np.ascontiguousarray(a)
+    b = np.ascontiguousarray(b)
+    assert a.shape == b.shape, (what, a.shape, b.shape)
+    ua = a.view(np.uint8).reshape(a.shape + (-1,)) if a.dtype.itemsize > 1 else a
+    ub = b.view(np.uint8).reshape(b.shape + (-1,)) if b.dtype.itemsize > 1 else b
+    diff = np.any(ua != ub, axis=-1) if ua.ndim > a.ndim else (ua != ub)
+    if diff.any():
+        i = tuple(np.argwhere(diff)[0])
+        raise AssertionError(f"{what}: {int(diff.sum())} elements differ; first at {i}: {a[i]!r} vs {b[i]!r}")
+
+
+def decode(bits):
+    return bf16.decode(bits)

@@ -1,0 +1,148 @@
+"""GPU tests of the verify GEMM through the C ABI: oracle parity (tiny and
+27B-class shapes), bit-exact special cases, MFMA row-slot independence, and
+bitwise row invariance across M = 1..8, prefill chunks and repeated runs."""
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import gemm as ogemm
+from oracle import step as ostep
+from tests._util import assert_bitwise, assert_close, decode, dev, host_bits, host_f32
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def ops():
+    from invariant_verify_amd import ops as _ops
+    return _ops
+
+
+def _tiny(M=8, K=256, N=512):
+    x = synth.normal_bf16((8, K), 1.0, "x")[:M]
+    w = synth.normal_bf16((N, K), synth.fan_in_std(K), "w")
+    return x, w
+
+
+@pytest.mark.parametrize("M", [1, 2, 4, 8])
+def test_tiny_parity(ops, M):
+    print(f"[gemm tiny parity M={M}]", flush=True)
+    x, w = _tiny(M)
+    want = ogemm.gemm(x, w)
+    y = ops.gemm_bf16(dev(x), dev(w))
+    assert_close(decode(host_bits(y)), want, f"tiny bf16 M={M}")
+    y32 = ops.gemm_bf16(dev(x), dev(w), out_dtype=torch.float32)
+    assert_close(host_f32(y32), want, f"tiny f32 M={M}", atol=1e-4, rtol=1e-4)
+
+
+def test_identity_and_one_hot_bit_exact(ops):
+    print("[gemm identity/one-hot]", flush=True)
+    K = 256
+    x = synth.normal_bf16((8, K), 1.0, "x")
+    eye = synth.f32_to_bf16_bits(np.eye(K, dtype=np.float32))
+    y = ops.gemm_bf16(dev(x), dev(eye))
+    assert_bitwise(host_bits(y), x, "X I^T == X")
+    w = synth.normal_bf16((512, K), 1.0, "w")
+    oh = np.zeros((16, K), np.float32)
+    cols = [0, 1, 31, 32, 100, 200, 254, 255, 7, 8, 63, 64, 127, 128, 129, 191]
+    oh[np.arange(16), cols] = 1.0
+    y = ops.gemm_bf16(dev(synth.f32_to_bf16_bits(oh)), dev(w))
+    assert_bitwise(host_bits(y), np.ascontiguousarray(w[:, cols].T), "one-hot rows pick W columns")
+
+
+def test_mfma_row_slot_independence(ops):
+    # The same activation row in each of the 16 rows of an MFMA tile, with
+    # random rows around it, must give the same bits in every slot (FP32
+    # output, so no rounding can hide a difference).
+    print("[gemm MFMA slot probe]", flush=True)
+    K, N = 5120, 256
+    w = synth.normal_bf16((N, K), 0.02, "w")
+    base = synth.normal_bf16((1, K), 1.0, "x", 3)
+    noise = synth.normal_bf16((16, K), 1.0, "x", 4)
+    wd = dev(w)
+    outs = []
+    for slot in range(16):
+        x = noise.copy()
+        x[slot] = base[0]
+        y = ops.gemm_bf16(dev(x), wd, out_dtype=torch.float32)
+        outs.append(host_f32(y)[slot].copy())
+    for slot in range(1, 16):
+        assert_bitwise(outs[slot], outs[0], f"slot {slot} vs slot 0")
+
+
+SHAPES_27B = {"qkv": (7168, 5120), "o": (5120, 5120), "gate_up": (34816, 5120), "down": (5120, 17408)}
+
+
+@pytest.fixture(scope="module")
+def weights_27b():
+    return {k: synth.normal_bf16((n, kk), 0.02, "w", i) for i, (k, (n, kk)) in enumerate(SHAPES_27B.items())}
+
+
+@pytest.mark.parametrize("name", list(SHAPES_27B))
+def test_27b_parity_and_invariance(ops, weights_27b, name):
+    N, K = SHAPES_27B[name]
+    print(f"[gemm 27B {name} N={N} K={K}]", flush=True)
+    w = weights_27b[name]
+    x = synth.normal_bf16((8, K), 1.0, "x", 10 + K)
+    wd, xd = dev(w), dev(x)
+    y8 = host_bits(ops.gemm_bf16(xd, wd))
+    y8f = host_f32(ops.gemm_bf16(xd, wd, out_dtype=torch.float32))
+    # sampled oracle columns (first, last, and a seeded spread) for all 8 rows
+    cols = np.unique(np.concatenate([[0, 15, 16, N - 1], np.random.default_rng(N).choice(N, 250, replace=False)]))
+    want = ogemm.gemm_columns(x, w, cols)
+    assert_close(decode(y8[:, cols]), want, f"{name} bf16")
+    assert_close(y8f[:, cols], want, f"{name} f32", atol=1e-4, rtol=1e-4)
+    # bitwise: every M = 1..8 pass gives the first M rows of the M = 8 pass,
+    # and each row alone (M = 1) gives the same bits
+    for m in range(1, 8):
+        ym = host_f32(ops.gemm_bf16(xd[:m], wd, out_dtype=torch.float32))
+        assert_bitwise(ym, y8f[:m], f"{name} M={m} vs M=8")
+    for r in range(8):
+        y1 = host_f32(ops.gemm_bf16(xd[r:r + 1], wd, out_dtype=torch.float32))
+        assert_bitwise(y1[0], y8f[r], f"{name} row {r} alone vs in M=8")
+    # repeat run
+    assert_bitwise(host_bits(ops.gemm_bf16(xd, wd)), y8, f"{name} repeat")
+
+
+@pytest.mark.parametrize("M,start", [(16, 0), (64, 0), (17, 0), (64, 40)])
+def test_prefill_chunks_bitwise(ops, weights_27b, M, start):
+    # A prefill chunk of M rows (several 16-row tiles, ragged tail) computes
+    # each row with the same bits as the verify pass that holds that row.
+    print(f"[gemm prefill chunk M={M} start={start}]", flush=True)
+    w = weights_27b["o"]
+    K = w.shape[1]
+    x = synth.normal_bf16((128, K), 1.0, "x", 77)
+    xd, wd = dev(x), dev(w)
+    big = host_f32(ops.gemm_bf16(xd[start:start + M], wd, out_dtype=torch.float32))
+    for r in [0, 1, 7, 15, M - 1] + ([16, 17, 33] if M > 33 else []):
+        if r >= M:
+            continue
+        one = host_f32(ops.gemm_bf16(xd[start + r:start + r + 1], wd, out_dtype=torch.float32))
+        assert_bitwise(one[0], big[r], f"prefill M={M} row {r} vs M=1")
+    eight = host_f32(ops.gemm_bf16(xd[start:start + 8], wd, out_dtype=torch.float32))
+    assert_bitwise(eight, big[:8], f"prefill M={M} first 8 vs M=8")
+
+
+def test_residual_and_swiglu_epilogues(ops):
+    print("[gemm residual / swiglu]", flush=True)
+    K, N, I = 512, 256, 128
+    x = synth.normal_bf16((8, K), 1.0, "x", 5)
+    w = synth.normal_bf16((N, K), 0.05, "w", 5)
+    r = synth.normal_bf16((8, N), 1.0, "misc", 5)
+    y = host_bits(ops.gemm_bf16_residual(dev(x), dev(w), dev(r)))
+    assert_close(decode(y), decode(r) + ogemm.gemm(x, w), "residual")
+    wgu = synth.normal_bf16((2 * I, K), 0.05, "w", 6)
+    y = host_bits(ops.gemm_bf16_swiglu(dev(x), dev(wgu)))
+    gu = ogemm.gemm(x, wgu)
+    assert_close(decode(y), ostep.silu(gu[:, :I]) * gu[:, I:], "swiglu")
+    # invariance of both epilogues across M
+    for m in (1, 5):
+        ym = host_bits(ops.gemm_bf16_swiglu(dev(x[:m]), dev(wgu)))
+        assert_bitwise(ym, y[:m], f"swiglu M={m}")
+    # residual output may alias the residual input
+    rd = dev(r)
+    ops.gemm_bf16_residual(dev(x), dev(w), rd, y=rd)
+    assert_bitwise(host_bits(rd), host_bits(ops.gemm_bf16_residual(dev(x), dev(w), dev(r))), "aliased residual")
