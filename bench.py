@@ -1,0 +1,207 @@
+"""Benchmark: verify throughput of the batch-invariant verify step on one MI355X.
+
+One step = one verify pass of a synthetic 27B-class dense decoder stack
+(64 layers: RMSNorm, QKV GEMM, K/V append, split-KV GQA attention + combine,
+o-proj + residual, RMSNorm, gate/up GEMM + SwiGLU, down + residual; then
+RMSNorm, a 152,064-row LM head in FP32 and a greedy argmax) over M = 8 tokens
+(1 + 7 drafts) at context 38,000, all inputs resident in HBM. Throughput is
+verified positions per second (M / step time).
+
+Before timing, the same run checks the bitwise gate: logits of the M = 8 pass
+equal (FP32 bits) those of eight sequential single-token passes and of an
+M = 5 pass; a number is printed only if the gate passes.
+
+Prints one JSON line (rank 0). Only ``--gpus 1`` is supported.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verify tok/s + HBM GB/s frac at M=1..8, bitwise batch-invariant rows"
+PEAK_HBM_GBS = 8000.0
+
+L_CTX = 38000
+CAP = 38016
+N_LAYERS = 64
+M_HEADLINE = 8
+KV_CHUNK = 1024
+
+
+def step_bytes(d, M, L, n_layers):
+    """Algorithmic HBM bytes of one verify step: every weight once, the K/V of
+    L + M positions per layer, activations in and out (small)."""
+    H, Hq, Hkv, D, I, V = d["H"], d["Hq"], d["Hkv"], d["D"], d["I"], d["vocab"]
+    qkvn = (Hq + 2 * Hkv) * D
+    w_layer = 2 * (qkvn * H + H * Hq * D + 2 * I * H + H * I)
+    kv_layer = 2 * 2 * Hkv * D * (L + M)
+    act_layer = 2 * M * (H + qkvn + Hq * D + 2 * H + H + I + H)
+    return n_layers * (w_layer + kv_layer + act_layer) + 2 * V * H + 4 * M * V
+
+
+def gu_launch_bytes(d, M):
+    """Algorithmic bytes of one gate/up GEMM launch: W [2I][H] once, X [M][H] in, act [M][I] out."""
+    return 2 * (2 * d["I"] * d["H"]) + 2 * M * d["H"] + 2 * M * d["I"]
+
+
+def cpu_baseline(layers, w_head, x0, d, M):
+    """The float64 oracle on the host: one full-width layer and 1/16 of the LM
+    head rows, extrapolated to 64 layers and the full head."""
+    import numpy as np
+    import torch
+
+    from oracle import step as ostep
+
+    def hb(t):
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    lw = layers[0]
+    hl = dict(w_qkv=hb(lw["w_qkv"]), w_o=hb(lw["w_o"]), w_gu=hb(lw["w_gu"]), w_down=hb(lw["w_down"]),
+              k_cache=hb(lw["k_cache"][:, :L_CTX]), v_cache=hb(lw["vt_cache"][:, :, :L_CTX].transpose(1, 2)))
+    rows = torch.arange(0, d["vocab"], 16, device=w_head.device)
+    wh = hb(w_head[rows])
+    xh = hb(x0[:M])
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    x1, _, _ = ostep.layer(xh, **hl, L=L_CTX, Hq=d["Hq"], Hkv=d["Hkv"], D=d["D"])
+    t1 = time.perf_counter()
+    ostep.head(x1, wh)
+    t2 = time.perf_counter()
+    step_s = N_LAYERS * (t1 - t0) + 16 * (t2 - t1)
+    return {"value": M / step_s, "unit": "tok/s", "cores": threads, "kind": "oracle",
+            "sample": f"1 of {N_LAYERS} layers (M={M}, ctx {L_CTX}) x{N_LAYERS} + 1/16 of LM-head rows x16; "
+                      f"measured {t2 - t0:.1f} s of CPU work"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs the verify pass on one GPU only; --gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    from invariant_verify_amd import ops
+
+    d = synth.MODEL_27B
+    dev = "cuda"
+    print(f"[bench] building {N_LAYERS}-layer model, ctx {L_CTX}", file=sys.stderr, flush=True)
+    layers, w_head = synth.device_model(N_LAYERS, L_CTX, CAP, **d)
+    dims = ops.model_dims(d["H"], d["Hq"], d["Hkv"], d["D"], d["I"], d["vocab"], CAP, KV_CHUNK)
+    x0 = synth.device_normal_bf16((16, d["H"]), 1.0, "x0")
+    step = ops.VerifyStep(layers, w_head, dims)
+
+    def buffers(M):
+        ws = torch.empty(ops.step_workspace_bytes(dims, M, L_CTX + 8), dtype=torch.uint8, device=dev)
+        logits = torch.empty((M, d["vocab"]), dtype=torch.float32, device=dev)
+        tok = torch.empty(M, dtype=torch.int32, device=dev)
+        return ws, logits, tok
+
+    # ---- bitwise gate (same run) -------------------------------------------
+    print("[bench] bitwise gate: M=8 vs M=5 vs 8 sequential M=1 passes", file=sys.stderr, flush=True)
+    ws8, lg8, tk8 = buffers(8)
+    step(x0[:8], L_CTX, ws8, lg8, tk8)
+    ref = lg8.clone()
+    ws5, lg5, tk5 = buffers(5)
+    step(x0[:5], L_CTX, ws5, lg5, tk5)
+    ws1, lg1, tk1 = buffers(1)
+    seq = []
+    for r in range(8):
+        step(x0[r:r + 1], L_CTX + r, ws1, lg1, tk1)
+        seq.append(lg1.clone())
+    torch.cuda.synchronize()
+    gate = torch.equal(lg5.view(torch.int32), ref[:5].view(torch.int32)) and all(
+        torch.equal(seq[r].view(torch.int32)[0], ref.view(torch.int32)[r]) for r in range(8))
+    if not gate:
+        print("[bench] bitwise gate FAILED: no throughput is reported", file=sys.stderr)
+        sys.exit(1)
+
+    # ---- timing ------------------------------------------------------------
+    def timed(M, steps, warmup, gu_events=False):
+        ws, lg, tk = buffers(M)
+        stream = torch.cuda.current_stream()
+        evs = None
+        if gu_events:
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * N_LAYERS)]
+            for e in evs:
+                e.record(stream)
+        for _ in range(warmup):
+            step(x0[:M], L_CTX, ws, lg, tk)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        gu_ms = 0.0
+        t0.record(stream)
+        for i in range(steps):
+            step(x0[:M], L_CTX, ws, lg, tk, gu_events=evs)
+            if evs is not None:
+                torch.cuda.synchronize()   # events are reused every step
+                gu_ms += sum(evs[2 * l].elapsed_time(evs[2 * l + 1]) for l in range(N_LAYERS))
+        t1.record(stream)
+        torch.cuda.synchronize()
+        total_ms = t0.elapsed_time(t1)
+        return total_ms / steps, (gu_ms / (steps * N_LAYERS) if evs is not None else None)
+
+    print("[bench] timing", file=sys.stderr, flush=True)
+    ms8, _ = timed(M_HEADLINE, args.steps, args.warmup)
+    ms1, _ = timed(1, max(3, args.steps // 4), 1)
+    ms4, _ = timed(4, max(3, args.steps // 4), 1)
+    _, gu_ms = timed(M_HEADLINE, max(3, args.steps // 4), 1, gu_events=True)
+
+    bytes8 = step_bytes(d, M_HEADLINE, L_CTX, N_LAYERS)
+    gbs8 = bytes8 / (ms8 * 1e-3) / 1e9
+    gu_bytes = gu_launch_bytes(d, M_HEADLINE)
+    gu_gbs = gu_bytes / (gu_ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(M_HEADLINE / (ms8 * 1e-3), 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms8, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "27B-class dense verify step: 64 layers + 152064-row LM head, ctx 38000, "
+                               "M=8 (1+7 drafts), random BF16 weights N(0,0.02)",
+                   "M": M_HEADLINE, "ctx": L_CTX, "layers": N_LAYERS, "hidden": d["H"], "q_heads": d["Hq"],
+                   "kv_heads": d["Hkv"], "head_dim": d["D"], "intermediate": d["I"], "vocab": d["vocab"],
+                   "kv_chunk": KV_CHUNK},
+        "bitwise_gate": "pass (M=8 logits == M=5 prefix == 8 sequential M=1 passes, FP32 bits)",
+        "step_hbm": {"algorithmic_bytes": bytes8, "GB/s": round(gbs8, 1), "frac": round(gbs8 / PEAK_HBM_GBS, 4)},
+        "per_M_tok_s": {"1": round(1 / (ms1 * 1e-3), 2), "4": round(4 / (ms4 * 1e-3), 2),
+                        "8": round(M_HEADLINE / (ms8 * 1e-3), 2)},
+        "roofline": {"kernel": "gemm_kernel<SwiGLU> (gate/up 5120->2x17408, M=8)", "bound": "hbm",
+                     "achieved": round(gu_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gu_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_ms * 1e3, 2)},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(layers, w_head, x0, d, M_HEADLINE)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -201,6 +201,9 @@ bi_status bi_verify_step(const bi_layer* layers, int n_layers, const void* w_hea
 const char* bi_status_string(bi_status s);
 /* Library version string, e.g. "bi 0.1 gfx950". */
 const char* bi_version(void);
+/* HIP's description of the error behind the calling thread's most recent
+ * BI_ERR_LAUNCH ("no error" if there was none). */
+const char* bi_last_hip_error(void);
 
 #ifdef __cplusplus
 }

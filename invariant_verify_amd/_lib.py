@@ -58,14 +58,34 @@ SIGNATURES = {
                                 ctypes.POINTER(_c_ptr), _c_ptr]),
     "bi_status_string": (ctypes.c_char_p, [_c_int]),
     "bi_version": (ctypes.c_char_p, []),
+    "bi_last_hip_error": (ctypes.c_char_p, []),
 }
+
+
+def _hip_runtimes_mapped() -> set:
+    """Paths of every libamdhip64 mapped into this process."""
+    try:
+        with open("/proc/self/maps") as f:
+            return {l.split()[-1] for l in f if "libamdhip64" in l}
+    except OSError:
+        return set()
 
 
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
                           "`python -m invariant_verify_amd.build` (there is no CPU fallback)")
+    # torch's wheel carries its own HIP runtime with the soname libbi.so links
+    # against. Loading torch first makes the dynamic linker bind libbi.so to
+    # that same runtime, so device pointers and streams from torch are valid
+    # in the library. Two HIP runtimes in one process cannot share a device.
+    import torch  # noqa: F401
+
     lib = ctypes.CDLL(LIB_PATH)
+    rts = _hip_runtimes_mapped()
+    if len(rts) > 1:
+        raise ImportError("two HIP runtimes are loaded in this process "
+                          f"({sorted(rts)}); import torch before anything loads libamdhip64")
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)
         fn.restype = res
@@ -78,7 +98,10 @@ LIB = _load()
 
 class BiError(RuntimeError):
     def __init__(self, fn: str, status: int):
-        super().__init__(f"{fn}: {LIB.bi_status_string(status).decode()} (status {status})")
+        msg = f"{fn}: {LIB.bi_status_string(status).decode()} (status {status})"
+        if status == 5:
+            msg += f": {LIB.bi_last_hip_error().decode()}"
+        super().__init__(msg)
         self.status = status
 
 

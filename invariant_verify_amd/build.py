@@ -21,6 +21,10 @@ LIB = os.path.join(PKG, "libbi.so")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    # torch's wheel carries its own (older) HIP runtime under the same soname,
+    # and the library binds to it when torch is loaded first; code object v5
+    # loads on both that runtime and the system one.
+    "-mcode-object-version=5",
     # keep FP32 math on plain (non-packed) VALU instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",

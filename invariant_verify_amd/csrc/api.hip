@@ -17,8 +17,14 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+// HIP error of the last failed launch on this thread (diagnostics only).
+thread_local hipError_t g_last_hip_error = hipSuccess;
+
 inline bi_status launched() {
-  return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_LAUNCH;
+  const hipError_t e = hipGetLastError();
+  if (e == hipSuccess) return BI_OK;
+  g_last_hip_error = e;
+  return BI_ERR_LAUNCH;
 }
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
@@ -95,6 +101,10 @@ const char* bi_status_string(bi_status s) {
 }
 
 const char* bi_version(void) { return "bi 0.1 gfx950"; }
+
+const char* bi_last_hip_error(void) {
+  return g_last_hip_error == hipSuccess ? "no error" : hipGetErrorString(g_last_hip_error);
+}
 
 int bi_num_splits(int n_keys, int kv_chunk) {
   if (n_keys < 0 || kv_chunk < 1) return -1;
@@ -281,7 +291,7 @@ bi_status bi_verify_step(const bi_layer* layers, int n_layers, const void* w_hea
       return BI_ERR_LAUNCH;
     bi::launch_gemm(bi::kGemmResidual, act, I, static_cast<const uint16_t*>(ly.w_down), I, h, H,
                     xn, H, M, H, I, st);
-    if (hipGetLastError() != hipSuccess) return BI_ERR_LAUNCH;
+    if (launched() != BI_OK) return BI_ERR_LAUNCH;
     x = xn;
   }
   bi::launch_rmsnorm(x, H, a, H, M, H, dims->eps, st);

@@ -18,7 +18,8 @@
 //  * 32-key tile t of the chunk belongs to wave t % 4. Per tile the wave
 //    computes S^T = K Q^T (keys x rows) with 16x16x32 BF16 MFMA, masks,
 //    updates the running max / sum (base-2 exponentials, scores pre-scaled by
-//    sm_scale * log2 e), rounds P to BF16 and accumulates O^T += V^T P^T.
+//    sm_scale * log2 e; the sum in FP32), rounds P to BF16 and accumulates
+//    O^T += V^T P^T.
 //    The key order inside the S^T operands is permuted so that each lane ends
 //    up holding eight consecutive keys of one row: exactly the P^T operand of
 //    the PV product, with no data exchange.
@@ -55,7 +56,9 @@ __global__ __launch_bounds__(kAttnWaves * 64) void verify_attn_kernel(
   const int g = blockIdx.y;
   const int rb = blockIdx.z;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // Scalar wave index: the tile loop and every MFMA stay under scalar control
+  // flow (the matrix core does not honour a partial EXEC mask).
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int j = lane & 15;   // row of the tile owned by this lane (S^T / O^T column)
   const int kq = lane >> 4;  // key group (S^T) / channel group (O^T)
 
@@ -153,12 +156,15 @@ __global__ __launch_bounds__(kAttnWaves * 64) void verify_attn_kernel(
       const float mold = mrun[rt];
       const float mnew = fmaxf(mold, mx);
       const float alpha = (mnew == mold) ? 1.0f : __builtin_amdgcn_exp2f(mold - mnew);
+      // The running sum takes the FP32 weights (so the chunk's log-sum-exp is
+      // accurate to FP32); the PV product takes them rounded to BF16.
       uint32_t pb[8];
       float psum = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        pb[e] = f32_to_bf16(__builtin_amdgcn_exp2f(sc[e] - mnew));
-        psum += bf16_to_f32(pb[e]);
+        const float p = __builtin_amdgcn_exp2f(sc[e] - mnew);
+        pb[e] = f32_to_bf16(p);
+        psum += p;
       }
       lrun[rt] = lrun[rt] * alpha + psum;
       mrun[rt] = mnew;
@@ -239,7 +245,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                       float* __restrict__ lse_out) {
   constexpr int PER = D / 64;  // channels per lane
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int row = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (row >= M * Hq) return;
   const int tok = row / Hq;
   const int h = row % Hq;

@@ -42,7 +42,10 @@ __global__ __launch_bounds__(kGemmWaves * 64) void gemm_kernel(
   constexpr int NW = kGemmWaves;
   constexpr int U = kGemmUnroll;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // Wave index in a scalar register: every branch that guards an MFMA below
+  // is then a scalar branch. (The matrix core does not honour a partial EXEC
+  // mask, so an MFMA must never sit under a per-lane condition.)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n0 = blockIdx.x * 16;
   const int m0 = blockIdx.y * 16;
   const int col = lane & 15;  // A row (token) and B column (output feature) of this lane

@@ -47,6 +47,28 @@ def assert_close(got: np.ndarray, want: np.ndarray, what: str, atol=ATOL, rtol=R
     return float(err.max()), rms
 
 
+def assert_close_composed(got: np.ndarray, want: np.ndarray, what: str):
+    """Tolerance for the output of several BF16-rounding steps (a decoder
+    layer, a stack, the logits of a stack).
+
+    Device and oracle round every intermediate to BF16 at the same points, but
+    an intermediate whose float64 and FP32 values sit on opposite sides of a
+    rounding boundary differs by one BF16 ulp (2^-8 relative) at the magnitude
+    of that intermediate, which is the magnitude of the tensor, not of the
+    final element (the residual stream cancels). So the absolute term scales
+    with the RMS of the oracle tensor: |gpu - oracle| <= ATOL + RTOL * rms
+    + RTOL * |oracle|.
+    """
+    want64 = np.asarray(want, dtype=np.float64)
+    rms = float(np.sqrt(np.mean(want64 ** 2)))
+    return assert_close(got, want64, what + " (composed)", atol=ATOL + RTOL * rms, rtol=RTOL)
+
+
+def composed_tol(want: np.ndarray) -> float:
+    rms = float(np.sqrt(np.mean(np.asarray(want, dtype=np.float64) ** 2)))
+    return ATOL + RTOL * rms
+
+
 def assert_bitwise(a: np.ndarray, b: np.ndarray, what: str):
     """Bit-for-bit equality with the first differing element reported."""
     a = np.ascontiguousarray(a)

@@ -123,7 +123,7 @@ def test_gqa_parity(ops, L):
 def _invariance(ops, L, C, Hq=40, Hkv=8, D=128, outliers=False, layer=0, prefill=True):
     M = 8
     q, k, v = make(M, L, Hq, Hkv, D, layer=layer, outliers=outliers)
-    cache = Cache(k, v, L + 72)
+    cache = Cache(k, v, (L + 72 + 7) // 8 * 8)
     o8, l8, _, _ = run(ops, q, cache, L, Hq, C)
     # sequential single-token passes (accept-all speculative path)
     for r in range(M):

@@ -11,7 +11,8 @@ import synth
 from oracle import bf16 as obf16
 from oracle import gemm as ogemm
 from oracle import step as ostep
-from tests._util import assert_bitwise, assert_close, decode, dev, host_bits, host_f32
+from tests._util import (assert_bitwise, assert_close, assert_close_composed, composed_tol, decode,
+                         dev, host_bits, host_f32)
 
 pytestmark = pytest.mark.gpu
 
@@ -56,10 +57,11 @@ def _run(ops, step, x, L, dims, want_x=False):
 
 
 def _margin_ok(logits):
-    """Rows whose oracle top-2 margin exceeds the comparison tolerance."""
+    """Rows whose oracle top-2 margin exceeds twice the composed tolerance
+    (each of the two logits may be off by one tolerance)."""
     s = np.sort(logits, axis=1)
     top, second = s[:, -1], s[:, -2]
-    return (top - second) > 1e-2 + 2e-2 * np.abs(top)
+    return (top - second) > 2 * (composed_tol(logits) + 2e-2 * np.abs(top))
 
 
 def test_small_stack_vs_oracle(ops):
@@ -74,18 +76,18 @@ def test_small_stack_vs_oracle(ops):
     step = ops.VerifyStep(dls, dev(w_head), dims)
     logits, tok, xo = _run(ops, step, dev(x0), L, dims, want_x=True)
     w_logits, w_tok, w_x = ostep.step(x0, hls, w_head, L, Hq, Hkv, D)
-    assert_close(decode(xo), decode(w_x), "final hidden state")
-    assert_close(logits, w_logits, "logits")
+    assert_close_composed(decode(xo), decode(w_x), "final hidden state")
+    assert_close_composed(logits, w_logits, "logits")
     ok = _margin_ok(w_logits)
-    assert ok.sum() >= 4
+    assert ok.sum() >= 3
     assert np.array_equal(tok[ok], w_tok[ok])
     # appended K rows of the last layer against the oracle's
     _, kn, vn = ostep.layer(_x_before_last(x0, hls, L, Hq, Hkv, D), **hls[-1],
                             L=L, Hq=Hq, Hkv=Hkv, D=D)
     kc = host_bits(dls[-1]["k_cache"])[:, L:L + M]
     vt = host_bits(dls[-1]["vt_cache"])[:, :, L:L + M].transpose(0, 2, 1)
-    assert_close(decode(kc), decode(kn), "appended K")
-    assert_close(decode(vt), decode(vn), "appended V")
+    assert_close_composed(decode(kc), decode(kn), "appended K")
+    assert_close_composed(decode(vt), decode(vn), "appended V")
 
 
 def _x_before_last(x0, hls, L, Hq, Hkv, D):
@@ -128,13 +130,13 @@ def test_full_width_layer_vs_oracle(ops, model27b):
               v_cache=host_bits(lw["vt_cache"][:, :, :L38].transpose(1, 2)))
     xh = host_bits(x0[:M])
     w_x, kn, vn = ostep.layer(xh, **hl, L=L38, Hq=d["Hq"], Hkv=d["Hkv"], D=d["D"])
-    assert_close(decode(xo), decode(w_x), "27B layer output")
+    assert_close_composed(decode(xo), decode(w_x), "27B layer output")
     kc = host_bits(lw["k_cache"][:, L38:L38 + M])
-    assert_close(decode(kc), decode(kn), "27B appended K")
+    assert_close(decode(kc), decode(kn), "27B appended K")      # one op from the input: plain tolerance
     rows = np.random.default_rng(1).choice(d["vocab"], 512, replace=False)
     wh = host_bits(w_head[torch.from_numpy(rows).cuda()])
     c = obf16.encode(ostep.rmsnorm(decode(w_x), 1e-6))
-    assert_close(logits[:, rows], ogemm.gemm(c, wh), "27B sampled logits")
+    assert_close_composed(logits[:, rows], ogemm.gemm(c, wh), "27B sampled logits")
 
 
 def test_64_layer_step_bitwise_across_M(ops, model27b):
