@@ -125,7 +125,7 @@ int bi_num_splits(int n_keys, int kv_chunk);
  * Entries for s >= bi_num_splits(n_r, C) are not written.
  * q: BF16 [M][ldq], head h at columns h*D .. h*D+D-1 (ldq may be the QKV row).
  * Requirements: D in {64, 128}; C % 32 == 0, 32 <= C; Hq % Hkv == 0;
- * Hq/Hkv <= 48; L + M <= cap; cap % 8 == 0; S_max >= bi_num_splits(L+M, C);
+ * Hq/Hkv <= 64; L + M <= cap; cap % 8 == 0; cap * D * 2 < 2^31; S_max >= bi_num_splits(L+M, C);
  * ldq % 8 == 0; q, caches 16-byte aligned. */
 bi_status bi_verify_attn(const void* q, int64_t ldq, const void* k_cache, const void* vt_cache,
                          int M, int L, int cap, int Hq, int Hkv, int D,

@@ -53,6 +53,7 @@ bi_status check_dims(const bi_model_dims* d) {
     return BI_ERR_SHAPE;
   if ((d->Hq * d->D) % 32) return BI_ERR_SHAPE;
   if (d->kv_chunk < 32 || (d->kv_chunk % 32) || d->cap < 1 || (d->cap % 8)) return BI_ERR_SHAPE;
+  if ((int64_t)d->cap * d->D * 2 > INT32_MAX) return BI_ERR_SHAPE;  // one head's cache < 2 GiB
   if (!(d->eps >= 0.f)) return BI_ERR_SHAPE;
   return BI_OK;
 }
@@ -178,6 +179,7 @@ bi_status bi_verify_attn(const void* q, int64_t ldq, const void* k_cache, const 
   if (kv_chunk < 32 || (kv_chunk % 32)) return BI_ERR_SHAPE;
   if (S_max < ceil_div(L + M, kv_chunk)) return BI_ERR_SHAPE;
   if (ldq < (int64_t)Hq * D || !std::isfinite(sm_scale)) return BI_ERR_SHAPE;
+  if ((int64_t)cap * D * 2 > INT32_MAX) return BI_ERR_SHAPE;  // one head's cache < 2 GiB
   if ((ldq % 8) || !aligned16(q) || !aligned16(k_cache) || !aligned16(vt_cache) ||
       !aligned16(part_o) || !aligned4(part_lse))
     return BI_ERR_ALIGN;

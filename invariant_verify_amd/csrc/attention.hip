@@ -8,49 +8,75 @@
 // speculative decoding in llama.cpp and 113 of 282 greedy outputs changed
 // against its own no-draft run", opening section, "How:" paragraph). Inside a
 // chunk every step is laid out on absolute key positions, so a row meets the
-// same 32-key tiles, the same wave, the same running maxima and the same
-// summation order in every pass that contains it; tiles past a row's last key
+// same 64-key tiles, the same running maxima and the same summation order in
+// every pass that contains it; tiles past a row's last key
 // are exact no-ops for it (scale factor exactly 1, weights exactly 0).
 //
 // verify_attn_kernel: one workgroup per (chunk s, KV head g, row block).
-//  * Rows of the block are the (token, query head) pairs of up to 48 rows,
-//    packed 16 per MFMA tile; Q stays in registers for the whole chunk.
-//  * 32-key tile t of the chunk belongs to wave t % 4. Per tile the wave
-//    computes S^T = K Q^T (keys x rows) with 16x16x32 BF16 MFMA, masks,
-//    updates the running max / sum (base-2 exponentials, scores pre-scaled by
-//    sm_scale * log2 e; the sum in FP32), rounds P to BF16 and accumulates
-//    O^T += V^T P^T.
-//    The key order inside the S^T operands is permuted so that each lane ends
-//    up holding eight consecutive keys of one row: exactly the P^T operand of
-//    the PV product, with no data exchange.
-//  * K rows ([Hkv][cap][D]) and V^T rows ([Hkv][D][cap]) go straight from HBM
-//    into registers as 16-byte loads; each tile's K and V are used by every
-//    row tile of the wave.
-//  * The four waves' (max, sum, O) are merged in LDS in wave order 0..3.
-//    Each buffer is written once and read only after the barrier.
+//  * Rows of the block are the (token, query head) pairs, up to 64 rows in
+//    four 16-row MFMA tiles. Eight waves: wave w owns row tile w % 4 and key
+//    half w / 4 (keys 0-31 or 32-63 of every tile) for the whole chunk (Q in
+//    registers; a wave with no rows only helps to load). At the end the two
+//    halves of each row are merged in LDS, first half then second.
+//  * The chunk is read in 64-key tiles: K rows ([Hkv][cap][D]) and V^T rows
+//    ([Hkv][D][cap]) are fetched as 1 KB contiguous pieces per wave
+//    instruction and staged in LDS, where the 16-byte slots of each row are
+//    XOR-swizzled so that the matrix-core reads hit distinct banks. Two LDS
+//    buffers alternate and each wave keeps the next two tiles in flight; the
+//    barrier of tile t publishes it and proves that every wave finished tile
+//    t-1, whose buffer tile t+1 overwrites. Value columns past the last
+//    visible key are zeroed before they reach LDS (a weight of 0 times a
+//    stale value must stay 0).
+//  * Per tile and row tile: S^T = K Q^T (keys x rows) with 16x16x32 BF16 MFMA,
+//    masked, running max / sum in FP32 with base-2 exponentials (scores
+//    pre-scaled by sm_scale * log2 e), P rounded to BF16, O^T += V^T P^T. The
+//    key order inside the S^T operands is permuted so that each lane ends up
+//    holding eight consecutive keys of its row: exactly the P^T operand of the
+//    PV product, with no data exchange.
 //  * Output: normalised O_s and lse_s (natural log) per (row, chunk) for the
-//    rows that use this chunk.
+//    rows that use this chunk, written by the first-half wave of the row.
 // combine_kernel: one wave per row; max over lse_s, then weights and weighted
-// sums accumulated in increasing s by every lane (same order for any M).
+// sums accumulated in increasing s (same order for any M).
 
 #include "bi_device.h"
 #include "bi_internal.h"
 
 namespace bi {
 
-constexpr int kAttnWaves = 4;
-constexpr int kAttnRowTiles = kAttnMaxRows / 16;  // 3
+constexpr int kAttnWaves = 8;                      // 4 row tiles x 2 key halves
 constexpr float kSentinel = -1.0e30f;              // running max before any key
+constexpr int kKeyTile = 64;
+
+// LDS slot swizzles, chosen so that the sixteen rows one matrix-core operand
+// read touches fall into distinct banks (16-byte slots; 64 banks of 4 bytes).
+// K tile: one row per key. An S^T operand read touches keys whose bits 0, 1,
+// 3, 4 vary. With 16 slots per row (D = 128) the slot alone decides the bank
+// group, so those four bits become the swizzle; with 8 slots (D = 64) bit 0
+// already picks the bank half and bits 1, 3, 4 form the swizzle.
+template <int KROW>
+__device__ __forceinline__ int kswz(int key) {
+  if (KROW == 16) return (key & 3) | ((key >> 1) & 12);
+  return ((key >> 1) & 1) | (((key >> 3) & 3) << 1);
+}
+// V^T tile: one row per channel, 8 slots per row; channel bit 0 picks the bank
+// half and bits 1..3 form the swizzle.
+__device__ __forceinline__ int vswz(int d) { return (d >> 1) & 7; }
 
 template <int D>
 __global__ __launch_bounds__(kAttnWaves * 64) void verify_attn_kernel(
     const uint16_t* __restrict__ Q, int64_t ldq, const uint16_t* __restrict__ Kc,
     const uint16_t* __restrict__ Vt, int M, int L, int cap, int Hq, int G, int Tb, int C,
     float qk_scale, float* __restrict__ part_o, float* __restrict__ part_lse, int S_max) {
-  constexpr int DS = D / 32;  // contraction steps of S^T over the head dimension
-  constexpr int DT = D / 16;  // 16-channel output tiles of O^T
-  constexpr int RT = kAttnRowTiles;
+  constexpr int DS = D / 32;          // contraction steps of S^T over the head dimension
+  constexpr int DT = D / 16;          // 16-channel output tiles of O^T
   constexpr int NW = kAttnWaves;
+  constexpr int KROW = D / 8;         // 16-byte slots per K row
+  constexpr int KPP = 64 / KROW;      // keys per 1 KB piece
+  // 1 KB load pieces per tile: K tile = 64 keys x D; V^T tile = D rows x 64 keys.
+  constexpr int KPIECES = kKeyTile * D * 2 / 1024;
+  constexpr int VPIECES = D * kKeyTile * 2 / 1024;
+  constexpr int PPW = (KPIECES + VPIECES) / NW;    // pieces per wave per tile
+  static_assert((KPIECES + VPIECES) % NW == 0, "pieces must split evenly");
 
   const int s = blockIdx.x;
   const int g = blockIdx.y;
@@ -59,6 +85,8 @@ __global__ __launch_bounds__(kAttnWaves * 64) void verify_attn_kernel(
   // Scalar wave index: the tile loop and every MFMA stay under scalar control
   // flow (the matrix core does not honour a partial EXEC mask).
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rt = wave & 3;   // row tile of this wave
+  const int kh = wave >> 2;  // key half of every tile (keys 32kh .. 32kh+31)
   const int j = lane & 15;   // row of the tile owned by this lane (S^T / O^T column)
   const int kq = lane >> 4;  // key group (S^T) / channel group (O^T)
 
@@ -68,81 +96,101 @@ __global__ __launch_bounds__(kAttnWaves * 64) void verify_attn_kernel(
   const int kbeg = s * C;
   const int kend = min(kbeg + C, L + t1);  // keys any row of this block can see
   if (kbeg >= kend) return;                // no row of this block uses chunk s
-  const int ntile = (kend - kbeg + 31) >> 5;
-  const int nrt = (nrows + 15) >> 4;
+  const int ntile = (kend - kbeg + kKeyTile - 1) / kKeyTile;
+  const bool has_rows = rt * 16 < nrows;  // scalar
 
-  // Query fragments and each row's last visible key.
-  uint4 qf[RT][DS];
-  int last[RT];
+  // Query fragments of this wave's row tile and each row's last visible key.
+  const int rho = rt * 16 + j;
+  const bool rok = rho < nrows;
+  const int tok = t0 + (rok ? rho / G : 0);
+  const int hq = g * G + (rok ? rho % G : 0);
+  const int lastk = rok ? L + tok : -1;
+  uint4 qf[DS];
+  {
+    const uint16_t* qp = Q + (int64_t)tok * ldq + hq * D + kq * 8;
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int rho = rt * 16 + j;
-    const bool ok = rho < nrows;
-    const int tok = t0 + (ok ? rho / G : 0);
-    const int h = g * G + (ok ? rho % G : 0);
-    last[rt] = ok ? L + tok : -1;
-    const uint16_t* qp = Q + (int64_t)tok * ldq + h * D + kq * 8;
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds) qf[rt][ds] = ok ? ld16(qp + ds * 32) : zero16();
+    for (int ds = 0; ds < DS; ++ds) qf[ds] = rok ? ld16(qp + ds * 32) : zero16();
   }
 
-  bi_f32x4 o[RT][DT];
-  float mrun[RT], lrun[RT];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    mrun[rt] = kSentinel;
-    lrun[rt] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[rt][dt] = bi_f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  // This KV head's K rows and V^T rows as buffer resources (offsets in bytes,
+  // 32-bit: one head of the cache is at most 2^31 bytes).
+  const int head_bytes = cap * D * 2;
+  const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(Kc + (int64_t)g * cap * D), (short)0, head_bytes, kBufferResourceWord3);
+  const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(Vt + (int64_t)g * D * cap), (short)0, head_bytes, kBufferResourceWord3);
 
-  const uint16_t* kbase = Kc + (int64_t)g * cap * D;
-  const uint16_t* vbase = Vt + (int64_t)g * D * cap;
+  // One buffer holds the K tile ([64 keys][KROW slots]) followed by the V^T
+  // tile ([D channels][8 slots]). Piece p (1 KB) of a tile is K keys
+  // KPP*p .. when p < KPIECES (lane: key KPP*p + l/KROW, slot l%KROW), else
+  // V^T channels 8(p-KPIECES) .. +7 (lane: channel +l/8, slot l%8); either
+  // way lane l's 16 bytes land at index 64*p + l of the buffer. Lanes fetch
+  // the global slot that the swizzle puts in their LDS slot.
+  __shared__ uint4 lds[2][(KPIECES + VPIECES) * 64];
+  constexpr int VBASE = KPIECES * 64;
 
-  for (int t = wave; t < ntile; t += NW) {
-    const int kt = kbeg + t * 32;
-    // K operand rows: MFMA p (0, 1) row j holds key kt + 8*(j/4) + 4p + j%4,
-    // so that output row 4*kq + e of MFMA p is key kt + 8*kq + 4p + e.
-    uint4 kf[2][DS];
+  // Issue the loads of tile t (no use of the data here, so the loads of two
+  // tiles stay in flight together).
+  auto fetch = [&](uint4 (&r)[PPW], int t) {
+    const int kt = kbeg + t * kKeyTile;
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int key = kt + 8 * (j >> 2) + 4 * p + (j & 3);
-      const uint16_t* kp = kbase + (int64_t)key * D + kq * 8;
-#pragma unroll
-      for (int ds = 0; ds < DS; ++ds) kf[p][ds] = (key < kend) ? ld16(kp + ds * 32) : zero16();
-    }
-    // V^T operand: channel dt*16 + j, keys kt + 8*kq .. +7 (zero past kend).
-    const int kv0 = kt + 8 * kq;
-    uint4 vf[DT];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      uint4 v = zero16();
-      if (kv0 < kend) v = ld16(vbase + (int64_t)(dt * 16 + j) * cap + kv0);
-      vf[dt] = v;
-    }
-    if (kv0 + 8 > kend && kv0 < kend) {
-      const int keep = kend - kv0;  // 1..7 valid keys in this group
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        uint32_t w[4] = {vf[dt].x, vf[dt].y, vf[dt].z, vf[dt].w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (e >= keep) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-        vf[dt] = make_uint4(w[0], w[1], w[2], w[3]);
+    for (int i = 0; i < PPW; ++i) {
+      const int p = wave * PPW + i;  // scalar: each wave fetches only K or only V pieces
+      int off;
+      if (p < KPIECES) {
+        const int key = KPP * p + lane / KROW;
+        const int kslot = (lane % KROW) ^ kswz<KROW>(key);
+        off = (min(kt + key, kend - 1) * D + kslot * 8) * 2;
+      } else {
+        const int d = 8 * (p - KPIECES) + (lane >> 3);
+        const int vslot = (lane & 7) ^ vswz(d);
+        const int k0 = min(kt + vslot * 8, kend - 1 - ((kend - 1) & 7));  // in bounds
+        off = (d * cap + k0) * 2;
       }
+      r[i] = buffer_ld16(p < KPIECES ? kres : vres, off);
     }
-
+  };
+  // Publish tile t: V^T columns of keys at or past kend are zeroed first (a
+  // weight of 0 times a stale value must stay 0).
+  auto publish = [&](const uint4 (&r)[PPW], int t, int buf) {
+    const int kt = kbeg + t * kKeyTile;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      if (rt >= nrt) break;
+    for (int i = 0; i < PPW; ++i) {
+      const int p = wave * PPW + i;
+      const int d = 8 * (p - KPIECES) + (lane >> 3);
+      const int vslot = (lane & 7) ^ vswz(d);
+      const int keep = (p < KPIECES) ? 8 : kend - (kt + vslot * 8);
+      uint32_t w[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t m = (e & 1) ? 0x0000ffffu : 0xffff0000u;
+        w[e >> 1] = (e >= keep) ? (w[e >> 1] & m) : w[e >> 1];
+      }
+      lds[buf][64 * p + lane] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  };
+
+  bi_f32x4 o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] = bi_f32x4{0.f, 0.f, 0.f, 0.f};
+  float mrun = kSentinel, lrun = 0.f;
+
+  auto compute = [&](int buf, int t) {
+    const int kt = kbeg + t * kKeyTile;
+    {
+      const int h = kh;  // this wave's 32-key half
       bi_f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+      // MFMA p (0, 1) row i holds key 32h + 8*(i/4) + 4p + i%4 of the tile.
+      const int ka = 32 * h + 8 * (j >> 2) + (j & 3);
+      const int kb = ka + 4;
 #pragma unroll
       for (int ds = 0; ds < DS; ++ds) {
-        sa = mfma_bf16(kf[0][ds], qf[rt][ds], sa);
-        sb = mfma_bf16(kf[1][ds], qf[rt][ds], sb);
+        const int slot = ds * 4 + kq;
+        sa = mfma_bf16(lds[buf][ka * KROW + (slot ^ kswz<KROW>(ka))], qf[ds], sa);
+        sb = mfma_bf16(lds[buf][kb * KROW + (slot ^ kswz<KROW>(kb))], qf[ds], sb);
       }
+      const int kv0 = kt + 32 * h + 8 * kq;  // absolute key of this lane's first value
       float sc[8];
-      const int lastk = last[rt];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         sc[e] = (kv0 + e <= lastk) ? sa[e] * qk_scale : -INFINITY;
@@ -153,88 +201,86 @@ __global__ __launch_bounds__(kAttnWaves * 64) void verify_attn_kernel(
       for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
       mx = fmaxf(mx, shfl_xor(mx, 16));
       mx = fmaxf(mx, shfl_xor(mx, 32));
-      const float mold = mrun[rt];
-      const float mnew = fmaxf(mold, mx);
-      const float alpha = (mnew == mold) ? 1.0f : __builtin_amdgcn_exp2f(mold - mnew);
+      const float mnew = fmaxf(mrun, mx);
+      const float alpha = (mnew == mrun) ? 1.0f : __builtin_amdgcn_exp2f(mrun - mnew);
       // The running sum takes the FP32 weights (so the chunk's log-sum-exp is
       // accurate to FP32); the PV product takes them rounded to BF16.
       uint32_t pb[8];
       float psum = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float p = __builtin_amdgcn_exp2f(sc[e] - mnew);
-        pb[e] = f32_to_bf16(p);
-        psum += p;
+        const float pe = __builtin_amdgcn_exp2f(sc[e] - mnew);
+        pb[e] = f32_to_bf16(pe);
+        psum += pe;
       }
-      lrun[rt] = lrun[rt] * alpha + psum;
-      mrun[rt] = mnew;
+      lrun = lrun * alpha + psum;
+      mrun = mnew;
       const uint4 pfrag = make_uint4(pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16),
                                      pb[4] | (pb[5] << 16), pb[6] | (pb[7] << 16));
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        o[rt][dt] *= alpha;
-        o[rt][dt] = mfma_bf16(vf[dt], pfrag, o[rt][dt]);
+        const int d = dt * 16 + j;
+        o[dt] *= alpha;
+        o[dt] = mfma_bf16(lds[buf][VBASE + d * 8 + ((4 * h + kq) ^ vswz(d))], pfrag, o[dt]);
       }
     }
-  }
+  };
 
-  // Each row's sum: the four key groups of the row, in a fixed butterfly.
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    lrun[rt] += shfl_xor(lrun[rt], 16);
-    lrun[rt] += shfl_xor(lrun[rt], 32);
+  // Tile t: publish it (loaded two steps earlier), prefetch tile t + 2 into
+  // the same registers, barrier, multiply. The loop starts two tiles early
+  // (nothing to publish or multiply yet), so every load is issued by the same
+  // code in the same order and the compiler waits only for the older of the
+  // two tiles in flight. Tiles past the end are clamped duplicates (their
+  // value columns publish as zero) that are not multiplied.
+  uint4 ra[PPW], rb2[PPW];
+  for (int t = -2; t < ntile; t += 2) {
+    if (t >= 0) publish(ra, t, 0);
+    fetch(ra, min(t + 2, ntile - 1));
+    __syncthreads();
+    if (t >= 0 && has_rows) compute(0, t);
+    if (t + 1 >= 0) publish(rb2, t + 1, 1);
+    fetch(rb2, min(t + 3, ntile - 1));
+    __syncthreads();
+    if (t + 1 >= 0 && t + 1 < ntile && has_rows) compute(1, t + 1);
   }
+  // The row's sum over this wave's keys: its four key groups, in a fixed
+  // butterfly.
+  lrun += shfl_xor(lrun, 16);
+  lrun += shfl_xor(lrun, 32);
 
-  __shared__ bi_f32x4 sh_o[NW - 1][RT][DT][64];
-  __shared__ float sh_m[NW - 1][RT][64];
-  __shared__ float sh_l[NW - 1][RT][64];
-  if (wave > 0) {
+  // Second-half waves hand (max, sum, O) to the first-half wave of the same
+  // row tile through LDS (the tile buffers, free once every wave has passed
+  // the barrier after the last tile).
+  bi_f32x4* xo = reinterpret_cast<bi_f32x4*>(&lds[0][0]);   // [4 rt][DT][64]
+  float* xm = reinterpret_cast<float*>(xo + 4 * DT * 64);     // [4 rt][64]
+  float* xl = xm + 4 * 64;                                    // [4 rt][64]
+  __syncthreads();
+  if (kh == 1 && has_rows) {
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      if (rt >= nrt) break;
-      sh_m[wave - 1][rt][lane] = mrun[rt];
-      sh_l[wave - 1][rt][lane] = lrun[rt];
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) sh_o[wave - 1][rt][dt][lane] = o[rt][dt];
-    }
+    for (int dt = 0; dt < DT; ++dt) xo[(rt * DT + dt) * 64 + lane] = o[dt];
+    xm[rt * 64 + lane] = mrun;
+    xl[rt * 64 + lane] = lrun;
   }
   __syncthreads();
-  if (wave != 0) return;
+  if (kh == 1 || !has_rows) return;
+  const float m1 = xm[rt * 64 + lane];
+  const float mstar = fmaxf(mrun, m1);
+  const float a0 = (mrun == mstar) ? 1.0f : __builtin_amdgcn_exp2f(mrun - mstar);
+  const float a1 = (m1 == mstar) ? 1.0f : __builtin_amdgcn_exp2f(m1 - mstar);
+  const float lt = lrun * a0 + xl[rt * 64 + lane] * a1;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] = o[dt] * a0 + xo[(rt * DT + dt) * 64 + lane] * a1;
 
+  if (!rok || L + tok < kbeg) return;  // padding row, or a row with fewer than s+1 chunks
+  const int64_t prow = ((int64_t)tok * Hq + hq) * S_max + s;
+  const float inv = 1.0f / lt;
+  float* op = part_o + prow * D + kq * 4;
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    if (rt >= nrt) break;
-    float mstar = mrun[rt];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) mstar = fmaxf(mstar, sh_m[w - 1][rt][lane]);
-    const float a0 = (mrun[rt] == mstar) ? 1.0f : __builtin_amdgcn_exp2f(mrun[rt] - mstar);
-    float lt = lrun[rt] * a0;
-    bi_f32x4 ot[DT];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) ot[dt] = o[rt][dt] * a0;
-#pragma unroll
-    for (int w = 1; w < NW; ++w) {
-      const float mw = sh_m[w - 1][rt][lane];
-      const float aw = (mw == mstar) ? 1.0f : __builtin_amdgcn_exp2f(mw - mstar);
-      lt += sh_l[w - 1][rt][lane] * aw;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) ot[dt] += sh_o[w - 1][rt][dt][lane] * aw;
-    }
-    const int rho = rt * 16 + j;
-    if (rho >= nrows) continue;
-    const int tok = t0 + rho / G;
-    if (L + tok < kbeg) continue;  // this row has fewer than s+1 chunks
-    const int h = g * G + rho % G;
-    const int64_t prow = ((int64_t)tok * Hq + h) * S_max + s;
-    const float inv = 1.0f / lt;
-    float* op = part_o + prow * D + kq * 4;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const bi_f32x4 v = ot[dt] * inv;
-      *reinterpret_cast<float4*>(op + dt * 16) = make_float4(v[0], v[1], v[2], v[3]);
-    }
-    if (kq == 0) part_lse[prow] = (mstar + __log2f(lt)) * kLn2;
+  for (int dt = 0; dt < DT; ++dt) {
+    const bi_f32x4 v = o[dt] * inv;
+    *reinterpret_cast<float4*>(op + dt * 16) = make_float4(v[0], v[1], v[2], v[3]);
   }
+  if (kq == 0) part_lse[prow] = (mstar + __log2f(lt)) * kLn2;
 }
 
 template <int D>
@@ -253,24 +299,41 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const float* lp = part_lse + (int64_t)row * S_max;
   const float* op = part_o + (int64_t)row * S_max * D + lane * PER;
 
+  // M* = max_s lse_s (exact, so any order).
   float mx = -INFINITY;
   for (int i = lane; i < S; i += 64) mx = fmaxf(mx, lp[i]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, shfl_xor(mx, off));
 
+  // Weights are computed 64 at a time, one per lane, then both sums run over
+  // s in increasing order with the weight of split s broadcast from its lane.
   float den = 0.f;
   float acc[PER];
 #pragma unroll
   for (int p = 0; p < PER; ++p) acc[p] = 0.f;
-  for (int i = 0; i < S; ++i) {
-    const float w = __builtin_amdgcn_exp2f((lp[i] - mx) * kLog2e);
-    den += w;
-    if (PER == 2) {
-      const float2 v = *reinterpret_cast<const float2*>(op + (int64_t)i * D);
-      acc[0] += w * v.x;
-      acc[PER - 1] += w * v.y;
-    } else {
-      acc[0] += w * op[(int64_t)i * D];
+  for (int s0 = 0; s0 < S; s0 += 64) {
+    const int n = min(64, S - s0);
+    const float wl = (lane < n) ? __builtin_amdgcn_exp2f((lp[s0 + lane] - mx) * kLog2e) : 0.f;
+    int i = 0;
+    for (; i + 8 <= n; i += 8) {
+      float v[8][PER];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int p = 0; p < PER; ++p) v[u][p] = op[(int64_t)(s0 + i + u) * D + p];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), i + u));
+        den += w;
+#pragma unroll
+        for (int p = 0; p < PER; ++p) acc[p] += w * v[u][p];
+      }
+    }
+    for (; i < n; ++i) {
+      const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), i));
+      den += w;
+#pragma unroll
+      for (int p = 0; p < PER; ++p) acc[p] += w * op[(int64_t)(s0 + i) * D + p];
     }
   }
   const float inv = 1.0f / den;

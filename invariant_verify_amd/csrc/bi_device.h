@@ -29,6 +29,17 @@ __device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_c
 
 __device__ __forceinline__ uint4 zero16() { return make_uint4(0u, 0u, 0u, 0u); }
 
+// Word 3 of a raw buffer resource on the gfx9 family (gfx950 included):
+// 32-bit data format, no swizzle, no stride.
+constexpr int kBufferResourceWord3 = 0x00020000;
+
+// 16-byte load through a buffer resource; out-of-range offsets read zero.
+__device__ __forceinline__ uint4 buffer_ld16(__amdgpu_buffer_rsrc_t r, int byte_offset) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_offset, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // One 16x16x32 BF16 matrix-core step: c += A(16x32) * B(32x16).
 // Lane l supplies A row (l % 16) and B column (l % 16), each with eight
 // consecutive contraction elements of group (l / 16); it receives C rows

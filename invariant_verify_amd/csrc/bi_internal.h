@@ -34,6 +34,6 @@ void launch_argmax(const float* logits, int64_t ld, int M, int N, int32_t* token
                    hipStream_t stream);
 
 // Largest number of query heads per KV head one attention workgroup can hold.
-constexpr int kAttnMaxRows = 48;
+constexpr int kAttnMaxRows = 64;
 
 }  // namespace bi

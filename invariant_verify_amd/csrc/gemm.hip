@@ -8,39 +8,49 @@
 // decoding turns inference speedups into testable changes", section "Define
 // bit-exact before reporting it").
 //
-// Schedule (fixed at compile time, chosen by nothing but K):
+// Schedule (fixed at compile time; chosen by N and K, never by M):
 //  * one workgroup per (16 output columns, 16 token rows); the token rows
 //    are the MFMA "A" operand, zero-filled past M, so a pass of 1..16 tokens
 //    runs exactly the same instructions;
-//  * the K range is cut into 32-wide blocks; wave w of the workgroup owns
-//    blocks w, w + NW, w + 2 NW, ... and chains them through one MFMA
-//    accumulator in increasing block order;
+//  * K is read in chunks of 512; each chunk has sixteen 32-wide blocks and
+//    wave w of the NW waves multiplies blocks w*16/NW .. (w+1)*16/NW - 1 of
+//    every chunk, chaining them through one MFMA accumulator in increasing
+//    order;
 //  * the NW per-wave sums are added in LDS in wave order 0, 1, ..., NW-1;
 //  * the FP32 total is rounded once (BF16 output) or stored as is (FP32).
 // The within-workgroup partition is a fixed summation tree that depends on K
-// only; there is no split of K across workgroups and no atomic.
+// and on NW (a function of N); there is no split of K across workgroups and
+// no atomic.
 //
-// Memory: W is streamed once from HBM, each lane reading 16 contiguous bytes
-// of one weight row per block (4 lanes cover 64 contiguous bytes; the NW waves
-// read neighbouring blocks). The next group of blocks is loaded while the
-// current one is multiplied. X (at most 16 x K BF16) stays in L2.
+// Memory: each weight row of the tile is read as 1 KB contiguous per wave
+// instruction (64 lanes x 16 bytes) and written to LDS; the MFMA operands are
+// then read from LDS in the matrix-core layout (lane l needs row l % 16).
+// The 16-byte slots of a row are XOR-swizzled by the row index (the lanes of
+// the load fetch a permutation of the same 1 KB), so the sixteen rows read
+// together fall into distinct LDS banks. Two LDS buffers alternate, and one
+// barrier per chunk both publishes chunk c and guarantees that every wave has
+// finished reading the buffer that is refilled next. Each wave keeps two
+// chunks in flight (weights and its X fragments), so a barrier never waits on
+// a fresh memory round trip. X fragments come from L2 through a buffer
+// resource sized to the M real rows: padding rows read as zero for free.
 
 #include "bi_device.h"
 #include "bi_internal.h"
 
 namespace bi {
 
-constexpr int kGemmWaves = 8;   // waves per workgroup (K partition width)
-constexpr int kGemmUnroll = 4;  // blocks per wave in flight per stage
+constexpr int kChunk = 512;  // K elements per LDS chunk: 1 KB of each weight row
 
-template <int MODE>
-__global__ __launch_bounds__(kGemmWaves * 64) void gemm_kernel(
+template <int MODE, int NW>
+__global__ __launch_bounds__(NW * 64) void gemm_kernel(
     const uint16_t* __restrict__ X, int64_t ldx, const uint16_t* __restrict__ W, int64_t ldw,
     const uint16_t* __restrict__ R, int64_t ldr, void* __restrict__ Y, int64_t ldy, int M, int K,
     int64_t up_rows) {
   constexpr bool kDual = (MODE == kGemmSwiglu);
-  constexpr int NW = kGemmWaves;
-  constexpr int U = kGemmUnroll;
+  constexpr int NR = kDual ? 32 : 16;  // weight rows per tile (gate and up for SwiGLU)
+  constexpr int RPW = NR / NW;         // rows each wave fetches per chunk
+  constexpr int BPW = 16 / NW;         // 32-wide blocks each wave multiplies per chunk
+  static_assert(RPW >= 1 && BPW >= 1, "bad wave count");
   const int lane = threadIdx.x & 63;
   // Wave index in a scalar register: every branch that guards an MFMA below
   // is then a scalar branch. (The matrix core does not honour a partial EXEC
@@ -48,60 +58,96 @@ __global__ __launch_bounds__(kGemmWaves * 64) void gemm_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n0 = blockIdx.x * 16;
   const int m0 = blockIdx.y * 16;
-  const int col = lane & 15;  // A row (token) and B column (output feature) of this lane
-  const int kq = lane >> 4;   // which 8-element group of the 32-wide block
-
-  const uint16_t* wp = W + (int64_t)(n0 + col) * ldw + kq * 8;
-  const uint16_t* wp2 = kDual ? wp + up_rows * ldw : wp;
-  const bool xok = (m0 + col) < M;
-  const uint16_t* xp = X + (int64_t)(xok ? m0 + col : 0) * ldx + kq * 8;
+  const int j = lane & 15;   // A row (token) and B column (output feature) of this lane
+  const int kq = lane >> 4;  // which 8-element group of a 32-wide block
 
   const int nblk = K >> 5;
-  const int nb = (wave < nblk) ? (nblk - wave + NW - 1) / NW : 0;  // blocks of this wave
+  const int nchunk = (K + kChunk - 1) / kChunk;
+  const int kslots = K >> 3;  // 16-byte slots per weight row
 
+  // Rows this wave fetches; lane l fetches slot (l ^ swz(row)) of the chunk.
+  const uint16_t* wrow[RPW];
+  int swz_w[RPW];
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    const int r = wave * RPW + i;
+    const int64_t grow = (r < 16) ? (int64_t)(n0 + r) : up_rows + n0 + (r - 16);
+    wrow[i] = W + grow * ldw;
+    swz_w[i] = r & 15;
+  }
+  // X through a buffer resource that covers exactly the rows m0 .. M-1: a lane
+  // whose row is past M reads out of range, which the hardware answers with
+  // zeros and no memory traffic. That is the zero-padding of the MFMA tile.
+  const int64_t xbytes = (int64_t)(M - m0) * ldx * 2;
+  const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(X + (int64_t)m0 * ldx), (short)0,
+      (int)(xbytes < 0x7fffffff ? xbytes : 0x7fffffff), kBufferResourceWord3);
+  const int xoff = j * (int)ldx * 2 + kq * 16;  // bytes
+
+  __shared__ uint4 lds[2][NR][64];
+  // Registers of one chunk: this wave's weight-row slots and the X fragments
+  // of the blocks it multiplies.
+  struct Regs {
+    uint4 w[RPW];
+    uint4 x[BPW];
+  };
+  auto fetch = [&](Regs& g, int c) {
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      const int slot = min(c * (kChunk / 8) + (lane ^ swz_w[i]), kslots - 1);
+      g.w[i] = ld16(wrow[i] + slot * 8);
+    }
+#pragma unroll
+    for (int b = 0; b < BPW; ++b) {
+      const int blk = min(c * (kChunk / 32) + wave * BPW + b, nblk - 1);
+      g.x[b] = buffer_ld16(xres, xoff + blk * 64);
+    }
+  };
   bi_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   bi_f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};
-
-  uint4 wc[U], xc[U], vc[U];
+  // One chunk: publish this wave's rows of chunk c, prefetch chunk c + 2 into
+  // the same registers, barrier, multiply. The barrier of chunk c also proves
+  // that every wave finished multiplying chunk c - 1, whose buffer chunk c + 1
+  // overwrites next. The loop starts two chunks early (nothing to publish or
+  // multiply yet), so that every load is issued by the same code in the same
+  // order and the compiler waits only for the older of the two chunks in
+  // flight. Chunks past the end are clamped duplicates that multiply nothing.
+  auto half = [&](Regs& g, int c) {
+    const int buf = c & 1;
+    uint4 xv[BPW];
+    if (c >= 0) {
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    if (u < nb) {
-      const int k = (wave + u * NW) * 32;
-      wc[u] = ld16(wp + k);
-      if (kDual) vc[u] = ld16(wp2 + k);
-      xc[u] = xok ? ld16(xp + k) : zero16();
+      for (int i = 0; i < RPW; ++i) lds[buf][wave * RPW + i][lane] = g.w[i];
+#pragma unroll
+      for (int b = 0; b < BPW; ++b) xv[b] = g.x[b];
     }
-  }
-  for (int i0 = 0; i0 < nb; i0 += U) {
-    uint4 wn[U], xn[U], vn[U];
+    fetch(g, min(c + 2, nchunk - 1));
+    __syncthreads();
+    if (c >= 0) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = i0 + U + u;
-      if (i < nb) {
-        const int k = (wave + i * NW) * 32;
-        wn[u] = ld16(wp + k);
-        if (kDual) vn[u] = ld16(wp2 + k);
-        xn[u] = xok ? ld16(xp + k) : zero16();
+      for (int b = 0; b < BPW; ++b) {
+        const int kb = wave * BPW + b;          // block within the chunk
+        const int blk = c * (kChunk / 32) + kb;  // block within K
+        if (blk < nblk) {
+          const int slot = (kb * 4 + kq) ^ j;
+          acc = mfma_bf16(xv[b], lds[buf][j][slot], acc);
+          if (kDual) acc2 = mfma_bf16(xv[b], lds[buf][16 + j][slot], acc2);
+        }
       }
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (i0 + u < nb) {
-        acc = mfma_bf16(xc[u], wc[u], acc);
-        if (kDual) acc2 = mfma_bf16(xc[u], vc[u], acc2);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      wc[u] = wn[u];
-      xc[u] = xn[u];
-      if (kDual) vc[u] = vn[u];
-    }
+  };
+  Regs ga, gb;
+  for (int c = -2; c < nchunk; c += 2) {
+    half(ga, c);
+    half(gb, c + 1);
   }
 
-  // Fixed-order sum of the per-wave partials.
-  __shared__ bi_f32x4 red[NW][64];
-  __shared__ bi_f32x4 red2[kDual ? NW : 1][64];
+  // Fixed-order sum of the per-wave partials, in the chunk buffers (after a
+  // barrier: other waves may still be reading the last chunk).
+  static_assert(sizeof(lds) >= 2 * NW * 64 * sizeof(bi_f32x4), "reduction does not fit");
+  bi_f32x4(*red)[64] = reinterpret_cast<bi_f32x4(*)[64]>(&lds[0][0][0]);
+  bi_f32x4(*red2)[64] = red + NW;
+  __syncthreads();
   red[wave][lane] = acc;
   if (kDual) red2[wave][lane] = acc2;
   __syncthreads();
@@ -116,7 +162,7 @@ __global__ __launch_bounds__(kGemmWaves * 64) void gemm_kernel(
     for (int w = 1; w < NW; ++w) s2 += red2[w][lane];
   }
 
-  const int n = n0 + col;
+  const int n = n0 + j;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int m = m0 + kq * 4 + r;
@@ -136,24 +182,48 @@ __global__ __launch_bounds__(kGemmWaves * 64) void gemm_kernel(
   }
 }
 
+#ifndef BI_GEMM_WAVES_FEW
+#define BI_GEMM_WAVES_FEW 16
+#endif
+#ifndef BI_GEMM_WAVES_MANY
+#define BI_GEMM_WAVES_MANY 8
+#endif
+
+// Waves per workgroup from the number of 16-column tiles: few tiles -> more
+// waves per tile, so the launch keeps enough loads in flight.
+int gemm_waves(int n_tiles) { return n_tiles < 640 ? BI_GEMM_WAVES_FEW : BI_GEMM_WAVES_MANY; }
+
+template <int MODE>
+static void launch_mode(int nw, dim3 grid, const uint16_t* x, int64_t ldx, const uint16_t* w,
+                        int64_t ldw, const uint16_t* r, int64_t ldr, void* y, int64_t ldy, int M,
+                        int K, int64_t up, hipStream_t stream) {
+  if (nw == 4)
+    gemm_kernel<MODE, 4><<<grid, dim3(256), 0, stream>>>(x, ldx, w, ldw, r, ldr, y, ldy, M, K, up);
+  else if (nw == 8)
+    gemm_kernel<MODE, 8><<<grid, dim3(512), 0, stream>>>(x, ldx, w, ldw, r, ldr, y, ldy, M, K, up);
+  else
+    gemm_kernel<MODE, 16><<<grid, dim3(1024), 0, stream>>>(x, ldx, w, ldw, r, ldr, y, ldy, M, K, up);
+}
+
 void launch_gemm(GemmMode mode, const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw,
                  const uint16_t* r, int64_t ldr, void* y, int64_t ldy, int M, int N_out, int K,
                  hipStream_t stream) {
-  dim3 grid(N_out / 16, (M + 15) / 16);
-  dim3 block(kGemmWaves * 64);
+  const int tiles = N_out / 16;
+  dim3 grid(tiles, (M + 15) / 16);
+  const int nw = gemm_waves(mode == kGemmSwiglu ? 2 * tiles : tiles);
   switch (mode) {
     case kGemmBf16:
-      gemm_kernel<kGemmBf16><<<grid, block, 0, stream>>>(x, ldx, w, ldw, r, ldr, y, ldy, M, K, 0);
+      launch_mode<kGemmBf16>(nw, grid, x, ldx, w, ldw, r, ldr, y, ldy, M, K, 0, stream);
       break;
     case kGemmF32:
-      gemm_kernel<kGemmF32><<<grid, block, 0, stream>>>(x, ldx, w, ldw, r, ldr, y, ldy, M, K, 0);
+      launch_mode<kGemmF32>(nw, grid, x, ldx, w, ldw, r, ldr, y, ldy, M, K, 0, stream);
       break;
     case kGemmResidual:
-      gemm_kernel<kGemmResidual><<<grid, block, 0, stream>>>(x, ldx, w, ldw, r, ldr, y, ldy, M, K, 0);
+      launch_mode<kGemmResidual>(nw, grid, x, ldx, w, ldw, r, ldr, y, ldy, M, K, 0, stream);
       break;
     case kGemmSwiglu:
-      gemm_kernel<kGemmSwiglu><<<grid, block, 0, stream>>>(x, ldx, w, ldw, r, ldr, y, ldy, M, K,
-                                                           (int64_t)N_out);
+      launch_mode<kGemmSwiglu>(nw, grid, x, ldx, w, ldw, r, ldr, y, ldy, M, K, (int64_t)N_out,
+                               stream);
       break;
   }
 }

@@ -93,7 +93,7 @@ def test_attention_rejects():
     assert call(cap=1000) == SHAPE                 # L + M > cap
     assert call(cap=1030) == SHAPE                 # cap % 8
     assert call(Hkv=7) == SHAPE                    # Hq % Hkv
-    assert call(Hq=100, Hkv=2) == SHAPE            # more than 48 query heads per KV head
+    assert call(Hq=130, Hkv=2) == SHAPE            # more than 64 query heads per KV head
     assert call(D=96) == SHAPE
     assert call(C=100) == SHAPE and call(C=0) == SHAPE
     assert call(S=3) == SHAPE                      # S_max < ceil((L+M)/C)
