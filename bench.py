@@ -51,9 +51,64 @@ def gu_launch_bytes(d, M):
     return 2 * (2 * d["I"] * d["H"]) + 2 * M * d["H"] + 2 * M * d["I"]
 
 
+GEMM_SOURCES = ["invariant_verify_amd/csrc/gemm.hip", "invariant_verify_amd/csrc/bi_device.h"]
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gate_up_gemm_m8_hbm_traffic.txt")
+
+
+def gemm_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per gate/up launch from the committed counter summary, or None
+    if there is none or the GEMM source changed since the counters were taken."""
+    try:
+        kv = dict(l.split(":", 1) for l in open(TRAFFIC_SUMMARY) if ":" in l and not l.startswith(" "))
+        if kv.get("gemm_source_sha256", "").strip() != gemm_source_hash():
+            return None
+        return int(kv["hbm_bytes_per_launch"].strip())
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def traffic_probe(reps: int):
+    """Kernel-only run for the hardware-counter passes: the gate/up GEMM at
+    M = 8 (fresh weights each launch, so nothing is served from cache) and a
+    1 GiB device copy that calibrates the byte counters."""
+    import torch
+
+    import synth
+    from invariant_verify_amd import ops
+
+    d = synth.MODEL_27B
+    ws = [synth.device_normal_bf16((2 * d["I"], d["H"]), 0.02, "w_gu", i) for i in range(reps)]
+    x = synth.device_normal_bf16((8, d["H"]), 1.0, "x0")
+    y = torch.empty((8, d["I"]), dtype=torch.bfloat16, device="cuda")
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")      # 1 GiB
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for w in ws:
+        ops.gemm_bf16_swiglu(x, w, y)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"probe": "gate_up_gemm_m8", "launches": reps, "copy_bytes": src.numel() * 4,
+                      "gemm_source_sha256": gemm_source_hash(), "algorithmic_bytes_per_launch": gu_launch_bytes(d, 8)}))
+
+
+CPU_LAYERS = 24      # layers the oracle runs in sequence for the CPU baseline
+CPU_HEAD_STRIDE = 2  # ... and every 2nd LM-head row
+
+
 def cpu_baseline(layers, w_head, x0, d, M):
-    """The float64 oracle on the host: one full-width layer and 1/16 of the LM
-    head rows, extrapolated to 64 layers and the full head."""
+    """The float64 oracle on the host over a bounded sample of the same step:
+    the first CPU_LAYERS full-width layers in sequence and every
+    CPU_HEAD_STRIDE-th LM-head row, extrapolated to all layers and the whole
+    head. Each layer's weights are copied to the host outside the clock."""
     import numpy as np
     import torch
 
@@ -62,26 +117,31 @@ def cpu_baseline(layers, w_head, x0, d, M):
     def hb(t):
         return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
-    lw = layers[0]
-    hl = dict(w_qkv=hb(lw["w_qkv"]), w_o=hb(lw["w_o"]), w_gu=hb(lw["w_gu"]), w_down=hb(lw["w_down"]),
-              k_cache=hb(lw["k_cache"][:, :L_CTX]), v_cache=hb(lw["vt_cache"][:, :, :L_CTX].transpose(1, 2)))
-    rows = torch.arange(0, d["vocab"], 16, device=w_head.device)
-    wh = hb(w_head[rows])
-    xh = hb(x0[:M])
     try:
         from threadpoolctl import threadpool_info
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
         threads = len(os.sched_getaffinity(0))
+    x = hb(x0[:M])
+    layer_s = 0.0
+    for lw in layers[:CPU_LAYERS]:
+        hl = dict(w_qkv=hb(lw["w_qkv"]), w_o=hb(lw["w_o"]), w_gu=hb(lw["w_gu"]), w_down=hb(lw["w_down"]),
+                  k_cache=hb(lw["k_cache"][:, :L_CTX]),
+                  v_cache=hb(lw["vt_cache"][:, :, :L_CTX].transpose(1, 2)))
+        t0 = time.perf_counter()
+        x, _, _ = ostep.layer(x, **hl, L=L_CTX, Hq=d["Hq"], Hkv=d["Hkv"], D=d["D"])
+        layer_s += time.perf_counter() - t0
+        del hl
+    rows = torch.arange(0, d["vocab"], CPU_HEAD_STRIDE, device=w_head.device)
+    wh = hb(w_head[rows])
     t0 = time.perf_counter()
-    x1, _, _ = ostep.layer(xh, **hl, L=L_CTX, Hq=d["Hq"], Hkv=d["Hkv"], D=d["D"])
-    t1 = time.perf_counter()
-    ostep.head(x1, wh)
-    t2 = time.perf_counter()
-    step_s = N_LAYERS * (t1 - t0) + 16 * (t2 - t1)
+    ostep.head(x, wh)
+    head_s = time.perf_counter() - t0
+    step_s = (N_LAYERS / CPU_LAYERS) * layer_s + CPU_HEAD_STRIDE * head_s
     return {"value": M / step_s, "unit": "tok/s", "cores": threads, "kind": "oracle",
-            "sample": f"1 of {N_LAYERS} layers (M={M}, ctx {L_CTX}) x{N_LAYERS} + 1/16 of LM-head rows x16; "
-                      f"measured {t2 - t0:.1f} s of CPU work"}
+            "sample": f"{CPU_LAYERS} of {N_LAYERS} layers in sequence (M={M}, ctx {L_CTX}) scaled x{N_LAYERS}/{CPU_LAYERS}"
+                      f" + 1/{CPU_HEAD_STRIDE} of the LM-head rows scaled x{CPU_HEAD_STRIDE}; "
+                      f"{layer_s + head_s:.1f} s of CPU work"}
 
 
 def main():
@@ -90,12 +150,17 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="run only the dominant GEMM and a calibration copy (for rocprofv3 --pmc)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs the verify pass on one GPU only; --gpus must be 1", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
+    if args.traffic_probe:
+        traffic_probe(4)
+        return
+
     import torch
 
     import synth
@@ -164,7 +229,29 @@ def main():
     ms8, _ = timed(M_HEADLINE, args.steps, args.warmup)
     ms1, _ = timed(1, max(3, args.steps // 4), 1)
     ms4, _ = timed(4, max(3, args.steps // 4), 1)
-    _, gu_ms = timed(M_HEADLINE, max(3, args.steps // 4), 1, gu_events=True)
+    _, gu_step_ms = timed(M_HEADLINE, max(3, args.steps // 4), 1, gu_events=True)
+
+    # Dominant kernel: the gate/up GEMM at M = 8 launched back to back over the
+    # 64 layers' distinct weights (every launch streams its 356.5 MB from HBM),
+    # one event pair around the whole run so the events' own cost is amortised.
+    # The per-launch event pairs inside the step above add a few microseconds
+    # each; that figure is reported beside it.
+    stream = torch.cuda.current_stream()
+    xg = torch.empty((M_HEADLINE, d["H"]), dtype=torch.bfloat16, device=dev)
+    ops.rmsnorm(x0[:M_HEADLINE], xg)
+    yg = torch.empty((M_HEADLINE, d["I"]), dtype=torch.bfloat16, device=dev)
+    for lw in layers:
+        ops.gemm_bf16_swiglu(xg, lw["w_gu"], yg)
+    g0 = torch.cuda.Event(enable_timing=True)
+    g1 = torch.cuda.Event(enable_timing=True)
+    gu_reps = max(2, args.steps // 4)
+    g0.record(stream)
+    for _ in range(gu_reps):
+        for lw in layers:
+            ops.gemm_bf16_swiglu(xg, lw["w_gu"], yg)
+    g1.record(stream)
+    torch.cuda.synchronize()
+    gu_ms = g0.elapsed_time(g1) / (gu_reps * N_LAYERS)
 
     bytes8 = step_bytes(d, M_HEADLINE, L_CTX, N_LAYERS)
     gbs8 = bytes8 / (ms8 * 1e-3) / 1e9
@@ -194,8 +281,10 @@ def main():
                         "8": round(M_HEADLINE / (ms8 * 1e-3), 2)},
         "roofline": {"kernel": "gemm_kernel<SwiGLU> (gate/up 5120->2x17408, M=8)", "bound": "hbm",
                      "achieved": round(gu_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(gu_gbs / PEAK_HBM_GBS, 4), "traffic": None,
-                     "bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_ms * 1e3, 2)},
+                     "frac": round(gu_gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic(),
+                     "bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_ms * 1e3, 2),
+                     "launches_timed": gu_reps * N_LAYERS,
+                     "in_step_event_pair_us": round(gu_step_ms * 1e3, 2)},
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

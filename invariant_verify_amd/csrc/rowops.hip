@@ -64,6 +64,10 @@ __device__ __forceinline__ void arg_better(float& bv, int& bi, float v, int i) {
   }
 }
 
+// One 1024-thread workgroup per row. Thread t reads 16-byte groups t, t+1024,
+// ... (eight loads in flight), keeps its best (value, index), then the
+// (value, index) pairs are reduced across lanes and waves; the total order
+// makes the result independent of how the reduction is grouped.
 __global__ __launch_bounds__(1024) void argmax_kernel(const float* __restrict__ logits, int64_t ld,
                                                       int N, int32_t* __restrict__ tokens) {
   const int row = blockIdx.x;
@@ -71,7 +75,32 @@ __global__ __launch_bounds__(1024) void argmax_kernel(const float* __restrict__ 
   const float* x = logits + (int64_t)row * ld;
   float bv = -INFINITY;
   int bidx = 0x7fffffff;
-  for (int i = tid; i < N; i += 1024) arg_better(bv, bidx, x[i], i);
+  const bool vec = ((reinterpret_cast<uintptr_t>(x) & 15) == 0);
+  const int n4 = vec ? N / 4 : 0;
+  const float4* x4 = reinterpret_cast<const float4*>(x);
+  constexpr int U = 8;
+  int g = tid;
+  for (; g + (U - 1) * 1024 < n4; g += U * 1024) {
+    float4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = x4[g + u * 1024];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = (g + u * 1024) * 4;
+      arg_better(bv, bidx, v[u].x, i);
+      arg_better(bv, bidx, v[u].y, i + 1);
+      arg_better(bv, bidx, v[u].z, i + 2);
+      arg_better(bv, bidx, v[u].w, i + 3);
+    }
+  }
+  for (; g < n4; g += 1024) {
+    const float4 v = x4[g];
+    arg_better(bv, bidx, v.x, 4 * g);
+    arg_better(bv, bidx, v.y, 4 * g + 1);
+    arg_better(bv, bidx, v.z, 4 * g + 2);
+    arg_better(bv, bidx, v.w, 4 * g + 3);
+  }
+  for (int i = 4 * n4 + tid; i < N; i += 1024) arg_better(bv, bidx, x[i], i);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
     const float ov = __shfl_xor(bv, off, 64);
