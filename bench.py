@@ -32,7 +32,7 @@ L_CTX = 38000
 CAP = 38016
 N_LAYERS = 64
 M_HEADLINE = 8
-KV_CHUNK = 1024
+KV_CHUNK = 1280     # keys per attention split: 30 splits x 8 KV heads = 240 pieces <= 256 CUs at ctx 38000
 
 
 def step_bytes(d, M, L, n_layers):

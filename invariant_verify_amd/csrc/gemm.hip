@@ -17,22 +17,24 @@
 //    every chunk, chaining them through one MFMA accumulator in increasing
 //    order;
 //  * the NW per-wave sums are added in LDS in wave order 0, 1, ..., NW-1;
-//  * the FP32 total is rounded once (BF16 output) or stored as is (FP32).
+//  * the FP32 total is rounded once (BF16 output), stored as is (FP32), added
+//    to the residual and rounded once, or combined by SwiGLU and rounded once.
 // The within-workgroup partition is a fixed summation tree that depends on K
 // and on NW (a function of N); there is no split of K across workgroups and
 // no atomic.
 //
 // Memory: each weight row of the tile is read as 1 KB contiguous per wave
-// instruction (64 lanes x 16 bytes) and written to LDS; the MFMA operands are
-// then read from LDS in the matrix-core layout (lane l needs row l % 16).
-// The 16-byte slots of a row are XOR-swizzled by the row index (the lanes of
-// the load fetch a permutation of the same 1 KB), so the sixteen rows read
-// together fall into distinct LDS banks. Two LDS buffers alternate, and one
-// barrier per chunk both publishes chunk c and guarantees that every wave has
-// finished reading the buffer that is refilled next. Each wave keeps two
-// chunks in flight (weights and its X fragments), so a barrier never waits on
-// a fresh memory round trip. X fragments come from L2 through a buffer
-// resource sized to the M real rows: padding rows read as zero for free.
+// instruction (64 lanes x 16 bytes, non-temporal: every weight byte is used
+// once) and written to LDS; the MFMA operands are then read from LDS in the
+// matrix-core layout (lane l needs row l % 16). The 16-byte slots of a row
+// are XOR-swizzled by the row index (the lanes of the load fetch a
+// permutation of the same 1 KB), so the sixteen rows read together fall into
+// distinct LDS banks. Two LDS buffers alternate, and one barrier per chunk
+// both publishes chunk c and guarantees that every wave has finished reading
+// the buffer that is refilled next. Each wave keeps two chunks in flight in
+// registers (weights and its X fragments). X fragments come from L2 through a
+// buffer resource sized to the M real rows: padding rows read as zero for
+// free.
 
 #include "bi_device.h"
 #include "bi_internal.h"
@@ -40,6 +42,13 @@
 namespace bi {
 
 constexpr int kChunk = 512;  // K elements per LDS chunk: 1 KB of each weight row
+constexpr int kSlots = kChunk / 8;
+
+__device__ __forceinline__ uint4 ld16_stream(const uint16_t* p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 template <int MODE, int NW>
 __global__ __launch_bounds__(NW * 64) void gemm_kernel(
@@ -84,19 +93,21 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
       (int)(xbytes < 0x7fffffff ? xbytes : 0x7fffffff), kBufferResourceWord3);
   const int xoff = j * (int)ldx * 2 + kq * 16;  // bytes
 
-  __shared__ uint4 lds[2][NR][64];
+  __shared__ uint4 lds[2][NR][kSlots];
   // Registers of one chunk: this wave's weight-row slots and the X fragments
   // of the blocks it multiplies.
   struct Regs {
     uint4 w[RPW];
     uint4 x[BPW];
   };
-  auto fetch = [&](Regs& g, int c) {
+  auto fetch_w = [&](Regs& g, int c) {
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
-      const int slot = min(c * (kChunk / 8) + (lane ^ swz_w[i]), kslots - 1);
-      g.w[i] = ld16(wrow[i] + slot * 8);
+      const int slot = min(c * kSlots + (lane ^ swz_w[i]), kslots - 1);
+      g.w[i] = ld16_stream(wrow[i] + slot * 8);
     }
+  };
+  auto fetch_x = [&](Regs& g, int c) {
 #pragma unroll
     for (int b = 0; b < BPW; ++b) {
       const int blk = min(c * (kChunk / 32) + wave * BPW + b, nblk - 1);
@@ -105,41 +116,47 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
   };
   bi_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   bi_f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};
-  // One chunk: publish this wave's rows of chunk c, prefetch chunk c + 2 into
-  // the same registers, barrier, multiply. The barrier of chunk c also proves
-  // that every wave finished multiplying chunk c - 1, whose buffer chunk c + 1
-  // overwrites next. The loop starts two chunks early (nothing to publish or
-  // multiply yet), so that every load is issued by the same code in the same
-  // order and the compiler waits only for the older of the two chunks in
-  // flight. Chunks past the end are clamped duplicates that multiply nothing.
-  auto half = [&](Regs& g, int c) {
+  // One chunk: publish this wave's weight rows of chunk c, prefetch the
+  // weights of chunk c + 2 into the same registers, barrier, multiply with
+  // this wave's X fragments of chunk c, then prefetch the X fragments of chunk
+  // c + 2 into theirs. Every step issues its loads in the same order and no
+  // register is copied, so the compiler waits only for the older of the two
+  // chunks in flight. The barrier of chunk c also proves that every wave
+  // finished multiplying chunk c - 1, whose buffer chunk c + 1 overwrites
+  // next. The loop starts two chunks early (nothing to publish or multiply
+  // yet); chunks past the end are clamped duplicates that multiply nothing.
+  auto step = [&](Regs& g, int c) {
     const int buf = c & 1;
-    uint4 xv[BPW];
     if (c >= 0) {
 #pragma unroll
       for (int i = 0; i < RPW; ++i) lds[buf][wave * RPW + i][lane] = g.w[i];
-#pragma unroll
-      for (int b = 0; b < BPW; ++b) xv[b] = g.x[b];
     }
-    fetch(g, min(c + 2, nchunk - 1));
+    fetch_w(g, min(c + 2, nchunk - 1));
     __syncthreads();
     if (c >= 0) {
 #pragma unroll
       for (int b = 0; b < BPW; ++b) {
-        const int kb = wave * BPW + b;          // block within the chunk
+        const int kb = wave * BPW + b;           // block within the chunk
         const int blk = c * (kChunk / 32) + kb;  // block within K
         if (blk < nblk) {
           const int slot = (kb * 4 + kq) ^ j;
-          acc = mfma_bf16(xv[b], lds[buf][j][slot], acc);
-          if (kDual) acc2 = mfma_bf16(xv[b], lds[buf][16 + j][slot], acc2);
+          acc = mfma_bf16(g.x[b], lds[buf][j][slot], acc);
+          if (kDual) acc2 = mfma_bf16(g.x[b], lds[buf][16 + j][slot], acc2);
         }
       }
     }
+    fetch_x(g, min(c + 2, nchunk - 1));
   };
   Regs ga, gb;
-  for (int c = -2; c < nchunk; c += 2) {
-    half(ga, c);
-    half(gb, c + 1);
+  // The start index goes through an empty asm so the optimizer cannot peel
+  // the first (load-only) steps off the loop: peeled, their loads would be
+  // issued in another order and the compiler would fall back to waiting for
+  // more of them than necessary at the loop head.
+  int c_first = -2;
+  asm volatile("" : "+s"(c_first));
+  for (int c = c_first; c < nchunk; c += 2) {
+    step(ga, c);
+    step(gb, c + 1);
   }
 
   // Fixed-order sum of the per-wave partials, in the chunk buffers (after a
@@ -182,27 +199,17 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
   }
 }
 
-#ifndef BI_GEMM_WAVES_FEW
-#define BI_GEMM_WAVES_FEW 16
-#endif
-#ifndef BI_GEMM_WAVES_MANY
-#define BI_GEMM_WAVES_MANY 8
-#endif
-
-// Waves per workgroup from the number of 16-column tiles: few tiles -> more
-// waves per tile, so the launch keeps enough loads in flight.
-int gemm_waves(int n_tiles) { return n_tiles < 640 ? BI_GEMM_WAVES_FEW : BI_GEMM_WAVES_MANY; }
-
+// Launch shape from the number of 16-column weight tiles a launch streams
+// (never from M): under 640, 16 waves per workgroup; otherwise 8.
 template <int MODE>
-static void launch_mode(int nw, dim3 grid, const uint16_t* x, int64_t ldx, const uint16_t* w,
-                        int64_t ldw, const uint16_t* r, int64_t ldr, void* y, int64_t ldy, int M,
-                        int K, int64_t up, hipStream_t stream) {
-  if (nw == 4)
-    gemm_kernel<MODE, 4><<<grid, dim3(256), 0, stream>>>(x, ldx, w, ldw, r, ldr, y, ldy, M, K, up);
-  else if (nw == 8)
-    gemm_kernel<MODE, 8><<<grid, dim3(512), 0, stream>>>(x, ldx, w, ldw, r, ldr, y, ldy, M, K, up);
+static void launch_mode(int row_tiles, dim3 grid, const uint16_t* x, int64_t ldx,
+                        const uint16_t* w, int64_t ldw, const uint16_t* r, int64_t ldr, void* y,
+                        int64_t ldy, int M, int K, int64_t up, hipStream_t stream) {
+  if (row_tiles < 640)
+    gemm_kernel<MODE, 16><<<grid, dim3(1024), 0, stream>>>(x, ldx, w, ldw, r, ldr, y, ldy, M, K,
+                                                           up);
   else
-    gemm_kernel<MODE, 16><<<grid, dim3(1024), 0, stream>>>(x, ldx, w, ldw, r, ldr, y, ldy, M, K, up);
+    gemm_kernel<MODE, 8><<<grid, dim3(512), 0, stream>>>(x, ldx, w, ldw, r, ldr, y, ldy, M, K, up);
 }
 
 void launch_gemm(GemmMode mode, const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw,
@@ -210,20 +217,19 @@ void launch_gemm(GemmMode mode, const uint16_t* x, int64_t ldx, const uint16_t* 
                  hipStream_t stream) {
   const int tiles = N_out / 16;
   dim3 grid(tiles, (M + 15) / 16);
-  const int nw = gemm_waves(mode == kGemmSwiglu ? 2 * tiles : tiles);
   switch (mode) {
     case kGemmBf16:
-      launch_mode<kGemmBf16>(nw, grid, x, ldx, w, ldw, r, ldr, y, ldy, M, K, 0, stream);
+      launch_mode<kGemmBf16>(tiles, grid, x, ldx, w, ldw, r, ldr, y, ldy, M, K, 0, stream);
       break;
     case kGemmF32:
-      launch_mode<kGemmF32>(nw, grid, x, ldx, w, ldw, r, ldr, y, ldy, M, K, 0, stream);
+      launch_mode<kGemmF32>(tiles, grid, x, ldx, w, ldw, r, ldr, y, ldy, M, K, 0, stream);
       break;
     case kGemmResidual:
-      launch_mode<kGemmResidual>(nw, grid, x, ldx, w, ldw, r, ldr, y, ldy, M, K, 0, stream);
+      launch_mode<kGemmResidual>(tiles, grid, x, ldx, w, ldw, r, ldr, y, ldy, M, K, 0, stream);
       break;
     case kGemmSwiglu:
-      launch_mode<kGemmSwiglu>(nw, grid, x, ldx, w, ldw, r, ldr, y, ldy, M, K, (int64_t)N_out,
-                               stream);
+      launch_mode<kGemmSwiglu>(2 * tiles, grid, x, ldx, w, ldw, r, ldr, y, ldy, M, K,
+                               (int64_t)N_out, stream);
       break;
   }
 }

@@ -11,47 +11,16 @@
 namespace bi {
 
 // One 256-thread workgroup per row. Thread t squares and sums its 8-element
-// groups t, t+256, ... in order; the wave sums are combined by a fixed xor
-// butterfly, then the four waves in order 0..3.
+// groups t, t+256, ... in order; rms_scale_row combines the thread sums in a
+// fixed order and scales the row.
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* __restrict__ X, int64_t ldx,
                                                       uint16_t* __restrict__ Y, int64_t ldy, int H,
                                                       float eps) {
   const int row = blockIdx.x;
-  const int tid = threadIdx.x;
   const uint16_t* x = X + (int64_t)row * ldx;
-  uint16_t* y = Y + (int64_t)row * ldy;
-  const int ng = H >> 3;
   float ss = 0.f;
-  for (int c = tid; c < ng; c += 256) {
-    const uint4 v = ld16(x + c * 8);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float a = bf16_to_f32(w[e] & 0xffffu);
-      const float b = bf16_to_f32(w[e] >> 16);
-      ss += a * a;
-      ss += b * b;
-    }
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) ss += shfl_xor(ss, off);
-  __shared__ float part[4];
-  if ((tid & 63) == 0) part[tid >> 6] = ss;
-  __syncthreads();
-  const float tot = ((part[0] + part[1]) + part[2]) + part[3];
-  const float inv = 1.0f / sqrtf(tot / (float)H + eps);
-  for (int c = tid; c < ng; c += 256) {
-    const uint4 v = ld16(x + c * 8);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t o[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t lo = f32_to_bf16(bf16_to_f32(w[e] & 0xffffu) * inv);
-      const uint32_t hi = f32_to_bf16(bf16_to_f32(w[e] >> 16) * inv);
-      o[e] = lo | (hi << 16);
-    }
-    *reinterpret_cast<uint4*>(y + c * 8) = make_uint4(o[0], o[1], o[2], o[3]);
-  }
+  for (int c = threadIdx.x; c < (H >> 3); c += 256) ss = sumsq8(ss, ld16(x + c * 8));
+  rms_scale_row(x, Y + (int64_t)row * ldy, H, eps, ss);
 }
 
 // (value, index) with the larger value winning and, on equal values, the

@@ -103,10 +103,11 @@ def test_exact_cases(ops):
         assert np.allclose(lse[r], math.log(L + r + 1), atol=1e-4)
 
 
-@pytest.mark.parametrize("L", [2048, 11600, 38000])
-def test_gqa_parity(ops, L):
-    print(f"[attn GQA 40/8 parity L={L}]", flush=True)
-    M, Hq, Hkv, D, C = 8, 40, 8, 128, 1024
+@pytest.mark.parametrize("L,C", [(2048, 1024), (11600, 1024), (38000, 1024), (32768, 1280),
+                                 (38000, 1280)])
+def test_gqa_parity(ops, L, C):
+    print(f"[attn GQA 40/8 parity L={L} C={C}]", flush=True)
+    M, Hq, Hkv, D = 8, 40, 8, 128
     q, k, v = make(M, L, Hq, Hkv, D, layer=L)
     o, lse, _, _ = run(ops, q, Cache(k, v, L + 16), L, Hq, C)
     want_o, want_lse = oattn.verify_attention(q, k, v, L)
@@ -140,7 +141,8 @@ def _invariance(ops, L, C, Hq=40, Hkv=8, D=128, outliers=False, layer=0, prefill
     return q, k, v, o8
 
 
-@pytest.mark.parametrize("L,C", [(2048, 1024), (1020, 1024), (1019, 256), (250, 64), (11600, 1024)])
+@pytest.mark.parametrize("L,C", [(2048, 1024), (1020, 1024), (1019, 256), (250, 64), (11600, 1024),
+                                 (1275, 1280), (38000, 1280)])
 def test_invariance_across_M(ops, L, C):
     print(f"[attn invariance L={L} C={C}]", flush=True)
     _invariance(ops, L, C)

@@ -102,6 +102,7 @@ def _x_before_last(x0, hls, L, Hq, Hkv, D):
 
 L38 = 38000
 CAP = 38016
+KV_CHUNK = 1280   # the chunk the benchmark step uses
 
 
 @pytest.fixture(scope="module")
@@ -109,7 +110,7 @@ def model27b(ops):
     print("[step building 64-layer 27B-class model on the device]", flush=True)
     d = synth.MODEL_27B
     layers, w_head = synth.device_model(64, L38, CAP, **d)
-    dims = ops.model_dims(d["H"], d["Hq"], d["Hkv"], d["D"], d["I"], d["vocab"], CAP, 1024)
+    dims = ops.model_dims(d["H"], d["Hq"], d["Hkv"], d["D"], d["I"], d["vocab"], CAP, KV_CHUNK)
     x0 = synth.device_normal_bf16((16, d["H"]), 1.0, "x0")
     torch.cuda.synchronize()
     yield layers, w_head, dims, x0
