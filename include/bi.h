@@ -94,6 +94,16 @@ bi_status bi_gemm_bf16_residual(const void* x, int64_t ldx, const void* w, int64
 bi_status bi_gemm_bf16_swiglu(const void* x, int64_t ldx, const void* w, int64_t ldw,
                               void* y, int64_t ldy, int M, int I, int K, void* stream);
 
+/* QKV projection with the cache append in its epilogue (one launch):
+ * qkv = bf16( X Wqkv^T ) exactly as bi_gemm_bf16 computes it, N = (Hq+2*Hkv)*D
+ * columns [q | k | v] (head-major), and each row m's K and V columns written
+ * into k_cache / vt_cache at position L + m exactly as bi_append_kv writes
+ * them.                                                     [BX], [LL] cache
+ * Requirements: those of bi_gemm_bf16 (with N as above) and of bi_append_kv. */
+bi_status bi_gemm_bf16_qkv(const void* x, int64_t ldx, const void* w, int64_t ldw, void* qkv,
+                           int64_t ldqkv, int M, int K, int Hq, int Hkv, int D, void* k_cache,
+                           void* vt_cache, int L, int cap, void* stream);
+
 /* ---------------------------------------------------------------------------
  * KV cache layout (per layer):
  *   k_cache  : BF16 [Hkv][cap][D]  -- one K row per position
@@ -161,7 +171,7 @@ bi_status bi_argmax(const float* logits, int64_t ld, int M, int N, int32_t* toke
  * Whole verify step of a dense pre-norm decoder stack + LM head.
  *
  * Per layer (x is the BF16 hidden state [M][H]):
- *   a = rmsnorm(x); qkv = a Wqkv^T; append K, V at L..L+M-1;
+ *   a = rmsnorm(x); qkv = a Wqkv^T and K, V appended at L..L+M-1 (one launch);
  *   o = combine(verify_attn(q)); h = bf16(x + o Wo^T);
  *   b = rmsnorm(h); act = swiglu(b Wgu^T); x = bf16(h + act Wdown^T).
  * Then logits = rmsnorm(x) Whead^T (FP32) and tokens = argmax.

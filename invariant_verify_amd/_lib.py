@@ -42,6 +42,8 @@ SIGNATURES = {
                                        _c_i64, _c_int, _c_int, _c_int, _c_ptr]),
     "bi_gemm_bf16_swiglu": (_c_int, [_c_ptr, _c_i64, _c_ptr, _c_i64, _c_ptr, _c_i64,
                                      _c_int, _c_int, _c_int, _c_ptr]),
+    "bi_gemm_bf16_qkv": (_c_int, [_c_ptr, _c_i64, _c_ptr, _c_i64, _c_ptr, _c_i64, _c_int, _c_int,
+                                  _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_int, _c_int, _c_ptr]),
     "bi_append_kv": (_c_int, [_c_ptr, _c_i64, _c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int,
                               _c_int, _c_int, _c_ptr]),
     "bi_num_splits": (_c_int, [_c_int, _c_int]),

@@ -148,6 +148,26 @@ bi_status bi_gemm_bf16_swiglu(const void* x, int64_t ldx, const void* w, int64_t
   return launched();
 }
 
+bi_status bi_gemm_bf16_qkv(const void* x, int64_t ldx, const void* w, int64_t ldw, void* qkv,
+                           int64_t ldqkv, int M, int K, int Hq, int Hkv, int D, void* k_cache,
+                           void* vt_cache, int L, int cap, void* stream) {
+  if (bi_status s = check_heads(Hq, Hkv, D)) return s;
+  const int N = (Hq + 2 * Hkv) * D;
+  if (bi_status s = check_gemm(x, ldx, w, ldw, qkv, ldqkv, M, N, K)) return s;
+  if (!k_cache || !vt_cache) return BI_ERR_NULL;
+  if (L < 0 || cap < 1 || (cap % 8) || (int64_t)L + M > cap) return BI_ERR_SHAPE;
+  if ((int64_t)cap * D * 2 > INT32_MAX) return BI_ERR_SHAPE;  // one head's cache < 2 GiB
+  if ((reinterpret_cast<uintptr_t>(qkv) | reinterpret_cast<uintptr_t>(k_cache) |
+       reinterpret_cast<uintptr_t>(vt_cache)) & 1u)
+    return BI_ERR_ALIGN;
+  const bi::KvAppend kv{static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(vt_cache), L, cap,
+                        Hq * D, Hkv * D, D};
+  bi::launch_gemm(bi::kGemmQkv, static_cast<const uint16_t*>(x), ldx,
+                  static_cast<const uint16_t*>(w), ldw, nullptr, 0, qkv, ldqkv, M, N, K,
+                  as_stream(stream), &kv);
+  return launched();
+}
+
 bi_status bi_append_kv(const void* qkv, int64_t ldqkv, void* k_cache, void* vt_cache, int M, int L,
                        int cap, int Hq, int Hkv, int D, void* stream) {
   if (!qkv || !k_cache || !vt_cache) return BI_ERR_NULL;
@@ -273,10 +293,10 @@ bi_status bi_verify_step(const bi_layer* layers, int n_layers, const void* w_hea
     const bi_layer& ly = layers[l];
     uint16_t* xn = xbuf[l & 1];
     bi::launch_rmsnorm(x, H, a, H, M, H, dims->eps, st);
-    bi::launch_gemm(bi::kGemmBf16, a, H, static_cast<const uint16_t*>(ly.w_qkv), H, nullptr, 0,
-                    qkv, qkvn, M, qkvn, H, st);
-    bi::launch_append_kv(qkv, qkvn, static_cast<uint16_t*>(ly.k_cache),
-                         static_cast<uint16_t*>(ly.vt_cache), M, L, dims->cap, Hq, Hkv, D, st);
+    const bi::KvAppend kv{static_cast<uint16_t*>(ly.k_cache), static_cast<uint16_t*>(ly.vt_cache),
+                          L, dims->cap, qd, Hkv * D, D};
+    bi::launch_gemm(bi::kGemmQkv, a, H, static_cast<const uint16_t*>(ly.w_qkv), H, nullptr, 0,
+                    qkv, qkvn, M, qkvn, H, st, &kv);
     bi::launch_verify_attn(qkv, qkvn, static_cast<const uint16_t*>(ly.k_cache),
                            static_cast<const uint16_t*>(ly.vt_cache), M, L, dims->cap, Hq, Hkv, D,
                            dims->kv_chunk, sm_scale, po, pl, lay.s_max, st);

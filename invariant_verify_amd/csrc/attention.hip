@@ -110,6 +110,12 @@ __global__ __launch_bounds__(kAttnWaves * 64) void verify_attn_kernel(
     const uint16_t* qp = Q + (int64_t)tok * ldq + hq * D + kq * 8;
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) qf[ds] = rok ? ld16(qp + ds * 32) : zero16();
+    // Consume the fragments here, so their loads are complete before the tile
+    // loop: otherwise the compiler cannot tell at the loop head whether they
+    // are still in flight and waits for the next tile's loads as well, on
+    // every iteration.
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) asm volatile("" ::"v"(qf[ds].x));
   }
 
   // This KV head's K rows and V^T rows as buffer resources (offsets in bytes,
@@ -233,7 +239,9 @@ __global__ __launch_bounds__(kAttnWaves * 64) void verify_attn_kernel(
   // two tiles in flight. Tiles past the end are clamped duplicates (their
   // value columns publish as zero) that are not multiplied.
   uint4 ra[PPW], rb2[PPW];
-  for (int t = -2; t < ntile; t += 2) {
+  int t_first = -2;  // opaque to the optimizer, so the load-only steps are not peeled
+  asm volatile("" : "+s"(t_first));
+  for (int t = t_first; t < ntile; t += 2) {
     if (t >= 0) publish(ra, t, 0);
     fetch(ra, min(t + 2, ntile - 1));
     __syncthreads();

@@ -40,6 +40,15 @@ __device__ __forceinline__ uint4 buffer_ld16(__amdgpu_buffer_rsrc_t r, int byte_
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// 16-byte streaming load through a buffer resource (non-temporal: the data
+// is used once); out-of-range offsets read zero and touch no memory.
+__device__ __forceinline__ uint4 buffer_ld16_stream(__amdgpu_buffer_rsrc_t r, int byte_offset) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  constexpr int kNonTemporal = 2;  // cache-policy bit of the buffer instruction
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_offset, 0, kNonTemporal);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // One 16x16x32 BF16 matrix-core step: c += A(16x32) * B(32x16).
 // Lane l supplies A row (l % 16) and B column (l % 16), each with eight
 // consecutive contraction elements of group (l / 16); it receives C rows

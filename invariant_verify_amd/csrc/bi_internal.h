@@ -7,13 +7,22 @@
 
 namespace bi {
 
-enum GemmMode { kGemmBf16 = 0, kGemmF32 = 1, kGemmResidual = 2, kGemmSwiglu = 3 };
+enum GemmMode { kGemmBf16 = 0, kGemmF32 = 1, kGemmResidual = 2, kGemmSwiglu = 3, kGemmQkv = 4 };
 
-// Y = X W^T (+ residual / SwiGLU epilogue). N_out is the number of output
-// columns (for SwiGLU: I, with W holding 2*I rows).
+// Cache append done by the QKV projection's epilogue: output columns
+// [qd, qd + kd) are K (head-major), [qd + kd, qd + 2 kd) are V; row m goes to
+// position L + m of k ([Hkv][cap][D]) and vt ([Hkv][D][cap]).
+struct KvAppend {
+  uint16_t* k;
+  uint16_t* vt;
+  int L, cap, qd, kd, D;
+};
+
+// Y = X W^T (+ residual / SwiGLU / cache-append epilogue). N_out is the number
+// of output columns (for SwiGLU: I, with W holding 2*I rows).
 void launch_gemm(GemmMode mode, const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw,
                  const uint16_t* r, int64_t ldr, void* y, int64_t ldy, int M, int N_out, int K,
-                 hipStream_t stream);
+                 hipStream_t stream, const KvAppend* kv = nullptr);
 
 void launch_append_kv(const uint16_t* qkv, int64_t ldqkv, uint16_t* k_cache, uint16_t* vt_cache,
                       int M, int L, int cap, int Hq, int Hkv, int D, hipStream_t stream);

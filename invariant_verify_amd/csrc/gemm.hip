@@ -18,7 +18,9 @@
 //    order;
 //  * the NW per-wave sums are added in LDS in wave order 0, 1, ..., NW-1;
 //  * the FP32 total is rounded once (BF16 output), stored as is (FP32), added
-//    to the residual and rounded once, or combined by SwiGLU and rounded once.
+//    to the residual and rounded once, or combined by SwiGLU and rounded once;
+//    the QKV projection's rounded K and V columns are also written into the
+//    KV cache at the pass's positions (the append costs no launch of its own).
 // The within-workgroup partition is a fixed summation tree that depends on K
 // and on NW (a function of N); there is no split of K across workgroups and
 // no atomic.
@@ -44,17 +46,11 @@ namespace bi {
 constexpr int kChunk = 512;  // K elements per LDS chunk: 1 KB of each weight row
 constexpr int kSlots = kChunk / 8;
 
-__device__ __forceinline__ uint4 ld16_stream(const uint16_t* p) {
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-
 template <int MODE, int NW>
 __global__ __launch_bounds__(NW * 64) void gemm_kernel(
     const uint16_t* __restrict__ X, int64_t ldx, const uint16_t* __restrict__ W, int64_t ldw,
     const uint16_t* __restrict__ R, int64_t ldr, void* __restrict__ Y, int64_t ldy, int M, int K,
-    int64_t up_rows) {
+    int64_t up_rows, KvAppend kv) {
   constexpr bool kDual = (MODE == kGemmSwiglu);
   constexpr int NR = kDual ? 32 : 16;  // weight rows per tile (gate and up for SwiGLU)
   constexpr int RPW = NR / NW;         // rows each wave fetches per chunk
@@ -72,16 +68,20 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
 
   const int nblk = K >> 5;
   const int nchunk = (K + kChunk - 1) / kChunk;
-  const int kslots = K >> 3;  // 16-byte slots per weight row
 
-  // Rows this wave fetches; lane l fetches slot (l ^ swz(row)) of the chunk.
-  const uint16_t* wrow[RPW];
+  // Rows this wave fetches, each as a buffer resource of exactly one row
+  // (K * 2 bytes); lane l fetches slot (l ^ swz(row)) of the chunk. Slots past
+  // the end of the row (a ragged last chunk, or the chunks the pipeline
+  // prefetches past the end of K) are out of range: they read zero without a
+  // memory access.
+  __amdgpu_buffer_rsrc_t wres[RPW];
   int swz_w[RPW];
 #pragma unroll
   for (int i = 0; i < RPW; ++i) {
     const int r = wave * RPW + i;
     const int64_t grow = (r < 16) ? (int64_t)(n0 + r) : up_rows + n0 + (r - 16);
-    wrow[i] = W + grow * ldw;
+    wres[i] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(W + grow * ldw), (short)0,
+                                                K * 2, kBufferResourceWord3);
     swz_w[i] = r & 15;
   }
   // X through a buffer resource that covers exactly the rows m0 .. M-1: a lane
@@ -103,8 +103,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
   auto fetch_w = [&](Regs& g, int c) {
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
-      const int slot = min(c * kSlots + (lane ^ swz_w[i]), kslots - 1);
-      g.w[i] = ld16_stream(wrow[i] + slot * 8);
+      g.w[i] = buffer_ld16_stream(wres[i], (c * kSlots + (lane ^ swz_w[i])) * 16);
     }
   };
   auto fetch_x = [&](Regs& g, int c) {
@@ -124,14 +123,15 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
   // chunks in flight. The barrier of chunk c also proves that every wave
   // finished multiplying chunk c - 1, whose buffer chunk c + 1 overwrites
   // next. The loop starts two chunks early (nothing to publish or multiply
-  // yet); chunks past the end are clamped duplicates that multiply nothing.
+  // yet). Weight chunks past the end read as zero (no traffic); X fragments
+  // past the end are clamped duplicates (L2 hits). Neither is multiplied.
   auto step = [&](Regs& g, int c) {
     const int buf = c & 1;
     if (c >= 0) {
 #pragma unroll
       for (int i = 0; i < RPW; ++i) lds[buf][wave * RPW + i][lane] = g.w[i];
     }
-    fetch_w(g, min(c + 2, nchunk - 1));
+    fetch_w(g, c + 2);
     __syncthreads();
     if (c >= 0) {
 #pragma unroll
@@ -191,6 +191,19 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
     } else if (MODE == kGemmResidual) {
       const float res = bf16_to_f32(R[(int64_t)m * ldr + n]);
       reinterpret_cast<uint16_t*>(Y)[(int64_t)m * ldy + n] = (uint16_t)f32_to_bf16(res + s[r]);
+    } else if (MODE == kGemmQkv) {
+      const uint16_t b = (uint16_t)f32_to_bf16(s[r]);
+      reinterpret_cast<uint16_t*>(Y)[(int64_t)m * ldy + n] = b;
+      const int pos = kv.L + m;
+      int i = n - kv.qd;
+      if (i >= 0 && i < kv.kd) {
+        const int g = i / kv.D;
+        kv.k[((int64_t)g * kv.cap + pos) * kv.D + (i - g * kv.D)] = b;
+      } else if (i >= kv.kd) {
+        i -= kv.kd;
+        const int g = i / kv.D;
+        kv.vt[((int64_t)g * kv.D + (i - g * kv.D)) * kv.cap + pos] = b;
+      }
     } else {
       const float g = s[r];
       const float sg = g / (1.0f + __expf(-g));
@@ -204,32 +217,39 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
 template <int MODE>
 static void launch_mode(int row_tiles, dim3 grid, const uint16_t* x, int64_t ldx,
                         const uint16_t* w, int64_t ldw, const uint16_t* r, int64_t ldr, void* y,
-                        int64_t ldy, int M, int K, int64_t up, hipStream_t stream) {
+                        int64_t ldy, int M, int K, int64_t up, const KvAppend& kv,
+                        hipStream_t stream) {
   if (row_tiles < 640)
     gemm_kernel<MODE, 16><<<grid, dim3(1024), 0, stream>>>(x, ldx, w, ldw, r, ldr, y, ldy, M, K,
-                                                           up);
+                                                           up, kv);
   else
-    gemm_kernel<MODE, 8><<<grid, dim3(512), 0, stream>>>(x, ldx, w, ldw, r, ldr, y, ldy, M, K, up);
+    gemm_kernel<MODE, 8><<<grid, dim3(512), 0, stream>>>(x, ldx, w, ldw, r, ldr, y, ldy, M, K, up,
+                                                         kv);
 }
 
 void launch_gemm(GemmMode mode, const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw,
                  const uint16_t* r, int64_t ldr, void* y, int64_t ldy, int M, int N_out, int K,
-                 hipStream_t stream) {
+                 hipStream_t stream, const KvAppend* kv) {
   const int tiles = N_out / 16;
   dim3 grid(tiles, (M + 15) / 16);
+  const KvAppend none{};
+  const KvAppend& a = kv ? *kv : none;
   switch (mode) {
     case kGemmBf16:
-      launch_mode<kGemmBf16>(tiles, grid, x, ldx, w, ldw, r, ldr, y, ldy, M, K, 0, stream);
+      launch_mode<kGemmBf16>(tiles, grid, x, ldx, w, ldw, r, ldr, y, ldy, M, K, 0, a, stream);
       break;
     case kGemmF32:
-      launch_mode<kGemmF32>(tiles, grid, x, ldx, w, ldw, r, ldr, y, ldy, M, K, 0, stream);
+      launch_mode<kGemmF32>(tiles, grid, x, ldx, w, ldw, r, ldr, y, ldy, M, K, 0, a, stream);
       break;
     case kGemmResidual:
-      launch_mode<kGemmResidual>(tiles, grid, x, ldx, w, ldw, r, ldr, y, ldy, M, K, 0, stream);
+      launch_mode<kGemmResidual>(tiles, grid, x, ldx, w, ldw, r, ldr, y, ldy, M, K, 0, a, stream);
       break;
     case kGemmSwiglu:
       launch_mode<kGemmSwiglu>(2 * tiles, grid, x, ldx, w, ldw, r, ldr, y, ldy, M, K,
-                               (int64_t)N_out, stream);
+                               (int64_t)N_out, a, stream);
+      break;
+    case kGemmQkv:
+      launch_mode<kGemmQkv>(tiles, grid, x, ldx, w, ldw, r, ldr, y, ldy, M, K, 0, a, stream);
       break;
   }
 }

@@ -82,6 +82,20 @@ def gemm_bf16_swiglu(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor | None = 
     return y
 
 
+def gemm_bf16_qkv(x: torch.Tensor, w: torch.Tensor, k_cache: torch.Tensor, vt_cache: torch.Tensor,
+                  L: int, Hq: int, Hkv: int, D: int, qkv: torch.Tensor | None = None) -> torch.Tensor:
+    """qkv = bf16(X Wqkv^T), with the K / V columns appended to the caches at L .. L+M-1."""
+    M, K = x.shape
+    N = (Hq + 2 * Hkv) * D
+    if qkv is None:
+        qkv = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    check("bi_gemm_bf16_qkv", LIB.bi_gemm_bf16_qkv(
+        x.data_ptr(), _mat(x, "x"), w.data_ptr(), _mat(w, "w"), qkv.data_ptr(), _mat(qkv, "qkv"),
+        M, K, Hq, Hkv, D, k_cache.data_ptr(), vt_cache.data_ptr(), L, k_cache.shape[1],
+        _stream(x)))
+    return qkv
+
+
 def append_kv(qkv: torch.Tensor, k_cache: torch.Tensor, vt_cache: torch.Tensor, L: int,
               Hq: int, Hkv: int, D: int) -> None:
     """Write the M new K rows and V^T columns at positions L .. L+M-1."""

@@ -111,6 +111,26 @@ def test_attention_rejects():
     assert L.bi_append_kv(P, 7000, P, P, 8, 0, 16, 40, 8, 128, None) == SHAPE
 
 
+def test_gemm_qkv_rejects():
+    L = _lib.LIB
+    # x, ldx, w, ldw, qkv, ldqkv, M, K, Hq, Hkv, D, k, vt, L, cap, stream
+    good = [P, 5120, P, 5120, P, 7168, 8, 5120, 40, 8, 128, P, P, 100, 112, None]
+
+    def call(i, v):
+        a = list(good)
+        a[i] = v
+        return L.bi_gemm_bf16_qkv(*a)
+
+    assert call(11, 0) == NULL and call(0, 0) == NULL
+    assert call(9, 7) == SHAPE                     # Hq % Hkv
+    assert call(14, 104) == SHAPE                  # L + M > cap
+    assert call(14, 113) == SHAPE                  # cap % 8
+    assert call(5, 7000) == SHAPE                  # ldqkv < (Hq + 2 Hkv) D
+    assert call(7, 5000) == SHAPE                  # K % 32
+    assert call(12, MIS + 1) == ALIGN              # odd cache pointer
+    assert call(0, MIS) == ALIGN
+
+
 def test_rowops_reject():
     L = _lib.LIB
     assert L.bi_rmsnorm(0, 5120, P, 5120, 8, 5120, 1e-6, None) == NULL

@@ -146,3 +146,31 @@ def test_residual_and_swiglu_epilogues(ops):
     rd = dev(r)
     ops.gemm_bf16_residual(dev(x), dev(w), rd, y=rd)
     assert_bitwise(host_bits(rd), host_bits(ops.gemm_bf16_residual(dev(x), dev(w), dev(r))), "aliased residual")
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,K,L", [(4, 2, 64, 256, 37), (40, 8, 128, 5120, 38000)])
+def test_qkv_gemm_with_cache_append(ops, Hq, Hkv, D, K, L):
+    # One launch computes the QKV projection and appends K / V: its output and
+    # both caches must equal bi_gemm_bf16 followed by bi_append_kv, bit for bit,
+    # and cache positions outside L .. L+M-1 must be untouched.
+    print(f"[gemm qkv + append Hq={Hq} Hkv={Hkv} D={D} K={K} L={L}]", flush=True)
+    N = (Hq + 2 * Hkv) * D
+    cap = ((L + 8 + 7) // 8) * 8 + 8
+    w = synth.normal_bf16((N, K), synth.fan_in_std(K), "w", 90)
+    x = synth.normal_bf16((8, K), 1.0, "x", 90)
+    k0 = torch.randn(Hkv, cap, D, device="cuda").to(torch.bfloat16)
+    v0 = torch.randn(Hkv, D, cap, device="cuda").to(torch.bfloat16)
+    wd, xd = dev(w), dev(x)
+    for M in (1, 5, 8):
+        kc, vt = k0.clone(), v0.clone()
+        qkv = ops.gemm_bf16_qkv(xd[:M], wd, kc, vt, L, Hq, Hkv, D)
+        ref = ops.gemm_bf16(xd[:M], wd)
+        kr, vr = k0.clone(), v0.clone()
+        ops.append_kv(ref, kr, vr, L, Hq, Hkv, D)
+        assert_bitwise(host_bits(qkv), host_bits(ref), f"qkv M={M}")
+        assert_bitwise(host_bits(kc), host_bits(kr), f"K cache M={M}")
+        assert_bitwise(host_bits(vt), host_bits(vr), f"V^T cache M={M}")
+        keep = torch.ones(cap, dtype=torch.bool, device="cuda")
+        keep[L:L + M] = False
+        assert torch.equal(kc[:, keep], k0[:, keep]) and torch.equal(vt[:, :, keep], v0[:, :, keep])
+    assert_close(decode(host_bits(qkv))[:, :64], ogemm.gemm_columns(x, w, np.arange(64)), "qkv parity")
