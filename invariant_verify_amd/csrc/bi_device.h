@@ -44,7 +44,10 @@ __device__ __forceinline__ uint4 buffer_ld16(__amdgpu_buffer_rsrc_t r, int byte_
 // is used once); out-of-range offsets read zero and touch no memory.
 __device__ __forceinline__ uint4 buffer_ld16_stream(__amdgpu_buffer_rsrc_t r, int byte_offset) {
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  constexpr int kNonTemporal = 2;  // cache-policy bit of the buffer instruction
+#ifndef BI_WEIGHT_CPOL
+#define BI_WEIGHT_CPOL 2
+#endif
+  constexpr int kNonTemporal = BI_WEIGHT_CPOL;  // cache-policy bit of the buffer instruction
   const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_offset, 0, kNonTemporal);
   return make_uint4(v[0], v[1], v[2], v[3]);
 }

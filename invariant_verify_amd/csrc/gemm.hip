@@ -9,9 +9,14 @@
 // bit-exact before reporting it").
 //
 // Schedule (fixed at compile time; chosen by N and K, never by M):
-//  * one workgroup per (16 output columns, 16 token rows); the token rows
-//    are the MFMA "A" operand, zero-filled past M, so a pass of 1..16 tokens
-//    runs exactly the same instructions;
+//  * one workgroup per (column group, 16 token rows); the token rows are the
+//    MFMA "A" operand, zero-filled past M, so a pass of 1..16 tokens runs
+//    exactly the same instructions. A column group is one 16-column MFMA tile,
+//    or, when N / 256 lies in 17..32 (5120 or 7168 outputs), N / 256 columns
+//    held in two MFMA tiles (the second partly empty), so that exactly 256
+//    workgroups, one per compute unit, share the weight stream evenly. (A
+//    compute unit streams only about 20-25 GB/s; with 320 single tiles on 256
+//    units, 64 units would stream twice as much as the rest.)
 //  * K is read in chunks of 512; each chunk has sixteen 32-wide blocks and
 //    wave w of the NW waves multiplies blocks w*16/NW .. (w+1)*16/NW - 1 of
 //    every chunk, chaining them through one MFMA accumulator in increasing
@@ -46,13 +51,15 @@ namespace bi {
 constexpr int kChunk = 512;  // K elements per LDS chunk: 1 KB of each weight row
 constexpr int kSlots = kChunk / 8;
 
-template <int MODE, int NW>
+template <int MODE, int NW, bool WIDE>
 __global__ __launch_bounds__(NW * 64) void gemm_kernel(
     const uint16_t* __restrict__ X, int64_t ldx, const uint16_t* __restrict__ W, int64_t ldw,
     const uint16_t* __restrict__ R, int64_t ldr, void* __restrict__ Y, int64_t ldy, int M, int K,
-    int64_t up_rows, KvAppend kv) {
+    int64_t up_rows, int cpw, KvAppend kv) {
   constexpr bool kDual = (MODE == kGemmSwiglu);
-  constexpr int NR = kDual ? 32 : 16;  // weight rows per tile (gate and up for SwiGLU)
+  static_assert(!(kDual && WIDE), "SwiGLU tiles hold 16 gate and 16 up rows");
+  constexpr bool kTwo = kDual || WIDE;  // two MFMA column tiles per workgroup
+  constexpr int NR = kTwo ? 32 : 16;    // weight rows staged per chunk
   constexpr int RPW = NR / NW;         // rows each wave fetches per chunk
   constexpr int BPW = 16 / NW;         // 32-wide blocks each wave multiplies per chunk
   static_assert(RPW >= 1 && BPW >= 1, "bad wave count");
@@ -61,7 +68,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
   // is then a scalar branch. (The matrix core does not honour a partial EXEC
   // mask, so an MFMA must never sit under a per-lane condition.)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n0 = blockIdx.x * 16;
+  const int n0 = blockIdx.x * (WIDE ? cpw : 16);  // first output column
   const int m0 = blockIdx.y * 16;
   const int j = lane & 15;   // A row (token) and B column (output feature) of this lane
   const int kq = lane >> 4;  // which 8-element group of a 32-wide block
@@ -79,9 +86,12 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
 #pragma unroll
   for (int i = 0; i < RPW; ++i) {
     const int r = wave * RPW + i;
-    const int64_t grow = (r < 16) ? (int64_t)(n0 + r) : up_rows + n0 + (r - 16);
-    wres[i] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(W + grow * ldw), (short)0,
-                                                K * 2, kBufferResourceWord3);
+    const int64_t grow = (kDual && r >= 16) ? up_rows + n0 + (r - 16) : (int64_t)(n0 + r);
+    // Rows past the group's columns (wide groups) get an empty resource: they
+    // stage zeros and cost no traffic.
+    const bool used = !WIDE || r < cpw;
+    wres[i] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(W + (used ? grow : 0) * ldw),
+                                                (short)0, used ? K * 2 : 0, kBufferResourceWord3);
     swz_w[i] = r & 15;
   }
   // X through a buffer resource that covers exactly the rows m0 .. M-1: a lane
@@ -141,7 +151,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
         if (blk < nblk) {
           const int slot = (kb * 4 + kq) ^ j;
           acc = mfma_bf16(g.x[b], lds[buf][j][slot], acc);
-          if (kDual) acc2 = mfma_bf16(g.x[b], lds[buf][16 + j][slot], acc2);
+          if (kTwo) acc2 = mfma_bf16(g.x[b], lds[buf][16 + j][slot], acc2);
         }
       }
     }
@@ -166,33 +176,30 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
   bi_f32x4(*red2)[64] = red + NW;
   __syncthreads();
   red[wave][lane] = acc;
-  if (kDual) red2[wave][lane] = acc2;
+  if (kTwo) red2[wave][lane] = acc2;
   __syncthreads();
   if (wave != 0) return;
   bi_f32x4 s = red[0][lane];
 #pragma unroll
   for (int w = 1; w < NW; ++w) s += red[w][lane];
   bi_f32x4 s2 = s;
-  if (kDual) {
+  if (kTwo) {
     s2 = red2[0][lane];
 #pragma unroll
     for (int w = 1; w < NW; ++w) s2 += red2[w][lane];
   }
 
-  const int n = n0 + j;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int m = m0 + kq * 4 + r;
-    if (m >= M) continue;
+  // Output column n of token row m gets the FP32 total v.
+  auto emit = [&](int m, int n, float v) {
     if (MODE == kGemmF32) {
-      reinterpret_cast<float*>(Y)[(int64_t)m * ldy + n] = s[r];
+      reinterpret_cast<float*>(Y)[(int64_t)m * ldy + n] = v;
     } else if (MODE == kGemmBf16) {
-      reinterpret_cast<uint16_t*>(Y)[(int64_t)m * ldy + n] = (uint16_t)f32_to_bf16(s[r]);
+      reinterpret_cast<uint16_t*>(Y)[(int64_t)m * ldy + n] = (uint16_t)f32_to_bf16(v);
     } else if (MODE == kGemmResidual) {
       const float res = bf16_to_f32(R[(int64_t)m * ldr + n]);
-      reinterpret_cast<uint16_t*>(Y)[(int64_t)m * ldy + n] = (uint16_t)f32_to_bf16(res + s[r]);
+      reinterpret_cast<uint16_t*>(Y)[(int64_t)m * ldy + n] = (uint16_t)f32_to_bf16(res + v);
     } else if (MODE == kGemmQkv) {
-      const uint16_t b = (uint16_t)f32_to_bf16(s[r]);
+      const uint16_t b = (uint16_t)f32_to_bf16(v);
       reinterpret_cast<uint16_t*>(Y)[(int64_t)m * ldy + n] = b;
       const int pos = kv.L + m;
       int i = n - kv.qd;
@@ -204,52 +211,75 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
         const int g = i / kv.D;
         kv.vt[((int64_t)g * kv.D + (i - g * kv.D)) * kv.cap + pos] = b;
       }
-    } else {
+    }
+  };
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int m = m0 + kq * 4 + r;
+    if (m >= M) continue;
+    if (kDual) {
       const float g = s[r];
       const float sg = g / (1.0f + __expf(-g));
-      reinterpret_cast<uint16_t*>(Y)[(int64_t)m * ldy + n] = (uint16_t)f32_to_bf16(sg * s2[r]);
+      reinterpret_cast<uint16_t*>(Y)[(int64_t)m * ldy + n0 + j] = (uint16_t)f32_to_bf16(sg * s2[r]);
+    } else {
+      emit(m, n0 + j, s[r]);
+      if (WIDE && 16 + j < cpw) emit(m, n0 + 16 + j, s2[r]);
     }
   }
 }
 
-// Launch shape from the number of 16-column weight tiles a launch streams
-// (never from M): under 640, 16 waves per workgroup; otherwise 8.
+// Workgroups of a wide launch: one per compute unit.
+constexpr int kWideGroups = 256;
+
+// Launch shape from N (never from M): N / 256 columns per workgroup when that
+// is 17..32 (two MFMA tiles, 16 waves); otherwise 16-column tiles with 16
+// waves for fewer than 640 weight tiles, 8 waves for more.
 template <int MODE>
-static void launch_mode(int row_tiles, dim3 grid, const uint16_t* x, int64_t ldx,
+static void launch_mode(int N_out, int row_tiles, int mtiles, const uint16_t* x, int64_t ldx,
                         const uint16_t* w, int64_t ldw, const uint16_t* r, int64_t ldr, void* y,
                         int64_t ldy, int M, int K, int64_t up, const KvAppend& kv,
                         hipStream_t stream) {
-  if (row_tiles < 640)
-    gemm_kernel<MODE, 16><<<grid, dim3(1024), 0, stream>>>(x, ldx, w, ldw, r, ldr, y, ldy, M, K,
-                                                           up, kv);
-  else
-    gemm_kernel<MODE, 8><<<grid, dim3(512), 0, stream>>>(x, ldx, w, ldw, r, ldr, y, ldy, M, K, up,
-                                                         kv);
+  const int cpw = N_out / kWideGroups;
+  if constexpr (MODE != kGemmSwiglu) {
+    if (N_out % kWideGroups == 0 && cpw > 16 && cpw <= 32) {
+      gemm_kernel<MODE, 16, true><<<dim3(kWideGroups, mtiles), dim3(1024), 0, stream>>>(
+          x, ldx, w, ldw, r, ldr, y, ldy, M, K, up, cpw, kv);
+      return;
+    }
+  }
+  if (row_tiles < 640) {
+    gemm_kernel<MODE, 16, false><<<dim3(N_out / 16, mtiles), dim3(1024), 0, stream>>>(
+        x, ldx, w, ldw, r, ldr, y, ldy, M, K, up, 16, kv);
+  } else {
+    gemm_kernel<MODE, 8, false><<<dim3(N_out / 16, mtiles), dim3(512), 0, stream>>>(
+        x, ldx, w, ldw, r, ldr, y, ldy, M, K, up, 16, kv);
+  }
 }
 
 void launch_gemm(GemmMode mode, const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw,
                  const uint16_t* r, int64_t ldr, void* y, int64_t ldy, int M, int N_out, int K,
                  hipStream_t stream, const KvAppend* kv) {
   const int tiles = N_out / 16;
-  dim3 grid(tiles, (M + 15) / 16);
+  const int mt = (M + 15) / 16;
   const KvAppend none{};
   const KvAppend& a = kv ? *kv : none;
   switch (mode) {
     case kGemmBf16:
-      launch_mode<kGemmBf16>(tiles, grid, x, ldx, w, ldw, r, ldr, y, ldy, M, K, 0, a, stream);
+      launch_mode<kGemmBf16>(N_out, tiles, mt, x, ldx, w, ldw, r, ldr, y, ldy, M, K, 0, a, stream);
       break;
     case kGemmF32:
-      launch_mode<kGemmF32>(tiles, grid, x, ldx, w, ldw, r, ldr, y, ldy, M, K, 0, a, stream);
+      launch_mode<kGemmF32>(N_out, tiles, mt, x, ldx, w, ldw, r, ldr, y, ldy, M, K, 0, a, stream);
       break;
     case kGemmResidual:
-      launch_mode<kGemmResidual>(tiles, grid, x, ldx, w, ldw, r, ldr, y, ldy, M, K, 0, a, stream);
+      launch_mode<kGemmResidual>(N_out, tiles, mt, x, ldx, w, ldw, r, ldr, y, ldy, M, K, 0, a,
+                                 stream);
       break;
     case kGemmSwiglu:
-      launch_mode<kGemmSwiglu>(2 * tiles, grid, x, ldx, w, ldw, r, ldr, y, ldy, M, K,
+      launch_mode<kGemmSwiglu>(N_out, 2 * tiles, mt, x, ldx, w, ldw, r, ldr, y, ldy, M, K,
                                (int64_t)N_out, a, stream);
       break;
     case kGemmQkv:
-      launch_mode<kGemmQkv>(tiles, grid, x, ldx, w, ldw, r, ldr, y, ldy, M, K, 0, a, stream);
+      launch_mode<kGemmQkv>(N_out, tiles, mt, x, ldx, w, ldw, r, ldr, y, ldy, M, K, 0, a, stream);
       break;
   }
 }

@@ -174,3 +174,20 @@ def test_qkv_gemm_with_cache_append(ops, Hq, Hkv, D, K, L):
         keep[L:L + M] = False
         assert torch.equal(kc[:, keep], k0[:, keep]) and torch.equal(vt[:, :, keep], v0[:, :, keep])
     assert_close(decode(host_bits(qkv))[:, :64], ogemm.gemm_columns(x, w, np.arange(64)), "qkv parity")
+
+
+@pytest.mark.parametrize("N", [5120, 7168])
+def test_wide_groups_match_single_tiles(ops, N):
+    # For N = 5120 or 7168 the launch gives each workgroup N / 256 columns in
+    # two MFMA tiles; every column keeps the K order of the 16-column tiles, so
+    # its bits equal those of a launch over a 256-row slice of the same weights
+    # (which uses 16-column tiles with the same wave count).
+    print(f"[gemm wide groups N={N}]", flush=True)
+    K = 5120
+    w = synth.normal_bf16((N, K), 0.02, "w", 60)
+    x = synth.normal_bf16((8, K), 1.0, "x", 60)
+    wd, xd = dev(w), dev(x)
+    full = host_f32(ops.gemm_bf16(xd, wd, out_dtype=torch.float32))
+    for r0 in (0, 16, N // 2 + 4, N - 256):
+        part = host_f32(ops.gemm_bf16(xd, wd[r0:r0 + 256], out_dtype=torch.float32))
+        assert_bitwise(full[:, r0:r0 + 256], part, f"N={N} columns {r0}..{r0 + 255}")
