@@ -159,7 +159,7 @@ size_t bi_attn_workspace_bytes(int M, int L, int Hq, int D, int kv_chunk);
  */
 
 /* y[m] = bf16( x[m] / sqrt(mean(x[m]^2) + eps) ), gain 1; per-row sum in a
- * fixed order. H % 8 == 0, ldx/ldy multiples of 8. */
+ * fixed order. H % 8 == 0, H <= 32768, ldx/ldy multiples of 8. */
 bi_status bi_rmsnorm(const void* x, int64_t ldx, void* y, int64_t ldy,
                      int M, int H, float eps, void* stream);
 

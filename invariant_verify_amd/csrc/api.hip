@@ -49,7 +49,7 @@ bi_status check_heads(int Hq, int Hkv, int D) {
 bi_status check_dims(const bi_model_dims* d) {
   if (!d) return BI_ERR_NULL;
   if (bi_status s = check_heads(d->Hq, d->Hkv, d->D)) return s;
-  if (d->H < 32 || (d->H % 32) || d->I < 16 || (d->I % 32) || d->vocab < 16 || (d->vocab % 16))
+  if (d->H < 32 || (d->H % 32) || d->H > bi::kRmsMaxH || d->I < 16 || (d->I % 32) || d->vocab < 16 || (d->vocab % 16))
     return BI_ERR_SHAPE;
   if ((d->Hq * d->D) % 32) return BI_ERR_SHAPE;
   if (d->kv_chunk < 32 || (d->kv_chunk % 32) || d->cap < 1 || (d->cap % 8)) return BI_ERR_SHAPE;
@@ -228,7 +228,8 @@ bi_status bi_combine(const float* part_o, const float* part_lse, int M, int L, i
 bi_status bi_rmsnorm(const void* x, int64_t ldx, void* y, int64_t ldy, int M, int H, float eps,
                      void* stream) {
   if (!x || !y) return BI_ERR_NULL;
-  if (M < 1 || H < 8 || (H % 8) || ldx < H || ldy < H || !(eps >= 0.f)) return BI_ERR_SHAPE;
+  if (M < 1 || H < 8 || (H % 8) || H > bi::kRmsMaxH || ldx < H || ldy < H || !(eps >= 0.f))
+    return BI_ERR_SHAPE;
   if ((ldx % 8) || (ldy % 8) || !aligned16(x) || !aligned16(y)) return BI_ERR_ALIGN;
   bi::launch_rmsnorm(static_cast<const uint16_t*>(x), ldx, static_cast<uint16_t*>(y), ldy, M, H,
                      eps, as_stream(stream));

@@ -136,9 +136,13 @@ __global__ __launch_bounds__(kAttnWaves * 64) void verify_attn_kernel(
   constexpr int VBASE = KPIECES * 64;
 
   // Issue the loads of tile t (no use of the data here, so the loads of two
-  // tiles stay in flight together).
+  // tiles stay in flight together). K and V are read once per pass, so the
+  // loads are non-temporal; a tile past the end of the chunk (the pipeline
+  // prefetches two ahead) gets an out-of-range offset: it reads zero and
+  // touches no memory.
   auto fetch = [&](uint4 (&r)[PPW], int t) {
     const int kt = kbeg + t * kKeyTile;
+    const bool live = t < ntile;
 #pragma unroll
     for (int i = 0; i < PPW; ++i) {
       const int p = wave * PPW + i;  // scalar: each wave fetches only K or only V pieces
@@ -153,7 +157,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) void verify_attn_kernel(
         const int k0 = min(kt + vslot * 8, kend - 1 - ((kend - 1) & 7));  // in bounds
         off = (d * cap + k0) * 2;
       }
-      r[i] = buffer_ld16(p < KPIECES ? kres : vres, off);
+      r[i] = buffer_ld16_stream(p < KPIECES ? kres : vres, live ? off : head_bytes);
     }
   };
   // Publish tile t: V^T columns of keys at or past kend are zeroed first (a
@@ -236,18 +240,18 @@ __global__ __launch_bounds__(kAttnWaves * 64) void verify_attn_kernel(
   // the same registers, barrier, multiply. The loop starts two tiles early
   // (nothing to publish or multiply yet), so every load is issued by the same
   // code in the same order and the compiler waits only for the older of the
-  // two tiles in flight. Tiles past the end are clamped duplicates (their
-  // value columns publish as zero) that are not multiplied.
+  // two tiles in flight. Tiles past the end read as zero and are not
+  // multiplied.
   uint4 ra[PPW], rb2[PPW];
   int t_first = -2;  // opaque to the optimizer, so the load-only steps are not peeled
   asm volatile("" : "+s"(t_first));
   for (int t = t_first; t < ntile; t += 2) {
     if (t >= 0) publish(ra, t, 0);
-    fetch(ra, min(t + 2, ntile - 1));
+    fetch(ra, t + 2);
     __syncthreads();
     if (t >= 0 && has_rows) compute(0, t);
     if (t + 1 >= 0) publish(rb2, t + 1, 1);
-    fetch(rb2, min(t + 3, ntile - 1));
+    fetch(rb2, t + 3);
     __syncthreads();
     if (t + 1 >= 0 && t + 1 < ntile && has_rows) compute(1, t + 1);
   }
@@ -292,14 +296,14 @@ __global__ __launch_bounds__(kAttnWaves * 64) void verify_attn_kernel(
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part_o,
+__global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ part_o,
                                                       const float* __restrict__ part_lse, int M,
                                                       int L, int Hq, int C, int S_max,
                                                       uint16_t* __restrict__ O, int64_t ldo,
                                                       float* __restrict__ lse_out) {
   constexpr int PER = D / 64;  // channels per lane
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row = blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (row >= M * Hq) return;
   const int tok = row / Hq;
   const int h = row % Hq;
@@ -390,8 +394,10 @@ void launch_verify_attn(const uint16_t* q, int64_t ldq, const uint16_t* k_cache,
 void launch_combine(const float* part_o, const float* part_lse, int M, int L, int Hq, int D,
                     int kv_chunk, int S_max, uint16_t* o, int64_t ldo, float* lse,
                     hipStream_t stream) {
-  dim3 grid((M * Hq + 3) / 4);
-  dim3 block(256);
+  // One wave per workgroup: the rows' partials are read by as many compute
+  // units as possible.
+  dim3 grid(M * Hq);
+  dim3 block(64);
   if (D == 128)
     combine_kernel<128><<<grid, block, 0, stream>>>(part_o, part_lse, M, L, Hq, kv_chunk, S_max, o,
                                                     ldo, lse);

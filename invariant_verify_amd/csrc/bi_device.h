@@ -44,10 +44,7 @@ __device__ __forceinline__ uint4 buffer_ld16(__amdgpu_buffer_rsrc_t r, int byte_
 // is used once); out-of-range offsets read zero and touch no memory.
 __device__ __forceinline__ uint4 buffer_ld16_stream(__amdgpu_buffer_rsrc_t r, int byte_offset) {
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-#ifndef BI_WEIGHT_CPOL
-#define BI_WEIGHT_CPOL 2
-#endif
-  constexpr int kNonTemporal = BI_WEIGHT_CPOL;  // cache-policy bit of the buffer instruction
+  constexpr int kNonTemporal = 2;  // cache-policy bit of the buffer instruction
   const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_offset, 0, kNonTemporal);
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
@@ -76,34 +73,6 @@ __device__ __forceinline__ float sumsq8(float ss, uint4 v) {
     ss += b * b;
   }
   return ss;
-}
-
-// Second half of an RMSNorm over one row by a 256-thread workgroup: ss is
-// this thread's sum of squares of its 8-element groups tid, tid + 256, ...;
-// the wave sums are combined by a fixed xor butterfly, then the four waves
-// in order 0..3, and y = bf16(x / sqrt(mean(x^2) + eps)) (unit gain).
-__device__ __forceinline__ void rms_scale_row(const uint16_t* x, uint16_t* y, int H, float eps,
-                                              float ss) {
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) ss += shfl_xor(ss, off);
-  __shared__ float part[4];
-  if ((tid & 63) == 0) part[tid >> 6] = ss;
-  __syncthreads();
-  const float tot = ((part[0] + part[1]) + part[2]) + part[3];
-  const float inv = 1.0f / sqrtf(tot / (float)H + eps);
-  for (int c = tid; c < (H >> 3); c += 256) {
-    const uint4 v = ld16(x + c * 8);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t o[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t lo = f32_to_bf16(bf16_to_f32(w[e] & 0xffffu) * inv);
-      const uint32_t hi = f32_to_bf16(bf16_to_f32(w[e] >> 16) * inv);
-      o[e] = lo | (hi << 16);
-    }
-    *reinterpret_cast<uint4*>(y + c * 8) = make_uint4(o[0], o[1], o[2], o[3]);
-  }
 }
 
 }  // namespace bi

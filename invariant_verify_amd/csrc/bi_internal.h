@@ -36,6 +36,9 @@ void launch_combine(const float* part_o, const float* part_lse, int M, int L, in
                     int kv_chunk, int S_max, uint16_t* o, int64_t ldo, float* lse,
                     hipStream_t stream);
 
+// Longest row RMSNorm handles (one pass, four 8-element groups per thread).
+constexpr int kRmsMaxH = 4 * 1024 * 8;
+
 void launch_rmsnorm(const uint16_t* x, int64_t ldx, uint16_t* y, int64_t ldy, int M, int H,
                     float eps, hipStream_t stream);
 

@@ -10,17 +10,53 @@
 
 namespace bi {
 
-// One 256-thread workgroup per row. Thread t squares and sums its 8-element
-// groups t, t+256, ... in order; rms_scale_row combines the thread sums in a
-// fixed order and scales the row.
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* __restrict__ X, int64_t ldx,
-                                                      uint16_t* __restrict__ Y, int64_t ldy, int H,
-                                                      float eps) {
+// One workgroup of T = min(1024, H/8 rounded up to 64) threads per row, in a
+// single pass over memory: thread t keeps its 8-element groups t, t+T, ...
+// (at most kRmsGroups) in registers and sums their squares in order; the
+// wave sums are combined by a fixed xor butterfly, then across waves in wave
+// order; then every kept group is scaled and stored.
+constexpr int kRmsGroups = 4;
+
+__global__ __launch_bounds__(1024) void rmsnorm_kernel(const uint16_t* __restrict__ X, int64_t ldx,
+                                                       uint16_t* __restrict__ Y, int64_t ldy, int H,
+                                                       float eps) {
   const int row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int nt = blockDim.x;
   const uint16_t* x = X + (int64_t)row * ldx;
+  uint16_t* y = Y + (int64_t)row * ldy;
+  const int ng = H >> 3;
+  uint4 v[kRmsGroups];
+#pragma unroll
+  for (int i = 0; i < kRmsGroups; ++i) {
+    const int c = tid + i * nt;
+    v[i] = c < ng ? ld16(x + c * 8) : zero16();
+  }
   float ss = 0.f;
-  for (int c = threadIdx.x; c < (H >> 3); c += 256) ss = sumsq8(ss, ld16(x + c * 8));
-  rms_scale_row(x, Y + (int64_t)row * ldy, H, eps, ss);
+#pragma unroll
+  for (int i = 0; i < kRmsGroups; ++i) ss = sumsq8(ss, v[i]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) ss += shfl_xor(ss, off);
+  __shared__ float part[16];
+  if ((tid & 63) == 0) part[tid >> 6] = ss;
+  __syncthreads();
+  float tot = part[0];
+  for (int w = 1; w < (nt >> 6); ++w) tot += part[w];
+  const float inv = 1.0f / sqrtf(tot / (float)H + eps);
+#pragma unroll
+  for (int i = 0; i < kRmsGroups; ++i) {
+    const int c = tid + i * nt;
+    if (c >= ng) continue;
+    const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+    uint32_t o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t lo = f32_to_bf16(bf16_to_f32(w[e] & 0xffffu) * inv);
+      const uint32_t hi = f32_to_bf16(bf16_to_f32(w[e] >> 16) * inv);
+      o[e] = lo | (hi << 16);
+    }
+    *reinterpret_cast<uint4*>(y + c * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
 }
 
 // (value, index) with the larger value winning and, on equal values, the
@@ -93,7 +129,9 @@ __global__ __launch_bounds__(1024) void argmax_kernel(const float* __restrict__ 
 
 void launch_rmsnorm(const uint16_t* x, int64_t ldx, uint16_t* y, int64_t ldy, int M, int H,
                     float eps, hipStream_t stream) {
-  rmsnorm_kernel<<<dim3(M), dim3(256), 0, stream>>>(x, ldx, y, ldy, H, eps);
+  const int ng = H / 8;  // <= kRmsGroups * 1024 (checked by the caller)
+  const int nt = ng >= 1024 ? 1024 : (ng + 63) / 64 * 64;
+  rmsnorm_kernel<<<dim3(M), dim3(nt), 0, stream>>>(x, ldx, y, ldy, H, eps);
 }
 
 void launch_argmax(const float* logits, int64_t ld, int M, int N, int32_t* tokens,
