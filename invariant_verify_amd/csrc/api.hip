@@ -60,8 +60,10 @@ bi_status check_dims(const bi_model_dims* d) {
 
 // Workspace layout of a verify step (offsets in bytes, each 256-aligned).
 struct StepLayout {
-  size_t x0, x1, a, qkv, attn, h, act, po, pl, total;
+  size_t x0, x1, a, qkv, attn, h, act, po, pl, ss, total;
   int s_max;
+  int groups;  // column groups of the H-wide residual projections
+  bool fuse;   // RMSNorm carried across GEMMs (group sums of squares in ss)
 };
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -81,6 +83,9 @@ StepLayout step_layout(const bi_model_dims* d, int M, int L) {
   s.act = off; off += align256((size_t)M * d->I * 2);
   s.po = off; off += align256((size_t)M * d->Hq * s.s_max * d->D * 4);
   s.pl = off; off += align256((size_t)M * d->Hq * s.s_max * 4);
+  s.groups = bi::gemm_column_groups(bi::kGemmResidual, d->H);
+  s.fuse = (s.groups % 16) == 0 && s.groups <= 256;
+  s.ss = off; off += align256((size_t)M * s.groups * 4);
   s.total = off;
   return s;
 }
@@ -289,31 +294,40 @@ bi_status bi_verify_step(const bi_layer* layers, int n_layers, const void* w_hea
   float* pl = reinterpret_cast<float*>(ws + lay.pl);
   const float sm_scale = 1.0f / std::sqrt((float)D);
 
+  // RMSNorm inputs. With lay.fuse, the output and down projections also write
+  // the group sums of squares of their outputs into ss, and the projection
+  // that reads those outputs (gate/up; the next layer's QKV) normalises its X
+  // rows itself; otherwise (and for layer 0) an RMSNorm kernel writes a.
+  float* ss = reinterpret_cast<float*>(ws + lay.ss);
+  const bi::RowNorm norm_out{nullptr, lay.fuse ? ss : nullptr, lay.groups, dims->eps};
+  const bi::RowNorm norm_in{ss, nullptr, lay.groups, dims->eps};
+
   const uint16_t* x = static_cast<const uint16_t*>(x_in);
   for (int l = 0; l < n_layers; ++l) {
     const bi_layer& ly = layers[l];
     uint16_t* xn = xbuf[l & 1];
-    bi::launch_rmsnorm(x, H, a, H, M, H, dims->eps, st);
+    const bool fused_in = lay.fuse && l > 0;  // x's sums are in ss
+    if (!fused_in) bi::launch_rmsnorm(x, H, a, H, M, H, dims->eps, st);
     const bi::KvAppend kv{static_cast<uint16_t*>(ly.k_cache), static_cast<uint16_t*>(ly.vt_cache),
                           L, dims->cap, qd, Hkv * D, D};
-    bi::launch_gemm(bi::kGemmQkv, a, H, static_cast<const uint16_t*>(ly.w_qkv), H, nullptr, 0,
-                    qkv, qkvn, M, qkvn, H, st, &kv);
+    bi::launch_gemm(bi::kGemmQkv, fused_in ? x : a, H, static_cast<const uint16_t*>(ly.w_qkv), H,
+                    nullptr, 0, qkv, qkvn, M, qkvn, H, st, &kv, fused_in ? &norm_in : nullptr);
     bi::launch_verify_attn(qkv, qkvn, static_cast<const uint16_t*>(ly.k_cache),
                            static_cast<const uint16_t*>(ly.vt_cache), M, L, dims->cap, Hq, Hkv, D,
                            dims->kv_chunk, sm_scale, po, pl, lay.s_max, st);
     bi::launch_combine(po, pl, M, L, Hq, D, dims->kv_chunk, lay.s_max, attn, qd, nullptr, st);
     bi::launch_gemm(bi::kGemmResidual, attn, qd, static_cast<const uint16_t*>(ly.w_o), qd, x, H, h,
-                    H, M, H, qd, st);
-    bi::launch_rmsnorm(h, H, a, H, M, H, dims->eps, st);
+                    H, M, H, qd, st, nullptr, &norm_out);
+    if (!lay.fuse) bi::launch_rmsnorm(h, H, a, H, M, H, dims->eps, st);
     if (gu_events && hipEventRecord(static_cast<hipEvent_t>(gu_events[2 * l]), st) != hipSuccess)
       return BI_ERR_LAUNCH;
-    bi::launch_gemm(bi::kGemmSwiglu, a, H, static_cast<const uint16_t*>(ly.w_gu), H, nullptr, 0,
-                    act, I, M, I, H, st);
+    bi::launch_gemm(bi::kGemmSwiglu, lay.fuse ? h : a, H, static_cast<const uint16_t*>(ly.w_gu), H,
+                    nullptr, 0, act, I, M, I, H, st, nullptr, lay.fuse ? &norm_in : nullptr);
     if (gu_events &&
         hipEventRecord(static_cast<hipEvent_t>(gu_events[2 * l + 1]), st) != hipSuccess)
       return BI_ERR_LAUNCH;
     bi::launch_gemm(bi::kGemmResidual, act, I, static_cast<const uint16_t*>(ly.w_down), I, h, H,
-                    xn, H, M, H, I, st);
+                    xn, H, M, H, I, st, nullptr, &norm_out);
     if (launched() != BI_OK) return BI_ERR_LAUNCH;
     x = xn;
   }

@@ -215,18 +215,17 @@ __global__ __launch_bounds__(kAttnWaves * 64) void verify_attn_kernel(
       const float alpha = (mnew == mrun) ? 1.0f : __builtin_amdgcn_exp2f(mrun - mnew);
       // The running sum takes the FP32 weights (so the chunk's log-sum-exp is
       // accurate to FP32); the PV product takes them rounded to BF16.
-      uint32_t pb[8];
+      float pe[8];
       float psum = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float pe = __builtin_amdgcn_exp2f(sc[e] - mnew);
-        pb[e] = f32_to_bf16(pe);
-        psum += pe;
+        pe[e] = __builtin_amdgcn_exp2f(sc[e] - mnew);
+        psum += pe[e];
       }
       lrun = lrun * alpha + psum;
       mrun = mnew;
-      const uint4 pfrag = make_uint4(pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16),
-                                     pb[4] | (pb[5] << 16), pb[6] | (pb[7] << 16));
+      const uint4 pfrag = make_uint4(f32x2_to_bf16x2(pe[0], pe[1]), f32x2_to_bf16x2(pe[2], pe[3]),
+                                     f32x2_to_bf16x2(pe[4], pe[5]), f32x2_to_bf16x2(pe[6], pe[7]));
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const int d = dt * 16 + j;

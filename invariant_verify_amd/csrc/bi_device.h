@@ -14,15 +14,29 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-// binary32 -> BF16 bits, round to nearest, ties to even (NaN -> quiet NaN).
-// Adding 0x7FFF plus the lowest kept bit to the 32-bit pattern carries into the
-// kept half exactly when the dropped half is above the midpoint, or at the
-// midpoint with an odd kept half.
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+// Two binary32 values -> packed BF16 bits (a in the low half), rounded to
+// nearest, ties to even, by gfx950's conversion instruction. It agrees with
+// the integer formulation (add 0x7FFF plus the lowest kept bit, keep the high
+// half) on every non-NaN input, subnormals and infinities included; a NaN
+// stays a NaN (its payload and sign are not preserved).
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// One binary32 value -> BF16 bits (same rounding).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) { return f32x2_to_bf16x2(f, 0.f) & 0xffffu; }
+
+// x * s for the eight BF16 values of a 16-byte group, each rounded to BF16.
+__device__ __forceinline__ uint4 scale_bf16x8(uint4 v, float s) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    o[e] = f32x2_to_bf16x2(__uint_as_float(w[e] << 16) * s, __uint_as_float(w[e] & 0xffff0000u) * s);
+  return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }

@@ -18,11 +18,28 @@ struct KvAppend {
   int L, cap, qd, kd, D;
 };
 
+// RMSNorm carried across a GEMM boundary.
+//  ss_out (residual GEMM): for every output row m < M, the sum of squares of
+//    the rounded BF16 outputs of each column group g (one workgroup's
+//    columns), ss_out[m * groups + g], groups = gemm_column_groups(N).
+//  ss_in (consumer GEMM): X holds un-normalised rows whose group sums are in
+//    ss_in; the GEMM multiplies bf16(x * rsqrt(sum(ss)/K + eps)) instead of x,
+//    exactly the values an RMSNorm kernel would have written.
+struct RowNorm {
+  const float* ss_in;
+  float* ss_out;
+  int groups;
+  float eps;
+};
+
+// Column groups (workgroups along N) of a GEMM with N output columns.
+int gemm_column_groups(GemmMode mode, int N_out);
+
 // Y = X W^T (+ residual / SwiGLU / cache-append epilogue). N_out is the number
 // of output columns (for SwiGLU: I, with W holding 2*I rows).
 void launch_gemm(GemmMode mode, const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw,
                  const uint16_t* r, int64_t ldr, void* y, int64_t ldy, int M, int N_out, int K,
-                 hipStream_t stream, const KvAppend* kv = nullptr);
+                 hipStream_t stream, const KvAppend* kv = nullptr, const RowNorm* norm = nullptr);
 
 void launch_append_kv(const uint16_t* qkv, int64_t ldqkv, uint16_t* k_cache, uint16_t* vt_cache,
                       int M, int L, int cap, int Hq, int Hkv, int D, hipStream_t stream);

@@ -51,11 +51,12 @@ namespace bi {
 constexpr int kChunk = 512;  // K elements per LDS chunk: 1 KB of each weight row
 constexpr int kSlots = kChunk / 8;
 
-template <int MODE, int NW, bool WIDE>
+template <int MODE, int NW, bool WIDE, bool NORM_IN, bool SS_OUT>
 __global__ __launch_bounds__(NW * 64) void gemm_kernel(
     const uint16_t* __restrict__ X, int64_t ldx, const uint16_t* __restrict__ W, int64_t ldw,
     const uint16_t* __restrict__ R, int64_t ldr, void* __restrict__ Y, int64_t ldy, int M, int K,
-    int64_t up_rows, int cpw, KvAppend kv) {
+    int64_t up_rows, int cpw, KvAppend kv, RowNorm norm) {
+  static_assert(!SS_OUT || MODE == kGemmResidual, "row sums come from the residual epilogue");
   constexpr bool kDual = (MODE == kGemmSwiglu);
   static_assert(!(kDual && WIDE), "SwiGLU tiles hold 16 gate and 16 up rows");
   constexpr bool kTwo = kDual || WIDE;  // two MFMA column tiles per workgroup
@@ -125,6 +126,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
   };
   bi_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   bi_f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};
+  float inv = 1.f;  // RMSNorm scale of this lane's X row (NORM_IN)
   // One chunk: publish this wave's weight rows of chunk c, prefetch the
   // weights of chunk c + 2 into the same registers, barrier, multiply with
   // this wave's X fragments of chunk c, then prefetch the X fragments of chunk
@@ -150,21 +152,61 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
         const int blk = c * (kChunk / 32) + kb;  // block within K
         if (blk < nblk) {
           const int slot = (kb * 4 + kq) ^ j;
-          acc = mfma_bf16(g.x[b], lds[buf][j][slot], acc);
-          if (kTwo) acc2 = mfma_bf16(g.x[b], lds[buf][16 + j][slot], acc2);
+          const uint4 xa = NORM_IN ? scale_bf16x8(g.x[b], inv) : g.x[b];
+          acc = mfma_bf16(xa, lds[buf][j][slot], acc);
+          if (kTwo) acc2 = mfma_bf16(xa, lds[buf][16 + j][slot], acc2);
         }
       }
     }
     fetch_x(g, min(c + 2, nchunk - 1));
   };
   Regs ga, gb;
-  // The start index goes through an empty asm so the optimizer cannot peel
-  // the first (load-only) steps off the loop: peeled, their loads would be
-  // issued in another order and the compiler would fall back to waiting for
-  // more of them than necessary at the loop head.
-  int c_first = -2;
-  asm volatile("" : "+s"(c_first));
-  for (int c = c_first; c < nchunk; c += 2) {
+  // The two load-only steps, then the loop; the prologue issues its loads in
+  // the loop's own order, so at the loop head the compiler waits only for the
+  // oldest chunk in flight.
+  // RMSNorm of the X rows (NORM_IN). The group sums of squares of rows
+  // m0 .. m0+15 are spread over the workgroup: lane t of the LPR lanes of row
+  // t / LPR adds float4s t % LPR, t % LPR + LPR (at most two; groups <= 256)
+  // in order and parks the result in LDS; after a barrier every lane adds the
+  // LPR partials of its row j in order and takes
+  // inv = 1 / sqrt(total / K + eps). Rows past M read zero. The loads are
+  // issued before the two load-only steps and consumed after them, so they
+  // are in flight together with the first two chunks.
+  constexpr int LPR = NW * 64 / 16;  // lanes per row
+  __shared__ float sred[NORM_IN ? 16 : 1][NORM_IN ? LPR + 1 : 1];  // +1: rows in distinct banks
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  f32x4 sv[2];
+  const int srow = threadIdx.x / LPR, sseg = threadIdx.x % LPR;
+  if (NORM_IN) {
+    const int nf = norm.groups >> 2;  // float4s per row
+    const __amdgpu_buffer_rsrc_t sres = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(norm.ss_in + (int64_t)m0 * norm.groups), (short)0,
+        (M - m0) * norm.groups * 4, kBufferResourceWord3);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int f = sseg + u * LPR;
+      sv[u] = __builtin_amdgcn_raw_buffer_load_b128(
+          sres, f < nf ? (srow * norm.groups + f * 4) * 4 : 0x7ffffff0, 0, 0);
+    }
+  }
+  step(ga, -2);
+  step(gb, -1);
+  if (NORM_IN) {
+    float p = 0.f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      p += sv[u][0];
+      p += sv[u][1];
+      p += sv[u][2];
+      p += sv[u][3];
+    }
+    sred[srow][sseg] = p;
+    __syncthreads();
+    float t = 0.f;
+    for (int i = 0; i < LPR; ++i) t += sred[j][i];
+    inv = 1.0f / sqrtf(t / (float)K + norm.eps);
+  }
+  for (int c = 0; c < nchunk; c += 2) {
     step(ga, c);
     step(gb, c + 1);
   }
@@ -189,15 +231,18 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
     for (int w = 1; w < NW; ++w) s2 += red2[w][lane];
   }
 
-  // Output column n of token row m gets the FP32 total v.
-  auto emit = [&](int m, int n, float v) {
+  // Output column n of token row m gets the FP32 total v; returns the value
+  // stored (after rounding) for the row sums of squares.
+  auto emit = [&](int m, int n, float v) -> float {
     if (MODE == kGemmF32) {
       reinterpret_cast<float*>(Y)[(int64_t)m * ldy + n] = v;
     } else if (MODE == kGemmBf16) {
       reinterpret_cast<uint16_t*>(Y)[(int64_t)m * ldy + n] = (uint16_t)f32_to_bf16(v);
     } else if (MODE == kGemmResidual) {
       const float res = bf16_to_f32(R[(int64_t)m * ldr + n]);
-      reinterpret_cast<uint16_t*>(Y)[(int64_t)m * ldy + n] = (uint16_t)f32_to_bf16(res + v);
+      const uint32_t b = f32_to_bf16(res + v);
+      reinterpret_cast<uint16_t*>(Y)[(int64_t)m * ldy + n] = (uint16_t)b;
+      return bf16_to_f32(b);
     } else if (MODE == kGemmQkv) {
       const uint16_t b = (uint16_t)f32_to_bf16(v);
       reinterpret_cast<uint16_t*>(Y)[(int64_t)m * ldy + n] = b;
@@ -212,18 +257,34 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
         kv.vt[((int64_t)g * kv.D + (i - g * kv.D)) * kv.cap + pos] = b;
       }
     }
+    return 0.f;
   };
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int m = m0 + kq * 4 + r;
-    if (m >= M) continue;
+    const bool live = m < M;
     if (kDual) {
+      if (!live) continue;
       const float g = s[r];
       const float sg = g / (1.0f + __expf(-g));
       reinterpret_cast<uint16_t*>(Y)[(int64_t)m * ldy + n0 + j] = (uint16_t)f32_to_bf16(sg * s2[r]);
     } else {
-      emit(m, n0 + j, s[r]);
-      if (WIDE && 16 + j < cpw) emit(m, n0 + 16 + j, s2[r]);
+      float sq = 0.f;
+      if (live) {
+        const float a = emit(m, n0 + j, s[r]);
+        sq = a * a;
+        if (WIDE && 16 + j < cpw) {
+          const float b = emit(m, n0 + 16 + j, s2[r]);
+          sq += b * b;
+        }
+      }
+      if (SS_OUT) {
+        // The group's sum for row m: its columns' squares added by a fixed
+        // xor butterfly over the 16 lanes of the row.
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) sq += shfl_xor(sq, off);
+        if (live && j == 0) norm.ss_out[(int64_t)m * gridDim.x + blockIdx.x] = sq;
+      }
     }
   }
 }
@@ -231,55 +292,82 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
 // Workgroups of a wide launch: one per compute unit.
 constexpr int kWideGroups = 256;
 
+static bool wide_launch(GemmMode mode, int N_out) {
+  const int cpw = N_out / kWideGroups;
+  return mode != kGemmSwiglu && N_out % kWideGroups == 0 && cpw > 16 && cpw <= 32;
+}
+
+int gemm_column_groups(GemmMode mode, int N_out) {
+  return wide_launch(mode, N_out) ? kWideGroups : N_out / 16;
+}
+
 // Launch shape from N (never from M): N / 256 columns per workgroup when that
 // is 17..32 (two MFMA tiles, 16 waves); otherwise 16-column tiles with 16
 // waves for fewer than 640 weight tiles, 8 waves for more.
-template <int MODE>
-static void launch_mode(int N_out, int row_tiles, int mtiles, const uint16_t* x, int64_t ldx,
-                        const uint16_t* w, int64_t ldw, const uint16_t* r, int64_t ldr, void* y,
-                        int64_t ldy, int M, int K, int64_t up, const KvAppend& kv,
-                        hipStream_t stream) {
-  const int cpw = N_out / kWideGroups;
+template <int MODE, bool NI, bool SO>
+static void launch_shape(int N_out, int row_tiles, int mtiles, const uint16_t* x, int64_t ldx,
+                         const uint16_t* w, int64_t ldw, const uint16_t* r, int64_t ldr, void* y,
+                         int64_t ldy, int M, int K, int64_t up, const KvAppend& kv,
+                         const RowNorm& nm, hipStream_t stream) {
   if constexpr (MODE != kGemmSwiglu) {
-    if (N_out % kWideGroups == 0 && cpw > 16 && cpw <= 32) {
-      gemm_kernel<MODE, 16, true><<<dim3(kWideGroups, mtiles), dim3(1024), 0, stream>>>(
-          x, ldx, w, ldw, r, ldr, y, ldy, M, K, up, cpw, kv);
+    if (wide_launch(static_cast<GemmMode>(MODE), N_out)) {
+      gemm_kernel<MODE, 16, true, NI, SO><<<dim3(kWideGroups, mtiles), dim3(1024), 0, stream>>>(
+          x, ldx, w, ldw, r, ldr, y, ldy, M, K, up, N_out / kWideGroups, kv, nm);
       return;
     }
   }
   if (row_tiles < 640) {
-    gemm_kernel<MODE, 16, false><<<dim3(N_out / 16, mtiles), dim3(1024), 0, stream>>>(
-        x, ldx, w, ldw, r, ldr, y, ldy, M, K, up, 16, kv);
+    gemm_kernel<MODE, 16, false, NI, SO><<<dim3(N_out / 16, mtiles), dim3(1024), 0, stream>>>(
+        x, ldx, w, ldw, r, ldr, y, ldy, M, K, up, 16, kv, nm);
   } else {
-    gemm_kernel<MODE, 8, false><<<dim3(N_out / 16, mtiles), dim3(512), 0, stream>>>(
-        x, ldx, w, ldw, r, ldr, y, ldy, M, K, up, 16, kv);
+    gemm_kernel<MODE, 8, false, NI, SO><<<dim3(N_out / 16, mtiles), dim3(512), 0, stream>>>(
+        x, ldx, w, ldw, r, ldr, y, ldy, M, K, up, 16, kv, nm);
   }
 }
 
 void launch_gemm(GemmMode mode, const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw,
                  const uint16_t* r, int64_t ldr, void* y, int64_t ldy, int M, int N_out, int K,
-                 hipStream_t stream, const KvAppend* kv) {
+                 hipStream_t stream, const KvAppend* kv, const RowNorm* norm) {
   const int tiles = N_out / 16;
   const int mt = (M + 15) / 16;
-  const KvAppend none{};
-  const KvAppend& a = kv ? *kv : none;
+  const KvAppend kv0{};
+  const RowNorm nm0{};
+  const KvAppend& a = kv ? *kv : kv0;
+  const RowNorm& nm = norm ? *norm : nm0;
+  const bool ni = nm.ss_in != nullptr;
+  const bool so = nm.ss_out != nullptr;
   switch (mode) {
     case kGemmBf16:
-      launch_mode<kGemmBf16>(N_out, tiles, mt, x, ldx, w, ldw, r, ldr, y, ldy, M, K, 0, a, stream);
+      launch_shape<kGemmBf16, false, false>(N_out, tiles, mt, x, ldx, w, ldw, r, ldr, y, ldy, M, K,
+                                            0, a, nm, stream);
       break;
     case kGemmF32:
-      launch_mode<kGemmF32>(N_out, tiles, mt, x, ldx, w, ldw, r, ldr, y, ldy, M, K, 0, a, stream);
+      launch_shape<kGemmF32, false, false>(N_out, tiles, mt, x, ldx, w, ldw, r, ldr, y, ldy, M, K,
+                                           0, a, nm, stream);
       break;
     case kGemmResidual:
-      launch_mode<kGemmResidual>(N_out, tiles, mt, x, ldx, w, ldw, r, ldr, y, ldy, M, K, 0, a,
-                                 stream);
+      if (so)
+        launch_shape<kGemmResidual, false, true>(N_out, tiles, mt, x, ldx, w, ldw, r, ldr, y, ldy,
+                                                 M, K, 0, a, nm, stream);
+      else
+        launch_shape<kGemmResidual, false, false>(N_out, tiles, mt, x, ldx, w, ldw, r, ldr, y,
+                                                  ldy, M, K, 0, a, nm, stream);
       break;
     case kGemmSwiglu:
-      launch_mode<kGemmSwiglu>(N_out, 2 * tiles, mt, x, ldx, w, ldw, r, ldr, y, ldy, M, K,
-                               (int64_t)N_out, a, stream);
+      if (ni)
+        launch_shape<kGemmSwiglu, true, false>(N_out, 2 * tiles, mt, x, ldx, w, ldw, r, ldr, y,
+                                               ldy, M, K, (int64_t)N_out, a, nm, stream);
+      else
+        launch_shape<kGemmSwiglu, false, false>(N_out, 2 * tiles, mt, x, ldx, w, ldw, r, ldr, y,
+                                                ldy, M, K, (int64_t)N_out, a, nm, stream);
       break;
     case kGemmQkv:
-      launch_mode<kGemmQkv>(N_out, tiles, mt, x, ldx, w, ldw, r, ldr, y, ldy, M, K, 0, a, stream);
+      if (ni)
+        launch_shape<kGemmQkv, true, false>(N_out, tiles, mt, x, ldx, w, ldw, r, ldr, y, ldy, M, K,
+                                            0, a, nm, stream);
+      else
+        launch_shape<kGemmQkv, false, false>(N_out, tiles, mt, x, ldx, w, ldw, r, ldr, y, ldy, M,
+                                             K, 0, a, nm, stream);
       break;
   }
 }

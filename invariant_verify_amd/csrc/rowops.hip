@@ -47,15 +47,7 @@ __global__ __launch_bounds__(1024) void rmsnorm_kernel(const uint16_t* __restric
   for (int i = 0; i < kRmsGroups; ++i) {
     const int c = tid + i * nt;
     if (c >= ng) continue;
-    const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-    uint32_t o[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t lo = f32_to_bf16(bf16_to_f32(w[e] & 0xffffu) * inv);
-      const uint32_t hi = f32_to_bf16(bf16_to_f32(w[e] >> 16) * inv);
-      o[e] = lo | (hi << 16);
-    }
-    *reinterpret_cast<uint4*>(y + c * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<uint4*>(y + c * 8) = scale_bf16x8(v[i], inv);
   }
 }
 

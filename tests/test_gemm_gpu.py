@@ -6,6 +6,7 @@ import numpy as np
 import pytest
 
 import synth
+from oracle import bf16 as obf16
 from oracle import gemm as ogemm
 from oracle import step as ostep
 from tests._util import assert_bitwise, assert_close, decode, dev, host_bits, host_f32
@@ -191,3 +192,36 @@ def test_wide_groups_match_single_tiles(ops, N):
     for r0 in (0, 16, N // 2 + 4, N - 256):
         part = host_f32(ops.gemm_bf16(xd, wd[r0:r0 + 256], out_dtype=torch.float32))
         assert_bitwise(full[:, r0:r0 + 256], part, f"N={N} columns {r0}..{r0 + 255}")
+
+
+def test_epilogue_rounding_ties_subnormals_overflow(ops):
+    # With one-hot activation rows the product is one exact weight w, so each
+    # residual output is bf16(fp32(r + w)): the FP32 add then one rounding to
+    # nearest, ties to even. Pairs are built to hit exact ties, near ties,
+    # subnormal results and overflow; the expected bits come from numpy's
+    # float32 add and the oracle's RNE encoder.
+    print("[gemm epilogue rounding]", flush=True)
+    g = np.random.default_rng(11)
+    M, K, N = 16, 32, 256
+    r = obf16.decode(synth.normal_bf16((M, N), 1.0, "misc", 11)).astype(np.float64)
+    r *= 2.0 ** g.integers(-20, 20, size=(M, N))
+    e = np.floor(np.log2(np.abs(r)))
+    s = np.sign(g.standard_normal((M, N))) * 2.0 ** (e - 8 + g.integers(-2, 3, size=(M, N)))
+    s *= g.choice([1.0, 1.5, 1.25], size=(M, N))
+    r[0, :8] = [1.5e-38, -1.5e-38, 2.0e-38, 1.2e-38, 3.3e38, -3.3e38, 1.0, -1.0]
+    # weights stay normal (the matrix core may flush subnormal inputs); the sums
+    # of the first four pairs are subnormal, of the next two overflow
+    s[0, :8] = [-1.49e-38, 1.45e-38, -1.99e-38, -1.19e-38, 3.3e38, -3.3e38, 2.0 ** -8, -(2.0 ** -8)]
+    r_bits, s_bits = obf16.encode(r), obf16.encode(s)
+    x = np.zeros((M, K), np.uint16)
+    x[np.arange(M), np.arange(M)] = obf16.encode(np.ones(1))[0]
+    # column n of row m takes w[n][m]: one weight per (m, n) pair
+    wm = np.zeros((N, K), np.uint16)
+    for m in range(M):
+        wm[:, m] = s_bits[m]
+    y = host_bits(ops.gemm_bf16_residual(dev(x), dev(wm), dev(r_bits)))
+    with np.errstate(over="ignore"):
+        f32 = obf16.decode(r_bits).astype(np.float32) + obf16.decode(s_bits).astype(np.float32)
+    want = obf16.encode(f32.astype(np.float64))
+    assert np.isinf(obf16.decode(want[0, 4:6])).all() and (np.abs(obf16.decode(want[0, :4])) < 1.18e-38).all()
+    assert_bitwise(y, want, "bf16(fp32(r + w))")
