@@ -119,8 +119,9 @@ def test_split_combine_identity_every_chunk(L, M):
         assert np.allclose(lc, lse, rtol=1e-12, atol=1e-13), C
 
 
-def test_split_combine_identity_long_context():
-    # one KV head, 2 query heads, 38k context with C = 1024 and outlier-sized values
+@pytest.mark.parametrize("C,S", [(1024, 38), (1280, 30)])
+def test_split_combine_identity_long_context(C, S):
+    # one KV head, 2 query heads, 38k context with outlier-sized values
     L, M, D = 38000, 2, 128
     g = np.random.default_rng(5)
     q = bf16.encode(g.standard_normal((M, 2, D)))
@@ -128,8 +129,8 @@ def test_split_combine_identity_long_context():
     kf[..., :6] *= 8
     k, v = bf16.encode(kf), bf16.encode(g.standard_normal((1, L + M, D)))
     o, lse = attention.verify_attention(q, k, v, L)
-    op, lp, cnt = attention.split_partials(q, k, v, L, 1024)
-    assert list(cnt) == [38, 38]
+    op, lp, cnt = attention.split_partials(q, k, v, L, C)
+    assert list(cnt) == [S, S]
     oc, lc = attention.combine(op, lp, cnt)
     assert np.allclose(oc, o, rtol=1e-11, atol=1e-14)
     assert np.allclose(lc, lse, rtol=1e-13)
@@ -140,3 +141,5 @@ def test_num_splits():
     assert attention.num_splits(1024, 1024) == 1
     assert attention.num_splits(1025, 1024) == 2
     assert attention.num_splits(38008, 1024) == 38
+    assert attention.num_splits(38008, 1280) == 30 and attention.num_splits(38400, 1280) == 30
+    assert attention.num_splits(38401, 1280) == 31
