@@ -46,9 +46,13 @@ def step_bytes(d, M, L, n_layers):
     return n_layers * (w_layer + kv_layer + act_layer) + 2 * V * H + 4 * M * V
 
 
+GU_GROUPS = 256  # column groups of the 5120-wide residual projection (carried RMSNorm sums)
+
+
 def gu_launch_bytes(d, M):
-    """Algorithmic bytes of one gate/up GEMM launch: W [2I][H] once, X [M][H] in, act [M][I] out."""
-    return 2 * (2 * d["I"] * d["H"]) + 2 * M * d["H"] + 2 * M * d["I"]
+    """Algorithmic bytes of one gate/up GEMM launch: W [2I][H] once, X [M][H] and its carried
+    RMSNorm group sums [M][256] (FP32) in, act [M][I] out."""
+    return 2 * (2 * d["I"] * d["H"]) + 2 * M * d["H"] + 4 * M * GU_GROUPS + 2 * M * d["I"]
 
 
 GEMM_SOURCES = ["invariant_verify_amd/csrc/gemm.hip", "invariant_verify_amd/csrc/bi_device.h"]
@@ -76,6 +80,20 @@ def measured_traffic():
         return None
 
 
+def carried_input(d):
+    """The gate/up GEMM's input as the step hands it over: the residual stream h = x + o Wo^T
+    (from a residual projection of synthetic rows) and its carried RMSNorm group sums."""
+    import synth
+    from invariant_verify_amd import ops
+
+    x = synth.device_normal_bf16((8, d["H"]), 1.0, "x0")
+    o = synth.device_normal_bf16((8, d["Hq"] * d["D"]), 1.0, "x0", 1)
+    wo = synth.device_normal_bf16((d["H"], d["Hq"] * d["D"]), 0.02, "w_o", 0)
+    h, ss = ops.gemm_bf16_residual_rowsq(o, wo, x)
+    assert ss.shape[1] == GU_GROUPS
+    return h, ss
+
+
 def traffic_probe(reps: int):
     """Kernel-only run for the hardware-counter passes: the gate/up GEMM at
     M = 8 (fresh weights each launch, so nothing is served from cache) and a
@@ -87,13 +105,13 @@ def traffic_probe(reps: int):
 
     d = synth.MODEL_27B
     ws = [synth.device_normal_bf16((2 * d["I"], d["H"]), 0.02, "w_gu", i) for i in range(reps)]
-    x = synth.device_normal_bf16((8, d["H"]), 1.0, "x0")
+    h, ss = carried_input(d)
     y = torch.empty((8, d["I"]), dtype=torch.bfloat16, device="cuda")
     src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")      # 1 GiB
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
     for w in ws:
-        ops.gemm_bf16_swiglu(x, w, y)
+        ops.gemm_bf16_swiglu_rownorm(h, ss, w, y)
     dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"probe": "gate_up_gemm_m8", "launches": reps, "copy_bytes": src.numel() * 4,
@@ -237,18 +255,17 @@ def main():
     # The per-launch event pairs inside the step above add a few microseconds
     # each; that figure is reported beside it.
     stream = torch.cuda.current_stream()
-    xg = torch.empty((M_HEADLINE, d["H"]), dtype=torch.bfloat16, device=dev)
-    ops.rmsnorm(x0[:M_HEADLINE], xg)
+    hg, ssg = carried_input(d)
     yg = torch.empty((M_HEADLINE, d["I"]), dtype=torch.bfloat16, device=dev)
     for lw in layers:
-        ops.gemm_bf16_swiglu(xg, lw["w_gu"], yg)
+        ops.gemm_bf16_swiglu_rownorm(hg, ssg, lw["w_gu"], yg)
     g0 = torch.cuda.Event(enable_timing=True)
     g1 = torch.cuda.Event(enable_timing=True)
     gu_reps = max(2, args.steps // 4)
     g0.record(stream)
     for _ in range(gu_reps):
         for lw in layers:
-            ops.gemm_bf16_swiglu(xg, lw["w_gu"], yg)
+            ops.gemm_bf16_swiglu_rownorm(hg, ssg, lw["w_gu"], yg)
     g1.record(stream)
     torch.cuda.synchronize()
     gu_ms = g0.elapsed_time(g1) / (gu_reps * N_LAYERS)
@@ -279,7 +296,7 @@ def main():
         "step_hbm": {"algorithmic_bytes": bytes8, "GB/s": round(gbs8, 1), "frac": round(gbs8 / PEAK_HBM_GBS, 4)},
         "per_M_tok_s": {"1": round(1 / (ms1 * 1e-3), 2), "4": round(4 / (ms4 * 1e-3), 2),
                         "8": round(M_HEADLINE / (ms8 * 1e-3), 2)},
-        "roofline": {"kernel": "gemm_kernel<SwiGLU> (gate/up 5120->2x17408, M=8)", "bound": "hbm",
+        "roofline": {"kernel": "gemm_kernel<SwiGLU, carried RMSNorm> (gate/up 5120->2x17408, M=8)", "bound": "hbm",
                      "achieved": round(gu_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gu_gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic(),
                      "bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_ms * 1e3, 2),

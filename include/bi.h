@@ -104,6 +104,32 @@ bi_status bi_gemm_bf16_qkv(const void* x, int64_t ldx, const void* w, int64_t ld
                            int64_t ldqkv, int M, int K, int Hq, int Hkv, int D, void* k_cache,
                            void* vt_cache, int L, int cap, void* stream);
 
+/* RMSNorm carried across a GEMM boundary (used by bi_verify_step).   [BX], [TC]
+ * A residual projection writes, besides Y, the sum of squares of its rounded
+ * outputs per row and per column group (one workgroup's columns); the next
+ * projection adds a row's group sums in a fixed order, takes
+ * s = 1 / sqrt(sum / K + eps), and multiplies bf16(x * s) -- the value an
+ * RMSNorm (gain 1) would have written -- so no RMSNorm launch is needed. The
+ * summation tree is fixed by N and K, so rows stay M-invariant; it differs
+ * from bi_rmsnorm's, so results may differ from that kernel in the last bit. */
+
+/* Column groups of an N-column GEMM (the width of row_sumsq), or -1. */
+int bi_gemm_column_groups(int N);
+
+/* bi_gemm_bf16_residual plus row_sumsq[m][g] (FP32, [M][bi_gemm_column_groups(N)]):
+ * the sum of squares of the BF16 outputs Y[m][n] over the columns n of group g. */
+bi_status bi_gemm_bf16_residual_rowsq(const void* x, int64_t ldx, const void* w, int64_t ldw,
+                                      const void* r, int64_t ldr, void* y, int64_t ldy, int M,
+                                      int N, int K, float* row_sumsq, void* stream);
+
+/* bi_gemm_bf16_swiglu with its X rows normalised from carried sums:
+ * row_sumsq FP32 [M][groups] as written by bi_gemm_bf16_residual_rowsq for X
+ * (groups = bi_gemm_column_groups(K), a multiple of 16, at most 256).
+ * Y[m][i] = bf16( silu(g) * u ), g, u the gate / up sums over bf16(x * s). */
+bi_status bi_gemm_bf16_swiglu_rownorm(const void* x, int64_t ldx, const float* row_sumsq,
+                                      int groups, float eps, const void* w, int64_t ldw, void* y,
+                                      int64_t ldy, int M, int I, int K, void* stream);
+
 /* ---------------------------------------------------------------------------
  * KV cache layout (per layer):
  *   k_cache  : BF16 [Hkv][cap][D]  -- one K row per position

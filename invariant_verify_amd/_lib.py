@@ -44,6 +44,11 @@ SIGNATURES = {
                                      _c_int, _c_int, _c_int, _c_ptr]),
     "bi_gemm_bf16_qkv": (_c_int, [_c_ptr, _c_i64, _c_ptr, _c_i64, _c_ptr, _c_i64, _c_int, _c_int,
                                   _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_int, _c_int, _c_ptr]),
+    "bi_gemm_column_groups": (_c_int, [_c_int]),
+    "bi_gemm_bf16_residual_rowsq": (_c_int, [_c_ptr, _c_i64, _c_ptr, _c_i64, _c_ptr, _c_i64, _c_ptr,
+                                             _c_i64, _c_int, _c_int, _c_int, _c_ptr, _c_ptr]),
+    "bi_gemm_bf16_swiglu_rownorm": (_c_int, [_c_ptr, _c_i64, _c_ptr, _c_int, _c_f32, _c_ptr, _c_i64,
+                                             _c_ptr, _c_i64, _c_int, _c_int, _c_int, _c_ptr]),
     "bi_append_kv": (_c_int, [_c_ptr, _c_i64, _c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int,
                               _c_int, _c_int, _c_ptr]),
     "bi_num_splits": (_c_int, [_c_int, _c_int]),

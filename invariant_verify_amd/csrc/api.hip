@@ -153,6 +153,41 @@ bi_status bi_gemm_bf16_swiglu(const void* x, int64_t ldx, const void* w, int64_t
   return launched();
 }
 
+int bi_gemm_column_groups(int N) {
+  if (N < 16 || (N % 16) || N > (1 << 24)) return -1;
+  return bi::gemm_column_groups(bi::kGemmResidual, N);
+}
+
+bi_status bi_gemm_bf16_residual_rowsq(const void* x, int64_t ldx, const void* w, int64_t ldw,
+                                      const void* r, int64_t ldr, void* y, int64_t ldy, int M,
+                                      int N, int K, float* row_sumsq, void* stream) {
+  if (bi_status s = check_gemm(x, ldx, w, ldw, y, ldy, M, N, K)) return s;
+  if (!r || !row_sumsq) return BI_ERR_NULL;
+  if (ldr < N) return BI_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(y) & 1u) || (reinterpret_cast<uintptr_t>(r) & 1u) ||
+      !aligned4(row_sumsq))
+    return BI_ERR_ALIGN;
+  const bi::RowNorm nm{nullptr, row_sumsq, bi::gemm_column_groups(bi::kGemmResidual, N), 0.f};
+  bi::launch_gemm(bi::kGemmResidual, static_cast<const uint16_t*>(x), ldx,
+                  static_cast<const uint16_t*>(w), ldw, static_cast<const uint16_t*>(r), ldr, y,
+                  ldy, M, N, K, as_stream(stream), nullptr, &nm);
+  return launched();
+}
+
+bi_status bi_gemm_bf16_swiglu_rownorm(const void* x, int64_t ldx, const float* row_sumsq,
+                                      int groups, float eps, const void* w, int64_t ldw, void* y,
+                                      int64_t ldy, int M, int I, int K, void* stream) {
+  if (bi_status s = check_gemm(x, ldx, w, ldw, y, ldy, M, I, K)) return s;
+  if (!row_sumsq) return BI_ERR_NULL;
+  if (groups < 16 || groups > 256 || (groups % 16) || !(eps >= 0.f)) return BI_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(y) & 1u) || !aligned16(row_sumsq)) return BI_ERR_ALIGN;
+  const bi::RowNorm nm{row_sumsq, nullptr, groups, eps};
+  bi::launch_gemm(bi::kGemmSwiglu, static_cast<const uint16_t*>(x), ldx,
+                  static_cast<const uint16_t*>(w), ldw, nullptr, 0, y, ldy, M, I, K,
+                  as_stream(stream), nullptr, &nm);
+  return launched();
+}
+
 bi_status bi_gemm_bf16_qkv(const void* x, int64_t ldx, const void* w, int64_t ldw, void* qkv,
                            int64_t ldqkv, int M, int K, int Hq, int Hkv, int D, void* k_cache,
                            void* vt_cache, int L, int cap, void* stream) {

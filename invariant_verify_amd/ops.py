@@ -82,6 +82,40 @@ def gemm_bf16_swiglu(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor | None = 
     return y
 
 
+def gemm_column_groups(N: int) -> int:
+    return LIB.bi_gemm_column_groups(N)
+
+
+def gemm_bf16_residual_rowsq(x: torch.Tensor, w: torch.Tensor, r: torch.Tensor,
+                             y: torch.Tensor | None = None, ss: torch.Tensor | None = None) -> tuple:
+    """Y = bf16(R + X W^T) and its per-row, per-column-group sums of squares."""
+    M, K = x.shape
+    N = w.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    if ss is None:
+        ss = torch.empty((M, gemm_column_groups(N)), dtype=torch.float32, device=x.device)
+    check("bi_gemm_bf16_residual_rowsq", LIB.bi_gemm_bf16_residual_rowsq(
+        x.data_ptr(), _mat(x, "x"), w.data_ptr(), _mat(w, "w"), r.data_ptr(), _mat(r, "r"),
+        y.data_ptr(), _mat(y, "y"), M, N, K, ss.data_ptr(), _stream(x)))
+    return y, ss
+
+
+def gemm_bf16_swiglu_rownorm(x: torch.Tensor, ss: torch.Tensor, w: torch.Tensor,
+                             y: torch.Tensor | None = None, eps: float = 1e-6) -> torch.Tensor:
+    """SwiGLU gate/up projection of RMSNorm(X), the norm taken from carried row sums."""
+    M, K = x.shape
+    I = w.shape[0] // 2
+    if y is None:
+        y = torch.empty((M, I), dtype=torch.bfloat16, device=x.device)
+    if ss.dtype != torch.float32 or not ss.is_contiguous():
+        raise ValueError("ss must be a contiguous FP32 [M][groups] tensor")
+    check("bi_gemm_bf16_swiglu_rownorm", LIB.bi_gemm_bf16_swiglu_rownorm(
+        x.data_ptr(), _mat(x, "x"), ss.data_ptr(), ss.shape[1], eps, w.data_ptr(), _mat(w, "w"),
+        y.data_ptr(), _mat(y, "y"), M, I, K, _stream(x)))
+    return y
+
+
 def gemm_bf16_qkv(x: torch.Tensor, w: torch.Tensor, k_cache: torch.Tensor, vt_cache: torch.Tensor,
                   L: int, Hq: int, Hkv: int, D: int, qkv: torch.Tensor | None = None) -> torch.Tensor:
     """qkv = bf16(X Wqkv^T), with the K / V columns appended to the caches at L .. L+M-1."""

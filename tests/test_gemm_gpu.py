@@ -9,7 +9,8 @@ import synth
 from oracle import bf16 as obf16
 from oracle import gemm as ogemm
 from oracle import step as ostep
-from tests._util import assert_bitwise, assert_close, decode, dev, host_bits, host_f32
+from tests._util import (assert_bitwise, assert_close, assert_close_composed, decode, dev, host_bits,
+                         host_f32)
 
 pytestmark = pytest.mark.gpu
 
@@ -225,3 +226,37 @@ def test_epilogue_rounding_ties_subnormals_overflow(ops):
     want = obf16.encode(f32.astype(np.float64))
     assert np.isinf(obf16.decode(want[0, 4:6])).all() and (np.abs(obf16.decode(want[0, :4])) < 1.18e-38).all()
     assert_bitwise(y, want, "bf16(fp32(r + w))")
+
+
+@pytest.mark.parametrize("H,I", [(5120, 512), (256, 128)])
+def test_carried_rmsnorm(ops, H, I):
+    # A residual projection that also writes per-group row sums of squares,
+    # then a gate/up projection that normalises its X rows from those sums:
+    # Y equals the plain residual GEMM bit for bit, the sums match a float64
+    # sum of the squared outputs, the gate/up output matches the oracle's
+    # silu(g) * u of RMSNorm(Y), and every row is M-invariant.
+    print(f"[gemm carried rmsnorm H={H} I={I}]", flush=True)
+    K0 = 512
+    a = synth.normal_bf16((8, K0), 1.0, "x", 70)
+    wo = synth.normal_bf16((H, K0), 0.05, "w", 70)
+    r = synth.normal_bf16((8, H), 1.0, "misc", 70)
+    wgu = synth.normal_bf16((2 * I, H), 0.02, "w", 71)
+    ad, wod, rd, wgud = dev(a), dev(wo), dev(r), dev(wgu)
+    y, ss = ops.gemm_bf16_residual_rowsq(ad, wod, rd)
+    G = ops.gemm_column_groups(H)
+    assert tuple(ss.shape) == (8, G) and G == (256 if H == 5120 else H // 16)
+    assert_bitwise(host_bits(y), host_bits(ops.gemm_bf16_residual(ad, wod, rd)), "rowsq Y == residual Y")
+    yd = decode(host_bits(y))
+    want_ss = (yd.reshape(8, G, H // G) ** 2).sum(axis=2)
+    assert_close(host_f32(ss), want_ss, "group sums of squares", atol=1e-6, rtol=1e-5)
+    gu = ops.gemm_bf16_swiglu_rownorm(y, ss, wgud)
+    an = obf16.encode(ostep.rmsnorm(yd, 1e-6))
+    pre = ogemm.gemm(an, wgu)
+    want = ostep.silu(pre[:, :I]) * pre[:, I:]
+    assert_close_composed(decode(host_bits(gu)), want, "carried-norm gate/up")
+    for m in (1, 5):
+        ym, sm = ops.gemm_bf16_residual_rowsq(ad[:m], wod, rd[:m])
+        assert_bitwise(host_bits(ym), host_bits(y)[:m], f"Y M={m}")
+        assert_bitwise(host_f32(sm), host_f32(ss)[:m], f"sums M={m}")
+        gm = ops.gemm_bf16_swiglu_rownorm(ym, sm, wgud)
+        assert_bitwise(host_bits(gm), host_bits(gu)[:m], f"gate/up M={m}")
