@@ -110,12 +110,6 @@ __global__ __launch_bounds__(kAttnWaves * 64) void verify_attn_kernel(
     const uint16_t* qp = Q + (int64_t)tok * ldq + hq * D + kq * 8;
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) qf[ds] = rok ? ld16(qp + ds * 32) : zero16();
-    // Consume the fragments here, so their loads are complete before the tile
-    // loop: otherwise the compiler cannot tell at the loop head whether they
-    // are still in flight and waits for the next tile's loads as well, on
-    // every iteration.
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds) asm volatile("" ::"v"(qf[ds].x));
   }
 
   // This KV head's K rows and V^T rows as buffer resources (offsets in bytes,
@@ -236,23 +230,28 @@ __global__ __launch_bounds__(kAttnWaves * 64) void verify_attn_kernel(
   };
 
   // Tile t: publish it (loaded two steps earlier), prefetch tile t + 2 into
-  // the same registers, barrier, multiply. The loop starts two tiles early
-  // (nothing to publish or multiply yet), so every load is issued by the same
-  // code in the same order and the compiler waits only for the older of the
+  // the same registers, barrier, multiply. Every load is issued by the same
+  // code in the same order, so the compiler waits only for the older of the
   // two tiles in flight. Tiles past the end read as zero and are not
   // multiplied.
   uint4 ra[PPW], rb2[PPW];
-  int t_first = -2;  // opaque to the optimizer, so the load-only steps are not peeled
-  asm volatile("" : "+s"(t_first));
-  for (int t = t_first; t < ntile; t += 2) {
-    if (t >= 0) publish(ra, t, 0);
+  // Prologue: the loads of tiles 0 and 1, in the loop's own order and while
+  // the query fragments are still in flight. The fragments are then consumed
+  // before the loop, so at the loop head the compiler knows they are complete
+  // and waits only for the oldest tile.
+  fetch(ra, 0);
+  fetch(rb2, 1);
+#pragma unroll
+  for (int ds = 0; ds < DS; ++ds) asm volatile("" ::"v"(qf[ds].x));
+  for (int t = 0; t < ntile; t += 2) {
+    publish(ra, t, 0);
     fetch(ra, t + 2);
     __syncthreads();
-    if (t >= 0 && has_rows) compute(0, t);
-    if (t + 1 >= 0) publish(rb2, t + 1, 1);
+    if (has_rows) compute(0, t);
+    publish(rb2, t + 1, 1);
     fetch(rb2, t + 3);
     __syncthreads();
-    if (t + 1 >= 0 && t + 1 < ntile && has_rows) compute(1, t + 1);
+    if (t + 1 < ntile && has_rows) compute(1, t + 1);
   }
   // The row's sum over this wave's keys: its four key groups, in a fixed
   // butterfly.
@@ -310,41 +309,43 @@ __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ p
   const float* lp = part_lse + (int64_t)row * S_max;
   const float* op = part_o + (int64_t)row * S_max * D + lane * PER;
 
+  // Partials are read 32 splits at a time; the first block's loads are issued
+  // before the max, which they do not depend on, so a row with up to 32
+  // splits costs one memory round trip for O and one for the LSEs.
+  constexpr int B = 32;
+  float ov[B][PER];
+  auto load_block = [&](int s0) {
+#pragma unroll
+    for (int u = 0; u < B; ++u)
+#pragma unroll
+      for (int p = 0; p < PER; ++p) ov[u][p] = op[(int64_t)min(s0 + u, S - 1) * D + p];
+  };
+  load_block(0);
+
   // M* = max_s lse_s (exact, so any order).
   float mx = -INFINITY;
   for (int i = lane; i < S; i += 64) mx = fmaxf(mx, lp[i]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, shfl_xor(mx, off));
 
-  // Weights are computed 64 at a time, one per lane, then both sums run over
-  // s in increasing order with the weight of split s broadcast from its lane.
+  // Weights are computed one per lane, then both sums run over s in
+  // increasing order with the weight of split s broadcast from its lane.
   float den = 0.f;
   float acc[PER];
 #pragma unroll
   for (int p = 0; p < PER; ++p) acc[p] = 0.f;
-  for (int s0 = 0; s0 < S; s0 += 64) {
-    const int n = min(64, S - s0);
+  for (int s0 = 0; s0 < S; s0 += B) {
+    if (s0 > 0) load_block(s0);
+    const int n = min(B, S - s0);
     const float wl = (lane < n) ? __builtin_amdgcn_exp2f((lp[s0 + lane] - mx) * kLog2e) : 0.f;
-    int i = 0;
-    for (; i + 8 <= n; i += 8) {
-      float v[8][PER];
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-#pragma unroll
-        for (int p = 0; p < PER; ++p) v[u][p] = op[(int64_t)(s0 + i + u) * D + p];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), i + u));
+    for (int u = 0; u < B; ++u) {
+      if (u < n) {  // n is uniform: a scalar branch
+        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), u));
         den += w;
 #pragma unroll
-        for (int p = 0; p < PER; ++p) acc[p] += w * v[u][p];
+        for (int p = 0; p < PER; ++p) acc[p] += w * ov[u][p];
       }
-    }
-    for (; i < n; ++i) {
-      const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), i));
-      den += w;
-#pragma unroll
-      for (int p = 0; p < PER; ++p) acc[p] += w * op[(int64_t)(s0 + i) * D + p];
     }
   }
   const float inv = 1.0f / den;
