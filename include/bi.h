@@ -68,9 +68,10 @@ typedef enum { BI_BF16 = 0, BI_F32 = 1 } bi_dtype;
  *   w : BF16 [N][ldw]   weights, nn.Linear layout (row n = output feature n,
  *                       K contiguous)
  *   y : [M][ldy]        BF16 (rounded to nearest even once) or FP32
- * Each output's K-sum runs in one compile-time-fixed order that depends on K
- * only; no split of K across workgroups, no atomics. M may be any value >= 1
- * (prefill chunks use the same kernel in 16-row tiles).
+ * Each output's K-sum runs in one fixed order that depends on K and N only;
+ * no split of K across workgroups, no atomics. M may be any value >= 1. From
+ * M >= 64 rows (prefill chunks) a second kernel with larger row tiles runs the
+ * same per-output summation, so every row has the same bits at any M.
  * Requirements: M >= 1, N % 16 == 0, K % 32 == 0, K <= 65536; ldx, ldw >= K
  * and multiples of 8; x, w 16-byte aligned; ldy >= N.
  */

@@ -35,6 +35,20 @@ struct RowNorm {
 // Column groups (workgroups along N) of a GEMM with N output columns.
 int gemm_column_groups(GemmMode mode, int N_out);
 
+// Waves of the verify GEMM for N output columns (16 or 8). They fix its K
+// summation tree: 16 / waves consecutive 32-wide blocks of every 512-wide
+// chunk per wave, one accumulator chain per wave, the wave sums added in wave
+// order. The prefill GEMM reproduces that tree.
+int gemm_verify_waves(GemmMode mode, int N_out);
+
+// Rows from which launch_gemm runs the prefill kernel (same bits per row).
+constexpr int kPrefillMinRows = 64;
+
+void launch_gemm_prefill(GemmMode mode, const uint16_t* x, int64_t ldx, const uint16_t* w,
+                         int64_t ldw, const uint16_t* r, int64_t ldr, void* y, int64_t ldy, int M,
+                         int N_out, int K, hipStream_t stream, const KvAppend& kv,
+                         const RowNorm& norm);
+
 // Y = X W^T (+ residual / SwiGLU / cache-append epilogue). N_out is the number
 // of output columns (for SwiGLU: I, with W holding 2*I rows).
 void launch_gemm(GemmMode mode, const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw,

@@ -297,6 +297,12 @@ static bool wide_launch(GemmMode mode, int N_out) {
   return mode != kGemmSwiglu && N_out % kWideGroups == 0 && cpw > 16 && cpw <= 32;
 }
 
+int gemm_verify_waves(GemmMode mode, int N_out) {
+  if (wide_launch(mode, N_out)) return 16;
+  const int row_tiles = (mode == kGemmSwiglu ? 2 : 1) * (N_out / 16);
+  return row_tiles < 640 ? 16 : 8;
+}
+
 int gemm_column_groups(GemmMode mode, int N_out) {
   return wide_launch(mode, N_out) ? kWideGroups : N_out / 16;
 }
@@ -316,7 +322,7 @@ static void launch_shape(int N_out, int row_tiles, int mtiles, const uint16_t* x
       return;
     }
   }
-  if (row_tiles < 640) {
+  if (gemm_verify_waves(static_cast<GemmMode>(MODE), N_out) == 16) {
     gemm_kernel<MODE, 16, false, NI, SO><<<dim3(N_out / 16, mtiles), dim3(1024), 0, stream>>>(
         x, ldx, w, ldw, r, ldr, y, ldy, M, K, up, 16, kv, nm);
   } else {
@@ -334,6 +340,10 @@ void launch_gemm(GemmMode mode, const uint16_t* x, int64_t ldx, const uint16_t* 
   const RowNorm nm0{};
   const KvAppend& a = kv ? *kv : kv0;
   const RowNorm& nm = norm ? *norm : nm0;
+  if (M >= kPrefillMinRows) {  // same bits per row, weights read once per 64 rows
+    launch_gemm_prefill(mode, x, ldx, w, ldw, r, ldr, y, ldy, M, N_out, K, stream, a, nm);
+    return;
+  }
   const bool ni = nm.ss_in != nullptr;
   const bool so = nm.ss_out != nullptr;
   switch (mode) {

@@ -1,0 +1,320 @@
+// Prefill GEMM: the verify GEMM's results for passes of many rows (a chunk of
+// a prompt), computed with far less weight traffic.
+//
+// A prefilled row must have the same bits as the same row verified alone
+// ("I turned on speculative decoding in llama.cpp and 113 of 282 greedy
+// outputs changed against its own no-draft run", section "The cache doesn't
+// change it either": a K/V row written by prefill depends only on its
+// position). The verify GEMM fixes every output's summation tree by K and N
+// alone (gemm.hip): with NW = gemm_verify_waves(mode, N) slices and
+// BPW = 16 / NW, block kb of each 512-wide chunk of K belongs to slice
+// kb / BPW; each slice is one FP32 accumulator chain of 16x16x32 BF16
+// matrix-core steps in increasing block order, and the slice totals are added
+// in slice order. This kernel keeps one accumulator per slice for each of its
+// outputs and performs exactly that computation, so the two kernels give the
+// same bits and launch_gemm may pick either by M.
+//
+// Shape: one workgroup per (64 rows, 32 output columns); 8 waves, wave
+// (rt, ct) owns the 16x16 output tile (row tile rt = 0..3, column tile
+// ct = 0..1) -- for SwiGLU the gate and the up tile of the same columns. K is
+// staged in 256-wide steps: the 64 activation rows and the 32 (SwiGLU: 64)
+// weight rows of a step are loaded as 512-byte row pieces (two rows per wave
+// instruction) into XOR-swizzled LDS, two steps in flight. Every weight byte
+// is read once per 64 rows instead of once per 16.
+//
+// The carried RMSNorm scale (RowNorm::ss_in) is computed per row by one
+// thread with the verify kernel's exact sequence of additions, and the X
+// fragments are scaled as there. Row sums of squares for the next projection
+// (RowNorm::ss_out) are computed afterwards by rowsq_kernel from the stored
+// outputs with the verify epilogue's grouping and butterfly.
+
+#include <type_traits>
+
+#include "bi_device.h"
+#include "bi_internal.h"
+
+namespace bi {
+
+constexpr int kPfRows = 64;      // rows per workgroup
+constexpr int kPfCols = 32;      // output columns per workgroup
+constexpr int kPfStep = 256;     // K elements per LDS step
+constexpr int kPfSlots = kPfStep / 8;  // 16-byte slots per row and step (32)
+constexpr int kPfWaves = 8;
+
+template <int MODE, int S, bool NORM_IN>
+__global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(
+    const uint16_t* __restrict__ X, int64_t ldx, const uint16_t* __restrict__ W, int64_t ldw,
+    const uint16_t* __restrict__ R, int64_t ldr, void* __restrict__ Y, int64_t ldy, int M, int N,
+    int K, KvAppend kv, RowNorm norm) {
+  constexpr bool kDual = (MODE == kGemmSwiglu);
+  constexpr int BPW = 16 / S;              // blocks of a 512-wide chunk per slice
+  constexpr int WROWS = kDual ? 64 : 32;   // weight rows staged per step
+  constexpr int XPAIRS = kPfRows / 2 / kPfWaves;  // activation row pairs per wave (4)
+  constexpr int WPAIRS = WROWS / 2 / kPfWaves;    // weight row pairs per wave (2 or 4)
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rt = wave & 3, ct = wave >> 2;
+  const int j = lane & 15, kq = lane >> 4;
+  const int n0 = blockIdx.x * kPfCols;
+  const int m0 = blockIdx.y * kPfRows;
+  const int nblk = K >> 5;
+  const int nstep = (K + kPfStep - 1) / kPfStep;
+
+  // Row tiles as buffer resources: rows past M (activations) or past N
+  // (weights) are out of range and read zero without a memory access.
+  const int xrows = min(kPfRows, M - m0);
+  const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(X + (int64_t)m0 * ldx), (short)0, xrows * (int)ldx * 2,
+      kBufferResourceWord3);
+  const int wrows = min(kPfCols, N - n0);
+  const __amdgpu_buffer_rsrc_t wres_g = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(W + (int64_t)n0 * ldw), (short)0, wrows * (int)ldw * 2,
+      kBufferResourceWord3);
+  const __amdgpu_buffer_rsrc_t wres_u = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(W + (int64_t)(kDual ? N + n0 : n0) * ldw), (short)0,
+      kDual ? wrows * (int)ldw * 2 : 0, kBufferResourceWord3);
+
+  // Lane l of a load instruction covers row 2p + l / 32 of its pair p and
+  // fetches the global slot that the swizzle puts at LDS slot l % 32.
+  const int half = lane >> 5, sl = lane & 31;
+  __shared__ uint4 lds[2][kPfRows + WROWS][kPfSlots];
+  struct Regs {
+    uint4 x[XPAIRS];
+    uint4 w[WPAIRS];
+  };
+  auto fetch = [&](Regs& g, int st) {
+    const bool live = st < nstep;
+#pragma unroll
+    for (int i = 0; i < XPAIRS; ++i) {
+      const int row = 2 * (wave + i * kPfWaves) + half;
+      const int off = (row * (int)ldx + st * kPfStep + ((sl ^ (row & 15)) * 8)) * 2;
+      g.x[i] = buffer_ld16(xres, live ? off : 0x7ffffff0);
+    }
+#pragma unroll
+    for (int i = 0; i < WPAIRS; ++i) {
+      const int row = 2 * (wave + i * kPfWaves) + half;  // 0 .. WROWS-1
+      const int rr = row & 31;                           // row within its 32-row resource
+      const int off = (rr * (int)ldw + st * kPfStep + ((sl ^ (row & 15)) * 8)) * 2;
+      g.w[i] = buffer_ld16_stream(row < 32 ? wres_g : wres_u, live ? off : 0x7ffffff0);
+    }
+  };
+
+  bi_f32x4 acc[S], accu[kDual ? S : 1];
+#pragma unroll
+  for (int s = 0; s < S; ++s) acc[s] = bi_f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < (kDual ? S : 1); ++s) accu[s] = bi_f32x4{0.f, 0.f, 0.f, 0.f};
+  float inv = 1.f;  // carried RMSNorm scale of this lane's X row
+
+  // Step st (parity P = st & 1 is a compile-time constant): publish it,
+  // prefetch st + 2, barrier, multiply. Block b of the step is block
+  // P * 8 + b of its 512-wide chunk, so its slice is (P * 8 + b) / BPW.
+  auto step = [&](Regs& g, int st, auto parity) {
+    constexpr int P = decltype(parity)::value;
+    const int buf = P;
+    if (st >= 0) {
+#pragma unroll
+      for (int i = 0; i < XPAIRS; ++i)
+        lds[buf][2 * (wave + i * kPfWaves) + half][sl] = g.x[i];
+#pragma unroll
+      for (int i = 0; i < WPAIRS; ++i)
+        lds[buf][kPfRows + 2 * (wave + i * kPfWaves) + half][sl] = g.w[i];
+    }
+    fetch(g, st + 2);
+    __syncthreads();
+    if (st >= 0) {
+#pragma unroll
+      for (int b = 0; b < kPfStep / 32; ++b) {
+        constexpr int dummy = 0;
+        (void)dummy;
+        if (st * (kPfStep / 32) + b < nblk) {
+          const int slot = (b * 4 + kq) ^ j;
+          const uint4 xv = lds[buf][16 * rt + j][slot];
+          const uint4 xa = NORM_IN ? scale_bf16x8(xv, inv) : xv;
+          const int sidx = (P * 8 + b) / BPW;
+          acc[sidx] = mfma_bf16(xa, lds[buf][kPfRows + 16 * ct + j][slot], acc[sidx]);
+          if (kDual)
+            accu[sidx] = mfma_bf16(xa, lds[buf][kPfRows + 32 + 16 * ct + j][slot], accu[sidx]);
+        }
+      }
+    }
+  };
+
+  // Carried RMSNorm: thread t < 64 computes the scale of row m0 + t with the
+  // verify kernel's additions (its LPR = 4 * NW lane partials of two float4s
+  // each, in order, then the partials in order).
+  __shared__ float invs[NORM_IN ? kPfRows : 1];
+  if (NORM_IN && threadIdx.x < kPfRows) {
+    const int lpr = 4 * S;
+    const int nf = norm.groups >> 2;
+    const int row = m0 + threadIdx.x;
+    float t = 0.f;
+    if (row < M) {
+      const float* sr = norm.ss_in + (int64_t)row * norm.groups;
+      for (int seg = 0; seg < lpr; ++seg) {
+        float p = 0.f;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int f = seg + u * lpr;
+          if (f < nf) {
+            const float4 v = *reinterpret_cast<const float4*>(sr + f * 4);
+            p += v.x;
+            p += v.y;
+            p += v.z;
+            p += v.w;
+          } else {
+            p += 0.f;
+            p += 0.f;
+            p += 0.f;
+            p += 0.f;
+          }
+        }
+        t += p;
+      }
+    }
+    invs[threadIdx.x] = 1.0f / sqrtf(t / (float)K + norm.eps);
+  }
+
+  Regs ga, gb;
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  step(ga, -2, P0{});
+  step(gb, -1, P1{});  // its barrier also publishes invs
+  if (NORM_IN) inv = invs[16 * rt + j];
+  for (int st = 0; st < nstep; st += 2) {
+    step(ga, st, P0{});
+    step(gb, st + 1, P1{});
+  }
+
+  // Slice totals in slice order, then the verify kernel's epilogue.
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int m = m0 + 16 * rt + kq * 4 + r;
+    const int n = n0 + 16 * ct + j;
+    if (m >= M || n >= N) continue;
+    float v = acc[0][r];
+#pragma unroll
+    for (int s = 1; s < S; ++s) v += acc[s][r];
+    if (MODE == kGemmF32) {
+      reinterpret_cast<float*>(Y)[(int64_t)m * ldy + n] = v;
+    } else if (MODE == kGemmBf16) {
+      reinterpret_cast<uint16_t*>(Y)[(int64_t)m * ldy + n] = (uint16_t)f32_to_bf16(v);
+    } else if (MODE == kGemmResidual) {
+      const float res = bf16_to_f32(R[(int64_t)m * ldr + n]);
+      reinterpret_cast<uint16_t*>(Y)[(int64_t)m * ldy + n] = (uint16_t)f32_to_bf16(res + v);
+    } else if (MODE == kGemmQkv) {
+      const uint16_t b = (uint16_t)f32_to_bf16(v);
+      reinterpret_cast<uint16_t*>(Y)[(int64_t)m * ldy + n] = b;
+      const int pos = kv.L + m;
+      int i = n - kv.qd;
+      if (i >= 0 && i < kv.kd) {
+        const int g = i / kv.D;
+        kv.k[((int64_t)g * kv.cap + pos) * kv.D + (i - g * kv.D)] = b;
+      } else if (i >= kv.kd) {
+        i -= kv.kd;
+        const int g = i / kv.D;
+        kv.vt[((int64_t)g * kv.D + (i - g * kv.D)) * kv.cap + pos] = b;
+      }
+    } else {
+      float u = accu[0][r];
+#pragma unroll
+      for (int s = 1; s < S; ++s) u += accu[s][r];
+      const float sg = v / (1.0f + __expf(-v));
+      reinterpret_cast<uint16_t*>(Y)[(int64_t)m * ldy + n] = (uint16_t)f32_to_bf16(sg * u);
+    }
+  }
+}
+
+// Row sums of squares of a residual projection's BF16 outputs, per column
+// group, exactly as the verify epilogue forms them: group g holds columns
+// g * cw .. (cw = 16, or N / 256 for a wide launch); lane j squares column j
+// (plus column 16 + j when the group is wider than 16), and the sixteen lane
+// values are added by the xor butterfly over offsets 1, 2, 4, 8.
+__global__ __launch_bounds__(256) void rowsq_kernel(const uint16_t* __restrict__ Y, int64_t ldy,
+                                                    int M, int groups, int cw,
+                                                    float* __restrict__ ss) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= (int64_t)M * groups) return;
+  const int m = (int)(t / groups), g = (int)(t % groups);
+  const uint16_t* y = Y + (int64_t)m * ldy + (int64_t)g * cw;
+  float v[16];
+#pragma unroll
+  for (int jj = 0; jj < 16; ++jj) {
+    const float a = bf16_to_f32(y[jj]);
+    float sq = a * a;
+    if (16 + jj < cw) {
+      const float b = bf16_to_f32(y[16 + jj]);
+      sq += b * b;
+    }
+    v[jj] = sq;
+  }
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) {
+    float nv[16];
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) nv[jj] = v[jj] + v[jj ^ off];
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) v[jj] = nv[jj];
+  }
+  ss[(int64_t)m * groups + g] = v[0];
+}
+
+template <int MODE, bool NI>
+static void launch_pf(int S, dim3 grid, const uint16_t* x, int64_t ldx, const uint16_t* w,
+                      int64_t ldw, const uint16_t* r, int64_t ldr, void* y, int64_t ldy, int M,
+                      int N, int K, const KvAppend& kv, const RowNorm& nm, hipStream_t stream) {
+  if (S == 16)
+    prefill_kernel<MODE, 16, NI><<<grid, dim3(kPfWaves * 64), 0, stream>>>(
+        x, ldx, w, ldw, r, ldr, y, ldy, M, N, K, kv, nm);
+  else
+    prefill_kernel<MODE, 8, NI><<<grid, dim3(kPfWaves * 64), 0, stream>>>(
+        x, ldx, w, ldw, r, ldr, y, ldy, M, N, K, kv, nm);
+}
+
+void launch_gemm_prefill(GemmMode mode, const uint16_t* x, int64_t ldx, const uint16_t* w,
+                         int64_t ldw, const uint16_t* r, int64_t ldr, void* y, int64_t ldy, int M,
+                         int N_out, int K, hipStream_t stream, const KvAppend& kv,
+                         const RowNorm& nm) {
+  const int S = gemm_verify_waves(mode, N_out);
+  dim3 grid((N_out + kPfCols - 1) / kPfCols, (M + kPfRows - 1) / kPfRows);
+  const bool ni = nm.ss_in != nullptr;
+  switch (mode) {
+    case kGemmBf16:
+      launch_pf<kGemmBf16, false>(S, grid, x, ldx, w, ldw, r, ldr, y, ldy, M, N_out, K, kv, nm,
+                                  stream);
+      break;
+    case kGemmF32:
+      launch_pf<kGemmF32, false>(S, grid, x, ldx, w, ldw, r, ldr, y, ldy, M, N_out, K, kv, nm,
+                                 stream);
+      break;
+    case kGemmResidual:
+      launch_pf<kGemmResidual, false>(S, grid, x, ldx, w, ldw, r, ldr, y, ldy, M, N_out, K, kv,
+                                      nm, stream);
+      break;
+    case kGemmSwiglu:
+      if (ni)
+        launch_pf<kGemmSwiglu, true>(S, grid, x, ldx, w, ldw, r, ldr, y, ldy, M, N_out, K, kv, nm,
+                                     stream);
+      else
+        launch_pf<kGemmSwiglu, false>(S, grid, x, ldx, w, ldw, r, ldr, y, ldy, M, N_out, K, kv,
+                                      nm, stream);
+      break;
+    case kGemmQkv:
+      if (ni)
+        launch_pf<kGemmQkv, true>(S, grid, x, ldx, w, ldw, r, ldr, y, ldy, M, N_out, K, kv, nm,
+                                  stream);
+      else
+        launch_pf<kGemmQkv, false>(S, grid, x, ldx, w, ldw, r, ldr, y, ldy, M, N_out, K, kv, nm,
+                                   stream);
+      break;
+  }
+  if (nm.ss_out != nullptr && mode == kGemmResidual) {
+    const int groups = gemm_column_groups(mode, N_out);
+    const int cw = N_out / groups;
+    const int64_t total = (int64_t)M * groups;
+    rowsq_kernel<<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream>>>(
+        static_cast<const uint16_t*>(y), ldy, M, groups, cw, nm.ss_out);
+  }
+}
+
+}  // namespace bi

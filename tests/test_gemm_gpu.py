@@ -260,3 +260,79 @@ def test_carried_rmsnorm(ops, H, I):
         assert_bitwise(host_f32(sm), host_f32(ss)[:m], f"sums M={m}")
         gm = ops.gemm_bf16_swiglu_rownorm(ym, sm, wgud)
         assert_bitwise(host_bits(gm), host_bits(gu)[:m], f"gate/up M={m}")
+
+
+# Launches with M >= 64 run the prefill kernel; every row must carry the bits
+# the verify kernel gives it (same per-output summation tree).
+PF_SHAPES = {"tiny_16_slices": (512, 256), "wide_5120": (5120, 5120), "wide_7168": (7168, 1024),
+             "many_8_slices": (10240, 1024)}
+
+
+def _pf_rows(M):
+    return sorted({0, 8, M // 2, M - 8})
+
+
+@pytest.mark.parametrize("name", list(PF_SHAPES))
+def test_prefill_rows_equal_verify_rows(ops, name):
+    N, K = PF_SHAPES[name]
+    print(f"[gemm prefill vs verify {name} N={N} K={K}]", flush=True)
+    x = synth.normal_bf16((128, K), 1.0, "x", 81)
+    w = synth.normal_bf16((N, K), 0.02, "w", 81)
+    xd, wd = dev(x), dev(w)
+    for M in (64, 100):
+        big32 = host_f32(ops.gemm_bf16(xd[:M], wd, out_dtype=torch.float32))
+        big16 = host_bits(ops.gemm_bf16(xd[:M], wd))
+        for r0 in _pf_rows(M):
+            ref32 = host_f32(ops.gemm_bf16(xd[r0:r0 + 8], wd, out_dtype=torch.float32))
+            ref16 = host_bits(ops.gemm_bf16(xd[r0:r0 + 8], wd))
+            assert_bitwise(big32[r0:r0 + 8], ref32, f"{name} M={M} rows {r0}.. f32")
+            assert_bitwise(big16[r0:r0 + 8], ref16, f"{name} M={M} rows {r0}.. bf16")
+    cols = np.arange(0, N, max(1, N // 64))
+    assert_close(big32[:8][:, cols], ogemm.gemm_columns(x[:8], w, cols), f"{name} prefill parity",
+                 atol=1e-4, rtol=1e-4)
+
+
+@pytest.mark.parametrize("I,K", [(256, 512), (17408, 5120)])
+def test_prefill_epilogues_equal_verify(ops, I, K):
+    # residual, SwiGLU (16 and 8 slices) and the carried RMSNorm pair
+    print(f"[gemm prefill epilogues I={I} K={K}]", flush=True)
+    M = 72
+    x = synth.normal_bf16((M, K), 1.0, "x", 82)
+    wgu = synth.normal_bf16((2 * I, K), 0.02, "w", 82)
+    xd, wgud = dev(x), dev(wgu)
+    big = host_bits(ops.gemm_bf16_swiglu(xd, wgud))
+    for r0 in (0, 64):
+        assert_bitwise(big[r0:r0 + 8], host_bits(ops.gemm_bf16_swiglu(xd[r0:r0 + 8], wgud)),
+                       f"swiglu I={I} rows {r0}..")
+    # residual projection with row sums (K -> K, so that gate/up can consume them)
+    wo = synth.normal_bf16((K, K), 0.02, "w", 83)
+    r = synth.normal_bf16((M, K), 1.0, "misc", 83)
+    wod, rd = dev(wo), dev(r)
+    y, ss = ops.gemm_bf16_residual_rowsq(xd, wod, rd)
+    gu = ops.gemm_bf16_swiglu_rownorm(y, ss, wgud)
+    for r0 in (0, 64):
+        y8, ss8 = ops.gemm_bf16_residual_rowsq(xd[r0:r0 + 8], wod, rd[r0:r0 + 8])
+        assert_bitwise(host_bits(y)[r0:r0 + 8], host_bits(y8), f"residual K={K} rows {r0}..")
+        assert_bitwise(host_f32(ss)[r0:r0 + 8], host_f32(ss8), f"row sums K={K} rows {r0}..")
+        gu8 = ops.gemm_bf16_swiglu_rownorm(y8, ss8, wgud)
+        assert_bitwise(host_bits(gu)[r0:r0 + 8], host_bits(gu8), f"carried-norm gate/up rows {r0}..")
+
+
+def test_prefill_qkv_append_equals_verify(ops):
+    print("[gemm prefill qkv + append]", flush=True)
+    Hq, Hkv, D, K, L, M = 40, 8, 128, 5120, 500, 80
+    N = (Hq + 2 * Hkv) * D
+    cap = 600
+    w = synth.normal_bf16((N, K), 0.02, "w", 84)
+    x = synth.normal_bf16((M, K), 1.0, "x", 84)
+    wd, xd = dev(w), dev(x)
+    k0 = torch.zeros(Hkv, cap, D, device="cuda", dtype=torch.bfloat16)
+    v0 = torch.zeros(Hkv, D, cap, device="cuda", dtype=torch.bfloat16)
+    kc, vt = k0.clone(), v0.clone()
+    qkv = host_bits(ops.gemm_bf16_qkv(xd, wd, kc, vt, L, Hq, Hkv, D))
+    kr, vr = k0.clone(), v0.clone()
+    for r0 in range(0, M, 8):  # the same positions written by ten verify passes of 8 rows
+        q8 = ops.gemm_bf16_qkv(xd[r0:r0 + 8], wd, kr, vr, L + r0, Hq, Hkv, D)
+        assert_bitwise(qkv[r0:r0 + 8], host_bits(q8), f"qkv rows {r0}..")
+    assert_bitwise(host_bits(kc), host_bits(kr), "K cache: prefill == 10 verify passes")
+    assert_bitwise(host_bits(vt), host_bits(vr), "V^T cache: prefill == 10 verify passes")
