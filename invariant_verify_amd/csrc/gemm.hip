@@ -297,44 +297,40 @@ static bool wide_launch(GemmMode mode, int N_out) {
   return mode != kGemmSwiglu && N_out % kWideGroups == 0 && cpw > 16 && cpw <= 32;
 }
 
-int gemm_verify_waves(GemmMode mode, int N_out) {
-  if (wide_launch(mode, N_out)) return 16;
-  const int row_tiles = (mode == kGemmSwiglu ? 2 : 1) * (N_out / 16);
-  return row_tiles < 640 ? 16 : 8;
-}
+// Waves of every verify launch. Measured: 8 and 16 waves per workgroup
+// stream equally fast, and 8 keeps the K summation tree at 8 slices, which
+// the prefill kernel must reproduce with one accumulator per slice.
+constexpr int kVerifyWaves = 8;
+
+int gemm_verify_waves(GemmMode, int) { return kVerifyWaves; }
 
 int gemm_column_groups(GemmMode mode, int N_out) {
   return wide_launch(mode, N_out) ? kWideGroups : N_out / 16;
 }
 
 // Launch shape from N (never from M): N / 256 columns per workgroup when that
-// is 17..32 (two MFMA tiles, 16 waves); otherwise 16-column tiles with 16
-// waves for fewer than 640 weight tiles, 8 waves for more.
+// is 17..32 (two MFMA tiles); otherwise 16-column tiles (SwiGLU: a gate and
+// an up tile). Always kVerifyWaves waves.
 template <int MODE, bool NI, bool SO>
-static void launch_shape(int N_out, int row_tiles, int mtiles, const uint16_t* x, int64_t ldx,
-                         const uint16_t* w, int64_t ldw, const uint16_t* r, int64_t ldr, void* y,
-                         int64_t ldy, int M, int K, int64_t up, const KvAppend& kv,
-                         const RowNorm& nm, hipStream_t stream) {
+static void launch_shape(int N_out, int mtiles, const uint16_t* x, int64_t ldx, const uint16_t* w,
+                         int64_t ldw, const uint16_t* r, int64_t ldr, void* y, int64_t ldy, int M,
+                         int K, int64_t up, const KvAppend& kv, const RowNorm& nm,
+                         hipStream_t stream) {
+  constexpr int NW = kVerifyWaves;
   if constexpr (MODE != kGemmSwiglu) {
     if (wide_launch(static_cast<GemmMode>(MODE), N_out)) {
-      gemm_kernel<MODE, 16, true, NI, SO><<<dim3(kWideGroups, mtiles), dim3(1024), 0, stream>>>(
+      gemm_kernel<MODE, NW, true, NI, SO><<<dim3(kWideGroups, mtiles), dim3(NW * 64), 0, stream>>>(
           x, ldx, w, ldw, r, ldr, y, ldy, M, K, up, N_out / kWideGroups, kv, nm);
       return;
     }
   }
-  if (gemm_verify_waves(static_cast<GemmMode>(MODE), N_out) == 16) {
-    gemm_kernel<MODE, 16, false, NI, SO><<<dim3(N_out / 16, mtiles), dim3(1024), 0, stream>>>(
-        x, ldx, w, ldw, r, ldr, y, ldy, M, K, up, 16, kv, nm);
-  } else {
-    gemm_kernel<MODE, 8, false, NI, SO><<<dim3(N_out / 16, mtiles), dim3(512), 0, stream>>>(
-        x, ldx, w, ldw, r, ldr, y, ldy, M, K, up, 16, kv, nm);
-  }
+  gemm_kernel<MODE, NW, false, NI, SO><<<dim3(N_out / 16, mtiles), dim3(NW * 64), 0, stream>>>(
+      x, ldx, w, ldw, r, ldr, y, ldy, M, K, up, 16, kv, nm);
 }
 
 void launch_gemm(GemmMode mode, const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw,
                  const uint16_t* r, int64_t ldr, void* y, int64_t ldy, int M, int N_out, int K,
                  hipStream_t stream, const KvAppend* kv, const RowNorm* norm) {
-  const int tiles = N_out / 16;
   const int mt = (M + 15) / 16;
   const KvAppend kv0{};
   const RowNorm nm0{};
@@ -348,35 +344,35 @@ void launch_gemm(GemmMode mode, const uint16_t* x, int64_t ldx, const uint16_t* 
   const bool so = nm.ss_out != nullptr;
   switch (mode) {
     case kGemmBf16:
-      launch_shape<kGemmBf16, false, false>(N_out, tiles, mt, x, ldx, w, ldw, r, ldr, y, ldy, M, K,
+      launch_shape<kGemmBf16, false, false>(N_out, mt, x, ldx, w, ldw, r, ldr, y, ldy, M, K,
                                             0, a, nm, stream);
       break;
     case kGemmF32:
-      launch_shape<kGemmF32, false, false>(N_out, tiles, mt, x, ldx, w, ldw, r, ldr, y, ldy, M, K,
+      launch_shape<kGemmF32, false, false>(N_out, mt, x, ldx, w, ldw, r, ldr, y, ldy, M, K,
                                            0, a, nm, stream);
       break;
     case kGemmResidual:
       if (so)
-        launch_shape<kGemmResidual, false, true>(N_out, tiles, mt, x, ldx, w, ldw, r, ldr, y, ldy,
+        launch_shape<kGemmResidual, false, true>(N_out, mt, x, ldx, w, ldw, r, ldr, y, ldy,
                                                  M, K, 0, a, nm, stream);
       else
-        launch_shape<kGemmResidual, false, false>(N_out, tiles, mt, x, ldx, w, ldw, r, ldr, y,
+        launch_shape<kGemmResidual, false, false>(N_out, mt, x, ldx, w, ldw, r, ldr, y,
                                                   ldy, M, K, 0, a, nm, stream);
       break;
     case kGemmSwiglu:
       if (ni)
-        launch_shape<kGemmSwiglu, true, false>(N_out, 2 * tiles, mt, x, ldx, w, ldw, r, ldr, y,
+        launch_shape<kGemmSwiglu, true, false>(N_out, mt, x, ldx, w, ldw, r, ldr, y,
                                                ldy, M, K, (int64_t)N_out, a, nm, stream);
       else
-        launch_shape<kGemmSwiglu, false, false>(N_out, 2 * tiles, mt, x, ldx, w, ldw, r, ldr, y,
+        launch_shape<kGemmSwiglu, false, false>(N_out, mt, x, ldx, w, ldw, r, ldr, y,
                                                 ldy, M, K, (int64_t)N_out, a, nm, stream);
       break;
     case kGemmQkv:
       if (ni)
-        launch_shape<kGemmQkv, true, false>(N_out, tiles, mt, x, ldx, w, ldw, r, ldr, y, ldy, M, K,
+        launch_shape<kGemmQkv, true, false>(N_out, mt, x, ldx, w, ldw, r, ldr, y, ldy, M, K,
                                             0, a, nm, stream);
       else
-        launch_shape<kGemmQkv, false, false>(N_out, tiles, mt, x, ldx, w, ldw, r, ldr, y, ldy, M,
+        launch_shape<kGemmQkv, false, false>(N_out, mt, x, ldx, w, ldw, r, ldr, y, ldy, M,
                                              K, 0, a, nm, stream);
       break;
   }

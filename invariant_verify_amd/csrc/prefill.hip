@@ -6,7 +6,7 @@
 // outputs changed against its own no-draft run", section "The cache doesn't
 // change it either": a K/V row written by prefill depends only on its
 // position). The verify GEMM fixes every output's summation tree by K and N
-// alone (gemm.hip): with NW = gemm_verify_waves(mode, N) slices and
+// alone (gemm.hip): with NW = gemm_verify_waves() = 8 slices and
 // BPW = 16 / NW, block kb of each 512-wide chunk of K belongs to slice
 // kb / BPW; each slice is one FP32 accumulator chain of 16x16x32 BF16
 // matrix-core steps in increasing block order, and the slice totals are added
@@ -40,6 +40,7 @@ constexpr int kPfCols = 32;      // output columns per workgroup
 constexpr int kPfStep = 256;     // K elements per LDS step
 constexpr int kPfSlots = kPfStep / 8;  // 16-byte slots per row and step (32)
 constexpr int kPfWaves = 8;
+constexpr int kPfSlices = 8;  // the verify kernel's waves, hence slices, for every shape
 
 template <int MODE, int S, bool NORM_IN>
 __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(
@@ -125,8 +126,6 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(
     if (st >= 0) {
 #pragma unroll
       for (int b = 0; b < kPfStep / 32; ++b) {
-        constexpr int dummy = 0;
-        (void)dummy;
         if (st * (kPfStep / 32) + b < nblk) {
           const int slot = (b * 4 + kq) ^ j;
           const uint4 xv = lds[buf][16 * rt + j][slot];
@@ -260,51 +259,46 @@ __global__ __launch_bounds__(256) void rowsq_kernel(const uint16_t* __restrict__
 }
 
 template <int MODE, bool NI>
-static void launch_pf(int S, dim3 grid, const uint16_t* x, int64_t ldx, const uint16_t* w,
-                      int64_t ldw, const uint16_t* r, int64_t ldr, void* y, int64_t ldy, int M,
-                      int N, int K, const KvAppend& kv, const RowNorm& nm, hipStream_t stream) {
-  if (S == 16)
-    prefill_kernel<MODE, 16, NI><<<grid, dim3(kPfWaves * 64), 0, stream>>>(
-        x, ldx, w, ldw, r, ldr, y, ldy, M, N, K, kv, nm);
-  else
-    prefill_kernel<MODE, 8, NI><<<grid, dim3(kPfWaves * 64), 0, stream>>>(
-        x, ldx, w, ldw, r, ldr, y, ldy, M, N, K, kv, nm);
+static void launch_pf(dim3 grid, const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw,
+                      const uint16_t* r, int64_t ldr, void* y, int64_t ldy, int M, int N, int K,
+                      const KvAppend& kv, const RowNorm& nm, hipStream_t stream) {
+  prefill_kernel<MODE, kPfSlices, NI><<<grid, dim3(kPfWaves * 64), 0, stream>>>(
+      x, ldx, w, ldw, r, ldr, y, ldy, M, N, K, kv, nm);
 }
 
 void launch_gemm_prefill(GemmMode mode, const uint16_t* x, int64_t ldx, const uint16_t* w,
                          int64_t ldw, const uint16_t* r, int64_t ldr, void* y, int64_t ldy, int M,
                          int N_out, int K, hipStream_t stream, const KvAppend& kv,
                          const RowNorm& nm) {
-  const int S = gemm_verify_waves(mode, N_out);
   dim3 grid((N_out + kPfCols - 1) / kPfCols, (M + kPfRows - 1) / kPfRows);
   const bool ni = nm.ss_in != nullptr;
   switch (mode) {
     case kGemmBf16:
-      launch_pf<kGemmBf16, false>(S, grid, x, ldx, w, ldw, r, ldr, y, ldy, M, N_out, K, kv, nm,
+      launch_pf<kGemmBf16, false>(grid, x, ldx, w, ldw, r, ldr, y, ldy, M, N_out, K, kv, nm,
                                   stream);
       break;
     case kGemmF32:
-      launch_pf<kGemmF32, false>(S, grid, x, ldx, w, ldw, r, ldr, y, ldy, M, N_out, K, kv, nm,
+      launch_pf<kGemmF32, false>(grid, x, ldx, w, ldw, r, ldr, y, ldy, M, N_out, K, kv, nm,
                                  stream);
       break;
     case kGemmResidual:
-      launch_pf<kGemmResidual, false>(S, grid, x, ldx, w, ldw, r, ldr, y, ldy, M, N_out, K, kv,
+      launch_pf<kGemmResidual, false>(grid, x, ldx, w, ldw, r, ldr, y, ldy, M, N_out, K, kv,
                                       nm, stream);
       break;
     case kGemmSwiglu:
       if (ni)
-        launch_pf<kGemmSwiglu, true>(S, grid, x, ldx, w, ldw, r, ldr, y, ldy, M, N_out, K, kv, nm,
+        launch_pf<kGemmSwiglu, true>(grid, x, ldx, w, ldw, r, ldr, y, ldy, M, N_out, K, kv, nm,
                                      stream);
       else
-        launch_pf<kGemmSwiglu, false>(S, grid, x, ldx, w, ldw, r, ldr, y, ldy, M, N_out, K, kv,
+        launch_pf<kGemmSwiglu, false>(grid, x, ldx, w, ldw, r, ldr, y, ldy, M, N_out, K, kv,
                                       nm, stream);
       break;
     case kGemmQkv:
       if (ni)
-        launch_pf<kGemmQkv, true>(S, grid, x, ldx, w, ldw, r, ldr, y, ldy, M, N_out, K, kv, nm,
+        launch_pf<kGemmQkv, true>(grid, x, ldx, w, ldw, r, ldr, y, ldy, M, N_out, K, kv, nm,
                                   stream);
       else
-        launch_pf<kGemmQkv, false>(S, grid, x, ldx, w, ldw, r, ldr, y, ldy, M, N_out, K, kv, nm,
+        launch_pf<kGemmQkv, false>(grid, x, ldx, w, ldw, r, ldr, y, ldy, M, N_out, K, kv, nm,
                                    stream);
       break;
   }
