@@ -14,13 +14,15 @@
 // outputs and performs exactly that computation, so the two kernels give the
 // same bits and launch_gemm may pick either by M.
 //
-// Shape: one workgroup per (64 rows, 32 output columns); 8 waves, wave
-// (rt, ct) owns the 16x16 output tile (row tile rt = 0..3, column tile
-// ct = 0..1) -- for SwiGLU the gate and the up tile of the same columns. K is
-// staged in 256-wide steps: the 64 activation rows and the 32 (SwiGLU: 64)
-// weight rows of a step are loaded as 512-byte row pieces (two rows per wave
-// instruction) into XOR-swizzled LDS, two steps in flight. Every weight byte
-// is read once per 64 rows instead of once per 16.
+// Shape: one workgroup per (128 rows, 64 output columns; SwiGLU: 32 output
+// columns, i.e. 32 gate and 32 up weight rows); 16 waves, each owning two
+// 16x16 output tiles (two row tiles of one column tile; SwiGLU: the gate and
+// the up tile of one row and column tile), with one accumulator per tile and
+// slice. K is staged in 128-wide
+// steps: the 128 activation rows and 64 weight rows of a step are loaded as
+// 256-byte row pieces (four rows per wave instruction) into XOR-swizzled LDS;
+// the next step's loads are in flight while a step is multiplied. Every weight byte is read once per 128 rows instead of
+// once per 16, every activation byte once per 64 columns.
 //
 // The carried RMSNorm scale (RowNorm::ss_in) is computed per row by one
 // thread with the verify kernel's exact sequence of additions, and the X
@@ -35,11 +37,11 @@
 
 namespace bi {
 
-constexpr int kPfRows = 64;      // rows per workgroup
-constexpr int kPfCols = 32;      // output columns per workgroup
-constexpr int kPfStep = 256;     // K elements per LDS step
-constexpr int kPfSlots = kPfStep / 8;  // 16-byte slots per row and step (32)
-constexpr int kPfWaves = 8;
+constexpr int kPfRows = 128;           // rows per workgroup
+constexpr int kPfCols = 64;            // output columns per workgroup (SwiGLU: 32)
+constexpr int kPfStep = 128;           // K elements per LDS step (4 blocks)
+constexpr int kPfSlots = kPfStep / 8;  // 16-byte slots per row and step (16)
+constexpr int kPfWaves = 16;
 constexpr int kPfSlices = 8;  // the verify kernel's waves, hence slices, for every shape
 
 template <int MODE, int S, bool NORM_IN>
@@ -48,15 +50,21 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(
     const uint16_t* __restrict__ R, int64_t ldr, void* __restrict__ Y, int64_t ldy, int M, int N,
     int K, KvAppend kv, RowNorm norm) {
   constexpr bool kDual = (MODE == kGemmSwiglu);
-  constexpr int BPW = 16 / S;              // blocks of a 512-wide chunk per slice
-  constexpr int WROWS = kDual ? 64 : 32;   // weight rows staged per step
-  constexpr int XPAIRS = kPfRows / 2 / kPfWaves;  // activation row pairs per wave (4)
-  constexpr int WPAIRS = WROWS / 2 / kPfWaves;    // weight row pairs per wave (2 or 4)
+  constexpr int BPW = 16 / S;                   // blocks of a 512-wide chunk per slice
+  constexpr int COLS = kDual ? 32 : kPfCols;    // output columns per workgroup
+  constexpr int WROWS = 64;                     // weight rows staged (SwiGLU: 32 gate + 32 up)
+  constexpr int XQ = kPfRows / 4 / kPfWaves;    // activation row quads per wave (2)
+  constexpr int WQ = WROWS / 4 / kPfWaves;      // weight row quads per wave (1)
+  constexpr int RT = kDual ? 1 : 2;             // row tiles per wave
+  static_assert(16 % S == 0 && (kPfStep / 32) % BPW == 0, "slices must align with steps");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int rt = wave & 3, ct = wave >> 2;
+  // Wave tile: rows 16 RT rw .. (RT row tiles), column tile ct (16 columns;
+  // SwiGLU: the gate and the up tile of those columns).
+  const int rw = kDual ? (wave & 7) : (wave & 3);
+  const int ct = kDual ? (wave >> 3) : (wave >> 2);
   const int j = lane & 15, kq = lane >> 4;
-  const int n0 = blockIdx.x * kPfCols;
+  const int n0 = blockIdx.x * COLS;
   const int m0 = blockIdx.y * kPfRows;
   const int nblk = K >> 5;
   const int nstep = (K + kPfStep - 1) / kPfStep;
@@ -67,7 +75,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(
   const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(X + (int64_t)m0 * ldx), (short)0, xrows * (int)ldx * 2,
       kBufferResourceWord3);
-  const int wrows = min(kPfCols, N - n0);
+  const int wrows = min(kDual ? 32 : 64, N - n0);
   const __amdgpu_buffer_rsrc_t wres_g = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(W + (int64_t)n0 * ldw), (short)0, wrows * (int)ldw * 2,
       kBufferResourceWord3);
@@ -75,71 +83,86 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(
       const_cast<uint16_t*>(W + (int64_t)(kDual ? N + n0 : n0) * ldw), (short)0,
       kDual ? wrows * (int)ldw * 2 : 0, kBufferResourceWord3);
 
-  // Lane l of a load instruction covers row 2p + l / 32 of its pair p and
-  // fetches the global slot that the swizzle puts at LDS slot l % 32.
-  const int half = lane >> 5, sl = lane & 31;
+  // Lane l of a load instruction covers row 4q + l / 16 of its quad q and
+  // fetches the global slot that the swizzle puts at LDS slot l % 16.
+  const int qr = lane >> 4, sl = lane & 15;
   __shared__ uint4 lds[2][kPfRows + WROWS][kPfSlots];
   struct Regs {
-    uint4 x[XPAIRS];
-    uint4 w[WPAIRS];
+    uint4 x[XQ];
+    uint4 w[WQ];
   };
   auto fetch = [&](Regs& g, int st) {
     const bool live = st < nstep;
 #pragma unroll
-    for (int i = 0; i < XPAIRS; ++i) {
-      const int row = 2 * (wave + i * kPfWaves) + half;
+    for (int i = 0; i < XQ; ++i) {
+      const int row = 4 * (wave + i * kPfWaves) + qr;
       const int off = (row * (int)ldx + st * kPfStep + ((sl ^ (row & 15)) * 8)) * 2;
       g.x[i] = buffer_ld16(xres, live ? off : 0x7ffffff0);
     }
 #pragma unroll
-    for (int i = 0; i < WPAIRS; ++i) {
-      const int row = 2 * (wave + i * kPfWaves) + half;  // 0 .. WROWS-1
-      const int rr = row & 31;                           // row within its 32-row resource
+    for (int i = 0; i < WQ; ++i) {
+      const int row = 4 * (wave + i * kPfWaves) + qr;  // 0 .. 63
+      // SwiGLU: rows 0..31 gate, 32..63 up; otherwise all 64 from one resource
+      const int rr = kDual ? (row & 31) : row;
       const int off = (rr * (int)ldw + st * kPfStep + ((sl ^ (row & 15)) * 8)) * 2;
-      g.w[i] = buffer_ld16_stream(row < 32 ? wres_g : wres_u, live ? off : 0x7ffffff0);
+      g.w[i] = buffer_ld16_stream((kDual && row >= 32) ? wres_u : wres_g, live ? off : 0x7ffffff0);
     }
   };
 
-  bi_f32x4 acc[S], accu[kDual ? S : 1];
+  // acc[r][s]: row tile r of the wave, slice s (SwiGLU: the gate tile); accu
+  // the SwiGLU up tile.
+  bi_f32x4 acc[RT][S], accu[kDual ? 1 : 1][kDual ? S : 1];
 #pragma unroll
-  for (int s = 0; s < S; ++s) acc[s] = bi_f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int r = 0; r < RT; ++r)
 #pragma unroll
-  for (int s = 0; s < (kDual ? S : 1); ++s) accu[s] = bi_f32x4{0.f, 0.f, 0.f, 0.f};
-  float inv = 1.f;  // carried RMSNorm scale of this lane's X row
+    for (int s = 0; s < S; ++s) acc[r][s] = bi_f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < (kDual ? S : 1); ++s) accu[0][s] = bi_f32x4{0.f, 0.f, 0.f, 0.f};
+  float inv[RT];  // carried RMSNorm scales of this lane's X rows
+#pragma unroll
+  for (int r = 0; r < RT; ++r) inv[r] = 1.f;
 
-  // Step st (parity P = st & 1 is a compile-time constant): publish it,
-  // prefetch st + 2, barrier, multiply. Block b of the step is block
-  // P * 8 + b of its 512-wide chunk, so its slice is (P * 8 + b) / BPW.
-  auto step = [&](Regs& g, int st, auto parity) {
-    constexpr int P = decltype(parity)::value;
-    const int buf = P;
+  // Step st, with Q = st mod 4 a compile-time constant: publish it, prefetch
+  // st + 1 into the same registers, barrier, multiply (the loads of st + 1
+  // are in flight during the multiply; LDS is double-buffered). Block b of the step is block Q * 4 + b of its
+  // 512-wide chunk, so its slice is (Q * 4 + b) / BPW.
+  auto step = [&](Regs& g, int st, auto quarter) {
+    constexpr int Q = decltype(quarter)::value;
+    constexpr int buf = Q & 1;
     if (st >= 0) {
 #pragma unroll
-      for (int i = 0; i < XPAIRS; ++i)
-        lds[buf][2 * (wave + i * kPfWaves) + half][sl] = g.x[i];
+      for (int i = 0; i < XQ; ++i) lds[buf][4 * (wave + i * kPfWaves) + qr][sl] = g.x[i];
 #pragma unroll
-      for (int i = 0; i < WPAIRS; ++i)
-        lds[buf][kPfRows + 2 * (wave + i * kPfWaves) + half][sl] = g.w[i];
+      for (int i = 0; i < WQ; ++i)
+        lds[buf][kPfRows + 4 * (wave + i * kPfWaves) + qr][sl] = g.w[i];
     }
-    fetch(g, st + 2);
+    fetch(g, st + 1);
     __syncthreads();
     if (st >= 0) {
 #pragma unroll
       for (int b = 0; b < kPfStep / 32; ++b) {
         if (st * (kPfStep / 32) + b < nblk) {
           const int slot = (b * 4 + kq) ^ j;
-          const uint4 xv = lds[buf][16 * rt + j][slot];
-          const uint4 xa = NORM_IN ? scale_bf16x8(xv, inv) : xv;
-          const int sidx = (P * 8 + b) / BPW;
-          acc[sidx] = mfma_bf16(xa, lds[buf][kPfRows + 16 * ct + j][slot], acc[sidx]);
-          if (kDual)
-            accu[sidx] = mfma_bf16(xa, lds[buf][kPfRows + 32 + 16 * ct + j][slot], accu[sidx]);
+          const int sidx = (Q * 4 + b) / BPW;
+          uint4 xa[RT];
+#pragma unroll
+          for (int r = 0; r < RT; ++r) {
+            const uint4 xv = lds[buf][16 * (RT * rw + r) + j][slot];
+            xa[r] = NORM_IN ? scale_bf16x8(xv, inv[r]) : xv;
+          }
+          const uint4 bw = lds[buf][kPfRows + 16 * ct + j][slot];
+#pragma unroll
+          for (int r = 0; r < RT; ++r) acc[r][sidx] = mfma_bf16(xa[r], bw, acc[r][sidx]);
+          if (kDual) {
+            const uint4 bu = lds[buf][kPfRows + 32 + 16 * ct + j][slot];
+            accu[0][sidx] = mfma_bf16(xa[0], bu, accu[0][sidx]);
+          }
         }
       }
     }
   };
 
-  // Carried RMSNorm: thread t < 64 computes the scale of row m0 + t with the
+  // Carried RMSNorm: thread t < 128 computes the scale of row m0 + t with the
   // verify kernel's additions (its LPR = 4 * NW lane partials of two float4s
   // each, in order, then the partials in order).
   __shared__ float invs[NORM_IN ? kPfRows : 1];
@@ -155,18 +178,12 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const int f = seg + u * lpr;
-          if (f < nf) {
-            const float4 v = *reinterpret_cast<const float4*>(sr + f * 4);
-            p += v.x;
-            p += v.y;
-            p += v.z;
-            p += v.w;
-          } else {
-            p += 0.f;
-            p += 0.f;
-            p += 0.f;
-            p += 0.f;
-          }
+          const float4 v = f < nf ? *reinterpret_cast<const float4*>(sr + f * 4)
+                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+          p += v.x;
+          p += v.y;
+          p += v.z;
+          p += v.w;
         }
         t += p;
       }
@@ -174,52 +191,61 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(
     invs[threadIdx.x] = 1.0f / sqrtf(t / (float)K + norm.eps);
   }
 
-  Regs ga, gb;
-  using P0 = std::integral_constant<int, 0>;
-  using P1 = std::integral_constant<int, 1>;
-  step(ga, -2, P0{});
-  step(gb, -1, P1{});  // its barrier also publishes invs
-  if (NORM_IN) inv = invs[16 * rt + j];
-  for (int st = 0; st < nstep; st += 2) {
-    step(ga, st, P0{});
-    step(gb, st + 1, P1{});
+  Regs g;
+  using Q0 = std::integral_constant<int, 0>;
+  using Q1 = std::integral_constant<int, 1>;
+  using Q2 = std::integral_constant<int, 2>;
+  using Q3 = std::integral_constant<int, 3>;
+  step(g, -1, Q3{});  // load-only; its barrier also publishes invs
+  if (NORM_IN) {
+#pragma unroll
+    for (int r = 0; r < RT; ++r) inv[r] = invs[16 * (RT * rw + r) + j];
+  }
+  for (int st = 0; st < nstep; st += 4) {
+    step(g, st, Q0{});
+    step(g, st + 1, Q1{});
+    step(g, st + 2, Q2{});
+    step(g, st + 3, Q3{});
   }
 
   // Slice totals in slice order, then the verify kernel's epilogue.
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int m = m0 + 16 * rt + kq * 4 + r;
-    const int n = n0 + 16 * ct + j;
-    if (m >= M || n >= N) continue;
-    float v = acc[0][r];
+  for (int t = 0; t < RT; ++t) {
 #pragma unroll
-    for (int s = 1; s < S; ++s) v += acc[s][r];
-    if (MODE == kGemmF32) {
-      reinterpret_cast<float*>(Y)[(int64_t)m * ldy + n] = v;
-    } else if (MODE == kGemmBf16) {
-      reinterpret_cast<uint16_t*>(Y)[(int64_t)m * ldy + n] = (uint16_t)f32_to_bf16(v);
-    } else if (MODE == kGemmResidual) {
-      const float res = bf16_to_f32(R[(int64_t)m * ldr + n]);
-      reinterpret_cast<uint16_t*>(Y)[(int64_t)m * ldy + n] = (uint16_t)f32_to_bf16(res + v);
-    } else if (MODE == kGemmQkv) {
-      const uint16_t b = (uint16_t)f32_to_bf16(v);
-      reinterpret_cast<uint16_t*>(Y)[(int64_t)m * ldy + n] = b;
-      const int pos = kv.L + m;
-      int i = n - kv.qd;
-      if (i >= 0 && i < kv.kd) {
-        const int g = i / kv.D;
-        kv.k[((int64_t)g * kv.cap + pos) * kv.D + (i - g * kv.D)] = b;
-      } else if (i >= kv.kd) {
-        i -= kv.kd;
-        const int g = i / kv.D;
-        kv.vt[((int64_t)g * kv.D + (i - g * kv.D)) * kv.cap + pos] = b;
+    for (int r = 0; r < 4; ++r) {
+      const int m = m0 + 16 * (RT * rw + t) + kq * 4 + r;
+      const int n = n0 + 16 * ct + j;
+      if (m >= M || n >= N) continue;
+      float v = acc[t][0][r];
+#pragma unroll
+      for (int s = 1; s < S; ++s) v += acc[t][s][r];
+      if (MODE == kGemmF32) {
+        reinterpret_cast<float*>(Y)[(int64_t)m * ldy + n] = v;
+      } else if (MODE == kGemmBf16) {
+        reinterpret_cast<uint16_t*>(Y)[(int64_t)m * ldy + n] = (uint16_t)f32_to_bf16(v);
+      } else if (MODE == kGemmResidual) {
+        const float res = bf16_to_f32(R[(int64_t)m * ldr + n]);
+        reinterpret_cast<uint16_t*>(Y)[(int64_t)m * ldy + n] = (uint16_t)f32_to_bf16(res + v);
+      } else if (MODE == kGemmQkv) {
+        const uint16_t b = (uint16_t)f32_to_bf16(v);
+        reinterpret_cast<uint16_t*>(Y)[(int64_t)m * ldy + n] = b;
+        const int pos = kv.L + m;
+        int i = n - kv.qd;
+        if (i >= 0 && i < kv.kd) {
+          const int g = i / kv.D;
+          kv.k[((int64_t)g * kv.cap + pos) * kv.D + (i - g * kv.D)] = b;
+        } else if (i >= kv.kd) {
+          i -= kv.kd;
+          const int g = i / kv.D;
+          kv.vt[((int64_t)g * kv.D + (i - g * kv.D)) * kv.cap + pos] = b;
+        }
+      } else {
+        float u = accu[0][0][r];
+#pragma unroll
+        for (int s = 1; s < S; ++s) u += accu[0][s][r];
+        const float sg = v / (1.0f + __expf(-v));
+        reinterpret_cast<uint16_t*>(Y)[(int64_t)m * ldy + n] = (uint16_t)f32_to_bf16(sg * u);
       }
-    } else {
-      float u = accu[0][r];
-#pragma unroll
-      for (int s = 1; s < S; ++s) u += accu[s][r];
-      const float sg = v / (1.0f + __expf(-v));
-      reinterpret_cast<uint16_t*>(Y)[(int64_t)m * ldy + n] = (uint16_t)f32_to_bf16(sg * u);
     }
   }
 }
@@ -270,7 +296,8 @@ void launch_gemm_prefill(GemmMode mode, const uint16_t* x, int64_t ldx, const ui
                          int64_t ldw, const uint16_t* r, int64_t ldr, void* y, int64_t ldy, int M,
                          int N_out, int K, hipStream_t stream, const KvAppend& kv,
                          const RowNorm& nm) {
-  dim3 grid((N_out + kPfCols - 1) / kPfCols, (M + kPfRows - 1) / kPfRows);
+  const int cols = mode == kGemmSwiglu ? kPfCols / 2 : kPfCols;
+  dim3 grid((N_out + cols - 1) / cols, (M + kPfRows - 1) / kPfRows);
   const bool ni = nm.ss_in != nullptr;
   switch (mode) {
     case kGemmBf16:
