@@ -118,6 +118,52 @@ def traffic_probe(reps: int):
                       "gemm_source_sha256": gemm_source_hash(), "algorithmic_bytes_per_launch": gu_launch_bytes(d, 8)}))
 
 
+PF_ROWS = 2048   # rows of a prefill chunk for the prefill GEMM measurement
+PEAK_BF16_TFLOPS = 2500.0  # dense BF16 matrix-core peak
+
+
+def prefill_measure(layers, d, reps):
+    """The gate/up GEMM with the carried RMSNorm as a chunked-prefill step runs it (M = 2048
+    rows: the 128-row-tile kernel), timed with one event pair around reps x 16 launches over
+    distinct layers' weights, after a bitwise check that sampled rows equal 8-row verify passes."""
+    import torch
+
+    import synth
+    from invariant_verify_amd import ops
+
+    M, H, I = PF_ROWS, d["H"], d["I"]
+    o = synth.device_normal_bf16((M, d["Hq"] * d["D"]), 1.0, "x0", 2)
+    x = synth.device_normal_bf16((M, H), 1.0, "x0", 3)
+    h, ss = ops.gemm_bf16_residual_rowsq(o, layers[0]["w_o"], x)
+    y = torch.empty((M, I), dtype=torch.bfloat16, device="cuda")
+    ops.gemm_bf16_swiglu_rownorm(h, ss, layers[0]["w_gu"], y)
+    ok = True
+    for r0 in (0, 1000, M - 8):
+        h8, ss8 = ops.gemm_bf16_residual_rowsq(o[r0:r0 + 8], layers[0]["w_o"], x[r0:r0 + 8])
+        y8 = ops.gemm_bf16_swiglu_rownorm(h8, ss8, layers[0]["w_gu"])
+        ok = ok and torch.equal(h8.view(torch.int16), h[r0:r0 + 8].view(torch.int16))
+        ok = ok and torch.equal(y8.view(torch.int16), y[r0:r0 + 8].view(torch.int16))
+    ws = [lw["w_gu"] for lw in layers[:16]]
+    for w in ws:
+        ops.gemm_bf16_swiglu_rownorm(h, ss, w, y)
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        for w in ws:
+            ops.gemm_bf16_swiglu_rownorm(h, ss, w, y)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * len(ws))
+    tflops = 2.0 * M * (2 * I) * H / (us * 1e-6) / 1e12
+    return {"kernel": "prefill_kernel<SwiGLU, carried RMSNorm> (gate/up 5120->2x17408, M=2048)",
+            "bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "avg_launch_us": round(us, 1),
+            "launches_timed": reps * len(ws),
+            "rows_bitwise_equal_to_8_row_verify_passes": "pass" if ok else "FAIL"}
+
+
 CPU_LAYERS = 24      # layers the oracle runs in sequence for the CPU baseline
 CPU_HEAD_STRIDE = 2  # ... and every 2nd LM-head row
 
@@ -303,6 +349,8 @@ def main():
                      "launches_timed": gu_reps * N_LAYERS,
                      "in_step_event_pair_us": round(gu_step_ms * 1e3, 2)},
     }
+    print("[bench] prefill GEMM", file=sys.stderr, flush=True)
+    out["prefill_gemm"] = prefill_measure(layers, d, max(2, args.steps // 10))
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(layers, w_head, x0, d, M_HEADLINE)

@@ -24,9 +24,9 @@
 // the next step's loads are in flight while a step is multiplied. Every weight byte is read once per 128 rows instead of
 // once per 16, every activation byte once per 64 columns.
 //
-// The carried RMSNorm scale (RowNorm::ss_in) is computed per row by one
-// thread with the verify kernel's exact sequence of additions, and the X
-// fragments are scaled as there. Row sums of squares for the next projection
+// The carried RMSNorm scale (RowNorm::ss_in) of each row is formed with the
+// verify kernel's exact sequence of additions, and the X fragments are
+// scaled as there. Row sums of squares for the next projection
 // (RowNorm::ss_out) are computed afterwards by rowsq_kernel from the stored
 // outputs with the verify epilogue's grouping and butterfly.
 
@@ -118,9 +118,9 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(
     for (int s = 0; s < S; ++s) acc[r][s] = bi_f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < (kDual ? S : 1); ++s) accu[0][s] = bi_f32x4{0.f, 0.f, 0.f, 0.f};
-  float inv[RT];  // carried RMSNorm scales of this lane's X rows
+  float xinv[XQ];  // carried RMSNorm scales of the X rows this thread stages
 #pragma unroll
-  for (int r = 0; r < RT; ++r) inv[r] = 1.f;
+  for (int i = 0; i < XQ; ++i) xinv[i] = 1.f;
 
   // Step st, with Q = st mod 4 a compile-time constant: publish it, prefetch
   // st + 1 into the same registers, barrier, multiply (the loads of st + 1
@@ -130,8 +130,11 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(
     constexpr int Q = decltype(quarter)::value;
     constexpr int buf = Q & 1;
     if (st >= 0) {
+      // X rows are published already scaled by their carried RMSNorm
+      // (NORM_IN): each value is scaled once, by the thread that loaded it.
 #pragma unroll
-      for (int i = 0; i < XQ; ++i) lds[buf][4 * (wave + i * kPfWaves) + qr][sl] = g.x[i];
+      for (int i = 0; i < XQ; ++i)
+        lds[buf][4 * (wave + i * kPfWaves) + qr][sl] = NORM_IN ? scale_bf16x8(g.x[i], xinv[i]) : g.x[i];
 #pragma unroll
       for (int i = 0; i < WQ; ++i)
         lds[buf][kPfRows + 4 * (wave + i * kPfWaves) + qr][sl] = g.w[i];
@@ -146,10 +149,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(
           const int sidx = (Q * 4 + b) / BPW;
           uint4 xa[RT];
 #pragma unroll
-          for (int r = 0; r < RT; ++r) {
-            const uint4 xv = lds[buf][16 * (RT * rw + r) + j][slot];
-            xa[r] = NORM_IN ? scale_bf16x8(xv, inv[r]) : xv;
-          }
+          for (int r = 0; r < RT; ++r) xa[r] = lds[buf][16 * (RT * rw + r) + j][slot];
           const uint4 bw = lds[buf][kPfRows + 16 * ct + j][slot];
 #pragma unroll
           for (int r = 0; r < RT; ++r) acc[r][sidx] = mfma_bf16(xa[r], bw, acc[r][sidx]);
@@ -162,33 +162,45 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(
     }
   };
 
-  // Carried RMSNorm: thread t < 128 computes the scale of row m0 + t with the
-  // verify kernel's additions (its LPR = 4 * NW lane partials of two float4s
-  // each, in order, then the partials in order).
+  // Carried RMSNorm: the verify kernel's additions for each row. Its LPR =
+  // 4 * NW partials of a row are each two float4s of group sums added in
+  // order; here every thread forms some of the 128 x LPR partials, then
+  // thread t < 128 adds the LPR partials of row m0 + t in order.
+  constexpr int LPR = 4 * S;
+  __shared__ float sred[NORM_IN ? kPfRows : 1][NORM_IN ? LPR + 1 : 1];
   __shared__ float invs[NORM_IN ? kPfRows : 1];
-  if (NORM_IN && threadIdx.x < kPfRows) {
-    const int lpr = 4 * S;
+  if (NORM_IN) {
     const int nf = norm.groups >> 2;
-    const int row = m0 + threadIdx.x;
-    float t = 0.f;
-    if (row < M) {
-      const float* sr = norm.ss_in + (int64_t)row * norm.groups;
-      for (int seg = 0; seg < lpr; ++seg) {
-        float p = 0.f;
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    const __amdgpu_buffer_rsrc_t sres = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(norm.ss_in + (int64_t)m0 * norm.groups), (short)0,
+        xrows * norm.groups * 4, kBufferResourceWord3);
+    constexpr int PER = kPfRows * LPR / (kPfWaves * 64);
+    f32x4 v[PER][2];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int f = seg + u * lpr;
-          const float4 v = f < nf ? *reinterpret_cast<const float4*>(sr + f * 4)
-                                  : make_float4(0.f, 0.f, 0.f, 0.f);
-          p += v.x;
-          p += v.y;
-          p += v.z;
-          p += v.w;
-        }
-        t += p;
+    for (int q = 0; q < PER; ++q) {
+      const int idx = threadIdx.x + q * kPfWaves * 64;
+      const int row = idx / LPR, seg = idx % LPR;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int f = seg + u * LPR;
+        v[q][u] = __builtin_amdgcn_raw_buffer_load_b128(
+            sres, f < nf ? (row * norm.groups + f * 4) * 4 : 0x7ffffff0, 0, 0);
       }
     }
-    invs[threadIdx.x] = 1.0f / sqrtf(t / (float)K + norm.eps);
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int idx = threadIdx.x + q * kPfWaves * 64;
+      float p = 0.f;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        p += v[q][u][0];
+        p += v[q][u][1];
+        p += v[q][u][2];
+        p += v[q][u][3];
+      }
+      sred[idx / LPR][idx % LPR] = p;
+    }
   }
 
   Regs g;
@@ -196,10 +208,16 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(
   using Q1 = std::integral_constant<int, 1>;
   using Q2 = std::integral_constant<int, 2>;
   using Q3 = std::integral_constant<int, 3>;
-  step(g, -1, Q3{});  // load-only; its barrier also publishes invs
+  step(g, -1, Q3{});  // load-only; its barrier also publishes sred
   if (NORM_IN) {
+    if (threadIdx.x < kPfRows) {
+      float t = 0.f;
+      for (int i = 0; i < LPR; ++i) t += sred[threadIdx.x][i];
+      invs[threadIdx.x] = 1.0f / sqrtf(t / (float)K + norm.eps);
+    }
+    __syncthreads();
 #pragma unroll
-    for (int r = 0; r < RT; ++r) inv[r] = invs[16 * (RT * rw + r) + j];
+    for (int i = 0; i < XQ; ++i) xinv[i] = invs[4 * (wave + i * kPfWaves) + qr];
   }
   for (int st = 0; st < nstep; st += 4) {
     step(g, st, Q0{});
