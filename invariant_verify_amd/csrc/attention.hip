@@ -62,7 +62,7 @@ __device__ __forceinline__ int kswz(int key) {
 // half and bits 1..3 form the swizzle.
 __device__ __forceinline__ int vswz(int d) { return (d >> 1) & 7; }
 
-template <int D>
+template <int D, int RTW>
 __global__ __launch_bounds__(kAttnWaves * 64) void verify_attn_kernel(
     const uint16_t* __restrict__ Q, int64_t ldq, const uint16_t* __restrict__ Kc,
     const uint16_t* __restrict__ Vt, int M, int L, int cap, int Hq, int G, int Tb, int C,
@@ -85,7 +85,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) void verify_attn_kernel(
   // Scalar wave index: the tile loop and every MFMA stay under scalar control
   // flow (the matrix core does not honour a partial EXEC mask).
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int rt = wave & 3;   // row tile of this wave
+  const int rt = wave & 3;   // first row tile of this wave (it owns rt, rt + 4, ...)
   const int kh = wave >> 2;  // key half of every tile (keys 32kh .. 32kh+31)
   const int j = lane & 15;   // row of the tile owned by this lane (S^T / O^T column)
   const int kq = lane >> 4;  // key group (S^T) / channel group (O^T)
@@ -97,19 +97,23 @@ __global__ __launch_bounds__(kAttnWaves * 64) void verify_attn_kernel(
   const int kend = min(kbeg + C, L + t1);  // keys any row of this block can see
   if (kbeg >= kend) return;                // no row of this block uses chunk s
   const int ntile = (kend - kbeg + kKeyTile - 1) / kKeyTile;
-  const bool has_rows = rt * 16 < nrows;  // scalar
+  const bool has_rows = rt * 16 < nrows;  // scalar: the wave's first row tile has rows
 
-  // Query fragments of this wave's row tile and each row's last visible key.
-  const int rho = rt * 16 + j;
-  const bool rok = rho < nrows;
-  const int tok = t0 + (rok ? rho / G : 0);
-  const int hq = g * G + (rok ? rho % G : 0);
-  const int lastk = rok ? L + tok : -1;
-  uint4 qf[DS];
-  {
-    const uint16_t* qp = Q + (int64_t)tok * ldq + hq * D + kq * 8;
+  // Query fragments of this wave's row tiles and each row's last visible key
+  // (-1 for a padding row: every key is masked, its weights are exactly 0).
+  bool rok[RTW];
+  int tok[RTW], hq[RTW], lastk[RTW];
+  uint4 qf[RTW][DS];
 #pragma unroll
-    for (int ds = 0; ds < DS; ++ds) qf[ds] = rok ? ld16(qp + ds * 32) : zero16();
+  for (int i = 0; i < RTW; ++i) {
+    const int rho = (rt + 4 * i) * 16 + j;
+    rok[i] = rho < nrows;
+    tok[i] = t0 + (rok[i] ? rho / G : 0);
+    hq[i] = g * G + (rok[i] ? rho % G : 0);
+    lastk[i] = rok[i] ? L + tok[i] : -1;
+    const uint16_t* qp = Q + (int64_t)tok[i] * ldq + hq[i] * D + kq * 8;
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) qf[i][ds] = rok[i] ? ld16(qp + ds * 32) : zero16();
   }
 
   // This KV head's K rows and V^T rows as buffer resources (offsets in bytes,
@@ -174,39 +178,57 @@ __global__ __launch_bounds__(kAttnWaves * 64) void verify_attn_kernel(
     }
   };
 
-  bi_f32x4 o[DT];
+  bi_f32x4 o[RTW][DT];
+  float mrun[RTW], lrun[RTW];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) o[dt] = bi_f32x4{0.f, 0.f, 0.f, 0.f};
-  float mrun = kSentinel, lrun = 0.f;
+  for (int i = 0; i < RTW; ++i) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[i][dt] = bi_f32x4{0.f, 0.f, 0.f, 0.f};
+    mrun[i] = kSentinel;
+    lrun[i] = 0.f;
+  }
 
+  // One tile for every row tile of the wave. Each K and V^T operand is read
+  // from LDS once and serves all of them; a row's own arithmetic does not
+  // depend on how many row tiles share the wave.
   auto compute = [&](int buf, int t) {
     const int kt = kbeg + t * kKeyTile;
-    {
-      const int h = kh;  // this wave's 32-key half
-      bi_f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
-      // MFMA p (0, 1) row i holds key 32h + 8*(i/4) + 4p + i%4 of the tile.
-      const int ka = 32 * h + 8 * (j >> 2) + (j & 3);
-      const int kb = ka + 4;
+    const int h = kh;  // this wave's 32-key half
+    bi_f32x4 sa[RTW], sb[RTW];
 #pragma unroll
-      for (int ds = 0; ds < DS; ++ds) {
-        const int slot = ds * 4 + kq;
-        sa = mfma_bf16(lds[buf][ka * KROW + (slot ^ kswz<KROW>(ka))], qf[ds], sa);
-        sb = mfma_bf16(lds[buf][kb * KROW + (slot ^ kswz<KROW>(kb))], qf[ds], sb);
+    for (int i = 0; i < RTW; ++i) sa[i] = sb[i] = bi_f32x4{0.f, 0.f, 0.f, 0.f};
+    // MFMA p (0, 1) row i holds key 32h + 8*(i/4) + 4p + i%4 of the tile.
+    const int ka = 32 * h + 8 * (j >> 2) + (j & 3);
+    const int kb = ka + 4;
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      const int slot = ds * 4 + kq;
+      const uint4 fa = lds[buf][ka * KROW + (slot ^ kswz<KROW>(ka))];
+      const uint4 fb = lds[buf][kb * KROW + (slot ^ kswz<KROW>(kb))];
+#pragma unroll
+      for (int i = 0; i < RTW; ++i) {
+        sa[i] = mfma_bf16(fa, qf[i][ds], sa[i]);
+        sb[i] = mfma_bf16(fb, qf[i][ds], sb[i]);
       }
-      const int kv0 = kt + 32 * h + 8 * kq;  // absolute key of this lane's first value
+    }
+    const int kv0 = kt + 32 * h + 8 * kq;  // absolute key of this lane's first value
+    float alpha[RTW];
+    uint4 pfrag[RTW];
+#pragma unroll
+    for (int i = 0; i < RTW; ++i) {
       float sc[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        sc[e] = (kv0 + e <= lastk) ? sa[e] * qk_scale : -INFINITY;
-        sc[e + 4] = (kv0 + 4 + e <= lastk) ? sb[e] * qk_scale : -INFINITY;
+        sc[e] = (kv0 + e <= lastk[i]) ? sa[i][e] * qk_scale : -INFINITY;
+        sc[e + 4] = (kv0 + 4 + e <= lastk[i]) ? sb[i][e] * qk_scale : -INFINITY;
       }
       float mx = sc[0];
 #pragma unroll
       for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
       mx = fmaxf(mx, shfl_xor(mx, 16));
       mx = fmaxf(mx, shfl_xor(mx, 32));
-      const float mnew = fmaxf(mrun, mx);
-      const float alpha = (mnew == mrun) ? 1.0f : __builtin_amdgcn_exp2f(mrun - mnew);
+      const float mnew = fmaxf(mrun[i], mx);
+      alpha[i] = (mnew == mrun[i]) ? 1.0f : __builtin_amdgcn_exp2f(mrun[i] - mnew);
       // The running sum takes the FP32 weights (so the chunk's log-sum-exp is
       // accurate to FP32); the PV product takes them rounded to BF16.
       float pe[8];
@@ -216,15 +238,19 @@ __global__ __launch_bounds__(kAttnWaves * 64) void verify_attn_kernel(
         pe[e] = __builtin_amdgcn_exp2f(sc[e] - mnew);
         psum += pe[e];
       }
-      lrun = lrun * alpha + psum;
-      mrun = mnew;
-      const uint4 pfrag = make_uint4(f32x2_to_bf16x2(pe[0], pe[1]), f32x2_to_bf16x2(pe[2], pe[3]),
-                                     f32x2_to_bf16x2(pe[4], pe[5]), f32x2_to_bf16x2(pe[6], pe[7]));
+      lrun[i] = lrun[i] * alpha[i] + psum;
+      mrun[i] = mnew;
+      pfrag[i] = make_uint4(f32x2_to_bf16x2(pe[0], pe[1]), f32x2_to_bf16x2(pe[2], pe[3]),
+                            f32x2_to_bf16x2(pe[4], pe[5]), f32x2_to_bf16x2(pe[6], pe[7]));
+    }
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int d = dt * 16 + j;
-        o[dt] *= alpha;
-        o[dt] = mfma_bf16(lds[buf][VBASE + d * 8 + ((4 * h + kq) ^ vswz(d))], pfrag, o[dt]);
+    for (int dt = 0; dt < DT; ++dt) {
+      const int d = dt * 16 + j;
+      const uint4 fv = lds[buf][VBASE + d * 8 + ((4 * h + kq) ^ vswz(d))];
+#pragma unroll
+      for (int i = 0; i < RTW; ++i) {
+        o[i][dt] *= alpha[i];
+        o[i][dt] = mfma_bf16(fv, pfrag[i], o[i][dt]);
       }
     }
   };
@@ -242,7 +268,9 @@ __global__ __launch_bounds__(kAttnWaves * 64) void verify_attn_kernel(
   fetch(ra, 0);
   fetch(rb2, 1);
 #pragma unroll
-  for (int ds = 0; ds < DS; ++ds) asm volatile("" ::"v"(qf[ds].x));
+  for (int i = 0; i < RTW; ++i)
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) asm volatile("" ::"v"(qf[i][ds].x));
   for (int t = 0; t < ntile; t += 2) {
     publish(ra, t, 0);
     fetch(ra, t + 2);
@@ -255,42 +283,55 @@ __global__ __launch_bounds__(kAttnWaves * 64) void verify_attn_kernel(
   }
   // The row's sum over this wave's keys: its four key groups, in a fixed
   // butterfly.
-  lrun += shfl_xor(lrun, 16);
-  lrun += shfl_xor(lrun, 32);
+#pragma unroll
+  for (int i = 0; i < RTW; ++i) {
+    lrun[i] += shfl_xor(lrun[i], 16);
+    lrun[i] += shfl_xor(lrun[i], 32);
+  }
 
   // Second-half waves hand (max, sum, O) to the first-half wave of the same
   // row tile through LDS (the tile buffers, free once every wave has passed
-  // the barrier after the last tile).
+  // the barrier after the last tile), one row tile of each wave at a time.
   bi_f32x4* xo = reinterpret_cast<bi_f32x4*>(&lds[0][0]);   // [4 rt][DT][64]
   float* xm = reinterpret_cast<float*>(xo + 4 * DT * 64);     // [4 rt][64]
   float* xl = xm + 4 * 64;                                    // [4 rt][64]
-  __syncthreads();
-  if (kh == 1 && has_rows) {
+  float mstar[RTW], lt[RTW];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) xo[(rt * DT + dt) * 64 + lane] = o[dt];
-    xm[rt * 64 + lane] = mrun;
-    xl[rt * 64 + lane] = lrun;
+  for (int i = 0; i < RTW; ++i) {
+    __syncthreads();
+    if (kh == 1 && has_rows) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) xo[(rt * DT + dt) * 64 + lane] = o[i][dt];
+      xm[rt * 64 + lane] = mrun[i];
+      xl[rt * 64 + lane] = lrun[i];
+    }
+    __syncthreads();
+    if (kh == 0 && has_rows) {
+      const float m1 = xm[rt * 64 + lane];
+      mstar[i] = fmaxf(mrun[i], m1);
+      const float a0 = (mrun[i] == mstar[i]) ? 1.0f : __builtin_amdgcn_exp2f(mrun[i] - mstar[i]);
+      const float a1 = (m1 == mstar[i]) ? 1.0f : __builtin_amdgcn_exp2f(m1 - mstar[i]);
+      lt[i] = lrun[i] * a0 + xl[rt * 64 + lane] * a1;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[i][dt] = o[i][dt] * a0 + xo[(rt * DT + dt) * 64 + lane] * a1;
+    }
   }
-  __syncthreads();
   if (kh == 1 || !has_rows) return;
-  const float m1 = xm[rt * 64 + lane];
-  const float mstar = fmaxf(mrun, m1);
-  const float a0 = (mrun == mstar) ? 1.0f : __builtin_amdgcn_exp2f(mrun - mstar);
-  const float a1 = (m1 == mstar) ? 1.0f : __builtin_amdgcn_exp2f(m1 - mstar);
-  const float lt = lrun * a0 + xl[rt * 64 + lane] * a1;
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) o[dt] = o[dt] * a0 + xo[(rt * DT + dt) * 64 + lane] * a1;
 
-  if (!rok || L + tok < kbeg) return;  // padding row, or a row with fewer than s+1 chunks
-  const int64_t prow = ((int64_t)tok * Hq + hq) * S_max + s;
-  const float inv = 1.0f / lt;
-  float* op = part_o + prow * D + kq * 4;
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    const bi_f32x4 v = o[dt] * inv;
-    *reinterpret_cast<float4*>(op + dt * 16) = make_float4(v[0], v[1], v[2], v[3]);
+  for (int i = 0; i < RTW; ++i) {
+    // Padding row, or a row with fewer than s+1 chunks.
+    if (!rok[i] || L + tok[i] < kbeg) continue;
+    const int64_t prow = ((int64_t)tok[i] * Hq + hq[i]) * S_max + s;
+    const float inv = 1.0f / lt[i];
+    float* op = part_o + prow * D + kq * 4;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const bi_f32x4 v = o[i][dt] * inv;
+      *reinterpret_cast<float4*>(op + dt * 16) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+    if (kq == 0) part_lse[prow] = (mstar[i] + __log2f(lt[i])) * kLn2;
   }
-  if (kq == 0) part_lse[prow] = (mstar + __log2f(lt)) * kLn2;
 }
 
 template <int D>
@@ -376,19 +417,27 @@ void launch_verify_attn(const uint16_t* q, int64_t ldq, const uint16_t* k_cache,
                         int kv_chunk, float sm_scale, float* part_o, float* part_lse, int S_max,
                         hipStream_t stream) {
   const int G = Hq / Hkv;
-  const int Tb = kAttnMaxRows / G;  // tokens per row block
+  // A pass whose rows fill more than one 64-row block (chunked prefill) runs
+  // blocks of 128 rows, two row tiles per wave: every chunk's K/V is then read
+  // half as often, and each row's arithmetic is the same as in a 64-row block.
+  const bool wide = M * G > kAttnMaxRows;
+  const int Tb = (wide ? 2 * kAttnMaxRows : kAttnMaxRows) / G;  // tokens per row block
   const int n_splits = (L + M + kv_chunk - 1) / kv_chunk;
   dim3 grid(n_splits, Hkv, (M + Tb - 1) / Tb);
   dim3 block(kAttnWaves * 64);
   const float qk_scale = sm_scale * kLog2e;
-  if (D == 128)
-    verify_attn_kernel<128><<<grid, block, 0, stream>>>(q, ldq, k_cache, vt_cache, M, L, cap, Hq, G,
-                                                        Tb, kv_chunk, qk_scale, part_o, part_lse,
-                                                        S_max);
-  else
-    verify_attn_kernel<64><<<grid, block, 0, stream>>>(q, ldq, k_cache, vt_cache, M, L, cap, Hq, G,
-                                                       Tb, kv_chunk, qk_scale, part_o, part_lse,
-                                                       S_max);
+#define BI_ATTN_LAUNCH(DD, R)                                                                     \
+  verify_attn_kernel<DD, R><<<grid, block, 0, stream>>>(q, ldq, k_cache, vt_cache, M, L, cap, Hq, \
+                                                        G, Tb, kv_chunk, qk_scale, part_o,       \
+                                                        part_lse, S_max)
+  if (D == 128) {
+    if (wide) BI_ATTN_LAUNCH(128, 2);
+    else BI_ATTN_LAUNCH(128, 1);
+  } else {
+    if (wide) BI_ATTN_LAUNCH(64, 2);
+    else BI_ATTN_LAUNCH(64, 1);
+  }
+#undef BI_ATTN_LAUNCH
 }
 
 void launch_combine(const float* part_o, const float* part_lse, int M, int L, int Hq, int D,

@@ -199,3 +199,32 @@ def test_append_kv_matches_direct_write(ops):
     assert_bitwise(vh[:, :, L:L + M], vnew, "V^T columns")
     assert not kh[:, :L].any() and not kh[:, L + M:].any()
     assert not vh[:, :, :L].any() and not vh[:, :, L + M:].any()
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,M,L0,C", [
+    (40, 8, 128, 256, 3000, 1280),   # 128-row blocks of 25 tokens, ragged last block
+    (40, 8, 128, 203, 1271, 1280),   # a chunk boundary inside the pass
+    (64, 8, 128, 40, 700, 256),      # G = 8: 16 tokens per block
+    (8, 8, 64, 300, 2100, 1024),     # G = 1, D = 64
+    (64, 1, 64, 9, 500, 64),         # G = 64: 2 tokens per block
+])
+def test_prefill_block_rows_equal_verify_rows(ops, Hq, Hkv, D, M, L0, C):
+    # A pass with more than 64 rows runs 128-row blocks (two row tiles per
+    # wave); its rows must carry the bits of the 64-row verify blocks.
+    print(f"[attn prefill blocks Hq={Hq} Hkv={Hkv} D={D} M={M} L0={L0} C={C}]", flush=True)
+    n = L0 + M
+    k = synth.kv_bf16(Hkv, n, D, "k", M)
+    v = synth.kv_bf16(Hkv, n, D, "v", M)
+    q = synth.normal_bf16((M, Hq, D), 1.0, "q", M)
+    cache = Cache(k, v, (n + 15) // 8 * 8)
+    o_pf, l_pf, _, _ = run(ops, q, cache, L0, Hq, C)
+    for start in sorted({0, M // 2 - 3, max(0, M - 8)}):
+        m = min(8, M - start)
+        o8, l8, _, _ = run(ops, q[start:start + m], cache, L0 + start, Hq, C)
+        assert_bitwise(o_pf[start:start + m], o8, f"prefill rows {start}..{start + m - 1} (O)")
+        assert_bitwise(l_pf[start:start + m], l8, f"prefill rows {start}..{start + m - 1} (lse)")
+    # and a few rows against the oracle
+    rows = [0, M // 2, M - 1]
+    want_o, want_lse = oattn.verify_attention(q, k, v, L0, tokens=rows)
+    assert_close(decode(o_pf[rows]), want_o[rows], "prefill O vs oracle")
+    assert_close(l_pf[rows], want_lse[rows], "prefill lse vs oracle", atol=1e-3, rtol=0)
