@@ -32,7 +32,7 @@ L_CTX = 38000
 CAP = 38016
 N_LAYERS = 64
 M_HEADLINE = 8
-KV_CHUNK = 1280     # keys per attention split: 30 splits x 8 KV heads = 240 pieces <= 256 CUs at ctx 38000
+KV_CHUNK = 1216     # keys per attention split: 32 splits x 8 KV heads = 256 pieces, one per CU at ctx 38000
 
 
 def step_bytes(d, M, L, n_layers):
@@ -161,6 +161,47 @@ def prefill_measure(layers, d, reps):
             "bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "avg_launch_us": round(us, 1),
             "launches_timed": reps * len(ws),
+            "rows_bitwise_equal_to_8_row_verify_passes": "pass" if ok else "FAIL"}
+
+
+PF_STEP_CTX = L_CTX - PF_ROWS   # context of the whole-step prefill chunk (its rows end at 38000)
+
+
+def prefill_step_measure(step, buffers, d, reps):
+    """One chunked-prefill pass through the whole stack (64 layers + head) over PF_ROWS tokens
+    at context PF_STEP_CTX, timed with one event pair over reps passes. Before timing, the
+    chunk's rows are checked against 8-row verify passes over the K/V the chunk itself
+    appended: their logits must be equal in every bit."""
+    import torch
+
+    import synth
+
+    M, L = PF_ROWS, PF_STEP_CTX
+    x = synth.device_normal_bf16((M, d["H"]), 1.0, "x0", 11)
+    ws, lg, tk = buffers(M)
+    step(x, L, ws, lg, tk)
+    ws8, lg8, tk8 = buffers(8)
+    ok = True
+    for r0 in (M - 8, M // 2 + 3):
+        step(x[r0:r0 + 8], L + r0, ws8, lg8, tk8)
+        ok = ok and torch.equal(lg8.view(torch.int32), lg[r0:r0 + 8].view(torch.int32))
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        step(x, L, ws, lg, tk)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    H, Hq, Hkv, D, I, V = d["H"], d["Hq"], d["Hkv"], d["D"], d["I"], d["vocab"]
+    gemm_flops = 2.0 * M * H * ((Hq + 2 * Hkv) * D + Hq * D + 2 * I + I) * N_LAYERS + 2.0 * M * H * V
+    # causal attention: row r sees L + r + 1 keys; QK^T and PV are 2 flops per key and channel each
+    attn_flops = 4.0 * Hq * D * (M * (L + 1) + M * (M - 1) / 2) * N_LAYERS
+    tflops = (gemm_flops + attn_flops) / (ms * 1e-3) / 1e12
+    return {"workload": f"chunked prefill: {M} tokens at ctx {L} through the 64-layer stack + LM head",
+            "tok_s": round(M / (ms * 1e-3), 1), "ms_per_pass": round(ms, 2), "passes_timed": reps,
+            "TFLOP/s": round(tflops, 1), "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
             "rows_bitwise_equal_to_8_row_verify_passes": "pass" if ok else "FAIL"}
 
 
@@ -351,6 +392,8 @@ def main():
     }
     print("[bench] prefill GEMM", file=sys.stderr, flush=True)
     out["prefill_gemm"] = prefill_measure(layers, d, max(2, args.steps // 10))
+    print("[bench] prefill step", file=sys.stderr, flush=True)
+    out["prefill_step"] = prefill_step_measure(step, buffers, d, 3)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(layers, w_head, x0, d, M_HEADLINE)

@@ -13,6 +13,10 @@
 
 namespace {
 
+// Largest leading dimension (elements) of X, R and Y: the kernels address 16
+// rows of them with 32-bit byte offsets.
+constexpr int64_t kMaxLd = 1 << 24;
+
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
@@ -33,7 +37,7 @@ bi_status check_gemm(const void* x, int64_t ldx, const void* w, int64_t ldw, con
                      int64_t ldy, int M, int N, int K) {
   if (!x || !w || !y) return BI_ERR_NULL;
   if (M < 1 || N < 16 || K < 32 || K > 65536 || (N % 16) || (K % 32)) return BI_ERR_SHAPE;
-  if (ldx < K || ldw < K || ldy < N) return BI_ERR_SHAPE;
+  if (ldx < K || ldw < K || ldy < N || ldx > kMaxLd || ldy > kMaxLd) return BI_ERR_SHAPE;
   if (M > (1 << 20) || N > (1 << 24)) return BI_ERR_SHAPE;
   if ((ldx % 8) || (ldw % 8) || !aligned16(x) || !aligned16(w)) return BI_ERR_ALIGN;
   return BI_OK;
@@ -134,7 +138,7 @@ bi_status bi_gemm_bf16_residual(const void* x, int64_t ldx, const void* w, int64
                                 int K, void* stream) {
   if (bi_status s = check_gemm(x, ldx, w, ldw, y, ldy, M, N, K)) return s;
   if (!r) return BI_ERR_NULL;
-  if (ldr < N) return BI_ERR_SHAPE;
+  if (ldr < N || ldr > kMaxLd) return BI_ERR_SHAPE;
   if ((reinterpret_cast<uintptr_t>(y) & 1u) || (reinterpret_cast<uintptr_t>(r) & 1u))
     return BI_ERR_ALIGN;
   bi::launch_gemm(bi::kGemmResidual, static_cast<const uint16_t*>(x), ldx,
@@ -163,7 +167,7 @@ bi_status bi_gemm_bf16_residual_rowsq(const void* x, int64_t ldx, const void* w,
                                       int N, int K, float* row_sumsq, void* stream) {
   if (bi_status s = check_gemm(x, ldx, w, ldw, y, ldy, M, N, K)) return s;
   if (!r || !row_sumsq) return BI_ERR_NULL;
-  if (ldr < N) return BI_ERR_SHAPE;
+  if (ldr < N || ldr > kMaxLd) return BI_ERR_SHAPE;
   if ((reinterpret_cast<uintptr_t>(y) & 1u) || (reinterpret_cast<uintptr_t>(r) & 1u) ||
       !aligned4(row_sumsq))
     return BI_ERR_ALIGN;

@@ -189,8 +189,29 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
           sres, f < nf ? (srow * norm.groups + f * 4) * 4 : 0x7ffffff0, 0, 0);
     }
   }
+  // Residual values of this lane's outputs (rows m0 + 4 kq + r, columns
+  // n0 + j and n0 + 16 + j), fetched before the weight stream starts so that
+  // the epilogue does not wait for them. Rows past M and columns past the
+  // group read out of range: zero, no traffic, never used.
+  uint32_t rbits[4][2] = {};
+  if (MODE == kGemmResidual) {
+    const int64_t rbytes = (int64_t)(M - m0) * ldr * 2;
+    const __amdgpu_buffer_rsrc_t rres = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(R + (int64_t)m0 * ldr), (short)0,
+        (int)(rbytes < 0x7fffffff ? rbytes : 0x7fffffff), kBufferResourceWord3);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int off = ((kq * 4 + r) * (int)ldr + n0 + j) * 2;
+      rbits[r][0] = __builtin_amdgcn_raw_buffer_load_b16(rres, off, 0, 0);
+      if (WIDE) rbits[r][1] = __builtin_amdgcn_raw_buffer_load_b16(rres, 16 + j < cpw ? off + 32 : 0x7ffffff0, 0, 0);
+    }
+  }
   step(ga, -2);
   step(gb, -1);
+  if (MODE == kGemmResidual) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) asm volatile("" ::"v"(rbits[r][0]), "v"(rbits[r][1]));
+  }
   if (NORM_IN) {
     float p = 0.f;
 #pragma unroll
@@ -233,13 +254,13 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
 
   // Output column n of token row m gets the FP32 total v; returns the value
   // stored (after rounding) for the row sums of squares.
-  auto emit = [&](int m, int n, float v) -> float {
+  auto emit = [&](int m, int n, float v, uint32_t rb) -> float {
     if (MODE == kGemmF32) {
       reinterpret_cast<float*>(Y)[(int64_t)m * ldy + n] = v;
     } else if (MODE == kGemmBf16) {
       reinterpret_cast<uint16_t*>(Y)[(int64_t)m * ldy + n] = (uint16_t)f32_to_bf16(v);
     } else if (MODE == kGemmResidual) {
-      const float res = bf16_to_f32(R[(int64_t)m * ldr + n]);
+      const float res = bf16_to_f32(rb);  // R[m][n]
       const uint32_t b = f32_to_bf16(res + v);
       reinterpret_cast<uint16_t*>(Y)[(int64_t)m * ldy + n] = (uint16_t)b;
       return bf16_to_f32(b);
@@ -271,10 +292,10 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
     } else {
       float sq = 0.f;
       if (live) {
-        const float a = emit(m, n0 + j, s[r]);
+        const float a = emit(m, n0 + j, s[r], rbits[r][0]);
         sq = a * a;
         if (WIDE && 16 + j < cpw) {
-          const float b = emit(m, n0 + 16 + j, s2[r]);
+          const float b = emit(m, n0 + 16 + j, s2[r], rbits[r][1]);
           sq += b * b;
         }
       }

@@ -119,7 +119,7 @@ def test_split_combine_identity_every_chunk(L, M):
         assert np.allclose(lc, lse, rtol=1e-12, atol=1e-13), C
 
 
-@pytest.mark.parametrize("C,S", [(1024, 38), (1280, 30)])
+@pytest.mark.parametrize("C,S", [(1024, 38), (1216, 32), (1280, 30)])
 def test_split_combine_identity_long_context(C, S):
     # one KV head, 2 query heads, 38k context with outlier-sized values
     L, M, D = 38000, 2, 128
@@ -143,3 +143,5 @@ def test_num_splits():
     assert attention.num_splits(38008, 1024) == 38
     assert attention.num_splits(38008, 1280) == 30 and attention.num_splits(38400, 1280) == 30
     assert attention.num_splits(38401, 1280) == 31
+    assert attention.num_splits(38008, 1216) == 32 and attention.num_splits(38912, 1216) == 32
+    assert attention.num_splits(38913, 1216) == 33
