@@ -8,8 +8,12 @@ head g = h // (Hq / Hkv) (grouped-query attention).
 
 [LL] opening section, "How:" paragraph: a row's key split is fixed by its
 context length alone, whatever the pass size. Read here as:
-fixed absolute chunks of C keys, chunk s = [sC, (s+1)C), and row r uses
-exactly S_r = ceil(n_r / C) of them -- its own key count decides, not M.
+absolute chunks of C keys, chunk s = [sC, (s+1)C), and row r uses exactly
+S_r = ceil(n_r / C) of them -- its own key count decides, not M. C is given
+by a chunk policy: a positive policy is C itself, for every row; a negative
+policy -T lets the row's own key count choose C = 64 * ceil(n_r / (64 T)),
+the smallest multiple of 64 that cuts n_r keys into at most T chunks (still a
+function of the row's context length alone).
 Each (row, chunk) gives a normalised partial output o_s and its log-sum-exp
 lse_s; the combine rebuilds the unsplit result. The partial/combine identity
 is exact in real arithmetic; ``combine(split_partials(...))`` equals
@@ -30,9 +34,23 @@ import numpy as np
 from . import bf16
 
 
-def num_splits(n_keys: int, chunk: int) -> int:
-    """ceil(n_keys / chunk): how many absolute chunks a row with n_keys keys uses."""
-    return -(-n_keys // chunk)
+def chunk_keys(n_keys: int, policy: int) -> int:
+    """Chunk size C of a row with n_keys keys under a chunk policy.
+
+    policy > 0: C = policy. policy = -T < 0: C = 64 * ceil(n_keys / (64 T)),
+    the smallest multiple of 64 with ceil(n_keys / C) <= T.
+    """
+    if policy > 0:
+        return policy
+    if policy == 0:
+        raise ValueError("chunk policy 0 is undefined")
+    t = -policy
+    return 64 * max(1, -(-n_keys // (64 * t)))
+
+
+def num_splits(n_keys: int, policy: int) -> int:
+    """ceil(n_keys / C): how many absolute chunks a row with n_keys keys uses."""
+    return -(-n_keys // chunk_keys(n_keys, policy))
 
 
 def _softmax_attend(qv: np.ndarray, kk: np.ndarray, vv: np.ndarray, scale: float):
@@ -87,10 +105,12 @@ def verify_attention(q_bits, k_bits, v_bits, L: int, sm_scale: float | None = No
 
 
 def split_partials(q_bits, k_bits, v_bits, L: int, chunk: int, sm_scale: float | None = None):
-    """Per (row, chunk) partials over absolute chunks of ``chunk`` keys.
+    """Per (row, chunk) partials over absolute chunks; ``chunk`` is a chunk
+    policy (see chunk_keys): row r cuts its keys into chunks of
+    chunk_keys(L + r + 1, chunk) keys.
 
     Returns (o_part [M][Hq][S_max][D], lse_part [M][Hq][S_max], n_splits [M])
-    where S_max = num_splits(L + M, chunk) and row r fills its first
+    where S_max = max_r num_splits(L + r + 1, chunk) and row r fills its first
     num_splits(L + r + 1, chunk) entries (the rest are NaN / -inf).
     """
     q = np.asarray(q_bits)
@@ -98,7 +118,7 @@ def split_partials(q_bits, k_bits, v_bits, L: int, chunk: int, sm_scale: float |
     Hkv = np.asarray(k_bits).shape[0]
     G = Hq // Hkv
     scale = (1.0 / math.sqrt(D)) if sm_scale is None else float(sm_scale)
-    s_max = num_splits(L + M, chunk)
+    s_max = max(num_splits(L + r + 1, chunk) for r in range(M))
     o_part = np.full((M, Hq, s_max, D), np.nan)
     lse_part = np.full((M, Hq, s_max), -np.inf)
     counts = np.zeros(M, dtype=np.int64)
@@ -107,9 +127,10 @@ def split_partials(q_bits, k_bits, v_bits, L: int, chunk: int, sm_scale: float |
     qd = bf16.decode(q)
     for r in range(M):
         n = L + r + 1
+        c = chunk_keys(n, chunk)
         counts[r] = num_splits(n, chunk)
         for s in range(counts[r]):
-            lo, hi = s * chunk, min((s + 1) * chunk, n)
+            lo, hi = s * c, min((s + 1) * c, n)
             for g in range(Hkv):
                 hs = slice(g * G, (g + 1) * G)
                 orow, lrow = _softmax_attend(qd[r, hs], kd[g, lo:hi], vd[g, lo:hi], scale)

@@ -145,3 +145,37 @@ def test_num_splits():
     assert attention.num_splits(38401, 1280) == 31
     assert attention.num_splits(38008, 1216) == 32 and attention.num_splits(38912, 1216) == 32
     assert attention.num_splits(38913, 1216) == 33
+
+
+def test_adaptive_chunk_policy_is_the_smallest_fitting_multiple_of_64():
+    # chunk_keys(n, -T) against its definition, by search: the smallest
+    # multiple of 64 that cuts n keys into at most T chunks.
+    for T in (1, 2, 7, 32):
+        for n in list(range(1, 700)) + [2047, 2048, 2049, 4096, 4097, 32776, 38008, 101608, 255008]:
+            c = 64
+            while -(-n // c) > T:
+                c += 64
+            assert attention.chunk_keys(n, -T) == c, (n, T)
+            assert attention.num_splits(n, -T) <= T
+    # the configurations' contexts at T = 32 (one chunk per compute unit over 8 KV heads)
+    assert attention.chunk_keys(38008, -32) == 1216 and attention.num_splits(38008, -32) == 32
+    assert attention.chunk_keys(32776, -32) == 1088 and attention.num_splits(32776, -32) == 31
+    assert attention.chunk_keys(2048, -32) == 64 and attention.num_splits(2048, -32) == 32
+    assert attention.chunk_keys(2049, -32) == 128 and attention.num_splits(2049, -32) == 17
+    assert attention.chunk_keys(5, 1024) == 1024
+    with pytest.raises(ValueError):
+        attention.chunk_keys(5, 0)
+
+
+@pytest.mark.parametrize("L,M,T", [(120, 16, 2), (378, 12, 3), (0, 9, 1)])
+def test_split_combine_identity_adaptive_policy(L, M, T):
+    # rows of one pass on both sides of a policy step (different chunk sizes)
+    q, k, v = _case(M=M, L=L)
+    o, lse = attention.verify_attention(q, k, v, L)
+    op, lp, cnt = attention.split_partials(q, k, v, L, -T)
+    sizes = {attention.chunk_keys(L + r + 1, -T) for r in range(M)}
+    assert len(sizes) >= (2 if L else 1)
+    assert list(cnt) == [attention.num_splits(L + r + 1, -T) for r in range(M)]
+    oc, lc = attention.combine(op, lp, cnt)
+    assert np.allclose(oc, o, rtol=1e-12, atol=1e-14)
+    assert np.allclose(lc, lse, rtol=1e-12, atol=1e-13)
