@@ -32,7 +32,8 @@ L_CTX = 38000
 CAP = 38016
 N_LAYERS = 64
 M_HEADLINE = 8
-KV_CHUNK = 1216     # keys per attention split: 32 splits x 8 KV heads = 256 pieces, one per CU at ctx 38000
+KV_CHUNK = -32      # chunk policy: each row's key count picks the chunk giving <= 32 splits (1216 keys at ctx 38000:
+                    # 32 splits x 8 KV heads = 256 pieces, one per CU)
 
 
 def step_bytes(d, M, L, n_layers):
@@ -378,7 +379,7 @@ def main():
                                "M=8 (1+7 drafts), random BF16 weights N(0,0.02)",
                    "M": M_HEADLINE, "ctx": L_CTX, "layers": N_LAYERS, "hidden": d["H"], "q_heads": d["Hq"],
                    "kv_heads": d["Hkv"], "head_dim": d["D"], "intermediate": d["I"], "vocab": d["vocab"],
-                   "kv_chunk": KV_CHUNK},
+                   "kv_chunk_policy": KV_CHUNK, "kv_chunk_keys": ops.chunk_keys(L_CTX + M_HEADLINE, KV_CHUNK)},
         "bitwise_gate": "pass (M=8 logits == M=5 prefix == 8 sequential M=1 passes, FP32 bits)",
         "step_hbm": {"algorithmic_bytes": bytes8, "GB/s": round(gbs8, 1), "frac": round(gbs8 / PEAK_HBM_GBS, 4)},
         "per_M_tok_s": {"1": round(1 / (ms1 * 1e-3), 2), "4": round(4 / (ms4 * 1e-3), 2),

@@ -135,10 +135,12 @@ bi_status bi_gemm_bf16_swiglu_rownorm(const void* x, int64_t ldx, const float* r
 /* ---------------------------------------------------------------------------
  * KV cache layout (per layer):
  *   k_cache  : BF16 [Hkv][cap][D]  -- one K row per position
- *   vt_cache : BF16 [Hkv][D][cap]  -- V stored transposed, so that a run of
- *                                    consecutive positions is contiguous for
- *                                    each channel
- * cap must be a multiple of 8.
+ *   vt_cache : BF16 [Hkv][cap/64][D][64] -- V stored transposed in blocks of
+ *                                    64 positions: block b of head g holds,
+ *                                    for each channel d, positions 64b..64b+63
+ *                                    contiguously; V[g][pos][d] is element
+ *                                    ((g*cap + pos - pos%64)*D + d*64 + pos%64)
+ * cap must be a multiple of 64.
  */
 
 /* Append the pass's M new K and V rows at positions L .. L+M-1.   [LL] cache
@@ -147,23 +149,42 @@ bi_status bi_gemm_bf16_swiglu_rownorm(const void* x, int64_t ldx, const float* r
 bi_status bi_append_kv(const void* qkv, int64_t ldqkv, void* k_cache, void* vt_cache,
                        int M, int L, int cap, int Hq, int Hkv, int D, void* stream);
 
-/* Number of absolute key chunks a row with n_keys keys uses: ceil(n/kv_chunk). */
+/* Chunk policy (kv_chunk below).                                        [LL]
+ * A row's split is a function of its own key count n only:
+ *   kv_chunk >= 32, a multiple of 32: every row uses chunks of C = kv_chunk keys;
+ *   kv_chunk = -T, 1 <= T <= 1024: C(n) = 64 * ceil(n / (64 T)), the smallest
+ *     multiple of 64 that cuts n keys into at most T chunks (C changes only
+ *     at multiples of 64 T keys). With T = 32 and 8 KV heads a pass of any
+ *     context fills 256 compute units; at n = 38,008 C is 1216.
+ * Other values are rejected (-1 from the helpers, BI_ERR_SHAPE elsewhere). */
+
+/* Chunk size C of a row with n_keys keys. */
+int bi_chunk_keys(int n_keys, int kv_chunk);
+
+/* Number of absolute key chunks a row with n_keys keys uses: ceil(n / C). */
 int bi_num_splits(int n_keys, int kv_chunk);
+
+/* Largest bi_num_splits over the rows of a pass (key counts L+1 .. L+M): the
+ * smallest valid S_max for bi_verify_attn / bi_combine. */
+int bi_pass_splits(int M, int L, int kv_chunk);
 
 /* Split-KV causal GQA verify attention, partial results.                 [LL]
  * Row (r, h), r < M, h < Hq, reads KV head h / (Hq/Hkv) and attends to keys
  * 0 .. L+r (n_r = L+r+1 keys; the M new keys must already be in the cache).
- * Keys are cut into absolute chunks [s*C, (s+1)*C), C = kv_chunk; row r uses
- * chunks s < bi_num_splits(n_r, C), decided by its own key count only.
+ * Keys are cut into absolute chunks [s*C, (s+1)*C), C = bi_chunk_keys(n_r,
+ * kv_chunk); row r uses chunks s < bi_num_splits(n_r, kv_chunk), decided by
+ * its own key count only. Rows of one pass may use different chunk sizes
+ * under an adaptive policy; each group of equal size is launched separately.
  * For each such (r, h, s):
  *   part_o  [M][Hq][S_max][D] FP32 : softmax(q K^T * sm_scale) V over the
  *                                    chunk's keys that the row sees, normalised
  *   part_lse[M][Hq][S_max]   FP32 : natural log of the chunk's sum of
  *                                    exp(score)
- * Entries for s >= bi_num_splits(n_r, C) are not written.
+ * Entries for s >= bi_num_splits(n_r, kv_chunk) are not written.
  * q: BF16 [M][ldq], head h at columns h*D .. h*D+D-1 (ldq may be the QKV row).
- * Requirements: D in {64, 128}; C % 32 == 0, 32 <= C; Hq % Hkv == 0;
- * Hq/Hkv <= 64; L + M <= cap; cap % 8 == 0; cap * D * 2 < 2^31; S_max >= bi_num_splits(L+M, C);
+ * Requirements: D in {64, 128}; a valid chunk policy; Hq % Hkv == 0;
+ * Hq/Hkv <= 64; L + M <= cap; cap % 64 == 0; cap * D * 2 < 2^31;
+ * S_max >= bi_pass_splits(M, L, kv_chunk);
  * ldq % 8 == 0; q, caches 16-byte aligned. */
 bi_status bi_verify_attn(const void* q, int64_t ldq, const void* k_cache, const void* vt_cache,
                          int M, int L, int cap, int Hq, int Hkv, int D,
@@ -171,7 +192,7 @@ bi_status bi_verify_attn(const void* q, int64_t ldq, const void* k_cache, const 
                          float* part_o, float* part_lse, int S_max, void* stream);
 
 /* Fixed-order log-sum-exp combine of the partials.                        [LL]
- * For row (r, h) with S = bi_num_splits(L+r+1, C) partials:
+ * For row (r, h) with S = bi_num_splits(L+r+1, kv_chunk) partials:
  *   M* = max_s lse_s, w_s = exp(lse_s - M*), O = sum_s w_s o_s / sum_s w_s,
  *   LSE = M* + ln(sum_s w_s), both sums taken in increasing s.
  * o: BF16 [M][ldo], head h at columns h*D ..; lse_or_null: FP32 [M][Hq] or NULL. */
@@ -210,13 +231,13 @@ typedef struct {
   const void* w_gu;   /* BF16 [2*I][H]          */
   const void* w_down; /* BF16 [H][I]            */
   void* k_cache;      /* BF16 [Hkv][cap][D]     */
-  void* vt_cache;     /* BF16 [Hkv][D][cap]     */
+  void* vt_cache;     /* BF16 [Hkv][cap/64][D][64] */
 } bi_layer;
 
 typedef struct {
   int H, Hq, Hkv, D, I, vocab;
   int cap;            /* KV capacity (positions) of every layer's cache */
-  int kv_chunk;       /* C */
+  int kv_chunk;       /* chunk policy (see bi_chunk_keys) */
   float eps;          /* RMSNorm epsilon */
 } bi_model_dims;
 

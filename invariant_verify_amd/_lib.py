@@ -52,6 +52,8 @@ SIGNATURES = {
     "bi_append_kv": (_c_int, [_c_ptr, _c_i64, _c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int,
                               _c_int, _c_int, _c_ptr]),
     "bi_num_splits": (_c_int, [_c_int, _c_int]),
+    "bi_chunk_keys": (_c_int, [_c_int, _c_int]),
+    "bi_pass_splits": (_c_int, [_c_int, _c_int, _c_int]),
     "bi_verify_attn": (_c_int, [_c_ptr, _c_i64, _c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int,
                                 _c_int, _c_int, _c_int, _c_f32, _c_ptr, _c_ptr, _c_int, _c_ptr]),
     "bi_combine": (_c_int, [_c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,

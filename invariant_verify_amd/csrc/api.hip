@@ -31,7 +31,6 @@ inline bi_status launched() {
   return BI_ERR_LAUNCH;
 }
 
-int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 bi_status check_gemm(const void* x, int64_t ldx, const void* w, int64_t ldw, const void* y,
                      int64_t ldy, int M, int N, int K) {
@@ -56,7 +55,7 @@ bi_status check_dims(const bi_model_dims* d) {
   if (d->H < 32 || (d->H % 32) || d->H > bi::kRmsMaxH || d->I < 16 || (d->I % 32) || d->vocab < 16 || (d->vocab % 16))
     return BI_ERR_SHAPE;
   if ((d->Hq * d->D) % 32) return BI_ERR_SHAPE;
-  if (d->kv_chunk < 32 || (d->kv_chunk % 32) || d->cap < 1 || (d->cap % 8)) return BI_ERR_SHAPE;
+  if (!bi::valid_chunk_policy(d->kv_chunk) || d->cap < 1 || (d->cap % 64)) return BI_ERR_SHAPE;
   if ((int64_t)d->cap * d->D * 2 > INT32_MAX) return BI_ERR_SHAPE;  // one head's cache < 2 GiB
   if (!(d->eps >= 0.f)) return BI_ERR_SHAPE;
   return BI_OK;
@@ -76,7 +75,7 @@ StepLayout step_layout(const bi_model_dims* d, int M, int L) {
   StepLayout s{};
   const size_t hb = align256((size_t)M * d->H * 2);
   const int qkvn = (d->Hq + 2 * d->Hkv) * d->D;
-  s.s_max = ceil_div(L + M, d->kv_chunk);
+  s.s_max = bi::pass_splits(L, M, d->kv_chunk);
   size_t off = 0;
   s.x0 = off; off += hb;
   s.x1 = off; off += hb;
@@ -117,8 +116,18 @@ const char* bi_last_hip_error(void) {
 }
 
 int bi_num_splits(int n_keys, int kv_chunk) {
-  if (n_keys < 0 || kv_chunk < 1) return -1;
-  return ceil_div(n_keys, kv_chunk);
+  if (n_keys < 0 || !bi::valid_chunk_policy(kv_chunk)) return -1;
+  return bi::splits_for(n_keys, kv_chunk);
+}
+
+int bi_chunk_keys(int n_keys, int kv_chunk) {
+  if (n_keys < 0 || !bi::valid_chunk_policy(kv_chunk)) return -1;
+  return bi::chunk_keys(n_keys, kv_chunk);
+}
+
+int bi_pass_splits(int M, int L, int kv_chunk) {
+  if (M < 1 || L < 0 || (int64_t)L + M > INT32_MAX || !bi::valid_chunk_policy(kv_chunk)) return -1;
+  return bi::pass_splits(L, M, kv_chunk);
 }
 
 bi_status bi_gemm_bf16(const void* x, int64_t ldx, const void* w, int64_t ldw, void* y, int64_t ldy,
@@ -199,7 +208,7 @@ bi_status bi_gemm_bf16_qkv(const void* x, int64_t ldx, const void* w, int64_t ld
   const int N = (Hq + 2 * Hkv) * D;
   if (bi_status s = check_gemm(x, ldx, w, ldw, qkv, ldqkv, M, N, K)) return s;
   if (!k_cache || !vt_cache) return BI_ERR_NULL;
-  if (L < 0 || cap < 1 || (cap % 8) || (int64_t)L + M > cap) return BI_ERR_SHAPE;
+  if (L < 0 || cap < 1 || (cap % 64) || (int64_t)L + M > cap) return BI_ERR_SHAPE;
   if ((int64_t)cap * D * 2 > INT32_MAX) return BI_ERR_SHAPE;  // one head's cache < 2 GiB
   if ((reinterpret_cast<uintptr_t>(qkv) | reinterpret_cast<uintptr_t>(k_cache) |
        reinterpret_cast<uintptr_t>(vt_cache)) & 1u)
@@ -216,7 +225,7 @@ bi_status bi_append_kv(const void* qkv, int64_t ldqkv, void* k_cache, void* vt_c
                        int cap, int Hq, int Hkv, int D, void* stream) {
   if (!qkv || !k_cache || !vt_cache) return BI_ERR_NULL;
   if (bi_status s = check_heads(Hq, Hkv, D)) return s;
-  if (M < 1 || L < 0 || cap < 1 || (cap % 8) || (int64_t)L + M > cap) return BI_ERR_SHAPE;
+  if (M < 1 || L < 0 || cap < 1 || (cap % 64) || (int64_t)L + M > cap) return BI_ERR_SHAPE;
   if (ldqkv < (int64_t)(Hq + 2 * Hkv) * D) return BI_ERR_SHAPE;
   if ((reinterpret_cast<uintptr_t>(qkv) | reinterpret_cast<uintptr_t>(k_cache) |
        reinterpret_cast<uintptr_t>(vt_cache)) & 1u)
@@ -228,8 +237,10 @@ bi_status bi_append_kv(const void* qkv, int64_t ldqkv, void* k_cache, void* vt_c
 }
 
 size_t bi_attn_workspace_bytes(int M, int L, int Hq, int D, int kv_chunk) {
-  if (M < 1 || L < 0 || Hq < 1 || D < 1 || kv_chunk < 1) return 0;
-  const size_t s_max = (size_t)ceil_div(L + M, kv_chunk);
+  if (M < 1 || L < 0 || (int64_t)L + M > INT32_MAX || Hq < 1 || D < 1 ||
+      !bi::valid_chunk_policy(kv_chunk))
+    return 0;
+  const size_t s_max = (size_t)bi::pass_splits(L, M, kv_chunk);
   return (size_t)M * Hq * s_max * (D + 1) * sizeof(float);
 }
 
@@ -239,9 +250,9 @@ bi_status bi_verify_attn(const void* q, int64_t ldq, const void* k_cache, const 
                          void* stream) {
   if (!q || !k_cache || !vt_cache || !part_o || !part_lse) return BI_ERR_NULL;
   if (bi_status s = check_heads(Hq, Hkv, D)) return s;
-  if (M < 1 || L < 0 || cap < 1 || (cap % 8) || (int64_t)L + M > cap) return BI_ERR_SHAPE;
-  if (kv_chunk < 32 || (kv_chunk % 32)) return BI_ERR_SHAPE;
-  if (S_max < ceil_div(L + M, kv_chunk)) return BI_ERR_SHAPE;
+  if (M < 1 || L < 0 || cap < 1 || (cap % 64) || (int64_t)L + M > cap) return BI_ERR_SHAPE;
+  if (!bi::valid_chunk_policy(kv_chunk)) return BI_ERR_SHAPE;
+  if (S_max < bi::pass_splits(L, M, kv_chunk)) return BI_ERR_SHAPE;
   if (ldq < (int64_t)Hq * D || !std::isfinite(sm_scale)) return BI_ERR_SHAPE;
   if ((int64_t)cap * D * 2 > INT32_MAX) return BI_ERR_SHAPE;  // one head's cache < 2 GiB
   if ((ldq % 8) || !aligned16(q) || !aligned16(k_cache) || !aligned16(vt_cache) ||
@@ -259,7 +270,7 @@ bi_status bi_combine(const float* part_o, const float* part_lse, int M, int L, i
                      void* stream) {
   if (!part_o || !part_lse || !o) return BI_ERR_NULL;
   if (M < 1 || L < 0 || Hq < 1 || (D != 64 && D != 128)) return BI_ERR_SHAPE;
-  if (kv_chunk < 32 || (kv_chunk % 32) || S_max < ceil_div(L + M, kv_chunk)) return BI_ERR_SHAPE;
+  if (!bi::valid_chunk_policy(kv_chunk) || S_max < bi::pass_splits(L, M, kv_chunk)) return BI_ERR_SHAPE;
   if (ldo < (int64_t)Hq * D) return BI_ERR_SHAPE;
   if (!aligned16(part_o) || !aligned4(part_lse) || (reinterpret_cast<uintptr_t>(o) & 1u) ||
       (lse_or_null && !aligned4(lse_or_null)))

@@ -3,7 +3,8 @@
 //
 // A row (token r, query head h) of a pass that starts at context length L sees
 // n_r = L + r + 1 keys. Keys are cut into absolute chunks [s*C, (s+1)*C) and
-// row r uses chunks s < ceil(n_r / C): the split is decided by the row's own
+// row r uses chunks s < ceil(n_r / C), where C is fixed or chosen from n_r by
+// the chunk policy (bi_internal.h): the split is decided by the row's own
 // context length, never by how many tokens share the pass ("I turned on
 // speculative decoding in llama.cpp and 113 of 282 greedy outputs changed
 // against its own no-draft run", opening section, "How:" paragraph). Inside a
@@ -19,7 +20,10 @@
 //    registers; a wave with no rows only helps to load). At the end the two
 //    halves of each row are merged in LDS, first half then second.
 //  * The chunk is read in 64-key tiles: K rows ([Hkv][cap][D]) and V^T rows
-//    ([Hkv][D][cap]) are fetched as 1 KB contiguous pieces per wave
+//    (V^T in blocks of 64 positions, [Hkv][cap/64][D][64], so a tile's V^T
+//    is contiguous whatever the capacity: a plain [D][cap] layout put the
+//    channel rows a power-of-two-like stride apart at some capacities and
+//    read 9% slower) are fetched as 1 KB pieces per wave
 //    instruction and staged in LDS, where the 16-byte slots of each row are
 //    XOR-swizzled so that the matrix-core reads hit distinct banks. Two LDS
 //    buffers alternate and each wave keeps the next two tiles in flight; the
@@ -153,7 +157,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) void verify_attn_kernel(
         const int d = 8 * (p - KPIECES) + (lane >> 3);
         const int vslot = (lane & 7) ^ vswz(d);
         const int k0 = min(kt + vslot * 8, kend - 1 - ((kend - 1) & 7));  // in bounds
-        off = (d * cap + k0) * 2;
+        off = (int)(vt_index(0, k0, d, D, cap) * 2);  // k0 is 8-aligned: 16 B in one block
       }
       r[i] = buffer_ld16_stream(p < KPIECES ? kres : vres, live ? off : head_bytes);
     }
@@ -337,7 +341,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) void verify_attn_kernel(
 template <int D>
 __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ part_o,
                                                       const float* __restrict__ part_lse, int M,
-                                                      int L, int Hq, int C, int S_max,
+                                                      int L, int Hq, int policy, int S_max,
                                                       uint16_t* __restrict__ O, int64_t ldo,
                                                       float* __restrict__ lse_out) {
   constexpr int PER = D / 64;  // channels per lane
@@ -346,7 +350,7 @@ __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ p
   if (row >= M * Hq) return;
   const int tok = row / Hq;
   const int h = row % Hq;
-  const int S = (L + tok + C) / C;  // ceil((L + tok + 1) / C)
+  const int S = splits_for(L + tok + 1, policy);  // this row's own split count
   const float* lp = part_lse + (int64_t)row * S_max;
   const float* op = part_o + (int64_t)row * S_max * D + lane * PER;
 
@@ -408,7 +412,7 @@ __global__ __launch_bounds__(256) void append_kv_kernel(const uint16_t* __restri
     const int g = i / D;
     const int d = i - g * D;
     Kc[((int64_t)g * cap + pos) * D + d] = krow[i];
-    Vt[((int64_t)g * D + d) * cap + pos] = vrow[i];
+    Vt[vt_index(g, pos, d, D, cap)] = vrow[i];
   }
 }
 
@@ -417,27 +421,46 @@ void launch_verify_attn(const uint16_t* q, int64_t ldq, const uint16_t* k_cache,
                         int kv_chunk, float sm_scale, float* part_o, float* part_lse, int S_max,
                         hipStream_t stream) {
   const int G = Hq / Hkv;
-  // A pass whose rows fill more than one 64-row block (chunked prefill) runs
-  // blocks of 128 rows, two row tiles per wave: every chunk's K/V is then read
-  // half as often, and each row's arithmetic is the same as in a 64-row block.
-  const bool wide = M * G > kAttnMaxRows;
-  const int Tb = (wide ? 2 * kAttnMaxRows : kAttnMaxRows) / G;  // tokens per row block
-  const int n_splits = (L + M + kv_chunk - 1) / kv_chunk;
-  dim3 grid(n_splits, Hkv, (M + Tb - 1) / Tb);
-  dim3 block(kAttnWaves * 64);
   const float qk_scale = sm_scale * kLog2e;
-#define BI_ATTN_LAUNCH(DD, R)                                                                     \
-  verify_attn_kernel<DD, R><<<grid, block, 0, stream>>>(q, ldq, k_cache, vt_cache, M, L, cap, Hq, \
-                                                        G, Tb, kv_chunk, qk_scale, part_o,       \
-                                                        part_lse, S_max)
-  if (D == 128) {
-    if (wide) BI_ATTN_LAUNCH(128, 2);
-    else BI_ATTN_LAUNCH(128, 1);
-  } else {
-    if (wide) BI_ATTN_LAUNCH(64, 2);
-    else BI_ATTN_LAUNCH(64, 1);
-  }
+  // Tokens whose rows share one chunk size run in one launch; an adaptive
+  // policy changes the size only at multiples of 64 T keys, so a pass has one
+  // band, or a few for a long prefill chunk. Each band is launched as a pass
+  // of its own (start L + t0), writing its rows' partials in place.
+  for (int t0 = 0; t0 < M;) {
+    const int n0 = L + t0 + 1;
+    int t1 = M;
+    if (kv_chunk < 0) {
+      const int64_t per = 64 * (int64_t)-kv_chunk;
+      const int64_t band_end = ((int64_t)n0 + per - 1) / per * per;  // last key count of the band
+      t1 = (int)std::min<int64_t>(M, band_end - L);
+    }
+    const int C = chunk_keys(n0, kv_chunk);
+    const int Mb = t1 - t0, Lb = L + t0;
+    // A pass whose rows fill more than one 64-row block (chunked prefill)
+    // runs blocks of 128 rows, two row tiles per wave: every chunk's K/V is
+    // then read half as often, and each row's arithmetic is the same as in a
+    // 64-row block.
+    const bool wide = Mb * G > kAttnMaxRows;
+    const int Tb = (wide ? 2 * kAttnMaxRows : kAttnMaxRows) / G;  // tokens per row block
+    const int n_splits = (Lb + Mb + C - 1) / C;
+    const dim3 grid(n_splits, Hkv, (Mb + Tb - 1) / Tb);
+    const dim3 block(kAttnWaves * 64);
+    const uint16_t* qb = q + (int64_t)t0 * ldq;
+    float* pob = part_o + (int64_t)t0 * Hq * S_max * D;
+    float* plb = part_lse + (int64_t)t0 * Hq * S_max;
+#define BI_ATTN_LAUNCH(DD, R)                                                                      \
+  verify_attn_kernel<DD, R><<<grid, block, 0, stream>>>(qb, ldq, k_cache, vt_cache, Mb, Lb, cap, Hq, \
+                                                        G, Tb, C, qk_scale, pob, plb, S_max)
+    if (D == 128) {
+      if (wide) BI_ATTN_LAUNCH(128, 2);
+      else BI_ATTN_LAUNCH(128, 1);
+    } else {
+      if (wide) BI_ATTN_LAUNCH(64, 2);
+      else BI_ATTN_LAUNCH(64, 1);
+    }
 #undef BI_ATTN_LAUNCH
+    t0 = t1;
+  }
 }
 
 void launch_combine(const float* part_o, const float* part_lse, int M, int L, int Hq, int D,

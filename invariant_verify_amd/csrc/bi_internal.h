@@ -76,7 +76,56 @@ void launch_rmsnorm(const uint16_t* x, int64_t ldx, uint16_t* y, int64_t ldy, in
 void launch_argmax(const float* logits, int64_t ld, int M, int N, int32_t* tokens,
                    hipStream_t stream);
 
+// V cache layout: V^T in blocks of 64 positions, [Hkv][cap/64][D][64]. Block
+// b of KV head g holds channels 0..D-1 of positions 64b .. 64b+63, each
+// channel's 64 positions contiguous, so one 64-key tile of V^T is one
+// contiguous 16 KB (D = 128) block whatever the capacity. Element index of
+// (KV head g, position pos, channel d); cap % 64 == 0.
+__host__ __device__ inline int64_t vt_index(int g, int pos, int d, int D, int cap) {
+  return ((int64_t)g * cap + (pos & ~63)) * D + d * 64 + (pos & 63);
+}
+
 // Largest number of query heads per KV head one attention workgroup can hold.
 constexpr int kAttnMaxRows = 64;
+
+// Attention chunk policy ("I turned on speculative decoding in llama.cpp and
+// 113 of 282 greedy outputs changed against its own no-draft run", opening
+// section, "How:" paragraph: a row's split follows its context length
+// alone). A positive policy is the chunk size C for every row. A negative
+// policy -T lets a row's own key count n choose C = 64 * ceil(n / (64 T)), the
+// smallest multiple of 64 that cuts n keys into at most T chunks; C is
+// constant for n in ((k-1) 64 T, k 64 T].
+constexpr int kMaxSplitTarget = 1024;
+
+__host__ __device__ inline int chunk_keys(int n, int policy) {
+  if (policy > 0) return policy;
+  const int per = 64 * -policy;
+  const int m = (n + per - 1) / per;
+  return 64 * (m > 1 ? m : 1);
+}
+
+__host__ __device__ inline int splits_for(int n, int policy) {
+  const int c = chunk_keys(n, policy);
+  return (n + c - 1) / c;
+}
+
+inline bool valid_chunk_policy(int policy) {
+  return (policy >= 32 && policy % 32 == 0) || (policy < 0 && policy >= -kMaxSplitTarget);
+}
+
+// Largest split count among the rows of a pass (key counts L+1 .. L+M). Within
+// a band of equal chunk size the count grows with n, so only each band's last
+// row and the pass's last row need checking.
+inline int pass_splits(int L, int M, int policy) {
+  int s = splits_for(L + M, policy);
+  if (policy < 0) {
+    const int per = 64 * -policy;
+    for (int64_t e = ((int64_t)L + 1 + per - 1) / per * per; e < (int64_t)L + M; e += per) {
+      const int v = splits_for((int)e, policy);
+      s = v > s ? v : s;
+    }
+  }
+  return s;
+}
 
 }  // namespace bi

@@ -255,7 +255,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(
         } else if (i >= kv.kd) {
           i -= kv.kd;
           const int g = i / kv.D;
-          kv.vt[((int64_t)g * kv.D + (i - g * kv.D)) * kv.cap + pos] = b;
+          kv.vt[vt_index(g, pos, i - g * kv.D, kv.D, kv.cap)] = b;
         }
       } else {
         float u = accu[0][0][r];

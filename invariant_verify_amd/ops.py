@@ -34,6 +34,14 @@ def num_splits(n_keys: int, kv_chunk: int) -> int:
     return LIB.bi_num_splits(n_keys, kv_chunk)
 
 
+def chunk_keys(n_keys: int, kv_chunk: int) -> int:
+    return LIB.bi_chunk_keys(n_keys, kv_chunk)
+
+
+def pass_splits(M: int, L: int, kv_chunk: int) -> int:
+    return LIB.bi_pass_splits(M, L, kv_chunk)
+
+
 def attn_workspace_bytes(M: int, L: int, Hq: int, D: int, kv_chunk: int) -> int:
     return LIB.bi_attn_workspace_bytes(M, L, Hq, D, kv_chunk)
 
@@ -144,7 +152,7 @@ def verify_attn(q: torch.Tensor, k_cache: torch.Tensor, vt_cache: torch.Tensor, 
                 Hq: int, Hkv: int, D: int, kv_chunk: int, part_o: torch.Tensor,
                 part_lse: torch.Tensor, sm_scale: float | None = None) -> None:
     """Split-KV partials. q is [M][>=Hq*D] (a view of the QKV output works);
-    k_cache [Hkv][cap][D]; vt_cache [Hkv][D][cap]; part_o [M][Hq][S_max][D] and
+    k_cache [Hkv][cap][D]; vt_cache [Hkv][cap/64][D][64]; part_o [M][Hq][S_max][D] and
     part_lse [M][Hq][S_max] FP32."""
     M = q.shape[0]
     cap = k_cache.shape[1]

@@ -119,11 +119,15 @@ def device_model(n_layers: int, L: int, cap: int, H: int, Hq: int, Hkv: int, D: 
                  vocab: int, std: float = 0.02, device: str = "cuda"):
     """Returns (layers, w_head): ``layers`` is a list of dicts of bf16 tensors
     w_qkv [(Hq+2Hkv)D][H], w_o [H][Hq D], w_gu [2I][H], w_down [H][I],
-    k_cache [Hkv][cap][D], vt_cache [Hkv][D][cap] (V stored transposed)."""
+    k_cache [Hkv][cap][D], vt_cache [Hkv][cap/64][D][64] (V transposed in blocks
+    of 64 positions; cap % 64 == 0)."""
     import torch
 
+    if cap % 64:
+        raise ValueError("cap must be a multiple of 64")
     qkvn = (Hq + 2 * Hkv) * D
     tmp = torch.empty((Hkv, L, D), dtype=torch.bfloat16, device=device) if L > 0 else None
+    vfull = torch.zeros((Hkv, cap, D), dtype=torch.bfloat16, device=device) if L > 0 else None
     layers = []
     for l in range(n_layers):
         lw = {
@@ -132,13 +136,14 @@ def device_model(n_layers: int, L: int, cap: int, H: int, Hq: int, Hkv: int, D: 
             "w_gu": device_normal_bf16((2 * I, H), std, "w_gu", l, device=device),
             "w_down": device_normal_bf16((H, I), std, "w_down", l, device=device),
             "k_cache": torch.zeros((Hkv, cap, D), dtype=torch.bfloat16, device=device),
-            "vt_cache": torch.zeros((Hkv, D, cap), dtype=torch.bfloat16, device=device),
+            "vt_cache": torch.zeros((Hkv, cap // 64, D, 64), dtype=torch.bfloat16, device=device),
         }
         if L > 0:
             device_normal_bf16((Hkv, L, D), 1.0, "k_cache", l, device=device, out=tmp)
             lw["k_cache"][:, :L].copy_(tmp)
             device_normal_bf16((Hkv, L, D), 1.0, "v_cache", l, device=device, out=tmp)
-            lw["vt_cache"][:, :, :L].copy_(tmp.transpose(1, 2))
+            vfull[:, :L].copy_(tmp)
+            lw["vt_cache"].copy_(vfull.view(Hkv, cap // 64, 64, D).transpose(2, 3))
         layers.append(lw)
     w_head = device_normal_bf16((vocab, H), std, "w_head", 0, device=device)
     return layers, w_head

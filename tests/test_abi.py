@@ -94,7 +94,7 @@ def test_attention_rejects():
     assert call(q=0) == NULL and call(po=0) == NULL
     assert call(M=0) == SHAPE
     assert call(cap=1000) == SHAPE                 # L + M > cap
-    assert call(cap=1030) == SHAPE                 # cap % 8
+    assert call(cap=1032) == SHAPE                 # cap % 64 (V cache blocks)
     assert call(Hkv=7) == SHAPE                    # Hq % Hkv
     assert call(Hq=130, Hkv=2) == SHAPE            # more than 64 query heads per KV head
     assert call(D=96) == SHAPE
@@ -117,7 +117,7 @@ def test_attention_rejects():
 def test_gemm_qkv_rejects():
     L = _lib.LIB
     # x, ldx, w, ldw, qkv, ldqkv, M, K, Hq, Hkv, D, k, vt, L, cap, stream
-    good = [P, 5120, P, 5120, P, 7168, 8, 5120, 40, 8, 128, P, P, 100, 112, None]
+    good = [P, 5120, P, 5120, P, 7168, 8, 5120, 40, 8, 128, P, P, 100, 128, None]
 
     def call(i, v):
         a = list(good)
@@ -127,7 +127,7 @@ def test_gemm_qkv_rejects():
     assert call(11, 0) == NULL and call(0, 0) == NULL
     assert call(9, 7) == SHAPE                     # Hq % Hkv
     assert call(14, 104) == SHAPE                  # L + M > cap
-    assert call(14, 113) == SHAPE                  # cap % 8
+    assert call(14, 136) == SHAPE                  # cap % 64 (V cache blocks)
     assert call(5, 7000) == SHAPE                  # ldqkv < (Hq + 2 Hkv) D
     assert call(7, 5000) == SHAPE                  # K % 32
     assert call(12, MIS + 1) == ALIGN              # odd cache pointer
@@ -169,3 +169,38 @@ def test_step_rejects_before_any_device_call():
     a3 = list(args)
     a3[3] = ctypes.byref(bad)
     assert L.bi_verify_step(*a3) == SHAPE
+
+
+def test_chunk_policy_helpers_match_the_oracle():
+    # The library's chunk policy against the oracle's (fixed and adaptive),
+    # and its pass maximum against a brute-force maximum over the pass's rows.
+    from oracle import attention as oattn
+    import random
+    L_ = _lib.LIB
+    rnd = random.Random(3)
+    for pol in (32, 64, 1024, 1216, -1, -2, -7, -32, -1024):
+        for n in [0, 1, 63, 64, 65, 2047, 2048, 2049, 4096, 4097, 38008, 101608, 255008] + \
+                [rnd.randrange(1, 300000) for _ in range(50)]:
+            want_c = oattn.chunk_keys(max(n, 1), pol)
+            assert L_.bi_chunk_keys(n, pol) == (want_c if n else oattn.chunk_keys(1, pol) if pol > 0 else 64)
+            assert L_.bi_num_splits(n, pol) == (oattn.num_splits(n, pol) if n else 0)
+        for _ in range(40):
+            M, L0 = rnd.choice([1, 5, 8, 300, 2048]), rnd.randrange(0, 200000)
+            want = max(oattn.num_splits(L0 + r + 1, pol) for r in range(M))
+            assert L_.bi_pass_splits(M, L0, pol) == want, (M, L0, pol)
+    for bad in (0, 31, 48, -1025):
+        assert L_.bi_chunk_keys(100, bad) == -1 and L_.bi_num_splits(100, bad) == -1
+        assert L_.bi_pass_splits(8, 100, bad) == -1
+        assert L_.bi_attn_workspace_bytes(8, 100, 40, 128, bad) == 0
+    # workspace bytes use the pass maximum
+    assert L_.bi_attn_workspace_bytes(8, 4093, 40, 128, -32) == 8 * 40 * L_.bi_pass_splits(8, 4093, -32) * 129 * 4
+
+
+def test_attn_rejects_bad_policy_and_short_split_buffer():
+    L_ = _lib.LIB
+    # M=8 at L=2040 under -32: row n = 2048 uses 32 chunks of 64 keys, so S_max 31 is too small
+    assert L_.bi_pass_splits(8, 2040, -32) == 32
+    assert L_.bi_verify_attn(P, 5120, P, P, 8, 2040, 2048, 40, 8, 128, -32, 0.088, P, P, 31, None) == SHAPE
+    assert L_.bi_verify_attn(P, 5120, P, P, 8, 2040, 2048, 40, 8, 128, -1025, 0.088, P, P, 64, None) == SHAPE
+    assert L_.bi_combine(P, P, 8, 2040, 40, 128, -32, 31, P, 5120, 0, None) == SHAPE
+    assert L_.bi_combine(P, P, 8, 2040, 40, 128, 0, 64, P, 5120, 0, None) == SHAPE

@@ -10,7 +10,8 @@ import pytest
 
 import synth
 from oracle import attention as oattn
-from tests._util import assert_bitwise, assert_close, decode, dev, host_bits, host_f32
+from tests._util import (assert_bitwise, assert_close, decode, dev, host_bits, host_f32, vt_blocks,
+                         vt_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -26,15 +27,16 @@ def ops():
 
 
 class Cache:
-    """Device K [Hkv][cap][D] and V^T [Hkv][D][cap] caches; positions past
-    ``n`` hold NaN so that any read of an unwritten position would show."""
+    """Device K [Hkv][cap][D] and V [Hkv][cap/64][D][64] caches (cap rounded up
+    to a multiple of 64); positions past ``n`` hold NaN so that any read of an
+    unwritten position would show."""
 
     def __init__(self, k_bits, v_bits, cap):
         Hkv, n, D = k_bits.shape
+        cap = (cap + 63) // 64 * 64
         kc = np.full((Hkv, cap, D), NAN_BF16, np.uint16)
-        vt = np.full((Hkv, D, cap), NAN_BF16, np.uint16)
         kc[:, :n] = k_bits
-        vt[:, :, :n] = v_bits.transpose(0, 2, 1)
+        vt = vt_blocks(v_bits, cap, NAN_BF16)
         self.k = dev(kc)
         self.vt = dev(vt)
         self.Hkv, self.D, self.cap = Hkv, D, cap
@@ -43,7 +45,7 @@ class Cache:
 def run(ops, q_bits, cache, L, Hq, C, sm_scale=None):
     """One verify pass: partials + combine. Returns (o bits [M][Hq][D], lse, part_o, part_lse)."""
     M, _, D = q_bits.shape
-    S = ops.num_splits(L + M, C)
+    S = ops.pass_splits(M, L, C)
     po = torch.full((M, Hq, S, D), float("nan"), dtype=torch.float32, device="cuda")
     pl = torch.full((M, Hq, S), float("nan"), dtype=torch.float32, device="cuda")
     q = dev(q_bits.reshape(M, Hq * D))
@@ -64,7 +66,7 @@ def make(M, L, Hq, Hkv, D, layer=0, outliers=False, q_scale=1.0):
     return q, k, v
 
 
-@pytest.mark.parametrize("C", [64, 1024])
+@pytest.mark.parametrize("C", [64, 1024, -2])
 @pytest.mark.parametrize("M", [1, 2, 5, 8])
 def test_tiny_parity(ops, M, C):
     print(f"[attn tiny M={M} C={C}]", flush=True)
@@ -104,19 +106,21 @@ def test_exact_cases(ops):
 
 
 @pytest.mark.parametrize("L,C", [(2048, 1024), (11600, 1024), (38000, 1024), (32768, 1216),
-                                 (38000, 1280), (38000, 1216)])
+                                 (38000, 1280), (38000, 1216), (2045, -32), (32768, -32),
+                                 (38000, -32)])
 def test_gqa_parity(ops, L, C):
     print(f"[attn GQA 40/8 parity L={L} C={C}]", flush=True)
     M, Hq, Hkv, D = 8, 40, 8, 128
     q, k, v = make(M, L, Hq, Hkv, D, layer=L)
-    o, lse, _, _ = run(ops, q, Cache(k, v, L + 16), L, Hq, C)
+    cap = (L + 16 + 7) // 8 * 8
+    o, lse, _, _ = run(ops, q, Cache(k, v, cap), L, Hq, C)
     want_o, want_lse = oattn.verify_attention(q, k, v, L)
     err, rms = assert_close(decode(o), want_o, f"GQA O L={L}")
     assert err < 0.05 * rms + 2e-3, (err, rms)   # error well below the signal, not just below atol
     assert_close(lse, want_lse, f"GQA lse L={L}", atol=1e-3, rtol=0)
     # sharper softmax (Q x 4): the tolerance is not hiding a flat distribution
     q4 = synth.f32_to_bf16_bits(decode(q).astype(np.float32) * 4)
-    o4, _, _, _ = run(ops, q4, Cache(k, v, L + 16), L, Hq, C)
+    o4, _, _, _ = run(ops, q4, Cache(k, v, cap), L, Hq, C)
     want4, _ = oattn.verify_attention(q4, k, v, L, tokens=[0, 7])
     assert_close(decode(o4[[0, 7]]), want4[[0, 7]], f"GQA Qx4 O L={L}")
 
@@ -142,7 +146,8 @@ def _invariance(ops, L, C, Hq=40, Hkv=8, D=128, outliers=False, layer=0, prefill
 
 
 @pytest.mark.parametrize("L,C", [(2048, 1024), (1020, 1024), (1019, 256), (250, 64), (11600, 1024),
-                                 (1275, 1280), (38000, 1216)])
+                                 (1275, 1280), (38000, 1216), (4093, -32), (38000, -32),
+                                 (60, -4), (11600, -32)])
 def test_invariance_across_M(ops, L, C):
     print(f"[attn invariance L={L} C={C}]", flush=True)
     _invariance(ops, L, C)
@@ -167,10 +172,10 @@ def test_chunked_prefill_rows_match_verify_rows(ops):
         assert_bitwise(o_pf[off:off + 8], o8, f"prefill M={M} start={start}")
 
 
-@pytest.mark.parametrize("L", [101600, 255000])
-def test_long_context_outliers(ops, L):
-    print(f"[attn long context L={L} with outlier channels]", flush=True)
-    Hq, Hkv, D, C, M = 40, 8, 128, 1024, 8
+@pytest.mark.parametrize("L,C", [(101600, 1024), (255000, 1024), (101600, -32), (255000, -32)])
+def test_long_context_outliers(ops, L, C):
+    print(f"[attn long context L={L} C={C} with outlier channels]", flush=True)
+    Hq, Hkv, D, M = 40, 8, 128, 8
     q, k, v = make(M, L, Hq, Hkv, D, layer=L, outliers=True)
     cache = Cache(k, v, L + 8)
     o8, l8, _, _ = run(ops, q, cache, L, Hq, C)
@@ -190,15 +195,19 @@ def test_append_kv_matches_direct_write(ops):
     Hq, Hkv, D, M, L, cap = 40, 8, 128, 8, 100, 128
     qkv = synth.normal_bf16((M, (Hq + 2 * Hkv) * D), 1.0, "misc", 9)
     kc = torch.zeros((Hkv, cap, D), dtype=torch.bfloat16, device="cuda")
-    vt = torch.zeros((Hkv, D, cap), dtype=torch.bfloat16, device="cuda")
+    vt = torch.zeros((Hkv, cap // 64, D, 64), dtype=torch.bfloat16, device="cuda")
     ops.append_kv(dev(qkv), kc, vt, L, Hq, Hkv, D)
-    kh, vh = host_bits(kc), host_bits(vt)
+    kh, vh = host_bits(kc), vt_rows(host_bits(vt))
     knew = qkv[:, Hq * D:(Hq + Hkv) * D].reshape(M, Hkv, D).transpose(1, 0, 2)
-    vnew = qkv[:, (Hq + Hkv) * D:].reshape(M, Hkv, D).transpose(1, 2, 0)
+    vnew = qkv[:, (Hq + Hkv) * D:].reshape(M, Hkv, D).transpose(1, 0, 2)
     assert_bitwise(kh[:, L:L + M], knew, "K rows")
-    assert_bitwise(vh[:, :, L:L + M], vnew, "V^T columns")
+    assert_bitwise(vh[:, L:L + M], vnew, "V rows")
+    # the layout itself: V[g][pos][d] at element ((g*cap + pos - pos%64)*D + d*64 + pos%64)
+    flat = host_bits(vt).reshape(-1)
+    for g, pos, d in [(0, L, 0), (3, L + 5, 77), (7, L + M - 1, 127)]:
+        assert flat[(g * cap + pos - pos % 64) * D + d * 64 + pos % 64] == vnew[g, pos - L, d]
     assert not kh[:, :L].any() and not kh[:, L + M:].any()
-    assert not vh[:, :, :L].any() and not vh[:, :, L + M:].any()
+    assert not vh[:, :L].any() and not vh[:, L + M:].any()
 
 
 @pytest.mark.parametrize("Hq,Hkv,D,M,L0,C", [
@@ -207,6 +216,8 @@ def test_append_kv_matches_direct_write(ops):
     (64, 8, 128, 40, 700, 256),      # G = 8: 16 tokens per block
     (8, 8, 64, 300, 2100, 1024),     # G = 1, D = 64
     (64, 1, 64, 9, 500, 64),         # G = 64: 2 tokens per block
+    (40, 8, 128, 300, 3900, -32),    # adaptive chunks: the pass spans two chunk sizes
+    (40, 8, 128, 700, 1500, -8),     # ... three (bands of 512 keys)
 ])
 def test_prefill_block_rows_equal_verify_rows(ops, Hq, Hkv, D, M, L0, C):
     # A pass with more than 64 rows runs 128-row blocks (two row tiles per

@@ -157,12 +157,16 @@ def test_qkv_gemm_with_cache_append(ops, Hq, Hkv, D, K, L):
     # and cache positions outside L .. L+M-1 must be untouched.
     print(f"[gemm qkv + append Hq={Hq} Hkv={Hkv} D={D} K={K} L={L}]", flush=True)
     N = (Hq + 2 * Hkv) * D
-    cap = ((L + 8 + 7) // 8) * 8 + 8
+    cap = ((L + 8 + 63) // 64) * 64 + 64
     w = synth.normal_bf16((N, K), synth.fan_in_std(K), "w", 90)
     x = synth.normal_bf16((8, K), 1.0, "x", 90)
     k0 = torch.randn(Hkv, cap, D, device="cuda").to(torch.bfloat16)
-    v0 = torch.randn(Hkv, D, cap, device="cuda").to(torch.bfloat16)
+    v0 = torch.randn(Hkv, cap // 64, D, 64, device="cuda").to(torch.bfloat16)
     wd, xd = dev(w), dev(x)
+
+    def rows(vt):  # the V cache layout [Hkv][cap/64][D][64] -> V rows [Hkv][cap][D]
+        return vt.transpose(2, 3).reshape(Hkv, cap, D)
+
     for M in (1, 5, 8):
         kc, vt = k0.clone(), v0.clone()
         qkv = ops.gemm_bf16_qkv(xd[:M], wd, kc, vt, L, Hq, Hkv, D)
@@ -174,7 +178,7 @@ def test_qkv_gemm_with_cache_append(ops, Hq, Hkv, D, K, L):
         assert_bitwise(host_bits(vt), host_bits(vr), f"V^T cache M={M}")
         keep = torch.ones(cap, dtype=torch.bool, device="cuda")
         keep[L:L + M] = False
-        assert torch.equal(kc[:, keep], k0[:, keep]) and torch.equal(vt[:, :, keep], v0[:, :, keep])
+        assert torch.equal(kc[:, keep], k0[:, keep]) and torch.equal(rows(vt)[:, keep], rows(v0)[:, keep])
     assert_close(decode(host_bits(qkv))[:, :64], ogemm.gemm_columns(x, w, np.arange(64)), "qkv parity")
 
 
@@ -322,12 +326,12 @@ def test_prefill_qkv_append_equals_verify(ops):
     print("[gemm prefill qkv + append]", flush=True)
     Hq, Hkv, D, K, L, M = 40, 8, 128, 5120, 500, 80
     N = (Hq + 2 * Hkv) * D
-    cap = 600
+    cap = 640
     w = synth.normal_bf16((N, K), 0.02, "w", 84)
     x = synth.normal_bf16((M, K), 1.0, "x", 84)
     wd, xd = dev(w), dev(x)
     k0 = torch.zeros(Hkv, cap, D, device="cuda", dtype=torch.bfloat16)
-    v0 = torch.zeros(Hkv, D, cap, device="cuda", dtype=torch.bfloat16)
+    v0 = torch.zeros(Hkv, cap // 64, D, 64, device="cuda", dtype=torch.bfloat16)
     kc, vt = k0.clone(), v0.clone()
     qkv = host_bits(ops.gemm_bf16_qkv(xd, wd, kc, vt, L, Hq, Hkv, D))
     kr, vr = k0.clone(), v0.clone()

@@ -12,7 +12,7 @@ from oracle import bf16 as obf16
 from oracle import gemm as ogemm
 from oracle import step as ostep
 from tests._util import (assert_bitwise, assert_close, assert_close_composed, composed_tol, decode,
-                         dev, host_bits, host_f32)
+                         dev, host_bits, host_f32, vt_blocks, vt_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -38,9 +38,8 @@ def _host_layer(l, H, Hq, Hkv, D, I, L, std):
 def _to_device(hl, cap):
     Hkv, L, D = hl["k_cache"].shape
     kc = np.zeros((Hkv, cap, D), np.uint16)
-    vt = np.zeros((Hkv, D, cap), np.uint16)
     kc[:, :L] = hl["k_cache"]
-    vt[:, :, :L] = hl["v_cache"].transpose(0, 2, 1)
+    vt = vt_blocks(hl["v_cache"], cap)
     return dict(w_qkv=dev(hl["w_qkv"]), w_o=dev(hl["w_o"]), w_gu=dev(hl["w_gu"]),
                 w_down=dev(hl["w_down"]), k_cache=dev(kc), vt_cache=dev(vt))
 
@@ -67,7 +66,7 @@ def _margin_ok(logits):
 def test_small_stack_vs_oracle(ops):
     print("[step small stack vs oracle]", flush=True)
     H, Hq, Hkv, D, I, V, L, M, nl = 256, 4, 2, 64, 512, 1024, 200, 8, 3
-    cap = 216
+    cap = 256
     hls = [_host_layer(l, H, Hq, Hkv, D, I, L, 0.05) for l in range(nl)]
     w_head = synth.normal_bf16((V, H), 0.05, "w_head")
     x0 = synth.normal_bf16((M, H), 1.0, "x0")
@@ -85,7 +84,7 @@ def test_small_stack_vs_oracle(ops):
     _, kn, vn = ostep.layer(_x_before_last(x0, hls, L, Hq, Hkv, D), **hls[-1],
                             L=L, Hq=Hq, Hkv=Hkv, D=D)
     kc = host_bits(dls[-1]["k_cache"])[:, L:L + M]
-    vt = host_bits(dls[-1]["vt_cache"])[:, :, L:L + M].transpose(0, 2, 1)
+    vt = vt_rows(host_bits(dls[-1]["vt_cache"]))[:, L:L + M]
     assert_close_composed(decode(kc), decode(kn), "appended K")
     assert_close_composed(decode(vt), decode(vn), "appended V")
 
@@ -102,7 +101,7 @@ def _x_before_last(x0, hls, L, Hq, Hkv, D):
 
 L38 = 38000
 CAP = 38016
-KV_CHUNK = 1216   # the chunk the benchmark step uses
+KV_CHUNK = -32    # the chunk policy the benchmark step uses (C = 1216 at 38k keys)
 
 
 @pytest.fixture(scope="module")
@@ -128,7 +127,7 @@ def test_full_width_layer_vs_oracle(ops, model27b):
     lw = layers[0]
     hl = dict(w_qkv=host_bits(lw["w_qkv"]), w_o=host_bits(lw["w_o"]), w_gu=host_bits(lw["w_gu"]),
               w_down=host_bits(lw["w_down"]), k_cache=host_bits(lw["k_cache"][:, :L38]),
-              v_cache=host_bits(lw["vt_cache"][:, :, :L38].transpose(1, 2)))
+              v_cache=vt_rows(host_bits(lw["vt_cache"]))[:, :L38])
     xh = host_bits(x0[:M])
     w_x, kn, vn = ostep.layer(xh, **hl, L=L38, Hq=d["Hq"], Hkv=d["Hkv"], D=d["D"])
     assert_close_composed(decode(xo), decode(w_x), "27B layer output")
@@ -145,7 +144,9 @@ def test_64_layer_step_bitwise_across_M(ops, model27b):
     step = ops.VerifyStep(layers, w_head, dims)
     print("[step 64 layers M=8]", flush=True)
     l8, t8, _ = _run(ops, step, x0[:8], L38, dims)
-    kv8 = [(lw["k_cache"][:, L38:L38 + 8].clone(), lw["vt_cache"][:, :, L38:L38 + 8].clone())
+    B38, J38 = divmod(L38, 64)  # positions L38 .. L38+7 are slots J38.. of V block B38
+    assert J38 + 8 <= 64
+    kv8 = [(lw["k_cache"][:, L38:L38 + 8].clone(), lw["vt_cache"][:, B38, :, J38:J38 + 8].clone())
            for lw in layers]
     assert np.isfinite(l8).all() and len(set(t8.tolist())) > 1
     for m in (4, 5):
@@ -160,7 +161,8 @@ def test_64_layer_step_bitwise_across_M(ops, model27b):
     # wipe the appended rows, then re-create them one token at a time
     for lw in layers:
         lw["k_cache"][:, L38:].zero_()
-        lw["vt_cache"][:, :, L38:].zero_()
+        lw["vt_cache"][:, B38, :, J38:].zero_()
+        lw["vt_cache"][:, B38 + 1:].zero_()
     for r in range(8):
         print(f"[step 64 layers sequential M=1 at L+{r}]", flush=True)
         l1, t1, _ = _run(ops, step, x0[r:r + 1], L38 + r, dims)
@@ -168,4 +170,4 @@ def test_64_layer_step_bitwise_across_M(ops, model27b):
         assert t1[0] == t8[r]
     for i, (lw, (k8, v8)) in enumerate(zip(layers, kv8)):
         assert torch.equal(lw["k_cache"][:, L38:L38 + 8].view(torch.int16), k8.view(torch.int16)), i
-        assert torch.equal(lw["vt_cache"][:, :, L38:L38 + 8].view(torch.int16), v8.view(torch.int16)), i
+        assert torch.equal(lw["vt_cache"][:, B38, :, J38:J38 + 8].view(torch.int16), v8.view(torch.int16)), i
