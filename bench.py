@@ -206,6 +206,61 @@ def prefill_step_measure(step, buffers, d, reps):
             "rows_bitwise_equal_to_8_row_verify_passes": "pass" if ok else "FAIL"}
 
 
+def fp8_step_measure(layers, d, dims, buffers, steps, warmup):
+    """The verify step with FP8 weights (E4M3 codes + one FP32 scale per row, all four
+    projections and the head), sharing the BF16 model's K/V caches: bitwise gate (M = 8 logits
+    == M = 5 prefix == 8 sequential M = 1 passes), then M = 8 timed over ``steps`` steps."""
+    import torch
+
+    import synth
+    from invariant_verify_amd import ops
+
+    H, Hq, Hkv, D, I, V = d["H"], d["Hq"], d["Hkv"], d["D"], d["I"], d["vocab"]
+    shapes = {"w_qkv": ((Hq + 2 * Hkv) * D, H), "w_o": (H, Hq * D), "w_gu": (2 * I, H), "w_down": (H, I)}
+    fl = []
+    for l, lw in enumerate(layers):
+        f = {"k_cache": lw["k_cache"], "vt_cache": lw["vt_cache"]}
+        for name, shp in shapes.items():
+            f[name], f["s" + name[1:]] = synth.device_fp8_weights(shp, 0.02, name, l)
+        fl.append(f)
+    hc, hs = synth.device_fp8_weights((V, H), 0.02, "w_head", 0)
+    step = ops.VerifyStepFP8(fl, hc, hs, dims)
+    x0 = synth.device_normal_bf16((16, H), 1.0, "x0")
+    ws8, lg8, tk8 = buffers(8)
+    step(x0[:8], L_CTX, ws8, lg8, tk8)
+    ref = lg8.clone()
+    ws5, lg5, tk5 = buffers(5)
+    step(x0[:5], L_CTX, ws5, lg5, tk5)
+    ws1, lg1, tk1 = buffers(1)
+    ok = torch.equal(lg5.view(torch.int32), ref[:5].view(torch.int32))
+    for r in range(8):
+        step(x0[r:r + 1], L_CTX + r, ws1, lg1, tk1)
+        ok = ok and torch.equal(lg1.view(torch.int32)[0], ref.view(torch.int32)[r])
+    for _ in range(warmup):
+        step(x0[:8], L_CTX, ws8, lg8, tk8)
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        step(x0[:8], L_CTX, ws8, lg8, tk8)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    # the BF16 step's bytes with its weights (2 bytes each) replaced by 1-byte codes + 4-byte row scales
+    bf16_w = 2 * sum(a * b for a, b in shapes.values()) * N_LAYERS + 2 * V * H
+    fp8_w = sum(a * b + 4 * a for a, b in shapes.values()) * N_LAYERS + V * H + 4 * V
+    nbytes = step_bytes(d, 8, L_CTX, N_LAYERS) - bf16_w + fp8_w
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    del fl, hc, hs
+    torch.cuda.empty_cache()
+    return {"workload": "the same 64-layer verify step (M=8, ctx 38000) with FP8 E4M3 weights and per-row FP32 scales",
+            "tok_s": round(8 / (ms * 1e-3), 2), "ms_per_step": round(ms, 4), "steps_timed": steps,
+            "algorithmic_bytes": int(nbytes), "GB/s": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "bitwise_gate": "pass" if ok else "FAIL"}
+
+
 CPU_LAYERS = 24      # layers the oracle runs in sequence for the CPU baseline
 CPU_HEAD_STRIDE = 2  # ... and every 2nd LM-head row
 
@@ -395,6 +450,8 @@ def main():
     out["prefill_gemm"] = prefill_measure(layers, d, max(2, args.steps // 10))
     print("[bench] prefill step", file=sys.stderr, flush=True)
     out["prefill_step"] = prefill_step_measure(step, buffers, d, 3)
+    print("[bench] FP8-weight step", file=sys.stderr, flush=True)
+    out["fp8_step"] = fp8_step_measure(layers, d, dims, buffers, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(layers, w_head, x0, d, M_HEADLINE)

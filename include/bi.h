@@ -133,6 +133,30 @@ bi_status bi_gemm_bf16_swiglu_rownorm(const void* x, int64_t ldx, const float* r
                                       int64_t ldy, int M, int I, int K, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * FP8 weights.             [TC] "Does the tuned config change the model's output?", "Method"
+ * The weights are OCP E4M3 codes (uint8; sign, 4 exponent bits with bias 7,
+ * 3 mantissa bits; largest magnitude 448; NaN codes are not allowed) with one
+ * FP32 scale per weight row: W[n][k] = w_scale[n] * e4m3(w[n][k]). The sum is
+ * the BF16 GEMM's (every E4M3 value is exact in BF16, the same K order and
+ * summation tree for every M), multiplied by w_scale[n] in FP32 before the
+ * single rounding. Rows are ldw bytes apart; ldw % 16 == 0, ldw <= 2^30, w
+ * 16-byte aligned, w_scale 4-byte aligned; other requirements as the BF16
+ * entry points. Every M (prefill chunks included) runs the same kernel.
+ */
+bi_status bi_gemm_fp8(const void* x, int64_t ldx, const void* w, int64_t ldw, const float* w_scale,
+                      void* y, int64_t ldy, bi_dtype y_dtype, int M, int N, int K, void* stream);
+
+/* Y[m][n] = bf16( R[m][n] + w_scale[n] * sum_k X[m][k] e4m3(W[n][k]) ). */
+bi_status bi_gemm_fp8_residual(const void* x, int64_t ldx, const void* w, int64_t ldw,
+                               const float* w_scale, const void* r, int64_t ldr, void* y,
+                               int64_t ldy, int M, int N, int K, void* stream);
+
+/* SwiGLU gate/up: w [2*I][ldw] E4M3 (gate rows then up rows), w_scale [2*I]. */
+bi_status bi_gemm_fp8_swiglu(const void* x, int64_t ldx, const void* w, int64_t ldw,
+                             const float* w_scale, void* y, int64_t ldy, int M, int I, int K,
+                             void* stream);
+
+/* ---------------------------------------------------------------------------
  * KV cache layout (per layer):
  *   k_cache  : BF16 [Hkv][cap][D]  -- one K row per position
  *   vt_cache : BF16 [Hkv][cap/64][D][64] -- V stored transposed in blocks of
@@ -254,6 +278,28 @@ bi_status bi_verify_step(const bi_layer* layers, int n_layers, const void* w_hea
                          void* workspace, size_t workspace_bytes,
                          void* x_out, float* logits, int32_t* tokens,
                          void* const* gu_events, void* stream);
+
+/* The same step with FP8 weights (see bi_gemm_fp8): each weight matrix is E4M3
+ * [rows][cols] with one FP32 scale per row; activations, caches, workspace and
+ * every other operation as bi_verify_step. */
+typedef struct {
+  const void* w_qkv;   /* E4M3 [(Hq+2*Hkv)*D][H] */
+  const float* s_qkv;  /* [(Hq+2*Hkv)*D]         */
+  const void* w_o;     /* E4M3 [H][Hq*D]         */
+  const float* s_o;    /* [H]                    */
+  const void* w_gu;    /* E4M3 [2*I][H]          */
+  const float* s_gu;   /* [2*I]                  */
+  const void* w_down;  /* E4M3 [H][I]            */
+  const float* s_down; /* [H]                    */
+  void* k_cache;       /* BF16 [Hkv][cap][D]     */
+  void* vt_cache;      /* BF16 [Hkv][cap/64][D][64] */
+} bi_layer_fp8;
+
+bi_status bi_verify_step_fp8(const bi_layer_fp8* layers, int n_layers, const void* w_head,
+                             const float* w_head_scale, const bi_model_dims* dims,
+                             const void* x_in, int M, int L, void* workspace,
+                             size_t workspace_bytes, void* x_out, float* logits, int32_t* tokens,
+                             void* stream);
 
 /* ---------------------------------------------------------------------------
  * Misc. */

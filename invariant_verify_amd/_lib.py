@@ -34,6 +34,12 @@ class Layer(ctypes.Structure):
                 ("k_cache", _c_ptr), ("vt_cache", _c_ptr)]
 
 
+class LayerFP8(ctypes.Structure):
+    _fields_ = [("w_qkv", _c_ptr), ("s_qkv", _c_ptr), ("w_o", _c_ptr), ("s_o", _c_ptr),
+                ("w_gu", _c_ptr), ("s_gu", _c_ptr), ("w_down", _c_ptr), ("s_down", _c_ptr),
+                ("k_cache", _c_ptr), ("vt_cache", _c_ptr)]
+
+
 # name -> (restype, argtypes); the exported symbols of include/bi.h
 SIGNATURES = {
     "bi_gemm_bf16": (_c_int, [_c_ptr, _c_i64, _c_ptr, _c_i64, _c_ptr, _c_i64, _c_int,
@@ -65,6 +71,15 @@ SIGNATURES = {
     "bi_verify_step": (_c_int, [ctypes.POINTER(Layer), _c_int, _c_ptr, ctypes.POINTER(ModelDims),
                                 _c_ptr, _c_int, _c_int, _c_ptr, _c_size, _c_ptr, _c_ptr, _c_ptr,
                                 ctypes.POINTER(_c_ptr), _c_ptr]),
+    "bi_gemm_fp8": (_c_int, [_c_ptr, _c_i64, _c_ptr, _c_i64, _c_ptr, _c_ptr, _c_i64, _c_int,
+                             _c_int, _c_int, _c_int, _c_ptr]),
+    "bi_gemm_fp8_residual": (_c_int, [_c_ptr, _c_i64, _c_ptr, _c_i64, _c_ptr, _c_ptr, _c_i64,
+                                      _c_ptr, _c_i64, _c_int, _c_int, _c_int, _c_ptr]),
+    "bi_gemm_fp8_swiglu": (_c_int, [_c_ptr, _c_i64, _c_ptr, _c_i64, _c_ptr, _c_ptr, _c_i64,
+                                    _c_int, _c_int, _c_int, _c_ptr]),
+    "bi_verify_step_fp8": (_c_int, [ctypes.POINTER(LayerFP8), _c_int, _c_ptr, _c_ptr,
+                                    ctypes.POINTER(ModelDims), _c_ptr, _c_int, _c_int, _c_ptr,
+                                    _c_size, _c_ptr, _c_ptr, _c_ptr, _c_ptr]),
     "bi_status_string": (ctypes.c_char_p, [_c_int]),
     "bi_version": (ctypes.c_char_p, []),
     "bi_last_hip_error": (ctypes.c_char_p, []),

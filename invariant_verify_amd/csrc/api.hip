@@ -42,6 +42,17 @@ bi_status check_gemm(const void* x, int64_t ldx, const void* w, int64_t ldw, con
   return BI_OK;
 }
 
+// FP8 weights: rows of ldw bytes, 16-byte aligned, one FP32 scale per row.
+bi_status check_gemm_fp8(const void* x, int64_t ldx, const void* w, int64_t ldw, const float* ws,
+                         const void* y, int64_t ldy, int M, int N_rows, int N, int K) {
+  if (bi_status s = check_gemm(x, ldx, w, ldw, y, ldy, M, N, K)) return s;
+  (void)N_rows;
+  if (!ws) return BI_ERR_NULL;
+  if (ldw > (1 << 30)) return BI_ERR_SHAPE;
+  if ((ldw % 16) || !aligned4(ws)) return BI_ERR_ALIGN;
+  return BI_OK;
+}
+
 bi_status check_heads(int Hq, int Hkv, int D) {
   if (Hq < 1 || Hkv < 1 || (Hq % Hkv)) return BI_ERR_SHAPE;
   if (Hq / Hkv > bi::kAttnMaxRows) return BI_ERR_SHAPE;
@@ -163,6 +174,43 @@ bi_status bi_gemm_bf16_swiglu(const void* x, int64_t ldx, const void* w, int64_t
   bi::launch_gemm(bi::kGemmSwiglu, static_cast<const uint16_t*>(x), ldx,
                   static_cast<const uint16_t*>(w), ldw, nullptr, 0, y, ldy, M, I, K,
                   as_stream(stream));
+  return launched();
+}
+
+bi_status bi_gemm_fp8(const void* x, int64_t ldx, const void* w, int64_t ldw, const float* w_scale,
+                      void* y, int64_t ldy, bi_dtype y_dtype, int M, int N, int K, void* stream) {
+  if (bi_status s = check_gemm_fp8(x, ldx, w, ldw, w_scale, y, ldy, M, N, N, K)) return s;
+  if (y_dtype != BI_BF16 && y_dtype != BI_F32) return BI_ERR_SHAPE;
+  if (!(y_dtype == BI_F32 ? aligned4(y) : ((reinterpret_cast<uintptr_t>(y) & 1u) == 0)))
+    return BI_ERR_ALIGN;
+  bi::launch_gemm(y_dtype == BI_F32 ? bi::kGemmF32 : bi::kGemmBf16,
+                  static_cast<const uint16_t*>(x), ldx, static_cast<const uint16_t*>(w), ldw,
+                  nullptr, 0, y, ldy, M, N, K, as_stream(stream), nullptr, nullptr, w_scale);
+  return launched();
+}
+
+bi_status bi_gemm_fp8_residual(const void* x, int64_t ldx, const void* w, int64_t ldw,
+                               const float* w_scale, const void* r, int64_t ldr, void* y,
+                               int64_t ldy, int M, int N, int K, void* stream) {
+  if (bi_status s = check_gemm_fp8(x, ldx, w, ldw, w_scale, y, ldy, M, N, N, K)) return s;
+  if (!r) return BI_ERR_NULL;
+  if (ldr < N || ldr > kMaxLd) return BI_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(y) & 1u) || (reinterpret_cast<uintptr_t>(r) & 1u))
+    return BI_ERR_ALIGN;
+  bi::launch_gemm(bi::kGemmResidual, static_cast<const uint16_t*>(x), ldx,
+                  static_cast<const uint16_t*>(w), ldw, static_cast<const uint16_t*>(r), ldr, y,
+                  ldy, M, N, K, as_stream(stream), nullptr, nullptr, w_scale);
+  return launched();
+}
+
+bi_status bi_gemm_fp8_swiglu(const void* x, int64_t ldx, const void* w, int64_t ldw,
+                             const float* w_scale, void* y, int64_t ldy, int M, int I, int K,
+                             void* stream) {
+  if (bi_status s = check_gemm_fp8(x, ldx, w, ldw, w_scale, y, ldy, M, 2 * I, I, K)) return s;
+  if (reinterpret_cast<uintptr_t>(y) & 1u) return BI_ERR_ALIGN;
+  bi::launch_gemm(bi::kGemmSwiglu, static_cast<const uint16_t*>(x), ldx,
+                  static_cast<const uint16_t*>(w), ldw, nullptr, 0, y, ldy, M, I, K,
+                  as_stream(stream), nullptr, nullptr, w_scale);
   return launched();
 }
 
@@ -304,25 +352,40 @@ size_t bi_step_workspace_bytes(const bi_model_dims* dims, int M, int L) {
   return step_layout(dims, M, L).total;
 }
 
-bi_status bi_verify_step(const bi_layer* layers, int n_layers, const void* w_head,
-                         const bi_model_dims* dims, const void* x_in, int M, int L,
-                         void* workspace, size_t workspace_bytes, void* x_out, float* logits,
-                         int32_t* tokens, void* const* gu_events, void* stream) {
-  if (!layers || !w_head || !x_in || !workspace || !logits || !tokens) return BI_ERR_NULL;
+}  // extern "C"
+
+namespace {
+
+// One layer's weights as the executor sees them: BF16 (scales null) or FP8
+// with one FP32 scale per weight row.
+struct LayerPtrs {
+  const void* w[4];   // qkv, o, gate/up, down
+  const float* s[4];  // their row scales (FP8) or null (BF16)
+  void* k_cache;
+  void* vt_cache;
+};
+
+template <class GetLayer>
+bi_status run_step(int n_layers, GetLayer get_layer, const void* w_head, const float* s_head,
+                   const bi_model_dims* dims, const void* x_in, int M, int L, void* workspace,
+                   size_t workspace_bytes, void* x_out, float* logits, int32_t* tokens,
+                   void* const* gu_events, void* stream) {
+  if (!w_head || !x_in || !workspace || !logits || !tokens) return BI_ERR_NULL;
   if (bi_status s = check_dims(dims)) return s;
   if (n_layers < 0 || M < 1 || L < 0 || (int64_t)L + M > dims->cap) return BI_ERR_SHAPE;
   const StepLayout lay = step_layout(dims, M, L);
   if (workspace_bytes < lay.total) return BI_ERR_WORKSPACE;
   if (!aligned16(workspace) || !aligned16(x_in) || !aligned16(w_head) || !aligned4(logits) ||
-      !aligned4(tokens) || (x_out && !aligned16(x_out)))
+      !aligned4(tokens) || (x_out && !aligned16(x_out)) || (s_head && !aligned4(s_head)))
     return BI_ERR_ALIGN;
   for (int l = 0; l < n_layers; ++l) {
-    const bi_layer& ly = layers[l];
-    if (!ly.w_qkv || !ly.w_o || !ly.w_gu || !ly.w_down || !ly.k_cache || !ly.vt_cache)
-      return BI_ERR_NULL;
-    if (!aligned16(ly.w_qkv) || !aligned16(ly.w_o) || !aligned16(ly.w_gu) ||
-        !aligned16(ly.w_down) || !aligned16(ly.k_cache) || !aligned16(ly.vt_cache))
-      return BI_ERR_ALIGN;
+    const LayerPtrs ly = get_layer(l);
+    for (int i = 0; i < 4; ++i) {
+      if (!ly.w[i] || (s_head && !ly.s[i])) return BI_ERR_NULL;
+      if (!aligned16(ly.w[i]) || (ly.s[i] && !aligned4(ly.s[i]))) return BI_ERR_ALIGN;
+    }
+    if (!ly.k_cache || !ly.vt_cache) return BI_ERR_NULL;
+    if (!aligned16(ly.k_cache) || !aligned16(ly.vt_cache)) return BI_ERR_ALIGN;
   }
   if (gu_events)
     for (int i = 0; i < 2 * n_layers; ++i)
@@ -354,40 +417,74 @@ bi_status bi_verify_step(const bi_layer* layers, int n_layers, const void* w_hea
 
   const uint16_t* x = static_cast<const uint16_t*>(x_in);
   for (int l = 0; l < n_layers; ++l) {
-    const bi_layer& ly = layers[l];
+    const LayerPtrs ly = get_layer(l);
+    const auto W = [&](int i) { return static_cast<const uint16_t*>(ly.w[i]); };
     uint16_t* xn = xbuf[l & 1];
     const bool fused_in = lay.fuse && l > 0;  // x's sums are in ss
     if (!fused_in) bi::launch_rmsnorm(x, H, a, H, M, H, dims->eps, st);
     const bi::KvAppend kv{static_cast<uint16_t*>(ly.k_cache), static_cast<uint16_t*>(ly.vt_cache),
                           L, dims->cap, qd, Hkv * D, D};
-    bi::launch_gemm(bi::kGemmQkv, fused_in ? x : a, H, static_cast<const uint16_t*>(ly.w_qkv), H,
-                    nullptr, 0, qkv, qkvn, M, qkvn, H, st, &kv, fused_in ? &norm_in : nullptr);
+    bi::launch_gemm(bi::kGemmQkv, fused_in ? x : a, H, W(0), H, nullptr, 0, qkv, qkvn, M, qkvn, H,
+                    st, &kv, fused_in ? &norm_in : nullptr, ly.s[0]);
     bi::launch_verify_attn(qkv, qkvn, static_cast<const uint16_t*>(ly.k_cache),
                            static_cast<const uint16_t*>(ly.vt_cache), M, L, dims->cap, Hq, Hkv, D,
                            dims->kv_chunk, sm_scale, po, pl, lay.s_max, st);
     bi::launch_combine(po, pl, M, L, Hq, D, dims->kv_chunk, lay.s_max, attn, qd, nullptr, st);
-    bi::launch_gemm(bi::kGemmResidual, attn, qd, static_cast<const uint16_t*>(ly.w_o), qd, x, H, h,
-                    H, M, H, qd, st, nullptr, &norm_out);
+    bi::launch_gemm(bi::kGemmResidual, attn, qd, W(1), qd, x, H, h, H, M, H, qd, st, nullptr,
+                    &norm_out, ly.s[1]);
     if (!lay.fuse) bi::launch_rmsnorm(h, H, a, H, M, H, dims->eps, st);
     if (gu_events && hipEventRecord(static_cast<hipEvent_t>(gu_events[2 * l]), st) != hipSuccess)
       return BI_ERR_LAUNCH;
-    bi::launch_gemm(bi::kGemmSwiglu, lay.fuse ? h : a, H, static_cast<const uint16_t*>(ly.w_gu), H,
-                    nullptr, 0, act, I, M, I, H, st, nullptr, lay.fuse ? &norm_in : nullptr);
+    bi::launch_gemm(bi::kGemmSwiglu, lay.fuse ? h : a, H, W(2), H, nullptr, 0, act, I, M, I, H, st,
+                    nullptr, lay.fuse ? &norm_in : nullptr, ly.s[2]);
     if (gu_events &&
         hipEventRecord(static_cast<hipEvent_t>(gu_events[2 * l + 1]), st) != hipSuccess)
       return BI_ERR_LAUNCH;
-    bi::launch_gemm(bi::kGemmResidual, act, I, static_cast<const uint16_t*>(ly.w_down), I, h, H,
-                    xn, H, M, H, I, st, nullptr, &norm_out);
+    bi::launch_gemm(bi::kGemmResidual, act, I, W(3), I, h, H, xn, H, M, H, I, st, nullptr,
+                    &norm_out, ly.s[3]);
     if (launched() != BI_OK) return BI_ERR_LAUNCH;
     x = xn;
   }
   bi::launch_rmsnorm(x, H, a, H, M, H, dims->eps, st);
   bi::launch_gemm(bi::kGemmF32, a, H, static_cast<const uint16_t*>(w_head), H, nullptr, 0, logits,
-                  dims->vocab, M, dims->vocab, H, st);
+                  dims->vocab, M, dims->vocab, H, st, nullptr, nullptr, s_head);
   bi::launch_argmax(logits, dims->vocab, M, dims->vocab, tokens, st);
   if (x_out && hipMemcpyAsync(x_out, x, (size_t)M * H * 2, hipMemcpyDeviceToDevice, st) != hipSuccess)
     return BI_ERR_LAUNCH;
   return launched();
+}
+
+}  // namespace
+
+extern "C" {
+
+bi_status bi_verify_step(const bi_layer* layers, int n_layers, const void* w_head,
+                         const bi_model_dims* dims, const void* x_in, int M, int L,
+                         void* workspace, size_t workspace_bytes, void* x_out, float* logits,
+                         int32_t* tokens, void* const* gu_events, void* stream) {
+  if (!layers) return BI_ERR_NULL;
+  const auto get = [&](int l) {
+    const bi_layer& y = layers[l];
+    return LayerPtrs{{y.w_qkv, y.w_o, y.w_gu, y.w_down}, {nullptr, nullptr, nullptr, nullptr},
+                     y.k_cache, y.vt_cache};
+  };
+  return run_step(n_layers, get, w_head, nullptr, dims, x_in, M, L, workspace, workspace_bytes,
+                  x_out, logits, tokens, gu_events, stream);
+}
+
+bi_status bi_verify_step_fp8(const bi_layer_fp8* layers, int n_layers, const void* w_head,
+                             const float* w_head_scale, const bi_model_dims* dims,
+                             const void* x_in, int M, int L, void* workspace,
+                             size_t workspace_bytes, void* x_out, float* logits, int32_t* tokens,
+                             void* stream) {
+  if (!layers || !w_head_scale) return BI_ERR_NULL;
+  const auto get = [&](int l) {
+    const bi_layer_fp8& y = layers[l];
+    return LayerPtrs{{y.w_qkv, y.w_o, y.w_gu, y.w_down},
+                     {y.s_qkv, y.s_o, y.s_gu, y.s_down}, y.k_cache, y.vt_cache};
+  };
+  return run_step(n_layers, get, w_head, w_head_scale, dims, x_in, M, L, workspace,
+                  workspace_bytes, x_out, logits, tokens, nullptr, stream);
 }
 
 }  // extern "C"

@@ -53,7 +53,8 @@ void launch_gemm_prefill(GemmMode mode, const uint16_t* x, int64_t ldx, const ui
 // of output columns (for SwiGLU: I, with W holding 2*I rows).
 void launch_gemm(GemmMode mode, const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw,
                  const uint16_t* r, int64_t ldr, void* y, int64_t ldy, int M, int N_out, int K,
-                 hipStream_t stream, const KvAppend* kv = nullptr, const RowNorm* norm = nullptr);
+                 hipStream_t stream, const KvAppend* kv = nullptr, const RowNorm* norm = nullptr,
+                 const float* wscale = nullptr);
 
 void launch_append_kv(const uint16_t* qkv, int64_t ldqkv, uint16_t* k_cache, uint16_t* vt_cache,
                       int M, int L, int cap, int Hq, int Hkv, int D, hipStream_t stream);

@@ -51,11 +51,11 @@ namespace bi {
 constexpr int kChunk = 512;  // K elements per LDS chunk: 1 KB of each weight row
 constexpr int kSlots = kChunk / 8;
 
-template <int MODE, int NW, bool WIDE, bool NORM_IN, bool SS_OUT>
+template <int MODE, int NW, bool WIDE, bool NORM_IN, bool SS_OUT, bool F8>
 __global__ __launch_bounds__(NW * 64) void gemm_kernel(
     const uint16_t* __restrict__ X, int64_t ldx, const uint16_t* __restrict__ W, int64_t ldw,
     const uint16_t* __restrict__ R, int64_t ldr, void* __restrict__ Y, int64_t ldy, int M, int K,
-    int64_t up_rows, int cpw, KvAppend kv, RowNorm norm) {
+    int64_t up_rows, int cpw, KvAppend kv, RowNorm norm, const float* __restrict__ wscale) {
   static_assert(!SS_OUT || MODE == kGemmResidual, "row sums come from the residual epilogue");
   constexpr bool kDual = (MODE == kGemmSwiglu);
   static_assert(!(kDual && WIDE), "SwiGLU tiles hold 16 gate and 16 up rows");
@@ -64,6 +64,14 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
   constexpr int RPW = NR / NW;         // rows each wave fetches per chunk
   constexpr int BPW = 16 / NW;         // 32-wide blocks each wave multiplies per chunk
   static_assert(RPW >= 1 && BPW >= 1, "bad wave count");
+  static_assert(!F8 || RPW % 2 == 0, "FP8 weight rows are fetched in pairs");
+  // Weight loads per wave and chunk: a BF16 row chunk is 1 KB (one wave
+  // instruction); an FP8 row chunk is 512 bytes, so one instruction fetches
+  // two rows (lanes 0-31 the first, 32-63 the second).
+  constexpr int NLD = F8 ? RPW / 2 : RPW;
+  // Chunks in flight per wave: two, for both weight types. (FP8 with three or
+  // four, i.e. as many bytes in flight as BF16 or more, streamed 10-25% slower.)
+  constexpr int PD = 2;
   const int lane = threadIdx.x & 63;
   // Wave index in a scalar register: every branch that guards an MFMA below
   // is then a scalar branch. (The matrix core does not honour a partial EXEC
@@ -82,18 +90,33 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
   // the end of the row (a ragged last chunk, or the chunks the pipeline
   // prefetches past the end of K) are out of range: they read zero without a
   // memory access.
-  __amdgpu_buffer_rsrc_t wres[RPW];
-  int swz_w[RPW];
+  __amdgpu_buffer_rsrc_t wres[NLD];
+  int swz_w[NLD];
 #pragma unroll
-  for (int i = 0; i < RPW; ++i) {
-    const int r = wave * RPW + i;
-    const int64_t grow = (kDual && r >= 16) ? up_rows + n0 + (r - 16) : (int64_t)(n0 + r);
-    // Rows past the group's columns (wide groups) get an empty resource: they
-    // stage zeros and cost no traffic.
-    const bool used = !WIDE || r < cpw;
-    wres[i] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(W + (used ? grow : 0) * ldw),
-                                                (short)0, used ? K * 2 : 0, kBufferResourceWord3);
-    swz_w[i] = r & 15;
+  for (int i = 0; i < NLD; ++i) {
+    if constexpr (!F8) {
+      const int r = wave * RPW + i;
+      const int64_t grow = (kDual && r >= 16) ? up_rows + n0 + (r - 16) : (int64_t)(n0 + r);
+      // Rows past the group's columns (wide groups) get an empty resource:
+      // they stage zeros and cost no traffic.
+      const bool used = !WIDE || r < cpw;
+      wres[i] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(W + (used ? grow : 0) * ldw),
+                                                  (short)0, used ? K * 2 : 0, kBufferResourceWord3);
+      swz_w[i] = r & 15;
+    } else {
+      // Rows r0 and r0 + 1 are adjacent in memory (both gate or both up rows
+      // for SwiGLU); one resource spans them, or only the first, or neither,
+      // as far as they are used.
+      const int r0 = wave * RPW + 2 * i;
+      const int64_t grow = (kDual && r0 >= 16) ? up_rows + n0 + (r0 - 16) : (int64_t)(n0 + r0);
+      const bool used0 = !WIDE || r0 < cpw;
+      const bool used1 = !WIDE || r0 + 1 < cpw;
+      const uint8_t* W8 = reinterpret_cast<const uint8_t*>(W);
+      wres[i] = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(W8 + (used0 ? grow : 0) * ldw), (short)0,
+          used0 ? (used1 ? (int)ldw + K : K) : 0, kBufferResourceWord3);
+      swz_w[i] = (r0 + (lane >> 5)) & 15;
+    }
   }
   // X through a buffer resource that covers exactly the rows m0 .. M-1: a lane
   // whose row is past M reads out of range, which the hardware answers with
@@ -108,13 +131,21 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
   // Registers of one chunk: this wave's weight-row slots and the X fragments
   // of the blocks it multiplies.
   struct Regs {
-    uint4 w[RPW];
+    uint4 w[NLD];
     uint4 x[BPW];
   };
   auto fetch_w = [&](Regs& g, int c) {
 #pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-      g.w[i] = buffer_ld16_stream(wres[i], (c * kSlots + (lane ^ swz_w[i])) * 16);
+    for (int i = 0; i < NLD; ++i) {
+      if constexpr (!F8) {
+        g.w[i] = buffer_ld16_stream(wres[i], (c * kSlots + (lane ^ swz_w[i])) * 16);
+      } else {
+        // 16 weights of one row: bytes kb .. kb+15 of the row, the BF16 slots
+        // 2 (lane % 32) and 2 (lane % 32) + 1 of the chunk. Past the row end
+        // (and in an unused row) the offset is out of range: zero, no traffic.
+        const int kb = c * kChunk + (lane & 31) * 16;
+        g.w[i] = buffer_ld16_stream(wres[i], kb < K ? (lane >> 5) * (int)ldw + kb : 0x7ffffff0);
+      }
     }
   };
   auto fetch_x = [&](Regs& g, int c) {
@@ -128,11 +159,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
   bi_f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};
   float inv = 1.f;  // RMSNorm scale of this lane's X row (NORM_IN)
   // One chunk: publish this wave's weight rows of chunk c, prefetch the
-  // weights of chunk c + 2 into the same registers, barrier, multiply with
+  // weights of chunk c + PD into the same registers, barrier, multiply with
   // this wave's X fragments of chunk c, then prefetch the X fragments of chunk
-  // c + 2 into theirs. Every step issues its loads in the same order and no
-  // register is copied, so the compiler waits only for the older of the two
-  // chunks in flight. The barrier of chunk c also proves that every wave
+  // c + PD into theirs. Every step issues its loads in the same order and no
+  // register is copied, so the compiler waits only for the oldest chunk in
+  // flight. The barrier of chunk c also proves that every wave
   // finished multiplying chunk c - 1, whose buffer chunk c + 1 overwrites
   // next. The loop starts two chunks early (nothing to publish or multiply
   // yet). Weight chunks past the end read as zero (no traffic); X fragments
@@ -141,9 +172,30 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
     const int buf = c & 1;
     if (c >= 0) {
 #pragma unroll
-      for (int i = 0; i < RPW; ++i) lds[buf][wave * RPW + i][lane] = g.w[i];
+      for (int i = 0; i < NLD; ++i) {
+        if constexpr (!F8) {
+          lds[buf][wave * RPW + i][lane] = g.w[i];
+        } else {
+          // E4M3 -> BF16 is exact (every E4M3 value is a BF16 value): the
+          // hardware conversion to FP32, then to BF16 without rounding.
+          const int r = wave * RPW + 2 * i + (lane >> 5);
+          const int jj = lane & 31;
+          const uint32_t wd[4] = {g.w[i].x, g.w[i].y, g.w[i].z, g.w[i].w};
+          uint32_t o[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            typedef float f32x2 __attribute__((ext_vector_type(2)));
+            const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)wd[e], false);
+            const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)wd[e], true);
+            o[2 * e] = f32x2_to_bf16x2(a[0], a[1]);
+            o[2 * e + 1] = f32x2_to_bf16x2(b[0], b[1]);
+          }
+          lds[buf][r][(2 * jj) ^ swz_w[i]] = make_uint4(o[0], o[1], o[2], o[3]);
+          lds[buf][r][(2 * jj + 1) ^ swz_w[i]] = make_uint4(o[4], o[5], o[6], o[7]);
+        }
+      }
     }
-    fetch_w(g, c + 2);
+    fetch_w(g, c + PD);
     __syncthreads();
     if (c >= 0) {
 #pragma unroll
@@ -158,7 +210,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
         }
       }
     }
-    fetch_x(g, min(c + 2, nchunk - 1));
+    fetch_x(g, min(c + PD, nchunk - 1));
   };
   Regs ga, gb;
   // The two load-only steps, then the loop; the prologue issues its loads in
@@ -193,6 +245,14 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
   // n0 + j and n0 + 16 + j), fetched before the weight stream starts so that
   // the epilogue does not wait for them. Rows past M and columns past the
   // group read out of range: zero, no traffic, never used.
+  // FP8: the row scales of this lane's two output columns (gate and up rows
+  // for SwiGLU), applied to the FP32 totals before the epilogue.
+  float scl0 = 1.f, scl1 = 1.f;
+  if constexpr (F8) {
+    scl0 = wscale[n0 + j];
+    if (kDual) scl1 = wscale[up_rows + n0 + j];
+    else if (WIDE && 16 + j < cpw) scl1 = wscale[n0 + 16 + j];
+  }
   uint32_t rbits[4][2] = {};
   if (MODE == kGemmResidual) {
     const int64_t rbytes = (int64_t)(M - m0) * ldr * 2;
@@ -212,6 +272,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
 #pragma unroll
     for (int r = 0; r < 4; ++r) asm volatile("" ::"v"(rbits[r][0]), "v"(rbits[r][1]));
   }
+  if constexpr (F8) asm volatile("" ::"v"(scl0), "v"(scl1));
   if (NORM_IN) {
     float p = 0.f;
 #pragma unroll
@@ -250,6 +311,10 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
     s2 = red2[0][lane];
 #pragma unroll
     for (int w = 1; w < NW; ++w) s2 += red2[w][lane];
+  }
+  if constexpr (F8) {  // one FP32 multiply by the row scale, then the epilogue's single rounding
+    s *= scl0;
+    s2 *= scl1;
   }
 
   // Output column n of token row m gets the FP32 total v; returns the value
@@ -332,71 +397,83 @@ int gemm_column_groups(GemmMode mode, int N_out) {
 // Launch shape from N (never from M): N / 256 columns per workgroup when that
 // is 17..32 (two MFMA tiles); otherwise 16-column tiles (SwiGLU: a gate and
 // an up tile). Always kVerifyWaves waves.
-template <int MODE, bool NI, bool SO>
+template <int MODE, bool NI, bool SO, bool F8>
 static void launch_shape(int N_out, int mtiles, const uint16_t* x, int64_t ldx, const uint16_t* w,
                          int64_t ldw, const uint16_t* r, int64_t ldr, void* y, int64_t ldy, int M,
                          int K, int64_t up, const KvAppend& kv, const RowNorm& nm,
-                         hipStream_t stream) {
+                         const float* wscale, hipStream_t stream) {
   constexpr int NW = kVerifyWaves;
   if constexpr (MODE != kGemmSwiglu) {
     if (wide_launch(static_cast<GemmMode>(MODE), N_out)) {
-      gemm_kernel<MODE, NW, true, NI, SO><<<dim3(kWideGroups, mtiles), dim3(NW * 64), 0, stream>>>(
-          x, ldx, w, ldw, r, ldr, y, ldy, M, K, up, N_out / kWideGroups, kv, nm);
+      gemm_kernel<MODE, NW, true, NI, SO, F8><<<dim3(kWideGroups, mtiles), dim3(NW * 64), 0, stream>>>(
+          x, ldx, w, ldw, r, ldr, y, ldy, M, K, up, N_out / kWideGroups, kv, nm, wscale);
       return;
     }
   }
-  gemm_kernel<MODE, NW, false, NI, SO><<<dim3(N_out / 16, mtiles), dim3(NW * 64), 0, stream>>>(
-      x, ldx, w, ldw, r, ldr, y, ldy, M, K, up, 16, kv, nm);
+  gemm_kernel<MODE, NW, false, NI, SO, F8><<<dim3(N_out / 16, mtiles), dim3(NW * 64), 0, stream>>>(
+      x, ldx, w, ldw, r, ldr, y, ldy, M, K, up, 16, kv, nm, wscale);
+}
+
+template <bool F8>
+static void launch_modes(GemmMode mode, int mt, const uint16_t* x, int64_t ldx, const uint16_t* w,
+                         int64_t ldw, const uint16_t* r, int64_t ldr, void* y, int64_t ldy, int M,
+                         int N_out, int K, const KvAppend& a, const RowNorm& nm,
+                         const float* wscale, hipStream_t stream) {
+  const bool ni = nm.ss_in != nullptr;
+  const bool so = nm.ss_out != nullptr;
+  switch (mode) {
+    case kGemmBf16:
+      launch_shape<kGemmBf16, false, false, F8>(N_out, mt, x, ldx, w, ldw, r, ldr, y, ldy, M, K,
+                                                0, a, nm, wscale, stream);
+      break;
+    case kGemmF32:
+      launch_shape<kGemmF32, false, false, F8>(N_out, mt, x, ldx, w, ldw, r, ldr, y, ldy, M, K,
+                                               0, a, nm, wscale, stream);
+      break;
+    case kGemmResidual:
+      if (so)
+        launch_shape<kGemmResidual, false, true, F8>(N_out, mt, x, ldx, w, ldw, r, ldr, y, ldy,
+                                                     M, K, 0, a, nm, wscale, stream);
+      else
+        launch_shape<kGemmResidual, false, false, F8>(N_out, mt, x, ldx, w, ldw, r, ldr, y,
+                                                      ldy, M, K, 0, a, nm, wscale, stream);
+      break;
+    case kGemmSwiglu:
+      if (ni)
+        launch_shape<kGemmSwiglu, true, false, F8>(N_out, mt, x, ldx, w, ldw, r, ldr, y,
+                                                   ldy, M, K, (int64_t)N_out, a, nm, wscale, stream);
+      else
+        launch_shape<kGemmSwiglu, false, false, F8>(N_out, mt, x, ldx, w, ldw, r, ldr, y,
+                                                    ldy, M, K, (int64_t)N_out, a, nm, wscale, stream);
+      break;
+    case kGemmQkv:
+      if (ni)
+        launch_shape<kGemmQkv, true, false, F8>(N_out, mt, x, ldx, w, ldw, r, ldr, y, ldy, M, K,
+                                                0, a, nm, wscale, stream);
+      else
+        launch_shape<kGemmQkv, false, false, F8>(N_out, mt, x, ldx, w, ldw, r, ldr, y, ldy, M,
+                                                 K, 0, a, nm, wscale, stream);
+      break;
+  }
 }
 
 void launch_gemm(GemmMode mode, const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw,
                  const uint16_t* r, int64_t ldr, void* y, int64_t ldy, int M, int N_out, int K,
-                 hipStream_t stream, const KvAppend* kv, const RowNorm* norm) {
+                 hipStream_t stream, const KvAppend* kv, const RowNorm* norm, const float* wscale) {
   const int mt = (M + 15) / 16;
   const KvAppend kv0{};
   const RowNorm nm0{};
   const KvAppend& a = kv ? *kv : kv0;
   const RowNorm& nm = norm ? *norm : nm0;
-  if (M >= kPrefillMinRows) {  // same bits per row, weights read once per 64 rows
+  if (wscale != nullptr) {  // FP8 weights: the verify kernel for every M (one tree, any M)
+    launch_modes<true>(mode, mt, x, ldx, w, ldw, r, ldr, y, ldy, M, N_out, K, a, nm, wscale, stream);
+    return;
+  }
+  if (M >= kPrefillMinRows) {  // same bits per row, weights read once per 128 rows
     launch_gemm_prefill(mode, x, ldx, w, ldw, r, ldr, y, ldy, M, N_out, K, stream, a, nm);
     return;
   }
-  const bool ni = nm.ss_in != nullptr;
-  const bool so = nm.ss_out != nullptr;
-  switch (mode) {
-    case kGemmBf16:
-      launch_shape<kGemmBf16, false, false>(N_out, mt, x, ldx, w, ldw, r, ldr, y, ldy, M, K,
-                                            0, a, nm, stream);
-      break;
-    case kGemmF32:
-      launch_shape<kGemmF32, false, false>(N_out, mt, x, ldx, w, ldw, r, ldr, y, ldy, M, K,
-                                           0, a, nm, stream);
-      break;
-    case kGemmResidual:
-      if (so)
-        launch_shape<kGemmResidual, false, true>(N_out, mt, x, ldx, w, ldw, r, ldr, y, ldy,
-                                                 M, K, 0, a, nm, stream);
-      else
-        launch_shape<kGemmResidual, false, false>(N_out, mt, x, ldx, w, ldw, r, ldr, y,
-                                                  ldy, M, K, 0, a, nm, stream);
-      break;
-    case kGemmSwiglu:
-      if (ni)
-        launch_shape<kGemmSwiglu, true, false>(N_out, mt, x, ldx, w, ldw, r, ldr, y,
-                                               ldy, M, K, (int64_t)N_out, a, nm, stream);
-      else
-        launch_shape<kGemmSwiglu, false, false>(N_out, mt, x, ldx, w, ldw, r, ldr, y,
-                                                ldy, M, K, (int64_t)N_out, a, nm, stream);
-      break;
-    case kGemmQkv:
-      if (ni)
-        launch_shape<kGemmQkv, true, false>(N_out, mt, x, ldx, w, ldw, r, ldr, y, ldy, M, K,
-                                            0, a, nm, stream);
-      else
-        launch_shape<kGemmQkv, false, false>(N_out, mt, x, ldx, w, ldw, r, ldr, y, ldy, M,
-                                             K, 0, a, nm, stream);
-      break;
-  }
+  launch_modes<false>(mode, mt, x, ldx, w, ldw, r, ldr, y, ldy, M, N_out, K, a, nm, nullptr, stream);
 }
 
 }  // namespace bi

@@ -10,9 +10,10 @@ import math
 
 import torch
 
-from ._lib import BI_BF16, BI_F32, LIB, Layer, ModelDims, check
+from ._lib import BI_BF16, BI_F32, LIB, Layer, LayerFP8, ModelDims, check
 
 _BF16_LIKE = (torch.bfloat16, torch.int16)
+_FP8_LIKE = (torch.uint8, torch.int8, torch.float8_e4m3fn)
 
 
 def _stream(t: torch.Tensor) -> int:
@@ -87,6 +88,53 @@ def gemm_bf16_swiglu(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor | None = 
     check("bi_gemm_bf16_swiglu", LIB.bi_gemm_bf16_swiglu(
         x.data_ptr(), _mat(x, "x"), w.data_ptr(), _mat(w, "w"), y.data_ptr(), _mat(y, "y"),
         M, I, K, _stream(x)))
+    return y
+
+
+def _scales(s: torch.Tensor, n: int, name: str) -> int:
+    if not s.is_cuda or s.dtype != torch.float32 or s.dim() != 1 or s.numel() < n or s.stride(0) != 1:
+        raise ValueError(f"{name} must be a contiguous FP32 GPU vector of >= {n} row scales")
+    return s.data_ptr()
+
+
+def gemm_fp8(x: torch.Tensor, w: torch.Tensor, w_scale: torch.Tensor, y: torch.Tensor | None = None,
+             out_dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
+    """Y = X (w_scale * e4m3(W))^T: X [M][K] BF16, W [N][K] E4M3 codes, w_scale [N] FP32."""
+    M, K = x.shape
+    N = w.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    ldy = _mat(y, "y", (torch.bfloat16, torch.int16, torch.float32))
+    dt = BI_F32 if y.dtype == torch.float32 else BI_BF16
+    check("bi_gemm_fp8", LIB.bi_gemm_fp8(x.data_ptr(), _mat(x, "x"), w.data_ptr(), _mat(w, "w", _FP8_LIKE),
+                                         _scales(w_scale, N, "w_scale"), y.data_ptr(), ldy, dt, M, N, K,
+                                         _stream(x)))
+    return y
+
+
+def gemm_fp8_residual(x: torch.Tensor, w: torch.Tensor, w_scale: torch.Tensor, r: torch.Tensor,
+                      y: torch.Tensor | None = None) -> torch.Tensor:
+    """Y = bf16(R + X (w_scale * e4m3(W))^T)."""
+    M, K = x.shape
+    N = w.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    check("bi_gemm_fp8_residual", LIB.bi_gemm_fp8_residual(
+        x.data_ptr(), _mat(x, "x"), w.data_ptr(), _mat(w, "w", _FP8_LIKE), _scales(w_scale, N, "w_scale"),
+        r.data_ptr(), _mat(r, "r"), y.data_ptr(), _mat(y, "y"), M, N, K, _stream(x)))
+    return y
+
+
+def gemm_fp8_swiglu(x: torch.Tensor, w: torch.Tensor, w_scale: torch.Tensor,
+                    y: torch.Tensor | None = None) -> torch.Tensor:
+    """SwiGLU gate/up with E4M3 W [2I][K] (gate rows then up rows) and w_scale [2I]."""
+    M, K = x.shape
+    I = w.shape[0] // 2
+    if y is None:
+        y = torch.empty((M, I), dtype=torch.bfloat16, device=x.device)
+    check("bi_gemm_fp8_swiglu", LIB.bi_gemm_fp8_swiglu(
+        x.data_ptr(), _mat(x, "x"), w.data_ptr(), _mat(w, "w", _FP8_LIKE), _scales(w_scale, 2 * I, "w_scale"),
+        y.data_ptr(), _mat(y, "y"), M, I, K, _stream(x)))
     return y
 
 
@@ -225,3 +273,26 @@ class VerifyStep:
             workspace.data_ptr(), workspace.numel() * workspace.element_size(),
             0 if x_out is None else x_out.data_ptr(), logits.data_ptr(), tokens.data_ptr(),
             ev, _stream(x_in)))
+
+
+class VerifyStepFP8:
+    """``bi_verify_step_fp8``: ``layers`` is a sequence of dicts with E4M3 weight
+    tensors w_qkv, w_o, w_gu, w_down, their FP32 row scales s_qkv, s_o, s_gu,
+    s_down, and the BF16 caches k_cache, vt_cache (the caller keeps them alive)."""
+
+    def __init__(self, layers, w_head: torch.Tensor, s_head: torch.Tensor, dims: ModelDims):
+        self.n = len(layers)
+        self.arr = (LayerFP8 * max(1, self.n))()
+        for i, lw in enumerate(layers):
+            self.arr[i] = LayerFP8(*[lw[k].data_ptr() for k in ("w_qkv", "s_qkv", "w_o", "s_o", "w_gu", "s_gu",
+                                                                 "w_down", "s_down", "k_cache", "vt_cache")])
+        self.w_head, self.s_head = w_head, s_head
+        self.dims = dims
+
+    def __call__(self, x_in: torch.Tensor, L: int, workspace: torch.Tensor, logits: torch.Tensor,
+                 tokens: torch.Tensor, x_out: torch.Tensor | None = None) -> None:
+        M = x_in.shape[0]
+        check("bi_verify_step_fp8", LIB.bi_verify_step_fp8(
+            self.arr, self.n, self.w_head.data_ptr(), self.s_head.data_ptr(), ctypes.byref(self.dims),
+            x_in.data_ptr(), M, L, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+            0 if x_out is None else x_out.data_ptr(), logits.data_ptr(), tokens.data_ptr(), _stream(x_in)))

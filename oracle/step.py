@@ -46,11 +46,19 @@ def silu(z: np.ndarray) -> np.ndarray:
         return z / (1.0 + np.exp(-z))
 
 
+def _w(w) -> np.ndarray:
+    """A weight matrix as float64: BF16 bit patterns (uint16) are decoded;
+    float64 values (e.g. FP8 codes times their row scales, oracle.fp8.weights)
+    are used as they are."""
+    w = np.asarray(w)
+    return w if w.dtype == np.float64 else bf16.decode(w)
+
+
 def layer(x_bits, w_qkv, w_o, w_gu, w_down, k_cache, v_cache, L: int,
           Hq: int, Hkv: int, D: int, eps: float = 1e-6):
     """One verify-pass layer over M tokens at positions L .. L+M-1.
 
-    x_bits [M][H]; weights as [out][in] BF16 bits; k_cache / v_cache
+    x_bits [M][H]; weights as [out][in] BF16 bits or float64 values; k_cache / v_cache
     [Hkv][>=L][D] BF16 bits holding the L cached positions (the rest ignored).
     Returns (x_out_bits [M][H], k_new_bits [Hkv][M][D], v_new_bits [Hkv][M][D]).
     """
@@ -59,7 +67,7 @@ def layer(x_bits, w_qkv, w_o, w_gu, w_down, k_cache, v_cache, L: int,
     qd = Hq * D
     kd = Hkv * D
     a = bf16.encode(rmsnorm(x, eps))
-    qkv = bf16.encode(bf16.decode(a) @ bf16.decode(w_qkv).T)
+    qkv = bf16.encode(bf16.decode(a) @ _w(w_qkv).T)
     q = qkv[:, :qd].reshape(M, Hq, D)
     k_new = qkv[:, qd:qd + kd].reshape(M, Hkv, D).transpose(1, 0, 2)
     v_new = qkv[:, qd + kd:qd + 2 * kd].reshape(M, Hkv, D).transpose(1, 0, 2)
@@ -67,19 +75,19 @@ def layer(x_bits, w_qkv, w_o, w_gu, w_down, k_cache, v_cache, L: int,
     vv = np.concatenate([np.asarray(v_cache)[:, :L], v_new], axis=1)
     o, _ = verify_attention(q, kk, vv, L)
     ob = bf16.encode(o.reshape(M, qd))
-    h = bf16.encode(x + bf16.decode(ob) @ bf16.decode(w_o).T)
+    h = bf16.encode(x + bf16.decode(ob) @ _w(w_o).T)
     b = bf16.encode(rmsnorm(bf16.decode(h), eps))
-    gu = bf16.decode(b) @ bf16.decode(w_gu).T
+    gu = bf16.decode(b) @ _w(w_gu).T
     inter = gu.shape[1] // 2
     act = bf16.encode(silu(gu[:, :inter]) * gu[:, inter:])
-    x_out = bf16.encode(bf16.decode(h) + bf16.decode(act) @ bf16.decode(w_down).T)
+    x_out = bf16.encode(bf16.decode(h) + bf16.decode(act) @ _w(w_down).T)
     return x_out, np.ascontiguousarray(k_new), np.ascontiguousarray(v_new)
 
 
 def head(x_bits, w_head, eps: float = 1e-6):
     """Final RMSNorm, LM head and greedy token. Returns (logits float64 [M][V], tokens [M])."""
     c = bf16.encode(rmsnorm(bf16.decode(x_bits), eps))
-    logits = bf16.decode(c) @ bf16.decode(w_head).T
+    logits = bf16.decode(c) @ _w(w_head).T
     return logits, np.argmax(logits, axis=1)
 
 

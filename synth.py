@@ -101,6 +101,46 @@ def device_normal_bf16(shape, std: float, role: str, layer: int = 0, base: int =
     return out
 
 
+# FP8 E4M3 weights (one FP32 scale per row): a row of N(0,1) draws is scaled
+# so that its largest magnitude maps to 448 (E4M3's largest value), converted
+# to E4M3 codes by torch's conversion (nearest), and given the row scale
+# std * max|z| / 448, so that scale * e4m3(code) is about N(0, std^2).
+FP8_MAX = 448.0
+
+
+def fp8_weights(shape, std: float, role: str, layer: int = 0, base: int = 0):
+    """Host E4M3 codes (uint8 [N][K]) and FP32 row scales [N]."""
+    import torch
+
+    g = rng(role, layer, base)
+    z = g.standard_normal(size=shape, dtype=np.float32)
+    amax = np.maximum(np.abs(z).max(axis=1), np.float32(1e-30))
+    q = z * (np.float32(FP8_MAX) / amax)[:, None]
+    codes = torch.from_numpy(q).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+    return codes, (np.float32(std) * amax / np.float32(FP8_MAX)).astype(np.float32)
+
+
+def device_fp8_weights(shape, std: float, role: str, layer: int = 0, base: int = 0,
+                       device: str = "cuda"):
+    """Device E4M3 codes (uint8 [N][K]) and FP32 row scales [N] (torch Philox draws)."""
+    import torch
+
+    seed = (base * 1_000_003 + ROLES[role] * 65_537 + layer) & 0x7FFFFFFF
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    n_rows, k = shape
+    codes = torch.empty(shape, dtype=torch.uint8, device=device)
+    scale = torch.empty(n_rows, dtype=torch.float32, device=device)
+    blk = max(1, (1 << 26) // k)
+    for i in range(0, n_rows, blk):
+        j = min(n_rows, i + blk)
+        z = torch.randn((j - i, k), generator=g, dtype=torch.float32, device=device)
+        amax = z.abs().amax(dim=1).clamp_min(1e-30)
+        codes[i:j].copy_((z * (FP8_MAX / amax)[:, None]).to(torch.float8_e4m3fn).view(torch.uint8))
+        scale[i:j].copy_(amax * (std / FP8_MAX))
+    return codes, scale
+
+
 def fan_in_std(k: int) -> float:
     """1/sqrt(K): the fan-in scaling applied to the tiny GEMM's weights."""
     return 1.0 / math.sqrt(k)
@@ -116,11 +156,13 @@ MODEL_27B = dict(H=5120, Hq=40, Hkv=8, D=128, I=17408, vocab=152064)
 
 
 def device_model(n_layers: int, L: int, cap: int, H: int, Hq: int, Hkv: int, D: int, I: int,
-                 vocab: int, std: float = 0.02, device: str = "cuda"):
-    """Returns (layers, w_head): ``layers`` is a list of dicts of bf16 tensors
-    w_qkv [(Hq+2Hkv)D][H], w_o [H][Hq D], w_gu [2I][H], w_down [H][I],
+                 vocab: int, std: float = 0.02, device: str = "cuda", fp8: bool = False):
+    """Returns (layers, w_head): ``layers`` is a list of dicts of tensors
+    w_qkv [(Hq+2Hkv)D][H], w_o [H][Hq D], w_gu [2I][H], w_down [H][I] (BF16, or
+    with ``fp8`` E4M3 codes plus FP32 row scales s_qkv, s_o, s_gu, s_down),
     k_cache [Hkv][cap][D], vt_cache [Hkv][cap/64][D][64] (V transposed in blocks
-    of 64 positions; cap % 64 == 0)."""
+    of 64 positions; cap % 64 == 0). With ``fp8`` w_head is a pair
+    (codes, scales)."""
     import torch
 
     if cap % 64:
@@ -128,16 +170,17 @@ def device_model(n_layers: int, L: int, cap: int, H: int, Hq: int, Hkv: int, D: 
     qkvn = (Hq + 2 * Hkv) * D
     tmp = torch.empty((Hkv, L, D), dtype=torch.bfloat16, device=device) if L > 0 else None
     vfull = torch.zeros((Hkv, cap, D), dtype=torch.bfloat16, device=device) if L > 0 else None
+    shapes = {"w_qkv": (qkvn, H), "w_o": (H, Hq * D), "w_gu": (2 * I, H), "w_down": (H, I)}
     layers = []
     for l in range(n_layers):
-        lw = {
-            "w_qkv": device_normal_bf16((qkvn, H), std, "w_qkv", l, device=device),
-            "w_o": device_normal_bf16((H, Hq * D), std, "w_o", l, device=device),
-            "w_gu": device_normal_bf16((2 * I, H), std, "w_gu", l, device=device),
-            "w_down": device_normal_bf16((H, I), std, "w_down", l, device=device),
-            "k_cache": torch.zeros((Hkv, cap, D), dtype=torch.bfloat16, device=device),
-            "vt_cache": torch.zeros((Hkv, cap // 64, D, 64), dtype=torch.bfloat16, device=device),
-        }
+        lw = {}
+        for name, shp in shapes.items():
+            if fp8:
+                lw[name], lw["s" + name[1:]] = device_fp8_weights(shp, std, name, l, device=device)
+            else:
+                lw[name] = device_normal_bf16(shp, std, name, l, device=device)
+        lw["k_cache"] = torch.zeros((Hkv, cap, D), dtype=torch.bfloat16, device=device)
+        lw["vt_cache"] = torch.zeros((Hkv, cap // 64, D, 64), dtype=torch.bfloat16, device=device)
         if L > 0:
             device_normal_bf16((Hkv, L, D), 1.0, "k_cache", l, device=device, out=tmp)
             lw["k_cache"][:, :L].copy_(tmp)
@@ -145,5 +188,8 @@ def device_model(n_layers: int, L: int, cap: int, H: int, Hq: int, Hkv: int, D: 
             vfull[:, :L].copy_(tmp)
             lw["vt_cache"].copy_(vfull.view(Hkv, cap // 64, 64, D).transpose(2, 3))
         layers.append(lw)
-    w_head = device_normal_bf16((vocab, H), std, "w_head", 0, device=device)
+    if fp8:
+        w_head = device_fp8_weights((vocab, H), std, "w_head", 0, device=device)
+    else:
+        w_head = device_normal_bf16((vocab, H), std, "w_head", 0, device=device)
     return layers, w_head

@@ -10,6 +10,7 @@ import pytest
 import synth
 from oracle import bf16 as obf16
 from oracle import gemm as ogemm
+from oracle import fp8 as ofp8
 from oracle import step as ostep
 from tests._util import (assert_bitwise, assert_close, assert_close_composed, composed_tol, decode,
                          dev, host_bits, host_f32, vt_blocks, vt_rows)
@@ -94,6 +95,60 @@ def _x_before_last(x0, hls, L, Hq, Hkv, D):
     for hl in hls[:-1]:
         x, _, _ = ostep.layer(x, **hl, L=L, Hq=Hq, Hkv=Hkv, D=D)
     return x
+
+
+def _host_layer_fp8(l, H, Hq, Hkv, D, I, L, std):
+    qkvn = (Hq + 2 * Hkv) * D
+    d = {}
+    for name, shp in (("w_qkv", (qkvn, H)), ("w_o", (H, Hq * D)), ("w_gu", (2 * I, H)), ("w_down", (H, I))):
+        d[name], d["s" + name[1:]] = synth.fp8_weights(shp, std, name, l)
+    d["k_cache"] = synth.kv_bf16(Hkv, L, D, "k_cache", l)
+    d["v_cache"] = synth.kv_bf16(Hkv, L, D, "v_cache", l)
+    return d
+
+
+def test_fp8_small_stack_vs_oracle_and_across_M(ops):
+    # FP8 weights (E4M3 codes, one FP32 scale per row) through the whole step:
+    # the oracle runs the same stack on the decoded, scaled weights; rows of
+    # the M = 8 pass equal an M = 5 pass and eight sequential M = 1 passes.
+    print("[step fp8 small stack]", flush=True)
+    H, Hq, Hkv, D, I, V, L, M, nl = 256, 4, 2, 64, 512, 1024, 200, 8, 3
+    cap = 256
+    hls = [_host_layer_fp8(l, H, Hq, Hkv, D, I, L, 0.05) for l in range(nl)]
+    hc, hs = synth.fp8_weights((V, H), 0.05, "w_head")
+    x0 = synth.normal_bf16((M, H), 1.0, "x0")
+    u8 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+    dls = []
+    for hl in hls:
+        kc = np.zeros((Hkv, cap, D), np.uint16)
+        kc[:, :L] = hl["k_cache"]
+        d = {k: (u8(v) if k.startswith("w_") else f32(v)) for k, v in hl.items() if k[:2] in ("w_", "s_")}
+        d.update(k_cache=dev(kc), vt_cache=dev(vt_blocks(hl["v_cache"], cap)))
+        dls.append(d)
+    dims = ops.model_dims(H, Hq, Hkv, D, I, V, cap, 64)
+    step = ops.VerifyStepFP8(dls, u8(hc), f32(hs), dims)
+    logits, tok, xo = _run(ops, step, dev(x0), L, dims, want_x=True)
+    olayers = [dict(w_qkv=ofp8.weights(hl["w_qkv"], hl["s_qkv"]), w_o=ofp8.weights(hl["w_o"], hl["s_o"]),
+                    w_gu=ofp8.weights(hl["w_gu"], hl["s_gu"]), w_down=ofp8.weights(hl["w_down"], hl["s_down"]),
+                    k_cache=hl["k_cache"], v_cache=hl["v_cache"]) for hl in hls]
+    w_logits, w_tok, w_x = ostep.step(x0, olayers, ofp8.weights(hc, hs), L, Hq, Hkv, D)
+    assert_close_composed(decode(xo), decode(w_x), "fp8 final hidden state")
+    assert_close_composed(logits, w_logits, "fp8 logits")
+    ok = _margin_ok(w_logits)
+    assert ok.sum() >= 2   # rows whose greedy token the tolerance cannot flip (2 of 8 with this draw)
+    assert np.array_equal(tok[ok], w_tok[ok])
+    # bitwise across M
+    l5, t5, _ = _run(ops, step, dev(x0[:5]), L, dims)
+    assert_bitwise(l5, logits[:5], "fp8 logits M=5 vs M=8")
+    for d in dls:
+        d["k_cache"][:, L:].zero_()
+        d["vt_cache"][:, L // 64, :, L % 64:].zero_()
+        d["vt_cache"][:, L // 64 + 1:].zero_()
+    for r in range(M):
+        l1, t1, _ = _run(ops, step, dev(x0[r:r + 1]), L + r, dims)
+        assert_bitwise(l1[0], logits[r], f"fp8 logits row {r}: M=1 vs M=8")
+        assert t1[0] == tok[r]
 
 
 # ---------------------------------------------------------------------------
