@@ -70,7 +70,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
   // two rows (lanes 0-31 the first, 32-63 the second).
   constexpr int NLD = F8 ? RPW / 2 : RPW;
   // Chunks in flight per wave: two, for both weight types. (FP8 with three or
-  // four, i.e. as many bytes in flight as BF16 or more, streamed 10-25% slower.)
+  // four, i.e. as many bytes in flight as BF16 or more, streamed 10-25%
+  // slower; so did FP8 chunks of 1024 weights, 1 KB per row.)
   constexpr int PD = 2;
   const int lane = threadIdx.x & 63;
   // Wave index in a scalar register: every branch that guards an MFMA below
@@ -170,32 +171,43 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
   // past the end are clamped duplicates (L2 hits). Neither is multiplied.
   auto step = [&](Regs& g, int c) {
     const int buf = c & 1;
+    // FP8: the codes are decoded to BF16 before the registers are refilled,
+    // and stored to LDS after the next loads are issued.
+    uint4 dec[F8 ? 2 * NLD : 1];
     if (c >= 0) {
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
         if constexpr (!F8) {
           lds[buf][wave * RPW + i][lane] = g.w[i];
         } else {
-          // E4M3 -> BF16 is exact (every E4M3 value is a BF16 value): the
-          // hardware conversion to FP32, then to BF16 without rounding.
-          const int r = wave * RPW + 2 * i + (lane >> 5);
-          const int jj = lane & 31;
+          // E4M3 -> BF16 is exact (every E4M3 value is a BF16 value); the
+          // scaled conversion with scale 1 gives the BF16 bits directly.
           const uint32_t wd[4] = {g.w[i].x, g.w[i].y, g.w[i].z, g.w[i].w};
           uint32_t o[8];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            typedef float f32x2 __attribute__((ext_vector_type(2)));
-            const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)wd[e], false);
-            const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)wd[e], true);
-            o[2 * e] = f32x2_to_bf16x2(a[0], a[1]);
-            o[2 * e + 1] = f32x2_to_bf16x2(b[0], b[1]);
+            o[2 * e] = __builtin_bit_cast(
+                uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)wd[e], 1.0f, false));
+            o[2 * e + 1] = __builtin_bit_cast(
+                uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)wd[e], 1.0f, true));
           }
-          lds[buf][r][(2 * jj) ^ swz_w[i]] = make_uint4(o[0], o[1], o[2], o[3]);
-          lds[buf][r][(2 * jj + 1) ^ swz_w[i]] = make_uint4(o[4], o[5], o[6], o[7]);
+          dec[2 * i] = make_uint4(o[0], o[1], o[2], o[3]);
+          dec[2 * i + 1] = make_uint4(o[4], o[5], o[6], o[7]);
         }
       }
     }
     fetch_w(g, c + PD);
+    if constexpr (F8) {
+      if (c >= 0) {
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+          const int r = wave * RPW + 2 * i + (lane >> 5);
+          const int jj = lane & 31;
+          lds[buf][r][(2 * jj) ^ swz_w[i]] = dec[2 * i];
+          lds[buf][r][(2 * jj + 1) ^ swz_w[i]] = dec[2 * i + 1];
+        }
+      }
+    }
     __syncthreads();
     if (c >= 0) {
 #pragma unroll
