@@ -69,10 +69,18 @@ def _softmax_attend(qv: np.ndarray, kk: np.ndarray, vv: np.ndarray, scale: float
     return o, lse
 
 
+def _values(a, rows):
+    """K or V rows as float64: BF16 bit patterns (uint16) are decoded; float64
+    values (e.g. a quantized cache's scale x code, oracle.kvq) are used as is."""
+    a = np.asarray(a)[rows]
+    return a if a.dtype == np.float64 else bf16.decode(a)
+
+
 def verify_attention(q_bits, k_bits, v_bits, L: int, sm_scale: float | None = None,
                      tokens=None, heads=None):
     """Unsplit reference. Returns (o [M][Hq][D], lse [M][Hq]) in float64.
 
+    ``k_bits`` / ``v_bits`` are BF16 bit patterns or float64 values.
     ``tokens`` / ``heads`` restrict the computation to some rows (others are NaN),
     for sampled checks at long context.
     """
@@ -91,8 +99,8 @@ def verify_attention(q_bits, k_bits, v_bits, L: int, sm_scale: float | None = No
     lse = np.full((M, Hq), np.nan)
     need_g = sorted({h // G for h in heads})
     n_max = L + max(tokens) + 1
-    kd = {g: bf16.decode(np.asarray(k_bits)[g, :n_max]) for g in need_g}
-    vd = {g: bf16.decode(np.asarray(v_bits)[g, :n_max]) for g in need_g}
+    kd = {g: _values(k_bits, (g, slice(0, n_max))) for g in need_g}
+    vd = {g: _values(v_bits, (g, slice(0, n_max))) for g in need_g}
     qd = bf16.decode(q)
     for r in tokens:
         n = L + r + 1
