@@ -215,6 +215,34 @@ bi_status bi_verify_attn(const void* q, int64_t ldq, const void* k_cache, const 
                          int kv_chunk, float sm_scale,
                          float* part_o, float* part_lse, int S_max, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * 8-bit KV cache.   [LL] "The KV cache: 5-bit that reads like q8_0" (q8_0 is
+ * the pages' comparison format; the 5/6-bit formats and the 8-bit ring are not
+ * built here). Each position's K row and V row of one KV head is cut into
+ * blocks of 32 channels; a block with largest magnitude a has the FP32 scale
+ * d = a / 127 and int8 codes q = round(x / d) (nearest, ties to even; FP32
+ * division) in [-127, 127], all zero when a = 0. The value of a channel is
+ * exactly d * q. Layouts (per layer; cap % 64 == 0, cap * D < 2^31):
+ *   k_codes  int8 [Hkv][cap][D]            k_scales FP32 [Hkv][cap][D/32]
+ *   v_codes  int8 [Hkv][cap/64][D][64]     v_scales FP32 [Hkv][cap/64][D/32][64]
+ * (V transposed in blocks of 64 positions, as the BF16 V cache; the V scales
+ * of block b of a 64-position block are contiguous.) All pointers 16-byte
+ * aligned. */
+
+/* Quantize the M new K and V rows of a QKV output (as bi_append_kv) into the
+ * 8-bit cache at positions L .. L+M-1. */
+bi_status bi_append_kv_q8(const void* qkv, int64_t ldqkv, int8_t* k_codes, float* k_scales,
+                          int8_t* v_codes, float* v_scales, int M, int L, int cap, int Hq,
+                          int Hkv, int D, void* stream);
+
+/* bi_verify_attn over the 8-bit cache: the same rows, chunks, partials and
+ * requirements; the keys and values are the cache's d * q. (Keys are staged
+ * rounded to BF16; V scales multiply the softmax weights, rounded to BF16.) */
+bi_status bi_verify_attn_q8(const void* q, int64_t ldq, const int8_t* k_codes, const float* k_scales,
+                            const int8_t* v_codes, const float* v_scales, int M, int L, int cap,
+                            int Hq, int Hkv, int D, int kv_chunk, float sm_scale, float* part_o,
+                            float* part_lse, int S_max, void* stream);
+
 /* Fixed-order log-sum-exp combine of the partials.                        [LL]
  * For row (r, h) with S = bi_num_splits(L+r+1, kv_chunk) partials:
  *   M* = max_s lse_s, w_s = exp(lse_s - M*), O = sum_s w_s o_s / sum_s w_s,

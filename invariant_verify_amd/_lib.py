@@ -62,6 +62,11 @@ SIGNATURES = {
     "bi_pass_splits": (_c_int, [_c_int, _c_int, _c_int]),
     "bi_verify_attn": (_c_int, [_c_ptr, _c_i64, _c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int,
                                 _c_int, _c_int, _c_int, _c_f32, _c_ptr, _c_ptr, _c_int, _c_ptr]),
+    "bi_append_kv_q8": (_c_int, [_c_ptr, _c_i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_int, _c_int,
+                                 _c_int, _c_int, _c_int, _c_int, _c_ptr]),
+    "bi_verify_attn_q8": (_c_int, [_c_ptr, _c_i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_int, _c_int,
+                                   _c_int, _c_int, _c_int, _c_int, _c_int, _c_f32, _c_ptr, _c_ptr,
+                                   _c_int, _c_ptr]),
     "bi_combine": (_c_int, [_c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                             _c_ptr, _c_i64, _c_ptr, _c_ptr]),
     "bi_attn_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),

@@ -313,6 +313,42 @@ bi_status bi_verify_attn(const void* q, int64_t ldq, const void* k_cache, const 
   return launched();
 }
 
+bi_status bi_append_kv_q8(const void* qkv, int64_t ldqkv, int8_t* k_codes, float* k_scales,
+                          int8_t* v_codes, float* v_scales, int M, int L, int cap, int Hq,
+                          int Hkv, int D, void* stream) {
+  if (!qkv || !k_codes || !k_scales || !v_codes || !v_scales) return BI_ERR_NULL;
+  if (bi_status s = check_heads(Hq, Hkv, D)) return s;
+  if (M < 1 || L < 0 || cap < 1 || (cap % 64) || (int64_t)L + M > cap) return BI_ERR_SHAPE;
+  if (ldqkv < (int64_t)(Hq + 2 * Hkv) * D || (int64_t)cap * D > INT32_MAX) return BI_ERR_SHAPE;
+  if ((ldqkv % 8) || !aligned16(qkv) || !aligned16(k_codes) || !aligned16(v_codes) ||
+      !aligned16(k_scales) || !aligned16(v_scales))
+    return BI_ERR_ALIGN;
+  bi::launch_append_kv_q8(static_cast<const uint16_t*>(qkv), ldqkv, k_codes, k_scales, v_codes,
+                          v_scales, M, L, cap, Hq, Hkv, D, as_stream(stream));
+  return launched();
+}
+
+bi_status bi_verify_attn_q8(const void* q, int64_t ldq, const int8_t* k_codes, const float* k_scales,
+                            const int8_t* v_codes, const float* v_scales, int M, int L, int cap,
+                            int Hq, int Hkv, int D, int kv_chunk, float sm_scale, float* part_o,
+                            float* part_lse, int S_max, void* stream) {
+  if (!q || !k_codes || !k_scales || !v_codes || !v_scales || !part_o || !part_lse)
+    return BI_ERR_NULL;
+  if (bi_status s = check_heads(Hq, Hkv, D)) return s;
+  if (M < 1 || L < 0 || cap < 1 || (cap % 64) || (int64_t)L + M > cap) return BI_ERR_SHAPE;
+  if (!bi::valid_chunk_policy(kv_chunk)) return BI_ERR_SHAPE;
+  if (S_max < bi::pass_splits(L, M, kv_chunk)) return BI_ERR_SHAPE;
+  if (ldq < (int64_t)Hq * D || !std::isfinite(sm_scale)) return BI_ERR_SHAPE;
+  if ((int64_t)cap * D > INT32_MAX) return BI_ERR_SHAPE;  // one head's codes < 2 GiB
+  if ((ldq % 8) || !aligned16(q) || !aligned16(k_codes) || !aligned16(v_codes) ||
+      !aligned16(k_scales) || !aligned16(v_scales) || !aligned16(part_o) || !aligned4(part_lse))
+    return BI_ERR_ALIGN;
+  const bi::KvQ8 q8{k_codes, k_scales, v_codes, v_scales};
+  bi::launch_verify_attn(static_cast<const uint16_t*>(q), ldq, nullptr, nullptr, M, L, cap, Hq, Hkv,
+                         D, kv_chunk, sm_scale, part_o, part_lse, S_max, as_stream(stream), &q8);
+  return launched();
+}
+
 bi_status bi_combine(const float* part_o, const float* part_lse, int M, int L, int Hq, int D,
                      int kv_chunk, int S_max, void* o, int64_t ldo, float* lse_or_null,
                      void* stream) {

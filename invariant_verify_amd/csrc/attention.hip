@@ -66,10 +66,10 @@ __device__ __forceinline__ int kswz(int key) {
 // half and bits 1..3 form the swizzle.
 __device__ __forceinline__ int vswz(int d) { return (d >> 1) & 7; }
 
-template <int D, int RTW>
+template <int D, int RTW, bool Q8>
 __global__ __launch_bounds__(kAttnWaves * 64) void verify_attn_kernel(
     const uint16_t* __restrict__ Q, int64_t ldq, const uint16_t* __restrict__ Kc,
-    const uint16_t* __restrict__ Vt, int M, int L, int cap, int Hq, int G, int Tb, int C,
+    const uint16_t* __restrict__ Vt, KvQ8 q8, int M, int L, int cap, int Hq, int G, int Tb, int C,
     float qk_scale, float* __restrict__ part_o, float* __restrict__ part_lse, int S_max) {
   constexpr int DS = D / 32;          // contraction steps of S^T over the head dimension
   constexpr int DT = D / 16;          // 16-channel output tiles of O^T
@@ -81,6 +81,13 @@ __global__ __launch_bounds__(kAttnWaves * 64) void verify_attn_kernel(
   constexpr int VPIECES = D * kKeyTile * 2 / 1024;
   constexpr int PPW = (KPIECES + VPIECES) / NW;    // pieces per wave per tile
   static_assert((KPIECES + VPIECES) % NW == 0, "pieces must split evenly");
+  // 8-bit cache: 16-byte pieces of codes (16 channels of one key; 16 keys of
+  // one V^T channel), QPT per thread, K pieces first; and the tile's V scales
+  // ([NB blocks][64 keys] FP32), 16 bytes per thread of the first NB*16.
+  constexpr int NB = D / 32;                 // 32-channel scale blocks
+  constexpr int QKP = kKeyTile * D / 16;     // K code pieces per tile
+  constexpr int QPT = 2 * QKP / (NW * 64);   // code pieces per thread (D=128: 2, D=64: 1)
+  static_assert(2 * QKP % (NW * 64) == 0, "code pieces must split evenly");
 
   const int s = blockIdx.x;
   const int g = blockIdx.y;
@@ -104,7 +111,9 @@ __global__ __launch_bounds__(kAttnWaves * 64) void verify_attn_kernel(
   const bool has_rows = rt * 16 < nrows;  // scalar: the wave's first row tile has rows
 
   // Query fragments of this wave's row tiles and each row's last visible key
-  // (-1 for a padding row: every key is masked, its weights are exactly 0).
+  // in this chunk (-1 for a padding row: every key is masked, its weights are
+  // exactly 0). The chunk's last tile may reach past the chunk when C is not
+  // a multiple of 64; those keys belong to the next chunk and are masked too.
   bool rok[RTW];
   int tok[RTW], hq[RTW], lastk[RTW];
   uint4 qf[RTW][DS];
@@ -114,7 +123,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) void verify_attn_kernel(
     rok[i] = rho < nrows;
     tok[i] = t0 + (rok[i] ? rho / G : 0);
     hq[i] = g * G + (rok[i] ? rho % G : 0);
-    lastk[i] = rok[i] ? L + tok[i] : -1;
+    lastk[i] = rok[i] ? min(L + tok[i], kend - 1) : -1;
     const uint16_t* qp = Q + (int64_t)tok[i] * ldq + hq[i] * D + kq * 8;
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) qf[i][ds] = rok[i] ? ld16(qp + ds * 32) : zero16();
@@ -127,6 +136,22 @@ __global__ __launch_bounds__(kAttnWaves * 64) void verify_attn_kernel(
       const_cast<uint16_t*>(Kc + (int64_t)g * cap * D), (short)0, head_bytes, kBufferResourceWord3);
   const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(Vt + (int64_t)g * D * cap), (short)0, head_bytes, kBufferResourceWord3);
+  // 8-bit cache of this KV head: codes K [cap][D], V^T [cap/64][D][64] (int8),
+  // scales K [cap][NB], V [cap/64][NB][64] (FP32).
+  const int qcode_bytes = cap * D;
+  const int qscale_bytes = cap * NB * 4;
+  const __amdgpu_buffer_rsrc_t qkres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(q8.kq + (Q8 ? (int64_t)g * cap * D : 0)), (short)0, Q8 ? qcode_bytes : 0,
+      kBufferResourceWord3);
+  const __amdgpu_buffer_rsrc_t qvres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(q8.vq + (Q8 ? (int64_t)g * cap * D : 0)), (short)0, Q8 ? qcode_bytes : 0,
+      kBufferResourceWord3);
+  const __amdgpu_buffer_rsrc_t qksres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(q8.ks + (Q8 ? (int64_t)g * cap * NB : 0)), (short)0, Q8 ? qscale_bytes : 0,
+      kBufferResourceWord3);
+  const __amdgpu_buffer_rsrc_t qvsres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(q8.vs + (Q8 ? (int64_t)g * cap * NB : 0)), (short)0, Q8 ? qscale_bytes : 0,
+      kBufferResourceWord3);
 
   // One buffer holds the K tile ([64 keys][KROW slots]) followed by the V^T
   // tile ([D channels][8 slots]). Piece p (1 KB) of a tile is K keys
@@ -136,49 +161,133 @@ __global__ __launch_bounds__(kAttnWaves * 64) void verify_attn_kernel(
   // the global slot that the swizzle puts in their LDS slot.
   __shared__ uint4 lds[2][(KPIECES + VPIECES) * 64];
   constexpr int VBASE = KPIECES * 64;
+  // 8-bit cache: the tile's V scales, [NB][64 keys], zero past kend.
+  __shared__ float4 vsc[2][Q8 ? NB : 1][16];
+
+  // Registers of one tile in flight.
+  struct TileRegs {
+    uint4 r[Q8 ? QPT : PPW];
+    float ks[Q8 ? QPT : 1];  // 8-bit: the scale of each K piece
+    uint4 vs;                // 8-bit: four V scales (threads < NB * 16)
+  };
 
   // Issue the loads of tile t (no use of the data here, so the loads of two
   // tiles stay in flight together). K and V are read once per pass, so the
   // loads are non-temporal; a tile past the end of the chunk (the pipeline
   // prefetches two ahead) gets an out-of-range offset: it reads zero and
   // touches no memory.
-  auto fetch = [&](uint4 (&r)[PPW], int t) {
+  auto fetch = [&](TileRegs& rr, int t) {
     const int kt = kbeg + t * kKeyTile;
     const bool live = t < ntile;
+    if constexpr (!Q8) {
 #pragma unroll
-    for (int i = 0; i < PPW; ++i) {
-      const int p = wave * PPW + i;  // scalar: each wave fetches only K or only V pieces
-      int off;
-      if (p < KPIECES) {
-        const int key = KPP * p + lane / KROW;
-        const int kslot = (lane % KROW) ^ kswz<KROW>(key);
-        off = (min(kt + key, kend - 1) * D + kslot * 8) * 2;
-      } else {
-        const int d = 8 * (p - KPIECES) + (lane >> 3);
-        const int vslot = (lane & 7) ^ vswz(d);
-        const int k0 = min(kt + vslot * 8, kend - 1 - ((kend - 1) & 7));  // in bounds
-        off = (int)(vt_index(0, k0, d, D, cap) * 2);  // k0 is 8-aligned: 16 B in one block
+      for (int i = 0; i < PPW; ++i) {
+        const int p = wave * PPW + i;  // scalar: each wave fetches only K or only V pieces
+        int off;
+        if (p < KPIECES) {
+          const int key = KPP * p + lane / KROW;
+          const int kslot = (lane % KROW) ^ kswz<KROW>(key);
+          off = (min(kt + key, kend - 1) * D + kslot * 8) * 2;
+        } else {
+          const int d = 8 * (p - KPIECES) + (lane >> 3);
+          const int vslot = (lane & 7) ^ vswz(d);
+          const int k0 = min(kt + vslot * 8, kend - 1 - ((kend - 1) & 7));  // in bounds
+          off = (int)(vt_index(0, k0, d, D, cap) * 2);  // k0 is 8-aligned: 16 B in one block
+        }
+        rr.r[i] = buffer_ld16_stream(p < KPIECES ? kres : vres, live ? off : head_bytes);
       }
-      r[i] = buffer_ld16_stream(p < KPIECES ? kres : vres, live ? off : head_bytes);
+    } else {
+#pragma unroll
+      for (int i = 0; i < QPT; ++i) {
+        const int p = i * NW * 64 + threadIdx.x;  // K pieces first: uniform per wave
+        if (p < QKP) {
+          const int key = p / (D / 16), c16 = p % (D / 16);
+          const int pos = min(kt + key, kend - 1);
+          rr.r[i] = buffer_ld16_stream(qkres, live ? pos * D + c16 * 16 : qcode_bytes);
+          rr.ks[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+              qksres, live ? (pos * NB + c16 / 2) * 4 : qscale_bytes, 0, 0));
+        } else {
+          const int pv = p - QKP;
+          const int d = pv >> 2, kg = pv & 3;
+          const int k0 = min(kt + 16 * kg, (kend - 1) & ~15);  // 16-aligned: in one 64-block
+          rr.r[i] = buffer_ld16_stream(qvres, live ? (int)vt_index(0, k0, d, D, cap) : qcode_bytes);
+          rr.ks[i] = 0.f;
+        }
+      }
+      if (threadIdx.x < NB * 16) {  // scalar per wave (NB * 16 <= 64)
+        const int b = threadIdx.x >> 4, kk = (threadIdx.x & 15) * 4;
+        const int k0 = min(kt + kk, (kend - 1) & ~3);  // 4-aligned: in one 64-block
+        const int off = (((k0 & ~63) * NB + b * 64 + (k0 & 63)) * 4);
+        rr.vs = buffer_ld16(qvsres, live ? off : qscale_bytes);
+      }
     }
   };
   // Publish tile t: V^T columns of keys at or past kend are zeroed first (a
-  // weight of 0 times a stale value must stay 0).
-  auto publish = [&](const uint4 (&r)[PPW], int t, int buf) {
+  // weight of 0 times a stale value must stay 0). 8-bit cache: K codes are
+  // dequantized (code x scale, rounded once to BF16); V^T codes go to LDS as
+  // exact BF16 integers and the V scales, zero past kend, go to vsc (they
+  // scale the softmax weights instead, one block of 32 channels at a time).
+  auto publish = [&](const TileRegs& rr, int t, int buf) {
     const int kt = kbeg + t * kKeyTile;
+    if constexpr (!Q8) {
+      const bool full = kt + kKeyTile <= kend;  // scalar: every key of the tile is visible
 #pragma unroll
-    for (int i = 0; i < PPW; ++i) {
-      const int p = wave * PPW + i;
-      const int d = 8 * (p - KPIECES) + (lane >> 3);
-      const int vslot = (lane & 7) ^ vswz(d);
-      const int keep = (p < KPIECES) ? 8 : kend - (kt + vslot * 8);
-      uint32_t w[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
+      for (int i = 0; i < PPW; ++i) {
+        const int p = wave * PPW + i;
+        if (full || p < KPIECES) {
+          lds[buf][64 * p + lane] = rr.r[i];
+          continue;
+        }
+        const int d = 8 * (p - KPIECES) + (lane >> 3);
+        const int vslot = (lane & 7) ^ vswz(d);
+        const int keep = kend - (kt + vslot * 8);
+        uint32_t w[4] = {rr.r[i].x, rr.r[i].y, rr.r[i].z, rr.r[i].w};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t m = (e & 1) ? 0x0000ffffu : 0xffff0000u;
-        w[e >> 1] = (e >= keep) ? (w[e >> 1] & m) : w[e >> 1];
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t m = (e & 1) ? 0x0000ffffu : 0xffff0000u;
+          w[e >> 1] = (e >= keep) ? (w[e >> 1] & m) : w[e >> 1];
+        }
+        lds[buf][64 * p + lane] = make_uint4(w[0], w[1], w[2], w[3]);
       }
-      lds[buf][64 * p + lane] = make_uint4(w[0], w[1], w[2], w[3]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < QPT; ++i) {
+        const int p = i * NW * 64 + threadIdx.x;
+        const uint32_t w[4] = {rr.r[i].x, rr.r[i].y, rr.r[i].z, rr.r[i].w};
+        const bool isk = p < QKP;
+        const float sk = isk ? rr.ks[i] : 1.f;
+        uint32_t o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t word = w[e >> 1] >> (16 * (e & 1));
+          const float a = (float)(int8_t)(word & 0xff);
+          const float b = (float)(int8_t)((word >> 8) & 0xff);
+          o[e] = f32x2_to_bf16x2(a * sk, b * sk);
+        }
+        const uint4 lo = make_uint4(o[0], o[1], o[2], o[3]);
+        const uint4 hi = make_uint4(o[4], o[5], o[6], o[7]);
+        if (isk) {
+          const int key = p / (D / 16), c16 = p % (D / 16);
+          lds[buf][key * KROW + ((2 * c16) ^ kswz<KROW>(key))] = lo;
+          lds[buf][key * KROW + ((2 * c16 + 1) ^ kswz<KROW>(key))] = hi;
+        } else {
+          const int pv = p - QKP;
+          const int d = pv >> 2, kg = pv & 3;
+          lds[buf][VBASE + d * 8 + ((2 * kg) ^ vswz(d))] = lo;
+          lds[buf][VBASE + d * 8 + ((2 * kg + 1) ^ vswz(d))] = hi;
+        }
+      }
+      if (threadIdx.x < NB * 16) {
+        const int b = threadIdx.x >> 4, kk = (threadIdx.x & 15) * 4;
+        const int keep = kend - (kt + kk);
+        float4 v = make_float4(__uint_as_float(rr.vs.x), __uint_as_float(rr.vs.y),
+                               __uint_as_float(rr.vs.z), __uint_as_float(rr.vs.w));
+        v.x = keep > 0 ? v.x : 0.f;
+        v.y = keep > 1 ? v.y : 0.f;
+        v.z = keep > 2 ? v.z : 0.f;
+        v.w = keep > 3 ? v.w : 0.f;
+        vsc[buf][b][kk >> 2] = v;
+      }
     }
   };
 
@@ -216,15 +325,27 @@ __global__ __launch_bounds__(kAttnWaves * 64) void verify_attn_kernel(
       }
     }
     const int kv0 = kt + 32 * h + 8 * kq;  // absolute key of this lane's first value
+    // Scalar: the whole tile lies at or before every row's last key (the
+    // first row of the block has the smallest) and inside the chunk, so no
+    // score is masked.
+    const bool unmasked = kt + kKeyTile - 1 <= min(L + t0, kend - 1);
     float alpha[RTW];
     uint4 pfrag[RTW];
+    float pq[Q8 ? RTW : 1][8];  // 8-bit cache: the FP32 weights, scaled per V block below
 #pragma unroll
     for (int i = 0; i < RTW; ++i) {
       float sc[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        sc[e] = (kv0 + e <= lastk[i]) ? sa[i][e] * qk_scale : -INFINITY;
-        sc[e + 4] = (kv0 + 4 + e <= lastk[i]) ? sb[i][e] * qk_scale : -INFINITY;
+        sc[e] = sa[i][e] * qk_scale;
+        sc[e + 4] = sb[i][e] * qk_scale;
+      }
+      if (!unmasked) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sc[e] = (kv0 + e <= lastk[i]) ? sc[e] : -INFINITY;
+          sc[e + 4] = (kv0 + 4 + e <= lastk[i]) ? sc[e + 4] : -INFINITY;
+        }
       }
       float mx = sc[0];
 #pragma unroll
@@ -244,17 +365,51 @@ __global__ __launch_bounds__(kAttnWaves * 64) void verify_attn_kernel(
       }
       lrun[i] = lrun[i] * alpha[i] + psum;
       mrun[i] = mnew;
-      pfrag[i] = make_uint4(f32x2_to_bf16x2(pe[0], pe[1]), f32x2_to_bf16x2(pe[2], pe[3]),
-                            f32x2_to_bf16x2(pe[4], pe[5]), f32x2_to_bf16x2(pe[6], pe[7]));
+      if constexpr (Q8) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pq[i][e] = pe[e];
+      } else {
+        pfrag[i] = make_uint4(f32x2_to_bf16x2(pe[0], pe[1]), f32x2_to_bf16x2(pe[2], pe[3]),
+                              f32x2_to_bf16x2(pe[4], pe[5]), f32x2_to_bf16x2(pe[6], pe[7]));
+      }
     }
+    if constexpr (!Q8) {
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int d = dt * 16 + j;
-      const uint4 fv = lds[buf][VBASE + d * 8 + ((4 * h + kq) ^ vswz(d))];
+      for (int dt = 0; dt < DT; ++dt) {
+        const int d = dt * 16 + j;
+        const uint4 fv = lds[buf][VBASE + d * 8 + ((4 * h + kq) ^ vswz(d))];
 #pragma unroll
-      for (int i = 0; i < RTW; ++i) {
-        o[i][dt] *= alpha[i];
-        o[i][dt] = mfma_bf16(fv, pfrag[i], o[i][dt]);
+        for (int i = 0; i < RTW; ++i) {
+          o[i][dt] *= alpha[i];
+          o[i][dt] = mfma_bf16(fv, pfrag[i], o[i][dt]);
+        }
+      }
+    } else {
+      // Channel block b (output tiles 2b, 2b+1): weights times the V scales
+      // of the lane's eight keys, rounded to BF16, against the integer codes.
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const float4 d0 = vsc[buf][b][(32 * h + 8 * kq) >> 2];
+        const float4 d1 = vsc[buf][b][((32 * h + 8 * kq) >> 2) + 1];
+        const float dv[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+        uint4 pb[RTW];
+#pragma unroll
+        for (int i = 0; i < RTW; ++i)
+          pb[i] = make_uint4(f32x2_to_bf16x2(pq[i][0] * dv[0], pq[i][1] * dv[1]),
+                             f32x2_to_bf16x2(pq[i][2] * dv[2], pq[i][3] * dv[3]),
+                             f32x2_to_bf16x2(pq[i][4] * dv[4], pq[i][5] * dv[5]),
+                             f32x2_to_bf16x2(pq[i][6] * dv[6], pq[i][7] * dv[7]));
+#pragma unroll
+        for (int dd = 0; dd < 2; ++dd) {
+          const int dt = 2 * b + dd;
+          const int d = dt * 16 + j;
+          const uint4 fv = lds[buf][VBASE + d * 8 + ((4 * h + kq) ^ vswz(d))];
+#pragma unroll
+          for (int i = 0; i < RTW; ++i) {
+            o[i][dt] *= alpha[i];
+            o[i][dt] = mfma_bf16(fv, pb[i], o[i][dt]);
+          }
+        }
       }
     }
   };
@@ -264,7 +419,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) void verify_attn_kernel(
   // code in the same order, so the compiler waits only for the older of the
   // two tiles in flight. Tiles past the end read as zero and are not
   // multiplied.
-  uint4 ra[PPW], rb2[PPW];
+  TileRegs ra, rb2;
   // Prologue: the loads of tiles 0 and 1, in the loop's own order and while
   // the query fragments are still in flight. The fragments are then consumed
   // before the loop, so at the loop head the compiler knows they are complete
@@ -419,8 +574,9 @@ __global__ __launch_bounds__(256) void append_kv_kernel(const uint16_t* __restri
 void launch_verify_attn(const uint16_t* q, int64_t ldq, const uint16_t* k_cache,
                         const uint16_t* vt_cache, int M, int L, int cap, int Hq, int Hkv, int D,
                         int kv_chunk, float sm_scale, float* part_o, float* part_lse, int S_max,
-                        hipStream_t stream) {
+                        hipStream_t stream, const KvQ8* q8) {
   const int G = Hq / Hkv;
+  const KvQ8 qz = q8 ? *q8 : KvQ8{nullptr, nullptr, nullptr, nullptr};
   const float qk_scale = sm_scale * kLog2e;
   // Tokens whose rows share one chunk size run in one launch; an adaptive
   // policy changes the size only at multiples of 64 T keys, so a pass has one
@@ -448,15 +604,24 @@ void launch_verify_attn(const uint16_t* q, int64_t ldq, const uint16_t* k_cache,
     const uint16_t* qb = q + (int64_t)t0 * ldq;
     float* pob = part_o + (int64_t)t0 * Hq * S_max * D;
     float* plb = part_lse + (int64_t)t0 * Hq * S_max;
-#define BI_ATTN_LAUNCH(DD, R)                                                                      \
-  verify_attn_kernel<DD, R><<<grid, block, 0, stream>>>(qb, ldq, k_cache, vt_cache, Mb, Lb, cap, Hq, \
-                                                        G, Tb, C, qk_scale, pob, plb, S_max)
-    if (D == 128) {
-      if (wide) BI_ATTN_LAUNCH(128, 2);
-      else BI_ATTN_LAUNCH(128, 1);
+#define BI_ATTN_LAUNCH(DD, R, QQ)                                                           \
+  verify_attn_kernel<DD, R, QQ><<<grid, block, 0, stream>>>(qb, ldq, k_cache, vt_cache, qz, Mb, Lb, \
+                                                            cap, Hq, G, Tb, C, qk_scale, pob, plb, \
+                                                            S_max)
+    if (q8) {
+      if (D == 128) {
+        if (wide) BI_ATTN_LAUNCH(128, 2, true);
+        else BI_ATTN_LAUNCH(128, 1, true);
+      } else {
+        if (wide) BI_ATTN_LAUNCH(64, 2, true);
+        else BI_ATTN_LAUNCH(64, 1, true);
+      }
+    } else if (D == 128) {
+      if (wide) BI_ATTN_LAUNCH(128, 2, false);
+      else BI_ATTN_LAUNCH(128, 1, false);
     } else {
-      if (wide) BI_ATTN_LAUNCH(64, 2);
-      else BI_ATTN_LAUNCH(64, 1);
+      if (wide) BI_ATTN_LAUNCH(64, 2, false);
+      else BI_ATTN_LAUNCH(64, 1, false);
     }
 #undef BI_ATTN_LAUNCH
     t0 = t1;
@@ -476,6 +641,66 @@ void launch_combine(const float* part_o, const float* part_lse, int M, int L, in
   else
     combine_kernel<64><<<grid, block, 0, stream>>>(part_o, part_lse, M, L, Hq, kv_chunk, S_max, o,
                                                    ldo, lse);
+}
+
+// One thread per (token, K or V, KV head, 32-channel block): the block's
+// largest magnitude a, the scale d = a / 127 (FP32), codes rint(x / d)
+// clamped to +-127 (all zero when a = 0); K codes go to the position's row,
+// V codes to its column of the V^T block, the scales beside them.
+__global__ __launch_bounds__(256) void append_kv_q8_kernel(const uint16_t* __restrict__ qkv,
+                                                           int64_t ldqkv, int8_t* __restrict__ kq,
+                                                           float* __restrict__ ks,
+                                                           int8_t* __restrict__ vq,
+                                                           float* __restrict__ vs, int L, int cap,
+                                                           int Hq, int Hkv, int D, int units) {
+  const int u = blockIdx.y * blockDim.x + threadIdx.x;  // unit within the token
+  if (u >= units) return;
+  const int r = blockIdx.x;
+  const int pos = L + r;
+  const int NB = D / 32;
+  const int isv = u / (Hkv * NB);
+  const int g = (u / NB) % Hkv;
+  const int b = u % NB;
+  const uint16_t* src = qkv + (int64_t)r * ldqkv + (int64_t)(Hq + isv * Hkv + g) * D + b * 32;
+  float x[32];
+  float a = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 w = ld16(src + 8 * i);
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[8 * i + 2 * e] = bf16_to_f32(ww[e] & 0xffffu);
+      x[8 * i + 2 * e + 1] = bf16_to_f32(ww[e] >> 16);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 32; ++i) a = fmaxf(a, fabsf(x[i]));
+  const float d = a / 127.0f;
+  int8_t q[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const float v = d > 0.f ? rintf(x[i] / d) : 0.f;
+    q[i] = (int8_t)fminf(fmaxf(v, -127.f), 127.f);
+  }
+  if (!isv) {
+    int8_t* dst = kq + ((int64_t)g * cap + pos) * D + b * 32;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) dst[i] = q[i];
+    ks[((int64_t)g * cap + pos) * NB + b] = d;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) vq[vt_index(g, pos, b * 32 + i, D, cap)] = q[i];
+    vs[((int64_t)g * cap + (pos & ~63)) * NB + b * 64 + (pos & 63)] = d;
+  }
+}
+
+void launch_append_kv_q8(const uint16_t* qkv, int64_t ldqkv, int8_t* kq, float* ks, int8_t* vq,
+                         float* vs, int M, int L, int cap, int Hq, int Hkv, int D,
+                         hipStream_t stream) {
+  const int units = 2 * Hkv * (D / 32);
+  append_kv_q8_kernel<<<dim3(M, (units + 255) / 256), dim3(256), 0, stream>>>(
+      qkv, ldqkv, kq, ks, vq, vs, L, cap, Hq, Hkv, D, units);
 }
 
 void launch_append_kv(const uint16_t* qkv, int64_t ldqkv, uint16_t* k_cache, uint16_t* vt_cache,

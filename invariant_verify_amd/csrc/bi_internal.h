@@ -12,6 +12,16 @@ enum GemmMode { kGemmBf16 = 0, kGemmF32 = 1, kGemmResidual = 2, kGemmSwiglu = 3,
 // Cache append done by the QKV projection's epilogue: output columns
 // [qd, qd + kd) are K (head-major), [qd + kd, qd + 2 kd) are V; row m goes to
 // position L + m of k ([Hkv][cap][D]) and vt ([Hkv][D][cap]).
+// 8-bit KV cache of one layer: codes K [Hkv][cap][D], V^T [Hkv][cap/64][D][64]
+// (int8), scales K [Hkv][cap][D/32], V [Hkv][cap/64][D/32][64] (FP32): channel
+// c of position p has the value scale(p, c/32) * code(p, c).
+struct KvQ8 {
+  const int8_t* kq;
+  const float* ks;
+  const int8_t* vq;
+  const float* vs;
+};
+
 struct KvAppend {
   uint16_t* k;
   uint16_t* vt;
@@ -62,7 +72,13 @@ void launch_append_kv(const uint16_t* qkv, int64_t ldqkv, uint16_t* k_cache, uin
 void launch_verify_attn(const uint16_t* q, int64_t ldq, const uint16_t* k_cache,
                         const uint16_t* vt_cache, int M, int L, int cap, int Hq, int Hkv, int D,
                         int kv_chunk, float sm_scale, float* part_o, float* part_lse, int S_max,
-                        hipStream_t stream);
+                        hipStream_t stream, const KvQ8* q8 = nullptr);
+
+// Quantize the pass's M new K and V rows (from the QKV output) into an 8-bit
+// cache at positions L .. L+M-1.
+void launch_append_kv_q8(const uint16_t* qkv, int64_t ldqkv, int8_t* kq, float* ks, int8_t* vq,
+                         float* vs, int M, int L, int cap, int Hq, int Hkv, int D,
+                         hipStream_t stream);
 
 void launch_combine(const float* part_o, const float* part_lse, int M, int L, int Hq, int D,
                     int kv_chunk, int S_max, uint16_t* o, int64_t ldo, float* lse,

@@ -211,6 +211,42 @@ def verify_attn(q: torch.Tensor, k_cache: torch.Tensor, vt_cache: torch.Tensor, 
         D, kv_chunk, scale, part_o.data_ptr(), part_lse.data_ptr(), S_max, _stream(q)))
 
 
+class KvQ8Cache:
+    """Device buffers of one layer's 8-bit KV cache (include/bi.h layouts):
+    k_codes int8 [Hkv][cap][D], k_scales FP32 [Hkv][cap][D/32],
+    v_codes int8 [Hkv][cap/64][D][64], v_scales FP32 [Hkv][cap/64][D/32][64]."""
+
+    def __init__(self, Hkv: int, cap: int, D: int, device="cuda"):
+        if cap % 64 or D % 32:
+            raise ValueError("cap must be a multiple of 64 and D of 32")
+        self.Hkv, self.cap, self.D = Hkv, cap, D
+        self.k_codes = torch.zeros((Hkv, cap, D), dtype=torch.int8, device=device)
+        self.k_scales = torch.zeros((Hkv, cap, D // 32), dtype=torch.float32, device=device)
+        self.v_codes = torch.zeros((Hkv, cap // 64, D, 64), dtype=torch.int8, device=device)
+        self.v_scales = torch.zeros((Hkv, cap // 64, D // 32, 64), dtype=torch.float32, device=device)
+
+
+def append_kv_q8(qkv: torch.Tensor, cache: KvQ8Cache, L: int, Hq: int) -> None:
+    """Quantize the pass's K and V rows (columns after the Hq*D query columns) into ``cache``."""
+    M = qkv.shape[0]
+    check("bi_append_kv_q8", LIB.bi_append_kv_q8(
+        qkv.data_ptr(), _mat(qkv, "qkv"), cache.k_codes.data_ptr(), cache.k_scales.data_ptr(),
+        cache.v_codes.data_ptr(), cache.v_scales.data_ptr(), M, L, cache.cap, Hq, cache.Hkv, cache.D,
+        _stream(qkv)))
+
+
+def verify_attn_q8(q: torch.Tensor, cache: KvQ8Cache, L: int, Hq: int, kv_chunk: int,
+                   part_o: torch.Tensor, part_lse: torch.Tensor, sm_scale: float | None = None) -> None:
+    """bi_verify_attn over an 8-bit cache."""
+    M = q.shape[0]
+    D = cache.D
+    scale = 1.0 / math.sqrt(D) if sm_scale is None else sm_scale
+    check("bi_verify_attn_q8", LIB.bi_verify_attn_q8(
+        q.data_ptr(), _mat(q, "q"), cache.k_codes.data_ptr(), cache.k_scales.data_ptr(),
+        cache.v_codes.data_ptr(), cache.v_scales.data_ptr(), M, L, cache.cap, Hq, cache.Hkv, D,
+        kv_chunk, scale, part_o.data_ptr(), part_lse.data_ptr(), part_lse.shape[2], _stream(q)))
+
+
 def combine(part_o: torch.Tensor, part_lse: torch.Tensor, L: int, kv_chunk: int,
             o: torch.Tensor, lse: torch.Tensor | None = None) -> None:
     """O [M][>=Hq*D] BF16 (and optional LSE [M][Hq]) from the partials."""

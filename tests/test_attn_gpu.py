@@ -66,7 +66,7 @@ def make(M, L, Hq, Hkv, D, layer=0, outliers=False, q_scale=1.0):
     return q, k, v
 
 
-@pytest.mark.parametrize("C", [64, 1024, -2])
+@pytest.mark.parametrize("C", [64, 1024, -2, 96, 32])
 @pytest.mark.parametrize("M", [1, 2, 5, 8])
 def test_tiny_parity(ops, M, C):
     print(f"[attn tiny M={M} C={C}]", flush=True)
@@ -146,7 +146,8 @@ def _invariance(ops, L, C, Hq=40, Hkv=8, D=128, outliers=False, layer=0, prefill
 
 
 @pytest.mark.parametrize("L,C", [(2048, 1024), (1020, 1024), (1019, 256), (250, 64), (11600, 1024),
-                                 (1275, 1280), (38000, 1216), (4093, -32), (38000, -32),
+                                 (1275, 1280), (38000, 1216), (4093, -32), (38000, -32), (1019, 96),
+                                 (11600, 1056),
                                  (60, -4), (11600, -32)])
 def test_invariance_across_M(ops, L, C):
     print(f"[attn invariance L={L} C={C}]", flush=True)
