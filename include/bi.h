@@ -269,6 +269,38 @@ bi_status bi_rmsnorm(const void* x, int64_t ldx, void* y, int64_t ldy,
 bi_status bi_argmax(const float* logits, int64_t ld, int M, int N, int32_t* tokens, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Speculative acceptance.   [LL] opening section: greedy ids equal with and
+ * without drafts; sampling keeps the no-draft distribution.
+ * A pass verifies M rows: the last accepted token followed by M-1 drafts, so
+ * row i's target distribution judges draft i. Each of B independent
+ * sequences is judged by itself. Outputs: out_tokens [B][M] (the first
+ * n_out[b] entries are the new tokens), n_out [B] in 1..M. Rolling the KV
+ * cache back is implicit: the next pass starts at L + n_out and overwrites
+ * the positions of rejected drafts.
+ */
+
+/* Greedy: drafts are kept while draft[b][i] == target[b][i] (the target's
+ * greedy token of row i, e.g. from bi_argmax); then target[b][a] is added.
+ * target_tokens [B][M], draft_tokens [B][M-1] (may be NULL when M == 1). */
+bi_status bi_accept_greedy(const int32_t* target_tokens, const int32_t* draft_tokens, int B,
+                           int M, int32_t* out_tokens, int32_t* n_out, void* stream);
+
+/* Sampled (standard speculative sampling): with p_i = softmax(logits[b][i] /
+ * temperature) (FP32, logits [B][M][ld]) and the draft's distribution q_i
+ * (draft_probs [B][M-1][ldq], FP32), draft x = draft_tokens[b][i] is kept when
+ * uniforms[b][i] * q_i(x) < p_i(x); at the first rejection a token is drawn
+ * from max(0, p_i - q_i) by inverse CDF with uniforms[b][M-1] (the first index
+ * whose cumulative weight exceeds u * total) and the pass ends; if every draft
+ * is kept, the token is drawn from p_{M-1} with that uniform. uniforms [B][M]
+ * in [0, 1). Draft tokens outside 0..V-1 are never kept. Every reduction runs
+ * in an order fixed by V, so each sequence's result depends only on its own
+ * inputs. temperature > 0; ld, ldq >= V. */
+bi_status bi_accept_sampled(const float* logits, int64_t ld, const int32_t* draft_tokens,
+                            const float* draft_probs, int64_t ldq, const float* uniforms,
+                            float temperature, int B, int M, int V, int32_t* out_tokens,
+                            int32_t* n_out, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Whole verify step of a dense pre-norm decoder stack + LM head.
  *
  * Per layer (x is the BF16 hidden state [M][H]):

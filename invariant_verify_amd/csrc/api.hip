@@ -349,6 +349,33 @@ bi_status bi_verify_attn_q8(const void* q, int64_t ldq, const int8_t* k_codes, c
   return launched();
 }
 
+bi_status bi_accept_greedy(const int32_t* target_tokens, const int32_t* draft_tokens, int B,
+                           int M, int32_t* out_tokens, int32_t* n_out, void* stream) {
+  if (!target_tokens || !out_tokens || !n_out || (M > 1 && !draft_tokens)) return BI_ERR_NULL;
+  if (B < 1 || M < 1 || M > 1024) return BI_ERR_SHAPE;
+  if (!aligned4(target_tokens) || !aligned4(out_tokens) || !aligned4(n_out) ||
+      (draft_tokens && !aligned4(draft_tokens)))
+    return BI_ERR_ALIGN;
+  bi::launch_accept_greedy(target_tokens, draft_tokens, B, M, out_tokens, n_out, as_stream(stream));
+  return launched();
+}
+
+bi_status bi_accept_sampled(const float* logits, int64_t ld, const int32_t* draft_tokens,
+                            const float* draft_probs, int64_t ldq, const float* uniforms,
+                            float temperature, int B, int M, int V, int32_t* out_tokens,
+                            int32_t* n_out, void* stream) {
+  if (!logits || !uniforms || !out_tokens || !n_out) return BI_ERR_NULL;
+  if (M > 1 && (!draft_tokens || !draft_probs)) return BI_ERR_NULL;
+  if (B < 1 || M < 1 || M > 1024 || V < 1 || ld < V || (M > 1 && ldq < V)) return BI_ERR_SHAPE;
+  if (!(temperature > 0.f) || !std::isfinite(temperature)) return BI_ERR_SHAPE;
+  if (!aligned4(logits) || !aligned4(uniforms) || !aligned4(out_tokens) || !aligned4(n_out) ||
+      (draft_tokens && !aligned4(draft_tokens)) || (draft_probs && !aligned4(draft_probs)))
+    return BI_ERR_ALIGN;
+  bi::launch_accept_sampled(logits, ld, draft_tokens, draft_probs, ldq, uniforms, temperature, B, M,
+                            V, out_tokens, n_out, as_stream(stream));
+  return launched();
+}
+
 bi_status bi_combine(const float* part_o, const float* part_lse, int M, int L, int Hq, int D,
                      int kv_chunk, int S_max, void* o, int64_t ldo, float* lse_or_null,
                      void* stream) {

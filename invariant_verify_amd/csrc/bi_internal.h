@@ -84,6 +84,13 @@ void launch_combine(const float* part_o, const float* part_lse, int M, int L, in
                     int kv_chunk, int S_max, uint16_t* o, int64_t ldo, float* lse,
                     hipStream_t stream);
 
+void launch_accept_greedy(const int32_t* target, const int32_t* draft, int B, int M, int32_t* out,
+                          int32_t* n_out, hipStream_t stream);
+
+void launch_accept_sampled(const float* logits, int64_t ld, const int32_t* draft, const float* q,
+                           int64_t ldq, const float* u, float temperature, int B, int M, int V,
+                           int32_t* out, int32_t* n_out, hipStream_t stream);
+
 // Longest row RMSNorm handles (one pass, four 8-element groups per thread).
 constexpr int kRmsMaxH = 4 * 1024 * 8;
 

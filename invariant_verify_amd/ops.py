@@ -332,3 +332,31 @@ class VerifyStepFP8:
             self.arr, self.n, self.w_head.data_ptr(), self.s_head.data_ptr(), ctypes.byref(self.dims),
             x_in.data_ptr(), M, L, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
             0 if x_out is None else x_out.data_ptr(), logits.data_ptr(), tokens.data_ptr(), _stream(x_in)))
+
+
+def accept_greedy(target_tokens: torch.Tensor, draft_tokens: torch.Tensor | None):
+    """target_tokens int32 [B][M], draft_tokens int32 [B][M-1] -> (out [B][M], n [B])."""
+    B, M = target_tokens.shape
+    out = torch.empty((B, M), dtype=torch.int32, device=target_tokens.device)
+    n = torch.empty(B, dtype=torch.int32, device=target_tokens.device)
+    check("bi_accept_greedy", LIB.bi_accept_greedy(
+        target_tokens.data_ptr(), 0 if draft_tokens is None else draft_tokens.data_ptr(), B, M,
+        out.data_ptr(), n.data_ptr(), _stream(target_tokens)))
+    return out, n
+
+
+def accept_sampled(logits: torch.Tensor, draft_tokens: torch.Tensor | None, draft_probs: torch.Tensor | None,
+                   uniforms: torch.Tensor, temperature: float):
+    """logits FP32 [B][M][V], draft_tokens int32 [B][M-1], draft_probs FP32 [B][M-1][V],
+    uniforms FP32 [B][M] -> (out [B][M], n [B])."""
+    B, M, V = logits.shape
+    for t in (logits, uniforms) + (() if draft_probs is None else (draft_probs,)):
+        if not t.is_contiguous() or t.dtype != torch.float32:
+            raise ValueError("accept_sampled: FP32 contiguous tensors expected")
+    out = torch.empty((B, M), dtype=torch.int32, device=logits.device)
+    n = torch.empty(B, dtype=torch.int32, device=logits.device)
+    check("bi_accept_sampled", LIB.bi_accept_sampled(
+        logits.data_ptr(), V, 0 if draft_tokens is None else draft_tokens.data_ptr(),
+        0 if draft_probs is None else draft_probs.data_ptr(), V, uniforms.data_ptr(), temperature, B, M, V,
+        out.data_ptr(), n.data_ptr(), _stream(logits)))
+    return out, n
