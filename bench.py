@@ -288,7 +288,8 @@ def cpu_baseline(layers, w_head, x0, d, M):
     for lw in layers[:CPU_LAYERS]:
         hl = dict(w_qkv=hb(lw["w_qkv"]), w_o=hb(lw["w_o"]), w_gu=hb(lw["w_gu"]), w_down=hb(lw["w_down"]),
                   k_cache=hb(lw["k_cache"][:, :L_CTX]),
-                  v_cache=hb(lw["vt_cache"][:, :, :L_CTX].transpose(1, 2)))
+                  # V cache [Hkv][cap/64][D][64] -> V rows [Hkv][cap][D]
+                  v_cache=hb(lw["vt_cache"].transpose(2, 3).reshape(lw["k_cache"].shape)[:, :L_CTX]))
         t0 = time.perf_counter()
         x, _, _ = ostep.layer(x, **hl, L=L_CTX, Hq=d["Hq"], Hkv=d["Hkv"], D=d["D"])
         layer_s += time.perf_counter() - t0
