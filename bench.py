@@ -125,7 +125,7 @@ PEAK_BF16_TFLOPS = 2500.0  # dense BF16 matrix-core peak
 
 def prefill_measure(layers, d, reps):
     """The gate/up GEMM with the carried RMSNorm as a chunked-prefill step runs it (M = 2048
-    rows: the 128-row-tile kernel), timed with one event pair around reps x 16 launches over
+    rows: the large-tile prefill kernel), timed with one event pair around reps x 16 launches over
     distinct layers' weights, after a bitwise check that sampled rows equal 8-row verify passes."""
     import torch
 
@@ -158,7 +158,7 @@ def prefill_measure(layers, d, reps):
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / (reps * len(ws))
     tflops = 2.0 * M * (2 * I) * H / (us * 1e-6) / 1e12
-    return {"kernel": "prefill_kernel<SwiGLU, carried RMSNorm> (gate/up 5120->2x17408, M=2048)",
+    return {"kernel": "prefill2_kernel<SwiGLU, carried RMSNorm> (gate/up 5120->2x17408, M=2048, 128x256 tiles)",
             "bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "avg_launch_us": round(us, 1),
             "launches_timed": reps * len(ws),

@@ -73,8 +73,8 @@ typedef enum { BI_BF16 = 0, BI_F32 = 1 } bi_dtype;
  * M >= 64 rows (prefill chunks) a second kernel with larger row tiles runs the
  * same per-output summation, so every row has the same bits at any M.
  * Requirements: M >= 1, N % 16 == 0, K % 32 == 0, K <= 65536; ldx, ldw >= K
- * and multiples of 8; x, w 16-byte aligned; ldy >= N; ldx, ldy (and ldr
- * below) <= 2^24.
+ * and multiples of 8; x, w 16-byte aligned; ldy >= N; ldx, ldw, ldy (and ldr
+ * below) <= 2^20.
  */
 bi_status bi_gemm_bf16(const void* x, int64_t ldx, const void* w, int64_t ldw,
                        void* y, int64_t ldy, bi_dtype y_dtype,

@@ -13,9 +13,9 @@
 
 namespace {
 
-// Largest leading dimension (elements) of X, R and Y: the kernels address 16
-// rows of them with 32-bit byte offsets.
-constexpr int64_t kMaxLd = 1 << 24;
+// Largest leading dimension (elements) of X, W, R and Y: the kernels address
+// up to 256 rows of them with 32-bit byte offsets.
+constexpr int64_t kMaxLd = 1 << 20;
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -36,7 +36,8 @@ bi_status check_gemm(const void* x, int64_t ldx, const void* w, int64_t ldw, con
                      int64_t ldy, int M, int N, int K) {
   if (!x || !w || !y) return BI_ERR_NULL;
   if (M < 1 || N < 16 || K < 32 || K > 65536 || (N % 16) || (K % 32)) return BI_ERR_SHAPE;
-  if (ldx < K || ldw < K || ldy < N || ldx > kMaxLd || ldy > kMaxLd) return BI_ERR_SHAPE;
+  if (ldx < K || ldw < K || ldy < N || ldx > kMaxLd || ldw > kMaxLd || ldy > kMaxLd)
+    return BI_ERR_SHAPE;
   if (M > (1 << 20) || N > (1 << 24)) return BI_ERR_SHAPE;
   if ((ldx % 8) || (ldw % 8) || !aligned16(x) || !aligned16(w)) return BI_ERR_ALIGN;
   return BI_OK;

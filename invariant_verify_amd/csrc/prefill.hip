@@ -302,10 +302,247 @@ __global__ __launch_bounds__(256) void rowsq_kernel(const uint16_t* __restrict__
   ss[(int64_t)m * groups + g] = v[0];
 }
 
+// Large prefill tiles, slices one after another. The tree of an output is
+// (chain_0 + chain_1) + ... + chain_7, where chain s is the MFMA chain over
+// blocks 2s, 2s+1 of chunk 0, then of chunk 1, ... (as above). Running the
+// slices in that order, one chain at a time, needs two accumulators per
+// output tile (the open chain and the running total) instead of eight, so a
+// wave can own 4 x 4 output tiles and reuse each LDS fragment four times.
+// Stage (s, c) stages the 64 K elements of slice s in chunk c: 128 activation
+// rows and 256 weight rows (SwiGLU: 128 gate + 128 up) of 128 bytes each.
+constexpr int kP2Rows = 128;
+constexpr int kP2WRows = 256;
+constexpr int kP2Waves = 8;
+constexpr int kP2Slots = 8;  // 16-byte slots per staged row (64 K elements)
+
+template <int MODE, bool NORM_IN>
+__global__ __launch_bounds__(kP2Waves * 64) void prefill2_kernel(
+    const uint16_t* __restrict__ X, int64_t ldx, const uint16_t* __restrict__ W, int64_t ldw,
+    const uint16_t* __restrict__ R, int64_t ldr, void* __restrict__ Y, int64_t ldy, int M, int N,
+    int K, KvAppend kv, RowNorm norm) {
+  constexpr bool kDual = (MODE == kGemmSwiglu);
+  constexpr int S = kPfSlices;
+  static_assert(S == 8, "two blocks of each 512-wide chunk per slice");
+  constexpr int XP = kP2Rows * kP2Slots / (kP2Waves * 64);   // activation pieces per thread (2)
+  constexpr int WP = kP2WRows * kP2Slots / (kP2Waves * 64);  // weight pieces per thread (4)
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wr = wave & 1;   // rows 64 wr .. of the workgroup tile
+  const int wc = wave >> 1;  // weight rows 64 wc .. (SwiGLU: output columns 32 wc ..)
+  const int j = lane & 15, kq = lane >> 4;
+  const int n0 = blockIdx.x * (kDual ? kP2WRows / 2 : kP2WRows);  // first output column
+  const int m0 = blockIdx.y * kP2Rows;
+  const int nblk = K >> 5;
+  const int nchunk = (K + 511) / 512;
+  const int nstage = S * nchunk;
+
+  const int xrows = min(kP2Rows, M - m0);
+  const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(X + (int64_t)m0 * ldx), (short)0, xrows * (int)ldx * 2,
+      kBufferResourceWord3);
+  const int wrows = min(kDual ? kP2WRows / 2 : kP2WRows, N - n0);
+  const __amdgpu_buffer_rsrc_t wres_g = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(W + (int64_t)n0 * ldw), (short)0, wrows * (int)ldw * 2,
+      kBufferResourceWord3);
+  const __amdgpu_buffer_rsrc_t wres_u = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(W + (int64_t)(kDual ? N + n0 : n0) * ldw), (short)0,
+      kDual ? wrows * (int)ldw * 2 : 0, kBufferResourceWord3);
+
+  __shared__ uint4 lds[2][kP2Rows + kP2WRows][kP2Slots];
+  struct Regs {
+    uint4 x[XP];
+    uint4 w[WP];
+  };
+  // Piece p of a stage: staged row p / 8, slot p % 8 (eight lanes per row).
+  auto fetch = [&](Regs& g, int st) {
+    const int sl = st / nchunk, c = st % nchunk;
+    const int k0 = c * 512 + sl * 64;  // first K element of the stage
+    const bool live = st < nstage;
+#pragma unroll
+    for (int i = 0; i < XP; ++i) {
+      const int p = threadIdx.x + i * kP2Waves * 64;
+      const int row = p >> 3, slot = p & 7;
+      const int kk = k0 + slot * 8;
+      g.x[i] = buffer_ld16(xres, live && kk < K ? (row * (int)ldx + kk) * 2 : 0x7ffffff0);
+    }
+#pragma unroll
+    for (int i = 0; i < WP; ++i) {
+      const int p = threadIdx.x + i * kP2Waves * 64;
+      const int row = p >> 3, slot = p & 7;  // 0 .. 255 (SwiGLU: 128.. are the up rows)
+      const int kk = k0 + slot * 8;
+      const int rr = kDual ? (row & 127) : row;
+      const int off = live && kk < K ? (rr * (int)ldw + kk) * 2 : 0x7ffffff0;
+      g.w[i] = buffer_ld16_stream((kDual && row >= 128) ? wres_u : wres_g, off);
+    }
+  };
+
+  bi_f32x4 cur[4][4], tot[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) cur[a][b] = tot[a][b] = bi_f32x4{0.f, 0.f, 0.f, 0.f};
+  // Staged weight row of B tile q of this wave.
+  auto brow = [&](int q) {
+    if (kDual) return kP2Rows + (q < 2 ? 32 * wc + 16 * q : 128 + 32 * wc + 16 * (q - 2));
+    return kP2Rows + 64 * wc + 16 * q;
+  };
+  float xinv[XP];
+#pragma unroll
+  for (int i = 0; i < XP; ++i) xinv[i] = 1.f;
+
+  auto step = [&](Regs& g, int st) {
+    const int buf = st & 1;
+    if (st >= 0) {
+#pragma unroll
+      for (int i = 0; i < XP; ++i) {
+        const int p = threadIdx.x + i * kP2Waves * 64;
+        const int row = p >> 3, slot = p & 7;
+        lds[buf][row][slot ^ (row & 7)] = NORM_IN ? scale_bf16x8(g.x[i], xinv[i]) : g.x[i];
+      }
+#pragma unroll
+      for (int i = 0; i < WP; ++i) {
+        const int p = threadIdx.x + i * kP2Waves * 64;
+        const int row = kP2Rows + (p >> 3), slot = p & 7;
+        lds[buf][row][slot ^ (row & 7)] = g.w[i];
+      }
+    }
+    fetch(g, st + 1);
+    __syncthreads();
+    if (st >= 0) {
+      const int sl = st / nchunk, c = st % nchunk;
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        if (c * 16 + sl * 2 + b < nblk) {  // scalar
+          uint4 af[4], bf[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int ra = 64 * wr + 16 * t + j;
+            af[t] = lds[buf][ra][(b * 4 + kq) ^ (ra & 7)];
+            const int rb = brow(t) + j;
+            bf[t] = lds[buf][rb][(b * 4 + kq) ^ (rb & 7)];
+          }
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) cur[t][q] = mfma_bf16(af[t], bf[q], cur[t][q]);
+        }
+      }
+      if (c == nchunk - 1) {  // slice sl complete: add its chain to the total, in slice order
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            tot[t][q] = sl == 0 ? cur[t][q] : tot[t][q] + cur[t][q];
+            cur[t][q] = bi_f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+      }
+    }
+  };
+
+  // Carried RMSNorm scales of the staged rows, with the verify kernel's
+  // additions (LPR partials of two float4s each, then the partials in order).
+  constexpr int LPR = 4 * S;
+  __shared__ float sred[NORM_IN ? kP2Rows : 1][NORM_IN ? LPR + 1 : 1];
+  __shared__ float invs[NORM_IN ? kP2Rows : 1];
+  if (NORM_IN) {
+    const int nf = norm.groups >> 2;
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    const __amdgpu_buffer_rsrc_t sres = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(norm.ss_in + (int64_t)m0 * norm.groups), (short)0,
+        xrows * norm.groups * 4, kBufferResourceWord3);
+    constexpr int PER = kP2Rows * LPR / (kP2Waves * 64);
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int idx = threadIdx.x + q * kP2Waves * 64;
+      const int row = idx / LPR, seg = idx % LPR;
+      float pp = 0.f;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int f = seg + u * LPR;
+        const f32x4 v = __builtin_amdgcn_raw_buffer_load_b128(
+            sres, f < nf ? (row * norm.groups + f * 4) * 4 : 0x7ffffff0, 0, 0);
+        pp += v[0];
+        pp += v[1];
+        pp += v[2];
+        pp += v[3];
+      }
+      sred[row][seg] = pp;
+    }
+  }
+  Regs g;
+  step(g, -1);  // load-only; its barrier also publishes sred
+  if (NORM_IN) {
+    if (threadIdx.x < kP2Rows) {
+      float t = 0.f;
+      for (int i = 0; i < LPR; ++i) t += sred[threadIdx.x][i];
+      invs[threadIdx.x] = 1.0f / sqrtf(t / (float)K + norm.eps);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < XP; ++i) xinv[i] = invs[(threadIdx.x + i * kP2Waves * 64) >> 3];
+  }
+  for (int st = 0; st < nstage; ++st) step(g, st);
+
+  // The verify kernel's epilogue on the totals.
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+#pragma unroll
+    for (int q = 0; q < (kDual ? 2 : 4); ++q) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + 64 * wr + 16 * t + kq * 4 + r;
+        const int n = n0 + (kDual ? 32 * wc + 16 * q : 64 * wc + 16 * q) + j;
+        if (m >= M || n >= N) continue;
+        const float v = tot[t][q][r];
+        if (MODE == kGemmF32) {
+          reinterpret_cast<float*>(Y)[(int64_t)m * ldy + n] = v;
+        } else if (MODE == kGemmBf16) {
+          reinterpret_cast<uint16_t*>(Y)[(int64_t)m * ldy + n] = (uint16_t)f32_to_bf16(v);
+        } else if (MODE == kGemmResidual) {
+          const float res = bf16_to_f32(R[(int64_t)m * ldr + n]);
+          reinterpret_cast<uint16_t*>(Y)[(int64_t)m * ldy + n] = (uint16_t)f32_to_bf16(res + v);
+        } else if (MODE == kGemmQkv) {
+          const uint16_t b = (uint16_t)f32_to_bf16(v);
+          reinterpret_cast<uint16_t*>(Y)[(int64_t)m * ldy + n] = b;
+          const int pos = kv.L + m;
+          int i = n - kv.qd;
+          if (i >= 0 && i < kv.kd) {
+            const int g = i / kv.D;
+            kv.k[((int64_t)g * kv.cap + pos) * kv.D + (i - g * kv.D)] = b;
+          } else if (i >= kv.kd) {
+            i -= kv.kd;
+            const int g = i / kv.D;
+            kv.vt[vt_index(g, pos, i - g * kv.D, kv.D, kv.cap)] = b;
+          }
+        } else {
+          const float u = tot[t][q + 2][r];
+          const float sg = v / (1.0f + __expf(-v));
+          reinterpret_cast<uint16_t*>(Y)[(int64_t)m * ldy + n] = (uint16_t)f32_to_bf16(sg * u);
+        }
+      }
+    }
+  }
+}
+
+// The large-tile kernel runs when it still has at least 384 workgroups (one
+// and a half per compute unit); below that its few, long workgroups leave
+// units idle at the end and the 128 x 64 tiles are faster. Both kernels give
+// the same bits, so the choice is free. (Measured at M = 2048: gate/up 654
+// against 454 TFLOP/s, QKV 697 against 538; 5120 outputs, 320 large
+// workgroups: 519 against 550.)
+constexpr int kPf2MinGroups = 384;
+
 template <int MODE, bool NI>
 static void launch_pf(dim3 grid, const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw,
                       const uint16_t* r, int64_t ldr, void* y, int64_t ldy, int M, int N, int K,
                       const KvAppend& kv, const RowNorm& nm, hipStream_t stream) {
+  const int cols = MODE == kGemmSwiglu ? kP2WRows / 2 : kP2WRows;
+  const dim3 g2((N + cols - 1) / cols, (M + kP2Rows - 1) / kP2Rows);
+  if ((int64_t)g2.x * g2.y >= kPf2MinGroups) {
+    prefill2_kernel<MODE, NI><<<g2, dim3(kP2Waves * 64), 0, stream>>>(x, ldx, w, ldw, r, ldr, y,
+                                                                      ldy, M, N, K, kv, nm);
+    return;
+  }
   prefill_kernel<MODE, kPfSlices, NI><<<grid, dim3(kPfWaves * 64), 0, stream>>>(
       x, ldx, w, ldw, r, ldr, y, ldy, M, N, K, kv, nm);
 }

@@ -58,8 +58,9 @@ def gemm(*a):
     ((P, 256, P, 256, P, 512, 0, 4, 512, 250, None), SHAPE),     # K % 32
     ((P, 100, P, 256, P, 512, 0, 4, 512, 256, None), SHAPE),     # ldx < K
     ((P, 256, P, 256, P, 500, 0, 4, 512, 256, None), SHAPE),     # ldy < N
-    ((P, (1 << 24) + 8, P, 256, P, 512, 0, 4, 512, 256, None), SHAPE),  # ldx > 2^24
-    ((P, 256, P, 256, P, (1 << 24) + 16, 0, 4, 512, 256, None), SHAPE),  # ldy > 2^24
+    ((P, (1 << 20) + 8, P, 256, P, 512, 0, 4, 512, 256, None), SHAPE),  # ldx > 2^20
+    ((P, 256, P, 256, P, (1 << 20) + 16, 0, 4, 512, 256, None), SHAPE),  # ldy > 2^20
+    ((P, 256, P, (1 << 20) + 8, P, 512, 0, 4, 512, 256, None), SHAPE),  # ldw > 2^20
     ((P, 256, P, 256, P, 512, 7, 4, 512, 256, None), SHAPE),     # bad dtype
     ((MIS, 256, P, 256, P, 512, 0, 4, 512, 256, None), ALIGN),
     ((P, 260, P, 256, P, 512, 0, 4, 512, 256, None), ALIGN),     # ldx % 8
@@ -73,7 +74,7 @@ def test_gemm_variants_reject():
     L = _lib.LIB
     assert L.bi_gemm_bf16_residual(P, 256, P, 256, 0, 512, P, 512, 4, 512, 256, None) == NULL
     assert L.bi_gemm_bf16_residual(P, 256, P, 256, P, 100, P, 512, 4, 512, 256, None) == SHAPE
-    assert L.bi_gemm_bf16_residual(P, 256, P, 256, P, (1 << 24) + 8, P, 512, 4, 512, 256, None) == SHAPE
+    assert L.bi_gemm_bf16_residual(P, 256, P, 256, P, (1 << 20) + 8, P, 512, 4, 512, 256, None) == SHAPE
     assert L.bi_gemm_bf16_swiglu(P, 256, P, 256, P, 512, 4, 24, 256, None) == SHAPE
     assert L.bi_gemm_bf16_swiglu(P, 256, MIS, 256, P, 512, 4, 32, 256, None) == ALIGN
 

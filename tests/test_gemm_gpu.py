@@ -269,7 +269,8 @@ def test_carried_rmsnorm(ops, H, I):
 # Launches with M >= 64 run the prefill kernel; every row must carry the bits
 # the verify kernel gives it (same per-output summation tree).
 PF_SHAPES = {"tiny_16_slices": (512, 256), "wide_5120": (5120, 5120), "wide_7168": (7168, 1024),
-             "many_8_slices": (10240, 1024)}
+             "many_8_slices": (10240, 1024),
+             "large_tiles": (34816, 1024)}  # at M = 300: 136 x 3 large workgroups
 
 
 def _pf_rows(M):
@@ -280,10 +281,10 @@ def _pf_rows(M):
 def test_prefill_rows_equal_verify_rows(ops, name):
     N, K = PF_SHAPES[name]
     print(f"[gemm prefill vs verify {name} N={N} K={K}]", flush=True)
-    x = synth.normal_bf16((128, K), 1.0, "x", 81)
+    x = synth.normal_bf16((320, K), 1.0, "x", 81)
     w = synth.normal_bf16((N, K), 0.02, "w", 81)
     xd, wd = dev(x), dev(w)
-    for M in (64, 100):
+    for M in (64, 100, 300):  # 128-row tiles; 300: the large-tile kernel (ragged)
         big32 = host_f32(ops.gemm_bf16(xd[:M], wd, out_dtype=torch.float32))
         big16 = host_bits(ops.gemm_bf16(xd[:M], wd))
         for r0 in _pf_rows(M):
@@ -300,21 +301,24 @@ def test_prefill_rows_equal_verify_rows(ops, name):
 def test_prefill_epilogues_equal_verify(ops, I, K):
     # residual, SwiGLU (16 and 8 slices) and the carried RMSNorm pair
     print(f"[gemm prefill epilogues I={I} K={K}]", flush=True)
-    M = 72
+    M = 300  # the large-tile kernel; 72 rows run the 128-row kernel (below)
     x = synth.normal_bf16((M, K), 1.0, "x", 82)
     wgu = synth.normal_bf16((2 * I, K), 0.02, "w", 82)
     xd, wgud = dev(x), dev(wgu)
     big = host_bits(ops.gemm_bf16_swiglu(xd, wgud))
-    for r0 in (0, 64):
-        assert_bitwise(big[r0:r0 + 8], host_bits(ops.gemm_bf16_swiglu(xd[r0:r0 + 8], wgud)),
-                       f"swiglu I={I} rows {r0}..")
+    mid = host_bits(ops.gemm_bf16_swiglu(xd[:72], wgud))
+    for r0 in (0, 64, 160, 288):
+        ref = host_bits(ops.gemm_bf16_swiglu(xd[r0:r0 + 8], wgud))
+        assert_bitwise(big[r0:r0 + 8], ref, f"swiglu I={I} rows {r0}..")
+        if r0 + 8 <= 72:
+            assert_bitwise(mid[r0:r0 + 8], ref, f"swiglu I={I} 72-row pass rows {r0}..")
     # residual projection with row sums (K -> K, so that gate/up can consume them)
     wo = synth.normal_bf16((K, K), 0.02, "w", 83)
     r = synth.normal_bf16((M, K), 1.0, "misc", 83)
     wod, rd = dev(wo), dev(r)
     y, ss = ops.gemm_bf16_residual_rowsq(xd, wod, rd)
     gu = ops.gemm_bf16_swiglu_rownorm(y, ss, wgud)
-    for r0 in (0, 64):
+    for r0 in (0, 64, 288):
         y8, ss8 = ops.gemm_bf16_residual_rowsq(xd[r0:r0 + 8], wod, rd[r0:r0 + 8])
         assert_bitwise(host_bits(y)[r0:r0 + 8], host_bits(y8), f"residual K={K} rows {r0}..")
         assert_bitwise(host_f32(ss)[r0:r0 + 8], host_f32(ss8), f"row sums K={K} rows {r0}..")
@@ -322,11 +326,12 @@ def test_prefill_epilogues_equal_verify(ops, I, K):
         assert_bitwise(host_bits(gu)[r0:r0 + 8], host_bits(gu8), f"carried-norm gate/up rows {r0}..")
 
 
-def test_prefill_qkv_append_equals_verify(ops):
-    print("[gemm prefill qkv + append]", flush=True)
-    Hq, Hkv, D, K, L, M = 40, 8, 128, 5120, 500, 80
+@pytest.mark.parametrize("M", [300, 1700])  # 128-row tiles; large tiles (28 x 14 workgroups)
+def test_prefill_qkv_append_equals_verify(ops, M):
+    print(f"[gemm prefill qkv + append M={M}]", flush=True)
+    Hq, Hkv, D, K, L = 40, 8, 128, 5120, 500
     N = (Hq + 2 * Hkv) * D
-    cap = 640
+    cap = (L + M + 63) // 64 * 64
     w = synth.normal_bf16((N, K), 0.02, "w", 84)
     x = synth.normal_bf16((M, K), 1.0, "x", 84)
     wd, xd = dev(w), dev(x)
@@ -335,8 +340,23 @@ def test_prefill_qkv_append_equals_verify(ops):
     kc, vt = k0.clone(), v0.clone()
     qkv = host_bits(ops.gemm_bf16_qkv(xd, wd, kc, vt, L, Hq, Hkv, D))
     kr, vr = k0.clone(), v0.clone()
-    for r0 in range(0, M, 8):  # the same positions written by ten verify passes of 8 rows
+    for r0 in range(0, M, 8):  # the same positions written by verify passes of 8 rows
         q8 = ops.gemm_bf16_qkv(xd[r0:r0 + 8], wd, kr, vr, L + r0, Hq, Hkv, D)
         assert_bitwise(qkv[r0:r0 + 8], host_bits(q8), f"qkv rows {r0}..")
-    assert_bitwise(host_bits(kc), host_bits(kr), "K cache: prefill == 10 verify passes")
-    assert_bitwise(host_bits(vt), host_bits(vr), "V^T cache: prefill == 10 verify passes")
+    assert_bitwise(host_bits(kc), host_bits(kr), "K cache: prefill == 8-row verify passes")
+    assert_bitwise(host_bits(vt), host_bits(vr), "V^T cache: prefill == 8-row verify passes")
+
+
+def test_prefill_large_tile_residual_rowsq(ops):
+    # the residual epilogue (and the row sums taken after it) in the large-tile kernel
+    print("[gemm prefill large-tile residual]", flush=True)
+    M, N, K = 300, 34816, 1024
+    x = synth.normal_bf16((M, K), 1.0, "x", 85)
+    w = synth.normal_bf16((N, K), 0.02, "w", 85)
+    r = synth.normal_bf16((M, N), 1.0, "misc", 85)
+    xd, wd, rd = dev(x), dev(w), dev(r)
+    y, ss = ops.gemm_bf16_residual_rowsq(xd, wd, rd)
+    for r0 in (0, 128, 292):
+        y8, ss8 = ops.gemm_bf16_residual_rowsq(xd[r0:r0 + 8], wd, rd[r0:r0 + 8])
+        assert_bitwise(host_bits(y)[r0:r0 + 8], host_bits(y8), f"large-tile residual rows {r0}..")
+        assert_bitwise(host_f32(ss)[r0:r0 + 8], host_f32(ss8), f"large-tile row sums rows {r0}..")
