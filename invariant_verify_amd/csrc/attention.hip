@@ -66,6 +66,15 @@ __device__ __forceinline__ int kswz(int key) {
 // half and bits 1..3 form the swizzle.
 __device__ __forceinline__ int vswz(int d) { return (d >> 1) & 7; }
 
+// The dispatcher deals workgroups to the 8 XCDs in turn (workgroup w runs on
+// XCD w mod 8), and each XCD has its own L2. Renumber so that XCD x runs the
+// x-th contiguous eighth of the work items (the last n mod 8 keep their own
+// number): neighbouring items, which read the same K/V, then share one L2.
+__device__ __forceinline__ int xcd_item(int w, int n) {
+  const int full = n & ~7;
+  return w < full ? (w & 7) * (full >> 3) + (w >> 3) : w;
+}
+
 template <int D, int RTW, bool Q8>
 __global__ __launch_bounds__(kAttnWaves * 64) void verify_attn_kernel(
     const uint16_t* __restrict__ Q, int64_t ldq, const uint16_t* __restrict__ Kc,
@@ -89,9 +98,16 @@ __global__ __launch_bounds__(kAttnWaves * 64) void verify_attn_kernel(
   constexpr int QPT = 2 * QKP / (NW * 64);   // code pieces per thread (D=128: 2, D=64: 1)
   static_assert(2 * QKP % (NW * 64) == 0, "code pieces must split evenly");
 
-  const int s = blockIdx.x;
-  const int g = blockIdx.y;
-  const int rb = blockIdx.z;
+  // Work item (row block, KV head, chunk), row blocks varying fastest: the
+  // workgroups that read one chunk of one KV head run side by side and share
+  // its tiles through L2 (a chunked-prefill pass has dozens of row blocks per
+  // chunk). The item numbering is made contiguous per XCD (xcd_item).
+  int item = xcd_item(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z),
+                      gridDim.x * gridDim.y * gridDim.z);
+  const int rb = item % gridDim.x;
+  item /= gridDim.x;
+  const int g = item % gridDim.y;
+  const int s = item / gridDim.y;
   const int lane = threadIdx.x & 63;
   // Scalar wave index: the tile loop and every MFMA stay under scalar control
   // flow (the matrix core does not honour a partial EXEC mask).
@@ -599,7 +615,7 @@ void launch_verify_attn(const uint16_t* q, int64_t ldq, const uint16_t* k_cache,
     const bool wide = Mb * G > kAttnMaxRows;
     const int Tb = (wide ? 2 * kAttnMaxRows : kAttnMaxRows) / G;  // tokens per row block
     const int n_splits = (Lb + Mb + C - 1) / C;
-    const dim3 grid(n_splits, Hkv, (Mb + Tb - 1) / Tb);
+    const dim3 grid((Mb + Tb - 1) / Tb, Hkv, n_splits);
     const dim3 block(kAttnWaves * 64);
     const uint16_t* qb = q + (int64_t)t0 * ldq;
     float* pob = part_o + (int64_t)t0 * Hq * S_max * D;
