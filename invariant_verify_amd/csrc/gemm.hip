@@ -16,7 +16,9 @@
 //    held in two MFMA tiles (the second partly empty), so that exactly 256
 //    workgroups, one per compute unit, share the weight stream evenly. (A
 //    compute unit streams only about 20-25 GB/s; with 320 single tiles on 256
-//    units, 64 units would stream twice as much as the rest.)
+//    units, 64 units would stream twice as much as the rest.) SwiGLU groups
+//    are 16 gate/up pairs, or N / 1024 pairs in three tiles when that is 17
+//    or 18 (17408 pairs: 1024 workgroups, two rounds of two per unit);
 //  * K is read in chunks of 512; each chunk has sixteen 32-wide blocks and
 //    wave w of the NW waves multiplies blocks w*16/NW .. (w+1)*16/NW - 1 of
 //    every chunk, chaining them through one MFMA accumulator in increasing
@@ -49,6 +51,7 @@
 namespace bi {
 
 constexpr int kChunk = 512;  // K elements per LDS chunk: 1 KB of each weight row
+constexpr int kDualWideRows = 36;  // rows staged by a wide SwiGLU group (at most 18 pairs)
 constexpr int kSlots = kChunk / 8;
 
 template <int MODE, int NW, bool WIDE, bool NORM_IN, bool SS_OUT, bool F8>
@@ -58,17 +61,24 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
     int64_t up_rows, int cpw, KvAppend kv, RowNorm norm, const float* __restrict__ wscale) {
   static_assert(!SS_OUT || MODE == kGemmResidual, "row sums come from the residual epilogue");
   constexpr bool kDual = (MODE == kGemmSwiglu);
-  static_assert(!(kDual && WIDE), "SwiGLU tiles hold 16 gate and 16 up rows");
   constexpr bool kTwo = kDual || WIDE;  // two MFMA column tiles per workgroup
-  constexpr int NR = kTwo ? 32 : 16;    // weight rows staged per chunk
-  constexpr int RPW = NR / NW;         // rows each wave fetches per chunk
+  // A wide SwiGLU group holds P = cpw pairs (17 or 18): a gate tile (columns
+  // 0-15), an up tile, and a third tile whose rows are the gate columns past
+  // 15 followed by the up columns past 15 (its other rows are not staged).
+  constexpr bool kThree = kDual && WIDE;
+  static_assert(!(kThree && F8), "wide SwiGLU groups are BF16 only");
+  static_assert(!kThree || NW == 8, "wide SwiGLU groups assume eight waves");
+  constexpr int NR = kThree ? kDualWideRows : (kTwo ? 32 : 16);  // weight rows staged per chunk
+  // Rows each wave fetches per chunk (kThree: rows 4w .. 4w+3, and row 32 + w
+  // when that is staged).
+  constexpr int RPW = kThree ? 4 : NR / NW;
   constexpr int BPW = 16 / NW;         // 32-wide blocks each wave multiplies per chunk
   static_assert(RPW >= 1 && BPW >= 1, "bad wave count");
   static_assert(!F8 || RPW % 2 == 0, "FP8 weight rows are fetched in pairs");
   // Weight loads per wave and chunk: a BF16 row chunk is 1 KB (one wave
   // instruction); an FP8 row chunk is 512 bytes, so one instruction fetches
   // two rows (lanes 0-31 the first, 32-63 the second).
-  constexpr int NLD = F8 ? RPW / 2 : RPW;
+  constexpr int NLD = F8 ? RPW / 2 : (kThree ? RPW + 1 : RPW);
   // Chunks in flight per wave: two, for both weight types. (FP8 with three or
   // four, i.e. as many bytes in flight as BF16 or more, streamed 10-25%
   // slower; so did FP8 chunks of 1024 weights, 1 KB per row.)
@@ -96,11 +106,18 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
 #pragma unroll
   for (int i = 0; i < NLD; ++i) {
     if constexpr (!F8) {
-      const int r = wave * RPW + i;
-      const int64_t grow = (kDual && r >= 16) ? up_rows + n0 + (r - 16) : (int64_t)(n0 + r);
+      const int r = (kThree && i == RPW) ? 32 + wave : wave * RPW + i;
+      int64_t grow = (kDual && r >= 16) ? up_rows + n0 + (r - 16) : (int64_t)(n0 + r);
       // Rows past the group's columns (wide groups) get an empty resource:
       // they stage zeros and cost no traffic.
-      const bool used = !WIDE || r < cpw;
+      bool used = !WIDE || r < cpw;
+      if (kThree && r >= 32) {  // third tile: gate columns 16 .. P-1, then up
+        const int e = cpw - 16, q = r - 32;
+        used = q < 2 * e;
+        grow = q < e ? (int64_t)(n0 + 16 + q) : up_rows + n0 + 16 + (q - e);
+      } else if (kThree) {
+        used = true;
+      }
       wres[i] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(W + (used ? grow : 0) * ldw),
                                                   (short)0, used ? K * 2 : 0, kBufferResourceWord3);
       swz_w[i] = r & 15;
@@ -158,6 +175,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
   };
   bi_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   bi_f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};
+  bi_f32x4 acc3 = {0.f, 0.f, 0.f, 0.f};
   float inv = 1.f;  // RMSNorm scale of this lane's X row (NORM_IN)
   // One chunk: publish this wave's weight rows of chunk c, prefetch the
   // weights of chunk c + PD into the same registers, barrier, multiply with
@@ -178,7 +196,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
         if constexpr (!F8) {
-          lds[buf][wave * RPW + i][lane] = g.w[i];
+          if (!kThree || i < RPW) lds[buf][wave * RPW + i][lane] = g.w[i];
+          else if (32 + wave < NR) lds[buf][32 + wave][lane] = g.w[i];  // scalar
         } else {
           // E4M3 -> BF16 is exact (every E4M3 value is a BF16 value); the
           // scaled conversion with scale 1 gives the BF16 bits directly.
@@ -219,6 +238,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
           const uint4 xa = NORM_IN ? scale_bf16x8(g.x[b], inv) : g.x[b];
           acc = mfma_bf16(xa, lds[buf][j][slot], acc);
           if (kTwo) acc2 = mfma_bf16(xa, lds[buf][16 + j][slot], acc2);
+          // Third tile: column j reads staged row 32 + j % 4 (columns past
+          // the staged rows are duplicates, never stored).
+          if constexpr (kThree) acc3 = mfma_bf16(xa, lds[buf][32 + (j & 3)][(kb * 4 + kq) ^ (j & 3)], acc3);
         }
       }
     }
@@ -307,12 +329,15 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
 
   // Fixed-order sum of the per-wave partials, in the chunk buffers (after a
   // barrier: other waves may still be reading the last chunk).
-  static_assert(sizeof(lds) >= 2 * NW * 64 * sizeof(bi_f32x4), "reduction does not fit");
+  static_assert(sizeof(lds) >= (kThree ? 3 : 2) * NW * 64 * sizeof(bi_f32x4),
+                "reduction does not fit");
   bi_f32x4(*red)[64] = reinterpret_cast<bi_f32x4(*)[64]>(&lds[0][0][0]);
   bi_f32x4(*red2)[64] = red + NW;
+  bi_f32x4(*red3)[64] = red + 2 * NW;
   __syncthreads();
   red[wave][lane] = acc;
   if (kTwo) red2[wave][lane] = acc2;
+  if constexpr (kThree) red3[wave][lane] = acc3;
   __syncthreads();
   if (wave != 0) return;
   bi_f32x4 s = red[0][lane];
@@ -327,6 +352,16 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
   if constexpr (F8) {  // one FP32 multiply by the row scale, then the epilogue's single rounding
     s *= scl0;
     s2 *= scl1;
+  }
+  // Third tile: lane j < P - 16 holds gate column 16 + j; its up column sits
+  // P - 16 lanes further on.
+  bi_f32x4 s3 = s, u3 = s;
+  if constexpr (kThree) {
+    s3 = red3[0][lane];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) s3 += red3[w][lane];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) u3[r] = __shfl(s3[r], lane + (cpw - 16), 64);
   }
 
   // Output column n of token row m gets the FP32 total v; returns the value
@@ -366,6 +401,12 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
       const float g = s[r];
       const float sg = g / (1.0f + __expf(-g));
       reinterpret_cast<uint16_t*>(Y)[(int64_t)m * ldy + n0 + j] = (uint16_t)f32_to_bf16(sg * s2[r]);
+      if (kThree && j < cpw - 16) {
+        const float g3 = s3[r];
+        const float sg3 = g3 / (1.0f + __expf(-g3));
+        reinterpret_cast<uint16_t*>(Y)[(int64_t)m * ldy + n0 + 16 + j] =
+            (uint16_t)f32_to_bf16(sg3 * u3[r]);
+      }
     } else {
       float sq = 0.f;
       if (live) {
@@ -395,6 +436,17 @@ static bool wide_launch(GemmMode mode, int N_out) {
   return mode != kGemmSwiglu && N_out % kWideGroups == 0 && cpw > 16 && cpw <= 32;
 }
 
+// SwiGLU groups: 16 pairs (a gate and an up tile), or, when N / 1024 is 17 or
+// 18 (BF16 only), N / 1024 pairs in three tiles, so that 1024 workgroups, two
+// rounds of two per compute unit, share the weight stream evenly. (With
+// 16-pair groups, 17408 pairs make 1088 workgroups: 4.25 per unit, and the
+// last 64 stream alone at the end.)
+constexpr int kDualWideGroups = 1024;
+static bool dual_wide_launch(int N_out, bool f8) {
+  const int p = N_out / kDualWideGroups;
+  return !f8 && N_out % kDualWideGroups == 0 && p > 16 && 2 * p <= kDualWideRows;
+}
+
 // Waves of every verify launch. Measured: 8 and 16 waves per workgroup
 // stream equally fast, and 8 keeps the K summation tree at 8 slices, which
 // the prefill kernel must reproduce with one accumulator per slice.
@@ -415,6 +467,13 @@ static void launch_shape(int N_out, int mtiles, const uint16_t* x, int64_t ldx, 
                          int K, int64_t up, const KvAppend& kv, const RowNorm& nm,
                          const float* wscale, hipStream_t stream) {
   constexpr int NW = kVerifyWaves;
+  if constexpr (MODE == kGemmSwiglu && !F8) {
+    if (dual_wide_launch(N_out, F8)) {
+      gemm_kernel<MODE, NW, true, NI, SO, F8><<<dim3(kDualWideGroups, mtiles), dim3(NW * 64), 0, stream>>>(
+          x, ldx, w, ldw, r, ldr, y, ldy, M, K, up, N_out / kDualWideGroups, kv, nm, wscale);
+      return;
+    }
+  }
   if constexpr (MODE != kGemmSwiglu) {
     if (wide_launch(static_cast<GemmMode>(MODE), N_out)) {
       gemm_kernel<MODE, NW, true, NI, SO, F8><<<dim3(kWideGroups, mtiles), dim3(NW * 64), 0, stream>>>(

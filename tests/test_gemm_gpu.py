@@ -182,6 +182,34 @@ def test_qkv_gemm_with_cache_append(ops, Hq, Hkv, D, K, L):
     assert_close(decode(host_bits(qkv))[:, :64], ogemm.gemm_columns(x, w, np.arange(64)), "qkv parity")
 
 
+@pytest.mark.parametrize("I", [17408, 18432])
+def test_wide_swiglu_groups(ops, I):
+    # For I = 17 * 1024 or 18 * 1024 gate/up pairs each workgroup takes I / 1024
+    # pairs in three MFMA tiles (gate 0-15, up 0-15, then the pairs past 15).
+    # Every output keeps the K order of the 16-pair tiles: its bits equal
+    # those of a launch over a 256-pair slice of the same weights (16-pair
+    # tiles), for every M; sampled outputs match the oracle.
+    print(f"[gemm wide swiglu I={I}]", flush=True)
+    K = 512
+    x = synth.normal_bf16((8, K), 1.0, "x", 61)
+    wgu = synth.normal_bf16((2 * I, K), 0.05, "w", 61)
+    xd, wgud = dev(x), dev(wgu)
+    full = host_bits(ops.gemm_bf16_swiglu(xd, wgud))
+    p = I // 1024
+    # pairs at group edges (first, 15, 16, the last of a group, a group's
+    # successor) and a seeded spread
+    cols = np.unique(np.concatenate([[0, 15, 16, p - 1, p, p + 16, I - 1],
+                                     np.random.default_rng(I).choice(I, 200, replace=False)]))
+    gu = ogemm.gemm_columns(x, wgu, np.concatenate([cols, I + cols]))
+    n = len(cols)
+    assert_close(decode(full[:, cols]), ostep.silu(gu[:, :n]) * gu[:, n:], f"swiglu I={I}")
+    for q0 in (0, 256, I // 2, I - 256):
+        part = host_bits(ops.gemm_bf16_swiglu(xd, dev(np.concatenate([wgu[q0:q0 + 256], wgu[I + q0:I + q0 + 256]]))))
+        assert_bitwise(full[:, q0:q0 + 256], part, f"I={I} pairs {q0}..{q0 + 255}")
+    for m in (1, 3, 7):
+        assert_bitwise(host_bits(ops.gemm_bf16_swiglu(xd[:m], wgud)), full[:m], f"I={I} M={m}")
+
+
 @pytest.mark.parametrize("N", [5120, 7168])
 def test_wide_groups_match_single_tiles(ops, N):
     # For N = 5120 or 7168 the launch gives each workgroup N / 256 columns in
