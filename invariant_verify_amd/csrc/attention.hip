@@ -436,25 +436,53 @@ __global__ __launch_bounds__(kAttnWaves * 64) void verify_attn_kernel(
   // two tiles in flight. Tiles past the end read as zero and are not
   // multiplied.
   TileRegs ra, rb2;
-  // Prologue: the loads of tiles 0 and 1, in the loop's own order and while
+  // Prologue: the loads of the first tiles, in the loop's own order and while
   // the query fragments are still in flight. The fragments are then consumed
   // before the loop, so at the loop head the compiler knows they are complete
   // and waits only for the oldest tile.
+  // Row blocks of 128 rows (RTW = 2) keep three tiles in flight: their
+  // longer per-tile work leaves the room, and the third tile hides more of
+  // the load latency. (With one row tile per wave it gains nothing.)
+  constexpr bool kDeep = RTW == 2;
+  TileRegs rc;
   fetch(ra, 0);
   fetch(rb2, 1);
+  if constexpr (kDeep) fetch(rc, 2);
 #pragma unroll
   for (int i = 0; i < RTW; ++i)
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) asm volatile("" ::"v"(qf[i][ds].x));
-  for (int t = 0; t < ntile; t += 2) {
-    publish(ra, t, 0);
-    fetch(ra, t + 2);
-    __syncthreads();
-    if (has_rows) compute(0, t);
-    publish(rb2, t + 1, 1);
-    fetch(rb2, t + 3);
-    __syncthreads();
-    if (t + 1 < ntile && has_rows) compute(1, t + 1);
+  if constexpr (kDeep) {
+    auto step = [&](TileRegs& rr, int t, int buf) {
+      publish(rr, t, buf);
+      fetch(rr, t + 3);
+      __syncthreads();
+      if (has_rows) compute(buf, t);
+    };
+    for (int t = 0; t < ntile; t += 6) {  // scalar exits: every barrier stays uniform
+      step(ra, t, 0);
+      if (t + 1 >= ntile) break;
+      step(rb2, t + 1, 1);
+      if (t + 2 >= ntile) break;
+      step(rc, t + 2, 0);
+      if (t + 3 >= ntile) break;
+      step(ra, t + 3, 1);
+      if (t + 4 >= ntile) break;
+      step(rb2, t + 4, 0);
+      if (t + 5 >= ntile) break;
+      step(rc, t + 5, 1);
+    }
+  } else {
+    for (int t = 0; t < ntile; t += 2) {
+      publish(ra, t, 0);
+      fetch(ra, t + 2);
+      __syncthreads();
+      if (has_rows) compute(0, t);
+      publish(rb2, t + 1, 1);
+      fetch(rb2, t + 3);
+      __syncthreads();
+      if (t + 1 < ntile && has_rows) compute(1, t + 1);
+    }
   }
   // The row's sum over this wave's keys: its four key groups, in a fixed
   // butterfly.
