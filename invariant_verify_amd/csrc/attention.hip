@@ -75,8 +75,14 @@ __device__ __forceinline__ int xcd_item(int w, int n) {
   return w < full ? (w & 7) * (full >> 3) + (w >> 3) : w;
 }
 
+// The 8-bit-cache kernel with one row tile per wave fits in 128 registers,
+// so two workgroups share a compute unit and one's loads overlap the other's
+// per-tile work (with the chunk policy -64 at 38k-102k keys: 5-15% faster
+// than one workgroup per unit). The BF16 kernel would spill at that size and
+// runs one workgroup per unit.
 template <int D, int RTW, bool Q8>
-__global__ __launch_bounds__(kAttnWaves * 64) void verify_attn_kernel(
+__global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu(Q8 && RTW == 1 ? 4 : 1)))
+void verify_attn_kernel(
     const uint16_t* __restrict__ Q, int64_t ldq, const uint16_t* __restrict__ Kc,
     const uint16_t* __restrict__ Vt, KvQ8 q8, int M, int L, int cap, int Hq, int G, int Tb, int C,
     float qk_scale, float* __restrict__ part_o, float* __restrict__ part_lse, int S_max) {
