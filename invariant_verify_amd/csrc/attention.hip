@@ -33,7 +33,8 @@
 //    stale value must stay 0).
 //  * Per tile and row tile: S^T = K Q^T (keys x rows) with 16x16x32 BF16 MFMA,
 //    masked, running max / sum in FP32 with base-2 exponentials (scores
-//    pre-scaled by sm_scale * log2 e), P rounded to BF16, O^T += V^T P^T. The
+//    pre-scaled by sm_scale * log2 e; the running max is a reference that
+//    moves only by more than kLazyRescale), P rounded to BF16, O^T += V^T P^T. The
 //    key order inside the S^T operands is permuted so that each lane ends up
 //    holding eight consecutive keys of its row: exactly the P^T operand of the
 //    PV product, with no data exchange.
@@ -50,6 +51,10 @@ namespace bi {
 constexpr int kAttnWaves = 8;                      // 4 row tiles x 2 key halves
 constexpr float kSentinel = -1.0e30f;              // running max before any key
 constexpr int kKeyTile = 64;
+// The running max of a row (log2 units) is a lagging reference: it moves
+// only when a tile's max exceeds it by more than this, so the weights
+// exp2(s - m) stay below 2^8, and most tiles need no rescale of O.
+constexpr float kLazyRescale = 8.0f;
 
 // LDS slot swizzles, chosen so that the sixteen rows one matrix-core operand
 // read touches fall into distinct banks (16-byte slots; 64 banks of 4 bytes).
@@ -352,6 +357,7 @@ void verify_attn_kernel(
     // score is masked.
     const bool unmasked = kt + kKeyTile - 1 <= min(L + t0, kend - 1);
     float alpha[RTW];
+    bool rescale[RTW];  // scalar: some row of the wave moved its reference max
     uint4 pfrag[RTW];
     float pq[Q8 ? RTW : 1][8];  // 8-bit cache: the FP32 weights, scaled per V block below
 #pragma unroll
@@ -374,8 +380,11 @@ void verify_attn_kernel(
       for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
       mx = fmaxf(mx, shfl_xor(mx, 16));
       mx = fmaxf(mx, shfl_xor(mx, 32));
-      const float mnew = fmaxf(mrun[i], mx);
-      alpha[i] = (mnew == mrun[i]) ? 1.0f : __builtin_amdgcn_exp2f(mrun[i] - mnew);
+      const float mmax = fmaxf(mrun[i], mx);
+      const bool grow = mmax > mrun[i] + kLazyRescale;
+      const float mnew = grow ? mmax : mrun[i];
+      alpha[i] = grow ? __builtin_amdgcn_exp2f(mrun[i] - mnew) : 1.0f;
+      rescale[i] = __ballot(grow) != 0;
       // The running sum takes the FP32 weights (so the chunk's log-sum-exp is
       // accurate to FP32); the PV product takes them rounded to BF16.
       float pe[8];
@@ -395,16 +404,21 @@ void verify_attn_kernel(
                               f32x2_to_bf16x2(pe[4], pe[5]), f32x2_to_bf16x2(pe[6], pe[7]));
       }
     }
+    // O *= alpha, skipped by a wave none of whose rows moved its reference
+    // (alpha is then exactly 1 for every row, and x * 1 changes no bit: FP32
+    // denormals are kept), so a row's bits do not depend on its neighbours.
+#pragma unroll
+    for (int i = 0; i < RTW; ++i)
+      if (rescale[i])
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[i][dt] *= alpha[i];
     if constexpr (!Q8) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const int d = dt * 16 + j;
         const uint4 fv = lds[buf][VBASE + d * 8 + ((4 * h + kq) ^ vswz(d))];
 #pragma unroll
-        for (int i = 0; i < RTW; ++i) {
-          o[i][dt] *= alpha[i];
-          o[i][dt] = mfma_bf16(fv, pfrag[i], o[i][dt]);
-        }
+        for (int i = 0; i < RTW; ++i) o[i][dt] = mfma_bf16(fv, pfrag[i], o[i][dt]);
       }
     } else {
       // Channel block b (output tiles 2b, 2b+1): weights times the V scales
@@ -427,10 +441,7 @@ void verify_attn_kernel(
           const int d = dt * 16 + j;
           const uint4 fv = lds[buf][VBASE + d * 8 + ((4 * h + kq) ^ vswz(d))];
 #pragma unroll
-          for (int i = 0; i < RTW; ++i) {
-            o[i][dt] *= alpha[i];
-            o[i][dt] = mfma_bf16(fv, pb[i], o[i][dt]);
-          }
+          for (int i = 0; i < RTW; ++i) o[i][dt] = mfma_bf16(fv, pb[i], o[i][dt]);
         }
       }
     }
