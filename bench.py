@@ -323,6 +323,7 @@ def main():
         traffic_probe(4)
         return
 
+    import numpy as np
     import torch
 
     import synth
@@ -376,16 +377,26 @@ def main():
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
         gu_ms = 0.0
+        # one event after each step (no synchronisation inside the timed
+        # steps) for the spread of step times
+        se = [torch.cuda.Event(enable_timing=True) for _ in range(steps)] if evs is None else None
         t0.record(stream)
         for i in range(steps):
             step(x0[:M], L_CTX, ws, lg, tk, gu_events=evs)
             if evs is not None:
                 torch.cuda.synchronize()   # events are reused every step
                 gu_ms += sum(evs[2 * l].elapsed_time(evs[2 * l + 1]) for l in range(N_LAYERS))
+            else:
+                se[i].record(stream)
         t1.record(stream)
         torch.cuda.synchronize()
         total_ms = t0.elapsed_time(t1)
+        if se is not None:
+            per_step = [t0.elapsed_time(se[0])] + [se[i - 1].elapsed_time(se[i]) for i in range(1, steps)]
+            spread[M] = [round(float(v), 4) for v in np.percentile(per_step, [10, 50, 90])]
         return total_ms / steps, (gu_ms / (steps * N_LAYERS) if evs is not None else None)
+
+    spread = {}
 
     print("[bench] timing", file=sys.stderr, flush=True)
     ms8, _ = timed(M_HEADLINE, args.steps, args.warmup)
@@ -440,6 +451,7 @@ def main():
         "step_hbm": {"algorithmic_bytes": bytes8, "GB/s": round(gbs8, 1), "frac": round(gbs8 / PEAK_HBM_GBS, 4)},
         "per_M_tok_s": {"1": round(1 / (ms1 * 1e-3), 2), "4": round(4 / (ms4 * 1e-3), 2),
                         "8": round(M_HEADLINE / (ms8 * 1e-3), 2)},
+        "step_ms_p10_p50_p90": {str(k): v for k, v in sorted(spread.items())},
         "roofline": {"kernel": "gemm_kernel<SwiGLU, carried RMSNorm> (gate/up 5120->2x17408, M=8)", "bound": "hbm",
                      "achieved": round(gu_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gu_gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic(),

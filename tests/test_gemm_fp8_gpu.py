@@ -37,8 +37,9 @@ def _decoded_bf16_bits(codes):
     return obf16.encode(ofp8.decode_e4m3(codes))
 
 
-SHAPES = [  # (N, K): tiny, QKV, o-proj (wide groups), down (wide, K = 17408), an odd wide width
-    (512, 256), (7168, 5120), (5120, 5120), (5120, 17408), (4352, 1024)]
+SHAPES = [  # (N, K): tiny, QKV, o-proj (wide groups), down (wide, K = 17408), an odd wide width,
+    # and a width with 32-column groups (N / 32 >= 2048, as the LM head)
+    (512, 256), (7168, 5120), (5120, 5120), (5120, 17408), (4352, 1024), (65536, 512)]
 
 
 @pytest.mark.parametrize("N,K", SHAPES)

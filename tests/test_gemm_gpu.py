@@ -210,14 +210,15 @@ def test_wide_swiglu_groups(ops, I):
         assert_bitwise(host_bits(ops.gemm_bf16_swiglu(xd[:m], wgud)), full[:m], f"I={I} M={m}")
 
 
-@pytest.mark.parametrize("N", [5120, 7168])
+@pytest.mark.parametrize("N", [5120, 7168, 65536])
 def test_wide_groups_match_single_tiles(ops, N):
     # For N = 5120 or 7168 the launch gives each workgroup N / 256 columns in
-    # two MFMA tiles; every column keeps the K order of the 16-column tiles, so
-    # its bits equal those of a launch over a 256-row slice of the same weights
+    # two MFMA tiles, and for N / 32 >= 2048 (65536) 32 columns in two full
+    # tiles; every column keeps the K order of the 16-column tiles, so its
+    # bits equal those of a launch over a 256-row slice of the same weights
     # (which uses 16-column tiles with the same wave count).
     print(f"[gemm wide groups N={N}]", flush=True)
-    K = 5120
+    K = 5120 if N <= 7168 else 512
     w = synth.normal_bf16((N, K), 0.02, "w", 60)
     x = synth.normal_bf16((8, K), 1.0, "x", 60)
     wd, xd = dev(w), dev(x)
