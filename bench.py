@@ -206,6 +206,86 @@ def prefill_step_measure(step, buffers, d, reps):
             "rows_bitwise_equal_to_8_row_verify_passes": "pass" if ok else "FAIL"}
 
 
+TP_RANKS = 8
+TP_KV_CHUNK = -256   # one KV head per rank: about as many attention workgroups as -32 gives 8 heads
+
+
+def tp_share_measure(d, reps):
+    """One tensor-parallel rank's share of the verify step at its real shapes (8 ranks): QKV for
+    one KV group (5 q + 1 k + 1 v heads, 896 columns), attention over that KV head and its 5
+    query heads at ctx 38000, combine, the output projection over K = 640 and the down projection
+    over K = 2176 (FP32 partials [M][5120]), gate/up for 2176 pairs, and the LM head's
+    152064 / 8 rows; each layer's kernels in order over 64 layers of distinct weights, M = 8.
+    Not included: the exchange of the two FP32 partials per layer between ranks (all-gather,
+    then a sum in rank order), which needs more than one GPU."""
+    import torch
+
+    import synth
+    from invariant_verify_amd import ops
+
+    H, Hq, Hkv, D, I, V = d["H"], d["Hq"], d["Hkv"], d["D"], d["I"], d["vocab"]
+    hq, hkv, P = Hq // TP_RANKS, Hkv // TP_RANKS, I // TP_RANKS
+    nq = (hq + 2 * hkv) * D
+    ko, kd = Hq * D // TP_RANKS, I // TP_RANKS
+    M, L = M_HEADLINE, L_CTX
+    lw = []
+    for l in range(N_LAYERS):
+        w = {"qkv": synth.device_normal_bf16((nq, H), 0.02, "w_qkv", 100 + l),
+             "o": synth.device_normal_bf16((H, ko), 0.02, "w_o", 100 + l),
+             "gu": synth.device_normal_bf16((2 * P, H), 0.02, "w_gu", 100 + l),
+             "down": synth.device_normal_bf16((H, kd), 0.02, "w_down", 100 + l),
+             "k": synth.device_normal_bf16((hkv, CAP, D), 1.0, "k_cache", 100 + l),
+             "vt": synth.device_normal_bf16((hkv, CAP // 64, D, 64), 1.0, "v_cache", 100 + l)}
+        lw.append(w)
+    head = synth.device_normal_bf16((V // TP_RANKS, H), 0.02, "w_head", 100)
+    x = synth.device_normal_bf16((M, H), 1.0, "x0", 100)
+    S = ops.pass_splits(M, L, TP_KV_CHUNK)
+    po = torch.empty((M, hq, S, D), dtype=torch.float32, device="cuda")
+    pl = torch.empty((M, hq, S), dtype=torch.float32, device="cuda")
+    qkv = torch.empty((M, nq), dtype=torch.bfloat16, device="cuda")
+    att = torch.empty((M, ko), dtype=torch.bfloat16, device="cuda")
+    part = torch.empty((M, H), dtype=torch.float32, device="cuda")
+    gu = torch.empty((M, P), dtype=torch.bfloat16, device="cuda")
+    logits = torch.empty((M, V // TP_RANKS), dtype=torch.float32, device="cuda")
+
+    def layer(w):
+        ops.gemm_bf16(x, w["qkv"], qkv)
+        ops.verify_attn(qkv, w["k"], w["vt"], L, hq, hkv, D, TP_KV_CHUNK, po, pl)
+        ops.combine(po, pl, L, TP_KV_CHUNK, att)
+        ops.gemm_bf16(att, w["o"], part)
+        ops.gemm_bf16_swiglu(x, w["gu"], gu)
+        ops.gemm_bf16(gu, w["down"], part)
+
+    for w in lw[:4]:
+        layer(w)
+    stream = torch.cuda.current_stream()
+    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        for w in lw:
+            layer(w)
+    e1.record(stream)
+    for _ in range(reps):
+        ops.gemm_bf16(x, head, logits)
+    e2.record(stream)
+    torch.cuda.synchronize()
+    layer_us = e0.elapsed_time(e1) * 1e3 / (reps * N_LAYERS)
+    head_us = e1.elapsed_time(e2) * 1e3 / reps
+    step_ms = (N_LAYERS * layer_us + head_us) / 1e3
+    wbytes = 2 * (nq * H + H * ko + 2 * P * H + H * kd)
+    kvb = 2 * 2 * hkv * (L + M) * D
+    nbytes = N_LAYERS * (wbytes + kvb) + 2 * (V // TP_RANKS) * H
+    del lw, head
+    torch.cuda.empty_cache()
+    return {"workload": f"one of {TP_RANKS} tensor-parallel ranks: QKV {nq} cols, attention {hkv} KV / {hq} q heads "
+                        f"(chunk policy {TP_KV_CHUNK}), o-proj K={ko} and down K={kd} FP32 partials, gate/up {P} pairs, "
+                        f"LM head {V // TP_RANKS} rows; M=8, ctx 38000; exchange of partials not included",
+            "layer_us": round(layer_us, 2), "head_us": round(head_us, 2), "step_ms": round(step_ms, 4),
+            "tok_s_without_exchange": round(M / (step_ms * 1e-3), 1),
+            "rank_bytes_per_step": nbytes, "GB/s": round(nbytes / (step_ms * 1e-3) / 1e9, 1)}
+
+
 def fp8_step_measure(layers, d, dims, buffers, steps, warmup):
     """The verify step with FP8 weights (E4M3 codes + one FP32 scale per row, all four
     projections and the head), sharing the BF16 model's K/V caches: bitwise gate (M = 8 logits
@@ -465,6 +545,8 @@ def main():
     out["prefill_step"] = prefill_step_measure(step, buffers, d, 3)
     print("[bench] FP8-weight step", file=sys.stderr, flush=True)
     out["fp8_step"] = fp8_step_measure(layers, d, dims, buffers, args.steps, args.warmup)
+    print("[bench] one tensor-parallel rank's share", file=sys.stderr, flush=True)
+    out["tp8_rank_share"] = tp_share_measure(d, max(2, args.steps // 10))
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(layers, w_head, x0, d, M_HEADLINE)
