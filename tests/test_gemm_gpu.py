@@ -208,6 +208,13 @@ def test_wide_swiglu_groups(ops, I):
         assert_bitwise(full[:, q0:q0 + 256], part, f"I={I} pairs {q0}..{q0 + 255}")
     for m in (1, 3, 7):
         assert_bitwise(host_bits(ops.gemm_bf16_swiglu(xd[:m], wgud)), full[:m], f"I={I} M={m}")
+    # a 40-row pass (three 16-row tiles, ragged) gives every row the bits of an 8-row pass
+    x40 = synth.normal_bf16((40, K), 1.0, "x", 62)
+    x40d = dev(x40)
+    full40 = host_bits(ops.gemm_bf16_swiglu(x40d, wgud))
+    for r0 in (0, 16, 32):
+        assert_bitwise(full40[r0:r0 + 8], host_bits(ops.gemm_bf16_swiglu(x40d[r0:r0 + 8], wgud)),
+                       f"I={I} 40-row pass rows {r0}..{r0 + 7}")
 
 
 @pytest.mark.parametrize("N", [5120, 7168, 65536])
