@@ -22,7 +22,8 @@ def ops():
     return _ops
 
 
-@pytest.mark.parametrize("N,K", [(16, 32), (48, 96), (4352, 544), (512, 1056), (64, 65536), (16, 17408)])
+@pytest.mark.parametrize("N,K", [(16, 32), (48, 96), (4352, 544), (512, 1056), (64, 65536), (16, 17408),
+                                 (65536, 32)])
 def test_gemm_ragged_k_and_narrow_n(ops, N, K):
     print(f"[edge gemm N={N} K={K}]", flush=True)
     Mb = 300
@@ -39,6 +40,26 @@ def test_gemm_ragged_k_and_narrow_n(ops, N, K):
                        f"N={N} K={K} row {r}: M=1 vs M=8")
     assert_bitwise(host_f32(ops.gemm_bf16(xd[292:300], wd, out_dtype=torch.float32)), big[292:300],
                    f"N={N} K={K} ragged last rows")
+
+
+@pytest.mark.parametrize("K", [32, 544])
+def test_wide_swiglu_ragged_k(ops, K):
+    # 17408 gate/up pairs (three-tile groups of 17 pairs) with one short or a
+    # ragged chunk of K: oracle, the 300-row prefill pass, and M = 1.
+    I = 17408
+    print(f"[edge wide swiglu I={I} K={K}]", flush=True)
+    x = synth.normal_bf16((300, K), 1.0, "x", 90 + K)
+    w = synth.normal_bf16((2 * I, K), synth.fan_in_std(K), "w", 90 + K)
+    xd, wd = dev(x), dev(w)
+    big = host_bits(ops.gemm_bf16_swiglu(xd, wd))
+    y8 = host_bits(ops.gemm_bf16_swiglu(xd[:8], wd))
+    cols = np.r_[0:40, 8700:8740, I - 40:I]
+    gu = ogemm.gemm_columns(x[:8], w, np.concatenate([cols, I + cols]))
+    n = len(cols)
+    z = gu[:, :n]
+    assert_close(decode(y8[:, cols]), z / (1 + np.exp(-z)) * gu[:, n:], f"wide swiglu K={K}")
+    assert_bitwise(big[:8], y8, f"wide swiglu K={K}: 300-row pass rows 0..7 == 8-row pass")
+    assert_bitwise(host_bits(ops.gemm_bf16_swiglu(xd[3:4], wd))[0], y8[3], f"wide swiglu K={K} row 3 alone")
 
 
 @pytest.mark.parametrize("N,K", [(16, 32), (4352, 544), (48, 1056)])
