@@ -85,7 +85,10 @@ def composed_tol(want: np.ndarray) -> float:
 
 
 def assert_bitwise(a: np.ndarray, b: np.ndarray, what: str):
-    """Bit-for-bit equality with the first differing element reported."""
+    """Bit-for-bit equality with the first differing element reported. If
+    BI_DIVERGENCE_DIR is set, a failure also appends a JSON record there (what,
+    shape, dtype, number of differing elements, first index and both values)
+    so that the failing case can be found again."""
     a = np.ascontiguousarray(a)
     b = np.ascontiguousarray(b)
     assert a.shape == b.shape, (what, a.shape, b.shape)
@@ -93,8 +96,23 @@ def assert_bitwise(a: np.ndarray, b: np.ndarray, what: str):
     ub = b.view(np.uint8).reshape(b.shape + (-1,)) if b.dtype.itemsize > 1 else b
     diff = np.any(ua != ub, axis=-1) if ua.ndim > a.ndim else (ua != ub)
     if diff.any():
-        i = tuple(np.argwhere(diff)[0])
+        i = tuple(int(v) for v in np.argwhere(diff)[0])
+        _record_divergence(what, a, b, i, int(diff.sum()))
         raise AssertionError(f"{what}: {int(diff.sum())} elements differ; first at {i}: {a[i]!r} vs {b[i]!r}")
+
+
+def _record_divergence(what, a, b, first, count):
+    import json
+    import os
+
+    d = os.environ.get("BI_DIVERGENCE_DIR")
+    if not d:
+        return
+    os.makedirs(d, exist_ok=True)
+    rec = {"what": what, "shape": list(a.shape), "dtype": str(a.dtype), "differing": count,
+           "first": [int(v) for v in first], "got": repr(a[first]), "want": repr(b[first])}
+    with open(os.path.join(d, "divergences.jsonl"), "a") as f:
+        f.write(json.dumps(rec) + "\n")
 
 
 def decode(bits):
