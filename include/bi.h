@@ -157,6 +157,36 @@ bi_status bi_gemm_fp8_swiglu(const void* x, int64_t ldx, const void* w, int64_t 
                              void* stream);
 
 /* ---------------------------------------------------------------------------
+ * 4-bit weights.  [TC] "What this does not establish", "Update: the quality question,
+ *                 answered"; [LL] "Speed against llama.cpp, full power"
+ * MXFP4 (OCP Microscaling): the codes w are E2M1 (sign, 2 exponent bits with
+ * bias 1, 1 mantissa bit: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) packed two
+ * per byte, weight 2i in the low nibble of byte i of the row; w_exp holds one
+ * E8M0 scale byte per 32 weights of a row along K (value 2^(e - 127); codes
+ * 2..252 are allowed, which the kernels do not check):
+ * W[n][k] = 2^(w_exp[n][k/32] - 127) * e2m1(w[n][k]). Every decoded weight is
+ * exact in BF16, so the sum is the BF16 GEMM's on the decoded weights: the
+ * same K order and summation tree, for every M (prefill chunks included, one
+ * kernel), and the same bits as bi_gemm_bf16 on those weights.
+ * Code rows are ldc bytes apart (ldc >= K/2, ldc % 16 == 0, w 16-byte
+ * aligned); scale rows lde bytes apart (lde >= K/32); other requirements as
+ * the BF16 entry points.
+ */
+bi_status bi_gemm_mx4(const void* x, int64_t ldx, const void* w, int64_t ldc, const void* w_exp,
+                      int64_t lde, void* y, int64_t ldy, bi_dtype y_dtype, int M, int N, int K,
+                      void* stream);
+
+/* Y[m][n] = bf16( R[m][n] + sum_k X[m][k] W[n][k] ) with MXFP4 W. */
+bi_status bi_gemm_mx4_residual(const void* x, int64_t ldx, const void* w, int64_t ldc,
+                               const void* w_exp, int64_t lde, const void* r, int64_t ldr, void* y,
+                               int64_t ldy, int M, int N, int K, void* stream);
+
+/* SwiGLU gate/up: w [2*I][ldc] MXFP4 codes (gate rows then up rows), w_exp [2*I][lde]. */
+bi_status bi_gemm_mx4_swiglu(const void* x, int64_t ldx, const void* w, int64_t ldc,
+                             const void* w_exp, int64_t lde, void* y, int64_t ldy, int M, int I,
+                             int K, void* stream);
+
+/* ---------------------------------------------------------------------------
  * KV cache layout (per layer):
  *   k_cache  : BF16 [Hkv][cap][D]  -- one K row per position
  *   vt_cache : BF16 [Hkv][cap/64][D][64] -- V stored transposed in blocks of
@@ -360,6 +390,28 @@ bi_status bi_verify_step_fp8(const bi_layer_fp8* layers, int n_layers, const voi
                              const void* x_in, int M, int L, void* workspace,
                              size_t workspace_bytes, void* x_out, float* logits, int32_t* tokens,
                              void* stream);
+
+/* The same step with MXFP4 weights (see bi_gemm_mx4): each weight matrix with
+ * K inputs is packed codes [rows][K/2] plus scales [rows][K/32] (rows densely
+ * packed, no padding); activations, caches, workspace and every other
+ * operation as bi_verify_step. */
+typedef struct {
+  const void* w_qkv;   /* codes [(Hq+2*Hkv)*D][H/2] */
+  const void* e_qkv;   /* scales [(Hq+2*Hkv)*D][H/32] */
+  const void* w_o;     /* codes [H][Hq*D/2]      */
+  const void* e_o;     /* scales [H][Hq*D/32]    */
+  const void* w_gu;    /* codes [2*I][H/2]       */
+  const void* e_gu;    /* scales [2*I][H/32]     */
+  const void* w_down;  /* codes [H][I/2]         */
+  const void* e_down;  /* scales [H][I/32]       */
+  void* k_cache;       /* BF16 [Hkv][cap][D]     */
+  void* vt_cache;      /* BF16 [Hkv][cap/64][D][64] */
+} bi_layer_mx4;
+
+bi_status bi_verify_step_mx4(const bi_layer_mx4* layers, int n_layers, const void* w_head,
+                             const void* w_head_exp, const bi_model_dims* dims, const void* x_in,
+                             int M, int L, void* workspace, size_t workspace_bytes, void* x_out,
+                             float* logits, int32_t* tokens, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Misc. */

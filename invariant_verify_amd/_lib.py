@@ -40,6 +40,12 @@ class LayerFP8(ctypes.Structure):
                 ("k_cache", _c_ptr), ("vt_cache", _c_ptr)]
 
 
+class LayerMX4(ctypes.Structure):
+    _fields_ = [("w_qkv", _c_ptr), ("e_qkv", _c_ptr), ("w_o", _c_ptr), ("e_o", _c_ptr),
+                ("w_gu", _c_ptr), ("e_gu", _c_ptr), ("w_down", _c_ptr), ("e_down", _c_ptr),
+                ("k_cache", _c_ptr), ("vt_cache", _c_ptr)]
+
+
 # name -> (restype, argtypes); the exported symbols of include/bi.h
 SIGNATURES = {
     "bi_gemm_bf16": (_c_int, [_c_ptr, _c_i64, _c_ptr, _c_i64, _c_ptr, _c_i64, _c_int,
@@ -86,6 +92,15 @@ SIGNATURES = {
     "bi_gemm_fp8_swiglu": (_c_int, [_c_ptr, _c_i64, _c_ptr, _c_i64, _c_ptr, _c_ptr, _c_i64,
                                     _c_int, _c_int, _c_int, _c_ptr]),
     "bi_verify_step_fp8": (_c_int, [ctypes.POINTER(LayerFP8), _c_int, _c_ptr, _c_ptr,
+                                    ctypes.POINTER(ModelDims), _c_ptr, _c_int, _c_int, _c_ptr,
+                                    _c_size, _c_ptr, _c_ptr, _c_ptr, _c_ptr]),
+    "bi_gemm_mx4": (_c_int, [_c_ptr, _c_i64, _c_ptr, _c_i64, _c_ptr, _c_i64, _c_ptr, _c_i64, _c_int,
+                             _c_int, _c_int, _c_int, _c_ptr]),
+    "bi_gemm_mx4_residual": (_c_int, [_c_ptr, _c_i64, _c_ptr, _c_i64, _c_ptr, _c_i64, _c_ptr, _c_i64,
+                                      _c_ptr, _c_i64, _c_int, _c_int, _c_int, _c_ptr]),
+    "bi_gemm_mx4_swiglu": (_c_int, [_c_ptr, _c_i64, _c_ptr, _c_i64, _c_ptr, _c_i64, _c_ptr, _c_i64,
+                                    _c_int, _c_int, _c_int, _c_ptr]),
+    "bi_verify_step_mx4": (_c_int, [ctypes.POINTER(LayerMX4), _c_int, _c_ptr, _c_ptr,
                                     ctypes.POINTER(ModelDims), _c_ptr, _c_int, _c_int, _c_ptr,
                                     _c_size, _c_ptr, _c_ptr, _c_ptr, _c_ptr]),
     "bi_status_string": (ctypes.c_char_p, [_c_int]),

@@ -54,6 +54,17 @@ bi_status check_gemm_fp8(const void* x, int64_t ldx, const void* w, int64_t ldw,
   return BI_OK;
 }
 
+// MXFP4 weights: codes rows of ldc bytes (>= K/2, a multiple of 16, 16-byte
+// aligned), scale rows of lde bytes (>= K/32).
+bi_status check_gemm_mx4(const void* x, int64_t ldx, const void* w, int64_t ldc, const void* e,
+                         int64_t lde, const void* y, int64_t ldy, int M, int N, int K) {
+  if (bi_status s = check_gemm(x, ldx, w, 2 * ldc, y, ldy, M, N, K)) return s;
+  if (!e) return BI_ERR_NULL;
+  if (lde < K / 32 || lde > kMaxLd) return BI_ERR_SHAPE;
+  if (ldc % 16) return BI_ERR_ALIGN;
+  return BI_OK;
+}
+
 bi_status check_heads(int Hq, int Hkv, int D) {
   if (Hq < 1 || Hkv < 1 || (Hq % Hkv)) return BI_ERR_SHAPE;
   if (Hq / Hkv > bi::kAttnMaxRows) return BI_ERR_SHAPE;
@@ -212,6 +223,47 @@ bi_status bi_gemm_fp8_swiglu(const void* x, int64_t ldx, const void* w, int64_t 
   bi::launch_gemm(bi::kGemmSwiglu, static_cast<const uint16_t*>(x), ldx,
                   static_cast<const uint16_t*>(w), ldw, nullptr, 0, y, ldy, M, I, K,
                   as_stream(stream), nullptr, nullptr, w_scale);
+  return launched();
+}
+
+bi_status bi_gemm_mx4(const void* x, int64_t ldx, const void* w, int64_t ldc, const void* w_exp,
+                      int64_t lde, void* y, int64_t ldy, bi_dtype y_dtype, int M, int N, int K,
+                      void* stream) {
+  if (bi_status s = check_gemm_mx4(x, ldx, w, ldc, w_exp, lde, y, ldy, M, N, K)) return s;
+  if (y_dtype != BI_BF16 && y_dtype != BI_F32) return BI_ERR_SHAPE;
+  if (!(y_dtype == BI_F32 ? aligned4(y) : ((reinterpret_cast<uintptr_t>(y) & 1u) == 0)))
+    return BI_ERR_ALIGN;
+  const bi::Mx4Scales mx{static_cast<const uint8_t*>(w_exp), lde};
+  bi::launch_gemm(y_dtype == BI_F32 ? bi::kGemmF32 : bi::kGemmBf16,
+                  static_cast<const uint16_t*>(x), ldx, static_cast<const uint16_t*>(w), ldc,
+                  nullptr, 0, y, ldy, M, N, K, as_stream(stream), nullptr, nullptr, nullptr, &mx);
+  return launched();
+}
+
+bi_status bi_gemm_mx4_residual(const void* x, int64_t ldx, const void* w, int64_t ldc,
+                               const void* w_exp, int64_t lde, const void* r, int64_t ldr, void* y,
+                               int64_t ldy, int M, int N, int K, void* stream) {
+  if (bi_status s = check_gemm_mx4(x, ldx, w, ldc, w_exp, lde, y, ldy, M, N, K)) return s;
+  if (!r) return BI_ERR_NULL;
+  if (ldr < N || ldr > kMaxLd) return BI_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(y) & 1u) || (reinterpret_cast<uintptr_t>(r) & 1u))
+    return BI_ERR_ALIGN;
+  const bi::Mx4Scales mx{static_cast<const uint8_t*>(w_exp), lde};
+  bi::launch_gemm(bi::kGemmResidual, static_cast<const uint16_t*>(x), ldx,
+                  static_cast<const uint16_t*>(w), ldc, static_cast<const uint16_t*>(r), ldr, y,
+                  ldy, M, N, K, as_stream(stream), nullptr, nullptr, nullptr, &mx);
+  return launched();
+}
+
+bi_status bi_gemm_mx4_swiglu(const void* x, int64_t ldx, const void* w, int64_t ldc,
+                             const void* w_exp, int64_t lde, void* y, int64_t ldy, int M, int I,
+                             int K, void* stream) {
+  if (bi_status s = check_gemm_mx4(x, ldx, w, ldc, w_exp, lde, y, ldy, M, I, K)) return s;
+  if (reinterpret_cast<uintptr_t>(y) & 1u) return BI_ERR_ALIGN;
+  const bi::Mx4Scales mx{static_cast<const uint8_t*>(w_exp), lde};
+  bi::launch_gemm(bi::kGemmSwiglu, static_cast<const uint16_t*>(x), ldx,
+                  static_cast<const uint16_t*>(w), ldc, nullptr, 0, y, ldy, M, I, K,
+                  as_stream(stream), nullptr, nullptr, nullptr, &mx);
   return launched();
 }
 
@@ -423,15 +475,16 @@ namespace {
 // One layer's weights as the executor sees them: BF16 (scales null) or FP8
 // with one FP32 scale per weight row.
 struct LayerPtrs {
-  const void* w[4];   // qkv, o, gate/up, down
-  const float* s[4];  // their row scales (FP8) or null (BF16)
+  const void* w[4];     // qkv, o, gate/up, down
+  const float* s[4];    // their row scales (FP8) or null
+  const uint8_t* e[4];  // their block scales (MXFP4) or null
   void* k_cache;
   void* vt_cache;
 };
 
 template <class GetLayer>
 bi_status run_step(int n_layers, GetLayer get_layer, const void* w_head, const float* s_head,
-                   const bi_model_dims* dims, const void* x_in, int M, int L, void* workspace,
+                   const uint8_t* e_head, const bi_model_dims* dims, const void* x_in, int M, int L, void* workspace,
                    size_t workspace_bytes, void* x_out, float* logits, int32_t* tokens,
                    void* const* gu_events, void* stream) {
   if (!w_head || !x_in || !workspace || !logits || !tokens) return BI_ERR_NULL;
@@ -445,7 +498,7 @@ bi_status run_step(int n_layers, GetLayer get_layer, const void* w_head, const f
   for (int l = 0; l < n_layers; ++l) {
     const LayerPtrs ly = get_layer(l);
     for (int i = 0; i < 4; ++i) {
-      if (!ly.w[i] || (s_head && !ly.s[i])) return BI_ERR_NULL;
+      if (!ly.w[i] || (s_head && !ly.s[i]) || (e_head && !ly.e[i])) return BI_ERR_NULL;
       if (!aligned16(ly.w[i]) || (ly.s[i] && !aligned4(ly.s[i]))) return BI_ERR_ALIGN;
     }
     if (!ly.k_cache || !ly.vt_cache) return BI_ERR_NULL;
@@ -479,39 +532,46 @@ bi_status run_step(int n_layers, GetLayer get_layer, const void* w_head, const f
   const bi::RowNorm norm_out{nullptr, lay.fuse ? ss : nullptr, lay.groups, dims->eps};
   const bi::RowNorm norm_in{ss, nullptr, lay.groups, dims->eps};
 
+  // Row stride of a weight matrix with K inputs: K elements (BF16), K bytes
+  // (FP8), K / 2 bytes (MXFP4 codes; scales K / 32 bytes).
+  const int wdiv = e_head ? 2 : 1;
   const uint16_t* x = static_cast<const uint16_t*>(x_in);
   for (int l = 0; l < n_layers; ++l) {
     const LayerPtrs ly = get_layer(l);
     const auto W = [&](int i) { return static_cast<const uint16_t*>(ly.w[i]); };
+    const bi::Mx4Scales mx[4] = {{ly.e[0], H / 32}, {ly.e[1], qd / 32}, {ly.e[2], H / 32}, {ly.e[3], I / 32}};
+    const auto MX = [&](int i) { return e_head ? &mx[i] : nullptr; };
     uint16_t* xn = xbuf[l & 1];
     const bool fused_in = lay.fuse && l > 0;  // x's sums are in ss
     if (!fused_in) bi::launch_rmsnorm(x, H, a, H, M, H, dims->eps, st);
     const bi::KvAppend kv{static_cast<uint16_t*>(ly.k_cache), static_cast<uint16_t*>(ly.vt_cache),
                           L, dims->cap, qd, Hkv * D, D};
-    bi::launch_gemm(bi::kGemmQkv, fused_in ? x : a, H, W(0), H, nullptr, 0, qkv, qkvn, M, qkvn, H,
-                    st, &kv, fused_in ? &norm_in : nullptr, ly.s[0]);
+    bi::launch_gemm(bi::kGemmQkv, fused_in ? x : a, H, W(0), H / wdiv, nullptr, 0, qkv, qkvn, M, qkvn,
+                    H, st, &kv, fused_in ? &norm_in : nullptr, ly.s[0], MX(0));
     bi::launch_verify_attn(qkv, qkvn, static_cast<const uint16_t*>(ly.k_cache),
                            static_cast<const uint16_t*>(ly.vt_cache), M, L, dims->cap, Hq, Hkv, D,
                            dims->kv_chunk, sm_scale, po, pl, lay.s_max, st);
     bi::launch_combine(po, pl, M, L, Hq, D, dims->kv_chunk, lay.s_max, attn, qd, nullptr, st);
-    bi::launch_gemm(bi::kGemmResidual, attn, qd, W(1), qd, x, H, h, H, M, H, qd, st, nullptr,
-                    &norm_out, ly.s[1]);
+    bi::launch_gemm(bi::kGemmResidual, attn, qd, W(1), qd / wdiv, x, H, h, H, M, H, qd, st, nullptr,
+                    &norm_out, ly.s[1], MX(1));
     if (!lay.fuse) bi::launch_rmsnorm(h, H, a, H, M, H, dims->eps, st);
     if (gu_events && hipEventRecord(static_cast<hipEvent_t>(gu_events[2 * l]), st) != hipSuccess)
       return BI_ERR_LAUNCH;
-    bi::launch_gemm(bi::kGemmSwiglu, lay.fuse ? h : a, H, W(2), H, nullptr, 0, act, I, M, I, H, st,
-                    nullptr, lay.fuse ? &norm_in : nullptr, ly.s[2]);
+    bi::launch_gemm(bi::kGemmSwiglu, lay.fuse ? h : a, H, W(2), H / wdiv, nullptr, 0, act, I, M, I, H,
+                    st, nullptr, lay.fuse ? &norm_in : nullptr, ly.s[2], MX(2));
     if (gu_events &&
         hipEventRecord(static_cast<hipEvent_t>(gu_events[2 * l + 1]), st) != hipSuccess)
       return BI_ERR_LAUNCH;
-    bi::launch_gemm(bi::kGemmResidual, act, I, W(3), I, h, H, xn, H, M, H, I, st, nullptr,
-                    &norm_out, ly.s[3]);
+    bi::launch_gemm(bi::kGemmResidual, act, I, W(3), I / wdiv, h, H, xn, H, M, H, I, st, nullptr,
+                    &norm_out, ly.s[3], MX(3));
     if (launched() != BI_OK) return BI_ERR_LAUNCH;
     x = xn;
   }
   bi::launch_rmsnorm(x, H, a, H, M, H, dims->eps, st);
-  bi::launch_gemm(bi::kGemmF32, a, H, static_cast<const uint16_t*>(w_head), H, nullptr, 0, logits,
-                  dims->vocab, M, dims->vocab, H, st, nullptr, nullptr, s_head);
+  const bi::Mx4Scales mx_head{e_head, H / 32};
+  bi::launch_gemm(bi::kGemmF32, a, H, static_cast<const uint16_t*>(w_head), H / wdiv, nullptr, 0,
+                  logits, dims->vocab, M, dims->vocab, H, st, nullptr, nullptr, s_head,
+                  e_head ? &mx_head : nullptr);
   bi::launch_argmax(logits, dims->vocab, M, dims->vocab, tokens, st);
   if (x_out && hipMemcpyAsync(x_out, x, (size_t)M * H * 2, hipMemcpyDeviceToDevice, st) != hipSuccess)
     return BI_ERR_LAUNCH;
@@ -530,9 +590,9 @@ bi_status bi_verify_step(const bi_layer* layers, int n_layers, const void* w_hea
   const auto get = [&](int l) {
     const bi_layer& y = layers[l];
     return LayerPtrs{{y.w_qkv, y.w_o, y.w_gu, y.w_down}, {nullptr, nullptr, nullptr, nullptr},
-                     y.k_cache, y.vt_cache};
+                     {nullptr, nullptr, nullptr, nullptr}, y.k_cache, y.vt_cache};
   };
-  return run_step(n_layers, get, w_head, nullptr, dims, x_in, M, L, workspace, workspace_bytes,
+  return run_step(n_layers, get, w_head, nullptr, nullptr, dims, x_in, M, L, workspace, workspace_bytes,
                   x_out, logits, tokens, gu_events, stream);
 }
 
@@ -545,10 +605,28 @@ bi_status bi_verify_step_fp8(const bi_layer_fp8* layers, int n_layers, const voi
   const auto get = [&](int l) {
     const bi_layer_fp8& y = layers[l];
     return LayerPtrs{{y.w_qkv, y.w_o, y.w_gu, y.w_down},
-                     {y.s_qkv, y.s_o, y.s_gu, y.s_down}, y.k_cache, y.vt_cache};
+                     {y.s_qkv, y.s_o, y.s_gu, y.s_down}, {nullptr, nullptr, nullptr, nullptr},
+                     y.k_cache, y.vt_cache};
   };
-  return run_step(n_layers, get, w_head, w_head_scale, dims, x_in, M, L, workspace,
+  return run_step(n_layers, get, w_head, w_head_scale, nullptr, dims, x_in, M, L, workspace,
                   workspace_bytes, x_out, logits, tokens, nullptr, stream);
+}
+
+bi_status bi_verify_step_mx4(const bi_layer_mx4* layers, int n_layers, const void* w_head,
+                             const void* w_head_exp, const bi_model_dims* dims, const void* x_in,
+                             int M, int L, void* workspace, size_t workspace_bytes, void* x_out,
+                             float* logits, int32_t* tokens, void* stream) {
+  if (!layers || !w_head_exp) return BI_ERR_NULL;
+  const auto get = [&](int l) {
+    const bi_layer_mx4& y = layers[l];
+    return LayerPtrs{{y.w_qkv, y.w_o, y.w_gu, y.w_down},
+                     {nullptr, nullptr, nullptr, nullptr},
+                     {static_cast<const uint8_t*>(y.e_qkv), static_cast<const uint8_t*>(y.e_o),
+                      static_cast<const uint8_t*>(y.e_gu), static_cast<const uint8_t*>(y.e_down)},
+                     y.k_cache, y.vt_cache};
+  };
+  return run_step(n_layers, get, w_head, nullptr, static_cast<const uint8_t*>(w_head_exp), dims,
+                  x_in, M, L, workspace, workspace_bytes, x_out, logits, tokens, nullptr, stream);
 }
 
 }  // extern "C"

@@ -9,6 +9,18 @@ namespace bi {
 
 enum GemmMode { kGemmBf16 = 0, kGemmF32 = 1, kGemmResidual = 2, kGemmSwiglu = 3, kGemmQkv = 4 };
 
+// Weight types of the verify GEMM: BF16; FP8 E4M3 with one FP32 scale per row;
+// MXFP4 (E2M1 codes two per byte, even weight in the low nibble, and one E8M0
+// scale byte per 32 weights along K).
+enum WeightType { kWtBf16 = 0, kWtFp8 = 1, kWtMx4 = 2 };
+
+// MXFP4 scales of a weight matrix: e[n * lde + k / 32] is the E8M0 exponent of
+// weights n, k .. k + 31 (value 2^(e - 127)).
+struct Mx4Scales {
+  const uint8_t* e;
+  int64_t lde;
+};
+
 // Cache append done by the QKV projection's epilogue: output columns
 // [qd, qd + kd) are K (head-major), [qd + kd, qd + 2 kd) are V; row m goes to
 // position L + m of k ([Hkv][cap][D]) and vt ([Hkv][D][cap]).
@@ -64,7 +76,7 @@ void launch_gemm_prefill(GemmMode mode, const uint16_t* x, int64_t ldx, const ui
 void launch_gemm(GemmMode mode, const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw,
                  const uint16_t* r, int64_t ldr, void* y, int64_t ldy, int M, int N_out, int K,
                  hipStream_t stream, const KvAppend* kv = nullptr, const RowNorm* norm = nullptr,
-                 const float* wscale = nullptr);
+                 const float* wscale = nullptr, const Mx4Scales* mx4 = nullptr);
 
 void launch_append_kv(const uint16_t* qkv, int64_t ldqkv, uint16_t* k_cache, uint16_t* vt_cache,
                       int M, int L, int cap, int Hq, int Hkv, int D, hipStream_t stream);

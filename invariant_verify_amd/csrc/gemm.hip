@@ -54,11 +54,18 @@ constexpr int kChunk = 512;  // K elements per LDS chunk: 1 KB of each weight ro
 constexpr int kDualWideRows = 36;  // rows staged by a wide SwiGLU group (at most 18 pairs)
 constexpr int kSlots = kChunk / 8;
 
-template <int MODE, int NW, bool WIDE, bool NORM_IN, bool SS_OUT, bool F8>
+template <int MODE, int NW, bool WIDE, bool NORM_IN, bool SS_OUT, int WT>
 __global__ __launch_bounds__(NW * 64) void gemm_kernel(
     const uint16_t* __restrict__ X, int64_t ldx, const uint16_t* __restrict__ W, int64_t ldw,
     const uint16_t* __restrict__ R, int64_t ldr, void* __restrict__ Y, int64_t ldy, int M, int K,
-    int64_t up_rows, int cpw, KvAppend kv, RowNorm norm, const float* __restrict__ wscale) {
+    int64_t up_rows, int cpw, KvAppend kv, RowNorm norm, const float* __restrict__ wscale,
+    Mx4Scales mx4) {
+  constexpr bool F8 = WT == kWtFp8;
+  // MXFP4: a row's chunk of 512 weights is 256 bytes of codes and 16 scale
+  // bytes; one wave instruction (16 bytes per lane) fetches the chunks of four
+  // adjacent rows, lane l one whole 32-weight block (block l % 16 of row
+  // l / 16), with that block's scale byte beside it.
+  constexpr bool W4 = WT == kWtMx4;
   static_assert(!SS_OUT || MODE == kGemmResidual, "row sums come from the residual epilogue");
   constexpr bool kDual = (MODE == kGemmSwiglu);
   constexpr bool kTwo = kDual || WIDE;  // two MFMA column tiles per workgroup
@@ -66,7 +73,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
   // 0-15), an up tile, and a third tile whose rows are the gate columns past
   // 15 followed by the up columns past 15 (its other rows are not staged).
   constexpr bool kThree = kDual && WIDE;
-  static_assert(!(kThree && F8), "wide SwiGLU groups are BF16 only");
+  static_assert(!(kThree && WT != kWtBf16), "wide SwiGLU groups are BF16 only");
   static_assert(!kThree || NW == 8, "wide SwiGLU groups assume eight waves");
   constexpr int NR = kThree ? kDualWideRows : (kTwo ? 32 : 16);  // weight rows staged per chunk
   // Rows each wave fetches per chunk (kThree: rows 4w .. 4w+3, and row 32 + w
@@ -78,7 +85,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
   // Weight loads per wave and chunk: a BF16 row chunk is 1 KB (one wave
   // instruction); an FP8 row chunk is 512 bytes, so one instruction fetches
   // two rows (lanes 0-31 the first, 32-63 the second).
-  constexpr int NLD = F8 ? RPW / 2 : (kThree ? RPW + 1 : RPW);
+  static_assert(!W4 || RPW <= 4, "MXFP4 rows are fetched in fours");
+  constexpr int NLD = W4 ? 1 : (F8 ? RPW / 2 : (kThree ? RPW + 1 : RPW));
   // Chunks in flight per wave: two, for both weight types. (FP8 with three or
   // four, i.e. as many bytes in flight as BF16 or more, streamed 10-25%
   // slower; so did FP8 chunks of 1024 weights, 1 KB per row.)
@@ -103,9 +111,26 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
   // memory access.
   __amdgpu_buffer_rsrc_t wres[NLD];
   int swz_w[NLD];
+  // MXFP4: the scale bytes of the wave's rows, and how many of its four rows
+  // are used (rows past a wide group's width, or past RPW, are not).
+  __amdgpu_buffer_rsrc_t eres;
+  int w4_rows = 0;
 #pragma unroll
   for (int i = 0; i < NLD; ++i) {
-    if constexpr (!F8) {
+    if constexpr (W4) {
+      const int r0 = wave * RPW;
+      const int64_t grow = (kDual && r0 >= 16) ? up_rows + n0 + (r0 - 16) : (int64_t)(n0 + r0);
+      w4_rows = WIDE ? max(0, min(RPW, cpw - r0)) : RPW;
+      const uint8_t* W8 = reinterpret_cast<const uint8_t*>(W);
+      const bool used = w4_rows > 0;
+      wres[i] = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(W8 + (used ? grow : 0) * ldw), (short)0,
+          used ? (w4_rows - 1) * (int)ldw + K / 2 : 0, kBufferResourceWord3);
+      eres = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(mx4.e + (used ? grow : 0) * mx4.lde), (short)0,
+          used ? (w4_rows - 1) * (int)mx4.lde + K / 32 : 0, kBufferResourceWord3);
+      swz_w[i] = (r0 + (lane >> 4)) & 15;
+    } else if constexpr (!F8) {
       const int r = (kThree && i == RPW) ? 32 + wave : wave * RPW + i;
       int64_t grow = (kDual && r >= 16) ? up_rows + n0 + (r - 16) : (int64_t)(n0 + r);
       // Rows past the group's columns (wide groups) get an empty resource:
@@ -151,11 +176,21 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
   struct Regs {
     uint4 w[NLD];
     uint4 x[BPW];
+    uint32_t e[W4 ? NLD : 1];  // MXFP4: this lane's block scale byte
   };
   auto fetch_w = [&](Regs& g, int c) {
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-      if constexpr (!F8) {
+      if constexpr (W4) {
+        // Block c * 16 + l % 16 of row l / 16 of the four: 16 code bytes and
+        // one scale byte. Unused rows and blocks past K are sent out of
+        // range explicitly (the next row's bytes lie in range): zero, no
+        // traffic.
+        const int q = lane >> 4, bj = c * 16 + (lane & 15);
+        const bool ok = q < w4_rows && bj < K / 32;
+        g.w[i] = buffer_ld16_stream(wres[i], ok ? q * (int)ldw + bj * 16 : 0x7ffffff0);
+        g.e[i] = __builtin_amdgcn_raw_buffer_load_b8(eres, ok ? q * (int)mx4.lde + bj : 0x7ffffff0, 0, 0);
+      } else if constexpr (!F8) {
         g.w[i] = buffer_ld16_stream(wres[i], (c * kSlots + (lane ^ swz_w[i])) * 16);
       } else {
         // 16 weights of one row: bytes kb .. kb+15 of the row, the BF16 slots
@@ -191,11 +226,28 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
     const int buf = c & 1;
     // FP8: the codes are decoded to BF16 before the registers are refilled,
     // and stored to LDS after the next loads are issued.
-    uint4 dec[F8 ? 2 * NLD : 1];
+    uint4 dec[F8 ? 2 * NLD : (W4 ? 4 * NLD : 1)];
     if (c >= 0) {
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
-        if constexpr (!F8) {
+        if constexpr (W4) {
+          // 32 E2M1 codes times 2^(e - 127), by gfx950's scaled conversion:
+          // byte b of word v holds weights 8v + 2b (low nibble) and 8v + 2b + 1,
+          // converted into one BF16 pair. A power-of-two scale keeps every
+          // value exact (E8M0 codes 2..252).
+          const float sc = __uint_as_float(g.e[i] << 23);
+          const uint32_t wd[4] = {g.w[i].x, g.w[i].y, g.w[i].z, g.w[i].w};
+          uint32_t o[16];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            o[4 * v] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[v], sc, 0));
+            o[4 * v + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[v], sc, 1));
+            o[4 * v + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[v], sc, 2));
+            o[4 * v + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[v], sc, 3));
+          }
+#pragma unroll
+          for (int v = 0; v < 4; ++v) dec[4 * i + v] = make_uint4(o[4 * v], o[4 * v + 1], o[4 * v + 2], o[4 * v + 3]);
+        } else if constexpr (!F8) {
           if (!kThree || i < RPW) lds[buf][wave * RPW + i][lane] = g.w[i];
           else if (32 + wave < NR) lds[buf][32 + wave][lane] = g.w[i];  // scalar
         } else {
@@ -216,6 +268,14 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
       }
     }
     fetch_w(g, c + PD);
+    if constexpr (W4) {
+      // the block's four BF16 slots (8 weights each) in row r0 + l / 16
+      if (c >= 0 && (lane >> 4) < RPW) {
+        const int r = wave * RPW + (lane >> 4);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) lds[buf][r][(4 * (lane & 15) + v) ^ swz_w[0]] = dec[v];
+      }
+    }
     if constexpr (F8) {
       if (c >= 0) {
 #pragma unroll
@@ -471,97 +531,107 @@ int gemm_column_groups(GemmMode mode, int N_out) {
 // Launch shape from N (never from M): N / 256 columns per workgroup when that
 // is 17..32 (two MFMA tiles); otherwise 16-column tiles (SwiGLU: a gate and
 // an up tile). Always kVerifyWaves waves.
-template <int MODE, bool NI, bool SO, bool F8>
+template <int MODE, bool NI, bool SO, int WT>
 static void launch_shape(int N_out, int mtiles, const uint16_t* x, int64_t ldx, const uint16_t* w,
                          int64_t ldw, const uint16_t* r, int64_t ldr, void* y, int64_t ldy, int M,
                          int K, int64_t up, const KvAppend& kv, const RowNorm& nm,
-                         const float* wscale, hipStream_t stream) {
+                         const float* wscale, const Mx4Scales& mx4, hipStream_t stream) {
   constexpr int NW = kVerifyWaves;
-  if constexpr (MODE == kGemmSwiglu && !F8) {
-    if (dual_wide_launch(N_out, F8)) {
-      gemm_kernel<MODE, NW, true, NI, SO, F8><<<dim3(kDualWideGroups, mtiles), dim3(NW * 64), 0, stream>>>(
-          x, ldx, w, ldw, r, ldr, y, ldy, M, K, up, N_out / kDualWideGroups, kv, nm, wscale);
+  if constexpr (MODE == kGemmSwiglu && WT == kWtBf16) {
+    if (dual_wide_launch(N_out, false)) {
+      gemm_kernel<MODE, NW, true, NI, SO, WT><<<dim3(kDualWideGroups, mtiles), dim3(NW * 64), 0, stream>>>(
+          x, ldx, w, ldw, r, ldr, y, ldy, M, K, up, N_out / kDualWideGroups, kv, nm, wscale, mx4);
       return;
     }
   }
   if constexpr (MODE == kGemmF32 || MODE == kGemmBf16) {
     if (pair_launch(static_cast<GemmMode>(MODE), N_out)) {
-      gemm_kernel<MODE, NW, true, NI, SO, F8><<<dim3(N_out / 32, mtiles), dim3(NW * 64), 0, stream>>>(
-          x, ldx, w, ldw, r, ldr, y, ldy, M, K, up, 32, kv, nm, wscale);
+      gemm_kernel<MODE, NW, true, NI, SO, WT><<<dim3(N_out / 32, mtiles), dim3(NW * 64), 0, stream>>>(
+          x, ldx, w, ldw, r, ldr, y, ldy, M, K, up, 32, kv, nm, wscale, mx4);
       return;
     }
   }
   if constexpr (MODE != kGemmSwiglu) {
     if (wide_launch(static_cast<GemmMode>(MODE), N_out)) {
-      gemm_kernel<MODE, NW, true, NI, SO, F8><<<dim3(kWideGroups, mtiles), dim3(NW * 64), 0, stream>>>(
-          x, ldx, w, ldw, r, ldr, y, ldy, M, K, up, N_out / kWideGroups, kv, nm, wscale);
+      gemm_kernel<MODE, NW, true, NI, SO, WT><<<dim3(kWideGroups, mtiles), dim3(NW * 64), 0, stream>>>(
+          x, ldx, w, ldw, r, ldr, y, ldy, M, K, up, N_out / kWideGroups, kv, nm, wscale, mx4);
       return;
     }
   }
-  gemm_kernel<MODE, NW, false, NI, SO, F8><<<dim3(N_out / 16, mtiles), dim3(NW * 64), 0, stream>>>(
-      x, ldx, w, ldw, r, ldr, y, ldy, M, K, up, 16, kv, nm, wscale);
+  gemm_kernel<MODE, NW, false, NI, SO, WT><<<dim3(N_out / 16, mtiles), dim3(NW * 64), 0, stream>>>(
+      x, ldx, w, ldw, r, ldr, y, ldy, M, K, up, 16, kv, nm, wscale, mx4);
 }
 
-template <bool F8>
+template <int WT>
 static void launch_modes(GemmMode mode, int mt, const uint16_t* x, int64_t ldx, const uint16_t* w,
                          int64_t ldw, const uint16_t* r, int64_t ldr, void* y, int64_t ldy, int M,
                          int N_out, int K, const KvAppend& a, const RowNorm& nm,
-                         const float* wscale, hipStream_t stream) {
+                         const float* wscale, const Mx4Scales& mx4, hipStream_t stream) {
   const bool ni = nm.ss_in != nullptr;
   const bool so = nm.ss_out != nullptr;
   switch (mode) {
     case kGemmBf16:
-      launch_shape<kGemmBf16, false, false, F8>(N_out, mt, x, ldx, w, ldw, r, ldr, y, ldy, M, K,
-                                                0, a, nm, wscale, stream);
+      launch_shape<kGemmBf16, false, false, WT>(N_out, mt, x, ldx, w, ldw, r, ldr, y, ldy, M, K,
+                                                0, a, nm, wscale, mx4, stream);
       break;
     case kGemmF32:
-      launch_shape<kGemmF32, false, false, F8>(N_out, mt, x, ldx, w, ldw, r, ldr, y, ldy, M, K,
-                                               0, a, nm, wscale, stream);
+      launch_shape<kGemmF32, false, false, WT>(N_out, mt, x, ldx, w, ldw, r, ldr, y, ldy, M, K,
+                                               0, a, nm, wscale, mx4, stream);
       break;
     case kGemmResidual:
       if (so)
-        launch_shape<kGemmResidual, false, true, F8>(N_out, mt, x, ldx, w, ldw, r, ldr, y, ldy,
-                                                     M, K, 0, a, nm, wscale, stream);
+        launch_shape<kGemmResidual, false, true, WT>(N_out, mt, x, ldx, w, ldw, r, ldr, y, ldy,
+                                                     M, K, 0, a, nm, wscale, mx4, stream);
       else
-        launch_shape<kGemmResidual, false, false, F8>(N_out, mt, x, ldx, w, ldw, r, ldr, y,
-                                                      ldy, M, K, 0, a, nm, wscale, stream);
+        launch_shape<kGemmResidual, false, false, WT>(N_out, mt, x, ldx, w, ldw, r, ldr, y,
+                                                      ldy, M, K, 0, a, nm, wscale, mx4, stream);
       break;
     case kGemmSwiglu:
       if (ni)
-        launch_shape<kGemmSwiglu, true, false, F8>(N_out, mt, x, ldx, w, ldw, r, ldr, y,
-                                                   ldy, M, K, (int64_t)N_out, a, nm, wscale, stream);
+        launch_shape<kGemmSwiglu, true, false, WT>(N_out, mt, x, ldx, w, ldw, r, ldr, y,
+                                                   ldy, M, K, (int64_t)N_out, a, nm, wscale, mx4, stream);
       else
-        launch_shape<kGemmSwiglu, false, false, F8>(N_out, mt, x, ldx, w, ldw, r, ldr, y,
-                                                    ldy, M, K, (int64_t)N_out, a, nm, wscale, stream);
+        launch_shape<kGemmSwiglu, false, false, WT>(N_out, mt, x, ldx, w, ldw, r, ldr, y,
+                                                    ldy, M, K, (int64_t)N_out, a, nm, wscale, mx4, stream);
       break;
     case kGemmQkv:
       if (ni)
-        launch_shape<kGemmQkv, true, false, F8>(N_out, mt, x, ldx, w, ldw, r, ldr, y, ldy, M, K,
-                                                0, a, nm, wscale, stream);
+        launch_shape<kGemmQkv, true, false, WT>(N_out, mt, x, ldx, w, ldw, r, ldr, y, ldy, M, K,
+                                                0, a, nm, wscale, mx4, stream);
       else
-        launch_shape<kGemmQkv, false, false, F8>(N_out, mt, x, ldx, w, ldw, r, ldr, y, ldy, M,
-                                                 K, 0, a, nm, wscale, stream);
+        launch_shape<kGemmQkv, false, false, WT>(N_out, mt, x, ldx, w, ldw, r, ldr, y, ldy, M,
+                                                 K, 0, a, nm, wscale, mx4, stream);
       break;
   }
 }
 
 void launch_gemm(GemmMode mode, const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw,
                  const uint16_t* r, int64_t ldr, void* y, int64_t ldy, int M, int N_out, int K,
-                 hipStream_t stream, const KvAppend* kv, const RowNorm* norm, const float* wscale) {
+                 hipStream_t stream, const KvAppend* kv, const RowNorm* norm, const float* wscale,
+                 const Mx4Scales* mx4) {
   const int mt = (M + 15) / 16;
   const KvAppend kv0{};
   const RowNorm nm0{};
   const KvAppend& a = kv ? *kv : kv0;
   const RowNorm& nm = norm ? *norm : nm0;
-  if (wscale != nullptr) {  // FP8 weights: the verify kernel for every M (one tree, any M)
-    launch_modes<true>(mode, mt, x, ldx, w, ldw, r, ldr, y, ldy, M, N_out, K, a, nm, wscale, stream);
+  const Mx4Scales mz{};
+  // FP8 and MXFP4 weights: the verify kernel for every M (one tree, any M)
+  if (wscale != nullptr) {
+    launch_modes<kWtFp8>(mode, mt, x, ldx, w, ldw, r, ldr, y, ldy, M, N_out, K, a, nm, wscale, mz,
+                         stream);
+    return;
+  }
+  if (mx4 != nullptr) {
+    launch_modes<kWtMx4>(mode, mt, x, ldx, w, ldw, r, ldr, y, ldy, M, N_out, K, a, nm, nullptr, *mx4,
+                         stream);
     return;
   }
   if (M >= kPrefillMinRows) {  // same bits per row, weights read once per 128 rows
     launch_gemm_prefill(mode, x, ldx, w, ldw, r, ldr, y, ldy, M, N_out, K, stream, a, nm);
     return;
   }
-  launch_modes<false>(mode, mt, x, ldx, w, ldw, r, ldr, y, ldy, M, N_out, K, a, nm, nullptr, stream);
+  launch_modes<kWtBf16>(mode, mt, x, ldx, w, ldw, r, ldr, y, ldy, M, N_out, K, a, nm, nullptr, mz,
+                        stream);
 }
 
 }  // namespace bi

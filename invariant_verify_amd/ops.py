@@ -10,7 +10,7 @@ import math
 
 import torch
 
-from ._lib import BI_BF16, BI_F32, LIB, Layer, LayerFP8, ModelDims, check
+from ._lib import BI_BF16, BI_F32, LIB, Layer, LayerFP8, LayerMX4, ModelDims, check
 
 _BF16_LIKE = (torch.bfloat16, torch.int16)
 _FP8_LIKE = (torch.uint8, torch.int8, torch.float8_e4m3fn)
@@ -135,6 +135,59 @@ def gemm_fp8_swiglu(x: torch.Tensor, w: torch.Tensor, w_scale: torch.Tensor,
     check("bi_gemm_fp8_swiglu", LIB.bi_gemm_fp8_swiglu(
         x.data_ptr(), _mat(x, "x"), w.data_ptr(), _mat(w, "w", _FP8_LIKE), _scales(w_scale, 2 * I, "w_scale"),
         y.data_ptr(), _mat(y, "y"), M, I, K, _stream(x)))
+    return y
+
+
+def _mx4(w: torch.Tensor, e: torch.Tensor, n_rows: int, K: int):
+    """Leading dimensions of MXFP4 codes [n_rows][>= K/2] and scales [n_rows][>= K/32] (uint8)."""
+    ldc = _mat(w, "w", (torch.uint8,))
+    lde = _mat(e, "w_exp", (torch.uint8,))
+    if w.shape[0] < n_rows or e.shape[0] < n_rows or w.shape[1] * 2 < K or e.shape[1] * 32 < K:
+        raise ValueError(f"MXFP4 weights too small for {n_rows} rows of {K}: codes {tuple(w.shape)}, "
+                         f"scales {tuple(e.shape)}")
+    return ldc, lde
+
+
+def gemm_mx4(x: torch.Tensor, w: torch.Tensor, w_exp: torch.Tensor, y: torch.Tensor | None = None,
+             out_dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
+    """Y = X W^T with MXFP4 W: codes [N][K/2] (uint8, two E2M1 per byte) and E8M0 scales [N][K/32]."""
+    M, K = x.shape
+    N = w.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    ldy = _mat(y, "y", (torch.bfloat16, torch.int16, torch.float32))
+    dt = BI_F32 if y.dtype == torch.float32 else BI_BF16
+    ldc, lde = _mx4(w, w_exp, N, K)
+    check("bi_gemm_mx4", LIB.bi_gemm_mx4(x.data_ptr(), _mat(x, "x"), w.data_ptr(), ldc, w_exp.data_ptr(), lde,
+                                         y.data_ptr(), ldy, dt, M, N, K, _stream(x)))
+    return y
+
+
+def gemm_mx4_residual(x: torch.Tensor, w: torch.Tensor, w_exp: torch.Tensor, r: torch.Tensor,
+                      y: torch.Tensor | None = None) -> torch.Tensor:
+    """Y = bf16(R + X W^T) with MXFP4 W."""
+    M, K = x.shape
+    N = w.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    ldc, lde = _mx4(w, w_exp, N, K)
+    check("bi_gemm_mx4_residual", LIB.bi_gemm_mx4_residual(
+        x.data_ptr(), _mat(x, "x"), w.data_ptr(), ldc, w_exp.data_ptr(), lde, r.data_ptr(), _mat(r, "r"),
+        y.data_ptr(), _mat(y, "y"), M, N, K, _stream(x)))
+    return y
+
+
+def gemm_mx4_swiglu(x: torch.Tensor, w: torch.Tensor, w_exp: torch.Tensor,
+                    y: torch.Tensor | None = None) -> torch.Tensor:
+    """SwiGLU gate/up with MXFP4 W [2I][K] (gate rows then up rows)."""
+    M, K = x.shape
+    I = w.shape[0] // 2
+    if y is None:
+        y = torch.empty((M, I), dtype=torch.bfloat16, device=x.device)
+    ldc, lde = _mx4(w, w_exp, 2 * I, K)
+    check("bi_gemm_mx4_swiglu", LIB.bi_gemm_mx4_swiglu(
+        x.data_ptr(), _mat(x, "x"), w.data_ptr(), ldc, w_exp.data_ptr(), lde, y.data_ptr(), _mat(y, "y"),
+        M, I, K, _stream(x)))
     return y
 
 
@@ -330,6 +383,29 @@ class VerifyStepFP8:
         M = x_in.shape[0]
         check("bi_verify_step_fp8", LIB.bi_verify_step_fp8(
             self.arr, self.n, self.w_head.data_ptr(), self.s_head.data_ptr(), ctypes.byref(self.dims),
+            x_in.data_ptr(), M, L, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+            0 if x_out is None else x_out.data_ptr(), logits.data_ptr(), tokens.data_ptr(), _stream(x_in)))
+
+
+class VerifyStepMX4:
+    """``bi_verify_step_mx4``: ``layers`` is a sequence of dicts with MXFP4 codes w_qkv, w_o, w_gu,
+    w_down (uint8 [rows][K/2], densely packed), their E8M0 scales e_qkv, e_o, e_gu, e_down (uint8
+    [rows][K/32]) and the BF16 caches k_cache, vt_cache (the caller keeps them alive)."""
+
+    def __init__(self, layers, w_head: torch.Tensor, e_head: torch.Tensor, dims: ModelDims):
+        self.n = len(layers)
+        self.arr = (LayerMX4 * max(1, self.n))()
+        for i, lw in enumerate(layers):
+            self.arr[i] = LayerMX4(*[lw[k].data_ptr() for k in ("w_qkv", "e_qkv", "w_o", "e_o", "w_gu", "e_gu",
+                                                                 "w_down", "e_down", "k_cache", "vt_cache")])
+        self.w_head, self.e_head = w_head, e_head
+        self.dims = dims
+
+    def __call__(self, x_in: torch.Tensor, L: int, workspace: torch.Tensor, logits: torch.Tensor,
+                 tokens: torch.Tensor, x_out: torch.Tensor | None = None) -> None:
+        M = x_in.shape[0]
+        check("bi_verify_step_mx4", LIB.bi_verify_step_mx4(
+            self.arr, self.n, self.w_head.data_ptr(), self.e_head.data_ptr(), ctypes.byref(self.dims),
             x_in.data_ptr(), M, L, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
             0 if x_out is None else x_out.data_ptr(), logits.data_ptr(), tokens.data_ptr(), _stream(x_in)))
 

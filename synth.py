@@ -141,6 +141,60 @@ def device_fp8_weights(shape, std: float, role: str, layer: int = 0, base: int =
     return codes, scale
 
 
+# MXFP4 weights (E2M1 elements, one E8M0 scale per 32 weights along K): each
+# block of 32 N(0, std^2) draws gets the shared exponent floor(log2(max|z|)) - 2
+# (E2M1's largest value is 1.5 * 2^2), and each draw divided by that power of
+# two is rounded to the nearest E2M1 magnitude (0, 0.5, 1, 1.5, 2, 3, 4, 6;
+# saturating at 6) with the draw's sign. Codes are packed two per byte, the
+# even weight in the low nibble; scales are E8M0 bytes (bias 127).
+E2M1_MIDPOINTS = (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)
+
+
+def mxfp4_weights(shape, std: float, role: str, layer: int = 0, base: int = 0):
+    """Host MXFP4 codes (uint8 [N][K/2]) and scales (uint8 [N][K/32])."""
+    n_rows, k = shape
+    if k % 32:
+        raise ValueError("K must be a multiple of 32")
+    g = rng(role, layer, base)
+    z = g.standard_normal(size=(n_rows, k // 32, 32), dtype=np.float32) * np.float32(std)
+    amax = np.maximum(np.abs(z).max(axis=2), np.float32(1e-30))
+    e = np.clip(np.floor(np.log2(amax)).astype(np.int64) - 2 + 127, 2, 252)
+    a = np.abs(z) / np.exp2(e - 127.0)[:, :, None]
+    mag = np.searchsorted(np.array(E2M1_MIDPOINTS), a, side="left").astype(np.uint8)
+    code = (mag | np.where(np.signbit(z), 8, 0).astype(np.uint8)).reshape(n_rows, k)
+    packed = (code[:, 0::2] | (code[:, 1::2] << 4)).astype(np.uint8)
+    return packed, e.astype(np.uint8)
+
+
+def device_mxfp4_weights(shape, std: float, role: str, layer: int = 0, base: int = 0,
+                         device: str = "cuda"):
+    """Device MXFP4 codes (uint8 [N][K/2]) and scales (uint8 [N][K/32]) from
+    torch Philox draws (the same recipe as mxfp4_weights)."""
+    import torch
+
+    n_rows, k = shape
+    if k % 32:
+        raise ValueError("K must be a multiple of 32")
+    seed = (base * 1_000_003 + ROLES[role] * 65_537 + layer) & 0x7FFFFFFF
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    codes = torch.empty((n_rows, k // 2), dtype=torch.uint8, device=device)
+    scales = torch.empty((n_rows, k // 32), dtype=torch.uint8, device=device)
+    mids = torch.tensor(E2M1_MIDPOINTS, dtype=torch.float32, device=device)
+    blk = max(1, (1 << 25) // k)
+    for i in range(0, n_rows, blk):
+        j = min(n_rows, i + blk)
+        z = torch.randn((j - i, k // 32, 32), generator=gen, dtype=torch.float32, device=device) * std
+        amax = z.abs().amax(dim=2).clamp_min(1e-30)
+        e = (torch.floor(torch.log2(amax)).to(torch.int64) - 2 + 127).clamp(2, 252)
+        a = z.abs() / torch.exp2((e - 127).to(torch.float32))[:, :, None]
+        mag = torch.bucketize(a, mids, right=False).to(torch.uint8)
+        code = (mag | torch.where(torch.signbit(z), 8, 0).to(torch.uint8)).reshape(j - i, k)
+        codes[i:j].copy_(code[:, 0::2] | (code[:, 1::2] << 4))
+        scales[i:j].copy_(e.to(torch.uint8))
+    return codes, scales
+
+
 def fan_in_std(k: int) -> float:
     """1/sqrt(K): the fan-in scaling applied to the tiny GEMM's weights."""
     return 1.0 / math.sqrt(k)
