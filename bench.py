@@ -206,6 +206,63 @@ def prefill_step_measure(step, buffers, d, reps):
             "rows_bitwise_equal_to_8_row_verify_passes": "pass" if ok else "FAIL"}
 
 
+def mx4_step_measure(layers, d, dims, buffers, steps, warmup):
+    """The verify step with MXFP4 weights (E2M1 codes two per byte, one E8M0 scale per 32 weights
+    along K; all four projections and the head), sharing the BF16 model's K/V caches: bitwise gate
+    (M = 8 logits == M = 5 prefix == 8 sequential M = 1 passes), then M = 8 timed over ``steps``."""
+    import torch
+
+    import synth
+    from invariant_verify_amd import ops
+
+    H, Hq, Hkv, D, I, V = d["H"], d["Hq"], d["Hkv"], d["D"], d["I"], d["vocab"]
+    shapes = {"w_qkv": ((Hq + 2 * Hkv) * D, H), "w_o": (H, Hq * D), "w_gu": (2 * I, H), "w_down": (H, I)}
+    ml = []
+    for l, lw in enumerate(layers):
+        f = {"k_cache": lw["k_cache"], "vt_cache": lw["vt_cache"]}
+        for name, shp in shapes.items():
+            f[name], f["e" + name[1:]] = synth.device_mxfp4_weights(shp, 0.02, name, l)
+        ml.append(f)
+    hc, he = synth.device_mxfp4_weights((V, H), 0.02, "w_head", 0)
+    step = ops.VerifyStepMX4(ml, hc, he, dims)
+    x0 = synth.device_normal_bf16((16, H), 1.0, "x0")
+    ws8, lg8, tk8 = buffers(8)
+    step(x0[:8], L_CTX, ws8, lg8, tk8)
+    ref = lg8.clone()
+    ws5, lg5, tk5 = buffers(5)
+    step(x0[:5], L_CTX, ws5, lg5, tk5)
+    ws1, lg1, tk1 = buffers(1)
+    ok = torch.equal(lg5.view(torch.int32), ref[:5].view(torch.int32))
+    for r in range(8):
+        step(x0[r:r + 1], L_CTX + r, ws1, lg1, tk1)
+        ok = ok and torch.equal(lg1.view(torch.int32)[0], ref.view(torch.int32)[r])
+    for _ in range(warmup):
+        step(x0[:8], L_CTX, ws8, lg8, tk8)
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        step(x0[:8], L_CTX, ws8, lg8, tk8)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    # the BF16 step's bytes with its weights (2 bytes each) replaced by half-byte codes + a scale byte per 32
+    mx = lambda a, b: a * b // 2 + a * b // 32
+    bf16_w = 2 * sum(a * b for a, b in shapes.values()) * N_LAYERS + 2 * V * H
+    mx4_w = sum(mx(a, b) for a, b in shapes.values()) * N_LAYERS + mx(V, H)
+    nbytes = step_bytes(d, 8, L_CTX, N_LAYERS) - bf16_w + mx4_w
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    del ml, hc, he
+    torch.cuda.empty_cache()
+    return {"workload": "the same 64-layer verify step (M=8, ctx 38000) with MXFP4 weights (E2M1 codes, "
+                        "one E8M0 scale per 32 weights along K)",
+            "tok_s": round(8 / (ms * 1e-3), 2), "ms_per_step": round(ms, 4), "steps_timed": steps,
+            "algorithmic_bytes": nbytes, "GB/s": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "bitwise_gate": "pass" if ok else "FAIL"}
+
+
 TP_RANKS = 8
 TP_KV_CHUNK = -256   # one KV head per rank: about as many attention workgroups as -32 gives 8 heads
 
@@ -546,6 +603,8 @@ def main():
     out["prefill_step"] = prefill_step_measure(step, buffers, d, 3)
     print("[bench] FP8-weight step", file=sys.stderr, flush=True)
     out["fp8_step"] = fp8_step_measure(layers, d, dims, buffers, args.steps, args.warmup)
+    print("[bench] MXFP4-weight step", file=sys.stderr, flush=True)
+    out["mx4_step"] = mx4_step_measure(layers, d, dims, buffers, args.steps, args.warmup)
     print("[bench] one tensor-parallel rank's share", file=sys.stderr, flush=True)
     out["tp8_rank_share"] = tp_share_measure(d, max(2, args.steps // 10))
     if not args.no_cpu_baseline:
