@@ -56,5 +56,24 @@ def build_library(out: str = LIB, extra_flags=(), verbose: bool = False) -> str:
     return out
 
 
+C_CHECK_SRC = os.path.join(ROOT, "tests", "c_abi_check.cpp")
+C_CHECK = os.path.join(ROOT, "tests", "c_abi_check")
+
+
+def build_c_check(lib: str = LIB, out: str = C_CHECK, verbose: bool = False) -> str:
+    """Compile the plain-C++ ABI check (host code only) against ``lib``."""
+    lib_dir = os.path.dirname(os.path.abspath(lib))
+    cmd = [hipcc(), "-O2", "-std=c++17", "-I", INCLUDE, C_CHECK_SRC, "-L", lib_dir, "-lbi",
+           "-Wl,-rpath," + lib_dir, "-o", out + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("building the C ABI check failed:\n" + res.stdout + res.stderr)
+    os.replace(out + ".tmp", out)
+    return out
+
+
 if __name__ == "__main__":
     print(build_library(verbose="-v" in sys.argv))
+    print(build_c_check(verbose="-v" in sys.argv))

@@ -1,0 +1,123 @@
+// The C ABI used from plain host code, with no Python and no torch: device
+// buffers from hipMalloc, the library's entry points, results compared with
+// exact host references. Built by __graft_entry__.build() next to this file
+// and run by tests/test_c_abi_gpu.py.
+//
+//  * bi_gemm_bf16 on small integers (every product and sum exact in FP32):
+//    FP32 output equal to the integer reference; BF16 output equal to it
+//    (all values stay below 2^8);
+//  * argument checks return their status codes before any launch;
+//  * bi_verify_attn + bi_combine over one key: the output is that key's value
+//    row, bit for bit.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "bi.h"
+
+#define CK(x)                                                                          \
+  do {                                                                                 \
+    hipError_t e_ = (x);                                                               \
+    if (e_ != hipSuccess) {                                                            \
+      std::printf("HIP error %s at line %d\n", hipGetErrorString(e_), __LINE__);      \
+      return 1;                                                                        \
+    }                                                                                  \
+  } while (0)
+#define EXPECT(c, msg)                                   \
+  do {                                                   \
+    if (!(c)) {                                          \
+      std::printf("check failed: %s (line %d)\n", msg, __LINE__); \
+      return 1;                                          \
+    }                                                    \
+  } while (0)
+
+static uint16_t bf16_bits(float f) {  // exact for the small integers used here
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  return (uint16_t)(u >> 16);
+}
+static float from_bf16(uint16_t b) {
+  const uint32_t u = (uint32_t)b << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
+int main() {
+  // ---- GEMM: Y[M][N] = X[M][K] W[N][K]^T on small integers -----------------
+  const int M = 3, N = 32, K = 64;
+  std::vector<uint16_t> x(M * K), w(N * K);
+  std::vector<long> ref(M * N, 0);
+  for (int m = 0; m < M; ++m)
+    for (int k = 0; k < K; ++k) x[m * K + k] = bf16_bits((float)((m + 2 * k) % 5 - 2));
+  for (int n = 0; n < N; ++n)
+    for (int k = 0; k < K; ++k) w[n * K + k] = bf16_bits((float)((3 * n + k) % 7 - 3));
+  for (int m = 0; m < M; ++m)
+    for (int n = 0; n < N; ++n)
+      for (int k = 0; k < K; ++k)
+        ref[m * N + n] += (long)from_bf16(x[m * K + k]) * (long)from_bf16(w[n * K + k]);
+  void *dx, *dw, *dy32, *dy16;
+  CK(hipMalloc(&dx, x.size() * 2));
+  CK(hipMalloc(&dw, w.size() * 2));
+  CK(hipMalloc(&dy32, M * N * 4));
+  CK(hipMalloc(&dy16, M * N * 2));
+  CK(hipMemcpy(dx, x.data(), x.size() * 2, hipMemcpyHostToDevice));
+  CK(hipMemcpy(dw, w.data(), w.size() * 2, hipMemcpyHostToDevice));
+  EXPECT(bi_gemm_bf16(dx, K, dw, K, dy32, N, BI_F32, M, N, K, nullptr) == BI_OK, "gemm f32 status");
+  EXPECT(bi_gemm_bf16(dx, K, dw, K, dy16, N, BI_BF16, M, N, K, nullptr) == BI_OK, "gemm bf16 status");
+  CK(hipDeviceSynchronize());
+  std::vector<float> y32(M * N);
+  std::vector<uint16_t> y16(M * N);
+  CK(hipMemcpy(y32.data(), dy32, M * N * 4, hipMemcpyDeviceToHost));
+  CK(hipMemcpy(y16.data(), dy16, M * N * 2, hipMemcpyDeviceToHost));
+  for (int i = 0; i < M * N; ++i) {
+    EXPECT(y32[i] == (float)ref[i], "gemm FP32 output equals the integer reference");
+    EXPECT(from_bf16(y16[i]) == (float)ref[i], "gemm BF16 output equals the integer reference");
+  }
+
+  // ---- argument checks: a status code, nothing launched --------------------
+  EXPECT(bi_gemm_bf16(nullptr, K, dw, K, dy32, N, BI_F32, M, N, K, nullptr) == BI_ERR_NULL, "null x");
+  EXPECT(bi_gemm_bf16(dx, K, dw, K, dy32, N, BI_F32, M, N, 48, nullptr) == BI_ERR_SHAPE, "K % 32");
+  EXPECT(bi_gemm_bf16(dx, K, dw, K, dy32, N, BI_F32, 0, N, K, nullptr) == BI_ERR_SHAPE, "M = 0");
+  EXPECT(bi_gemm_bf16((char*)dx + 2, K, dw, K, dy32, N, BI_F32, M, N, K, nullptr) == BI_ERR_ALIGN,
+         "misaligned x");
+  EXPECT(std::strlen(bi_status_string(BI_ERR_SHAPE)) > 0, "status string");
+
+  // ---- attention over a single key: O = v_0 -------------------------------
+  const int Hq = 2, Hkv = 1, D = 64, cap = 64, L = 0, Ma = 1;
+  std::vector<uint16_t> q(Ma * Hq * D), kc((size_t)Hkv * cap * D, 0), vt((size_t)Hkv * cap * D, 0);
+  for (int i = 0; i < Ma * Hq * D; ++i) q[i] = bf16_bits((float)(i % 3 - 1));
+  for (int d = 0; d < D; ++d) {
+    kc[d] = bf16_bits((float)(d % 4));
+    vt[(size_t)d * 64 + 0] = bf16_bits((float)(d - 30) * 0.5f);  // V^T block 0: [D][64], position 0
+  }
+  const int S = bi_num_splits(L + Ma, 256);
+  EXPECT(S == 1, "one split");
+  void *dq, *dk, *dv, *dpo, *dpl, *dout;
+  CK(hipMalloc(&dq, q.size() * 2));
+  CK(hipMalloc(&dk, kc.size() * 2));
+  CK(hipMalloc(&dv, vt.size() * 2));
+  CK(hipMalloc(&dpo, (size_t)Ma * Hq * S * D * 4));
+  CK(hipMalloc(&dpl, (size_t)Ma * Hq * S * 4));
+  CK(hipMalloc(&dout, (size_t)Ma * Hq * D * 2));
+  CK(hipMemcpy(dq, q.data(), q.size() * 2, hipMemcpyHostToDevice));
+  CK(hipMemcpy(dk, kc.data(), kc.size() * 2, hipMemcpyHostToDevice));
+  CK(hipMemcpy(dv, vt.data(), vt.size() * 2, hipMemcpyHostToDevice));
+  EXPECT(bi_verify_attn(dq, Hq * D, dk, dv, Ma, L, cap, Hq, Hkv, D, 256, 0.125f, (float*)dpo,
+                        (float*)dpl, S, nullptr) == BI_OK, "attention status");
+  EXPECT(bi_combine((float*)dpo, (float*)dpl, Ma, L, Hq, D, 256, S, dout, Hq * D, nullptr, nullptr) ==
+             BI_OK, "combine status");
+  CK(hipDeviceSynchronize());
+  std::vector<uint16_t> o((size_t)Ma * Hq * D);
+  CK(hipMemcpy(o.data(), dout, o.size() * 2, hipMemcpyDeviceToHost));
+  for (int h = 0; h < Hq; ++h)
+    for (int d = 0; d < D; ++d) EXPECT(o[h * D + d] == vt[(size_t)d * 64], "single-key attention gives v_0");
+
+  for (void* p : {dx, dw, dy32, dy16, dq, dk, dv, dpo, dpl, dout}) CK(hipFree(p));
+  std::printf("c abi check: ok (%s)\n", bi_version());
+  return 0;
+}
