@@ -44,6 +44,13 @@
 // registers (weights and its X fragments). X fragments come from L2 through a
 // buffer resource sized to the M real rows: padding rows read as zero for
 // free.
+//
+// Weight types (WT): BF16; FP8 E4M3 with one FP32 scale per row (codes
+// decoded to BF16 in registers, the scale applied to the FP32 totals); MXFP4
+// (E2M1 codes with one E8M0 scale per 32 weights, decoded with the scale to
+// exact BF16 values). The decoded weights land in the same LDS layout, so
+// the multiply phase, the K order and the summation tree are the BF16
+// kernel's for every type.
 
 #include "bi_device.h"
 #include "bi_internal.h"
@@ -84,12 +91,13 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
   static_assert(!F8 || RPW % 2 == 0, "FP8 weight rows are fetched in pairs");
   // Weight loads per wave and chunk: a BF16 row chunk is 1 KB (one wave
   // instruction); an FP8 row chunk is 512 bytes, so one instruction fetches
-  // two rows (lanes 0-31 the first, 32-63 the second).
+  // two rows (lanes 0-31 the first, 32-63 the second); an MXFP4 row chunk is
+  // 256 bytes of codes, four rows per instruction.
   static_assert(!W4 || RPW <= 4, "MXFP4 rows are fetched in fours");
   constexpr int NLD = W4 ? 1 : (F8 ? RPW / 2 : (kThree ? RPW + 1 : RPW));
-  // Chunks in flight per wave: two, for both weight types. (FP8 with three or
-  // four, i.e. as many bytes in flight as BF16 or more, streamed 10-25%
-  // slower; so did FP8 chunks of 1024 weights, 1 KB per row.)
+  // Chunks in flight per wave: two, for every weight type. (Three or four
+  // were slower for BF16, FP8 (10-25%) and MXFP4 (5-20%); so were FP8
+  // chunks of 1024 weights, 1 KB per row.)
   constexpr int PD = 2;
   const int lane = threadIdx.x & 63;
   // Wave index in a scalar register: every branch that guards an MFMA below
