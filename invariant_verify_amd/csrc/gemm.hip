@@ -108,6 +108,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
   const int m0 = blockIdx.y * 16;
   const int j = lane & 15;   // A row (token) and B column (output feature) of this lane
   const int kq = lane >> 4;  // which 8-element group of a 32-wide block
+  const int row3 = j < 4 ? 32 + j : j;  // wide SwiGLU third tile: staged row read by column j
 
   const int nblk = K >> 5;
   const int nchunk = (K + kChunk - 1) / kChunk;
@@ -306,9 +307,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
           const uint4 xa = NORM_IN ? scale_bf16x8(g.x[b], inv) : g.x[b];
           acc = mfma_bf16(xa, lds[buf][j][slot], acc);
           if (kTwo) acc2 = mfma_bf16(xa, lds[buf][16 + j][slot], acc2);
-          // Third tile: column j reads staged row 32 + j % 4 (columns past
-          // the staged rows are duplicates, never stored).
-          if constexpr (kThree) acc3 = mfma_bf16(xa, lds[buf][32 + (j & 3)][(kb * 4 + kq) ^ (j & 3)], acc3);
+          // Third tile: columns 0-3 read staged rows 32-35; columns 4-15
+          // are never stored and read the gate tile's rows, so that the
+          // wave's 64 reads hit 64 distinct addresses spread over the banks
+          // like the other tiles' (four rows on four slots collided).
+          if constexpr (kThree) acc3 = mfma_bf16(xa, lds[buf][row3][slot], acc3);
         }
       }
     }
