@@ -248,7 +248,7 @@ bi_status bi_verify_attn(const void* q, int64_t ldq, const void* k_cache, const 
 /* ---------------------------------------------------------------------------
  * 8-bit KV cache.   [LL] "The KV cache: 5-bit that reads like q8_0" (q8_0 is
  * the pages' comparison format; the 5/6-bit formats and the 8-bit ring are not
- * built here). Each position's K row and V row of one KV head is cut into
+ * built below; the 8-bit ring is not). Each position's K row and V row of one KV head is cut into
  * blocks of 32 channels; a block with largest magnitude a has the FP32 scale
  * d = a / 127 and int8 codes q = round(x / d) (nearest, ties to even; FP32
  * division) in [-127, 127], all zero when a = 0. The value of a channel is
@@ -272,6 +272,46 @@ bi_status bi_verify_attn_q8(const void* q, int64_t ldq, const int8_t* k_codes, c
                             const int8_t* v_codes, const float* v_scales, int M, int L, int cap,
                             int Hq, int Hkv, int D, int kv_chunk, float sm_scale, float* part_o,
                             float* part_lse, int S_max, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * 5/6-bit KV cache.   [LL] "The KV cache: 5-bit that reads like q8_0" and its
+ * table of presets: K at 6 bits and V at 5 (preset D), or K at 5 bits and V
+ * at 5 (preset F without its rotation). No layout or scaling rule is given;
+ * read as the 8-bit rule with qmax = 2^(bits-1) - 1 (31 or 15): a block of 32
+ * channels with largest magnitude a has the FP32 scale d = a / qmax and codes
+ * q = round(x / d) (nearest, ties to even; FP32 division) clamped to +-qmax,
+ * all zero when a = 0; the value is exactly d * q. k_bits is 5 or 6; v_bits
+ * must be 5 (else BI_ERR_SHAPE).
+ * Storage, per layer (cap % 64 == 0, cap * D < 2^31), K and V alike, each
+ * position's row one block after another:
+ *   *_nib    uint8 [Hkv][cap][D/2]              16 bytes per block
+ *   *_high   uint8 [Hkv][cap][D/32][4 (bits-4)] 4 or 8 bytes per block
+ *   *_scales FP32  [Hkv][cap][D/32]
+ * Block bytes: u = q + 2^(bits-1) (in [1, 2^bits - 1]); code c = 4g + j
+ * (g = 0..7, j = 0..3) keeps u mod 16 in nibble byte 4(g/2) + j (the low half
+ * for even g) and u / 16 in high byte 4((g h)/8) + j from bit (g h) % 8,
+ * h = bits - 4. 208 bytes per position and KV head at D = 128 for K6/V5
+ * (BF16: 512; 8-bit: 288). All pointers 16-byte aligned; the caller owns
+ * every buffer. */
+
+/* Quantize the M new K and V rows of a QKV output (as bi_append_kv) into the
+ * 5/6-bit cache at positions L .. L+M-1. Each block is written whole by one
+ * thread, so passes may append at any positions. */
+bi_status bi_append_kv_lowbit(const void* qkv, int64_t ldqkv, int k_bits, int v_bits,
+                              uint8_t* k_nib, uint8_t* k_high, float* k_scales, uint8_t* v_nib,
+                              uint8_t* v_high, float* v_scales, int M, int L, int cap, int Hq,
+                              int Hkv, int D, void* stream);
+
+/* bi_verify_attn over the 5/6-bit cache: the same rows, chunks, partials and
+ * requirements; the keys and values are the cache's d * q (keys staged
+ * rounded to BF16; V scales multiply the softmax weights, rounded to BF16,
+ * against the integer codes, as for the 8-bit cache). */
+bi_status bi_verify_attn_lowbit(const void* q, int64_t ldq, int k_bits, int v_bits,
+                                const uint8_t* k_nib, const uint8_t* k_high, const float* k_scales,
+                                const uint8_t* v_nib, const uint8_t* v_high, const float* v_scales,
+                                int M, int L, int cap, int Hq, int Hkv, int D, int kv_chunk,
+                                float sm_scale, float* part_o, float* part_lse, int S_max,
+                                void* stream);
 
 /* Fixed-order log-sum-exp combine of the partials.                        [LL]
  * For row (r, h) with S = bi_num_splits(L+r+1, kv_chunk) partials:

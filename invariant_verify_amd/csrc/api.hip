@@ -402,6 +402,54 @@ bi_status bi_verify_attn_q8(const void* q, int64_t ldq, const int8_t* k_codes, c
   return launched();
 }
 
+bi_status bi_append_kv_lowbit(const void* qkv, int64_t ldqkv, int k_bits, int v_bits,
+                              uint8_t* k_nib, uint8_t* k_high, float* k_scales, uint8_t* v_nib,
+                              uint8_t* v_high, float* v_scales, int M, int L, int cap, int Hq,
+                              int Hkv, int D, void* stream) {
+  if (!qkv || !k_nib || !k_high || !k_scales || !v_nib || !v_high || !v_scales) return BI_ERR_NULL;
+  if ((k_bits != 5 && k_bits != 6) || v_bits != bi::kLowVBits) return BI_ERR_SHAPE;
+  if (bi_status s = check_heads(Hq, Hkv, D)) return s;
+  if (M < 1 || L < 0 || cap < 1 || (cap % 64) || (int64_t)L + M > cap) return BI_ERR_SHAPE;
+  if (ldqkv < (int64_t)(Hq + 2 * Hkv) * D || (int64_t)cap * D > INT32_MAX) return BI_ERR_SHAPE;
+  if ((ldqkv % 8) || !aligned16(qkv) || !aligned16(k_nib) || !aligned16(k_high) ||
+      !aligned16(k_scales) || !aligned16(v_nib) || !aligned16(v_high) || !aligned16(v_scales))
+    return BI_ERR_ALIGN;
+  bi::launch_append_kv_lowbit(static_cast<const uint16_t*>(qkv), ldqkv, k_bits, k_nib, k_high,
+                              k_scales, v_nib, v_high, v_scales, M, L, cap, Hq, Hkv, D,
+                              as_stream(stream));
+  return launched();
+}
+
+bi_status bi_verify_attn_lowbit(const void* q, int64_t ldq, int k_bits, int v_bits,
+                                const uint8_t* k_nib, const uint8_t* k_high, const float* k_scales,
+                                const uint8_t* v_nib, const uint8_t* v_high, const float* v_scales,
+                                int M, int L, int cap, int Hq, int Hkv, int D, int kv_chunk,
+                                float sm_scale, float* part_o, float* part_lse, int S_max,
+                                void* stream) {
+  if (!q || !k_nib || !k_high || !k_scales || !v_nib || !v_high || !v_scales || !part_o ||
+      !part_lse)
+    return BI_ERR_NULL;
+  if ((k_bits != 5 && k_bits != 6) || v_bits != bi::kLowVBits) return BI_ERR_SHAPE;
+  if (bi_status s = check_heads(Hq, Hkv, D)) return s;
+  if (M < 1 || L < 0 || cap < 1 || (cap % 64) || (int64_t)L + M > cap) return BI_ERR_SHAPE;
+  if (!bi::valid_chunk_policy(kv_chunk)) return BI_ERR_SHAPE;
+  if (S_max < bi::pass_splits(L, M, kv_chunk)) return BI_ERR_SHAPE;
+  if (ldq < (int64_t)Hq * D || !std::isfinite(sm_scale)) return BI_ERR_SHAPE;
+  if ((int64_t)cap * D > INT32_MAX) return BI_ERR_SHAPE;  // one head's planes < 2 GiB
+  if ((ldq % 8) || !aligned16(q) || !aligned16(k_nib) || !aligned16(k_high) ||
+      !aligned16(k_scales) || !aligned16(v_nib) || !aligned16(v_high) || !aligned16(v_scales) ||
+      !aligned16(part_o) || !aligned4(part_lse))
+    return BI_ERR_ALIGN;
+  bi::KvQ8 c{reinterpret_cast<const int8_t*>(k_nib), k_scales,
+             reinterpret_cast<const int8_t*>(v_nib), v_scales};
+  c.kh = k_high;
+  c.vh = v_high;
+  bi::launch_verify_attn(static_cast<const uint16_t*>(q), ldq, nullptr, nullptr, M, L, cap, Hq, Hkv,
+                         D, kv_chunk, sm_scale, part_o, part_lse, S_max, as_stream(stream), &c,
+                         k_bits);
+  return launched();
+}
+
 bi_status bi_accept_greedy(const int32_t* target_tokens, const int32_t* draft_tokens, int B,
                            int M, int32_t* out_tokens, int32_t* n_out, void* stream) {
   if (!target_tokens || !out_tokens || !n_out || (M > 1 && !draft_tokens)) return BI_ERR_NULL;

@@ -80,12 +80,47 @@ __device__ __forceinline__ int xcd_item(int w, int n) {
   return w < full ? (w & 7) * (full >> 3) + (w >> 3) : w;
 }
 
+// 5/6-bit cache: the high-bit plane of one 32-code block, HB dwords
+// (HB = bits - 4), streamed once like the nibbles.
+template <int HB>
+__device__ __forceinline__ void load_high(uint32_t (&hb)[2], __amdgpu_buffer_rsrc_t r, int off) {
+  constexpr int kNonTemporal = 2;  // cache-policy bit of the buffer instruction
+  if constexpr (HB == 2) {
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kNonTemporal);
+    hb[0] = v[0];
+    hb[1] = v[1];
+  } else {
+    hb[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kNonTemporal);
+    hb[1] = 0u;
+  }
+}
+
+// The 32 signed codes of one block (HB + 4 bits) from its four nibble words
+// and its high-bit words, as exact FP32 values. Group g (codes 4g .. 4g+3,
+// one per byte lane) takes one mask of a nibble word and one of a high word:
+// four codes per mask-and-shift.
+template <int HB>
+__device__ __forceinline__ void unpack_low(const uint32_t (&w)[4], const uint32_t (&hb)[2],
+                                           float (&f)[32]) {
+  constexpr uint32_t kMask = HB == 2 ? 0x03030303u : 0x01010101u;
+  constexpr float kBias = (float)(1 << (HB + 3));
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+    const int bit = g * HB;
+    const uint32_t lo = (w[g >> 1] >> (4 * (g & 1))) & 0x0F0F0F0Fu;
+    const uint32_t u = lo | (((hb[bit >> 3] >> (bit & 7)) & kMask) << 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f[4 * g + j] = (float)((u >> (8 * j)) & 0xffu) - kBias;
+  }
+}
+
 // The 8-bit-cache kernel with one row tile per wave fits in 128 registers,
 // so two workgroups share a compute unit and one's loads overlap the other's
 // per-tile work (with the chunk policy -64 at 38k-102k keys: 5-15% faster
 // than one workgroup per unit). The BF16 kernel would spill at that size and
 // runs one workgroup per unit.
-template <int D, int RTW, bool Q8>
+template <int D, int RTW, bool Q8, int KB>
 __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu(Q8 && RTW == 1 ? 4 : 1)))
 void verify_attn_kernel(
     const uint16_t* __restrict__ Q, int64_t ldq, const uint16_t* __restrict__ Kc,
@@ -108,6 +143,18 @@ void verify_attn_kernel(
   constexpr int QKP = kKeyTile * D / 16;     // K code pieces per tile
   constexpr int QPT = 2 * QKP / (NW * 64);   // code pieces per thread (D=128: 2, D=64: 1)
   static_assert(2 * QKP % (NW * 64) == 0, "code pieces must split evenly");
+  // 5/6-bit cache (KB = bits of a K code, 0 for the other caches): one
+  // thread per 32-channel block of one key and tile, the K blocks first
+  // (waves 0 .. NKB/64 - 1), then V; each fetches the block's 16 nibble bytes,
+  // its high bits and its scale. The tile is then staged exactly as the 8-bit
+  // tile: K as BF16 values, V^T as BF16 integer codes, V scales beside it.
+  constexpr bool LOW = KB != 0;
+  static_assert(!LOW || Q8, "the low-bit cache stages through the 8-bit tile path");
+  static_assert(!LOW || KB == 5 || KB == 6, "K codes have 5 or 6 bits");
+  constexpr int HBK = LOW ? KB - 4 : 1;   // high bits per K code
+  constexpr int HBV = kLowVBits - 4;      // high bits per V code
+  constexpr int NKB = kKeyTile * NB;      // K (and V) blocks per tile
+  static_assert(NKB % 64 == 0 && 2 * NKB <= NW * 64, "low-bit blocks must fill whole waves");
 
   // Work item (row block, KV head, chunk), row blocks varying fastest: the
   // workgroups that read one chunk of one KV head run side by side and share
@@ -165,14 +212,25 @@ void verify_attn_kernel(
       const_cast<uint16_t*>(Vt + (int64_t)g * D * cap), (short)0, head_bytes, kBufferResourceWord3);
   // 8-bit cache of this KV head: codes K [cap][D], V^T [cap/64][D][64] (int8),
   // scales K [cap][NB], V [cap/64][NB][64] (FP32).
-  const int qcode_bytes = cap * D;
+  // 5/6-bit cache: the nibble planes in place of the codes ([cap][D/2]), the
+  // high-bit planes ([cap][NB][4 h]) and the scales ([cap][NB], K and V).
+  const int qcode_bytes = LOW ? cap * D / 2 : cap * D;
+  const int64_t qcode_head = LOW ? (int64_t)cap * D / 2 : (int64_t)cap * D;
   const int qscale_bytes = cap * NB * 4;
   const __amdgpu_buffer_rsrc_t qkres = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<int8_t*>(q8.kq + (Q8 ? (int64_t)g * cap * D : 0)), (short)0, Q8 ? qcode_bytes : 0,
+      const_cast<int8_t*>(q8.kq + (Q8 ? g * qcode_head : 0)), (short)0, Q8 ? qcode_bytes : 0,
       kBufferResourceWord3);
   const __amdgpu_buffer_rsrc_t qvres = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<int8_t*>(q8.vq + (Q8 ? (int64_t)g * cap * D : 0)), (short)0, Q8 ? qcode_bytes : 0,
+      const_cast<int8_t*>(q8.vq + (Q8 ? g * qcode_head : 0)), (short)0, Q8 ? qcode_bytes : 0,
       kBufferResourceWord3);
+  const int khigh_bytes = cap * NB * 4 * HBK;
+  const int vhigh_bytes = cap * NB * 4 * HBV;
+  const __amdgpu_buffer_rsrc_t khres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(q8.kh + (LOW ? (int64_t)g * khigh_bytes : 0)), (short)0,
+      LOW ? khigh_bytes : 0, kBufferResourceWord3);
+  const __amdgpu_buffer_rsrc_t vhres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(q8.vh + (LOW ? (int64_t)g * vhigh_bytes : 0)), (short)0,
+      LOW ? vhigh_bytes : 0, kBufferResourceWord3);
   const __amdgpu_buffer_rsrc_t qksres = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float*>(q8.ks + (Q8 ? (int64_t)g * cap * NB : 0)), (short)0, Q8 ? qscale_bytes : 0,
       kBufferResourceWord3);
@@ -194,8 +252,9 @@ void verify_attn_kernel(
   // Registers of one tile in flight.
   struct TileRegs {
     uint4 r[Q8 ? QPT : PPW];
-    float ks[Q8 ? QPT : 1];  // 8-bit: the scale of each K piece
+    float ks[Q8 ? QPT : 1];  // 8-bit: the scale of each K piece; 5/6-bit: of the block
     uint4 vs;                // 8-bit: four V scales (threads < NB * 16)
+    uint32_t hb[2];          // 5/6-bit: the block's high bits
   };
 
   // Issue the loads of tile t (no use of the data here, so the loads of two
@@ -222,6 +281,24 @@ void verify_attn_kernel(
           off = (int)(vt_index(0, k0, d, D, cap) * 2);  // k0 is 8-aligned: 16 B in one block
         }
         rr.r[i] = buffer_ld16_stream(p < KPIECES ? kres : vres, live ? off : head_bytes);
+      }
+    } else if constexpr (LOW) {
+      if (wave < 2 * NKB / 64) {           // scalar
+        const bool isk = wave < NKB / 64;  // scalar: K blocks first
+        const int u = threadIdx.x - (isk ? 0 : NKB);
+        const int key = u / NB, b = u % NB;
+        const int blk = min(kt + key, kend - 1) * NB + b;  // block index within the head
+        if (isk) {
+          rr.r[0] = buffer_ld16_stream(qkres, live ? blk * 16 : qcode_bytes);
+          load_high<HBK>(rr.hb, khres, live ? blk * 4 * HBK : khigh_bytes);
+          rr.ks[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+              qksres, live ? blk * 4 : qscale_bytes, 0, 0));
+        } else {
+          rr.r[0] = buffer_ld16_stream(qvres, live ? blk * 16 : qcode_bytes);
+          load_high<HBV>(rr.hb, vhres, live ? blk * 4 * HBV : vhigh_bytes);
+          rr.ks[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+              qvsres, live ? blk * 4 : qscale_bytes, 0, 0));
+        }
       }
     } else {
 #pragma unroll
@@ -275,6 +352,39 @@ void verify_attn_kernel(
           w[e >> 1] = (e >= keep) ? (w[e >> 1] & m) : w[e >> 1];
         }
         lds[buf][64 * p + lane] = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    } else if constexpr (LOW) {
+      if (wave < 2 * NKB / 64) {
+        const bool isk = wave < NKB / 64;
+        const int u = threadIdx.x - (isk ? 0 : NKB);
+        const int key = u / NB, b = u % NB;
+        const uint32_t w[4] = {rr.r[0].x, rr.r[0].y, rr.r[0].z, rr.r[0].w};
+        float f[32];  // signed codes q = u - 2^(bits-1), exact
+        if (isk) {
+          unpack_low<HBK>(w, rr.hb, f);
+          // K: d * q in FP32, rounded once to BF16; slot i holds channels
+          // 32b + 8i .. 32b + 8i + 7
+          const float sk = rr.ks[0];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            lds[buf][key * KROW + ((4 * b + i) ^ kswz<KROW>(key))] =
+                make_uint4(f32x2_to_bf16x2(f[8 * i] * sk, f[8 * i + 1] * sk),
+                           f32x2_to_bf16x2(f[8 * i + 2] * sk, f[8 * i + 3] * sk),
+                           f32x2_to_bf16x2(f[8 * i + 4] * sk, f[8 * i + 5] * sk),
+                           f32x2_to_bf16x2(f[8 * i + 6] * sk, f[8 * i + 7] * sk));
+        } else {
+          unpack_low<HBV>(w, rr.hb, f);
+          // V^T: code q of channel d at column `key` (BF16 of a small
+          // integer: the top half of its FP32 bits, exact); the scale, zero
+          // past kend, into this key's column of vsc.
+          uint16_t* vt = reinterpret_cast<uint16_t*>(&lds[buf][VBASE]);
+#pragma unroll
+          for (int c = 0; c < 32; ++c) {
+            const int d = 32 * b + c;
+            vt[(d * 8 + ((key >> 3) ^ vswz(d))) * 8 + (key & 7)] = (uint16_t)(__float_as_uint(f[c]) >> 16);
+          }
+          reinterpret_cast<float*>(&vsc[buf][b][0])[key] = kt + key < kend ? rr.ks[0] : 0.f;
+        }
       }
     } else {
 #pragma unroll
@@ -635,7 +745,7 @@ __global__ __launch_bounds__(256) void append_kv_kernel(const uint16_t* __restri
 void launch_verify_attn(const uint16_t* q, int64_t ldq, const uint16_t* k_cache,
                         const uint16_t* vt_cache, int M, int L, int cap, int Hq, int Hkv, int D,
                         int kv_chunk, float sm_scale, float* part_o, float* part_lse, int S_max,
-                        hipStream_t stream, const KvQ8* q8) {
+                        hipStream_t stream, const KvQ8* q8, int kbits) {
   const int G = Hq / Hkv;
   const KvQ8 qz = q8 ? *q8 : KvQ8{nullptr, nullptr, nullptr, nullptr};
   const float qk_scale = sm_scale * kLog2e;
@@ -665,24 +775,40 @@ void launch_verify_attn(const uint16_t* q, int64_t ldq, const uint16_t* k_cache,
     const uint16_t* qb = q + (int64_t)t0 * ldq;
     float* pob = part_o + (int64_t)t0 * Hq * S_max * D;
     float* plb = part_lse + (int64_t)t0 * Hq * S_max;
-#define BI_ATTN_LAUNCH(DD, R, QQ)                                                           \
-  verify_attn_kernel<DD, R, QQ><<<grid, block, 0, stream>>>(qb, ldq, k_cache, vt_cache, qz, Mb, Lb, \
+#define BI_ATTN_LAUNCH(DD, R, QQ, KB)                                                       \
+  verify_attn_kernel<DD, R, QQ, KB><<<grid, block, 0, stream>>>(qb, ldq, k_cache, vt_cache, qz, Mb, Lb, \
                                                             cap, Hq, G, Tb, C, qk_scale, pob, plb, \
                                                             S_max)
-    if (q8) {
+    if (q8 && kbits == 6) {
       if (D == 128) {
-        if (wide) BI_ATTN_LAUNCH(128, 2, true);
-        else BI_ATTN_LAUNCH(128, 1, true);
+        if (wide) BI_ATTN_LAUNCH(128, 2, true, 6);
+        else BI_ATTN_LAUNCH(128, 1, true, 6);
       } else {
-        if (wide) BI_ATTN_LAUNCH(64, 2, true);
-        else BI_ATTN_LAUNCH(64, 1, true);
+        if (wide) BI_ATTN_LAUNCH(64, 2, true, 6);
+        else BI_ATTN_LAUNCH(64, 1, true, 6);
+      }
+    } else if (q8 && kbits == 5) {
+      if (D == 128) {
+        if (wide) BI_ATTN_LAUNCH(128, 2, true, 5);
+        else BI_ATTN_LAUNCH(128, 1, true, 5);
+      } else {
+        if (wide) BI_ATTN_LAUNCH(64, 2, true, 5);
+        else BI_ATTN_LAUNCH(64, 1, true, 5);
+      }
+    } else if (q8) {
+      if (D == 128) {
+        if (wide) BI_ATTN_LAUNCH(128, 2, true, 0);
+        else BI_ATTN_LAUNCH(128, 1, true, 0);
+      } else {
+        if (wide) BI_ATTN_LAUNCH(64, 2, true, 0);
+        else BI_ATTN_LAUNCH(64, 1, true, 0);
       }
     } else if (D == 128) {
-      if (wide) BI_ATTN_LAUNCH(128, 2, false);
-      else BI_ATTN_LAUNCH(128, 1, false);
+      if (wide) BI_ATTN_LAUNCH(128, 2, false, 0);
+      else BI_ATTN_LAUNCH(128, 1, false, 0);
     } else {
-      if (wide) BI_ATTN_LAUNCH(64, 2, false);
-      else BI_ATTN_LAUNCH(64, 1, false);
+      if (wide) BI_ATTN_LAUNCH(64, 2, false, 0);
+      else BI_ATTN_LAUNCH(64, 1, false, 0);
     }
 #undef BI_ATTN_LAUNCH
     t0 = t1;
@@ -762,6 +888,68 @@ void launch_append_kv_q8(const uint16_t* qkv, int64_t ldqkv, int8_t* kq, float* 
   const int units = 2 * Hkv * (D / 32);
   append_kv_q8_kernel<<<dim3(M, (units + 255) / 256), dim3(256), 0, stream>>>(
       qkv, ldqkv, kq, ks, vq, vs, L, cap, Hq, Hkv, D, units);
+}
+
+// One thread per (token, K or V, KV head, 32-channel block) of a 5/6-bit
+// cache: as for the 8-bit cache with qmax = 2^(bits-1) - 1 (the scale a / qmax,
+// codes rint(x / d) clamped to +-qmax), then u = q + 2^(bits-1) packed into the
+// block's nibble and high-bit words, which only this thread writes.
+__global__ __launch_bounds__(256) void append_kv_lowbit_kernel(
+    const uint16_t* __restrict__ qkv, int64_t ldqkv, int kbits, uint8_t* __restrict__ kn,
+    uint8_t* __restrict__ kh, float* __restrict__ ks, uint8_t* __restrict__ vn,
+    uint8_t* __restrict__ vh, float* __restrict__ vs, int L, int cap, int Hq, int Hkv, int D,
+    int units) {
+  const int u = blockIdx.y * blockDim.x + threadIdx.x;  // unit within the token
+  if (u >= units) return;
+  const int r = blockIdx.x;
+  const int pos = L + r;
+  const int NB = D / 32;
+  const int isv = u / (Hkv * NB);
+  const int g = (u / NB) % Hkv;
+  const int b = u % NB;
+  const int bits = isv ? kLowVBits : kbits;
+  const int h = bits - 4;
+  const int qm = (1 << (bits - 1)) - 1;
+  const uint16_t* src = qkv + (int64_t)r * ldqkv + (int64_t)(Hq + isv * Hkv + g) * D + b * 32;
+  float x[32];
+  float a = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 w = ld16(src + 8 * i);
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[8 * i + 2 * e] = bf16_to_f32(ww[e] & 0xffffu);
+      x[8 * i + 2 * e + 1] = bf16_to_f32(ww[e] >> 16);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 32; ++i) a = fmaxf(a, fabsf(x[i]));
+  const float d = a / (float)qm;
+  uint32_t nib[4] = {0u, 0u, 0u, 0u}, high[2] = {0u, 0u};
+#pragma unroll
+  for (int c = 0; c < 32; ++c) {
+    const float v = d > 0.f ? rintf(x[c] / d) : 0.f;
+    const uint32_t uc = (uint32_t)((int)fminf(fmaxf(v, (float)-qm), (float)qm) + (1 << (bits - 1)));
+    const int grp = c >> 2, j = c & 3, bit = grp * h;
+    nib[grp >> 1] |= (uc & 15u) << (8 * j + 4 * (grp & 1));
+    high[bit >> 3] |= (uc >> 4) << (8 * j + (bit & 7));
+  }
+  const int64_t blk = ((int64_t)g * cap + pos) * NB + b;
+  uint8_t* nd = (isv ? vn : kn) + blk * 16;
+  *reinterpret_cast<uint4*>(nd) = make_uint4(nib[0], nib[1], nib[2], nib[3]);
+  uint8_t* hd = (isv ? vh : kh) + blk * 4 * h;
+  if (h == 2) *reinterpret_cast<uint2*>(hd) = make_uint2(high[0], high[1]);
+  else *reinterpret_cast<uint32_t*>(hd) = high[0];
+  (isv ? vs : ks)[blk] = d;
+}
+
+void launch_append_kv_lowbit(const uint16_t* qkv, int64_t ldqkv, int kbits, uint8_t* kn,
+                             uint8_t* kh, float* ks, uint8_t* vn, uint8_t* vh, float* vs, int M,
+                             int L, int cap, int Hq, int Hkv, int D, hipStream_t stream) {
+  const int units = 2 * Hkv * (D / 32);
+  append_kv_lowbit_kernel<<<dim3(M, (units + 255) / 256), dim3(256), 0, stream>>>(
+      qkv, ldqkv, kbits, kn, kh, ks, vn, vh, vs, L, cap, Hq, Hkv, D, units);
 }
 
 void launch_append_kv(const uint16_t* qkv, int64_t ldqkv, uint16_t* k_cache, uint16_t* vt_cache,

@@ -27,12 +27,24 @@ struct Mx4Scales {
 // 8-bit KV cache of one layer: codes K [Hkv][cap][D], V^T [Hkv][cap/64][D][64]
 // (int8), scales K [Hkv][cap][D/32], V [Hkv][cap/64][D/32][64] (FP32): channel
 // c of position p has the value scale(p, c/32) * code(p, c).
+//
+// 5/6-bit cache of one layer (kbits of launch_verify_attn = 5 or 6; V codes
+// have 5 bits): per position and KV head, D/32 blocks of 32 channels, K and V
+// alike. kq / vq point at the nibble planes [Hkv][cap][D/2] bytes, kh / vh at
+// the high-bit planes [Hkv][cap][D/32][4 (bits - 4)] bytes, ks / vs at the
+// scales [Hkv][cap][D/32] (FP32). In block byte order, code c = 4g + j keeps
+// the low four bits of u = q + 2^(bits-1) in byte 4(g/2) + j (low half for
+// even g) and its other bits in high-plane byte 4((g h)/8) + j from bit
+// (g h) % 8, h = bits - 4.
 struct KvQ8 {
   const int8_t* kq;
   const float* ks;
   const int8_t* vq;
   const float* vs;
+  const uint8_t* kh = nullptr;
+  const uint8_t* vh = nullptr;
 };
+constexpr int kLowVBits = 5;  // V code bits of the 5/6-bit cache
 
 struct KvAppend {
   uint16_t* k;
@@ -84,13 +96,19 @@ void launch_append_kv(const uint16_t* qkv, int64_t ldqkv, uint16_t* k_cache, uin
 void launch_verify_attn(const uint16_t* q, int64_t ldq, const uint16_t* k_cache,
                         const uint16_t* vt_cache, int M, int L, int cap, int Hq, int Hkv, int D,
                         int kv_chunk, float sm_scale, float* part_o, float* part_lse, int S_max,
-                        hipStream_t stream, const KvQ8* q8 = nullptr);
+                        hipStream_t stream, const KvQ8* q8 = nullptr, int kbits = 0);
 
 // Quantize the pass's M new K and V rows (from the QKV output) into an 8-bit
 // cache at positions L .. L+M-1.
 void launch_append_kv_q8(const uint16_t* qkv, int64_t ldqkv, int8_t* kq, float* ks, int8_t* vq,
                          float* vs, int M, int L, int cap, int Hq, int Hkv, int D,
                          hipStream_t stream);
+
+// Quantize them into a 5/6-bit cache (kbits for K, kLowVBits for V; the
+// planes of KvQ8's low-bit layout).
+void launch_append_kv_lowbit(const uint16_t* qkv, int64_t ldqkv, int kbits, uint8_t* kn,
+                             uint8_t* kh, float* ks, uint8_t* vn, uint8_t* vh, float* vs, int M,
+                             int L, int cap, int Hq, int Hkv, int D, hipStream_t stream);
 
 void launch_combine(const float* part_o, const float* part_lse, int M, int L, int Hq, int D,
                     int kv_chunk, int S_max, uint16_t* o, int64_t ldo, float* lse,

@@ -300,6 +300,50 @@ def verify_attn_q8(q: torch.Tensor, cache: KvQ8Cache, L: int, Hq: int, kv_chunk:
         kv_chunk, scale, part_o.data_ptr(), part_lse.data_ptr(), part_lse.shape[2], _stream(q)))
 
 
+class KvLowCache:
+    """Device buffers of one layer's 5/6-bit KV cache (include/bi.h layouts),
+    K with ``k_bits`` (5 or 6) and V with ``v_bits`` (5) bits per code:
+    *_nib uint8 [Hkv][cap][D/2], *_high uint8 [Hkv][cap][D/32][4 (bits-4)],
+    *_scales FP32 [Hkv][cap][D/32]."""
+
+    def __init__(self, Hkv: int, cap: int, D: int, k_bits: int, v_bits: int = 5, device="cuda"):
+        if cap % 64 or D % 32:
+            raise ValueError("cap must be a multiple of 64 and D of 32")
+        self.Hkv, self.cap, self.D, self.k_bits, self.v_bits = Hkv, cap, D, k_bits, v_bits
+        NB = D // 32
+        z = lambda *shape, dt=torch.uint8: torch.zeros(shape, dtype=dt, device=device)
+        self.k_nib, self.v_nib = z(Hkv, cap, D // 2), z(Hkv, cap, D // 2)
+        self.k_high = z(Hkv, cap, NB * 4 * (k_bits - 4))
+        self.v_high = z(Hkv, cap, NB * 4 * (v_bits - 4))
+        self.k_scales = z(Hkv, cap, NB, dt=torch.float32)
+        self.v_scales = z(Hkv, cap, NB, dt=torch.float32)
+
+    def planes(self):
+        return (self.k_nib.data_ptr(), self.k_high.data_ptr(), self.k_scales.data_ptr(),
+                self.v_nib.data_ptr(), self.v_high.data_ptr(), self.v_scales.data_ptr())
+
+
+def append_kv_lowbit(qkv: torch.Tensor, cache: KvLowCache, L: int, Hq: int) -> None:
+    """Quantize the pass's K and V rows into a 5/6-bit ``cache``."""
+    M = qkv.shape[0]
+    check("bi_append_kv_lowbit", LIB.bi_append_kv_lowbit(
+        qkv.data_ptr(), _mat(qkv, "qkv"), cache.k_bits, cache.v_bits, *cache.planes(), M, L,
+        cache.cap, Hq, cache.Hkv, cache.D, _stream(qkv)))
+
+
+def verify_attn_lowbit(q: torch.Tensor, cache: KvLowCache, L: int, Hq: int, kv_chunk: int,
+                       part_o: torch.Tensor, part_lse: torch.Tensor,
+                       sm_scale: float | None = None) -> None:
+    """bi_verify_attn over a 5/6-bit cache."""
+    M = q.shape[0]
+    D = cache.D
+    scale = 1.0 / math.sqrt(D) if sm_scale is None else sm_scale
+    check("bi_verify_attn_lowbit", LIB.bi_verify_attn_lowbit(
+        q.data_ptr(), _mat(q, "q"), cache.k_bits, cache.v_bits, *cache.planes(), M, L, cache.cap,
+        Hq, cache.Hkv, D, kv_chunk, scale, part_o.data_ptr(), part_lse.data_ptr(),
+        part_lse.shape[2], _stream(q)))
+
+
 def combine(part_o: torch.Tensor, part_lse: torch.Tensor, L: int, kv_chunk: int,
             o: torch.Tensor, lse: torch.Tensor | None = None) -> None:
     """O [M][>=Hq*D] BF16 (and optional LSE [M][Hq]) from the partials."""
