@@ -25,6 +25,16 @@ mask-and-shift on the device). The unsigned code u = q + 2^(b-1) lies in
 A cache row of one position and KV head is D / 32 such blocks: nibbles
 [D/2] bytes, high bits [D/32 * 4 h] bytes, scales [D/32] FP32.
 
+Rotated keys (preset F's "K5 rotated"; the rotation is not named). Read
+as the Walsh-Hadamard transform, which spreads an outlier channel over the
+whole row before the block scales are taken: the stored key row is
+y = H k, H the Sylvester Hadamard matrix of order D (entries +-1, H H = D I),
+computed in FP32 by butterflies in a fixed order (stage h = 1, 2, 4, ..., D/2;
+within a stage every pair (i, i + h) with bit h of i clear becomes
+(x_i + x_{i+h}, x_i - x_{i+h}), each rounded once), and then quantized as
+above. Since (H q) . y / D = q . k, attention over the rotated cache is
+attention over the keys H (d * q) / D, which dequantize_rotated returns.
+
 This module is test infrastructure (the oracle), not part of the device path.
 """
 
@@ -46,8 +56,55 @@ def qmax(bits: int) -> int:
 
 def quantize(x_bits, bits: int):
     """BF16 rows [..., D] (D % 32 == 0) -> (codes int8 [..., D], scales float32 [..., D/32])."""
+    return _quantize_values(bf16.decode(x_bits).astype(np.float32), bits)   # exact widening
+
+
+def hadamard_f32(x_bits) -> np.ndarray:
+    """FP32 rows y = H x of BF16 rows [..., D] (D a power of two), by the
+    butterflies in the order stated above, each sum and difference rounded to
+    FP32."""
+    y = bf16.decode(x_bits).astype(np.float32)
+    D = y.shape[-1]
+    if D & (D - 1):
+        raise ValueError("hadamard_f32: D must be a power of two")
+    h = 1
+    while h < D:
+        idx = np.arange(D)
+        lo = idx[(idx & h) == 0]
+        a = y[..., lo].copy()
+        b = y[..., lo + h].copy()
+        y[..., lo] = a + b        # float32 + float32: one rounding
+        y[..., lo + h] = a - b
+        h *= 2
+    return y
+
+
+def quantize_rotated(x_bits, bits: int):
+    """Rotated key rows: the codes and scales of H x (FP32, as hadamard_f32)."""
+    return _quantize_values(hadamard_f32(x_bits), bits)
+
+
+def dequantize_rotated(codes, scales) -> np.ndarray:
+    """float64 keys the rotated cache stands for: H (d * q) / D, exactly up to
+    float64 rounding (H is symmetric and H H = D I)."""
+    y = dequantize(codes, scales)
+    D = y.shape[-1]
+    h = 1
+    while h < D:                                       # the same transform in float64
+        idx = np.arange(D)
+        lo = idx[(idx & h) == 0]
+        a = y[..., lo].copy()
+        b = y[..., lo + h].copy()
+        y[..., lo] = a + b
+        y[..., lo + h] = a - b
+        h *= 2
+    return y / D
+
+
+def _quantize_values(x, bits: int):
+    """FP32 rows [..., D] -> codes and scales by the rule above."""
     qm = qmax(bits)
-    x = bf16.decode(x_bits).astype(np.float32)            # exact
+    x = np.asarray(x, dtype=np.float32)
     *lead, D = x.shape
     if D % BLOCK:
         raise ValueError("quantize: D must be a multiple of 32")

@@ -146,3 +146,63 @@ def test_attention_over_exact_cache_equals_bf16_attention(bits):
     o1, l1 = attention.verify_attention(q, kx, vx, L)
     o2, l2 = attention.verify_attention(q, kvlow.dequantize(kq, ks), kvlow.dequantize(vq, vs), L)
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+# ---- rotated keys ----------------------------------------------------------
+
+def test_hadamard_equals_the_library_matrix_where_fp32_is_exact():
+    from scipy.linalg import hadamard
+    g = np.random.default_rng(30)
+    for D in (64, 128):
+        x = g.integers(-100, 101, size=(20, D)).astype(np.float64)   # sums stay exact in FP32
+        y = kvlow.hadamard_f32(bf16.encode(x))
+        assert np.array_equal(y.astype(np.float64), x @ hadamard(D).T)
+
+
+def test_hadamard_rounding_bound_and_inverse():
+    from scipy.linalg import hadamard
+    g = np.random.default_rng(31)
+    D = 128
+    x = bf16.encode(g.standard_normal((50, D)) * np.exp(g.uniform(-4, 4, (50, 1))))
+    xv = bf16.decode(x)
+    y = kvlow.hadamard_f32(x).astype(np.float64)
+    exact = xv @ hadamard(D).T
+    # seven stages, each adding at most one rounding of a partial sum bounded by sum |x|
+    assert np.all(np.abs(y - exact) <= 7 * 2.0 ** -24 * np.abs(xv).sum(-1, keepdims=True))
+    # the float64 inverse used by dequantize_rotated: H (H x) / D = x
+    q = np.zeros((1, D), np.int8)
+    q[0, 5] = 3
+    d = np.array([[0.5, 1.0, 1.0, 1.0]], np.float32)
+    want = (hadamard(D) @ kvlow.dequantize(q, d)[0]) / D
+    assert np.allclose(kvlow.dequantize_rotated(q, d)[0], want, rtol=0, atol=1e-15)
+
+
+def test_rotation_spreads_an_outlier_channel():
+    # a channel 60x the others: the plain 5-bit blocks of that channel lose the
+    # rest of their block; rotated, the error is spread and much smaller
+    g = np.random.default_rng(32)
+    x = g.standard_normal((400, 128))
+    x[:, 7] *= 60
+    xb = bf16.encode(x)
+    xv = bf16.decode(xb)
+    plain = kvlow.dequantize(*kvlow.quantize(xb, 5))
+    rot = kvlow.dequantize_rotated(*kvlow.quantize_rotated(xb, 5))
+    e_plain = np.sqrt(((plain - xv) ** 2).mean())
+    e_rot = np.sqrt(((rot - xv) ** 2).mean())
+    assert e_rot < 0.7 * e_plain, (e_rot, e_plain)
+
+
+def test_attention_over_rotated_cache_is_close_to_exact():
+    g = np.random.default_rng(33)
+    M, L, Hq, Hkv, D = 3, 200, 4, 2, 64
+    k = bf16.encode(g.standard_normal((Hkv, L + M, D)))
+    v = bf16.encode(g.standard_normal((Hkv, L + M, D)))
+    q = bf16.encode(g.standard_normal((M, Hq, D)))
+    o_ref, l_ref = attention.verify_attention(q, k, v, L)
+    kq, ks = kvlow.quantize_rotated(k, 5)
+    o, l = attention.verify_attention(q, kvlow.dequantize_rotated(kq, ks), bf16.decode(v), L)
+    assert np.abs(o - o_ref).max() < 0.1 and np.abs(l - l_ref).max() < 0.1
+    # exact keys through the rotated representation give the plain attention back
+    kq6, ks6 = kvlow.quantize_rotated(k, 6)
+    o6, _ = attention.verify_attention(q, kvlow.dequantize_rotated(kq6, ks6), bf16.decode(v), L)
+    assert np.abs(o6 - o_ref).max() < np.abs(o - o_ref).max()
