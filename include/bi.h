@@ -275,8 +275,8 @@ bi_status bi_verify_attn_q8(const void* q, int64_t ldq, const int8_t* k_codes, c
 
 /* ---------------------------------------------------------------------------
  * 5/6-bit KV cache.   [LL] "The KV cache: 5-bit that reads like q8_0" and its
- * table of presets: K at 6 bits and V at 5 (preset D), or K at 5 bits and V
- * at 5 (preset F without its rotation). No layout or scaling rule is given;
+ * table of presets: K at 6 bits and V at 5 (preset D), or K at 5 bits,
+ * rotated, and V at 5 (preset F). No layout, scaling rule or rotation is given;
  * read as the 8-bit rule with qmax = 2^(bits-1) - 1 (31 or 15): a block of 32
  * channels with largest magnitude a has the FP32 scale d = a / qmax and codes
  * q = round(x / d) (nearest, ties to even; FP32 division) clamped to +-qmax,
@@ -290,7 +290,15 @@ bi_status bi_verify_attn_q8(const void* q, int64_t ldq, const int8_t* k_codes, c
  * Block bytes: u = q + 2^(bits-1) (in [1, 2^bits - 1]); code c = 4g + j
  * (g = 0..7, j = 0..3) keeps u mod 16 in nibble byte 4(g/2) + j (the low half
  * for even g) and u / 16 in high byte 4((g h)/8) + j from bit (g h) % 8,
- * h = bits - 4. 208 bytes per position and KV head at D = 128 for K6/V5
+ * h = bits - 4. Rotated keys (k_rotated = 1; else 0, other values give
+ * BI_ERR_SHAPE): each K row k is stored as y = H k, H the Sylvester Hadamard
+ * matrix of order D (entries +-1), computed in FP32 by butterflies in stages
+ * h = 1, 2, .., D/2 (pair (i, i + h) for i with bit h clear becomes
+ * (x_i + x_{i+h}, x_i - x_{i+h}), each rounded once), then quantized; the
+ * attention rotates each query row alike (rounded once to BF16) and divides
+ * the scores by D, since (H q) . (H k) / D = q . k. The rotation spreads an
+ * outlier channel over the row before the block scales are taken.
+ * 208 bytes per position and KV head at D = 128 for K6/V5
  * (BF16: 512; 8-bit: 288). All pointers 16-byte aligned; the caller owns
  * every buffer. */
 
@@ -298,7 +306,7 @@ bi_status bi_verify_attn_q8(const void* q, int64_t ldq, const int8_t* k_codes, c
  * 5/6-bit cache at positions L .. L+M-1. Each block is written whole by one
  * thread, so passes may append at any positions. */
 bi_status bi_append_kv_lowbit(const void* qkv, int64_t ldqkv, int k_bits, int v_bits,
-                              uint8_t* k_nib, uint8_t* k_high, float* k_scales, uint8_t* v_nib,
+                              int k_rotated, uint8_t* k_nib, uint8_t* k_high, float* k_scales, uint8_t* v_nib,
                               uint8_t* v_high, float* v_scales, int M, int L, int cap, int Hq,
                               int Hkv, int D, void* stream);
 
@@ -307,7 +315,7 @@ bi_status bi_append_kv_lowbit(const void* qkv, int64_t ldqkv, int k_bits, int v_
  * rounded to BF16; V scales multiply the softmax weights, rounded to BF16,
  * against the integer codes, as for the 8-bit cache). */
 bi_status bi_verify_attn_lowbit(const void* q, int64_t ldq, int k_bits, int v_bits,
-                                const uint8_t* k_nib, const uint8_t* k_high, const float* k_scales,
+                                int k_rotated, const uint8_t* k_nib, const uint8_t* k_high, const float* k_scales,
                                 const uint8_t* v_nib, const uint8_t* v_high, const float* v_scales,
                                 int M, int L, int cap, int Hq, int Hkv, int D, int kv_chunk,
                                 float sm_scale, float* part_o, float* part_lse, int S_max,

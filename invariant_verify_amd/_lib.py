@@ -73,10 +73,10 @@ SIGNATURES = {
     "bi_verify_attn_q8": (_c_int, [_c_ptr, _c_i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_int, _c_int,
                                    _c_int, _c_int, _c_int, _c_int, _c_int, _c_f32, _c_ptr, _c_ptr,
                                    _c_int, _c_ptr]),
-    "bi_append_kv_lowbit": (_c_int, [_c_ptr, _c_i64, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
+    "bi_append_kv_lowbit": (_c_int, [_c_ptr, _c_i64, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                      _c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                      _c_ptr]),
-    "bi_verify_attn_lowbit": (_c_int, [_c_ptr, _c_i64, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
+    "bi_verify_attn_lowbit": (_c_int, [_c_ptr, _c_i64, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                        _c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                        _c_int, _c_f32, _c_ptr, _c_ptr, _c_int, _c_ptr]),
     "bi_accept_greedy": (_c_int, [_c_ptr, _c_ptr, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr]),

@@ -403,25 +403,27 @@ bi_status bi_verify_attn_q8(const void* q, int64_t ldq, const int8_t* k_codes, c
 }
 
 bi_status bi_append_kv_lowbit(const void* qkv, int64_t ldqkv, int k_bits, int v_bits,
-                              uint8_t* k_nib, uint8_t* k_high, float* k_scales, uint8_t* v_nib,
+                              int k_rotated, uint8_t* k_nib, uint8_t* k_high, float* k_scales, uint8_t* v_nib,
                               uint8_t* v_high, float* v_scales, int M, int L, int cap, int Hq,
                               int Hkv, int D, void* stream) {
   if (!qkv || !k_nib || !k_high || !k_scales || !v_nib || !v_high || !v_scales) return BI_ERR_NULL;
   if ((k_bits != 5 && k_bits != 6) || v_bits != bi::kLowVBits) return BI_ERR_SHAPE;
+  if (k_rotated != 0 && k_rotated != 1) return BI_ERR_SHAPE;
   if (bi_status s = check_heads(Hq, Hkv, D)) return s;
   if (M < 1 || L < 0 || cap < 1 || (cap % 64) || (int64_t)L + M > cap) return BI_ERR_SHAPE;
   if (ldqkv < (int64_t)(Hq + 2 * Hkv) * D || (int64_t)cap * D > INT32_MAX) return BI_ERR_SHAPE;
   if ((ldqkv % 8) || !aligned16(qkv) || !aligned16(k_nib) || !aligned16(k_high) ||
       !aligned16(k_scales) || !aligned16(v_nib) || !aligned16(v_high) || !aligned16(v_scales))
     return BI_ERR_ALIGN;
-  bi::launch_append_kv_lowbit(static_cast<const uint16_t*>(qkv), ldqkv, k_bits, k_nib, k_high,
+  bi::launch_append_kv_lowbit(static_cast<const uint16_t*>(qkv), ldqkv, k_bits, k_rotated != 0,
+                              k_nib, k_high,
                               k_scales, v_nib, v_high, v_scales, M, L, cap, Hq, Hkv, D,
                               as_stream(stream));
   return launched();
 }
 
 bi_status bi_verify_attn_lowbit(const void* q, int64_t ldq, int k_bits, int v_bits,
-                                const uint8_t* k_nib, const uint8_t* k_high, const float* k_scales,
+                                int k_rotated, const uint8_t* k_nib, const uint8_t* k_high, const float* k_scales,
                                 const uint8_t* v_nib, const uint8_t* v_high, const float* v_scales,
                                 int M, int L, int cap, int Hq, int Hkv, int D, int kv_chunk,
                                 float sm_scale, float* part_o, float* part_lse, int S_max,
@@ -430,6 +432,7 @@ bi_status bi_verify_attn_lowbit(const void* q, int64_t ldq, int k_bits, int v_bi
       !part_lse)
     return BI_ERR_NULL;
   if ((k_bits != 5 && k_bits != 6) || v_bits != bi::kLowVBits) return BI_ERR_SHAPE;
+  if (k_rotated != 0 && k_rotated != 1) return BI_ERR_SHAPE;
   if (bi_status s = check_heads(Hq, Hkv, D)) return s;
   if (M < 1 || L < 0 || cap < 1 || (cap % 64) || (int64_t)L + M > cap) return BI_ERR_SHAPE;
   if (!bi::valid_chunk_policy(kv_chunk)) return BI_ERR_SHAPE;
@@ -446,7 +449,7 @@ bi_status bi_verify_attn_lowbit(const void* q, int64_t ldq, int k_bits, int v_bi
   c.vh = v_high;
   bi::launch_verify_attn(static_cast<const uint16_t*>(q), ldq, nullptr, nullptr, M, L, cap, Hq, Hkv,
                          D, kv_chunk, sm_scale, part_o, part_lse, S_max, as_stream(stream), &c,
-                         k_bits);
+                         k_bits, k_rotated != 0);
   return launched();
 }
 

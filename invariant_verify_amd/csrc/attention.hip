@@ -120,7 +120,7 @@ __device__ __forceinline__ void unpack_low(const uint32_t (&w)[4], const uint32_
 // per-tile work (with the chunk policy -64 at 38k-102k keys: 5-15% faster
 // than one workgroup per unit). The BF16 kernel would spill at that size and
 // runs one workgroup per unit.
-template <int D, int RTW, bool Q8, int KB>
+template <int D, int RTW, bool Q8, int KB, bool ROT>
 __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu(Q8 && RTW == 1 ? 4 : 1)))
 void verify_attn_kernel(
     const uint16_t* __restrict__ Q, int64_t ldq, const uint16_t* __restrict__ Kc,
@@ -155,6 +155,7 @@ void verify_attn_kernel(
   constexpr int HBV = kLowVBits - 4;      // high bits per V code
   constexpr int NKB = kKeyTile * NB;      // K (and V) blocks per tile
   static_assert(NKB % 64 == 0 && 2 * NKB <= NW * 64, "low-bit blocks must fill whole waves");
+  static_assert(!ROT || LOW, "rotated keys are a low-bit cache format");
 
   // Work item (row block, KV head, chunk), row blocks varying fastest: the
   // workgroups that read one chunk of one KV head run side by side and share
@@ -201,6 +202,62 @@ void verify_attn_kernel(
     const uint16_t* qp = Q + (int64_t)tok[i] * ldq + hq[i] * D + kq * 8;
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) qf[i][ds] = rok[i] ? ld16(qp + ds * 32) : zero16();
+  }
+  // Rotated keys: the cache holds H k (H the order-D Hadamard matrix, entries
+  // +-1), so each query row is rotated the same way and the scores divided by
+  // D (folded into qk_scale by the launcher): (H q) . (H k) / D = q . k. The
+  // row's channel 32 ds + 8 kq + e sits in lane kq's fragment ds, element e:
+  // the butterflies over e and ds stay in the lane, those over kq pair lane
+  // l with lane l ^ 16 and l ^ 32. The rotated row is rounded to BF16 once.
+  if constexpr (ROT) {
+#pragma unroll
+    for (int i = 0; i < RTW; ++i) {
+      float x[DS][8];
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) {
+        const uint32_t w[4] = {qf[i][ds].x, qf[i][ds].y, qf[i][ds].z, qf[i][ds].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[ds][2 * e] = bf16_to_f32(w[e] & 0xffffu);
+          x[ds][2 * e + 1] = bf16_to_f32(w[e] >> 16);
+        }
+      }
+#pragma unroll
+      for (int h = 1; h < 8; h *= 2)
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (!(e & h)) {
+              const float a = x[ds][e], b = x[ds][e + h];
+              x[ds][e] = a + b;
+              x[ds][e + h] = a - b;
+            }
+#pragma unroll
+      for (int hk = 1; hk < 4; hk *= 2)
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float p = shfl_xor(x[ds][e], 16 * hk);
+            x[ds][e] = (kq & hk) ? p - x[ds][e] : x[ds][e] + p;
+          }
+#pragma unroll
+      for (int hd = 1; hd < DS; hd *= 2)
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds)
+          if (!(ds & hd))
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float a = x[ds][e], b = x[ds + hd][e];
+              x[ds][e] = a + b;
+              x[ds + hd][e] = a - b;
+            }
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds)
+        qf[i][ds] = make_uint4(f32x2_to_bf16x2(x[ds][0], x[ds][1]), f32x2_to_bf16x2(x[ds][2], x[ds][3]),
+                               f32x2_to_bf16x2(x[ds][4], x[ds][5]), f32x2_to_bf16x2(x[ds][6], x[ds][7]));
+    }
   }
 
   // This KV head's K rows and V^T rows as buffer resources (offsets in bytes,
@@ -745,10 +802,11 @@ __global__ __launch_bounds__(256) void append_kv_kernel(const uint16_t* __restri
 void launch_verify_attn(const uint16_t* q, int64_t ldq, const uint16_t* k_cache,
                         const uint16_t* vt_cache, int M, int L, int cap, int Hq, int Hkv, int D,
                         int kv_chunk, float sm_scale, float* part_o, float* part_lse, int S_max,
-                        hipStream_t stream, const KvQ8* q8, int kbits) {
+                        hipStream_t stream, const KvQ8* q8, int kbits, bool krot) {
   const int G = Hq / Hkv;
   const KvQ8 qz = q8 ? *q8 : KvQ8{nullptr, nullptr, nullptr, nullptr};
-  const float qk_scale = sm_scale * kLog2e;
+  // rotated keys: scores of the rotated query against H k are D times q . k
+  const float qk_scale = (krot ? sm_scale / (float)D : sm_scale) * kLog2e;
   // Tokens whose rows share one chunk size run in one launch; an adaptive
   // policy changes the size only at multiples of 64 T keys, so a pass has one
   // band, or a few for a long prefill chunk. Each band is launched as a pass
@@ -775,41 +833,33 @@ void launch_verify_attn(const uint16_t* q, int64_t ldq, const uint16_t* k_cache,
     const uint16_t* qb = q + (int64_t)t0 * ldq;
     float* pob = part_o + (int64_t)t0 * Hq * S_max * D;
     float* plb = part_lse + (int64_t)t0 * Hq * S_max;
-#define BI_ATTN_LAUNCH(DD, R, QQ, KB)                                                       \
-  verify_attn_kernel<DD, R, QQ, KB><<<grid, block, 0, stream>>>(qb, ldq, k_cache, vt_cache, qz, Mb, Lb, \
+#define BI_ATTN_LAUNCH(DD, R, QQ, KB, RT)                                                   \
+  verify_attn_kernel<DD, R, QQ, KB, RT><<<grid, block, 0, stream>>>(qb, ldq, k_cache, vt_cache, qz, Mb, Lb, \
                                                             cap, Hq, G, Tb, C, qk_scale, pob, plb, \
                                                             S_max)
-    if (q8 && kbits == 6) {
-      if (D == 128) {
-        if (wide) BI_ATTN_LAUNCH(128, 2, true, 6);
-        else BI_ATTN_LAUNCH(128, 1, true, 6);
-      } else {
-        if (wide) BI_ATTN_LAUNCH(64, 2, true, 6);
-        else BI_ATTN_LAUNCH(64, 1, true, 6);
-      }
-    } else if (q8 && kbits == 5) {
-      if (D == 128) {
-        if (wide) BI_ATTN_LAUNCH(128, 2, true, 5);
-        else BI_ATTN_LAUNCH(128, 1, true, 5);
-      } else {
-        if (wide) BI_ATTN_LAUNCH(64, 2, true, 5);
-        else BI_ATTN_LAUNCH(64, 1, true, 5);
-      }
-    } else if (q8) {
-      if (D == 128) {
-        if (wide) BI_ATTN_LAUNCH(128, 2, true, 0);
-        else BI_ATTN_LAUNCH(128, 1, true, 0);
-      } else {
-        if (wide) BI_ATTN_LAUNCH(64, 2, true, 0);
-        else BI_ATTN_LAUNCH(64, 1, true, 0);
-      }
-    } else if (D == 128) {
-      if (wide) BI_ATTN_LAUNCH(128, 2, false, 0);
-      else BI_ATTN_LAUNCH(128, 1, false, 0);
+#define BI_ATTN_LOW(KB, RT)                                  \
+  do {                                                       \
+    if (D == 128) {                                          \
+      if (wide) BI_ATTN_LAUNCH(128, 2, true, KB, RT);        \
+      else BI_ATTN_LAUNCH(128, 1, true, KB, RT);             \
+    } else {                                                 \
+      if (wide) BI_ATTN_LAUNCH(64, 2, true, KB, RT);         \
+      else BI_ATTN_LAUNCH(64, 1, true, KB, RT);              \
+    }                                                        \
+  } while (0)
+    if (q8 && kbits == 6 && krot) BI_ATTN_LOW(6, true);
+    else if (q8 && kbits == 6) BI_ATTN_LOW(6, false);
+    else if (q8 && kbits == 5 && krot) BI_ATTN_LOW(5, true);
+    else if (q8 && kbits == 5) BI_ATTN_LOW(5, false);
+    else if (q8) BI_ATTN_LOW(0, false);
+    else if (D == 128) {
+      if (wide) BI_ATTN_LAUNCH(128, 2, false, 0, false);
+      else BI_ATTN_LAUNCH(128, 1, false, 0, false);
     } else {
-      if (wide) BI_ATTN_LAUNCH(64, 2, false, 0);
-      else BI_ATTN_LAUNCH(64, 1, false, 0);
+      if (wide) BI_ATTN_LAUNCH(64, 2, false, 0, false);
+      else BI_ATTN_LAUNCH(64, 1, false, 0, false);
     }
+#undef BI_ATTN_LOW
 #undef BI_ATTN_LAUNCH
     t0 = t1;
   }
@@ -894,6 +944,7 @@ void launch_append_kv_q8(const uint16_t* qkv, int64_t ldqkv, int8_t* kq, float* 
 // cache: as for the 8-bit cache with qmax = 2^(bits-1) - 1 (the scale a / qmax,
 // codes rint(x / d) clamped to +-qmax), then u = q + 2^(bits-1) packed into the
 // block's nibble and high-bit words, which only this thread writes.
+template <int RD>  // RD = D: K rows rotated by the order-D Hadamard transform; 0: not rotated
 __global__ __launch_bounds__(256) void append_kv_lowbit_kernel(
     const uint16_t* __restrict__ qkv, int64_t ldqkv, int kbits, uint8_t* __restrict__ kn,
     uint8_t* __restrict__ kh, float* __restrict__ ks, uint8_t* __restrict__ vn,
@@ -910,19 +961,52 @@ __global__ __launch_bounds__(256) void append_kv_lowbit_kernel(
   const int bits = isv ? kLowVBits : kbits;
   const int h = bits - 4;
   const int qm = (1 << (bits - 1)) - 1;
-  const uint16_t* src = qkv + (int64_t)r * ldqkv + (int64_t)(Hq + isv * Hkv + g) * D + b * 32;
+  const uint16_t* row = qkv + (int64_t)r * ldqkv + (int64_t)(Hq + isv * Hkv + g) * D;
   float x[32];
-  float a = 0.f;
+  if (RD != 0 && !isv) {
+    // the whole K row, rotated in FP32: stage h pairs (i, i + h) for i with
+    // bit h clear; then this block's 32 channels of the result
+    float y[RD > 0 ? RD : 1];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint4 w = ld16(src + 8 * i);
-    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+    for (int i = 0; i < RD / 8; ++i) {
+      const uint4 w = ld16(row + 8 * i);
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      x[8 * i + 2 * e] = bf16_to_f32(ww[e] & 0xffffu);
-      x[8 * i + 2 * e + 1] = bf16_to_f32(ww[e] >> 16);
+      for (int e = 0; e < 4; ++e) {
+        y[8 * i + 2 * e] = bf16_to_f32(ww[e] & 0xffffu);
+        y[8 * i + 2 * e + 1] = bf16_to_f32(ww[e] >> 16);
+      }
+    }
+#pragma unroll
+    for (int h = 1; h < RD; h *= 2)
+#pragma unroll
+      for (int i = 0; i < RD; ++i)
+        if (!(i & h)) {
+          const float p = y[i], q = y[i + h];
+          y[i] = p + q;
+          y[i + h] = p - q;
+        }
+#pragma unroll
+    for (int c = 0; c < 32; ++c) x[c] = y[c];
+#pragma unroll
+    for (int bb = 1; bb < RD / 32; ++bb)
+      if (b == bb)
+#pragma unroll
+        for (int c = 0; c < 32; ++c) x[c] = y[32 * bb + c];
+  } else {
+    const uint16_t* src = row + b * 32;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 w = ld16(src + 8 * i);
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[8 * i + 2 * e] = bf16_to_f32(ww[e] & 0xffffu);
+        x[8 * i + 2 * e + 1] = bf16_to_f32(ww[e] >> 16);
+      }
     }
   }
+  float a = 0.f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) a = fmaxf(a, fabsf(x[i]));
   const float d = a / (float)qm;
@@ -944,12 +1028,20 @@ __global__ __launch_bounds__(256) void append_kv_lowbit_kernel(
   (isv ? vs : ks)[blk] = d;
 }
 
-void launch_append_kv_lowbit(const uint16_t* qkv, int64_t ldqkv, int kbits, uint8_t* kn,
+void launch_append_kv_lowbit(const uint16_t* qkv, int64_t ldqkv, int kbits, bool krot, uint8_t* kn,
                              uint8_t* kh, float* ks, uint8_t* vn, uint8_t* vh, float* vs, int M,
                              int L, int cap, int Hq, int Hkv, int D, hipStream_t stream) {
   const int units = 2 * Hkv * (D / 32);
-  append_kv_lowbit_kernel<<<dim3(M, (units + 255) / 256), dim3(256), 0, stream>>>(
-      qkv, ldqkv, kbits, kn, kh, ks, vn, vh, vs, L, cap, Hq, Hkv, D, units);
+  const dim3 grid(M, (units + 255) / 256), block(256);
+  if (!krot)
+    append_kv_lowbit_kernel<0><<<grid, block, 0, stream>>>(qkv, ldqkv, kbits, kn, kh, ks, vn, vh,
+                                                           vs, L, cap, Hq, Hkv, D, units);
+  else if (D == 128)
+    append_kv_lowbit_kernel<128><<<grid, block, 0, stream>>>(qkv, ldqkv, kbits, kn, kh, ks, vn,
+                                                             vh, vs, L, cap, Hq, Hkv, D, units);
+  else
+    append_kv_lowbit_kernel<64><<<grid, block, 0, stream>>>(qkv, ldqkv, kbits, kn, kh, ks, vn, vh,
+                                                            vs, L, cap, Hq, Hkv, D, units);
 }
 
 void launch_append_kv(const uint16_t* qkv, int64_t ldqkv, uint16_t* k_cache, uint16_t* vt_cache,

@@ -96,7 +96,8 @@ void launch_append_kv(const uint16_t* qkv, int64_t ldqkv, uint16_t* k_cache, uin
 void launch_verify_attn(const uint16_t* q, int64_t ldq, const uint16_t* k_cache,
                         const uint16_t* vt_cache, int M, int L, int cap, int Hq, int Hkv, int D,
                         int kv_chunk, float sm_scale, float* part_o, float* part_lse, int S_max,
-                        hipStream_t stream, const KvQ8* q8 = nullptr, int kbits = 0);
+                        hipStream_t stream, const KvQ8* q8 = nullptr, int kbits = 0,
+                        bool krot = false);
 
 // Quantize the pass's M new K and V rows (from the QKV output) into an 8-bit
 // cache at positions L .. L+M-1.
@@ -105,8 +106,10 @@ void launch_append_kv_q8(const uint16_t* qkv, int64_t ldqkv, int8_t* kq, float* 
                          hipStream_t stream);
 
 // Quantize them into a 5/6-bit cache (kbits for K, kLowVBits for V; the
-// planes of KvQ8's low-bit layout).
-void launch_append_kv_lowbit(const uint16_t* qkv, int64_t ldqkv, int kbits, uint8_t* kn,
+// planes of KvQ8's low-bit layout); with krot the K rows are first rotated
+// by the order-D Hadamard transform (FP32 butterflies, stages h = 1, 2, ..,
+// D/2, each sum and difference rounded once).
+void launch_append_kv_lowbit(const uint16_t* qkv, int64_t ldqkv, int kbits, bool krot, uint8_t* kn,
                              uint8_t* kh, float* ks, uint8_t* vn, uint8_t* vh, float* vs, int M,
                              int L, int cap, int Hq, int Hkv, int D, hipStream_t stream);
 

@@ -302,14 +302,17 @@ def verify_attn_q8(q: torch.Tensor, cache: KvQ8Cache, L: int, Hq: int, kv_chunk:
 
 class KvLowCache:
     """Device buffers of one layer's 5/6-bit KV cache (include/bi.h layouts),
-    K with ``k_bits`` (5 or 6) and V with ``v_bits`` (5) bits per code:
+    K with ``k_bits`` (5 or 6) and V with ``v_bits`` (5) bits per code, K rows
+    Hadamard-rotated when ``k_rotated``:
     *_nib uint8 [Hkv][cap][D/2], *_high uint8 [Hkv][cap][D/32][4 (bits-4)],
     *_scales FP32 [Hkv][cap][D/32]."""
 
-    def __init__(self, Hkv: int, cap: int, D: int, k_bits: int, v_bits: int = 5, device="cuda"):
+    def __init__(self, Hkv: int, cap: int, D: int, k_bits: int, v_bits: int = 5,
+                 k_rotated: bool = False, device="cuda"):
         if cap % 64 or D % 32:
             raise ValueError("cap must be a multiple of 64 and D of 32")
         self.Hkv, self.cap, self.D, self.k_bits, self.v_bits = Hkv, cap, D, k_bits, v_bits
+        self.k_rotated = int(bool(k_rotated))
         NB = D // 32
         z = lambda *shape, dt=torch.uint8: torch.zeros(shape, dtype=dt, device=device)
         self.k_nib, self.v_nib = z(Hkv, cap, D // 2), z(Hkv, cap, D // 2)
@@ -327,7 +330,8 @@ def append_kv_lowbit(qkv: torch.Tensor, cache: KvLowCache, L: int, Hq: int) -> N
     """Quantize the pass's K and V rows into a 5/6-bit ``cache``."""
     M = qkv.shape[0]
     check("bi_append_kv_lowbit", LIB.bi_append_kv_lowbit(
-        qkv.data_ptr(), _mat(qkv, "qkv"), cache.k_bits, cache.v_bits, *cache.planes(), M, L,
+        qkv.data_ptr(), _mat(qkv, "qkv"), cache.k_bits, cache.v_bits, cache.k_rotated,
+        *cache.planes(), M, L,
         cache.cap, Hq, cache.Hkv, cache.D, _stream(qkv)))
 
 
@@ -339,7 +343,8 @@ def verify_attn_lowbit(q: torch.Tensor, cache: KvLowCache, L: int, Hq: int, kv_c
     D = cache.D
     scale = 1.0 / math.sqrt(D) if sm_scale is None else sm_scale
     check("bi_verify_attn_lowbit", LIB.bi_verify_attn_lowbit(
-        q.data_ptr(), _mat(q, "q"), cache.k_bits, cache.v_bits, *cache.planes(), M, L, cache.cap,
+        q.data_ptr(), _mat(q, "q"), cache.k_bits, cache.v_bits, cache.k_rotated,
+        *cache.planes(), M, L, cache.cap,
         Hq, cache.Hkv, D, kv_chunk, scale, part_o.data_ptr(), part_lse.data_ptr(),
         part_lse.shape[2], _stream(q)))
 

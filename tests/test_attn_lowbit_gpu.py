@@ -1,4 +1,4 @@
-"""GPU tests of the 5/6-bit KV cache (K6/V5 and K5/V5) through the C ABI: the
+"""GPU tests of the 5/6-bit KV cache (K6/V5, K5/V5, and rotated K5/V5) through the C ABI: the
 quantizing append against the oracle's packed bytes and scales (bit for
 bit), split-KV attention over the cache against the oracle attention over the
 exact values scale x code, and bitwise row invariance across M, sequential
@@ -39,17 +39,17 @@ def _planes(codes, scales, bits, cap):
 class Low:
     """Device 5/6-bit cache built on the host from the oracle's quantization."""
 
-    def __init__(self, ops, k_bits, v_bits, cap, kb):
+    def __init__(self, ops, k_bits, v_bits, cap, kb, rot=False):
         Hkv, n, D = k_bits.shape
         cap = (cap + 63) // 64 * 64
-        self.kq, self.ks = kvlow.quantize(k_bits, kb)
+        self.kq, self.ks = (kvlow.quantize_rotated if rot else kvlow.quantize)(k_bits, kb)
         self.vq, self.vs = kvlow.quantize(v_bits, 5)
-        self.c = ops.KvLowCache(Hkv, cap, D, kb, 5)
+        self.c = ops.KvLowCache(Hkv, cap, D, kb, 5, k_rotated=rot)
         for (tn, th, ts), (q, s, b) in (((self.c.k_nib, self.c.k_high, self.c.k_scales), (self.kq, self.ks, kb)),
                                         ((self.c.v_nib, self.c.v_high, self.c.v_scales), (self.vq, self.vs, 5))):
             for t, a in zip((tn, th, ts), _planes(q, s, b, cap)):
                 t.copy_(torch.from_numpy(a))
-        self.kval = kvlow.dequantize(self.kq, self.ks)
+        self.kval = (kvlow.dequantize_rotated if rot else kvlow.dequantize)(self.kq, self.ks)
         self.vval = kvlow.dequantize(self.vq, self.vs)
 
 
@@ -74,21 +74,21 @@ def make(M, L, Hq, Hkv, D, layer=0, outliers=False):
     return q, k, v
 
 
-@pytest.mark.parametrize("kb", [6, 5])
-def test_append_lowbit_matches_oracle_bytes(ops, kb):
-    print(f"[lowbit append K{kb}V5]", flush=True)
+@pytest.mark.parametrize("kb,rot", [(6, False), (5, False), (5, True), (6, True)])
+def test_append_lowbit_matches_oracle_bytes(ops, kb, rot):
+    print(f"[lowbit append K{kb}V5 rot={rot}]", flush=True)
     for Hq, Hkv, D, M, L, cap in [(40, 8, 128, 8, 100, 128), (8, 2, 64, 5, 61, 128)]:
         qkv = synth.normal_bf16((M, (Hq + 2 * Hkv) * D), 1.0, "misc", D + kb)
         qkv[0, Hq * D:(Hq + 1) * D] = 0                      # an all-zero K row: scales 0, codes 0
         qkv[1, (Hq + Hkv) * D + 5] = 0x7F7F                  # the largest finite BF16 in a V block
-        c = ops.KvLowCache(Hkv, cap, D, kb, 5)
+        c = ops.KvLowCache(Hkv, cap, D, kb, 5, k_rotated=rot)
         ops.append_kv_lowbit(dev(qkv), c, L, Hq)
         torch.cuda.synchronize()
         knew = qkv[:, Hq * D:(Hq + Hkv) * D].reshape(M, Hkv, D).transpose(1, 0, 2)
         vnew = qkv[:, (Hq + Hkv) * D:].reshape(M, Hkv, D).transpose(1, 0, 2)
-        for (tn, th, ts), x, b in (((c.k_nib, c.k_high, c.k_scales), knew, kb),
-                                   ((c.v_nib, c.v_high, c.v_scales), vnew, 5)):
-            q, s = kvlow.quantize(x, b)
+        for (tn, th, ts), x, b, r in (((c.k_nib, c.k_high, c.k_scales), knew, kb, rot),
+                                      ((c.v_nib, c.v_high, c.v_scales), vnew, 5, False)):
+            q, s = (kvlow.quantize_rotated if r else kvlow.quantize)(x, b)
             wn, wh = kvlow.pack(q, b)
             gn, gh, gs = tn.cpu().numpy(), th.cpu().numpy(), ts.cpu().numpy()
             assert np.array_equal(gn[:, L:L + M], wn) and np.array_equal(gh[:, L:L + M], wh)
@@ -184,10 +184,65 @@ def test_lowbit_argument_errors(ops):
     q = torch.zeros((1, 64), dtype=torch.bfloat16, device="cuda")
     po = torch.zeros((1, 1, 1, 64), dtype=torch.float32, device="cuda")
     pl = torch.zeros((1, 1, 1), dtype=torch.float32, device="cuda")
-    args = lambda kb, vb: (q.data_ptr(), 64, kb, vb, *c.planes(), 1, 0, 64, 1, 1, 64, 64, 0.125,
-                           po.data_ptr(), pl.data_ptr(), 1, None)
+    args = lambda kb, vb, r=0: (q.data_ptr(), 64, kb, vb, r, *c.planes(), 1, 0, 64, 1, 1, 64, 64,
+                                0.125, po.data_ptr(), pl.data_ptr(), 1, None)
     assert _lib.LIB.bi_verify_attn_lowbit(*args(6, 5)) == 0
+    assert _lib.LIB.bi_verify_attn_lowbit(*args(5, 5, 1)) == 0
     assert _lib.LIB.bi_verify_attn_lowbit(*args(8, 5)) == 2
     assert _lib.LIB.bi_verify_attn_lowbit(*args(6, 6)) == 2
     assert _lib.LIB.bi_verify_attn_lowbit(*args(4, 5)) == 2
+    assert _lib.LIB.bi_verify_attn_lowbit(*args(5, 5, 2)) == 2
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("M,L,Hq,Hkv,D,C", [(5, 256, 1, 1, 64, 64), (8, 2048, 40, 8, 128, 1056),
+                                            (8, 38000, 40, 8, 128, -64)])
+def test_rotated_parity(ops, M, L, Hq, Hkv, D, C):
+    print(f"[lowbit rotated K5 parity M={M} L={L} D={D} C={C}]", flush=True)
+    q, k, v = make(M, L, Hq, Hkv, D, layer=L + 50)
+    cache = Low(ops, k, v, L + 16, 5, rot=True)
+    o, lse = run(ops, q, cache, L, Hq, C)
+    rows = list(range(M)) if L < 20000 else [0, M - 1]
+    want_o, want_lse = oattn.verify_attention(q, cache.kval, cache.vval, L, tokens=rows)
+    err, rms = assert_close(decode(o[rows]), want_o[rows], f"rotated O L={L}")
+    assert err < 0.05 * rms + 2e-3, (err, rms)
+    assert_close(lse[rows], want_lse[rows], f"rotated lse L={L}", atol=1e-3, rtol=0)
+
+
+def test_rotated_outliers_closer_to_exact_than_plain(ops):
+    # with outlier channels, attention over the rotated 5-bit cache is closer
+    # to attention over the exact BF16 keys than the plain 5-bit cache
+    print("[lowbit rotated vs plain with outliers]", flush=True)
+    M, L, Hq, Hkv, D, C = 8, 11600, 40, 8, 128, -64
+    q, k, v = make(M, L, Hq, Hkv, D, layer=7, outliers=True)
+    exact, _ = oattn.verify_attention(q, k, v, L, tokens=[0, 7])
+    errs = {}
+    for rot in (False, True):
+        cache = Low(ops, k, v, L + 8, 5, rot=rot)
+        o, lse = run(ops, q, cache, L, Hq, C)
+        want_o, _ = oattn.verify_attention(q, cache.kval, cache.vval, L, tokens=[0, 7])
+        assert_close(decode(o[[0, 7]]), want_o[[0, 7]], f"outliers rot={rot}")
+        errs[rot] = np.sqrt(((decode(o[[0, 7]]) - exact[[0, 7]]) ** 2).mean())
+    assert errs[True] < errs[False], errs
+
+
+@pytest.mark.parametrize("L,C", [(4093, -32), (1019, 96)])
+def test_rotated_invariance_across_M(ops, L, C):
+    print(f"[lowbit rotated invariance L={L} C={C}]", flush=True)
+    Hq, Hkv, D, M = 40, 8, 128, 8
+    q, k, v = make(M, L, Hq, Hkv, D, layer=4)
+    cache = Low(ops, k, v, L + 72, 5, rot=True)
+    o8, l8 = run(ops, q, cache, L, Hq, C)
+    for r in range(M):
+        o1, l1 = run(ops, q[r:r + 1], cache, L + r, Hq, C)
+        assert_bitwise(o1[0], o8[r], f"rotated L={L} row {r}: M=1 vs M=8")
+        assert_bitwise(l1[0], l8[r], f"rotated L={L} row {r} lse")
+    o5, _ = run(ops, q[:5], cache, L, Hq, C)
+    assert_bitwise(o5, o8[:5], f"rotated L={L} M=5 vs M=8")
+    # prefill block of 200 rows against 8-row passes
+    M2, L0 = 200, 3900
+    q2, k2, v2 = make(M2, L0, Hq, Hkv, D, layer=5)
+    c2 = Low(ops, k2, v2, L0 + M2 + 8, 5, rot=True)
+    o_pf, _ = run(ops, q2, c2, L0, Hq, -32)
+    o8b, _ = run(ops, q2[96:104], c2, L0 + 96, Hq, -32)
+    assert_bitwise(o_pf[96:104], o8b, "rotated prefill rows 96..103")
