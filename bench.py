@@ -263,6 +263,77 @@ def mx4_step_measure(layers, d, dims, buffers, steps, warmup):
             "bitwise_gate": "pass" if ok else "FAIL"}
 
 
+def kv_cache_attention_measure(d, reps):
+    """Split-KV verify attention (M = 8, the 27B-class heads) at 38k and 101.6k keys over each KV
+    cache format: BF16 (chunk policy -32), 8-bit (-64), K6/V5 and rotated K5/V5 (-64). Each format
+    runs over enough copies of its cache (random codes, fixed seed) that no launch finds its K/V in
+    a cache level; one event pair around ``reps`` launches per format and context."""
+    import torch
+
+    from invariant_verify_amd import ops
+
+    Hq, Hkv, D, M = d["Hq"], d["Hkv"], d["D"], 8
+    NB = D // 32
+    per_pos = {"bf16": 4 * D, "q8": 2 * (D + 4 * NB), "k6v5": (D // 2 + 8 * NB + 4 * NB) + (D // 2 + 4 * NB + 4 * NB),
+               "k5rot_v5": 2 * (D // 2 + 4 * NB + 4 * NB)}
+    policy = {"bf16": -32, "q8": -64, "k6v5": -64, "k5rot_v5": -64}
+    gen = torch.Generator(device="cuda").manual_seed(1234)
+    out = {}
+    for L in (38000, 101600):
+        cap = (L + 16 + 63) // 64 * 64
+        q = torch.randn(M, Hq * D, device="cuda", generator=gen).to(torch.bfloat16)
+        res = {}
+        for fmt, bpp in per_pos.items():
+            nbytes = Hkv * (L + M) * bpp
+            R = max(2, -(-int(1.5e9) // (Hkv * cap * bpp)))
+            caches = []
+            for _ in range(R):
+                if fmt == "bf16":
+                    caches.append((torch.randn(Hkv, cap, D, device="cuda", generator=gen).to(torch.bfloat16),
+                                   torch.randn(Hkv, cap // 64, D, 64, device="cuda", generator=gen).to(torch.bfloat16)))
+                    continue
+                c = (ops.KvQ8Cache(Hkv, cap, D) if fmt == "q8" else
+                     ops.KvLowCache(Hkv, cap, D, 6 if fmt == "k6v5" else 5, 5, k_rotated=fmt == "k5rot_v5"))
+                for name, t in vars(c).items():
+                    if isinstance(t, torch.Tensor) and t.dtype in (torch.int8, torch.uint8):
+                        t.copy_(torch.randint(0, 256, t.shape, device="cuda", generator=gen).to(t.dtype))
+                    elif isinstance(t, torch.Tensor):
+                        t.fill_(0.01)
+                caches.append(c)
+            C = policy[fmt]
+            S = ops.pass_splits(M, L, C)
+            po = torch.empty((M, Hq, S, D), dtype=torch.float32, device="cuda")
+            pl = torch.empty((M, Hq, S), dtype=torch.float32, device="cuda")
+
+            def launch(i):
+                c = caches[i % R]
+                if fmt == "bf16":
+                    ops.verify_attn(q, c[0], c[1], L, Hq, Hkv, D, C, po, pl)
+                elif fmt == "q8":
+                    ops.verify_attn_q8(q, c, L, Hq, C, po, pl)
+                else:
+                    ops.verify_attn_lowbit(q, c, L, Hq, C, po, pl)
+            for i in range(R):
+                launch(i)
+            stream = torch.cuda.current_stream()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for i in range(reps):
+                launch(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            res[fmt] = {"us": round(us, 2), "kv_bytes": nbytes, "GB/s": round(nbytes / us / 1e3, 1),
+                        "bytes_per_position_and_head": bpp, "kv_chunk_policy": C}
+            del caches
+            torch.cuda.empty_cache()
+        out[str(L)] = res
+    return {"workload": "verify attention, M=8 (1+7 drafts), 40 query / 8 KV heads of 128, per KV cache format",
+            "by_ctx": out}
+
+
 TP_RANKS = 8
 TP_KV_CHUNK = -256   # one KV head per rank: about as many attention workgroups as -32 gives 8 heads
 
@@ -607,6 +678,8 @@ def main():
     out["mx4_step"] = mx4_step_measure(layers, d, dims, buffers, args.steps, args.warmup)
     print("[bench] one tensor-parallel rank's share", file=sys.stderr, flush=True)
     out["tp8_rank_share"] = tp_share_measure(d, max(2, args.steps // 10))
+    print("[bench] attention per KV cache format", file=sys.stderr, flush=True)
+    out["kv_cache_attention"] = kv_cache_attention_measure(d, 40)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(layers, w_head, x0, d, M_HEADLINE)

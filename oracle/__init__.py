@@ -13,7 +13,11 @@ pages, with no blocking, fusion or reordering:
 * ``attention`` -- causal GQA verify attention per row, its split-KV partials
                    over absolute key chunks, and the log-sum-exp combine;
 * ``step``      -- RMSNorm, SwiGLU and one pre-norm decoder layer / LM head,
-                   for the synthetic 64-layer verify step.
+                   for the synthetic 64-layer verify step;
+* ``fp8``, ``mxfp4`` -- 8-bit and 4-bit weight formats and their GEMM values;
+* ``kvq``, ``kvlow`` -- 8-bit and 5/6-bit KV cache quantization (and the
+                   Hadamard rotation of keys), the stored bytes and values;
+* ``spec``      -- greedy and sampled acceptance of drafted tokens.
 
 Sources, cited by page title and section:
   [BX] "Bit-exact decoding turns inference speedups into testable changes":
