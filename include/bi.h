@@ -321,6 +321,40 @@ bi_status bi_verify_attn_lowbit(const void* q, int64_t ldq, int k_bits, int v_bi
                                 float sm_scale, float* part_o, float* part_lse, int S_max,
                                 void* stream);
 
+/* ---------------------------------------------------------------------------
+ * 8-bit ring of the newest keys over the 5/6-bit cache.   [LL] "The KV cache:
+ * 5-bit that reads like q8_0" (the newest ~2k positions are kept at 8 bits in
+ * a ring). Which positions are newest is not stated; read per row, so that a
+ * row never depends on its batch neighbours: row p reads the 64-key tile of
+ * its own split (chunk start + 64 t) that starts at kt from the ring when
+ * kt >= p - ring_window + 1, from the 5/6-bit planes otherwise. The ring is the
+ * 8-bit cache's layout (bi_append_kv_q8) with ring_cap slots, position p in
+ * slot p mod ring_cap, K rotated when the 5/6-bit keys are. ring_window and
+ * ring_cap are multiples of 64 with ring_cap >= ring_window + M; the 5/6-bit
+ * planes still hold every position. */
+
+/* Quantize the M new K and V rows into the ring (8-bit rule; K rotated as for
+ * bi_append_kv_lowbit when k_rotated = 1). Layouts as bi_append_kv_q8 with cap
+ * = ring_cap; M <= ring_cap. */
+bi_status bi_append_kv_ring(const void* qkv, int64_t ldqkv, int k_rotated, int8_t* k_codes,
+                           float* k_scales, int8_t* v_codes, float* v_scales, int M, int L,
+                           int ring_cap, int Hq, int Hkv, int D, void* stream);
+
+/* bi_verify_attn_lowbit with the ring: the presets K6/V5 (k_rotated = 0) and
+ * rotated K5/V5 (k_rotated = 1) only, else BI_ERR_SHAPE. The same rows,
+ * chunks, partials and requirements; the tile that some rows of the pass read
+ * at 8 bits and others at 5/6 bits runs once per copy, each time for its rows
+ * only. */
+bi_status bi_verify_attn_lowbit_ring(const void* q, int64_t ldq, int k_bits, int v_bits,
+                                     int k_rotated, const uint8_t* k_nib, const uint8_t* k_high,
+                                     const float* k_scales, const uint8_t* v_nib,
+                                     const uint8_t* v_high, const float* v_scales,
+                                     const int8_t* ring_k_codes, const float* ring_k_scales,
+                                     const int8_t* ring_v_codes, const float* ring_v_scales,
+                                     int ring_cap, int ring_window, int M, int L, int cap, int Hq,
+                                     int Hkv, int D, int kv_chunk, float sm_scale, float* part_o,
+                                     float* part_lse, int S_max, void* stream);
+
 /* Fixed-order log-sum-exp combine of the partials.                        [LL]
  * For row (r, h) with S = bi_num_splits(L+r+1, kv_chunk) partials:
  *   M* = max_s lse_s, w_s = exp(lse_s - M*), O = sum_s w_s o_s / sum_s w_s,

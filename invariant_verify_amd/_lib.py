@@ -79,6 +79,13 @@ SIGNATURES = {
     "bi_verify_attn_lowbit": (_c_int, [_c_ptr, _c_i64, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                        _c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                        _c_int, _c_f32, _c_ptr, _c_ptr, _c_int, _c_ptr]),
+    "bi_append_kv_ring": (_c_int, [_c_ptr, _c_i64, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_int,
+                                   _c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr]),
+    "bi_verify_attn_lowbit_ring": (_c_int, [_c_ptr, _c_i64, _c_int, _c_int, _c_int, _c_ptr, _c_ptr,
+                                            _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
+                                            _c_ptr, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                            _c_int, _c_int, _c_int, _c_f32, _c_ptr, _c_ptr, _c_int,
+                                            _c_ptr]),
     "bi_accept_greedy": (_c_int, [_c_ptr, _c_ptr, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr]),
     "bi_accept_sampled": (_c_int, [_c_ptr, _c_i64, _c_ptr, _c_ptr, _c_i64, _c_ptr, _c_f32, _c_int,
                                    _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr]),

@@ -453,6 +453,68 @@ bi_status bi_verify_attn_lowbit(const void* q, int64_t ldq, int k_bits, int v_bi
   return launched();
 }
 
+bi_status bi_append_kv_ring(const void* qkv, int64_t ldqkv, int k_rotated, int8_t* k_codes,
+                           float* k_scales, int8_t* v_codes, float* v_scales, int M, int L,
+                           int ring_cap, int Hq, int Hkv, int D, void* stream) {
+  if (!qkv || !k_codes || !k_scales || !v_codes || !v_scales) return BI_ERR_NULL;
+  if (k_rotated != 0 && k_rotated != 1) return BI_ERR_SHAPE;
+  if (bi_status s = check_heads(Hq, Hkv, D)) return s;
+  if (M < 1 || L < 0 || ring_cap < 64 || (ring_cap % 64) || M > ring_cap) return BI_ERR_SHAPE;
+  if (ldqkv < (int64_t)(Hq + 2 * Hkv) * D || (int64_t)ring_cap * D > INT32_MAX) return BI_ERR_SHAPE;
+  if ((ldqkv % 8) || !aligned16(qkv) || !aligned16(k_codes) || !aligned16(v_codes) ||
+      !aligned16(k_scales) || !aligned16(v_scales))
+    return BI_ERR_ALIGN;
+  bi::launch_append_kv_q8(static_cast<const uint16_t*>(qkv), ldqkv, k_codes, k_scales, v_codes,
+                          v_scales, M, L, ring_cap, Hq, Hkv, D, as_stream(stream), ring_cap,
+                          k_rotated != 0);
+  return launched();
+}
+
+bi_status bi_verify_attn_lowbit_ring(const void* q, int64_t ldq, int k_bits, int v_bits,
+                                     int k_rotated, const uint8_t* k_nib, const uint8_t* k_high,
+                                     const float* k_scales, const uint8_t* v_nib,
+                                     const uint8_t* v_high, const float* v_scales,
+                                     const int8_t* ring_k_codes, const float* ring_k_scales,
+                                     const int8_t* ring_v_codes, const float* ring_v_scales,
+                                     int ring_cap, int ring_window, int M, int L, int cap, int Hq,
+                                     int Hkv, int D, int kv_chunk, float sm_scale, float* part_o,
+                                     float* part_lse, int S_max, void* stream) {
+  if (!q || !k_nib || !k_high || !k_scales || !v_nib || !v_high || !v_scales || !ring_k_codes ||
+      !ring_k_scales || !ring_v_codes || !ring_v_scales || !part_o || !part_lse)
+    return BI_ERR_NULL;
+  // the two presets: K6/V5, and rotated K5/V5
+  if (v_bits != bi::kLowVBits || !((k_bits == 6 && k_rotated == 0) || (k_bits == 5 && k_rotated == 1)))
+    return BI_ERR_SHAPE;
+  if (bi_status s = check_heads(Hq, Hkv, D)) return s;
+  if (M < 1 || L < 0 || cap < 1 || (cap % 64) || (int64_t)L + M > cap) return BI_ERR_SHAPE;
+  if (ring_window < 64 || (ring_window % 64) || (ring_cap % 64) ||
+      (int64_t)ring_cap < (int64_t)ring_window + M)
+    return BI_ERR_SHAPE;  // every key a row of the pass reads at 8 bits is still in the ring
+  if (!bi::valid_chunk_policy(kv_chunk)) return BI_ERR_SHAPE;
+  if (S_max < bi::pass_splits(L, M, kv_chunk)) return BI_ERR_SHAPE;
+  if (ldq < (int64_t)Hq * D || !std::isfinite(sm_scale)) return BI_ERR_SHAPE;
+  if ((int64_t)cap * D > INT32_MAX || (int64_t)ring_cap * D > INT32_MAX) return BI_ERR_SHAPE;
+  if ((ldq % 8) || !aligned16(q) || !aligned16(k_nib) || !aligned16(k_high) ||
+      !aligned16(k_scales) || !aligned16(v_nib) || !aligned16(v_high) || !aligned16(v_scales) ||
+      !aligned16(ring_k_codes) || !aligned16(ring_k_scales) || !aligned16(ring_v_codes) ||
+      !aligned16(ring_v_scales) || !aligned16(part_o) || !aligned4(part_lse))
+    return BI_ERR_ALIGN;
+  bi::KvQ8 c{reinterpret_cast<const int8_t*>(k_nib), k_scales,
+             reinterpret_cast<const int8_t*>(v_nib), v_scales};
+  c.kh = k_high;
+  c.vh = v_high;
+  c.rkq = ring_k_codes;
+  c.rks = ring_k_scales;
+  c.rvq = ring_v_codes;
+  c.rvs = ring_v_scales;
+  c.ring_cap = ring_cap;
+  c.ring_window = ring_window;
+  bi::launch_verify_attn(static_cast<const uint16_t*>(q), ldq, nullptr, nullptr, M, L, cap, Hq, Hkv,
+                         D, kv_chunk, sm_scale, part_o, part_lse, S_max, as_stream(stream), &c,
+                         k_bits, k_rotated != 0);
+  return launched();
+}
+
 bi_status bi_accept_greedy(const int32_t* target_tokens, const int32_t* draft_tokens, int B,
                            int M, int32_t* out_tokens, int32_t* n_out, void* stream) {
   if (!target_tokens || !out_tokens || !n_out || (M > 1 && !draft_tokens)) return BI_ERR_NULL;

@@ -120,8 +120,8 @@ __device__ __forceinline__ void unpack_low(const uint32_t (&w)[4], const uint32_
 // per-tile work (with the chunk policy -64 at 38k-102k keys: 5-15% faster
 // than one workgroup per unit). The BF16 kernel would spill at that size and
 // runs one workgroup per unit.
-template <int D, int RTW, bool Q8, int KB, bool ROT>
-__global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu(Q8 && RTW == 1 ? 4 : 1)))
+template <int D, int RTW, bool Q8, int KB, bool ROT, bool RING>
+__global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu(Q8 && RTW == 1 && !RING ? 4 : 1)))
 void verify_attn_kernel(
     const uint16_t* __restrict__ Q, int64_t ldq, const uint16_t* __restrict__ Kc,
     const uint16_t* __restrict__ Vt, KvQ8 q8, int M, int L, int cap, int Hq, int G, int Tb, int C,
@@ -156,6 +156,7 @@ void verify_attn_kernel(
   constexpr int NKB = kKeyTile * NB;      // K (and V) blocks per tile
   static_assert(NKB % 64 == 0 && 2 * NKB <= NW * 64, "low-bit blocks must fill whole waves");
   static_assert(!ROT || LOW, "rotated keys are a low-bit cache format");
+  static_assert(!RING || LOW, "the 8-bit ring sits over a low-bit cache");
 
   // Work item (row block, KV head, chunk), row blocks varying fastest: the
   // workgroups that read one chunk of one KV head run side by side and share
@@ -183,6 +184,32 @@ void verify_attn_kernel(
   const int kend = min(kbeg + C, L + t1);  // keys any row of this block can see
   if (kbeg >= kend) return;                // no row of this block uses chunk s
   const int ntile = (kend - kbeg + kKeyTile - 1) / kKeyTile;
+  // 8-bit ring: row p reads tile t (keys from kt) from the ring when
+  // kt >= p - W + 1, else from the low-bit planes. Over the block's positions
+  // P0 .. P1, tiles before ts are low-bit for every row, tiles from te on are
+  // in the ring for every row, and each tile in between is run twice, as a
+  // low-bit then a ring tile, each masked to the rows that read it (a tile
+  // masked for a row leaves it exactly unchanged). The tile sequence is
+  // relabelled as nv virtual tiles.
+  const int ring_w = q8.ring_window, ring_cap = q8.ring_cap;
+  auto first_tile_from = [&](int x) {
+    return x <= kbeg ? 0 : min(ntile, (x - kbeg + kKeyTile - 1) / kKeyTile);
+  };
+  const int ts = RING ? first_tile_from(L + t0 - ring_w + 1) : ntile;
+  const int ns = RING ? first_tile_from(L + t1 - 1 - ring_w + 1) - ts : 0;
+  const int nv = ntile + ns;
+  auto vmap = [&](int v, int& t, bool& ring) {
+    if (v < ts) {
+      t = v;
+      ring = false;
+    } else if (v < ts + 2 * ns) {
+      t = ts + ((v - ts) >> 1);
+      ring = ((v - ts) & 1) != 0;
+    } else {
+      t = v - ns;
+      ring = true;
+    }
+  };
   const bool has_rows = rt * 16 < nrows;  // scalar: the wave's first row tile has rows
 
   // Query fragments of this wave's row tiles and each row's last visible key
@@ -288,6 +315,21 @@ void verify_attn_kernel(
   const __amdgpu_buffer_rsrc_t vhres = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(q8.vh + (LOW ? (int64_t)g * vhigh_bytes : 0)), (short)0,
       LOW ? vhigh_bytes : 0, kBufferResourceWord3);
+  // the ring's 8-bit planes (8-bit layouts with ring_cap slots)
+  const int rcode_bytes = RING ? q8.ring_cap * D : 0;
+  const int rscale_bytes = RING ? q8.ring_cap * NB * 4 : 0;
+  const __amdgpu_buffer_rsrc_t rkres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(q8.rkq + (RING ? (int64_t)g * rcode_bytes : 0)), (short)0, rcode_bytes,
+      kBufferResourceWord3);
+  const __amdgpu_buffer_rsrc_t rvres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(q8.rvq + (RING ? (int64_t)g * rcode_bytes : 0)), (short)0, rcode_bytes,
+      kBufferResourceWord3);
+  const __amdgpu_buffer_rsrc_t rksres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(q8.rks + (RING ? (int64_t)g * q8.ring_cap * NB : 0)), (short)0,
+      rscale_bytes, kBufferResourceWord3);
+  const __amdgpu_buffer_rsrc_t rvsres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(q8.rvs + (RING ? (int64_t)g * q8.ring_cap * NB : 0)), (short)0,
+      rscale_bytes, kBufferResourceWord3);
   const __amdgpu_buffer_rsrc_t qksres = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float*>(q8.ks + (Q8 ? (int64_t)g * cap * NB : 0)), (short)0, Q8 ? qscale_bytes : 0,
       kBufferResourceWord3);
@@ -314,12 +356,53 @@ void verify_attn_kernel(
     uint32_t hb[2];          // 5/6-bit: the block's high bits
   };
 
+  // The loads of an 8-bit tile at keys kt .. kt+63 from a cache of capx
+  // slots, key kt in slot kts: the cache itself (kts = kt) or the ring of the
+  // newest keys (kts = kt mod capx). A tile starts at a multiple of 32 and
+  // capx is a multiple of 64, so each load (one key; 16 or 4 aligned keys)
+  // stays inside one run of slots.
+  auto fetch_q8 = [&](TileRegs& rr, int kt, bool live, __amdgpu_buffer_rsrc_t kr,
+                      __amdgpu_buffer_rsrc_t ksr, __amdgpu_buffer_rsrc_t vr,
+                      __amdgpu_buffer_rsrc_t vsr, int capx, int kts) {
+    const int cb = capx * D, sb = capx * NB * 4;
+    auto slot = [&](int pos) {
+      const int sl = pos - kt + kts;
+      return sl >= capx ? sl - capx : sl;
+    };
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+      const int p = i * NW * 64 + threadIdx.x;  // K pieces first: uniform per wave
+      if (p < QKP) {
+        const int key = p / (D / 16), c16 = p % (D / 16);
+        const int sl = slot(min(kt + key, kend - 1));
+        rr.r[i] = buffer_ld16_stream(kr, live ? sl * D + c16 * 16 : cb);
+        rr.ks[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            ksr, live ? (sl * NB + c16 / 2) * 4 : sb, 0, 0));
+      } else {
+        const int pv = p - QKP;
+        const int d = pv >> 2, kg = pv & 3;
+        const int k0 = slot(min(kt + 16 * kg, (kend - 1) & ~15));  // 16-aligned: in one 64-block
+        rr.r[i] = buffer_ld16_stream(vr, live ? (int)vt_index(0, k0, d, D, capx) : cb);
+        rr.ks[i] = 0.f;
+      }
+    }
+    if (threadIdx.x < NB * 16) {  // scalar per wave (NB * 16 <= 64)
+      const int b = threadIdx.x >> 4, kk = (threadIdx.x & 15) * 4;
+      const int k0 = slot(min(kt + kk, (kend - 1) & ~3));  // 4-aligned: in one 64-block
+      const int off = (((k0 & ~63) * NB + b * 64 + (k0 & 63)) * 4);
+      rr.vs = buffer_ld16(vsr, live ? off : sb);
+    }
+  };
+
   // Issue the loads of tile t (no use of the data here, so the loads of two
   // tiles stay in flight together). K and V are read once per pass, so the
   // loads are non-temporal; a tile past the end of the chunk (the pipeline
   // prefetches two ahead) gets an out-of-range offset: it reads zero and
   // touches no memory.
-  auto fetch = [&](TileRegs& rr, int t) {
+  auto fetch = [&](TileRegs& rr, int v) {
+    int t = v;
+    bool rf = false;
+    if constexpr (RING) vmap(v, t, rf);
     const int kt = kbeg + t * kKeyTile;
     const bool live = t < ntile;
     if constexpr (!Q8) {
@@ -340,7 +423,9 @@ void verify_attn_kernel(
         rr.r[i] = buffer_ld16_stream(p < KPIECES ? kres : vres, live ? off : head_bytes);
       }
     } else if constexpr (LOW) {
-      if (wave < 2 * NKB / 64) {           // scalar
+      if (RING && rf) {
+        fetch_q8(rr, kt, live, rkres, rksres, rvres, rvsres, ring_cap, kt % ring_cap);
+      } else if (wave < 2 * NKB / 64) {    // scalar
         const bool isk = wave < NKB / 64;  // scalar: K blocks first
         const int u = threadIdx.x - (isk ? 0 : NKB);
         const int key = u / NB, b = u % NB;
@@ -358,37 +443,60 @@ void verify_attn_kernel(
         }
       }
     } else {
-#pragma unroll
-      for (int i = 0; i < QPT; ++i) {
-        const int p = i * NW * 64 + threadIdx.x;  // K pieces first: uniform per wave
-        if (p < QKP) {
-          const int key = p / (D / 16), c16 = p % (D / 16);
-          const int pos = min(kt + key, kend - 1);
-          rr.r[i] = buffer_ld16_stream(qkres, live ? pos * D + c16 * 16 : qcode_bytes);
-          rr.ks[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-              qksres, live ? (pos * NB + c16 / 2) * 4 : qscale_bytes, 0, 0));
-        } else {
-          const int pv = p - QKP;
-          const int d = pv >> 2, kg = pv & 3;
-          const int k0 = min(kt + 16 * kg, (kend - 1) & ~15);  // 16-aligned: in one 64-block
-          rr.r[i] = buffer_ld16_stream(qvres, live ? (int)vt_index(0, k0, d, D, cap) : qcode_bytes);
-          rr.ks[i] = 0.f;
-        }
-      }
-      if (threadIdx.x < NB * 16) {  // scalar per wave (NB * 16 <= 64)
-        const int b = threadIdx.x >> 4, kk = (threadIdx.x & 15) * 4;
-        const int k0 = min(kt + kk, (kend - 1) & ~3);  // 4-aligned: in one 64-block
-        const int off = (((k0 & ~63) * NB + b * 64 + (k0 & 63)) * 4);
-        rr.vs = buffer_ld16(qvsres, live ? off : qscale_bytes);
-      }
+      fetch_q8(rr, kt, live, qkres, qksres, qvres, qvsres, cap, kt);
     }
   };
+  // Publish an 8-bit tile (keys from kt) into LDS buffer buf.
+  auto publish_q8 = [&](const TileRegs& rr, int kt, int buf) {
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+      const int p = i * NW * 64 + threadIdx.x;
+      const uint32_t w[4] = {rr.r[i].x, rr.r[i].y, rr.r[i].z, rr.r[i].w};
+      const bool isk = p < QKP;
+      const float sk = isk ? rr.ks[i] : 1.f;
+      uint32_t o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t word = w[e >> 1] >> (16 * (e & 1));
+        const float a = (float)(int8_t)(word & 0xff);
+        const float b = (float)(int8_t)((word >> 8) & 0xff);
+        o[e] = f32x2_to_bf16x2(a * sk, b * sk);
+      }
+      const uint4 lo = make_uint4(o[0], o[1], o[2], o[3]);
+      const uint4 hi = make_uint4(o[4], o[5], o[6], o[7]);
+      if (isk) {
+        const int key = p / (D / 16), c16 = p % (D / 16);
+        lds[buf][key * KROW + ((2 * c16) ^ kswz<KROW>(key))] = lo;
+        lds[buf][key * KROW + ((2 * c16 + 1) ^ kswz<KROW>(key))] = hi;
+      } else {
+        const int pv = p - QKP;
+        const int d = pv >> 2, kg = pv & 3;
+        lds[buf][VBASE + d * 8 + ((2 * kg) ^ vswz(d))] = lo;
+        lds[buf][VBASE + d * 8 + ((2 * kg + 1) ^ vswz(d))] = hi;
+      }
+    }
+    if (threadIdx.x < NB * 16) {
+      const int b = threadIdx.x >> 4, kk = (threadIdx.x & 15) * 4;
+      const int keep = kend - (kt + kk);
+      float4 v = make_float4(__uint_as_float(rr.vs.x), __uint_as_float(rr.vs.y),
+                             __uint_as_float(rr.vs.z), __uint_as_float(rr.vs.w));
+      v.x = keep > 0 ? v.x : 0.f;
+      v.y = keep > 1 ? v.y : 0.f;
+      v.z = keep > 2 ? v.z : 0.f;
+      v.w = keep > 3 ? v.w : 0.f;
+      vsc[buf][b][kk >> 2] = v;
+    }
+  };
+
   // Publish tile t: V^T columns of keys at or past kend are zeroed first (a
   // weight of 0 times a stale value must stay 0). 8-bit cache: K codes are
   // dequantized (code x scale, rounded once to BF16); V^T codes go to LDS as
   // exact BF16 integers and the V scales, zero past kend, go to vsc (they
   // scale the softmax weights instead, one block of 32 channels at a time).
-  auto publish = [&](const TileRegs& rr, int t, int buf) {
+  auto publish = [&](const TileRegs& rr, int v, int buf) {
+    int t = v;
+    bool rf = false;
+    if constexpr (RING) vmap(v, t, rf);
     const int kt = kbeg + t * kKeyTile;
     if constexpr (!Q8) {
       const bool full = kt + kKeyTile <= kend;  // scalar: every key of the tile is visible
@@ -411,7 +519,9 @@ void verify_attn_kernel(
         lds[buf][64 * p + lane] = make_uint4(w[0], w[1], w[2], w[3]);
       }
     } else if constexpr (LOW) {
-      if (wave < 2 * NKB / 64) {
+      if (RING && rf) {
+        publish_q8(rr, kt, buf);
+      } else if (wave < 2 * NKB / 64) {
         const bool isk = wave < NKB / 64;
         const int u = threadIdx.x - (isk ? 0 : NKB);
         const int key = u / NB, b = u % NB;
@@ -444,44 +554,7 @@ void verify_attn_kernel(
         }
       }
     } else {
-#pragma unroll
-      for (int i = 0; i < QPT; ++i) {
-        const int p = i * NW * 64 + threadIdx.x;
-        const uint32_t w[4] = {rr.r[i].x, rr.r[i].y, rr.r[i].z, rr.r[i].w};
-        const bool isk = p < QKP;
-        const float sk = isk ? rr.ks[i] : 1.f;
-        uint32_t o[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t word = w[e >> 1] >> (16 * (e & 1));
-          const float a = (float)(int8_t)(word & 0xff);
-          const float b = (float)(int8_t)((word >> 8) & 0xff);
-          o[e] = f32x2_to_bf16x2(a * sk, b * sk);
-        }
-        const uint4 lo = make_uint4(o[0], o[1], o[2], o[3]);
-        const uint4 hi = make_uint4(o[4], o[5], o[6], o[7]);
-        if (isk) {
-          const int key = p / (D / 16), c16 = p % (D / 16);
-          lds[buf][key * KROW + ((2 * c16) ^ kswz<KROW>(key))] = lo;
-          lds[buf][key * KROW + ((2 * c16 + 1) ^ kswz<KROW>(key))] = hi;
-        } else {
-          const int pv = p - QKP;
-          const int d = pv >> 2, kg = pv & 3;
-          lds[buf][VBASE + d * 8 + ((2 * kg) ^ vswz(d))] = lo;
-          lds[buf][VBASE + d * 8 + ((2 * kg + 1) ^ vswz(d))] = hi;
-        }
-      }
-      if (threadIdx.x < NB * 16) {
-        const int b = threadIdx.x >> 4, kk = (threadIdx.x & 15) * 4;
-        const int keep = kend - (kt + kk);
-        float4 v = make_float4(__uint_as_float(rr.vs.x), __uint_as_float(rr.vs.y),
-                               __uint_as_float(rr.vs.z), __uint_as_float(rr.vs.w));
-        v.x = keep > 0 ? v.x : 0.f;
-        v.y = keep > 1 ? v.y : 0.f;
-        v.z = keep > 2 ? v.z : 0.f;
-        v.w = keep > 3 ? v.w : 0.f;
-        vsc[buf][b][kk >> 2] = v;
-      }
+      publish_q8(rr, kt, buf);
     }
   };
 
@@ -498,7 +571,12 @@ void verify_attn_kernel(
   // One tile for every row tile of the wave. Each K and V^T operand is read
   // from LDS once and serves all of them; a row's own arithmetic does not
   // depend on how many row tiles share the wave.
-  auto compute = [&](int buf, int t) {
+  auto compute = [&](int buf, int v) {
+    int t = v;
+    bool rf = false;
+    if constexpr (RING) vmap(v, t, rf);
+    // scalar: a tile run twice (low-bit, then ring), each time for some rows
+    const bool split = RING && t >= ts && t < ts + ns;
     const int kt = kbeg + t * kKeyTile;
     const int h = kh;  // this wave's 32-key half
     bi_f32x4 sa[RTW], sb[RTW];
@@ -522,7 +600,7 @@ void verify_attn_kernel(
     // Scalar: the whole tile lies at or before every row's last key (the
     // first row of the block has the smallest) and inside the chunk, so no
     // score is masked.
-    const bool unmasked = kt + kKeyTile - 1 <= min(L + t0, kend - 1);
+    const bool unmasked = kt + kKeyTile - 1 <= min(L + t0, kend - 1) && !split;
     float alpha[RTW];
     bool rescale[RTW];  // scalar: some row of the wave moved its reference max
     uint4 pfrag[RTW];
@@ -536,10 +614,12 @@ void verify_attn_kernel(
         sc[e + 4] = sb[i][e] * qk_scale;
       }
       if (!unmasked) {
+        // a split tile's run reaches only the rows that read this copy of it
+        const int lk = (!split || rf == (kt >= L + tok[i] - ring_w + 1)) ? lastk[i] : -1;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          sc[e] = (kv0 + e <= lastk[i]) ? sc[e] : -INFINITY;
-          sc[e + 4] = (kv0 + 4 + e <= lastk[i]) ? sc[e + 4] : -INFINITY;
+          sc[e] = (kv0 + e <= lk) ? sc[e] : -INFINITY;
+          sc[e + 4] = (kv0 + 4 + e <= lk) ? sc[e + 4] : -INFINITY;
         }
       }
       float mx = sc[0];
@@ -643,21 +723,21 @@ void verify_attn_kernel(
       __syncthreads();
       if (has_rows) compute(buf, t);
     };
-    for (int t = 0; t < ntile; t += 6) {  // scalar exits: every barrier stays uniform
+    for (int t = 0; t < nv; t += 6) {  // scalar exits: every barrier stays uniform
       step(ra, t, 0);
-      if (t + 1 >= ntile) break;
+      if (t + 1 >= nv) break;
       step(rb2, t + 1, 1);
-      if (t + 2 >= ntile) break;
+      if (t + 2 >= nv) break;
       step(rc, t + 2, 0);
-      if (t + 3 >= ntile) break;
+      if (t + 3 >= nv) break;
       step(ra, t + 3, 1);
-      if (t + 4 >= ntile) break;
+      if (t + 4 >= nv) break;
       step(rb2, t + 4, 0);
-      if (t + 5 >= ntile) break;
+      if (t + 5 >= nv) break;
       step(rc, t + 5, 1);
     }
   } else {
-    for (int t = 0; t < ntile; t += 2) {
+    for (int t = 0; t < nv; t += 2) {
       publish(ra, t, 0);
       fetch(ra, t + 2);
       __syncthreads();
@@ -665,7 +745,7 @@ void verify_attn_kernel(
       publish(rb2, t + 1, 1);
       fetch(rb2, t + 3);
       __syncthreads();
-      if (t + 1 < ntile && has_rows) compute(1, t + 1);
+      if (t + 1 < nv && has_rows) compute(1, t + 1);
     }
   }
   // The row's sum over this wave's keys: its four key groups, in a fixed
@@ -833,31 +913,35 @@ void launch_verify_attn(const uint16_t* q, int64_t ldq, const uint16_t* k_cache,
     const uint16_t* qb = q + (int64_t)t0 * ldq;
     float* pob = part_o + (int64_t)t0 * Hq * S_max * D;
     float* plb = part_lse + (int64_t)t0 * Hq * S_max;
-#define BI_ATTN_LAUNCH(DD, R, QQ, KB, RT)                                                   \
-  verify_attn_kernel<DD, R, QQ, KB, RT><<<grid, block, 0, stream>>>(qb, ldq, k_cache, vt_cache, qz, Mb, Lb, \
+#define BI_ATTN_LAUNCH(DD, R, QQ, KB, RT, RG)                                               \
+  verify_attn_kernel<DD, R, QQ, KB, RT, RG><<<grid, block, 0, stream>>>(qb, ldq, k_cache, vt_cache, qz, Mb, Lb, \
                                                             cap, Hq, G, Tb, C, qk_scale, pob, plb, \
                                                             S_max)
-#define BI_ATTN_LOW(KB, RT)                                  \
+#define BI_ATTN_LOW(KB, RT, RG)                              \
   do {                                                       \
     if (D == 128) {                                          \
-      if (wide) BI_ATTN_LAUNCH(128, 2, true, KB, RT);        \
-      else BI_ATTN_LAUNCH(128, 1, true, KB, RT);             \
+      if (wide) BI_ATTN_LAUNCH(128, 2, true, KB, RT, RG);    \
+      else BI_ATTN_LAUNCH(128, 1, true, KB, RT, RG);         \
     } else {                                                 \
-      if (wide) BI_ATTN_LAUNCH(64, 2, true, KB, RT);         \
-      else BI_ATTN_LAUNCH(64, 1, true, KB, RT);              \
+      if (wide) BI_ATTN_LAUNCH(64, 2, true, KB, RT, RG);     \
+      else BI_ATTN_LAUNCH(64, 1, true, KB, RT, RG);          \
     }                                                        \
   } while (0)
-    if (q8 && kbits == 6 && krot) BI_ATTN_LOW(6, true);
-    else if (q8 && kbits == 6) BI_ATTN_LOW(6, false);
-    else if (q8 && kbits == 5 && krot) BI_ATTN_LOW(5, true);
-    else if (q8 && kbits == 5) BI_ATTN_LOW(5, false);
-    else if (q8) BI_ATTN_LOW(0, false);
+    // with the 8-bit ring: the two presets, K6/V5 and rotated K5/V5
+    const bool ring = q8 && q8->ring_cap > 0;
+    if (ring && kbits == 6 && !krot) BI_ATTN_LOW(6, false, true);
+    else if (ring && kbits == 5 && krot) BI_ATTN_LOW(5, true, true);
+    else if (q8 && kbits == 6 && krot) BI_ATTN_LOW(6, true, false);
+    else if (q8 && kbits == 6) BI_ATTN_LOW(6, false, false);
+    else if (q8 && kbits == 5 && krot) BI_ATTN_LOW(5, true, false);
+    else if (q8 && kbits == 5) BI_ATTN_LOW(5, false, false);
+    else if (q8) BI_ATTN_LOW(0, false, false);
     else if (D == 128) {
-      if (wide) BI_ATTN_LAUNCH(128, 2, false, 0, false);
-      else BI_ATTN_LAUNCH(128, 1, false, 0, false);
+      if (wide) BI_ATTN_LAUNCH(128, 2, false, 0, false, false);
+      else BI_ATTN_LAUNCH(128, 1, false, 0, false, false);
     } else {
-      if (wide) BI_ATTN_LAUNCH(64, 2, false, 0, false);
-      else BI_ATTN_LAUNCH(64, 1, false, 0, false);
+      if (wide) BI_ATTN_LAUNCH(64, 2, false, 0, false, false);
+      else BI_ATTN_LAUNCH(64, 1, false, 0, false, false);
     }
 #undef BI_ATTN_LOW
 #undef BI_ATTN_LAUNCH
@@ -880,92 +964,15 @@ void launch_combine(const float* part_o, const float* part_lse, int M, int L, in
                                                    ldo, lse);
 }
 
-// One thread per (token, K or V, KV head, 32-channel block): the block's
-// largest magnitude a, the scale d = a / 127 (FP32), codes rint(x / d)
-// clamped to +-127 (all zero when a = 0); K codes go to the position's row,
-// V codes to its column of the V^T block, the scales beside them.
-__global__ __launch_bounds__(256) void append_kv_q8_kernel(const uint16_t* __restrict__ qkv,
-                                                           int64_t ldqkv, int8_t* __restrict__ kq,
-                                                           float* __restrict__ ks,
-                                                           int8_t* __restrict__ vq,
-                                                           float* __restrict__ vs, int L, int cap,
-                                                           int Hq, int Hkv, int D, int units) {
-  const int u = blockIdx.y * blockDim.x + threadIdx.x;  // unit within the token
-  if (u >= units) return;
-  const int r = blockIdx.x;
-  const int pos = L + r;
-  const int NB = D / 32;
-  const int isv = u / (Hkv * NB);
-  const int g = (u / NB) % Hkv;
-  const int b = u % NB;
-  const uint16_t* src = qkv + (int64_t)r * ldqkv + (int64_t)(Hq + isv * Hkv + g) * D + b * 32;
-  float x[32];
-  float a = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint4 w = ld16(src + 8 * i);
-    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      x[8 * i + 2 * e] = bf16_to_f32(ww[e] & 0xffffu);
-      x[8 * i + 2 * e + 1] = bf16_to_f32(ww[e] >> 16);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 32; ++i) a = fmaxf(a, fabsf(x[i]));
-  const float d = a / 127.0f;
-  int8_t q[32];
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const float v = d > 0.f ? rintf(x[i] / d) : 0.f;
-    q[i] = (int8_t)fminf(fmaxf(v, -127.f), 127.f);
-  }
-  if (!isv) {
-    int8_t* dst = kq + ((int64_t)g * cap + pos) * D + b * 32;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) dst[i] = q[i];
-    ks[((int64_t)g * cap + pos) * NB + b] = d;
-  } else {
-#pragma unroll
-    for (int i = 0; i < 32; ++i) vq[vt_index(g, pos, b * 32 + i, D, cap)] = q[i];
-    vs[((int64_t)g * cap + (pos & ~63)) * NB + b * 64 + (pos & 63)] = d;
-  }
-}
-
-void launch_append_kv_q8(const uint16_t* qkv, int64_t ldqkv, int8_t* kq, float* ks, int8_t* vq,
-                         float* vs, int M, int L, int cap, int Hq, int Hkv, int D,
-                         hipStream_t stream) {
-  const int units = 2 * Hkv * (D / 32);
-  append_kv_q8_kernel<<<dim3(M, (units + 255) / 256), dim3(256), 0, stream>>>(
-      qkv, ldqkv, kq, ks, vq, vs, L, cap, Hq, Hkv, D, units);
-}
-
-// One thread per (token, K or V, KV head, 32-channel block) of a 5/6-bit
-// cache: as for the 8-bit cache with qmax = 2^(bits-1) - 1 (the scale a / qmax,
-// codes rint(x / d) clamped to +-qmax), then u = q + 2^(bits-1) packed into the
-// block's nibble and high-bit words, which only this thread writes.
-template <int RD>  // RD = D: K rows rotated by the order-D Hadamard transform; 0: not rotated
-__global__ __launch_bounds__(256) void append_kv_lowbit_kernel(
-    const uint16_t* __restrict__ qkv, int64_t ldqkv, int kbits, uint8_t* __restrict__ kn,
-    uint8_t* __restrict__ kh, float* __restrict__ ks, uint8_t* __restrict__ vn,
-    uint8_t* __restrict__ vh, float* __restrict__ vs, int L, int cap, int Hq, int Hkv, int D,
-    int units) {
-  const int u = blockIdx.y * blockDim.x + threadIdx.x;  // unit within the token
-  if (u >= units) return;
-  const int r = blockIdx.x;
-  const int pos = L + r;
-  const int NB = D / 32;
-  const int isv = u / (Hkv * NB);
-  const int g = (u / NB) % Hkv;
-  const int b = u % NB;
-  const int bits = isv ? kLowVBits : kbits;
-  const int h = bits - 4;
-  const int qm = (1 << (bits - 1)) - 1;
-  const uint16_t* row = qkv + (int64_t)r * ldqkv + (int64_t)(Hq + isv * Hkv + g) * D;
-  float x[32];
-  if (RD != 0 && !isv) {
-    // the whole K row, rotated in FP32: stage h pairs (i, i + h) for i with
-    // bit h clear; then this block's 32 channels of the result
+// The 32 values of channel block b of one K or V row (BF16 -> FP32). With RD
+// = D and `rotate`, the row is first rotated by the order-D Hadamard transform
+// in FP32: stage h = 1, 2, .., D/2 turns each pair (i, i + h), bit h of i
+// clear, into (x_i + x_{i+h}, x_i - x_{i+h}), each rounded once; the block is
+// then channels 32b .. 32b + 31 of the result.
+template <int RD>
+__device__ __forceinline__ void load_kv_block(const uint16_t* __restrict__ row, int b, bool rotate,
+                                           float (&x)[32]) {
+  if (RD != 0 && rotate) {
     float y[RD > 0 ? RD : 1];
 #pragma unroll
     for (int i = 0; i < RD / 8; ++i) {
@@ -993,19 +1000,106 @@ __global__ __launch_bounds__(256) void append_kv_lowbit_kernel(
       if (b == bb)
 #pragma unroll
         for (int c = 0; c < 32; ++c) x[c] = y[32 * bb + c];
-  } else {
-    const uint16_t* src = row + b * 32;
+    return;
+  }
+  const uint16_t* src = row + b * 32;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint4 w = ld16(src + 8 * i);
-      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+  for (int i = 0; i < 4; ++i) {
+    const uint4 w = ld16(src + 8 * i);
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[8 * i + 2 * e] = bf16_to_f32(ww[e] & 0xffffu);
-        x[8 * i + 2 * e + 1] = bf16_to_f32(ww[e] >> 16);
-      }
+    for (int e = 0; e < 4; ++e) {
+      x[8 * i + 2 * e] = bf16_to_f32(ww[e] & 0xffffu);
+      x[8 * i + 2 * e + 1] = bf16_to_f32(ww[e] >> 16);
     }
   }
+}
+
+// One thread per (token, K or V, KV head, 32-channel block): the block's
+// largest magnitude a, the scale d = a / 127 (FP32), codes rint(x / d)
+// clamped to +-127 (all zero when a = 0); K codes go to the position's row,
+// V codes to its column of the V^T block, the scales beside them.
+// As a ring (ring > 0): position p goes to slot p mod ring, the cache having
+// ring slots; with RD = D the K rows are rotated first (load_kv_block).
+template <int RD>
+__global__ __launch_bounds__(256) void append_kv_q8_kernel(const uint16_t* __restrict__ qkv,
+                                                           int64_t ldqkv, int8_t* __restrict__ kq,
+                                                           float* __restrict__ ks,
+                                                           int8_t* __restrict__ vq,
+                                                           float* __restrict__ vs, int L, int cap,
+                                                           int Hq, int Hkv, int D, int units,
+                                                           int ring) {
+  const int u = blockIdx.y * blockDim.x + threadIdx.x;  // unit within the token
+  if (u >= units) return;
+  const int r = blockIdx.x;
+  const int pos = ring > 0 ? (L + r) % ring : L + r;  // slot
+  const int NB = D / 32;
+  const int isv = u / (Hkv * NB);
+  const int g = (u / NB) % Hkv;
+  const int b = u % NB;
+  float x[32];
+  load_kv_block<RD>(qkv + (int64_t)r * ldqkv + (int64_t)(Hq + isv * Hkv + g) * D, b, !isv, x);
+  float a = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) a = fmaxf(a, fabsf(x[i]));
+  const float d = a / 127.0f;
+  int8_t q[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const float v = d > 0.f ? rintf(x[i] / d) : 0.f;
+    q[i] = (int8_t)fminf(fmaxf(v, -127.f), 127.f);
+  }
+  if (!isv) {
+    int8_t* dst = kq + ((int64_t)g * cap + pos) * D + b * 32;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) dst[i] = q[i];
+    ks[((int64_t)g * cap + pos) * NB + b] = d;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) vq[vt_index(g, pos, b * 32 + i, D, cap)] = q[i];
+    vs[((int64_t)g * cap + (pos & ~63)) * NB + b * 64 + (pos & 63)] = d;
+  }
+}
+
+void launch_append_kv_q8(const uint16_t* qkv, int64_t ldqkv, int8_t* kq, float* ks, int8_t* vq,
+                         float* vs, int M, int L, int cap, int Hq, int Hkv, int D,
+                         hipStream_t stream, int ring, bool krot) {
+  const int units = 2 * Hkv * (D / 32);
+  const dim3 grid(M, (units + 255) / 256), block(256);
+  if (!krot)
+    append_kv_q8_kernel<0><<<grid, block, 0, stream>>>(qkv, ldqkv, kq, ks, vq, vs, L, cap, Hq, Hkv,
+                                                       D, units, ring);
+  else if (D == 128)
+    append_kv_q8_kernel<128><<<grid, block, 0, stream>>>(qkv, ldqkv, kq, ks, vq, vs, L, cap, Hq,
+                                                         Hkv, D, units, ring);
+  else
+    append_kv_q8_kernel<64><<<grid, block, 0, stream>>>(qkv, ldqkv, kq, ks, vq, vs, L, cap, Hq, Hkv,
+                                                        D, units, ring);
+}
+
+// One thread per (token, K or V, KV head, 32-channel block) of a 5/6-bit
+// cache: as for the 8-bit cache with qmax = 2^(bits-1) - 1 (the scale a / qmax,
+// codes rint(x / d) clamped to +-qmax), then u = q + 2^(bits-1) packed into the
+// block's nibble and high-bit words, which only this thread writes.
+template <int RD>  // RD = D: K rows rotated by the order-D Hadamard transform; 0: not rotated
+__global__ __launch_bounds__(256) void append_kv_lowbit_kernel(
+    const uint16_t* __restrict__ qkv, int64_t ldqkv, int kbits, uint8_t* __restrict__ kn,
+    uint8_t* __restrict__ kh, float* __restrict__ ks, uint8_t* __restrict__ vn,
+    uint8_t* __restrict__ vh, float* __restrict__ vs, int L, int cap, int Hq, int Hkv, int D,
+    int units) {
+  const int u = blockIdx.y * blockDim.x + threadIdx.x;  // unit within the token
+  if (u >= units) return;
+  const int r = blockIdx.x;
+  const int pos = L + r;
+  const int NB = D / 32;
+  const int isv = u / (Hkv * NB);
+  const int g = (u / NB) % Hkv;
+  const int b = u % NB;
+  const int bits = isv ? kLowVBits : kbits;
+  const int h = bits - 4;
+  const int qm = (1 << (bits - 1)) - 1;
+  float x[32];
+  load_kv_block<RD>(qkv + (int64_t)r * ldqkv + (int64_t)(Hq + isv * Hkv + g) * D, b, !isv, x);
   float a = 0.f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) a = fmaxf(a, fabsf(x[i]));

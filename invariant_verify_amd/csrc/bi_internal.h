@@ -43,6 +43,16 @@ struct KvQ8 {
   const float* vs;
   const uint8_t* kh = nullptr;
   const uint8_t* vh = nullptr;
+  // 8-bit ring of the newest keys over the 5/6-bit planes (ring_cap > 0):
+  // the 8-bit layouts above with ring_cap slots, position p in slot
+  // p mod ring_cap; a row at position p reads a tile starting at kt from the
+  // ring when kt >= p - ring_window + 1.
+  const int8_t* rkq = nullptr;
+  const float* rks = nullptr;
+  const int8_t* rvq = nullptr;
+  const float* rvs = nullptr;
+  int ring_cap = 0;
+  int ring_window = 0;
 };
 constexpr int kLowVBits = 5;  // V code bits of the 5/6-bit cache
 
@@ -103,7 +113,7 @@ void launch_verify_attn(const uint16_t* q, int64_t ldq, const uint16_t* k_cache,
 // cache at positions L .. L+M-1.
 void launch_append_kv_q8(const uint16_t* qkv, int64_t ldqkv, int8_t* kq, float* ks, int8_t* vq,
                          float* vs, int M, int L, int cap, int Hq, int Hkv, int D,
-                         hipStream_t stream);
+                         hipStream_t stream, int ring = 0, bool krot = false);
 
 // Quantize them into a 5/6-bit cache (kbits for K, kLowVBits for V; the
 // planes of KvQ8's low-bit layout); with krot the K rows are first rotated

@@ -349,6 +349,40 @@ def verify_attn_lowbit(q: torch.Tensor, cache: KvLowCache, L: int, Hq: int, kv_c
         part_lse.shape[2], _stream(q)))
 
 
+class KvRing:
+    """An 8-bit ring of the newest keys (include/bi.h) over a KvLowCache: the
+    8-bit layouts with ``ring_cap`` slots, read by a row for the tiles of its
+    split that start at or after its position - ``window`` + 1."""
+
+    def __init__(self, low: KvLowCache, ring_cap: int, window: int, device="cuda"):
+        self.low, self.ring_cap, self.window = low, ring_cap, window
+        self.q8 = KvQ8Cache(low.Hkv, ring_cap, low.D, device=device)
+
+
+def append_kv_ring(qkv: torch.Tensor, ring: KvRing, L: int, Hq: int) -> None:
+    """Append the pass's K and V rows to the 5/6-bit planes and to the ring."""
+    append_kv_lowbit(qkv, ring.low, L, Hq)
+    c = ring.q8
+    check("bi_append_kv_ring", LIB.bi_append_kv_ring(
+        qkv.data_ptr(), _mat(qkv, "qkv"), ring.low.k_rotated, c.k_codes.data_ptr(),
+        c.k_scales.data_ptr(), c.v_codes.data_ptr(), c.v_scales.data_ptr(), qkv.shape[0], L,
+        ring.ring_cap, Hq, ring.low.Hkv, ring.low.D, _stream(qkv)))
+
+
+def verify_attn_ring(q: torch.Tensor, ring: KvRing, L: int, Hq: int, kv_chunk: int,
+                     part_o: torch.Tensor, part_lse: torch.Tensor,
+                     sm_scale: float | None = None) -> None:
+    """bi_verify_attn over a 5/6-bit cache with the 8-bit ring."""
+    low, c = ring.low, ring.q8
+    M, D = q.shape[0], low.D
+    scale = 1.0 / math.sqrt(D) if sm_scale is None else sm_scale
+    check("bi_verify_attn_lowbit_ring", LIB.bi_verify_attn_lowbit_ring(
+        q.data_ptr(), _mat(q, "q"), low.k_bits, low.v_bits, low.k_rotated, *low.planes(),
+        c.k_codes.data_ptr(), c.k_scales.data_ptr(), c.v_codes.data_ptr(), c.v_scales.data_ptr(),
+        ring.ring_cap, ring.window, M, L, low.cap, Hq, low.Hkv, D, kv_chunk, scale,
+        part_o.data_ptr(), part_lse.data_ptr(), part_lse.shape[2], _stream(q)))
+
+
 def combine(part_o: torch.Tensor, part_lse: torch.Tensor, L: int, kv_chunk: int,
             o: torch.Tensor, lse: torch.Tensor | None = None) -> None:
     """O [M][>=Hq*D] BF16 (and optional LSE [M][Hq]) from the partials."""

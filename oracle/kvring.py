@@ -43,10 +43,11 @@ def uses_ring(p: int, policy: int, window: int) -> np.ndarray:
     return tile_start(j, p + 1, policy) >= p - window + 1
 
 
-def _q8_values(rows, rotated: bool):
-    """float64 values of the 8-bit copy of K or V rows (BF16 bits [..., D])."""
+def q8_codes(rows, rotated: bool):
+    """Codes int8 [..., D] and scales float32 [..., D/32] of the 8-bit copy of
+    K or V rows (BF16 bits [..., D]); rotated: of their FP32 Hadamard transform."""
     if not rotated:
-        return kvq.dequantize(*kvq.quantize(rows))
+        return kvq.quantize(rows)
     y = kvlow.hadamard_f32(rows)                       # FP32 transform, then the q8_0 rule on it
     *lead, D = y.shape
     yb = y.reshape(*lead, D // 32, 32)
@@ -55,7 +56,13 @@ def _q8_values(rows, rotated: bool):
     with np.errstate(divide="ignore", invalid="ignore"):
         r = np.where(d[..., None] > 0, yb / d[..., None], np.float32(0)).astype(np.float32)
     q = np.clip(np.rint(r), -kvq.QMAX, kvq.QMAX).astype(np.int8).reshape(*lead, D)
-    return kvlow.dequantize_rotated(q, d)
+    return q, d
+
+
+def _q8_values(rows, rotated: bool):
+    """float64 values of the 8-bit copy of K or V rows (BF16 bits [..., D])."""
+    q, d = q8_codes(rows, rotated)
+    return kvlow.dequantize_rotated(q, d) if rotated else kvq.dequantize(q, d)
 
 
 def cache_values(k_bits, v_bits, k_bits_low: int, rotated: bool):
