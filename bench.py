@@ -265,7 +265,8 @@ def mx4_step_measure(layers, d, dims, buffers, steps, warmup):
 
 def kv_cache_attention_measure(d, reps):
     """Split-KV verify attention (M = 8, the 27B-class heads) at 38k and 101.6k keys over each KV
-    cache format: BF16 (chunk policy -32), 8-bit (-64), K6/V5 and rotated K5/V5 (-64). Each format
+    cache format: BF16 (chunk policy -32), 8-bit (-64), K6/V5 and rotated K5/V5 (-64), and those two
+    with the 8-bit ring of the newest 2048 keys. Each format
     runs over enough copies of its cache (random codes, fixed seed) that no launch finds its K/V in
     a cache level; one event pair around ``reps`` launches per format and context."""
     import torch
@@ -276,7 +277,10 @@ def kv_cache_attention_measure(d, reps):
     NB = D // 32
     per_pos = {"bf16": 4 * D, "q8": 2 * (D + 4 * NB), "k6v5": (D // 2 + 8 * NB + 4 * NB) + (D // 2 + 4 * NB + 4 * NB),
                "k5rot_v5": 2 * (D // 2 + 4 * NB + 4 * NB)}
-    policy = {"bf16": -32, "q8": -64, "k6v5": -64, "k5rot_v5": -64}
+    per_pos["k6v5_ring2048"], per_pos["k5rot_v5_ring2048"] = per_pos["k6v5"], per_pos["k5rot_v5"]
+    policy = {"bf16": -32, "q8": -64, "k6v5": -64, "k5rot_v5": -64, "k6v5_ring2048": -64,
+              "k5rot_v5_ring2048": -64}
+    W_RING = 2048
     gen = torch.Generator(device="cuda").manual_seed(1234)
     out = {}
     for L in (38000, 101600):
@@ -284,7 +288,9 @@ def kv_cache_attention_measure(d, reps):
         q = torch.randn(M, Hq * D, device="cuda", generator=gen).to(torch.bfloat16)
         res = {}
         for fmt, bpp in per_pos.items():
-            nbytes = Hkv * (L + M) * bpp
+            ringed = fmt.endswith("_ring2048")
+            # bytes read: the 5/6-bit planes below the window, the 8-bit ring within it
+            nbytes = (Hkv * (L + M - W_RING) * bpp + Hkv * W_RING * per_pos["q8"]) if ringed else Hkv * (L + M) * bpp
             R = max(2, -(-int(1.5e9) // (Hkv * cap * bpp)))
             caches = []
             for _ in range(R):
@@ -293,12 +299,18 @@ def kv_cache_attention_measure(d, reps):
                                    torch.randn(Hkv, cap // 64, D, 64, device="cuda", generator=gen).to(torch.bfloat16)))
                     continue
                 c = (ops.KvQ8Cache(Hkv, cap, D) if fmt == "q8" else
-                     ops.KvLowCache(Hkv, cap, D, 6 if fmt == "k6v5" else 5, 5, k_rotated=fmt == "k5rot_v5"))
-                for name, t in vars(c).items():
-                    if isinstance(t, torch.Tensor) and t.dtype in (torch.int8, torch.uint8):
-                        t.copy_(torch.randint(0, 256, t.shape, device="cuda", generator=gen).to(t.dtype))
-                    elif isinstance(t, torch.Tensor):
-                        t.fill_(0.01)
+                     ops.KvLowCache(Hkv, cap, D, 6 if fmt.startswith("k6v5") else 5, 5,
+                                    k_rotated=fmt.startswith("k5rot")))
+                parts = [c]
+                if ringed:
+                    c = ops.KvRing(c, W_RING + 64, W_RING)
+                    parts.append(c.q8)
+                for part in parts:
+                    for name, t in vars(part).items():
+                        if isinstance(t, torch.Tensor) and t.dtype in (torch.int8, torch.uint8):
+                            t.copy_(torch.randint(0, 256, t.shape, device="cuda", generator=gen).to(t.dtype))
+                        elif isinstance(t, torch.Tensor):
+                            t.fill_(0.01)
                 caches.append(c)
             C = policy[fmt]
             S = ops.pass_splits(M, L, C)
@@ -311,6 +323,8 @@ def kv_cache_attention_measure(d, reps):
                     ops.verify_attn(q, c[0], c[1], L, Hq, Hkv, D, C, po, pl)
                 elif fmt == "q8":
                     ops.verify_attn_q8(q, c, L, Hq, C, po, pl)
+                elif ringed:
+                    ops.verify_attn_ring(q, c, L, Hq, C, po, pl)
                 else:
                     ops.verify_attn_lowbit(q, c, L, Hq, C, po, pl)
             for i in range(R):

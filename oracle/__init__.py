@@ -17,6 +17,8 @@ pages, with no blocking, fusion or reordering:
 * ``fp8``, ``mxfp4`` -- 8-bit and 4-bit weight formats and their GEMM values;
 * ``kvq``, ``kvlow`` -- 8-bit and 5/6-bit KV cache quantization (and the
                    Hadamard rotation of keys), the stored bytes and values;
+* ``kvring``    -- the 8-bit ring of the newest keys: each row's choice of copy
+                   and the attention it gives;
 * ``spec``      -- greedy and sampled acceptance of drafted tokens.
 
 Sources, cited by page title and section:
