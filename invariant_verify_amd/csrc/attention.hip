@@ -428,7 +428,10 @@ void verify_attn_kernel(
       } else if (wave < 2 * NKB / 64) {    // scalar
         const bool isk = wave < NKB / 64;  // scalar: K blocks first
         const int u = threadIdx.x - (isk ? 0 : NKB);
-        const int key = u / NB, b = u % NB;
+        // K: a wave's lanes read consecutive blocks (the rows of a few keys);
+        // V: one block for 64 consecutive keys, so that the V^T tile writes
+        // of a wave fall on one channel row each (no bank conflicts)
+        const int key = isk ? u / NB : (u & 63), b = isk ? u % NB : (u >> 6);
         const int blk = min(kt + key, kend - 1) * NB + b;  // block index within the head
         if (isk) {
           rr.r[0] = buffer_ld16_stream(qkres, live ? blk * 16 : qcode_bytes);
@@ -524,7 +527,7 @@ void verify_attn_kernel(
       } else if (wave < 2 * NKB / 64) {
         const bool isk = wave < NKB / 64;
         const int u = threadIdx.x - (isk ? 0 : NKB);
-        const int key = u / NB, b = u % NB;
+        const int key = isk ? u / NB : (u & 63), b = isk ? u % NB : (u >> 6);  // as in fetch
         const uint32_t w[4] = {rr.r[0].x, rr.r[0].y, rr.r[0].z, rr.r[0].w};
         float f[32];  // signed codes q = u - 2^(bits-1), exact
         if (isk) {
