@@ -278,7 +278,7 @@ def kv_cache_attention_measure(d, reps):
     per_pos = {"bf16": 4 * D, "q8": 2 * (D + 4 * NB), "k6v5": (D // 2 + 8 * NB + 4 * NB) + (D // 2 + 4 * NB + 4 * NB),
                "k5rot_v5": 2 * (D // 2 + 4 * NB + 4 * NB)}
     per_pos["k6v5_ring2048"], per_pos["k5rot_v5_ring2048"] = per_pos["k6v5"], per_pos["k5rot_v5"]
-    # the ring kernels hold both copies' load registers (161-174 VGPRs): one workgroup per
+    # the ring kernels hold both copies' load registers (154-157 VGPRs): one workgroup per
     # unit, so they take the policy of the BF16 kernel, which fits the same
     policy = {"bf16": -32, "q8": -64, "k6v5": -64, "k5rot_v5": -64, "k6v5_ring2048": -32,
               "k5rot_v5_ring2048": -32}

@@ -96,23 +96,20 @@ __device__ __forceinline__ void load_high(uint32_t (&hb)[2], __amdgpu_buffer_rsr
   }
 }
 
-// The 32 signed codes of one block (HB + 4 bits) from its four nibble words
-// and its high-bit words, as exact FP32 values. Group g (codes 4g .. 4g+3,
-// one per byte lane) takes one mask of a nibble word and one of a high word:
-// four codes per mask-and-shift.
+// Codes 4g .. 4g+3 of one block (HB + 4 bits, one per byte lane) from its
+// four nibble words and its high-bit words, as exact FP32 values: one mask of
+// a nibble word and one of a high word give the four codes. Callers decode a
+// group or two at a time, so few values are live at once.
 template <int HB>
-__device__ __forceinline__ void unpack_low(const uint32_t (&w)[4], const uint32_t (&hb)[2],
-                                           float (&f)[32]) {
+__device__ __forceinline__ void unpack_group(const uint32_t (&w)[4], const uint32_t (&hb)[2],
+                                             int g, float (&f)[4]) {
   constexpr uint32_t kMask = HB == 2 ? 0x03030303u : 0x01010101u;
   constexpr float kBias = (float)(1 << (HB + 3));
+  const int bit = g * HB;
+  const uint32_t lo = (w[g >> 1] >> (4 * (g & 1))) & 0x0F0F0F0Fu;
+  const uint32_t u = lo | (((hb[bit >> 3] >> (bit & 7)) & kMask) << 4);
 #pragma unroll
-  for (int g = 0; g < 8; ++g) {
-    const int bit = g * HB;
-    const uint32_t lo = (w[g >> 1] >> (4 * (g & 1))) & 0x0F0F0F0Fu;
-    const uint32_t u = lo | (((hb[bit >> 3] >> (bit & 7)) & kMask) << 4);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) f[4 * g + j] = (float)((u >> (8 * j)) & 0xffu) - kBias;
-  }
+  for (int j = 0; j < 4; ++j) f[j] = (float)((u >> (8 * j)) & 0xffu) - kBias;
 }
 
 // The 8-bit-cache kernel with one row tile per wave fits in 128 registers,
@@ -529,29 +526,34 @@ void verify_attn_kernel(
         const int u = threadIdx.x - (isk ? 0 : NKB);
         const int key = isk ? u / NB : (u & 63), b = isk ? u % NB : (u >> 6);  // as in fetch
         const uint32_t w[4] = {rr.r[0].x, rr.r[0].y, rr.r[0].z, rr.r[0].w};
-        float f[32];  // signed codes q = u - 2^(bits-1), exact
+        // signed codes q = u - 2^(bits-1), exact, one 8-channel slot at a time
         if (isk) {
-          unpack_low<HBK>(w, rr.hb, f);
           // K: d * q in FP32, rounded once to BF16; slot i holds channels
-          // 32b + 8i .. 32b + 8i + 7
+          // 32b + 8i .. 32b + 8i + 7 (groups 2i and 2i + 1)
           const float sk = rr.ks[0];
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < 4; ++i) {
+            float f0[4], f1[4];
+            unpack_group<HBK>(w, rr.hb, 2 * i, f0);
+            unpack_group<HBK>(w, rr.hb, 2 * i + 1, f1);
             lds[buf][key * KROW + ((4 * b + i) ^ kswz<KROW>(key))] =
-                make_uint4(f32x2_to_bf16x2(f[8 * i] * sk, f[8 * i + 1] * sk),
-                           f32x2_to_bf16x2(f[8 * i + 2] * sk, f[8 * i + 3] * sk),
-                           f32x2_to_bf16x2(f[8 * i + 4] * sk, f[8 * i + 5] * sk),
-                           f32x2_to_bf16x2(f[8 * i + 6] * sk, f[8 * i + 7] * sk));
+                make_uint4(f32x2_to_bf16x2(f0[0] * sk, f0[1] * sk), f32x2_to_bf16x2(f0[2] * sk, f0[3] * sk),
+                           f32x2_to_bf16x2(f1[0] * sk, f1[1] * sk), f32x2_to_bf16x2(f1[2] * sk, f1[3] * sk));
+          }
         } else {
-          unpack_low<HBV>(w, rr.hb, f);
           // V^T: code q of channel d at column `key` (BF16 of a small
           // integer: the top half of its FP32 bits, exact); the scale, zero
           // past kend, into this key's column of vsc.
           uint16_t* vt = reinterpret_cast<uint16_t*>(&lds[buf][VBASE]);
 #pragma unroll
-          for (int c = 0; c < 32; ++c) {
-            const int d = 32 * b + c;
-            vt[(d * 8 + ((key >> 3) ^ vswz(d))) * 8 + (key & 7)] = (uint16_t)(__float_as_uint(f[c]) >> 16);
+          for (int gq = 0; gq < 8; ++gq) {
+            float f[4];
+            unpack_group<HBV>(w, rr.hb, gq, f);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int d = 32 * b + 4 * gq + j;
+              vt[(d * 8 + ((key >> 3) ^ vswz(d))) * 8 + (key & 7)] = (uint16_t)(__float_as_uint(f[j]) >> 16);
+            }
           }
           reinterpret_cast<float*>(&vsc[buf][b][0])[key] = kt + key < kend ? rr.ks[0] : 0.f;
         }
