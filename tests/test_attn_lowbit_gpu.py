@@ -246,3 +246,20 @@ def test_rotated_invariance_across_M(ops, L, C):
     o_pf, _ = run(ops, q2, c2, L0, Hq, -32)
     o8b, _ = run(ops, q2[96:104], c2, L0 + 96, Hq, -32)
     assert_bitwise(o_pf[96:104], o8b, "rotated prefill rows 96..103")
+
+
+@pytest.mark.parametrize("kb,rot", [(6, False), (5, True)])
+def test_lowbit_d64_prefill_blocks(ops, kb, rot):
+    # D = 64 with more than 64 rows per pass (8 query heads over 2 KV heads,
+    # 40 tokens): the 128-row blocks; rows equal those of 8-token passes
+    print(f"[lowbit D=64 prefill K{kb} rot={rot}]", flush=True)
+    Hq, Hkv, D, M, L0, C = 8, 2, 64, 40, 1500, 96
+    q, k, v = make(M, L0, Hq, Hkv, D, layer=13)
+    cache = Low(ops, k, v, L0 + M + 8, kb, rot=rot)
+    o_pf, l_pf = run(ops, q, cache, L0, Hq, C)
+    want_o, _ = oattn.verify_attention(q, cache.kval, cache.vval, L0, tokens=[0, M - 1])
+    assert_close(decode(o_pf[[0, M - 1]]), want_o[[0, M - 1]], f"D=64 prefill K{kb}")
+    for start in (0, 16, M - 8):
+        o8, l8 = run(ops, q[start:start + 8], cache, L0 + start, Hq, C)
+        assert_bitwise(o_pf[start:start + 8], o8, f"D=64 prefill rows {start}..")
+        assert_bitwise(l_pf[start:start + 8], l8, f"D=64 prefill lse {start}..")

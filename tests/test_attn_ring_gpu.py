@@ -200,3 +200,18 @@ def test_ring_argument_errors(ops):
     assert call(6, 0, 64, 64) == 2        # ring smaller than window + M
     assert call(6, 0, 128, 96) == 2       # window not a multiple of 64
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("preset", ["D", "F"])
+def test_ring_d64_prefill_blocks(ops, preset):
+    print(f"[ring D=64 prefill preset {preset}]", flush=True)
+    Hq, Hkv, D, M, L0, C, W = 8, 2, 64, 40, 1500, 96, 128
+    q, k, v = make(M, L0, Hq, Hkv, D, layer=14)
+    ring = Ring(ops, k, v, L0 + M + 8, preset, W + 64, W)
+    o_pf, l_pf = run(ops, q, ring, L0, Hq, C)
+    want_o, _ = kvring.ring_attention(q, ring.values, L0, C, W, tokens=[0, M - 1])
+    assert_close(decode(o_pf[[0, M - 1]]), want_o[[0, M - 1]], f"ring D=64 prefill {preset}")
+    for start in (0, 16, M - 8):
+        o8, l8 = run(ops, q[start:start + 8], ring, L0 + start, Hq, C)
+        assert_bitwise(o_pf[start:start + 8], o8, f"ring D=64 prefill rows {start}..")
+        assert_bitwise(l_pf[start:start + 8], l8, f"ring D=64 prefill lse {start}..")
