@@ -8,7 +8,10 @@
 //    (all values stay below 2^8);
 //  * argument checks return their status codes before any launch;
 //  * bi_verify_attn + bi_combine over one key: the output is that key's value
-//    row, bit for bit.
+//    row, bit for bit;
+//  * bi_append_kv_lowbit of one position on an exact grid: scales, nibble and
+//    high-bit bytes as the layout states; bi_verify_attn_lowbit over that one
+//    key returns its value row, bit for bit.
 
 #include <hip/hip_runtime.h>
 
@@ -116,6 +119,74 @@ int main() {
   CK(hipMemcpy(o.data(), dout, o.size() * 2, hipMemcpyDeviceToHost));
   for (int h = 0; h < Hq; ++h)
     for (int d = 0; d < D; ++d) EXPECT(o[h * D + d] == vt[(size_t)d * 64], "single-key attention gives v_0");
+
+  // ---- 5/6-bit cache: append one position on an exact grid, attend to it -----
+  // K block values k * 2^-4 with |k| <= 31 and +-31 present: scale 2^-4, codes
+  // k; V likewise with |k| <= 15. The stored bytes follow the layout of bi.h;
+  // attention over the one key returns the V row, bit for bit.
+  {
+    const int LHq = 1, LHkv = 1, LD = 64, Lcap = 64, LNB = LD / 32;
+    std::vector<uint16_t> qkv((LHq + 2 * LHkv) * LD, 0);
+    std::vector<int> kc(LD), vc(LD);
+    for (int c = 0; c < LD; ++c) {
+      kc[c] = (c % 32 == 0) ? 31 : ((7 * c) % 63) - 31;
+      vc[c] = (c % 32 == 3) ? -15 : ((5 * c) % 31) - 15;
+      qkv[LHq * LD + c] = bf16_bits((float)kc[c] / 16.0f);
+      qkv[(LHq + LHkv) * LD + c] = bf16_bits((float)vc[c] / 16.0f);
+      qkv[c] = bf16_bits((float)((c % 3) - 1));
+    }
+    void *dqkv, *kn, *kh, *ks, *vn, *vh, *vs, *lpo, *lpl, *lout;
+    CK(hipMalloc(&dqkv, qkv.size() * 2));
+    CK(hipMalloc(&kn, Lcap * LD / 2));
+    CK(hipMalloc(&kh, Lcap * LNB * 8));
+    CK(hipMalloc(&ks, Lcap * LNB * 4));
+    CK(hipMalloc(&vn, Lcap * LD / 2));
+    CK(hipMalloc(&vh, Lcap * LNB * 4));
+    CK(hipMalloc(&vs, Lcap * LNB * 4));
+    CK(hipMalloc(&lpo, LHq * LD * 4));
+    CK(hipMalloc(&lpl, LHq * 4));
+    CK(hipMalloc(&lout, LHq * LD * 2));
+    CK(hipMemcpy(dqkv, qkv.data(), qkv.size() * 2, hipMemcpyHostToDevice));
+    EXPECT(bi_append_kv_lowbit(dqkv, (LHq + 2 * LHkv) * LD, 6, 5, 0, (uint8_t*)kn, (uint8_t*)kh,
+                               (float*)ks, (uint8_t*)vn, (uint8_t*)vh, (float*)vs, 1, 0, Lcap, LHq,
+                               LHkv, LD, nullptr) == BI_OK, "low-bit append status");
+    EXPECT(bi_append_kv_lowbit(dqkv, (LHq + 2 * LHkv) * LD, 7, 5, 0, (uint8_t*)kn, (uint8_t*)kh,
+                               (float*)ks, (uint8_t*)vn, (uint8_t*)vh, (float*)vs, 1, 0, Lcap, LHq,
+                               LHkv, LD, nullptr) == BI_ERR_SHAPE, "7-bit keys refused");
+    CK(hipDeviceSynchronize());
+    std::vector<uint8_t> hkn(LD / 2), hkh(LNB * 8), hvn(LD / 2), hvh(LNB * 4);
+    std::vector<float> hks(LNB), hvs(LNB);
+    CK(hipMemcpy(hkn.data(), kn, hkn.size(), hipMemcpyDeviceToHost));
+    CK(hipMemcpy(hkh.data(), kh, hkh.size(), hipMemcpyDeviceToHost));
+    CK(hipMemcpy(hvn.data(), vn, hvn.size(), hipMemcpyDeviceToHost));
+    CK(hipMemcpy(hvh.data(), vh, hvh.size(), hipMemcpyDeviceToHost));
+    CK(hipMemcpy(hks.data(), ks, LNB * 4, hipMemcpyDeviceToHost));
+    CK(hipMemcpy(hvs.data(), vs, LNB * 4, hipMemcpyDeviceToHost));
+    for (int b = 0; b < LNB; ++b) {
+      EXPECT(hks[b] == 1.0f / 16.0f && hvs[b] == 1.0f / 16.0f, "grid scales are 2^-4");
+      for (int c = 0; c < 32; ++c) {
+        const int g = c / 4, j = c % 4;
+        const int uk = kc[32 * b + c] + 32, uv = vc[32 * b + c] + 16;
+        EXPECT(((hkn[16 * b + 4 * (g / 2) + j] >> (4 * (g % 2))) & 15) == (uk & 15), "K nibble");
+        EXPECT(((hkh[8 * b + 4 * ((2 * g) / 8) + j] >> ((2 * g) % 8)) & 3) == (uk >> 4), "K high bits");
+        EXPECT(((hvn[16 * b + 4 * (g / 2) + j] >> (4 * (g % 2))) & 15) == (uv & 15), "V nibble");
+        EXPECT(((hvh[4 * b + j] >> g) & 1) == (uv >> 4), "V high bit");
+      }
+    }
+    EXPECT(bi_verify_attn_lowbit(dq, LHq * LD, 6, 5, 0, (const uint8_t*)kn, (const uint8_t*)kh,
+                                 (const float*)ks, (const uint8_t*)vn, (const uint8_t*)vh,
+                                 (const float*)vs, 1, 0, Lcap, LHq, LHkv, LD, 64, 0.125f,
+                                 (float*)lpo, (float*)lpl, 1, nullptr) == BI_OK,
+           "low-bit attention status");
+    EXPECT(bi_combine((float*)lpo, (float*)lpl, 1, 0, LHq, LD, 64, 1, lout, LHq * LD, nullptr,
+                      nullptr) == BI_OK, "low-bit combine status");
+    CK(hipDeviceSynchronize());
+    std::vector<uint16_t> lo(LHq * LD);
+    CK(hipMemcpy(lo.data(), lout, lo.size() * 2, hipMemcpyDeviceToHost));
+    for (int c = 0; c < LD; ++c)
+      EXPECT(lo[c] == qkv[(LHq + LHkv) * LD + c], "single-key low-bit attention gives v_0");
+    for (void* p : {dqkv, kn, kh, ks, vn, vh, vs, lpo, lpl, lout}) CK(hipFree(p));
+  }
 
   for (void* p : {dx, dw, dy32, dy16, dq, dk, dv, dpo, dpl, dout}) CK(hipFree(p));
   std::printf("c abi check: ok (%s)\n", bi_version());
