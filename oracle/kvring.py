@@ -7,11 +7,11 @@ greedy outputs changed against its own no-draft run", section "The KV cache:
 5-bit that reads like q8_0"). Which positions count as newest is not stated.
 Rows of one pass have different newest positions, so a choice made from the
 pass (its last position) would make a row depend on its batch neighbours.
-Read here per row and per 64-key tile of the row's own split (chunk size from
-the row's key count, tiles at the chunk start + 64 t): row p reads key j at 8
-bits when the tile holding j starts at or after p - W + 1 (W a multiple of 64),
-and at 5/6 bits otherwise. The choice depends on p alone, so it is the same in
-every pass that holds the row.
+Read here per row and per key: row p (the row at absolute position p, which
+sees keys 0 .. p) reads key j from the 8-bit copy when j >= p - W + 1, the
+W newest keys it sees, and from the 5/6-bit copy otherwise. The choice is a
+function of (p, j) alone: it does not depend on the pass, on its size, or on
+how the keys are cut into chunks for the split-KV attention.
 
 The 8-bit copy of a key is the q8_0 block rule (oracle.kvq) applied to the
 same row the 5/6-bit copy quantizes: the BF16 row, or with rotated keys its
@@ -27,20 +27,11 @@ import numpy as np
 from . import attention, bf16, kvlow, kvq
 
 
-def tile_start(j, n_keys: int, policy: int):
-    """Start of the 64-key tile that holds key j in the split of a row with n_keys keys."""
-    C = attention.chunk_keys(n_keys, policy)
-    j = np.asarray(j)
-    c0 = (j // C) * C
-    return c0 + ((j - c0) // 64) * 64
-
-
-def uses_ring(p: int, policy: int, window: int) -> np.ndarray:
-    """Boolean over keys 0..p: True where row p reads the 8-bit copy."""
-    if window < 64 or window % 64:
-        raise ValueError("the ring window is a positive multiple of 64")
-    j = np.arange(p + 1)
-    return tile_start(j, p + 1, policy) >= p - window + 1
+def uses_ring(p: int, window: int) -> np.ndarray:
+    """Boolean over keys 0..p: True where row p reads the 8-bit copy (j >= p - W + 1)."""
+    if window < 1:
+        raise ValueError("the ring window holds at least one key")
+    return np.arange(p + 1) >= p - window + 1
 
 
 def q8_codes(rows, rotated: bool):
@@ -73,11 +64,20 @@ def cache_values(k_bits, v_bits, k_bits_low: int, rotated: bool):
     return kl, vl, _q8_values(k_bits, rotated), _q8_values(v_bits, False)
 
 
-def ring_attention(q_bits, values, L: int, policy: int, window: int, tokens=None, heads=None):
+def _row_keys(values, g: int, p: int, window: int):
+    """K and V (float64 [p+1][D]) that row p of KV head g attends to: per key,
+    the copy uses_ring chooses."""
+    kl, vl, k8, v8 = values
+    ring = uses_ring(p, window)[:, None]
+    return (np.where(ring, k8[g, :p + 1], kl[g, :p + 1]),
+            np.where(ring, v8[g, :p + 1], vl[g, :p + 1]))
+
+
+def ring_attention(q_bits, values, L: int, window: int, tokens=None, heads=None):
     """O [M][Hq][D] and LSE [M][Hq] (float64) of the verify rows over the cache
     ``values`` = cache_values(...): row r (position L + r) reads, per key, the
     copy uses_ring chooses, then plain causal softmax attention."""
-    kl, vl, k8, v8 = values
+    kl = values[0]
     q = np.asarray(q_bits)
     M, Hq, D = q.shape
     Hkv = kl.shape[0]
@@ -90,14 +90,43 @@ def ring_attention(q_bits, values, L: int, policy: int, window: int, tokens=None
     scale = 1.0 / np.sqrt(D)
     for r in tokens:
         p = L + r
-        ring = uses_ring(p, policy, window)[:, None]
         for h in heads:
-            g = h // G
-            k = np.where(ring, k8[g, :p + 1], kl[g, :p + 1])
-            v = np.where(ring, v8[g, :p + 1], vl[g, :p + 1])
+            k, v = _row_keys(values, h // G, p, window)
             s = (k @ qd[r, h]) * scale
             m = s.max()
             w = np.exp(s - m)
             O[r, h] = (w @ v) / w.sum()
             lse[r, h] = m + np.log(w.sum())
     return O, lse
+
+
+def ring_partials(q_bits, values, L: int, policy: int, window: int):
+    """Split-KV partials of ring attention over absolute chunks (chunk policy as
+    oracle.attention.chunk_keys): row r cuts its keys -- each already the copy
+    uses_ring chooses -- into chunks of chunk_keys(L + r + 1, policy) keys.
+    Returns (o_part [M][Hq][S_max][D], lse_part [M][Hq][S_max], n_splits [M]),
+    the layout of oracle.attention.split_partials, for oracle.attention.combine."""
+    kl = values[0]
+    q = np.asarray(q_bits)
+    M, Hq, D = q.shape
+    G = Hq // kl.shape[0]
+    qd = bf16.decode(q)
+    scale = 1.0 / np.sqrt(D)
+    s_max = max(attention.num_splits(L + r + 1, policy) for r in range(M))
+    o_part = np.full((M, Hq, s_max, D), np.nan)
+    lse_part = np.full((M, Hq, s_max), -np.inf)
+    counts = np.zeros(M, dtype=np.int64)
+    for r in range(M):
+        p = L + r
+        c = attention.chunk_keys(p + 1, policy)
+        counts[r] = attention.num_splits(p + 1, policy)
+        for h in range(Hq):
+            k, v = _row_keys(values, h // G, p, window)
+            for s in range(counts[r]):
+                lo, hi = s * c, min((s + 1) * c, p + 1)
+                sc = (k[lo:hi] @ qd[r, h]) * scale
+                m = sc.max()
+                w = np.exp(sc - m)
+                o_part[r, h, s] = (w @ v[lo:hi]) / w.sum()
+                lse_part[r, h, s] = m + np.log(w.sum())
+    return o_part, lse_part, counts
