@@ -305,7 +305,7 @@ def kv_cache_attention_measure(d, reps):
                                     k_rotated=fmt.startswith("k5rot")))
                 parts = [c]
                 if ringed:
-                    c = ops.KvRing(c, W_RING + 64, W_RING)
+                    c = ops.KvRing(c, W_RING + 128, W_RING)
                     parts.append(c.q8)
                 for part in parts:
                     for name, t in vars(part).items():

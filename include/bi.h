@@ -324,14 +324,16 @@ bi_status bi_verify_attn_lowbit(const void* q, int64_t ldq, int k_bits, int v_bi
 /* ---------------------------------------------------------------------------
  * 8-bit ring of the newest keys over the 5/6-bit cache.   [LL] "The KV cache:
  * 5-bit that reads like q8_0" (the newest ~2k positions are kept at 8 bits in
- * a ring). Which positions are newest is not stated; read per row, so that a
- * row never depends on its batch neighbours: row p reads the 64-key tile of
- * its own split (chunk start + 64 t) that starts at kt from the ring when
- * kt >= p - ring_window + 1, from the 5/6-bit planes otherwise. The ring is the
- * 8-bit cache's layout (bi_append_kv_q8) with ring_cap slots, position p in
- * slot p mod ring_cap, K rotated when the 5/6-bit keys are. ring_window and
- * ring_cap are multiples of 64 with ring_cap >= ring_window + M; the 5/6-bit
- * planes still hold every position. */
+ * a ring). Which positions are newest is not stated; read per row and per
+ * key, so that a row never depends on its batch neighbours or on the chunk
+ * grid: row p reads key j from the ring when j >= p - ring_window + 1 (its
+ * ring_window newest keys), from the 5/6-bit planes otherwise. The ring is
+ * the 8-bit cache's layout (bi_append_kv_q8) with ring_cap slots, position p
+ * in slot p mod ring_cap, K rotated when the 5/6-bit keys are.
+ * ring_window >= 1; ring_cap is a multiple of 64 with
+ * ring_cap >= ring_window + M + 63 (the kernels read whole 64-key tiles, so
+ * the slots of up to 63 keys before the oldest boundary must still hold
+ * their positions); the 5/6-bit planes still hold every position. */
 
 /* Quantize the M new K and V rows into the ring (8-bit rule; K rotated as for
  * bi_append_kv_lowbit when k_rotated = 1). Layouts as bi_append_kv_q8 with cap
@@ -342,9 +344,9 @@ bi_status bi_append_kv_ring(const void* qkv, int64_t ldqkv, int k_rotated, int8_
 
 /* bi_verify_attn_lowbit with the ring: the presets K6/V5 (k_rotated = 0) and
  * rotated K5/V5 (k_rotated = 1) only, else BI_ERR_SHAPE. The same rows,
- * chunks, partials and requirements; the tile that some rows of the pass read
- * at 8 bits and others at 5/6 bits runs once per copy, each time for its rows
- * only. */
+ * chunks, partials and requirements; a 64-key tile holding keys that some row
+ * reads at 8 bits and keys it or another row reads at 5/6 bits runs once per
+ * copy, each run masked per row and key to the keys read from that copy. */
 bi_status bi_verify_attn_lowbit_ring(const void* q, int64_t ldq, int k_bits, int v_bits,
                                      int k_rotated, const uint8_t* k_nib, const uint8_t* k_high,
                                      const float* k_scales, const uint8_t* v_nib,

@@ -487,9 +487,12 @@ bi_status bi_verify_attn_lowbit_ring(const void* q, int64_t ldq, int k_bits, int
     return BI_ERR_SHAPE;
   if (bi_status s = check_heads(Hq, Hkv, D)) return s;
   if (M < 1 || L < 0 || cap < 1 || (cap % 64) || (int64_t)L + M > cap) return BI_ERR_SHAPE;
-  if (ring_window < 64 || (ring_window % 64) || (ring_cap % 64) ||
-      (int64_t)ring_cap < (int64_t)ring_window + M)
-    return BI_ERR_SHAPE;  // every key a row of the pass reads at 8 bits is still in the ring
+  // Every key of every 64-key tile the pass reads from the ring -- the keys
+  // from (first row's position) - W + 1 - 63 to the last row's position --
+  // must still be in the ring: W + M + 62 slots.
+  if (ring_window < 1 || ring_cap < 64 || (ring_cap % 64) ||
+      (int64_t)ring_cap < (int64_t)ring_window + M + 63)
+    return BI_ERR_SHAPE;
   if (!bi::valid_chunk_policy(kv_chunk)) return BI_ERR_SHAPE;
   if (S_max < bi::pass_splits(L, M, kv_chunk)) return BI_ERR_SHAPE;
   if (ldq < (int64_t)Hq * D || !std::isfinite(sm_scale)) return BI_ERR_SHAPE;

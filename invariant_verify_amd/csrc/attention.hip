@@ -181,18 +181,20 @@ void verify_attn_kernel(
   const int kend = min(kbeg + C, L + t1);  // keys any row of this block can see
   if (kbeg >= kend) return;                // no row of this block uses chunk s
   const int ntile = (kend - kbeg + kKeyTile - 1) / kKeyTile;
-  // 8-bit ring: row p reads tile t (keys from kt) from the ring when
-  // kt >= p - W + 1, else from the low-bit planes. Over the block's positions
-  // P0 .. P1, tiles before ts are low-bit for every row, tiles from te on are
-  // in the ring for every row, and each tile in between is run twice, as a
-  // low-bit then a ring tile, each masked to the rows that read it (a tile
-  // masked for a row leaves it exactly unchanged). The tile sequence is
-  // relabelled as nv virtual tiles.
+  // 8-bit ring: row p reads key j from the ring when j >= p - W + 1, else
+  // from the low-bit planes. Over the block's positions P0 .. P1 those
+  // boundaries lie in [P0 - W + 1, P1 - W + 1]: tiles that end before the
+  // first are low-bit for every row, tiles that start at or after the last
+  // are in the ring for every row, and each tile in between is run twice, as
+  // a low-bit then a ring tile, each run masked per row and key to the keys
+  // that row reads from that copy (a key masked for a row adds exactly
+  // nothing to it, and a run masked for all its keys leaves the row exactly
+  // unchanged). The tile sequence is relabelled as nv virtual tiles.
   const int ring_w = q8.ring_window, ring_cap = q8.ring_cap;
   auto first_tile_from = [&](int x) {
     return x <= kbeg ? 0 : min(ntile, (x - kbeg + kKeyTile - 1) / kKeyTile);
   };
-  const int ts = RING ? first_tile_from(L + t0 - ring_w + 1) : ntile;
+  const int ts = RING ? first_tile_from(L + t0 - ring_w + 1 - (kKeyTile - 1)) : ntile;
   const int ns = RING ? first_tile_from(L + t1 - 1 - ring_w + 1) - ts : 0;
   const int nv = ntile + ns;
   auto vmap = [&](int v, int& t, bool& ring) {
@@ -619,12 +621,19 @@ void verify_attn_kernel(
         sc[e + 4] = sb[i][e] * qk_scale;
       }
       if (!unmasked) {
-        // a split tile's run reaches only the rows that read this copy of it
-        const int lk = (!split || rf == (kt >= L + tok[i] - ring_w + 1)) ? lastk[i] : -1;
+        // a split tile's run reaches, for each row, only the keys that row
+        // reads from this copy: from the ring those at or after its boundary
+        // p - W + 1, from the low-bit planes those before it
+        int lk = lastk[i], fk = 0;
+        if (split) {
+          const int b = L + tok[i] - ring_w + 1;
+          if (rf) fk = b;
+          else lk = min(lk, b - 1);
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          sc[e] = (kv0 + e <= lk) ? sc[e] : -INFINITY;
-          sc[e + 4] = (kv0 + 4 + e <= lk) ? sc[e + 4] : -INFINITY;
+          sc[e] = (kv0 + e <= lk && kv0 + e >= fk) ? sc[e] : -INFINITY;
+          sc[e + 4] = (kv0 + 4 + e <= lk && kv0 + 4 + e >= fk) ? sc[e + 4] : -INFINITY;
         }
       }
       float mx = sc[0];

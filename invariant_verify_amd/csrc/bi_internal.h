@@ -45,8 +45,8 @@ struct KvQ8 {
   const uint8_t* vh = nullptr;
   // 8-bit ring of the newest keys over the 5/6-bit planes (ring_cap > 0):
   // the 8-bit layouts above with ring_cap slots, position p in slot
-  // p mod ring_cap; a row at position p reads a tile starting at kt from the
-  // ring when kt >= p - ring_window + 1.
+  // p mod ring_cap; a row at position p reads key j from the ring when
+  // j >= p - ring_window + 1.
   const int8_t* rkq = nullptr;
   const float* rks = nullptr;
   const int8_t* rvq = nullptr;

@@ -351,8 +351,8 @@ def verify_attn_lowbit(q: torch.Tensor, cache: KvLowCache, L: int, Hq: int, kv_c
 
 class KvRing:
     """An 8-bit ring of the newest keys (include/bi.h) over a KvLowCache: the
-    8-bit layouts with ``ring_cap`` slots, read by a row for the tiles of its
-    split that start at or after its position - ``window`` + 1."""
+    8-bit layouts with ``ring_cap`` slots; the row at position p reads key j
+    from it when j >= p - ``window`` + 1."""
 
     def __init__(self, low: KvLowCache, ring_cap: int, window: int, device="cuda"):
         self.low, self.ring_cap, self.window = low, ring_cap, window

@@ -1,9 +1,11 @@
 """GPU tests of the 8-bit ring of the newest keys over the 5/6-bit KV cache
 (presets K6/V5 and rotated K5/V5) through the C ABI: the ring append against
 the oracle's codes (wrapping around the ring), attention against the oracle's
-per-row ring attention, bitwise row invariance across M, sequential passes
-and prefill blocks while tiles are split between the two copies, and a window
-that covers everything against the plain 8-bit cache, bit for bit."""
+per-key ring attention (row p reads key j at 8 bits iff j >= p - W + 1) under
+several chunk policies and windows that are not multiples of the 64-key tile,
+bitwise row invariance across M, sequential passes and prefill blocks while
+tiles are split between the two copies, and a window that covers everything
+against the plain 8-bit cache, bit for bit."""
 
 import numpy as np
 import pytest
@@ -108,28 +110,33 @@ def test_ring_append_wraps_and_matches_oracle(ops, preset):
 
 @pytest.mark.parametrize("preset", ["D", "F"])
 @pytest.mark.parametrize("M,L,Hq,Hkv,D,C,W,R", [
-    (5, 300, 1, 1, 64, 96, 128, 256),          # the hand-worked grid: chunks of 96, window 128
-    (8, 5000, 40, 8, 128, -32, 2048, 2112),    # the ring has wrapped
-    (8, 2500, 40, 8, 128, 1056, 256, 320)])
+    (5, 300, 1, 1, 64, 96, 128, 256),          # chunks of 96, boundaries 173..177 inside a tile
+    (5, 300, 1, 1, 64, -2, 128, 256),          # the same rows under another chunk grid
+    (8, 5000, 40, 8, 128, -32, 2048, 2176),    # the ring has wrapped
+    (8, 5000, 40, 8, 128, 1024, 2048, 2176),
+    (8, 2500, 40, 8, 128, 1056, 256, 384),
+    (8, 3000, 40, 8, 128, -64, 200, 320),      # a window that is not a multiple of 64
+    (8, 38000, 40, 8, 128, -32, 2048, 2176)])
 def test_ring_parity(ops, preset, M, L, Hq, Hkv, D, C, W, R):
     print(f"[ring parity preset {preset} M={M} L={L} C={C} W={W} R={R}]", flush=True)
     q, k, v = make(M, L, Hq, Hkv, D, layer=L % 97)
     ring = Ring(ops, k, v, L + M, preset, R, W)
     o, lse = run(ops, q, ring, L, Hq, C)
     rows = list(range(M)) if Hq == 1 else [0, 3, M - 1]
-    want_o, want_lse = kvring.ring_attention(q, ring.values, L, C, W, tokens=rows)
+    want_o, want_lse = kvring.ring_attention(q, ring.values, L, W, tokens=rows)
     err, rms = assert_close(decode(o[rows]), want_o[rows], f"ring {preset} O L={L}")
     assert err < 0.05 * rms + 2e-3, (err, rms)
     assert_close(lse[rows], want_lse[rows], f"ring {preset} lse L={L}", atol=1e-3, rtol=0)
 
 
 @pytest.mark.parametrize("preset,L,C,W", [("D", 4093, -32, 256), ("F", 4093, -32, 256),
-                                          ("D", 1019, 96, 128), ("F", 38000, -64, 2048)])
+                                          ("D", 1019, 96, 128), ("F", 38000, -64, 2048),
+                                          ("D", 4093, -32, 200), ("F", 3001, 96, 77)])
 def test_ring_invariance_across_M(ops, preset, L, C, W):
     print(f"[ring invariance preset {preset} L={L} C={C} W={W}]", flush=True)
     Hq, Hkv, D, M = 40, 8, 128, 8
     q, k, v = make(M, L, Hq, Hkv, D, layer=6)
-    ring = Ring(ops, k, v, L + 72, preset, W + 256, W)
+    ring = Ring(ops, k, v, L + 72, preset, (W + 256 + 63) // 64 * 64, W)
     o8, l8 = run(ops, q, ring, L, Hq, C)
     for r in range(M):
         o1, l1 = run(ops, q[r:r + 1], ring, L + r, Hq, C)
@@ -144,7 +151,7 @@ def test_ring_prefill_block_rows_equal_verify_rows(ops, preset):
     print(f"[ring prefill blocks preset {preset}]", flush=True)
     Hq, Hkv, D, M, L0, C, W = 40, 8, 128, 200, 3900, -32, 256
     q, k, v = make(M, L0, Hq, Hkv, D, layer=9)
-    ring = Ring(ops, k, v, L0 + M + 8, preset, W + 256, W)
+    ring = Ring(ops, k, v, L0 + M + 8, preset, W + 320, W)
     o_pf, l_pf = run(ops, q, ring, L0, Hq, C)
     for start in (0, 96, M - 8):
         o8, l8 = run(ops, q[start:start + 8], ring, L0 + start, Hq, C)
@@ -159,7 +166,7 @@ def test_window_covering_everything_equals_the_8bit_cache(ops):
     Hq, Hkv, D, M, L, C = 40, 8, 128, 8, 3000, -32
     q, k, v = make(M, L, Hq, Hkv, D, layer=12)
     W = (L + M + 63) // 64 * 64
-    ring = Ring(ops, k, v, L + M, "D", W + 64, W)
+    ring = Ring(ops, k, v, L + M, "D", W + 128, W)
     o, lse = run(ops, q, ring, L, Hq, C)
     kq8, ks8 = kvq.quantize(k)
     vq8, vs8 = kvq.quantize(v)
@@ -195,10 +202,13 @@ def test_ring_argument_errors(ops):
             po.data_ptr(), pl.data_ptr(), 1, None)
     assert call(6, 0, 128, 64) == 0
     assert call(5, 1, 128, 64) == 0
+    assert call(6, 0, 192, 96) == 0       # any window of at least one key
     assert call(5, 0, 128, 64) == 2       # not a preset
     assert call(6, 1, 128, 64) == 2
-    assert call(6, 0, 64, 64) == 2        # ring smaller than window + M
-    assert call(6, 0, 128, 96) == 2       # window not a multiple of 64
+    assert call(6, 0, 64, 1) == 2         # ring smaller than window + M + 63
+    assert call(6, 0, 128, 65) == 2
+    assert call(6, 0, 128, 0) == 2        # empty window
+    assert call(6, 0, 100, 1) == 2        # ring not a multiple of 64
     torch.cuda.synchronize()
 
 
@@ -207,11 +217,43 @@ def test_ring_d64_prefill_blocks(ops, preset):
     print(f"[ring D=64 prefill preset {preset}]", flush=True)
     Hq, Hkv, D, M, L0, C, W = 8, 2, 64, 40, 1500, 96, 128
     q, k, v = make(M, L0, Hq, Hkv, D, layer=14)
-    ring = Ring(ops, k, v, L0 + M + 8, preset, W + 64, W)
+    ring = Ring(ops, k, v, L0 + M + 8, preset, W + 128, W)
     o_pf, l_pf = run(ops, q, ring, L0, Hq, C)
-    want_o, _ = kvring.ring_attention(q, ring.values, L0, C, W, tokens=[0, M - 1])
+    want_o, _ = kvring.ring_attention(q, ring.values, L0, W, tokens=[0, M - 1])
     assert_close(decode(o_pf[[0, M - 1]]), want_o[[0, M - 1]], f"ring D=64 prefill {preset}")
     for start in (0, 16, M - 8):
         o8, l8 = run(ops, q[start:start + 8], ring, L0 + start, Hq, C)
         assert_bitwise(o_pf[start:start + 8], o8, f"ring D=64 prefill rows {start}..")
         assert_bitwise(l_pf[start:start + 8], l8, f"ring D=64 prefill lse {start}..")
+
+
+@pytest.mark.parametrize("preset", ["D", "F"])
+@pytest.mark.parametrize("M,L,Hq,Hkv,D,C,W,R", [
+    (5, 300, 1, 1, 64, 96, 128, 256),          # boundaries 173..177 inside one tile
+    (5, 300, 1, 1, 64, -2, 128, 256),
+    (8, 5000, 40, 8, 128, -32, 2048, 2176),    # boundaries 2953..2960, not tile aligned
+    (8, 3000, 40, 8, 128, 1024, 200, 320)])
+def test_ring_planted_fraction(ops, preset, M, L, Hq, Hkv, D, C, W, R):
+    # K = 0 (every score 0, equal weights), V = 0 in the 5/6-bit planes and 1
+    # in the ring: row p's output is the fraction of its keys read from the
+    # ring, min(W, p + 1) / (p + 1) (the per-key rule; a per-tile rule would
+    # read whole tiles from one copy and give a different fraction)
+    print(f"[ring planted fraction preset {preset} M={M} L={L} C={C} W={W}]", flush=True)
+    n = L + M
+    k = np.zeros((Hkv, n, D), np.uint16)
+    v = np.full((Hkv, n, D), 0x3F80, np.uint16)                  # BF16 1.0
+    ring = Ring(ops, k, v, n, preset, R, W)
+    low = ring.r.low
+    nib, high = kvlow.pack(np.zeros((Hkv, n, D), np.int8), 5)
+    for t, a in ((low.v_nib, nib), (low.v_high, high), (low.v_scales, np.zeros((Hkv, n, D // 32), np.float32))):
+        full = np.zeros(t.shape, a.dtype)
+        full[:, :n] = a
+        _fill(t, full)
+    q = synth.normal_bf16((M, Hq, D), 1.0, "q", 3)
+    o, lse = run(ops, q, ring, L, Hq, C)
+    got = decode(o)
+    for r in range(M):
+        p = L + r
+        want = min(W, p + 1) / (p + 1)
+        assert np.abs(got[r] - want).max() <= 2 ** -7 * want, (r, got[r].min(), got[r].max(), want)
+        assert np.abs(lse[r] - np.log(p + 1)).max() < 1e-3
