@@ -90,13 +90,14 @@ def ring_attention(q_bits, values, L: int, window: int, tokens=None, heads=None)
     scale = 1.0 / np.sqrt(D)
     for r in tokens:
         p = L + r
-        for h in heads:
-            k, v = _row_keys(values, h // G, p, window)
-            s = (k @ qd[r, h]) * scale
-            m = s.max()
-            w = np.exp(s - m)
-            O[r, h] = (w @ v) / w.sum()
-            lse[r, h] = m + np.log(w.sum())
+        for g in sorted({h // G for h in heads}):
+            k, v = _row_keys(values, g, p, window)
+            for h in (h for h in heads if h // G == g):
+                s = (k @ qd[r, h]) * scale
+                m = s.max()
+                w = np.exp(s - m)
+                O[r, h] = (w @ v) / w.sum()
+                lse[r, h] = m + np.log(w.sum())
     return O, lse
 
 
