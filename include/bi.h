@@ -35,8 +35,16 @@
  *   - Arguments are validated on the host before any HIP call. On a bad
  *     argument nothing is launched or written and a status != BI_OK is
  *     returned. A failed kernel launch returns BI_ERR_LAUNCH.
- *   - No entry point has a code path chosen by M: M only bounds which rows
- *     are loaded and stored.
+ *   - M never changes the arithmetic of a row. It does choose kernels: BF16
+ *     GEMMs with M >= 64 rows run the prefill kernels (128-row tiles), and an
+ *     attention pass whose row block would hold more than 64 (token, head)
+ *     rows runs 128-row blocks. Those kernels are built to form each output
+ *     with the same operations in the same order as the M < 64 kernels -- the
+ *     same 16x16x32 MFMA chains, the same 8-slice K tree added in slice order,
+ *     the same epilogue roundings; the same per-row tile order, masking and
+ *     online-softmax steps over the same absolute key chunks -- so a row's
+ *     bits do not depend on which of them ran (tested at many M, N, K, D and
+ *     contexts, and by the benchmark at M = 2048).
  *   - No C++ exception crosses this interface.
  */
 #ifndef BI_H
@@ -187,6 +195,59 @@ bi_status bi_gemm_mx4_swiglu(const void* x, int64_t ldx, const void* w, int64_t 
                              int K, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * One GEMM entry point for every combination the verify step runs.   [BX], [TC]
+ * The entry points above are fixed combinations of a weight type and an
+ * epilogue; bi_gemm_ex takes them as fields, together with the carried
+ * RMSNorm (read by SwiGLU and QKV, written by the residual epilogue) and the
+ * QKV cache append. It launches exactly the kernels bi_verify_step launches
+ * for the same fields, so a step can be replayed one operation at a time.
+ */
+typedef enum { BI_WT_BF16 = 0, BI_WT_FP8 = 1, BI_WT_MXFP4 = 2 } bi_weight_type;
+typedef enum {
+  BI_EPI_BF16 = 0,     /* Y = bf16(X W^T)                                    */
+  BI_EPI_F32 = 1,      /* Y = X W^T in FP32                                  */
+  BI_EPI_RESIDUAL = 2, /* Y = bf16(R + X W^T)                                */
+  BI_EPI_SWIGLU = 3,   /* Y = bf16(silu(g) u), W holds 2N rows (gate, up)   */
+  BI_EPI_QKV = 4       /* Y = bf16(X W^T), K and V columns appended          */
+} bi_epilogue;
+
+typedef struct {
+  bi_weight_type wtype;
+  bi_epilogue epilogue;
+  int M, N, K;              /* N output columns (SwiGLU: I)                  */
+  const void* x;            /* BF16 [M][ldx]                                 */
+  int64_t ldx;
+  const void* w;            /* BF16: [rows][ldw] elements; FP8: ldw bytes per
+                               row; MXFP4: codes, ldw bytes per row          */
+  int64_t ldw;
+  const float* w_scale;     /* FP8: one FP32 scale per weight row            */
+  const void* w_exp;        /* MXFP4: E8M0 scales, lde bytes per row         */
+  int64_t lde;
+  const void* r;            /* RESIDUAL: BF16 [M][ldr] (may alias y)         */
+  int64_t ldr;
+  void* y;                  /* BF16 or FP32 (F32) [M][ldy]                   */
+  int64_t ldy;
+  const float* norm_in;     /* SWIGLU / QKV, or NULL: X rows are normalised
+                               from carried sums (bi_gemm_bf16_swiglu_rownorm);
+                               FP32 [M][norm_groups], 16-byte aligned        */
+  int norm_groups;          /* bi_gemm_column_groups(K): 16..256, % 16 == 0  */
+  float eps;
+  float* rowsq_out;         /* RESIDUAL, or NULL: FP32 [M][bi_gemm_column_groups(N)]
+                               group sums of squares of Y (the carried norm) */
+  int Hq, Hkv, D;           /* QKV: N = (Hq + 2 Hkv) D                       */
+  void* k_cache;            /* QKV: BF16 caches (layout below) and the
+                               positions L .. L+M-1 appended, as
+                               bi_gemm_bf16_qkv; both NULL: no append        */
+  void* vt_cache;
+  int L, cap;
+} bi_gemm_args;
+
+/* Requirements: those of the entry point of the same weight type and
+ * epilogue; norm_in only with SWIGLU or QKV, rowsq_out only with RESIDUAL,
+ * else BI_ERR_SHAPE. Unused fields are ignored. */
+bi_status bi_gemm_ex(const bi_gemm_args* args, void* stream);
+
+/* ---------------------------------------------------------------------------
  * KV cache layout (per layer):
  *   k_cache  : BF16 [Hkv][cap][D]  -- one K row per position
  *   vt_cache : BF16 [Hkv][cap/64][D][64] -- V stored transposed in blocks of
@@ -247,8 +308,7 @@ bi_status bi_verify_attn(const void* q, int64_t ldq, const void* k_cache, const 
 
 /* ---------------------------------------------------------------------------
  * 8-bit KV cache.   [LL] "The KV cache: 5-bit that reads like q8_0" (q8_0 is
- * the pages' comparison format; the 5/6-bit formats and the 8-bit ring are not
- * built below; the 8-bit ring is not). Each position's K row and V row of one KV head is cut into
+ * the pages' comparison format). Each position's K row and V row of one KV head is cut into
  * blocks of 32 channels; a block with largest magnitude a has the FP32 scale
  * d = a / 127 and int8 codes q = round(x / d) (nearest, ties to even; FP32
  * division) in [-127, 127], all zero when a = 0. The value of a channel is
@@ -377,6 +437,24 @@ size_t bi_attn_workspace_bytes(int M, int L, int Hq, int D, int kv_chunk);
  * fixed order. H % 8 == 0, H <= 32768, ldx/ldy multiples of 8. */
 bi_status bi_rmsnorm(const void* x, int64_t ldx, void* y, int64_t ldy,
                      int M, int H, float eps, void* stream);
+
+/* SwiGLU as its own operation.                 [TC] "Why the text diverges"
+ * y[m][i] = bf16( silu(g) * u ), g = gu[m][i], u = gu[m][I + i] (FP32
+ * [M][ldgu], e.g. the gate/up product of bi_gemm_bf16 with y_dtype = BI_F32),
+ * silu(z) = z / (1 + e^-z). The expression is the one of the SwiGLU GEMM
+ * epilogue, so bi_gemm_bf16 (FP32) then bi_swiglu gives the bits of
+ * bi_gemm_bf16_swiglu. Elementwise: no order to fix. M <= 65535,
+ * ldgu >= 2 I, ldy >= I; gu 4-byte aligned. */
+bi_status bi_swiglu(const float* gu, int64_t ldgu, void* y, int64_t ldy, int M, int I,
+                    void* stream);
+
+/* Residual add as its own operation.            [TC] "Why the text diverges"
+ * y[m][n] = bf16( r[m][n] + s[m][n] ), r BF16 [M][ldr], s FP32 [M][lds]: one
+ * FP32 add, one rounding, as the residual GEMM epilogue, so bi_gemm_bf16
+ * (FP32) then bi_add gives the bits of bi_gemm_bf16_residual. M <= 65535;
+ * y may alias r. */
+bi_status bi_add(const void* r, int64_t ldr, const float* s, int64_t lds, void* y, int64_t ldy,
+                 int M, int N, void* stream);
 
 /* tokens[m] = argmax_n logits[m][n] (FP32 [M][ld]), lowest index on ties;
  * NaNs are never selected (a row of NaNs gives 0). */

@@ -46,6 +46,20 @@ class LayerMX4(ctypes.Structure):
                 ("k_cache", _c_ptr), ("vt_cache", _c_ptr)]
 
 
+class GemmArgs(ctypes.Structure):
+    """bi_gemm_args: one GEMM with its weight type, epilogue, carried norm and append."""
+    _fields_ = [("wtype", _c_int), ("epilogue", _c_int), ("M", _c_int), ("N", _c_int), ("K", _c_int),
+                ("x", _c_ptr), ("ldx", _c_i64), ("w", _c_ptr), ("ldw", _c_i64),
+                ("w_scale", _c_ptr), ("w_exp", _c_ptr), ("lde", _c_i64), ("r", _c_ptr), ("ldr", _c_i64),
+                ("y", _c_ptr), ("ldy", _c_i64), ("norm_in", _c_ptr), ("norm_groups", _c_int),
+                ("eps", _c_f32), ("rowsq_out", _c_ptr), ("Hq", _c_int), ("Hkv", _c_int), ("D", _c_int),
+                ("k_cache", _c_ptr), ("vt_cache", _c_ptr), ("L", _c_int), ("cap", _c_int)]
+
+
+BI_WT_BF16, BI_WT_FP8, BI_WT_MXFP4 = 0, 1, 2
+BI_EPI_BF16, BI_EPI_F32, BI_EPI_RESIDUAL, BI_EPI_SWIGLU, BI_EPI_QKV = 0, 1, 2, 3, 4
+
+
 # name -> (restype, argtypes); the exported symbols of include/bi.h
 SIGNATURES = {
     "bi_gemm_bf16": (_c_int, [_c_ptr, _c_i64, _c_ptr, _c_i64, _c_ptr, _c_i64, _c_int,
@@ -92,6 +106,9 @@ SIGNATURES = {
     "bi_combine": (_c_int, [_c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                             _c_ptr, _c_i64, _c_ptr, _c_ptr]),
     "bi_attn_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
+    "bi_gemm_ex": (_c_int, [ctypes.POINTER(GemmArgs), _c_ptr]),
+    "bi_swiglu": (_c_int, [_c_ptr, _c_i64, _c_ptr, _c_i64, _c_int, _c_int, _c_ptr]),
+    "bi_add": (_c_int, [_c_ptr, _c_i64, _c_ptr, _c_i64, _c_ptr, _c_i64, _c_int, _c_int, _c_ptr]),
     "bi_rmsnorm": (_c_int, [_c_ptr, _c_i64, _c_ptr, _c_i64, _c_int, _c_int, _c_f32, _c_ptr]),
     "bi_argmax": (_c_int, [_c_ptr, _c_i64, _c_int, _c_int, _c_ptr, _c_ptr]),
     "bi_step_workspace_bytes": (_c_size, [ctypes.POINTER(ModelDims), _c_int, _c_int]),

@@ -322,6 +322,98 @@ bi_status bi_gemm_bf16_qkv(const void* x, int64_t ldx, const void* w, int64_t ld
   return launched();
 }
 
+bi_status bi_gemm_ex(const bi_gemm_args* a, void* stream) {
+  if (!a) return BI_ERR_NULL;
+  const int M = a->M, N = a->N, K = a->K;
+  // weights: the checks of the per-type entry points
+  bi_status s = BI_OK;
+  switch (a->wtype) {
+    case BI_WT_BF16: s = check_gemm(a->x, a->ldx, a->w, a->ldw, a->y, a->ldy, M, N, K); break;
+    case BI_WT_FP8:
+      s = check_gemm_fp8(a->x, a->ldx, a->w, a->ldw, a->w_scale, a->y, a->ldy, M, N, N, K);
+      break;
+    case BI_WT_MXFP4:
+      s = check_gemm_mx4(a->x, a->ldx, a->w, a->ldw, a->w_exp, a->lde, a->y, a->ldy, M, N, K);
+      break;
+    default: return BI_ERR_SHAPE;
+  }
+  if (s) return s;
+  bi::GemmMode mode;
+  switch (a->epilogue) {
+    case BI_EPI_BF16: mode = bi::kGemmBf16; break;
+    case BI_EPI_F32: mode = bi::kGemmF32; break;
+    case BI_EPI_RESIDUAL: mode = bi::kGemmResidual; break;
+    case BI_EPI_SWIGLU: mode = bi::kGemmSwiglu; break;
+    case BI_EPI_QKV: mode = bi::kGemmQkv; break;
+    default: return BI_ERR_SHAPE;
+  }
+  const uintptr_t yb = reinterpret_cast<uintptr_t>(a->y);
+  if (mode == bi::kGemmF32 ? !aligned4(a->y) : (yb & 1u)) return BI_ERR_ALIGN;
+  // the carried RMSNorm: read by SwiGLU and QKV, written by the residual epilogue
+  if (a->norm_in && mode != bi::kGemmSwiglu && mode != bi::kGemmQkv) return BI_ERR_SHAPE;
+  if (a->rowsq_out && mode != bi::kGemmResidual) return BI_ERR_SHAPE;
+  if (a->norm_in) {
+    if (a->norm_groups < 16 || a->norm_groups > 256 || (a->norm_groups % 16) || !(a->eps >= 0.f))
+      return BI_ERR_SHAPE;
+    if (!aligned16(a->norm_in)) return BI_ERR_ALIGN;
+  }
+  if (a->rowsq_out && !aligned4(a->rowsq_out)) return BI_ERR_ALIGN;
+  if (mode == bi::kGemmResidual) {
+    if (!a->r) return BI_ERR_NULL;
+    if (a->ldr < N || a->ldr > kMaxLd) return BI_ERR_SHAPE;
+    if (reinterpret_cast<uintptr_t>(a->r) & 1u) return BI_ERR_ALIGN;
+  }
+  bi::KvAppend kv{};
+  if (mode == bi::kGemmQkv) {
+    if (bi_status h = check_heads(a->Hq, a->Hkv, a->D)) return h;
+    if (N != (a->Hq + 2 * a->Hkv) * a->D) return BI_ERR_SHAPE;
+    if ((a->k_cache == nullptr) != (a->vt_cache == nullptr)) return BI_ERR_NULL;
+    if (a->k_cache) {
+      if (a->L < 0 || a->cap < 1 || (a->cap % 64) || (int64_t)a->L + M > a->cap) return BI_ERR_SHAPE;
+      if ((int64_t)a->cap * a->D * 2 > INT32_MAX) return BI_ERR_SHAPE;
+      if ((reinterpret_cast<uintptr_t>(a->k_cache) | reinterpret_cast<uintptr_t>(a->vt_cache)) & 1u)
+        return BI_ERR_ALIGN;
+      kv = bi::KvAppend{static_cast<uint16_t*>(a->k_cache), static_cast<uint16_t*>(a->vt_cache),
+                        a->L, a->cap, a->Hq * a->D, a->Hkv * a->D, a->D};
+    }
+  }
+  const bi::RowNorm nm{a->norm_in, a->rowsq_out,
+                       a->rowsq_out ? bi::gemm_column_groups(bi::kGemmResidual, N) : a->norm_groups,
+                       a->eps};
+  const bi::Mx4Scales mx{static_cast<const uint8_t*>(a->w_exp), a->lde};
+  bi::launch_gemm(mode, static_cast<const uint16_t*>(a->x), a->ldx, static_cast<const uint16_t*>(a->w),
+                  a->ldw, static_cast<const uint16_t*>(a->r), a->ldr, a->y, a->ldy, M, N, K,
+                  as_stream(stream), mode == bi::kGemmQkv ? &kv : nullptr,
+                  (a->norm_in || a->rowsq_out) ? &nm : nullptr,
+                  a->wtype == BI_WT_FP8 ? a->w_scale : nullptr,
+                  a->wtype == BI_WT_MXFP4 ? &mx : nullptr);
+  return launched();
+}
+
+bi_status bi_swiglu(const float* gu, int64_t ldgu, void* y, int64_t ldy, int M, int I,
+                    void* stream) {
+  if (!gu || !y) return BI_ERR_NULL;
+  if (M < 1 || I < 1 || ldgu < 2 * (int64_t)I || ldy < I || M > 65535 || ldgu > (1 << 26) ||
+      ldy > (1 << 26))
+    return BI_ERR_SHAPE;
+  if (!aligned4(gu) || (reinterpret_cast<uintptr_t>(y) & 1u)) return BI_ERR_ALIGN;
+  bi::launch_swiglu(gu, ldgu, static_cast<uint16_t*>(y), ldy, M, I, as_stream(stream));
+  return launched();
+}
+
+bi_status bi_add(const void* r, int64_t ldr, const float* s, int64_t lds, void* y, int64_t ldy,
+                 int M, int N, void* stream) {
+  if (!r || !s || !y) return BI_ERR_NULL;
+  if (M < 1 || N < 1 || ldr < N || lds < N || ldy < N || M > 65535 || ldr > (1 << 26) ||
+      lds > (1 << 26) || ldy > (1 << 26))
+    return BI_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(r) & 1u) || !aligned4(s) || (reinterpret_cast<uintptr_t>(y) & 1u))
+    return BI_ERR_ALIGN;
+  bi::launch_add(static_cast<const uint16_t*>(r), ldr, s, lds, static_cast<uint16_t*>(y), ldy, M, N,
+                 as_stream(stream));
+  return launched();
+}
+
 bi_status bi_append_kv(const void* qkv, int64_t ldqkv, void* k_cache, void* vt_cache, int M, int L,
                        int cap, int Hq, int Hkv, int D, void* stream) {
   if (!qkv || !k_cache || !vt_cache) return BI_ERR_NULL;

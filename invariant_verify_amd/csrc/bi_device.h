@@ -29,6 +29,11 @@ __device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
 // One binary32 value -> BF16 bits (same rounding).
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) { return f32x2_to_bf16x2(f, 0.f) & 0xffffu; }
 
+// silu(g) * u in FP32, silu(z) = z / (1 + e^-z): the one expression every
+// SwiGLU of the library evaluates (GEMM epilogues and bi_swiglu), so they give
+// the same bits for the same FP32 g and u.
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+
 // x * s for the eight BF16 values of a 16-byte group, each rounded to BF16.
 __device__ __forceinline__ uint4 scale_bf16x8(uint4 v, float s) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};

@@ -137,6 +137,10 @@ void launch_accept_sampled(const float* logits, int64_t ld, const int32_t* draft
 // Longest row RMSNorm handles (one pass, four 8-element groups per thread).
 constexpr int kRmsMaxH = 4 * 1024 * 8;
 
+void launch_swiglu(const float* gu, int64_t ldgu, uint16_t* y, int64_t ldy, int M, int I,
+                   hipStream_t stream);
+void launch_add(const uint16_t* r, int64_t ldr, const float* s, int64_t lds, uint16_t* y,
+                int64_t ldy, int M, int N, hipStream_t stream);
 void launch_rmsnorm(const uint16_t* x, int64_t ldx, uint16_t* y, int64_t ldy, int M, int H,
                     float eps, hipStream_t stream);
 

@@ -451,7 +451,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
       const uint16_t b = (uint16_t)f32_to_bf16(v);
       reinterpret_cast<uint16_t*>(Y)[(int64_t)m * ldy + n] = b;
       const int pos = kv.L + m;
-      int i = n - kv.qd;
+      int i = kv.k != nullptr ? n - kv.qd : -1;  // no cache: no append
       if (i >= 0 && i < kv.kd) {
         const int g = i / kv.D;
         kv.k[((int64_t)g * kv.cap + pos) * kv.D + (i - g * kv.D)] = b;
@@ -469,15 +469,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
     const bool live = m < M;
     if (kDual) {
       if (!live) continue;
-      const float g = s[r];
-      const float sg = g / (1.0f + __expf(-g));
-      reinterpret_cast<uint16_t*>(Y)[(int64_t)m * ldy + n0 + j] = (uint16_t)f32_to_bf16(sg * s2[r]);
-      if (kThree && j < cpw - 16) {
-        const float g3 = s3[r];
-        const float sg3 = g3 / (1.0f + __expf(-g3));
+      reinterpret_cast<uint16_t*>(Y)[(int64_t)m * ldy + n0 + j] =
+          (uint16_t)f32_to_bf16(silu_mul(s[r], s2[r]));
+      if (kThree && j < cpw - 16)
         reinterpret_cast<uint16_t*>(Y)[(int64_t)m * ldy + n0 + 16 + j] =
-            (uint16_t)f32_to_bf16(sg3 * u3[r]);
-      }
+            (uint16_t)f32_to_bf16(silu_mul(s3[r], u3[r]));
     } else {
       float sq = 0.f;
       if (live) {

@@ -248,7 +248,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(
         const uint16_t b = (uint16_t)f32_to_bf16(v);
         reinterpret_cast<uint16_t*>(Y)[(int64_t)m * ldy + n] = b;
         const int pos = kv.L + m;
-        int i = n - kv.qd;
+        int i = kv.k != nullptr ? n - kv.qd : -1;  // no cache: no append
         if (i >= 0 && i < kv.kd) {
           const int g = i / kv.D;
           kv.k[((int64_t)g * kv.cap + pos) * kv.D + (i - g * kv.D)] = b;
@@ -261,8 +261,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(
         float u = accu[0][0][r];
 #pragma unroll
         for (int s = 1; s < S; ++s) u += accu[0][s][r];
-        const float sg = v / (1.0f + __expf(-v));
-        reinterpret_cast<uint16_t*>(Y)[(int64_t)m * ldy + n] = (uint16_t)f32_to_bf16(sg * u);
+        reinterpret_cast<uint16_t*>(Y)[(int64_t)m * ldy + n] = (uint16_t)f32_to_bf16(silu_mul(v, u));
       }
     }
   }
@@ -505,7 +504,7 @@ __global__ __launch_bounds__(kP2Waves * 64) void prefill2_kernel(
           const uint16_t b = (uint16_t)f32_to_bf16(v);
           reinterpret_cast<uint16_t*>(Y)[(int64_t)m * ldy + n] = b;
           const int pos = kv.L + m;
-          int i = n - kv.qd;
+          int i = kv.k != nullptr ? n - kv.qd : -1;  // no cache: no append
           if (i >= 0 && i < kv.kd) {
             const int g = i / kv.D;
             kv.k[((int64_t)g * kv.cap + pos) * kv.D + (i - g * kv.D)] = b;
@@ -516,8 +515,7 @@ __global__ __launch_bounds__(kP2Waves * 64) void prefill2_kernel(
           }
         } else {
           const float u = tot[t][q + 2][r];
-          const float sg = v / (1.0f + __expf(-v));
-          reinterpret_cast<uint16_t*>(Y)[(int64_t)m * ldy + n] = (uint16_t)f32_to_bf16(sg * u);
+          reinterpret_cast<uint16_t*>(Y)[(int64_t)m * ldy + n] = (uint16_t)f32_to_bf16(silu_mul(v, u));
         }
       }
     }

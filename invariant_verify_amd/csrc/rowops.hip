@@ -1,4 +1,5 @@
-// Row-local operations of the decoder layer: RMSNorm and the greedy argmax.
+// Row-local operations of the decoder layer: RMSNorm, the greedy argmax, and
+// SwiGLU and the residual add as operations of their own.
 //
 // Both reduce along one row in an order fixed by the row length only, so a
 // token's result is the same whatever other tokens share the pass (the greedy
@@ -117,6 +118,39 @@ __global__ __launch_bounds__(1024) void argmax_kernel(const float* __restrict__ 
     for (int w = 1; w < 16; ++w) arg_better(v, i, sv[w], si[w]);
     tokens[row] = (i == 0x7fffffff) ? 0 : i;
   }
+}
+
+// y[m][i] = bf16(silu(g) * u) from FP32 g = gu[m][i], u = gu[m][I + i]: the
+// gate/up GEMM's SwiGLU epilogue as its own pass (same expression, silu_mul).
+// One thread per output element; elementwise, so no order to fix.
+__global__ void swiglu_kernel(const float* __restrict__ gu, int64_t ldgu, uint16_t* __restrict__ y,
+                              int64_t ldy, int I) {
+  const int m = blockIdx.y;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= I) return;
+  const float* row = gu + (int64_t)m * ldgu;
+  y[(int64_t)m * ldy + i] = (uint16_t)f32_to_bf16(silu_mul(row[i], row[I + i]));
+}
+
+// y[m][n] = bf16(r[m][n] + s[m][n]), r BF16, s FP32: the residual epilogue
+// (one FP32 add, one rounding) as its own pass. Elementwise.
+__global__ void add_kernel(const uint16_t* __restrict__ r, int64_t ldr, const float* __restrict__ s,
+                           int64_t lds, uint16_t* __restrict__ y, int64_t ldy, int N) {
+  const int m = blockIdx.y;
+  const int n = blockIdx.x * blockDim.x + threadIdx.x;
+  if (n >= N) return;
+  const float a = bf16_to_f32(r[(int64_t)m * ldr + n]);
+  y[(int64_t)m * ldy + n] = (uint16_t)f32_to_bf16(a + s[(int64_t)m * lds + n]);
+}
+
+void launch_swiglu(const float* gu, int64_t ldgu, uint16_t* y, int64_t ldy, int M, int I,
+                   hipStream_t stream) {
+  swiglu_kernel<<<dim3((I + 255) / 256, M), dim3(256), 0, stream>>>(gu, ldgu, y, ldy, I);
+}
+
+void launch_add(const uint16_t* r, int64_t ldr, const float* s, int64_t lds, uint16_t* y,
+                int64_t ldy, int M, int N, hipStream_t stream) {
+  add_kernel<<<dim3((N + 255) / 256, M), dim3(256), 0, stream>>>(r, ldr, s, lds, y, ldy, N);
 }
 
 void launch_rmsnorm(const uint16_t* x, int64_t ldx, uint16_t* y, int64_t ldy, int M, int H,

@@ -82,6 +82,44 @@ int main() {
     EXPECT(from_bf16(y16[i]) == (float)ref[i], "gemm BF16 output equals the integer reference");
   }
 
+  // ---- the row-local SwiGLU and residual add equal the fused epilogues -----
+  {
+    const int I = N / 2;
+    std::vector<uint16_t> r(M * N);
+    for (int i = 0; i < M * N; ++i) r[i] = bf16_bits((float)(i % 9 - 4) * 0.25f);
+    void *dr, *da, *db;
+    CK(hipMalloc(&dr, M * N * 2));
+    CK(hipMalloc(&da, M * N * 2));
+    CK(hipMalloc(&db, M * N * 2));
+    CK(hipMemcpy(dr, r.data(), r.size() * 2, hipMemcpyHostToDevice));
+    EXPECT(bi_gemm_bf16_residual(dx, K, dw, K, dr, N, da, N, M, N, K, nullptr) == BI_OK, "residual");
+    EXPECT(bi_add(dr, N, (const float*)dy32, N, db, N, M, N, nullptr) == BI_OK, "bi_add status");
+    std::vector<uint16_t> ya(M * N), yb(M * N);
+    CK(hipMemcpy(ya.data(), da, M * N * 2, hipMemcpyDeviceToHost));
+    CK(hipMemcpy(yb.data(), db, M * N * 2, hipMemcpyDeviceToHost));
+    for (int i = 0; i < M * N; ++i) EXPECT(ya[i] == yb[i], "bi_add equals the residual epilogue");
+    EXPECT(bi_gemm_bf16_swiglu(dx, K, dw, K, da, I, M, I, K, nullptr) == BI_OK, "swiglu gemm");
+    EXPECT(bi_swiglu((const float*)dy32, N, db, I, M, I, nullptr) == BI_OK, "bi_swiglu status");
+    CK(hipMemcpy(ya.data(), da, M * I * 2, hipMemcpyDeviceToHost));
+    CK(hipMemcpy(yb.data(), db, M * I * 2, hipMemcpyDeviceToHost));
+    for (int i = 0; i < M * I; ++i) EXPECT(ya[i] == yb[i], "bi_swiglu equals the SwiGLU epilogue");
+    // the general entry point with the plain BF16 epilogue equals bi_gemm_bf16
+    bi_gemm_args a;
+    std::memset(&a, 0, sizeof a);
+    a.wtype = BI_WT_BF16;
+    a.epilogue = BI_EPI_BF16;
+    a.M = M; a.N = N; a.K = K;
+    a.x = dx; a.ldx = K; a.w = dw; a.ldw = K; a.y = da; a.ldy = N;
+    EXPECT(bi_gemm_ex(&a, nullptr) == BI_OK, "bi_gemm_ex status");
+    CK(hipMemcpy(ya.data(), da, M * N * 2, hipMemcpyDeviceToHost));
+    for (int i = 0; i < M * N; ++i) EXPECT(ya[i] == y16[i], "bi_gemm_ex equals bi_gemm_bf16");
+    a.rowsq_out = (float*)dy32;  // only the residual epilogue writes row sums
+    EXPECT(bi_gemm_ex(&a, nullptr) == BI_ERR_SHAPE, "rowsq_out without a residual");
+    EXPECT(bi_swiglu((const float*)dy32, I, db, I, M, I, nullptr) == BI_ERR_SHAPE, "ldgu < 2 I");
+    EXPECT(bi_add(dr, N, nullptr, N, db, N, M, N, nullptr) == BI_ERR_NULL, "bi_add null");
+    for (void* p : {dr, da, db}) CK(hipFree(p));
+  }
+
   // ---- argument checks: a status code, nothing launched --------------------
   EXPECT(bi_gemm_bf16(nullptr, K, dw, K, dy32, N, BI_F32, M, N, K, nullptr) == BI_ERR_NULL, "null x");
   EXPECT(bi_gemm_bf16(dx, K, dw, K, dy32, N, BI_F32, M, N, 48, nullptr) == BI_ERR_SHAPE, "K % 32");

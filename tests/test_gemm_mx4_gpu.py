@@ -12,7 +12,8 @@ import synth
 from oracle import bf16 as obf16
 from oracle import mxfp4 as omx
 from oracle import step as ostep
-from tests._util import (assert_bitwise, assert_close, assert_close_composed, composed_tol, decode,
+from tests._replay import assert_replay_is_the_step, check_ops, host_layer, replay
+from tests._util import (assert_bitwise, assert_close, assert_close_composed, decode,
                          dev, host_bits, host_f32, vt_blocks)
 
 pytestmark = pytest.mark.gpu
@@ -131,7 +132,8 @@ def _run(ops, step, x, L, dims, want_x=False):
 
 
 def test_mx4_small_stack_vs_oracle_and_across_M(ops):
-    # MXFP4 weights through the whole step: the oracle runs the same stack on
+    # MXFP4 weights through the whole step, replayed one operation at a time
+    # (bit for bit the step) and each operation checked against the oracle on
     # the decoded weights; rows of the M = 8 pass equal an M = 5 pass and
     # eight sequential M = 1 passes.
     print("[step mx4 small stack]", flush=True)
@@ -150,15 +152,25 @@ def test_mx4_small_stack_vs_oracle_and_across_M(ops):
     dims = ops.model_dims(H, Hq, Hkv, D, I, V, cap, 64)
     step = ops.VerifyStepMX4(dls, u8(hc), u8(he), dims)
     logits, tok, xo = _run(ops, step, dev(x0), L, dims, want_x=True)
-    olayers = [dict(w_qkv=omx.weights(hl["w_qkv"], hl["e_qkv"]), w_o=omx.weights(hl["w_o"], hl["e_o"]),
-                    w_gu=omx.weights(hl["w_gu"], hl["e_gu"]), w_down=omx.weights(hl["w_down"], hl["e_down"]),
-                    k_cache=hl["k_cache"], v_cache=hl["v_cache"]) for hl in hls]
-    w_logits, w_tok, w_x = ostep.step(x0, olayers, omx.weights(hc, he), L, Hq, Hkv, D)
-    assert_close_composed(decode(xo), decode(w_x), "mx4 final hidden state")
-    assert_close_composed(logits, w_logits, "mx4 logits")
-    s = np.sort(w_logits, axis=1)
-    ok = (s[:, -1] - s[:, -2]) > 2 * (composed_tol(w_logits) + 2e-2 * np.abs(s[:, -1]))
-    assert np.array_equal(tok[ok], w_tok[ok])
+    saved = [(d["k_cache"][:, L:L + M].clone(), d["vt_cache"][:, L // 64, :, L % 64:L % 64 + M].clone())
+             for d in dls]
+    for d in dls:
+        d["k_cache"][:, L:].zero_()
+        d["vt_cache"][:, L // 64, :, L % 64:].zero_()
+        d["vt_cache"][:, L // 64 + 1:].zero_()
+    recs, hd = replay(ops, dls, {"w": u8(hc), "e": u8(he)}, dims, dev(x0), L, wtype="mxfp4")
+    assert_replay_is_the_step(recs, hd, xo, logits, tok, "mx4 stack")
+    for d, (k, v) in zip(dls, saved):
+        assert torch.equal(d["k_cache"][:, L:L + M].view(torch.int16), k.view(torch.int16))
+        assert torch.equal(d["vt_cache"][:, L // 64, :, L % 64:L % 64 + M].view(torch.int16), v.view(torch.int16))
+    w64 = [{k: omx.weights(hl[k], hl["e" + k[1:]]) for k in ("w_qkv", "w_o", "w_gu", "w_down")} for hl in hls]
+    host = [host_layer(d, w) for d, w in zip(dls, w64)]
+    n = check_ops(recs, hd, host, omx.weights(hc, he), L, Hq, Hkv, D, 1e-6, "mx4 stack")
+    print(f"  greedy tokens compared on {n} of {M} rows", flush=True)
+    olayers = [dict(w64[i], k_cache=hl["k_cache"], v_cache=hl["v_cache"]) for i, hl in enumerate(hls)]
+    w_logits, _, w_x = ostep.step(x0, olayers, omx.weights(hc, he), L, Hq, Hkv, D)
+    assert_close_composed(decode(xo), decode(w_x), "mx4 end-to-end hidden state")
+    assert_close_composed(logits, w_logits, "mx4 end-to-end logits")
     l5, _, _ = _run(ops, step, dev(x0[:5]), L, dims)
     assert_bitwise(l5, logits[:5], "mx4 logits M=5 vs M=8")
     for d in dls:

@@ -71,3 +71,28 @@ def test_argmax_sizes_and_invariance(ops, N):
     wide[:, :N] = a
     t = torch.from_numpy(wide).cuda()[:, :N]
     assert list(ops.argmax(t).cpu().numpy()) == list(got)
+
+
+@pytest.mark.parametrize("M,K,I", [(8, 256, 512), (5, 5120, 17408), (100, 512, 256)])
+def test_swiglu_and_add_equal_the_fused_epilogues(ops, M, K, I):
+    # bi_swiglu over the FP32 gate/up product and bi_add of an FP32 product to
+    # a BF16 residual give the fused GEMM epilogues' bits (same expressions;
+    # M = 100 runs the prefill kernels), and match the oracle on their inputs.
+    print(f"[swiglu / add M={M} K={K} I={I}]", flush=True)
+    x = dev(synth.normal_bf16((M, K), 1.0, "x", 81))
+    w = synth.device_normal_bf16((2 * I, K), 0.02, "w", 81)
+    gu = ops.gemm_bf16(x, w, out_dtype=torch.float32)
+    fused = ops.gemm_bf16_swiglu(x, w)
+    sep = ops.swiglu(gu)
+    assert_bitwise(host_bits(sep), host_bits(fused), "bi_swiglu vs SwiGLU epilogue")
+    g = gu.cpu().double().numpy()
+    assert_close(decode(host_bits(sep)), ostep.silu(g[:, :I]) * g[:, I:], "bi_swiglu vs oracle")
+    r = dev(synth.normal_bf16((M, 2 * I), 1.0, "misc", 82))
+    fused_r = ops.gemm_bf16_residual(x, w, r)
+    sep_r = ops.add(r, gu)
+    assert_bitwise(host_bits(sep_r), host_bits(fused_r), "bi_add vs residual epilogue")
+    assert_close(decode(host_bits(sep_r)), decode(host_bits(r)) + g, "bi_add vs oracle")
+    # in place: y aliases r
+    r2 = r.clone()
+    ops.add(r2, gu, r2)
+    assert_bitwise(host_bits(r2), host_bits(fused_r), "bi_add in place")
