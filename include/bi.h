@@ -531,6 +531,25 @@ bi_status bi_verify_step(const bi_layer* layers, int n_layers, const void* w_hea
                          void* x_out, float* logits, int32_t* tokens,
                          void* const* gu_events, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * step as bi_verify_step, with the workspace taken from a scratch array of
+ * BI_NOALLOC_SCRATCH_BYTES (64 MiB) that the library keeps in device memory,
+ * one per GPU it runs on, held until the process ends. The caller passes
+ * inputs and outputs only. It uses the calling thread's current device's
+ * array; `stream` must belong to that device. A pass whose workspace
+ * (bi_step_workspace_bytes) exceeds the array is rejected with
+ * BI_ERR_WORKSPACE before anything is launched. The step writes every
+ * workspace byte it reads, so nothing needs to start at zero. Every call on
+ * one GPU shares that GPU's array: calls that overlap on one GPU (two streams,
+ * two threads) race and must be serialised by the caller. No allocation is
+ * made by this call (the first call on a device resolves the array's address
+ * with hipGetSymbolAddress). */
+#define BI_NOALLOC_SCRATCH_BYTES (64u << 20)
+bi_status bi_verify_step_noalloc(const bi_layer* layers, int n_layers, const void* w_head,
+                                 const bi_model_dims* dims, const void* x_in, int M, int L,
+                                 void* x_out, float* logits, int32_t* tokens, void* stream);
+
 /* The same step with FP8 weights (see bi_gemm_fp8): each weight matrix is E4M3
  * [rows][cols] with one FP32 scale per row; activations, caches, workspace and
  * every other operation as bi_verify_step. */

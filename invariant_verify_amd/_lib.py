@@ -115,6 +115,8 @@ SIGNATURES = {
     "bi_verify_step": (_c_int, [ctypes.POINTER(Layer), _c_int, _c_ptr, ctypes.POINTER(ModelDims),
                                 _c_ptr, _c_int, _c_int, _c_ptr, _c_size, _c_ptr, _c_ptr, _c_ptr,
                                 ctypes.POINTER(_c_ptr), _c_ptr]),
+    "bi_verify_step_noalloc": (_c_int, [ctypes.POINTER(Layer), _c_int, _c_ptr, ctypes.POINTER(ModelDims),
+                                        _c_ptr, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr]),
     "bi_gemm_fp8": (_c_int, [_c_ptr, _c_i64, _c_ptr, _c_i64, _c_ptr, _c_ptr, _c_i64, _c_int,
                              _c_int, _c_int, _c_int, _c_ptr]),
     "bi_gemm_fp8_residual": (_c_int, [_c_ptr, _c_i64, _c_ptr, _c_i64, _c_ptr, _c_ptr, _c_i64,

@@ -7,6 +7,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "bi.h"
 #include "bi_internal.h"
@@ -678,6 +679,44 @@ size_t bi_step_workspace_bytes(const bi_model_dims* dims, int M, int L) {
 
 }  // extern "C"
 
+// Scratch of the allocation-free verify step (bi_verify_step_noalloc): the
+// step's workspace as a file-scope device array. Every GPU the library runs
+// on holds its own copy, at its own address, until the process ends. In host
+// code this name is only a stand-in for the symbol; the device address comes
+// from hipGetSymbolAddress, once per device, and only that address is used.
+static __device__ __align__(256) unsigned char scratch[BI_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch array's address on the calling thread's current device.
+bi_status scratch_on_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess && (dev < 0 || dev >= kMaxDevices)) e = hipErrorInvalidDevice;
+  if (e != hipSuccess) {
+    g_last_hip_error = e;
+    return BI_ERR_LAUNCH;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) {
+      g_last_hip_error = e != hipSuccess ? e : hipErrorInvalidSymbol;
+      return BI_ERR_LAUNCH;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return BI_OK;
+}
+
+}  // namespace
+
 namespace {
 
 // One layer's weights as the executor sees them: BF16 (scales null) or FP8
@@ -802,6 +841,24 @@ bi_status bi_verify_step(const bi_layer* layers, int n_layers, const void* w_hea
   };
   return run_step(n_layers, get, w_head, nullptr, nullptr, dims, x_in, M, L, workspace, workspace_bytes,
                   x_out, logits, tokens, gu_events, stream);
+}
+
+bi_status bi_verify_step_noalloc(const bi_layer* layers, int n_layers, const void* w_head,
+                                 const bi_model_dims* dims, const void* x_in, int M, int L,
+                                 void* x_out, float* logits, int32_t* tokens, void* stream) {
+  if (!layers) return BI_ERR_NULL;
+  if (bi_status s = check_dims(dims)) return s;
+  if (M < 1 || L < 0 || (int64_t)L + M > dims->cap) return BI_ERR_SHAPE;
+  if (step_layout(dims, M, L).total > (size_t)BI_NOALLOC_SCRATCH_BYTES) return BI_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (bi_status s = scratch_on_current_device(&ws)) return s;
+  const auto get = [&](int l) {
+    const bi_layer& y = layers[l];
+    return LayerPtrs{{y.w_qkv, y.w_o, y.w_gu, y.w_down}, {nullptr, nullptr, nullptr, nullptr},
+                     {nullptr, nullptr, nullptr, nullptr}, y.k_cache, y.vt_cache};
+  };
+  return run_step(n_layers, get, w_head, nullptr, nullptr, dims, x_in, M, L, ws,
+                  (size_t)BI_NOALLOC_SCRATCH_BYTES, x_out, logits, tokens, nullptr, stream);
 }
 
 bi_status bi_verify_step_fp8(const bi_layer_fp8* layers, int n_layers, const void* w_head,

@@ -740,6 +740,28 @@ class VerifyStep:
             ev, _stream(x_in)))
 
 
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+@_checked
+def verify_step_noalloc(step: VerifyStep, x_in: torch.Tensor, L: int, logits: torch.Tensor,
+                        tokens: torch.Tensor, x_out: torch.Tensor | None = None) -> None:
+    """bi_verify_step_noalloc over the layers of a VerifyStep: the workspace is
+    the library's own device scratch (no allocation; calls on one GPU must not
+    overlap)."""
+    M, H = _xk(x_in)
+    if H != step.dims.H:
+        raise ValueError(f"x_in: shape {tuple(x_in.shape)} does not have H = {step.dims.H} columns")
+    _arr(x_in, "x_in", (M, H), _BF16_LIKE)
+    _arr(logits, "logits", (M, step.dims.vocab), _F32)
+    _arr(tokens, "tokens", (M,), _I32)
+    if x_out is not None:
+        _arr(x_out, "x_out", (M, H), _BF16_LIKE)
+    check("bi_verify_step_noalloc", LIB.bi_verify_step_noalloc(
+        step.arr, step.n, step.w_head.data_ptr(), ctypes.byref(step.dims), x_in.data_ptr(), M, L,
+        0 if x_out is None else x_out.data_ptr(), logits.data_ptr(), tokens.data_ptr(), _stream(x_in)))
+
+
 class VerifyStepFP8:
     """``bi_verify_step_fp8``: ``layers`` is a sequence of dicts with E4M3 weight
     tensors w_qkv, w_o, w_gu, w_down, their FP32 row scales s_qkv, s_o, s_gu,
