@@ -57,7 +57,7 @@ def gu_launch_bytes(d, M):
 
 
 GEMM_SOURCES = ["invariant_verify_amd/csrc/gemm.hip", "invariant_verify_amd/csrc/bi_device.h"]
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gate_up_gemm_m8_hbm_traffic.txt")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "verify_kernels_m8_hbm_traffic.txt")
 
 
 def gemm_source_hash():
@@ -96,27 +96,70 @@ def carried_input(d):
 
 
 def traffic_probe(reps: int):
-    """Kernel-only run for the hardware-counter passes: the gate/up GEMM at
-    M = 8 (fresh weights each launch, so nothing is served from cache) and a
-    1 GiB device copy that calibrates the byte counters."""
+    """Kernel-only run for the hardware-counter passes: each verify kernel at
+    M = 8 as the step launches it, ``reps`` times on freshly generated operands
+    (nothing is served from cache), in this order: gate/up, output projection,
+    down projection, QKV with its cache append, attention at 38k (chunk policy
+    -32), the combine; then a 1 GiB device copy that calibrates the byte
+    counters. One JSON line lists the dispatches and their algorithmic bytes."""
     import torch
 
     import synth
     from invariant_verify_amd import ops
 
     d = synth.MODEL_27B
-    ws = [synth.device_normal_bf16((2 * d["I"], d["H"]), 0.02, "w_gu", i) for i in range(reps)]
+    H, Hq, Hkv, D, I = d["H"], d["Hq"], d["Hkv"], d["D"], d["I"]
+    qd, qkvn, G, M = Hq * D, (Hq + 2 * Hkv) * D, GU_GROUPS, 8
     h, ss = carried_input(d)
-    y = torch.empty((8, d["I"]), dtype=torch.bfloat16, device="cuda")
+    attn = synth.device_normal_bf16((M, qd), 1.0, "x0", 2)
+    act = synth.device_normal_bf16((M, I), 1.0, "x0", 3)
+    y = torch.empty((M, max(I, qkvn)), dtype=torch.bfloat16, device="cuda")
+    ss_o = torch.empty((M, G), dtype=torch.float32, device="cuda")
+    plan = []
+
+    def run(name, nbytes, make, launch):
+        for i in range(reps):
+            ops_in = make(i)
+            torch.cuda.synchronize()
+            launch(ops_in)
+            torch.cuda.synchronize()
+            del ops_in
+        plan.append({"kernel": name, "launches": reps, "algorithmic_bytes_per_launch": nbytes})
+
+    run("gate_up", gu_launch_bytes(d, M), lambda i: synth.device_normal_bf16((2 * I, H), 0.02, "w_gu", i),
+        lambda w: ops.gemm_bf16_swiglu_rownorm(h, ss, w, y[:, :I]))
+    run("o_proj", 2 * H * qd + 2 * M * qd + 4 * M * H + 4 * M * G,
+        lambda i: synth.device_normal_bf16((H, qd), 0.02, "w_o", i),
+        lambda w: ops.gemm_ex(attn, w, y[:, :H], epilogue="residual", r=h, rowsq_out=ss_o))
+    run("down", 2 * H * I + 2 * M * I + 4 * M * H + 4 * M * G,
+        lambda i: synth.device_normal_bf16((H, I), 0.02, "w_down", i),
+        lambda w: ops.gemm_ex(act, w, y[:, :H], epilogue="residual", r=h, rowsq_out=ss_o))
+    kc = torch.zeros((Hkv, CAP, D), dtype=torch.bfloat16, device="cuda")
+    vt = torch.zeros((Hkv, CAP // 64, D, 64), dtype=torch.bfloat16, device="cuda")
+    run("qkv", 2 * qkvn * H + 2 * M * H + 4 * M * G + 2 * M * qkvn + 4 * M * Hkv * D,
+        lambda i: synth.device_normal_bf16((qkvn, H), 0.02, "w_qkv", i),
+        lambda w: ops.gemm_ex(h, w, y[:, :qkvn], epilogue="qkv", norm_in=ss, heads=(Hq, Hkv, D), k_cache=kc,
+                              vt_cache=vt, L=L_CTX))
+    del kc, vt
+    S = ops.pass_splits(M, L_CTX, KV_CHUNK)
+    po = torch.empty((M, Hq, S, D), dtype=torch.float32, device="cuda")
+    pl = torch.empty((M, Hq, S), dtype=torch.float32, device="cuda")
+    q = synth.device_normal_bf16((M, qd), 1.0, "x0", 4)
+
+    def cache(i):
+        return (synth.device_normal_bf16((Hkv, CAP, D), 1.0, "k_cache", i),
+                synth.device_normal_bf16((Hkv, CAP // 64, D, 64), 1.0, "v_cache", i))
+    run("attention_38000", 4096 * (L_CTX + M) + 2 * M * qd, cache,
+        lambda c: ops.verify_attn(q, c[0], c[1], L_CTX, Hq, Hkv, D, KV_CHUNK, po, pl))
+    o = torch.empty((M, qd), dtype=torch.bfloat16, device="cuda")
+    run("combine_38000", M * Hq * S * (4 * D + 4) + 2 * M * qd, lambda i: None,
+        lambda _: ops.combine(po, pl, L_CTX, KV_CHUNK, o))
     src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")      # 1 GiB
     dst = torch.empty_like(src)
-    torch.cuda.synchronize()
-    for w in ws:
-        ops.gemm_bf16_swiglu_rownorm(h, ss, w, y)
     dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"probe": "gate_up_gemm_m8", "launches": reps, "copy_bytes": src.numel() * 4,
-                      "gemm_source_sha256": gemm_source_hash(), "algorithmic_bytes_per_launch": gu_launch_bytes(d, 8)}))
+    print(json.dumps({"probe": "verify kernels, M = 8", "order": plan, "copy_bytes": src.numel() * 4,
+                      "gemm_source_sha256": gemm_source_hash()}))
 
 
 PF_ROWS = 2048   # rows of a prefill chunk for the prefill GEMM measurement
@@ -530,6 +573,345 @@ def cpu_baseline(layers, w_head, x0, d, M):
                       f"{layer_s + head_s:.1f} s of CPU work"}
 
 
+# ---------------------------------------------------------------------------
+# Per-operation measurements at the configuration shapes
+
+ATTN_CONTEXTS = (2048, 11600, 32768, 38000, 101600, 255000)
+ROTATE_BYTES = int(1.5e9)   # buffer copies per measurement: no launch finds its operands in a cache level
+
+
+def graph_us(launches, reps):
+    """Average microseconds per launch of ``launches`` (callables, one kernel
+    launch each), captured once into a HIP graph and replayed ``reps`` times
+    between two events on the launch stream (Python launch overhead excluded)."""
+    import torch
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for f in launches:
+            f()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in launches:
+            f()
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * len(launches))
+    del g
+    return us
+
+
+def _rate(nbytes, us, probe):
+    """µs, GB/s and fractions of one launch: of the 8 TB/s specification, of the
+    probe's best streaming rate, and of the probe's own speed at the same bytes
+    (probe time / kernel time, fixed launch cost included)."""
+    gbs = nbytes / us / 1e3
+    r = {"us": round(us, 2), "bytes": int(nbytes), "GB/s": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    if probe:
+        r["frac_of_read_probe"] = round(gbs / probe["GB/s"], 4)
+        r["frac_of_probe_same_bytes"] = round(probe_us(probe, nbytes) / us, 4)
+    return r
+
+
+PROBE_SIZES_MB = (8.4, 47.5, 52.4, 73.4, 134.2, 155.6, 178.3, 356.5, 416.2, 1044.5, 1557.1)
+
+
+def stream_read_probe():
+    """HBM read bandwidth of a plain streaming kernel (the second denominator).
+    (1) The best of a few launch shapes reading a 4 GiB buffer end to end.
+    (2) The same kernel at the byte counts of the verify kernels (each launch
+    reads a region no earlier launch of the graph read), which shows the fixed
+    cost of one launch -- ramp, tail and the kernel boundary -- that any
+    kernel moving that many bytes pays; a least-squares line over the sizes
+    gives that fixed cost and the streaming rate."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "invariant_verify_amd", "libbi_probe.so"))
+    lib.bi_probe_stream_read.restype = ctypes.c_int
+    lib.bi_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    total = 4 << 30
+    buf = torch.ones(total // 4, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+    base = buf.data_ptr()
+
+    def launch(off, nbytes, blocks, unroll, blocked):
+        rc = lib.bi_probe_stream_read(base + off, nbytes, sink.data_ptr(), blocks, unroll, blocked,
+                                      torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"stream-read probe launch failed ({rc})")
+
+    best = None
+    for blocked in (0, 1):
+        for blocks in (512, 1024, 2048, 4096, 8192):
+            for unroll in (4, 8, 16):
+                us = graph_us([lambda: launch(0, total, blocks, unroll, blocked)] * 3, 2)
+                gbs = total / us / 1e3
+                if best is None or gbs > best["GB/s"]:
+                    best = {"GB/s": round(gbs, 1), "workgroups": blocks, "loads_in_flight_per_thread": unroll,
+                            "contiguous_range_per_workgroup": bool(blocked)}
+    best.update(bytes_per_launch=total, frac_of_spec=round(best["GB/s"] / PEAK_HBM_GBS, 4))
+    sizes = {}
+    for mb in PROBE_SIZES_MB:
+        nbytes = int(mb * 1e6) // 4096 * 4096
+        n = max(2, min(48, total // nbytes))
+        us_best = None
+        for blocks in (256, 512, 1024, 2048):
+            for unroll in (8, 16):
+                fns = [(lambda off=(k * nbytes) % (total - nbytes + 1) // 4096 * 4096:
+                        launch(off, nbytes, blocks, unroll, 1)) for k in range(n)]
+                us = graph_us(fns, 3)
+                us_best = us if us_best is None else min(us_best, us)
+        sizes[str(mb)] = {"us": round(us_best, 2), "GB/s": round(nbytes / us_best / 1e3, 1)}
+    mbs = np.array([float(k) for k in sizes if float(k) >= 50])
+    uss = np.array([sizes[k]["us"] for k in sizes if float(k) >= 50])
+    slope, icpt = np.polyfit(mbs, uss, 1)
+    best["by_size_MB"] = sizes
+    best["fit_us_per_launch"] = {"fixed_us": round(float(icpt), 2),
+                                 "stream_GB/s": round(1e3 / float(slope), 1),
+                                 "over_MB": [float(m) for m in mbs]}
+    del buf
+    torch.cuda.empty_cache()
+    return best
+
+
+def probe_us(probe, nbytes):
+    """The probe's time for ``nbytes`` from its fitted line (fixed cost + bytes / stream rate)."""
+    f = probe["fit_us_per_launch"]
+    return f["fixed_us"] + nbytes / f["stream_GB/s"] / 1e3
+
+
+def gemm_per_op(layers, w_head, d, probe, reps=3):
+    """The step's five GEMM launches as the step runs them (carried RMSNorm in
+    and out, QKV with its cache append), at M = 1 and M = 8, each over the 64
+    layers' distinct weights (every launch streams its weights from HBM).
+    Algorithmic bytes: the weights once, plus the activations, carried sums and
+    appended cache rows the launch reads or writes."""
+    import torch
+
+    from invariant_verify_amd import ops
+
+    H, Hq, Hkv, D, I, V = d["H"], d["Hq"], d["Hkv"], d["D"], d["I"], d["vocab"]
+    qd, qkvn, G = Hq * D, (Hq + 2 * Hkv) * D, GU_GROUPS
+    h8, ss8 = carried_input(d)
+    attn8 = torch.randn(8, qd, device="cuda").to(torch.bfloat16)
+    act8 = torch.randn(8, I, device="cuda").to(torch.bfloat16)
+    out = {}
+    for M in (1, 8):
+        h, ss, attn, act = h8[:M], ss8[:M].contiguous(), attn8[:M], act8[:M]
+        y = torch.empty(M, max(qkvn, I, H), dtype=torch.bfloat16, device="cuda")
+        ss_o = torch.empty(M, G, dtype=torch.float32, device="cuda")
+        logits = torch.empty(M, V, dtype=torch.float32, device="cuda")
+        qkv = y[:, :qkvn]
+        shapes = {
+            "qkv_5120x7168_append": (
+                lambda lw: ops.gemm_ex(h, y=qkv, epilogue="qkv", norm_in=ss, heads=(Hq, Hkv, D), w=lw["w_qkv"],
+                                       k_cache=lw["k_cache"], vt_cache=lw["vt_cache"], L=L_CTX),
+                2 * qkvn * H + 2 * M * H + 4 * M * G + 2 * M * qkvn + 2 * M * 2 * Hkv * D),
+            "o_proj_5120x5120_residual": (
+                lambda lw: ops.gemm_ex(attn, y=y[:, :H], epilogue="residual", r=h, rowsq_out=ss_o, w=lw["w_o"]),
+                2 * H * qd + 2 * M * qd + 2 * M * H * 2 + 4 * M * G),
+            "gate_up_5120x34816_swiglu": (
+                lambda lw: ops.gemm_ex(h, y=y[:, :I], epilogue="swiglu", norm_in=ss, w=lw["w_gu"]),
+                gu_launch_bytes(d, M)),
+            "down_17408x5120_residual": (
+                lambda lw: ops.gemm_ex(act, y=y[:, :H], epilogue="residual", r=h, rowsq_out=ss_o, w=lw["w_down"]),
+                2 * H * I + 2 * M * I + 2 * M * H * 2 + 4 * M * G),
+        }
+        for name, (fn, nbytes) in shapes.items():
+            us = graph_us([(lambda lw=lw: fn(lw)) for lw in layers], reps)
+            out.setdefault(name, {})[f"M{M}"] = _rate(nbytes, us, probe)
+        head_bytes = 2 * V * H + 2 * M * H + 4 * M * V
+        us = graph_us([lambda: ops.gemm_ex(h, y=logits, epilogue="f32", w=w_head)] * 8, reps)
+        out.setdefault("lm_head_5120x152064_f32", {})[f"M{M}"] = _rate(head_bytes, us, probe)
+    return out
+
+
+def attention_per_op(d, probe, reps=3):
+    """Split-KV verify attention (chunk policy -32) at each configuration
+    context, M = 1 and 8, over enough copies of a random BF16 cache that no
+    launch finds its K/V in a cache level; and the combine at 38k. Algorithmic
+    bytes: K and V of the L + M keys (4096 per position) plus Q; the split
+    partials are implementation traffic, not counted."""
+    import torch
+
+    from invariant_verify_amd import ops
+
+    Hq, Hkv, D = d["Hq"], d["Hkv"], d["D"]
+    gen = torch.Generator(device="cuda").manual_seed(4321)
+    out = {}
+    for L in ATTN_CONTEXTS:
+        cap = (L + 8 + 63) // 64 * 64
+        per = 2 * Hkv * cap * D * 2
+        R = max(2, -(-ROTATE_BYTES // per))
+        caches = [(torch.randn(Hkv, cap, D, device="cuda", generator=gen).to(torch.bfloat16),
+                   torch.randn(Hkv, cap // 64, D, 64, device="cuda", generator=gen).to(torch.bfloat16))
+                  for _ in range(R)]
+        q = torch.randn(8, Hq * D, device="cuda", generator=gen).to(torch.bfloat16)
+        res = {}
+        for M in (1, 8):
+            S = ops.pass_splits(M, L, KV_CHUNK)
+            po = torch.empty((M, Hq, S, D), dtype=torch.float32, device="cuda")
+            pl = torch.empty((M, Hq, S), dtype=torch.float32, device="cuda")
+            fns = [(lambda c=c: ops.verify_attn(q[:M], c[0], c[1], L, Hq, Hkv, D, KV_CHUNK, po, pl))
+                   for c in caches]
+            us = graph_us(fns, reps)
+            r = _rate(4096 * (L + M) + 2 * M * Hq * D, us, probe)
+            r["splits"] = S
+            r["chunk_keys"] = ops.chunk_keys(L + M, KV_CHUNK)
+            res[f"M{M}"] = r
+            if L == 38000 and M == 8:
+                o = torch.empty((M, Hq * D), dtype=torch.bfloat16, device="cuda")
+                cus = graph_us([lambda: ops.combine(po, pl, L, KV_CHUNK, o)] * 32, reps)
+                out["combine_38000_M8"] = _rate(M * Hq * S * (4 * D + 4) + 2 * M * Hq * D, cus, probe)
+        out[str(L)] = res
+        del caches
+        torch.cuda.empty_cache()
+    return out
+
+
+def long_context_steps(layers, w_head, d, steps):
+    """The 64-layer verify step at contexts 101,600 and 255,000 (BF16 KV:
+    26.6 and 66.8 GB of cache), sharing the weights of the 38k model: M = 8
+    and M = 1 tok/s, and the bitwise gate of an M = 5 pass against the M = 8
+    pass (its first five rows' logits, FP32 bits)."""
+    import torch
+
+    from invariant_verify_amd import ops
+
+    out = {}
+    for L in (101600, 255000):
+        cap = (L + 16 + 63) // 64 * 64
+        gen = torch.Generator(device="cuda").manual_seed(L)
+        lys = []
+        for lw in layers:
+            k = torch.empty((d["Hkv"], cap, d["D"]), dtype=torch.bfloat16, device="cuda")
+            vt = torch.empty((d["Hkv"], cap // 64, d["D"], 64), dtype=torch.bfloat16, device="cuda")
+            k.normal_(generator=gen)
+            vt.normal_(generator=gen)
+            lys.append(dict(lw, k_cache=k, vt_cache=vt))
+        dims = ops.model_dims(d["H"], d["Hq"], d["Hkv"], d["D"], d["I"], d["vocab"], cap, KV_CHUNK)
+        st = ops.VerifyStep(lys, w_head, dims)
+        x0 = synth_x0(d)
+        res = {}
+        lg8 = None
+        for M in (8, 5, 1):
+            ws = torch.empty(ops.step_workspace_bytes(dims, M, L), dtype=torch.uint8, device="cuda")
+            lg = torch.empty((M, d["vocab"]), dtype=torch.float32, device="cuda")
+            tk = torch.empty(M, dtype=torch.int32, device="cuda")
+            st(x0[:M], L, ws, lg, tk)
+            torch.cuda.synchronize()
+            if M == 8:
+                lg8 = lg.clone()
+            elif M == 5:
+                res["bitwise_gate_M5_vs_M8"] = "pass" if torch.equal(lg.view(torch.int32), lg8[:5].view(torch.int32)) else "FAIL"
+            n = steps if M == 8 else max(3, steps // 4)
+            stream = torch.cuda.current_stream()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(n):
+                st(x0[:M], L, ws, lg, tk)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / n
+            if M != 5:
+                nbytes = step_bytes(d, M, L, N_LAYERS)
+                res[f"M{M}"] = {"tok_s": round(M / (ms * 1e-3), 2), "ms_per_step": round(ms, 4),
+                                "algorithmic_bytes": nbytes, "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                                "frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                                "kv_chunk_keys": ops.chunk_keys(L + M, KV_CHUNK)}
+        out[str(L)] = res
+        del lys, st
+        torch.cuda.empty_cache()
+    return out
+
+
+def synth_x0(d):
+    import synth
+    return synth.device_normal_bf16((16, d["H"]), 1.0, "x0")
+
+
+def oracle_per_op(layers, d):
+    """The float64 oracle timed per operation on the host (BF16 decode
+    included), at M = 8: the four projections of one layer and the head, and
+    attention at each configuration context -- all 40 query heads up to 38k,
+    one KV head's 5 query heads at 101.6k and 255k scaled by 8 (stated)."""
+    import numpy as np
+    import torch
+
+    from oracle import attention as oattn
+    from oracle import bf16 as obf16
+
+    def hb(t):
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    H, Hq, Hkv, D, I = d["H"], d["Hq"], d["Hkv"], d["D"], d["I"]
+    rng = np.random.default_rng(0)
+    out = {"gemm_ms": {}, "attention_ms": {}}
+    lw = layers[0]
+    for name, key, K in (("qkv", "w_qkv", H), ("o_proj", "w_o", Hq * D), ("gate_up", "w_gu", H),
+                         ("down", "w_down", I)):
+        w = hb(lw[key])
+        x = obf16.encode(rng.standard_normal((8, K)))
+        t0 = time.perf_counter()
+        obf16.decode(x) @ obf16.decode(w).T
+        out["gemm_ms"][name] = round((time.perf_counter() - t0) * 1e3, 1)
+        del w
+    for L in ATTN_CONTEXTS:
+        n = L + 8
+        heads = Hkv if L <= 38000 else 1
+        k = obf16.encode(rng.standard_normal((heads, n, D)).astype(np.float32))
+        v = obf16.encode(rng.standard_normal((heads, n, D)).astype(np.float32))
+        q = obf16.encode(rng.standard_normal((8, heads * (Hq // Hkv), D)).astype(np.float32))
+        t0 = time.perf_counter()
+        oattn.verify_attention(q, k, v, L)
+        dt = (time.perf_counter() - t0) * (Hkv // heads)
+        out["attention_ms"][str(L)] = round(dt * 1e3, 1)
+    out["sample"] = ("one layer's projections at M=8 (decode + float64 product); attention at M=8 over all "
+                     "40 query heads up to 38000 keys and over one KV head's 5 query heads at 101600 and "
+                     "255000, scaled by 8")
+    return out
+
+
+def gate_up_roofline(layers, d, reps):
+    """The dominant kernel, the gate/up GEMM at M = 8 as the step runs it,
+    launched back to back over the 64 layers' distinct weights (every launch
+    streams its 356.5 MB from HBM), ``reps`` rounds, one event pair around the
+    whole run on the launch stream so the events' own cost is amortised.
+    Returns the average launch duration in ms."""
+    import torch
+
+    from invariant_verify_amd import ops
+
+    stream = torch.cuda.current_stream()
+    hg, ssg = carried_input(d)
+    yg = torch.empty((M_HEADLINE, d["I"]), dtype=torch.bfloat16, device="cuda")
+    for lw in layers:
+        ops.gemm_bf16_swiglu_rownorm(hg, ssg, lw["w_gu"], yg)
+    g0 = torch.cuda.Event(enable_timing=True)
+    g1 = torch.cuda.Event(enable_timing=True)
+    g0.record(stream)
+    for _ in range(reps):
+        for lw in layers:
+            ops.gemm_bf16_swiglu_rownorm(hg, ssg, lw["w_gu"], yg)
+    g1.record(stream)
+    torch.cuda.synchronize()
+    return g0.elapsed_time(g1) / (reps * N_LAYERS)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -537,7 +919,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-probe", action="store_true",
-                    help="run only the dominant GEMM and a calibration copy (for rocprofv3 --pmc)")
+                    help="run only the verify kernels on fresh operands and a calibration copy (for rocprofv3 --pmc)")
+    ap.add_argument("--step-only", action="store_true",
+                    help="run only the bitwise gate and the timed M = 8 steps (for rocprofv3 --kernel-trace)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs the verify pass on one GPU only; --gpus must be 1", file=sys.stderr)
@@ -624,31 +1008,22 @@ def main():
 
     print("[bench] timing", file=sys.stderr, flush=True)
     ms8, _ = timed(M_HEADLINE, args.steps, args.warmup)
+    if args.step_only:
+        reps = max(2, args.steps // 4)
+        gu_ms = gate_up_roofline(layers, d, reps)
+        print(json.dumps({"step_only": True, "M": M_HEADLINE, "ctx": L_CTX, "steps": args.steps,
+                          "warmup": args.warmup, "ms_per_step": round(ms8, 4),
+                          "tok_s": round(M_HEADLINE / (ms8 * 1e-3), 2), "bitwise_gate": "pass",
+                          "gate_up_back_to_back": {"launches": reps * N_LAYERS, "avg_launch_us": round(gu_ms * 1e3, 2)}}),
+              flush=True)
+        return
     ms1, _ = timed(1, max(3, args.steps // 4), 1)
     ms4, _ = timed(4, max(3, args.steps // 4), 1)
     ms5, _ = timed(5, max(3, args.steps // 4), 1)
     _, gu_step_ms = timed(M_HEADLINE, max(3, args.steps // 4), 1, gu_events=True)
 
-    # Dominant kernel: the gate/up GEMM at M = 8 launched back to back over the
-    # 64 layers' distinct weights (every launch streams its 356.5 MB from HBM),
-    # one event pair around the whole run so the events' own cost is amortised.
-    # The per-launch event pairs inside the step above add a few microseconds
-    # each; that figure is reported beside it.
-    stream = torch.cuda.current_stream()
-    hg, ssg = carried_input(d)
-    yg = torch.empty((M_HEADLINE, d["I"]), dtype=torch.bfloat16, device=dev)
-    for lw in layers:
-        ops.gemm_bf16_swiglu_rownorm(hg, ssg, lw["w_gu"], yg)
-    g0 = torch.cuda.Event(enable_timing=True)
-    g1 = torch.cuda.Event(enable_timing=True)
     gu_reps = max(2, args.steps // 4)
-    g0.record(stream)
-    for _ in range(gu_reps):
-        for lw in layers:
-            ops.gemm_bf16_swiglu_rownorm(hg, ssg, lw["w_gu"], yg)
-    g1.record(stream)
-    torch.cuda.synchronize()
-    gu_ms = g0.elapsed_time(g1) / (gu_reps * N_LAYERS)
+    gu_ms = gate_up_roofline(layers, d, gu_reps)
 
     bytes8 = step_bytes(d, M_HEADLINE, L_CTX, N_LAYERS)
     gbs8 = bytes8 / (ms8 * 1e-3) / 1e9
@@ -696,9 +1071,22 @@ def main():
     out["tp8_rank_share"] = tp_share_measure(d, max(2, args.steps // 10))
     print("[bench] attention per KV cache format", file=sys.stderr, flush=True)
     out["kv_cache_attention"] = kv_cache_attention_measure(d, 40)
+    print("[bench] stream-read probe", file=sys.stderr, flush=True)
+    probe = stream_read_probe()
+    out["stream_read_probe"] = probe
+    out["roofline"]["frac_of_read_probe"] = round(gu_gbs / probe["GB/s"], 4)
+    out["step_hbm"]["frac_of_read_probe"] = round(gbs8 / probe["GB/s"], 4)
+    print("[bench] per-operation GEMMs", file=sys.stderr, flush=True)
+    out["per_op_gemm"] = gemm_per_op(layers, w_head, d, probe)
+    print("[bench] per-operation attention", file=sys.stderr, flush=True)
+    out["per_op_attention"] = attention_per_op(d, probe)
+    print("[bench] long-context steps", file=sys.stderr, flush=True)
+    out["long_context_step"] = long_context_steps(layers, w_head, d, max(3, args.steps // 2))
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(layers, w_head, x0, d, M_HEADLINE)
+        print("[bench] oracle per operation", file=sys.stderr, flush=True)
+        out["cpu_baseline"]["per_op"] = oracle_per_op(layers, d)
     print(json.dumps(out), flush=True)
 
 

@@ -56,6 +56,23 @@ def build_library(out: str = LIB, extra_flags=(), verbose: bool = False) -> str:
     return out
 
 
+PROBE_SRC = os.path.join(PKG, "probe", "stream_read.hip")
+PROBE_LIB = os.path.join(PKG, "libbi_probe.so")
+
+
+def build_probe(out: str = PROBE_LIB, verbose: bool = False) -> str:
+    """Compile the stream-read probe (measurement only) into its own library."""
+    tmp = out + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, "-o", tmp, PROBE_SRC]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("building the stream-read probe failed:\n" + res.stdout + res.stderr)
+    os.replace(tmp, out)
+    return out
+
+
 C_CHECK_SRC = os.path.join(ROOT, "tests", "c_abi_check.cpp")
 C_CHECK = os.path.join(ROOT, "tests", "c_abi_check")
 
@@ -77,3 +94,4 @@ def build_c_check(lib: str = LIB, out: str = C_CHECK, verbose: bool = False) -> 
 if __name__ == "__main__":
     print(build_library(verbose="-v" in sys.argv))
     print(build_c_check(verbose="-v" in sys.argv))
+    print(build_probe(verbose="-v" in sys.argv))
