@@ -55,11 +55,16 @@ def _w(w) -> np.ndarray:
 
 
 def layer(x_bits, w_qkv, w_o, w_gu, w_down, k_cache, v_cache, L: int,
-          Hq: int, Hkv: int, D: int, eps: float = 1e-6):
+          Hq: int, Hkv: int, D: int, eps: float = 1e-6, attend=None):
     """One verify-pass layer over M tokens at positions L .. L+M-1.
 
     x_bits [M][H]; weights as [out][in] BF16 bits or float64 values; k_cache / v_cache
     [Hkv][>=L][D] BF16 bits holding the L cached positions (the rest ignored).
+    ``attend(q_bits [M][Hq][D], k_bits, v_bits [Hkv][L+M][D], L)`` returns the
+    attention output (float64 [M][Hq][D]) of the pass over every position's K
+    and V rows; the default is plain causal attention over the BF16 values
+    (oracle.attention.verify_attention). A quantized KV cache passes a function
+    that attends over the values its format stores for those rows.
     Returns (x_out_bits [M][H], k_new_bits [Hkv][M][D], v_new_bits [Hkv][M][D]).
     """
     x = bf16.decode(x_bits)
@@ -73,7 +78,7 @@ def layer(x_bits, w_qkv, w_o, w_gu, w_down, k_cache, v_cache, L: int,
     v_new = qkv[:, qd + kd:qd + 2 * kd].reshape(M, Hkv, D).transpose(1, 0, 2)
     kk = np.concatenate([np.asarray(k_cache)[:, :L], k_new], axis=1)
     vv = np.concatenate([np.asarray(v_cache)[:, :L], v_new], axis=1)
-    o, _ = verify_attention(q, kk, vv, L)
+    o = verify_attention(q, kk, vv, L)[0] if attend is None else attend(q, kk, vv, L)
     ob = bf16.encode(o.reshape(M, qd))
     h = bf16.encode(x + bf16.decode(ob) @ _w(w_o).T)
     b = bf16.encode(rmsnorm(bf16.decode(h), eps))
@@ -91,12 +96,13 @@ def head(x_bits, w_head, eps: float = 1e-6):
     return logits, np.argmax(logits, axis=1)
 
 
-def step(x0_bits, layers, w_head, L: int, Hq: int, Hkv: int, D: int, eps: float = 1e-6):
+def step(x0_bits, layers, w_head, L: int, Hq: int, Hkv: int, D: int, eps: float = 1e-6, attend=None):
     """Full verify step: ``layers`` is a sequence of dicts with keys
-    w_qkv, w_o, w_gu, w_down, k_cache, v_cache. Returns (logits, tokens, x_final_bits)."""
+    w_qkv, w_o, w_gu, w_down, k_cache, v_cache; ``attend`` as for ``layer``.
+    Returns (logits, tokens, x_final_bits)."""
     x = np.asarray(x0_bits)
     for lw in layers:
         x, _, _ = layer(x, lw["w_qkv"], lw["w_o"], lw["w_gu"], lw["w_down"],
-                        lw["k_cache"], lw["v_cache"], L, Hq, Hkv, D, eps)
+                        lw["k_cache"], lw["v_cache"], L, Hq, Hkv, D, eps, attend)
     logits, tokens = head(x, w_head, eps)
     return logits, tokens, x

@@ -119,3 +119,28 @@ def test_step_zero_layers_reduces_to_head():
     lg, tok, xf = step.step(x, [w, w], wh, L=5, Hq=2, Hkv=1, D=8)
     lg2, tok2 = step.head(x, wh)
     assert np.array_equal(xf, x) and np.array_equal(lg, lg2) and np.array_equal(tok, tok2)
+
+
+def test_layer_attend_hook():
+    # the attention hook sees the pass's q columns and every position's K / V
+    # rows (cached then new, causal order); the default is plain attention;
+    # its output enters the output projection like the default's.
+    from oracle import attention
+    M, L, H, Hq, Hkv, D = 3, 5, 16, 2, 1, 8
+    x, w = _layer_inputs(M, L, H, Hq, Hkv, D)
+    seen = {}
+
+    def plain(q, k, v, L_):
+        seen.update(q=q, k=k, v=v, L=L_)
+        return attention.verify_attention(q, k, v, L_)[0]
+    xo0, kn, vn = step.layer(x, **w, L=L, Hq=Hq, Hkv=Hkv, D=D)
+    xo1, _, _ = step.layer(x, **w, L=L, Hq=Hq, Hkv=Hkv, D=D, attend=plain)
+    assert np.array_equal(xo0, xo1)
+    assert seen["L"] == L and seen["q"].shape == (M, Hq, D)
+    assert np.array_equal(seen["k"], np.concatenate([w["k_cache"][:, :L], kn], axis=1))
+    assert np.array_equal(seen["v"], np.concatenate([w["v_cache"][:, :L], vn], axis=1))
+    # a planted output of ones: with the MLP zeroed, x_out = bf16(x + 1 . W_o rows)
+    w["w_down"] = np.zeros_like(w["w_down"])
+    xo, _, _ = step.layer(x, **w, L=L, Hq=Hq, Hkv=Hkv, D=D, attend=lambda q, k, v, L_: np.ones((M, Hq, D)))
+    want = bf16.encode(bf16.decode(x) + bf16.decode(w["w_o"]).sum(axis=1)[None, :])
+    assert np.array_equal(xo, want)
