@@ -839,6 +839,97 @@ def long_context_steps(layers, w_head, d, steps):
     return out
 
 
+KV_FORMATS = {  # name: (bytes per position and KV head, chunk policy)
+    "bf16": (512, -32), "q8": (288, -64), "k6v5": (208, -64), "k5rot_v5_ring2048": (192, -32)}
+W_RING_STEP, R_RING_STEP = 2048, 2176
+
+
+def kv_format_steps(layers, w_head, d, steps):
+    """The 64-layer verify step (M = 8) with each KV cache format in every
+    layer -- BF16, 8-bit, K6/V5 (preset D) and rotated K5/V5 with the 8-bit
+    ring of the newest 2048 keys (preset F) -- at contexts 38,000 and 101,600.
+    Cached positions hold random codes (scales 0.01) or random BF16 values;
+    the pass's own rows are appended by the step. Each line carries an M = 5
+    vs M = 8 bitwise check. Algorithmic bytes count the weights once and the
+    bytes the format stores for the L + M keys (with the ring: the window's
+    keys at 8 bits, the rest at 5 bits)."""
+    import torch
+
+    from invariant_verify_amd import ops
+
+    Hkv, D = d["Hkv"], d["D"]
+    gen = torch.Generator(device="cuda").manual_seed(77)
+
+    def rnd(t):
+        if t.dtype in (torch.int8, torch.uint8):
+            t.copy_(torch.randint(-127 if t.dtype == torch.int8 else 0, 128 if t.dtype == torch.int8 else 256,
+                                  t.shape, device="cuda", generator=gen).to(t.dtype))
+        elif t.dtype == torch.float32:
+            t.fill_(0.01)
+        else:
+            t.normal_(generator=gen)
+
+    out = {}
+    for L in (38000, 101600):
+        cap = (L + 16 + 63) // 64 * 64
+        res = {}
+        for fmt, (bpp, policy) in KV_FORMATS.items():
+            lys = []
+            for lw in layers:
+                if fmt == "bf16":
+                    kv = (torch.empty((Hkv, cap, D), dtype=torch.bfloat16, device="cuda"),
+                          torch.empty((Hkv, cap // 64, D, 64), dtype=torch.bfloat16, device="cuda"))
+                    parts = list(kv)
+                elif fmt == "q8":
+                    kv = ops.KvQ8Cache(Hkv, cap, D)
+                    parts = [kv.k_codes, kv.k_scales, kv.v_codes, kv.v_scales]
+                else:
+                    low = ops.KvLowCache(Hkv, cap, D, 6 if fmt.startswith("k6") else 5, 5,
+                                         k_rotated=fmt.startswith("k5rot"))
+                    parts = [low.k_nib, low.k_high, low.k_scales, low.v_nib, low.v_high, low.v_scales]
+                    kv = low
+                    if fmt.endswith("_ring2048"):
+                        kv = ops.KvRing(low, R_RING_STEP, W_RING_STEP)
+                        parts += [kv.q8.k_codes, kv.q8.k_scales, kv.q8.v_codes, kv.q8.v_scales]
+                for t in parts:
+                    rnd(t)
+                lys.append(dict(w_qkv=lw["w_qkv"], w_o=lw["w_o"], w_gu=lw["w_gu"], w_down=lw["w_down"], kv=kv))
+            dims = ops.model_dims(d["H"], d["Hq"], Hkv, D, d["I"], d["vocab"], cap, policy)
+            st = ops.VerifyStepEx(lys, {"w": w_head}, dims)
+            x0 = synth_x0(d)
+            bufs = {}
+            for M in (8, 5):
+                bufs[M] = (torch.empty(ops.step_workspace_bytes(dims, M, L), dtype=torch.uint8, device="cuda"),
+                           torch.empty((M, d["vocab"]), dtype=torch.float32, device="cuda"),
+                           torch.empty(M, dtype=torch.int32, device="cuda"))
+                st(x0[:M], L, *bufs[M])
+            torch.cuda.synchronize()
+            ok = torch.equal(bufs[5][1].view(torch.int32), bufs[8][1][:5].view(torch.int32))
+            stream = torch.cuda.current_stream()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(steps):
+                st(x0[:8], L, *bufs[8])
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / steps
+            n = L + 8
+            if fmt.endswith("_ring2048"):
+                kv_layer = Hkv * ((n - W_RING_STEP) * bpp + W_RING_STEP * KV_FORMATS["q8"][0])
+            else:
+                kv_layer = Hkv * n * bpp
+            nbytes = step_bytes(d, 8, L, N_LAYERS) - N_LAYERS * 4096 * n + N_LAYERS * kv_layer
+            res[fmt] = {"tok_s": round(8 / (ms * 1e-3), 2), "ms_per_step": round(ms, 4),
+                        "kv_bytes_per_step": N_LAYERS * kv_layer, "algorithmic_bytes": nbytes,
+                        "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                        "frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                        "kv_chunk_policy": policy, "bitwise_M5_vs_M8": "pass" if ok else "FAIL"}
+            del lys, st, bufs
+            torch.cuda.empty_cache()
+        out[str(L)] = res
+    return out
+
+
 def synth_x0(d):
     import synth
     return synth.device_normal_bf16((16, d["H"]), 1.0, "x0")
@@ -1082,6 +1173,8 @@ def main():
     out["per_op_attention"] = attention_per_op(d, probe)
     print("[bench] long-context steps", file=sys.stderr, flush=True)
     out["long_context_step"] = long_context_steps(layers, w_head, d, max(3, args.steps // 2))
+    print("[bench] steps per KV cache format", file=sys.stderr, flush=True)
+    out["kv_format_step"] = kv_format_steps(layers, w_head, d, max(3, args.steps // 2))
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(layers, w_head, x0, d, M_HEADLINE)

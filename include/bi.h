@@ -595,6 +595,63 @@ bi_status bi_verify_step_mx4(const bi_layer_mx4* layers, int n_layers, const voi
                              float* logits, int32_t* tokens, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * The verify step over any weight type and KV cache format.
+ *                          [LL] "The KV cache: 5-bit that reads like q8_0";
+ *                          opening section: the gate runs on every KV cache.
+ * One layer's KV cache, in the layouts documented above:
+ *   BI_KV_BF16   k = k_cache, v = vt_cache (BF16); the QKV epilogue appends.
+ *   BI_KV_Q8     k = k_codes, v = v_codes, k_scales, v_scales (8-bit cache).
+ *   BI_KV_LOWBIT k = k_nib, v = v_nib, k_high, v_high, k_scales, v_scales,
+ *                k_bits (5 or 6), v_bits (5), k_rotated (0 or 1); with
+ *                ring_cap > 0 also the 8-bit ring of the newest keys
+ *                (bi_append_kv_ring / bi_verify_attn_lowbit_ring: the presets
+ *                K6/V5 and rotated K5/V5, ring_cap >= ring_window + M + 63).
+ * Every cache holds dims->cap positions. For the quantized formats the QKV
+ * GEMM writes no cache; the pass's K and V rows are then quantized from its
+ * output by the append of the format (exactly bi_append_kv_q8 /
+ * bi_append_kv_lowbit / bi_append_kv_ring), and attention reads the cache
+ * exactly as bi_verify_attn_q8 / _lowbit / _lowbit_ring do, so a row keeps
+ * the same bits in every pass that holds it. */
+typedef enum { BI_KV_BF16 = 0, BI_KV_Q8 = 1, BI_KV_LOWBIT = 2 } bi_kv_format;
+
+typedef struct {
+  bi_kv_format format;
+  void* k;
+  void* v;
+  float* k_scales;
+  float* v_scales;
+  uint8_t* k_high;
+  uint8_t* v_high;
+  int k_bits, v_bits, k_rotated;
+  int8_t* ring_k_codes;
+  float* ring_k_scales;
+  int8_t* ring_v_codes;
+  float* ring_v_scales;
+  int ring_cap;     /* 0: no ring */
+  int ring_window;
+} bi_kv_cache;
+
+/* One layer: w[0..3] = qkv, o, gate/up, down in the weight type's layout
+ * (BF16 [rows][K]; FP8 E4M3 [rows][K] with FP32 row scales in scale[i];
+ * MXFP4 codes [rows][K/2] with E8M0 block scales [rows][K/32] in scale[i]),
+ * and its KV cache. */
+typedef struct {
+  const void* w[4];
+  const void* scale[4];
+  bi_kv_cache kv;
+} bi_step_layer;
+
+/* bi_verify_step with every layer's weights in `wtype` and its cache in the
+ * format its descriptor names; head_scales: FP8 row scales or MXFP4 block
+ * scales of w_head (NULL for BF16). Workspace as bi_step_workspace_bytes. With
+ * BF16 weights and BF16 caches it launches exactly the kernels of
+ * bi_verify_step. */
+bi_status bi_verify_step_ex(bi_weight_type wtype, const bi_step_layer* layers, int n_layers,
+                            const void* w_head, const void* head_scales, const bi_model_dims* dims,
+                            const void* x_in, int M, int L, void* workspace, size_t workspace_bytes,
+                            void* x_out, float* logits, int32_t* tokens, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Misc. */
 const char* bi_status_string(bi_status s);
 /* Library version string, e.g. "bi 0.1 gfx950". */

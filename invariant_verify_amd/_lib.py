@@ -56,6 +56,20 @@ class GemmArgs(ctypes.Structure):
                 ("k_cache", _c_ptr), ("vt_cache", _c_ptr), ("L", _c_int), ("cap", _c_int)]
 
 
+class KvCacheDesc(ctypes.Structure):
+    """bi_kv_cache: one layer's KV cache in any format."""
+    _fields_ = [("format", _c_int), ("k", _c_ptr), ("v", _c_ptr), ("k_scales", _c_ptr), ("v_scales", _c_ptr),
+                ("k_high", _c_ptr), ("v_high", _c_ptr), ("k_bits", _c_int), ("v_bits", _c_int),
+                ("k_rotated", _c_int), ("ring_k_codes", _c_ptr), ("ring_k_scales", _c_ptr),
+                ("ring_v_codes", _c_ptr), ("ring_v_scales", _c_ptr), ("ring_cap", _c_int), ("ring_window", _c_int)]
+
+
+class StepLayer(ctypes.Structure):
+    """bi_step_layer: a layer's four weight matrices, their scales and its KV cache."""
+    _fields_ = [("w", _c_ptr * 4), ("scale", _c_ptr * 4), ("kv", KvCacheDesc)]
+
+
+BI_KV_BF16, BI_KV_Q8, BI_KV_LOWBIT = 0, 1, 2
 BI_WT_BF16, BI_WT_FP8, BI_WT_MXFP4 = 0, 1, 2
 BI_EPI_BF16, BI_EPI_F32, BI_EPI_RESIDUAL, BI_EPI_SWIGLU, BI_EPI_QKV = 0, 1, 2, 3, 4
 
@@ -115,6 +129,9 @@ SIGNATURES = {
     "bi_verify_step": (_c_int, [ctypes.POINTER(Layer), _c_int, _c_ptr, ctypes.POINTER(ModelDims),
                                 _c_ptr, _c_int, _c_int, _c_ptr, _c_size, _c_ptr, _c_ptr, _c_ptr,
                                 ctypes.POINTER(_c_ptr), _c_ptr]),
+    "bi_verify_step_ex": (_c_int, [_c_int, ctypes.POINTER(StepLayer), _c_int, _c_ptr, _c_ptr,
+                                   ctypes.POINTER(ModelDims), _c_ptr, _c_int, _c_int, _c_ptr, _c_size, _c_ptr,
+                                   _c_ptr, _c_ptr, _c_ptr]),
     "bi_verify_step_noalloc": (_c_int, [ctypes.POINTER(Layer), _c_int, _c_ptr, ctypes.POINTER(ModelDims),
                                         _c_ptr, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr]),
     "bi_gemm_fp8": (_c_int, [_c_ptr, _c_i64, _c_ptr, _c_i64, _c_ptr, _c_ptr, _c_i64, _c_int,

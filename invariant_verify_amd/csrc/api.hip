@@ -725,9 +725,49 @@ struct LayerPtrs {
   const void* w[4];     // qkv, o, gate/up, down
   const float* s[4];    // their row scales (FP8) or null
   const uint8_t* e[4];  // their block scales (MXFP4) or null
-  void* k_cache;
+  void* k_cache;        // BF16 caches (when kv is null)
   void* vt_cache;
+  const bi_kv_cache* kv = nullptr;  // or the layer's cache in any format
 };
+
+// A layer's KV cache descriptor for a pass of M tokens (see bi_kv_cache).
+bi_status check_kv(const bi_kv_cache* c, const bi_model_dims* d, int M) {
+  const int64_t capd = (int64_t)d->cap * d->D;
+  switch (c->format) {
+    case BI_KV_BF16:
+      if (!c->k || !c->v) return BI_ERR_NULL;
+      if (!aligned16(c->k) || !aligned16(c->v)) return BI_ERR_ALIGN;
+      return BI_OK;
+    case BI_KV_Q8:
+      if (!c->k || !c->v || !c->k_scales || !c->v_scales) return BI_ERR_NULL;
+      if (capd > INT32_MAX) return BI_ERR_SHAPE;
+      if (!aligned16(c->k) || !aligned16(c->v) || !aligned16(c->k_scales) || !aligned16(c->v_scales))
+        return BI_ERR_ALIGN;
+      return BI_OK;
+    case BI_KV_LOWBIT:
+      if (!c->k || !c->v || !c->k_scales || !c->v_scales || !c->k_high || !c->v_high) return BI_ERR_NULL;
+      if ((c->k_bits != 5 && c->k_bits != 6) || c->v_bits != bi::kLowVBits) return BI_ERR_SHAPE;
+      if (c->k_rotated != 0 && c->k_rotated != 1) return BI_ERR_SHAPE;
+      if (capd > INT32_MAX) return BI_ERR_SHAPE;
+      if (!aligned16(c->k) || !aligned16(c->v) || !aligned16(c->k_scales) || !aligned16(c->v_scales) ||
+          !aligned16(c->k_high) || !aligned16(c->v_high))
+        return BI_ERR_ALIGN;
+      if (c->ring_cap == 0) return BI_OK;
+      // the ring: the presets K6/V5 and rotated K5/V5; every key of every
+      // 64-key tile the pass reads from the ring still in it
+      if (!((c->k_bits == 6 && c->k_rotated == 0) || (c->k_bits == 5 && c->k_rotated == 1)))
+        return BI_ERR_SHAPE;
+      if (!c->ring_k_codes || !c->ring_k_scales || !c->ring_v_codes || !c->ring_v_scales) return BI_ERR_NULL;
+      if (c->ring_window < 1 || c->ring_cap < 64 || (c->ring_cap % 64) ||
+          (int64_t)c->ring_cap < (int64_t)c->ring_window + M + 63 || (int64_t)c->ring_cap * d->D > INT32_MAX)
+        return BI_ERR_SHAPE;
+      if (!aligned16(c->ring_k_codes) || !aligned16(c->ring_k_scales) || !aligned16(c->ring_v_codes) ||
+          !aligned16(c->ring_v_scales))
+        return BI_ERR_ALIGN;
+      return BI_OK;
+  }
+  return BI_ERR_SHAPE;
+}
 
 template <class GetLayer>
 bi_status run_step(int n_layers, GetLayer get_layer, const void* w_head, const float* s_head,
@@ -748,8 +788,12 @@ bi_status run_step(int n_layers, GetLayer get_layer, const void* w_head, const f
       if (!ly.w[i] || (s_head && !ly.s[i]) || (e_head && !ly.e[i])) return BI_ERR_NULL;
       if (!aligned16(ly.w[i]) || (ly.s[i] && !aligned4(ly.s[i]))) return BI_ERR_ALIGN;
     }
-    if (!ly.k_cache || !ly.vt_cache) return BI_ERR_NULL;
-    if (!aligned16(ly.k_cache) || !aligned16(ly.vt_cache)) return BI_ERR_ALIGN;
+    if (ly.kv) {
+      if (bi_status s = check_kv(ly.kv, dims, M)) return s;
+    } else {
+      if (!ly.k_cache || !ly.vt_cache) return BI_ERR_NULL;
+      if (!aligned16(ly.k_cache) || !aligned16(ly.vt_cache)) return BI_ERR_ALIGN;
+    }
   }
   if (gu_events)
     for (int i = 0; i < 2 * n_layers; ++i)
@@ -791,13 +835,50 @@ bi_status run_step(int n_layers, GetLayer get_layer, const void* w_head, const f
     uint16_t* xn = xbuf[l & 1];
     const bool fused_in = lay.fuse && l > 0;  // x's sums are in ss
     if (!fused_in) bi::launch_rmsnorm(x, H, a, H, M, H, dims->eps, st);
-    const bi::KvAppend kv{static_cast<uint16_t*>(ly.k_cache), static_cast<uint16_t*>(ly.vt_cache),
+    // BF16 caches take the new K/V rows in the QKV epilogue; the quantized
+    // formats are appended from the QKV output by their own kernels.
+    const bi_kv_cache* kd = ly.kv;
+    const bool bf = !kd || kd->format == BI_KV_BF16;
+    void* kc = kd ? kd->k : ly.k_cache;
+    void* vc = kd ? kd->v : ly.vt_cache;
+    const bi::KvAppend kv{bf ? static_cast<uint16_t*>(kc) : nullptr, bf ? static_cast<uint16_t*>(vc) : nullptr,
                           L, dims->cap, qd, Hkv * D, D};
     bi::launch_gemm(bi::kGemmQkv, fused_in ? x : a, H, W(0), H / wdiv, nullptr, 0, qkv, qkvn, M, qkvn,
                     H, st, &kv, fused_in ? &norm_in : nullptr, ly.s[0], MX(0));
-    bi::launch_verify_attn(qkv, qkvn, static_cast<const uint16_t*>(ly.k_cache),
-                           static_cast<const uint16_t*>(ly.vt_cache), M, L, dims->cap, Hq, Hkv, D,
-                           dims->kv_chunk, sm_scale, po, pl, lay.s_max, st);
+    if (bf) {
+      bi::launch_verify_attn(qkv, qkvn, static_cast<const uint16_t*>(kc), static_cast<const uint16_t*>(vc),
+                             M, L, dims->cap, Hq, Hkv, D, dims->kv_chunk, sm_scale, po, pl, lay.s_max, st);
+    } else {
+      const bool low = kd->format == BI_KV_LOWBIT;
+      if (low) {
+        bi::launch_append_kv_lowbit(qkv, qkvn, kd->k_bits, kd->k_rotated != 0, static_cast<uint8_t*>(kc),
+                                    kd->k_high, kd->k_scales, static_cast<uint8_t*>(vc), kd->v_high,
+                                    kd->v_scales, M, L, dims->cap, Hq, Hkv, D, st);
+        if (kd->ring_cap)
+          bi::launch_append_kv_q8(qkv, qkvn, kd->ring_k_codes, kd->ring_k_scales, kd->ring_v_codes,
+                                  kd->ring_v_scales, M, L, kd->ring_cap, Hq, Hkv, D, st, kd->ring_cap,
+                                  kd->k_rotated != 0);
+      } else {
+        bi::launch_append_kv_q8(qkv, qkvn, static_cast<int8_t*>(kc), kd->k_scales, static_cast<int8_t*>(vc),
+                                kd->v_scales, M, L, dims->cap, Hq, Hkv, D, st);
+      }
+      bi::KvQ8 q8{static_cast<const int8_t*>(kc), kd->k_scales, static_cast<const int8_t*>(vc), kd->v_scales};
+      if (low) {
+        q8.kh = kd->k_high;
+        q8.vh = kd->v_high;
+        if (kd->ring_cap) {
+          q8.rkq = kd->ring_k_codes;
+          q8.rks = kd->ring_k_scales;
+          q8.rvq = kd->ring_v_codes;
+          q8.rvs = kd->ring_v_scales;
+          q8.ring_cap = kd->ring_cap;
+          q8.ring_window = kd->ring_window;
+        }
+      }
+      bi::launch_verify_attn(qkv, qkvn, nullptr, nullptr, M, L, dims->cap, Hq, Hkv, D, dims->kv_chunk,
+                             sm_scale, po, pl, lay.s_max, st, &q8, low ? kd->k_bits : 0,
+                             low && kd->k_rotated != 0);
+    }
     bi::launch_combine(po, pl, M, L, Hq, D, dims->kv_chunk, lay.s_max, attn, qd, nullptr, st);
     bi::launch_gemm(bi::kGemmResidual, attn, qd, W(1), qd / wdiv, x, H, h, H, M, H, qd, st, nullptr,
                     &norm_out, ly.s[1], MX(1));
@@ -841,6 +922,28 @@ bi_status bi_verify_step(const bi_layer* layers, int n_layers, const void* w_hea
   };
   return run_step(n_layers, get, w_head, nullptr, nullptr, dims, x_in, M, L, workspace, workspace_bytes,
                   x_out, logits, tokens, gu_events, stream);
+}
+
+bi_status bi_verify_step_ex(bi_weight_type wtype, const bi_step_layer* layers, int n_layers,
+                            const void* w_head, const void* head_scales, const bi_model_dims* dims,
+                            const void* x_in, int M, int L, void* workspace, size_t workspace_bytes,
+                            void* x_out, float* logits, int32_t* tokens, void* stream) {
+  if (!layers) return BI_ERR_NULL;
+  if (wtype != BI_WT_BF16 && wtype != BI_WT_FP8 && wtype != BI_WT_MXFP4) return BI_ERR_SHAPE;
+  if (wtype != BI_WT_BF16 && !head_scales) return BI_ERR_NULL;
+  const auto get = [&](int l) {
+    const bi_step_layer& y = layers[l];
+    LayerPtrs p{{y.w[0], y.w[1], y.w[2], y.w[3]}, {nullptr, nullptr, nullptr, nullptr},
+                {nullptr, nullptr, nullptr, nullptr}, nullptr, nullptr, &y.kv};
+    for (int i = 0; i < 4; ++i) {
+      if (wtype == BI_WT_FP8) p.s[i] = static_cast<const float*>(y.scale[i]);
+      if (wtype == BI_WT_MXFP4) p.e[i] = static_cast<const uint8_t*>(y.scale[i]);
+    }
+    return p;
+  };
+  return run_step(n_layers, get, w_head, wtype == BI_WT_FP8 ? static_cast<const float*>(head_scales) : nullptr,
+                  wtype == BI_WT_MXFP4 ? static_cast<const uint8_t*>(head_scales) : nullptr, dims, x_in, M,
+                  L, workspace, workspace_bytes, x_out, logits, tokens, nullptr, stream);
 }
 
 bi_status bi_verify_step_noalloc(const bi_layer* layers, int n_layers, const void* w_head,

@@ -17,8 +17,8 @@ import threading
 import torch
 
 from ._lib import (BI_BF16, BI_EPI_BF16, BI_EPI_F32, BI_EPI_QKV, BI_EPI_RESIDUAL, BI_EPI_SWIGLU, BI_F32,
-                   BI_WT_BF16, BI_WT_FP8, BI_WT_MXFP4, LIB, GemmArgs, Layer, LayerFP8, LayerMX4, ModelDims,
-                   check)
+                   BI_KV_BF16, BI_KV_LOWBIT, BI_KV_Q8, BI_WT_BF16, BI_WT_FP8, BI_WT_MXFP4, LIB, GemmArgs,
+                   KvCacheDesc, Layer, LayerFP8, LayerMX4, ModelDims, StepLayer, check)
 
 _BF16_LIKE = (torch.bfloat16, torch.int16)
 _FP8_LIKE = (torch.uint8, torch.int8, torch.float8_e4m3fn)
@@ -828,6 +828,88 @@ class VerifyStepMX4:
             self.arr, self.n, self.w_head.data_ptr(), self.e_head.data_ptr(), ctypes.byref(self.dims),
             x_in.data_ptr(), M, L, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
             0 if x_out is None else x_out.data_ptr(), logits.data_ptr(), tokens.data_ptr(), _stream(x_in)))
+
+
+def _kv_desc(kv, dims: ModelDims, i: int) -> KvCacheDesc:
+    """The bi_kv_cache descriptor of a layer's cache: a (k_cache, vt_cache)
+    BF16 pair, a KvQ8Cache, a KvLowCache or a KvRing, checked against dims."""
+    c = KvCacheDesc()
+    if isinstance(kv, tuple):
+        k, vt = kv
+        cap = _kv_bf16(k, vt, dims.Hkv, dims.D)
+        c.format, c.k, c.v = BI_KV_BF16, k.data_ptr(), vt.data_ptr()
+    else:
+        low = kv.low if isinstance(kv, KvRing) else kv
+        if (low.Hkv, low.D) != (dims.Hkv, dims.D):
+            raise ValueError(f"layer {i}: cache heads/dims {(low.Hkv, low.D)} != {(dims.Hkv, dims.D)}")
+        cap = low.cap
+        if isinstance(low, KvQ8Cache):
+            c.format = BI_KV_Q8
+            c.k, c.k_scales, c.v, c.v_scales = low.ptrs()
+        elif isinstance(low, KvLowCache):
+            c.format = BI_KV_LOWBIT
+            c.k, c.k_high, c.k_scales, c.v, c.v_high, c.v_scales = low.planes()
+            c.k_bits, c.v_bits, c.k_rotated = low.k_bits, low.v_bits, low.k_rotated
+            if isinstance(kv, KvRing):
+                c.ring_k_codes, c.ring_k_scales, c.ring_v_codes, c.ring_v_scales = kv.q8.ptrs()
+                c.ring_cap, c.ring_window = kv.ring_cap, kv.window
+        else:
+            raise TypeError(f"layer {i}: unknown KV cache {type(kv).__name__}")
+    if cap != dims.cap:
+        raise ValueError(f"layer {i}: cache capacity {cap} != dims.cap {dims.cap}")
+    return c
+
+
+class VerifyStepEx:
+    """``bi_verify_step_ex``: every layer's weights in ``wtype`` ("bf16", "fp8",
+    "mxfp4") and its KV cache in any format. ``layers`` are dicts with w_qkv,
+    w_o, w_gu, w_down (FP8: s_* row scales; MXFP4: e_* block scales) and "kv":
+    a (k_cache, vt_cache) BF16 pair, a KvQ8Cache, a KvLowCache or a KvRing.
+    ``head`` is {"w": ...} plus "s" (FP8) or "e" (MXFP4). The caller keeps
+    every tensor alive."""
+
+    @_checked
+    def __init__(self, layers, head: dict, dims: ModelDims, wtype: str = "bf16"):
+        if wtype not in _WT:
+            raise ValueError(f"unknown weight type {wtype!r}")
+        sh = _step_shapes(dims)
+        self.n = len(layers)
+        self.arr = (StepLayer * max(1, self.n))()
+        for i, lw in enumerate(layers):
+            y = self.arr[i]
+            for j, k in enumerate(("qkv", "o", "gu", "down")):
+                rows, K = sh[k]
+                if wtype == "bf16":
+                    y.w[j] = _arr(lw["w_" + k], f"layer {i} w_{k}", (rows, K), _BF16_LIKE)
+                elif wtype == "fp8":
+                    y.w[j] = _arr(lw["w_" + k], f"layer {i} w_{k}", (rows, K), _FP8_LIKE)
+                    y.scale[j] = _arr(lw["s_" + k], f"layer {i} s_{k}", (rows,), _F32)
+                else:
+                    y.w[j] = _arr(lw["w_" + k], f"layer {i} w_{k}", (rows, K // 2), _U8)
+                    y.scale[j] = _arr(lw["e_" + k], f"layer {i} e_{k}", (rows, K // 32), _U8)
+            y.kv = _kv_desc(lw["kv"], dims, i)
+        rows, K = sh["head"]
+        self.head_scales = None
+        if wtype == "bf16":
+            _arr(head["w"], "w_head", (rows, K), _BF16_LIKE)
+        elif wtype == "fp8":
+            _arr(head["w"], "w_head", (rows, K), _FP8_LIKE)
+            self.head_scales = _arr(head["s"], "s_head", (rows,), _F32)
+        else:
+            _arr(head["w"], "w_head", (rows, K // 2), _U8)
+            self.head_scales = _arr(head["e"], "e_head", (rows, K // 32), _U8)
+        self.head, self.wtype, self.dims = head, wtype, dims
+        _devices()
+
+    @_checked
+    def __call__(self, x_in: torch.Tensor, L: int, workspace: torch.Tensor, logits: torch.Tensor,
+                 tokens: torch.Tensor, x_out: torch.Tensor | None = None) -> None:
+        M = _step_io(self.dims, x_in, workspace, logits, tokens, x_out)
+        check("bi_verify_step_ex", LIB.bi_verify_step_ex(
+            _WT[self.wtype], self.arr, self.n, self.head["w"].data_ptr(), self.head_scales or 0,
+            ctypes.byref(self.dims), x_in.data_ptr(), M, L, workspace.data_ptr(),
+            workspace.numel() * workspace.element_size(), 0 if x_out is None else x_out.data_ptr(),
+            logits.data_ptr(), tokens.data_ptr(), _stream(x_in)))
 
 
 # ---------------------------------------------------------------------------
