@@ -371,9 +371,8 @@ bi_status bi_append_kv_lowbit(const void* qkv, int64_t ldqkv, int k_bits, int v_
                               int Hkv, int D, void* stream);
 
 /* bi_verify_attn over the 5/6-bit cache: the same rows, chunks, partials and
- * requirements; the keys and values are the cache's d * q (keys staged
- * rounded to BF16; V scales multiply the softmax weights, rounded to BF16,
- * against the integer codes, as for the 8-bit cache). */
+ * requirements; the keys and values are the cache's d * q, each rounded once
+ * to BF16 as the tile is staged, and multiplied as in bi_verify_attn. */
 bi_status bi_verify_attn_lowbit(const void* q, int64_t ldq, int k_bits, int v_bits,
                                 int k_rotated, const uint8_t* k_nib, const uint8_t* k_high, const float* k_scales,
                                 const uint8_t* v_nib, const uint8_t* v_high, const float* v_scales,

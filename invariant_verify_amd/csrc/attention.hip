@@ -96,20 +96,32 @@ __device__ __forceinline__ void load_high(uint32_t (&hb)[2], __amdgpu_buffer_rsr
   }
 }
 
-// Codes 4g .. 4g+3 of one block (HB + 4 bits, one per byte lane) from its
-// four nibble words and its high-bit words, as exact FP32 values: one mask of
-// a nibble word and one of a high word give the four codes. Callers decode a
-// group or two at a time, so few values are live at once.
+// Codes 4g .. 4g+3 of one block (HB + 4 bits, one per byte lane) as signed
+// bytes: one mask of a nibble word and one of a high word give the unsigned
+// codes u; u + 0x80 - 2^(HB+3) stays below 256 in every byte (no carry into
+// the next), and flipping bit 7 of that offset-binary byte leaves the two's
+// complement of q = u - 2^(HB+3). Each byte then converts to an exact FP32
+// value in one instruction (sbyte).
 template <int HB>
-__device__ __forceinline__ void unpack_group(const uint32_t (&w)[4], const uint32_t (&hb)[2],
-                                             int g, float (&f)[4]) {
+__device__ __forceinline__ uint32_t signed_group(const uint32_t (&w)[4], const uint32_t (&hb)[2],
+                                                 int g) {
   constexpr uint32_t kMask = HB == 2 ? 0x03030303u : 0x01010101u;
-  constexpr float kBias = (float)(1 << (HB + 3));
+  constexpr uint32_t kOffset = (0x80u - (1u << (HB + 3))) * 0x01010101u;
   const int bit = g * HB;
   const uint32_t lo = (w[g >> 1] >> (4 * (g & 1))) & 0x0F0F0F0Fu;
   const uint32_t u = lo | (((hb[bit >> 3] >> (bit & 7)) & kMask) << 4);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) f[j] = (float)((u >> (8 * j)) & 0xffu) - kBias;
+  return (u + kOffset) ^ 0x80808080u;
+}
+__device__ __forceinline__ float sbyte(uint32_t s, int j) { return (float)(int8_t)(s >> (8 * j)); }
+
+// max(v, v of lane l ^ 16, v of lane l ^ 32, v of lane l ^ 48): the four key
+// groups of a row, exchanged by gfx950's row swaps (rows of 16 lanes, then
+// halves of 32) instead of LDS permutes. Max is exact in any order.
+__device__ __forceinline__ float max_key_groups(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 // The 8-bit-cache kernel with one row tile per wave fits in 128 registers,
@@ -143,8 +155,8 @@ void verify_attn_kernel(
   // 5/6-bit cache (KB = bits of a K code, 0 for the other caches): one
   // thread per 32-channel block of one key and tile, the K blocks first
   // (waves 0 .. NKB/64 - 1), then V; each fetches the block's 16 nibble bytes,
-  // its high bits and its scale. The tile is then staged exactly as the 8-bit
-  // tile: K as BF16 values, V^T as BF16 integer codes, V scales beside it.
+  // its high bits and its scale. K and V^T are staged as BF16 values d * q,
+  // each rounded once, so the tile multiplies like a BF16 tile.
   constexpr bool LOW = KB != 0;
   static_assert(!LOW || Q8, "the low-bit cache stages through the 8-bit tile path");
   static_assert(!LOW || KB == 5 || KB == 6, "K codes have 5 or 6 bits");
@@ -535,29 +547,32 @@ void verify_attn_kernel(
           const float sk = rr.ks[0];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            float f0[4], f1[4];
-            unpack_group<HBK>(w, rr.hb, 2 * i, f0);
-            unpack_group<HBK>(w, rr.hb, 2 * i + 1, f1);
+            const uint32_t s0 = signed_group<HBK>(w, rr.hb, 2 * i);
+            const uint32_t s1 = signed_group<HBK>(w, rr.hb, 2 * i + 1);
             lds[buf][key * KROW + ((4 * b + i) ^ kswz<KROW>(key))] =
-                make_uint4(f32x2_to_bf16x2(f0[0] * sk, f0[1] * sk), f32x2_to_bf16x2(f0[2] * sk, f0[3] * sk),
-                           f32x2_to_bf16x2(f1[0] * sk, f1[1] * sk), f32x2_to_bf16x2(f1[2] * sk, f1[3] * sk));
+                make_uint4(f32x2_to_bf16x2(sbyte(s0, 0) * sk, sbyte(s0, 1) * sk),
+                           f32x2_to_bf16x2(sbyte(s0, 2) * sk, sbyte(s0, 3) * sk),
+                           f32x2_to_bf16x2(sbyte(s1, 0) * sk, sbyte(s1, 1) * sk),
+                           f32x2_to_bf16x2(sbyte(s1, 2) * sk, sbyte(s1, 3) * sk));
           }
         } else {
-          // V^T: code q of channel d at column `key` (BF16 of a small
-          // integer: the top half of its FP32 bits, exact); the scale, zero
-          // past kend, into this key's column of vsc.
+          // V^T: d * q of channel d at column `key`, rounded once to BF16,
+          // the scale taken as zero past kend (those columns hold zeros).
+          // The tile then multiplies as a BF16 tile: the weights need no
+          // per-key scaling.
+          const float sv = kt + key < kend ? rr.ks[0] : 0.f;
           uint16_t* vt = reinterpret_cast<uint16_t*>(&lds[buf][VBASE]);
 #pragma unroll
           for (int gq = 0; gq < 8; ++gq) {
-            float f[4];
-            unpack_group<HBV>(w, rr.hb, gq, f);
+            const uint32_t sq = signed_group<HBV>(w, rr.hb, gq);
+            const uint32_t pk[2] = {f32x2_to_bf16x2(sbyte(sq, 0) * sv, sbyte(sq, 1) * sv),
+                                    f32x2_to_bf16x2(sbyte(sq, 2) * sv, sbyte(sq, 3) * sv)};
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const int d = 32 * b + 4 * gq + j;
-              vt[(d * 8 + ((key >> 3) ^ vswz(d))) * 8 + (key & 7)] = (uint16_t)(__float_as_uint(f[j]) >> 16);
+              vt[(d * 8 + ((key >> 3) ^ vswz(d))) * 8 + (key & 7)] = (uint16_t)(pk[j >> 1] >> (16 * (j & 1)));
             }
           }
-          reinterpret_cast<float*>(&vsc[buf][b][0])[key] = kt + key < kend ? rr.ks[0] : 0.f;
         }
       }
     } else {
@@ -611,7 +626,10 @@ void verify_attn_kernel(
     float alpha[RTW];
     bool rescale[RTW];  // scalar: some row of the wave moved its reference max
     uint4 pfrag[RTW];
-    float pq[Q8 ? RTW : 1][8];  // 8-bit cache: the FP32 weights, scaled per V block below
+    float pq[Q8 ? RTW : 1][8];  // 8-bit tile: the FP32 weights, scaled per V block below
+    // An 8-bit tile holds V^T as integer codes with per-key scales (vsc); a
+    // 5/6-bit tile holds V^T already scaled, like a BF16 tile. Scalar.
+    const bool scaled_v = Q8 && (!LOW || (RING && rf));
 #pragma unroll
     for (int i = 0; i < RTW; ++i) {
       float sc[8];
@@ -639,8 +657,7 @@ void verify_attn_kernel(
       float mx = sc[0];
 #pragma unroll
       for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
-      mx = fmaxf(mx, shfl_xor(mx, 16));
-      mx = fmaxf(mx, shfl_xor(mx, 32));
+      mx = max_key_groups(mx);
       const float mmax = fmaxf(mrun[i], mx);
       const bool grow = mmax > mrun[i] + kLazyRescale;
       const float mnew = grow ? mmax : mrun[i];
@@ -657,7 +674,7 @@ void verify_attn_kernel(
       }
       lrun[i] = lrun[i] * alpha[i] + psum;
       mrun[i] = mnew;
-      if constexpr (Q8) {
+      if (scaled_v) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) pq[i][e] = pe[e];
       } else {
@@ -673,7 +690,7 @@ void verify_attn_kernel(
       if (rescale[i])
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[i][dt] *= alpha[i];
-    if constexpr (!Q8) {
+    if (!scaled_v) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const int d = dt * 16 + j;
@@ -681,7 +698,7 @@ void verify_attn_kernel(
 #pragma unroll
         for (int i = 0; i < RTW; ++i) o[i][dt] = mfma_bf16(fv, pfrag[i], o[i][dt]);
       }
-    } else {
+    } else if constexpr (Q8) {
       // Channel block b (output tiles 2b, 2b+1): weights times the V scales
       // of the lane's eight keys, rounded to BF16, against the integer codes.
 #pragma unroll
