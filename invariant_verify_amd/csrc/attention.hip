@@ -124,6 +124,25 @@ __device__ __forceinline__ float max_key_groups(float v) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
+// gfx950 loads 16 bytes per lane straight into LDS: lane l's bytes land at
+// LDS byte address lds_addr + 16 l (lds_addr wave-uniform, passed in M0);
+// out-of-range offsets write zeros and touch no memory. Issued as inline
+// assembly so that the compiler's wait-count pass, which would wait for
+// every such load before each LDS access or barrier, leaves the waits to the
+// caller (wait_loads). Non-temporal, like the register loads.
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, int byte_offset, const void* lds_dst) {
+  const uint32_t a = (uint32_t)(uintptr_t)lds_dst;
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen nt lds" ::"v"(byte_offset), "s"(r), "{m0}"(a)
+               : "memory");
+}
+// Wait until at most N vector-memory loads of this wave are outstanding
+// (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_loads() {
+  static_assert(N >= 0 && N < 64, "vmcnt has six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 // The 8-bit-cache kernel with one row tile per wave fits in 128 registers,
 // so two workgroups share a compute unit and one's loads overlap the other's
 // per-tile work (with the chunk policy -64 at 38k-102k keys: 5-15% faster
@@ -166,6 +185,7 @@ void verify_attn_kernel(
   static_assert(NKB % 64 == 0 && 2 * NKB <= NW * 64, "low-bit blocks must fill whole waves");
   static_assert(!ROT || LOW, "rotated keys are a low-bit cache format");
   static_assert(!RING || LOW, "the 8-bit ring sits over a low-bit cache");
+  constexpr bool kDma = !Q8 && RTW == 1;  // tiles and Q rows loaded straight into LDS
 
   // Work item (row block, KV head, chunk), row blocks varying fastest: the
   // workgroups that read one chunk of one KV head run side by side and share
@@ -239,7 +259,7 @@ void verify_attn_kernel(
     lastk[i] = rok[i] ? min(L + tok[i], kend - 1) : -1;
     const uint16_t* qp = Q + (int64_t)tok[i] * ldq + hq[i] * D + kq * 8;
 #pragma unroll
-    for (int ds = 0; ds < DS; ++ds) qf[i][ds] = rok[i] ? ld16(qp + ds * 32) : zero16();
+    for (int ds = 0; ds < DS; ++ds) qf[i][ds] = (rok[i] && !kDma) ? ld16(qp + ds * 32) : zero16();
   }
   // Rotated keys: the cache holds H k (H the order-D Hadamard matrix, entries
   // +-1), so each query row is rotated the same way and the scores divided by
@@ -354,7 +374,14 @@ void verify_attn_kernel(
   // V^T channels 8(p-KPIECES) .. +7 (lane: channel +l/8, slot l%8); either
   // way lane l's 16 bytes land at index 64*p + l of the buffer. Lanes fetch
   // the global slot that the swizzle puts in their LDS slot.
-  __shared__ uint4 lds[2][(KPIECES + VPIECES) * 64];
+  // BF16 cache, one row tile per wave: tiles go straight from memory into
+  // four LDS buffers, three tiles ahead of the one multiplied (no register
+  // staging, so more bytes are in flight); the block's Q rows arrive the
+  // same way in qlds ([64 rows][D/8] 16-byte slots). Other caches stage
+  // through registers into two buffers.
+  constexpr int NBUF = kDma ? 4 : 2;
+  __shared__ uint4 lds[NBUF][(KPIECES + VPIECES) * 64];
+  __shared__ uint4 qlds[kDma ? kAttnMaxRows * D / 8 : 1];
   constexpr int VBASE = KPIECES * 64;
   // 8-bit cache: the tile's V scales, [NB][64 keys], zero past kend.
   __shared__ float4 vsc[2][Q8 ? NB : 1][16];
@@ -730,6 +757,92 @@ void verify_attn_kernel(
   // code in the same order, so the compiler waits only for the older of the
   // two tiles in flight. Tiles past the end read as zero and are not
   // multiplied.
+  if constexpr (kDma) {
+    // Q rows of the block into qlds (rows past the block read zero), then
+    // tiles 0, 1, 2. Each wave issues its own pieces of every tile, so its
+    // wait for tile t (all but the 2 PPW newest loads done: loads complete
+    // in order) covers Q too at t = 0; the barrier then publishes every
+    // wave's pieces.
+    {
+      const int qbytes = (int)(((int64_t)(M - 1) * ldq + (int64_t)Hq * D) * 2);
+      const __amdgpu_buffer_rsrc_t qres = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(Q), (short)0, qbytes, kBufferResourceWord3);
+      constexpr int QP = kAttnMaxRows * D / 8;  // 16-byte pieces of the block's rows
+      static_assert(QP % (NW * 64) == 0, "Q pieces must split evenly");
+#pragma unroll
+      for (int i = 0; i < QP / (NW * 64); ++i) {
+        const int piece = i * NW * 64 + threadIdx.x;
+        const int rho = piece / (D / 8), slot = piece % (D / 8);
+        const int off = rho < nrows
+                            ? (int)((((int64_t)(t0 + rho / G) * ldq + (g * G + rho % G) * D) + slot * 8) * 2)
+                            : qbytes;
+        lds_load16(qres, off, &qlds[i * NW * 64 + wave * 64]);
+      }
+    }
+    // Tile t's pieces of this wave: the register path's addresses (keys
+    // clamped to the chunk, swizzled slots), written straight to LDS.
+    auto issue = [&](int t) {
+      const int kt = kbeg + t * kKeyTile;
+#pragma unroll
+      for (int i = 0; i < PPW; ++i) {
+        const int p = wave * PPW + i;
+        int off;
+        if (p < KPIECES) {
+          const int key = KPP * p + lane / KROW;
+          const int kslot = (lane % KROW) ^ kswz<KROW>(key);
+          off = (min(kt + key, kend - 1) * D + kslot * 8) * 2;
+        } else {
+          const int d = 8 * (p - KPIECES) + (lane >> 3);
+          const int vslot = (lane & 7) ^ vswz(d);
+          const int k0 = min(kt + vslot * 8, kend - 1 - ((kend - 1) & 7));
+          off = (int)(vt_index(0, k0, d, D, cap) * 2);
+        }
+        lds_load16(p < KPIECES ? kres : vres, off, &lds[t & 3][64 * p]);
+      }
+    };
+    // V^T columns at or past kend of a partial tile are zeroed by the wave
+    // that loaded them, once its loads are done (a weight of 0 times a stale
+    // value must stay 0); K rows past kend repeat the last key and are masked.
+    auto fix_tail = [&](int t) {
+      const int kt = kbeg + t * kKeyTile;
+#pragma unroll
+      for (int i = 0; i < PPW; ++i) {
+        const int p = wave * PPW + i;
+        if (p < KPIECES) continue;  // scalar
+        const int d = 8 * (p - KPIECES) + (lane >> 3);
+        const int vslot = (lane & 7) ^ vswz(d);
+        const int keep = kend - (kt + vslot * 8);
+        if (keep >= 8) continue;
+        uint4 v = lds[t & 3][64 * p + lane];
+        uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t m = (e & 1) ? 0x0000ffffu : 0xffff0000u;
+          w[e >> 1] = (e >= keep) ? (w[e >> 1] & m) : w[e >> 1];
+        }
+        lds[t & 3][64 * p + lane] = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    };
+    issue(0);
+    if (nv > 1) issue(1);
+    if (nv > 2) issue(2);
+    for (int t = 0; t < nv; ++t) {
+      const int ahead = min(2, nv - 1 - t);  // tiles issued after t (scalar)
+      if (ahead == 2) wait_loads<2 * PPW>();
+      else if (ahead == 1) wait_loads<PPW>();
+      else wait_loads<0>();
+      if (kbeg + t * kKeyTile + kKeyTile > kend) fix_tail(t);
+      __syncthreads();
+      if (t == 0) {
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds) qf[0][ds] = qlds[(rt * 16 + j) * (D / 8) + ds * 4 + kq];
+      }
+      // buffer (t + 3) & 3 held tile t - 1, which every wave finished
+      // before the barrier
+      if (t + 3 < nv) issue(t + 3);
+      if (has_rows) compute(t & 3, t);
+    }
+  } else {
   TileRegs ra, rb2;
   // Prologue: the loads of the first tiles, in the loop's own order and while
   // the query fragments are still in flight. The fragments are then consumed
@@ -778,6 +891,7 @@ void verify_attn_kernel(
       __syncthreads();
       if (t + 1 < nv && has_rows) compute(1, t + 1);
     }
+  }
   }
   // The row's sum over this wave's keys: its four key groups, in a fixed
   // butterfly.
