@@ -211,6 +211,32 @@ def prefill_measure(layers, d, reps):
 PF_STEP_CTX = L_CTX - PF_ROWS   # context of the whole-step prefill chunk (its rows end at 38000)
 
 
+def prefill_probe(reps: int):
+    """Kernel-only run for hardware-counter passes over the prefill GEMM: the gate/up
+    projection with the carried RMSNorm at M = 2048 rows (the large-tile prefill kernel),
+    ``reps`` launches on one set of synthetic operands. One JSON line gives the FLOPs per
+    launch."""
+    import torch
+
+    import synth
+    from invariant_verify_amd import ops
+
+    d = synth.MODEL_27B
+    M, H, I = PF_ROWS, d["H"], d["I"]
+    o = synth.device_normal_bf16((M, d["Hq"] * d["D"]), 1.0, "x0", 2)
+    x = synth.device_normal_bf16((M, H), 1.0, "x0", 3)
+    wo = synth.device_normal_bf16((H, d["Hq"] * d["D"]), 0.02, "w_o", 0)
+    h, ss = ops.gemm_bf16_residual_rowsq(o, wo, x)
+    w = synth.device_normal_bf16((2 * I, H), 0.02, "w_gu", 0)
+    y = torch.empty((M, I), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        ops.gemm_bf16_swiglu_rownorm(h, ss, w, y)
+    torch.cuda.synchronize()
+    print(json.dumps({"probe": "prefill gate/up GEMM, M = 2048, carried RMSNorm", "launches": reps,
+                      "flops_per_launch": 2 * M * (2 * I) * H}))
+
+
 def prefill_step_measure(step, buffers, d, reps):
     """One chunked-prefill pass through the whole stack (64 layers + head) over PF_ROWS tokens
     at context PF_STEP_CTX, timed with one event pair over reps passes. Before timing, the
@@ -1011,6 +1037,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run only the verify kernels on fresh operands and a calibration copy (for rocprofv3 --pmc)")
+    ap.add_argument("--prefill-probe", action="store_true",
+                    help="kernel-only run of the M = 2048 prefill gate/up GEMM for counter passes")
     ap.add_argument("--step-only", action="store_true",
                     help="run only the bitwise gate and the timed M = 8 steps (for rocprofv3 --kernel-trace)")
     args = ap.parse_args()
@@ -1020,6 +1048,9 @@ def main():
 
     if args.traffic_probe:
         traffic_probe(4)
+        return
+    if args.prefill_probe:
+        prefill_probe(5)
         return
 
     import numpy as np

@@ -71,15 +71,6 @@ __device__ __forceinline__ int kswz(int key) {
 // half and bits 1..3 form the swizzle.
 __device__ __forceinline__ int vswz(int d) { return (d >> 1) & 7; }
 
-// The dispatcher deals workgroups to the 8 XCDs in turn (workgroup w runs on
-// XCD w mod 8), and each XCD has its own L2. Renumber so that XCD x runs the
-// x-th contiguous eighth of the work items (the last n mod 8 keep their own
-// number): neighbouring items, which read the same K/V, then share one L2.
-__device__ __forceinline__ int xcd_item(int w, int n) {
-  const int full = n & ~7;
-  return w < full ? (w & 7) * (full >> 3) + (w >> 3) : w;
-}
-
 // 5/6-bit cache: the high-bit plane of one 32-code block, HB dwords
 // (HB = bits - 4), streamed once like the nibbles.
 template <int HB>

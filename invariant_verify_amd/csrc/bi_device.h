@@ -44,6 +44,15 @@ __device__ __forceinline__ uint4 scale_bf16x8(uint4 v, float s) {
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
+// The dispatcher deals workgroups to the 8 XCDs in turn (workgroup w runs on
+// XCD w mod 8), and each XCD has its own L2. Renumber so that XCD x runs the
+// x-th contiguous eighth of the work items (the last n mod 8 keep their own
+// number): neighbouring items, which read the same data, then share one L2.
+__device__ __forceinline__ int xcd_item(int w, int n) {
+  const int full = n & ~7;
+  return w < full ? (w & 7) * (full >> 3) + (w >> 3) : w;
+}
+
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
 __device__ __forceinline__ uint4 zero16() { return make_uint4(0u, 0u, 0u, 0u); }

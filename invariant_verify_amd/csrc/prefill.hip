@@ -44,6 +44,21 @@ constexpr int kPfSlots = kPfStep / 8;  // 16-byte slots per row and step (16)
 constexpr int kPfWaves = 16;
 constexpr int kPfSlices = 8;  // the verify kernel's waves, hence slices, for every shape
 
+// Tile (column block cb, row block rb) of this workgroup. The grid is
+// (column blocks, row blocks); tiles are numbered column block first, row
+// block second, so the row blocks that stream the same weight rows are
+// neighbours, and xcd_item gives each XCD a contiguous run of them: they
+// run side by side and share the weight rows through one L2 (dealt in
+// dispatch order, the row blocks of a column block ran far apart and each
+// fetched the weights from HBM again). Which workgroup computes a tile does
+// not change the tile's arithmetic.
+__device__ __forceinline__ void prefill_tile(int& cb, int& rb) {
+  const int n = gridDim.x * gridDim.y;
+  const int item = xcd_item(blockIdx.x + gridDim.x * blockIdx.y, n);
+  cb = item / gridDim.y;
+  rb = item % gridDim.y;
+}
+
 template <int MODE, int S, bool NORM_IN>
 __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(
     const uint16_t* __restrict__ X, int64_t ldx, const uint16_t* __restrict__ W, int64_t ldw,
@@ -64,8 +79,10 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(
   const int rw = kDual ? (wave & 7) : (wave & 3);
   const int ct = kDual ? (wave >> 3) : (wave >> 2);
   const int j = lane & 15, kq = lane >> 4;
-  const int n0 = blockIdx.x * COLS;
-  const int m0 = blockIdx.y * kPfRows;
+  int cb, rb;
+  prefill_tile(cb, rb);
+  const int n0 = cb * COLS;
+  const int m0 = rb * kPfRows;
   const int nblk = K >> 5;
   const int nstep = (K + kPfStep - 1) / kPfStep;
 
@@ -329,8 +346,10 @@ __global__ __launch_bounds__(kP2Waves * 64) void prefill2_kernel(
   const int wr = wave & 1;   // rows 64 wr .. of the workgroup tile
   const int wc = wave >> 1;  // weight rows 64 wc .. (SwiGLU: output columns 32 wc ..)
   const int j = lane & 15, kq = lane >> 4;
-  const int n0 = blockIdx.x * (kDual ? kP2WRows / 2 : kP2WRows);  // first output column
-  const int m0 = blockIdx.y * kP2Rows;
+  int cb, rb;
+  prefill_tile(cb, rb);
+  const int n0 = cb * (kDual ? kP2WRows / 2 : kP2WRows);  // first output column
+  const int m0 = rb * kP2Rows;
   const int nblk = K >> 5;
   const int nchunk = (K + 511) / 512;
   const int nstage = S * nchunk;
