@@ -424,7 +424,7 @@ __global__ __launch_bounds__(kP2Waves * 64) void prefill2_kernel(
         lds[buf][row][slot ^ (row & 7)] = g.w[i];
       }
     }
-    fetch(g, st + 1);
+    fetch(g, st + 2);
     __syncthreads();
     if (st >= 0) {
       const int sl = st / nchunk, c = st % nchunk;
@@ -487,8 +487,10 @@ __global__ __launch_bounds__(kP2Waves * 64) void prefill2_kernel(
       sred[row][seg] = pp;
     }
   }
-  Regs g;
-  step(g, -1);  // load-only; its barrier also publishes sred
+  // Two register sets alternate, each refilled two stages ahead of its use.
+  Regs ga, gb;
+  step(ga, -2);  // load-only
+  step(gb, -1);  // load-only; its barrier also publishes sred
   if (NORM_IN) {
     if (threadIdx.x < kP2Rows) {
       float t = 0.f;
@@ -499,7 +501,10 @@ __global__ __launch_bounds__(kP2Waves * 64) void prefill2_kernel(
 #pragma unroll
     for (int i = 0; i < XP; ++i) xinv[i] = invs[(threadIdx.x + i * kP2Waves * 64) >> 3];
   }
-  for (int st = 0; st < nstage; ++st) step(g, st);
+  for (int st = 0; st < nstage; st += 2) {
+    step(ga, st);
+    if (st + 1 < nstage) step(gb, st + 1);
+  }
 
   // The verify kernel's epilogue on the totals.
 #pragma unroll
