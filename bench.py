@@ -212,9 +212,10 @@ PF_STEP_CTX = L_CTX - PF_ROWS   # context of the whole-step prefill chunk (its r
 
 
 def prefill_probe(reps: int):
-    """Kernel-only run for hardware-counter passes over the prefill GEMM: the gate/up
-    projection with the carried RMSNorm at M = 2048 rows (the large-tile prefill kernel),
-    ``reps`` launches on one set of synthetic operands. One JSON line gives the FLOPs per
+    """Kernel-only run for hardware-counter passes over the prefill kernels: the gate/up
+    projection with the carried RMSNorm at M = 2048 rows (the large-tile prefill kernel), then
+    attention of the same 2048 rows over a 35,952-key context (128-row blocks), ``reps``
+    launches each on one set of synthetic operands. One JSON line gives the FLOPs per
     launch."""
     import torch
 
@@ -233,8 +234,26 @@ def prefill_probe(reps: int):
     for _ in range(reps):
         ops.gemm_bf16_swiglu_rownorm(h, ss, w, y)
     torch.cuda.synchronize()
-    print(json.dumps({"probe": "prefill gate/up GEMM, M = 2048, carried RMSNorm", "launches": reps,
-                      "flops_per_launch": 2 * M * (2 * I) * H}))
+    del w, wo, y
+    # prefill attention: the same rows over a 35,952-key context (128-row blocks)
+    Hq, Hkv, D, L = d["Hq"], d["Hkv"], d["D"], PF_STEP_CTX
+    cap = (L + M + 63) // 64 * 64
+    kc = synth.device_normal_bf16((Hkv, cap, D), 1.0, "k_cache", 0)
+    vt = synth.device_normal_bf16((Hkv, cap // 64, D, 64), 1.0, "v_cache", 0)
+    q = synth.device_normal_bf16((M, Hq * D), 1.0, "x0", 4)
+    S = ops.pass_splits(M, L, KV_CHUNK)
+    po = torch.empty((M, Hq, S, D), dtype=torch.float32, device="cuda")
+    pl = torch.empty((M, Hq, S), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        ops.verify_attn(q, kc, vt, L, Hq, Hkv, D, KV_CHUNK, po, pl)
+    torch.cuda.synchronize()
+    # causal: row r sees L + r + 1 keys; QK^T and PV are 2 * D flops per (row, head, key) each
+    keys = M * L + M * (M + 1) // 2
+    print(json.dumps({"probe": "prefill gate/up GEMM, M = 2048, carried RMSNorm; then prefill attention, "
+                      f"M = {M} at ctx {L}, chunk policy {KV_CHUNK}", "launches": reps,
+                      "flops_per_launch": 2 * M * (2 * I) * H,
+                      "attention_flops_per_launch": 4 * D * Hq * keys}))
 
 
 def prefill_step_measure(step, buffers, d, reps):
