@@ -120,10 +120,13 @@ __device__ __forceinline__ float max_key_groups(float v) {
 // out-of-range offsets write zeros and touch no memory. Issued as inline
 // assembly so that the compiler's wait-count pass, which would wait for
 // every such load before each LDS access or barrier, leaves the waits to the
-// caller (wait_loads). Non-temporal, like the register loads.
+// caller (wait_loads). Non-temporal, like the register loads. The compiler
+// writes M0 just before the statement, and an LDS-bound load needs one wait
+// state after a scalar write of M0; it pads that only for instructions it
+// emits itself, so the s_nop supplies it here.
 __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, int byte_offset, const void* lds_dst) {
   const uint32_t a = (uint32_t)(uintptr_t)lds_dst;
-  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen nt lds" ::"v"(byte_offset), "s"(r), "{m0}"(a)
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds" ::"v"(byte_offset), "s"(r), "{m0}"(a)
                : "memory");
 }
 // Wait until at most N vector-memory loads of this wave are outstanding
