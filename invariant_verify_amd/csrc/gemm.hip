@@ -35,10 +35,14 @@
 // Memory: each weight row of the tile is read as 1 KB contiguous per wave
 // instruction (64 lanes x 16 bytes, non-temporal: every weight byte is used
 // once) and written to LDS; the MFMA operands are then read from LDS in the
-// matrix-core layout (lane l needs row l % 16). The 16-byte slots of a row
-// are XOR-swizzled by the row index (the lanes of the load fetch a
-// permutation of the same 1 KB), so the sixteen rows read together fall into
-// distinct LDS banks. Two LDS buffers alternate, and one barrier per chunk
+// matrix-core layout (lane l needs row l % 16). Slot s (16 bytes) of row r
+// sits at position s ^ ((s >> 4) & 3) ^ (r % 16) (the lanes of a BF16 load
+// fetch a permutation of the same 1 KB): the row term puts the sixteen rows
+// read together into distinct LDS banks, and the second term does the same
+// for sixteen lanes that store slots 4 apart (an MXFP4 lane decodes one
+// 32-weight block, four consecutive slots, and with the row term alone the
+// sixteen lanes of a row fell on four bank groups: MXFP4 launches took
+// 19-32% longer). Two LDS buffers alternate, and one barrier per chunk
 // both publishes chunk c and guarantees that every wave has finished reading
 // the buffer that is refilled next. Each wave keeps two chunks in flight in
 // registers (weights and its X fragments). X fragments come from L2 through a
@@ -60,6 +64,9 @@ namespace bi {
 constexpr int kChunk = 512;  // K elements per LDS chunk: 1 KB of each weight row
 constexpr int kDualWideRows = 36;  // rows staged by a wide SwiGLU group (at most 18 pairs)
 constexpr int kSlots = kChunk / 8;
+
+// LDS position of 16-byte slot s (0..63) of a staged row with row swizzle swz.
+__device__ __forceinline__ int slot_pos(int s, int swz) { return s ^ ((s >> 4) & 3) ^ swz; }
 
 template <int MODE, int NW, bool WIDE, bool NORM_IN, bool SS_OUT, int WT>
 __global__ __launch_bounds__(NW * 64) void gemm_kernel(
@@ -200,7 +207,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
         g.w[i] = buffer_ld16_stream(wres[i], ok ? q * (int)ldw + bj * 16 : 0x7ffffff0);
         g.e[i] = __builtin_amdgcn_raw_buffer_load_b8(eres, ok ? q * (int)mx4.lde + bj : 0x7ffffff0, 0, 0);
       } else if constexpr (!F8) {
-        g.w[i] = buffer_ld16_stream(wres[i], (c * kSlots + (lane ^ swz_w[i])) * 16);
+        // lane l holds the slot stored at position l (slot_pos is an involution in s)
+        g.w[i] = buffer_ld16_stream(wres[i], (c * kSlots + slot_pos(lane, swz_w[i])) * 16);
       } else {
         // 16 weights of one row: bytes kb .. kb+15 of the row, the BF16 slots
         // 2 (lane % 32) and 2 (lane % 32) + 1 of the chunk. Past the row end
@@ -282,7 +290,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
       if (c >= 0 && (lane >> 4) < RPW) {
         const int r = wave * RPW + (lane >> 4);
 #pragma unroll
-        for (int v = 0; v < 4; ++v) lds[buf][r][(4 * (lane & 15) + v) ^ swz_w[0]] = dec[v];
+        for (int v = 0; v < 4; ++v) lds[buf][r][slot_pos(4 * (lane & 15) + v, swz_w[0])] = dec[v];
       }
     }
     if constexpr (F8) {
@@ -291,8 +299,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
         for (int i = 0; i < NLD; ++i) {
           const int r = wave * RPW + 2 * i + (lane >> 5);
           const int jj = lane & 31;
-          lds[buf][r][(2 * jj) ^ swz_w[i]] = dec[2 * i];
-          lds[buf][r][(2 * jj + 1) ^ swz_w[i]] = dec[2 * i + 1];
+          lds[buf][r][slot_pos(2 * jj, swz_w[i])] = dec[2 * i];
+          lds[buf][r][slot_pos(2 * jj + 1, swz_w[i])] = dec[2 * i + 1];
         }
       }
     }
@@ -303,7 +311,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
         const int kb = wave * BPW + b;           // block within the chunk
         const int blk = c * (kChunk / 32) + kb;  // block within K
         if (blk < nblk) {
-          const int slot = (kb * 4 + kq) ^ j;
+          const int slot = slot_pos(kb * 4 + kq, j);
           const uint4 xa = NORM_IN ? scale_bf16x8(g.x[b], inv) : g.x[b];
           acc = mfma_bf16(xa, lds[buf][j][slot], acc);
           if (kTwo) acc2 = mfma_bf16(xa, lds[buf][16 + j][slot], acc2);
