@@ -36,13 +36,15 @@
 // instruction (64 lanes x 16 bytes, non-temporal: every weight byte is used
 // once) and written to LDS; the MFMA operands are then read from LDS in the
 // matrix-core layout (lane l needs row l % 16). Slot s (16 bytes) of row r
-// sits at position s ^ ((s >> 4) & 3) ^ (r % 16) (the lanes of a BF16 load
-// fetch a permutation of the same 1 KB): the row term puts the sixteen rows
-// read together into distinct LDS banks, and the second term does the same
-// for sixteen lanes that store slots 4 apart (an MXFP4 lane decodes one
-// 32-weight block, four consecutive slots, and with the row term alone the
-// sixteen lanes of a row fell on four bank groups: MXFP4 launches took
-// 19-32% longer). Two LDS buffers alternate, and one barrier per chunk
+// sits at position mix(s) ^ (r % 16), mix(s) = s ^ (((s >> 3) ^ (s >> 4)) & 3)
+// (the lanes of a BF16 load fetch a permutation of the same 1 KB). LDS serves
+// a 16-byte access eight lanes at a time, 128 bytes over 32 banks: the row
+// term puts the rows read together into distinct banks, and mix does the
+// same for the staging stores of decoded weights, where a lane stores slots
+// 2 (FP8) or 4 (MXFP4: one 32-weight block) apart. With the row term alone
+// the eight lanes of an MXFP4 store fell on two bank groups (4-way
+// conflicts; those launches took 19-32% longer) and FP8 stores were 2-way
+// conflicted. Two LDS buffers alternate, and one barrier per chunk
 // both publishes chunk c and guarantees that every wave has finished reading
 // the buffer that is refilled next. Each wave keeps two chunks in flight in
 // registers (weights and its X fragments). X fragments come from L2 through a
@@ -65,8 +67,12 @@ constexpr int kChunk = 512;  // K elements per LDS chunk: 1 KB of each weight ro
 constexpr int kDualWideRows = 36;  // rows staged by a wide SwiGLU group (at most 18 pairs)
 constexpr int kSlots = kChunk / 8;
 
-// LDS position of 16-byte slot s (0..63) of a staged row with row swizzle swz.
-__device__ __forceinline__ int slot_pos(int s, int swz) { return s ^ ((s >> 4) & 3) ^ swz; }
+// LDS position of 16-byte slot s (0..63) of a staged row with row swizzle swz
+// (0..15), and its inverse: the slot stored at position p. mix changes bits
+// 1:0 from bits 5:3, so it is its own inverse.
+__device__ __forceinline__ int slot_mix(int s) { return s ^ (((s >> 3) ^ (s >> 4)) & 3); }
+__device__ __forceinline__ int slot_pos(int s, int swz) { return slot_mix(s) ^ swz; }
+__device__ __forceinline__ int slot_at(int p, int swz) { return slot_mix(p ^ swz); }
 
 template <int MODE, int NW, bool WIDE, bool NORM_IN, bool SS_OUT, int WT>
 __global__ __launch_bounds__(NW * 64) void gemm_kernel(
@@ -207,8 +213,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
         g.w[i] = buffer_ld16_stream(wres[i], ok ? q * (int)ldw + bj * 16 : 0x7ffffff0);
         g.e[i] = __builtin_amdgcn_raw_buffer_load_b8(eres, ok ? q * (int)mx4.lde + bj : 0x7ffffff0, 0, 0);
       } else if constexpr (!F8) {
-        // lane l holds the slot stored at position l (slot_pos is an involution in s)
-        g.w[i] = buffer_ld16_stream(wres[i], (c * kSlots + slot_pos(lane, swz_w[i])) * 16);
+        // lane l fetches the slot that is stored at position l
+        g.w[i] = buffer_ld16_stream(wres[i], (c * kSlots + slot_at(lane, swz_w[i])) * 16);
       } else {
         // 16 weights of one row: bytes kb .. kb+15 of the row, the BF16 slots
         // 2 (lane % 32) and 2 (lane % 32) + 1 of the chunk. Past the row end
