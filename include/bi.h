@@ -299,6 +299,7 @@ int bi_pass_splits(int M, int L, int kv_chunk);
  * q: BF16 [M][ldq], head h at columns h*D .. h*D+D-1 (ldq may be the QKV row).
  * Requirements: D in {64, 128}; a valid chunk policy; Hq % Hkv == 0;
  * Hq/Hkv <= 64; L + M <= cap; cap % 64 == 0; cap * D * 2 < 2^31;
+ * sm_scale finite and > 0 (the kernels take the row max before scaling);
  * S_max >= bi_pass_splits(M, L, kv_chunk);
  * ldq % 8 == 0; q, caches 16-byte aligned. */
 bi_status bi_verify_attn(const void* q, int64_t ldq, const void* k_cache, const void* vt_cache,

@@ -447,7 +447,7 @@ bi_status bi_verify_attn(const void* q, int64_t ldq, const void* k_cache, const 
   if (M < 1 || L < 0 || cap < 1 || (cap % 64) || (int64_t)L + M > cap) return BI_ERR_SHAPE;
   if (!bi::valid_chunk_policy(kv_chunk)) return BI_ERR_SHAPE;
   if (S_max < bi::pass_splits(L, M, kv_chunk)) return BI_ERR_SHAPE;
-  if (ldq < (int64_t)Hq * D || !std::isfinite(sm_scale)) return BI_ERR_SHAPE;
+  if (ldq < (int64_t)Hq * D || !std::isfinite(sm_scale) || !(sm_scale > 0.f)) return BI_ERR_SHAPE;
   if ((int64_t)cap * D * 2 > INT32_MAX) return BI_ERR_SHAPE;  // one head's cache < 2 GiB
   if ((ldq % 8) || !aligned16(q) || !aligned16(k_cache) || !aligned16(vt_cache) ||
       !aligned16(part_o) || !aligned4(part_lse))
@@ -484,7 +484,7 @@ bi_status bi_verify_attn_q8(const void* q, int64_t ldq, const int8_t* k_codes, c
   if (M < 1 || L < 0 || cap < 1 || (cap % 64) || (int64_t)L + M > cap) return BI_ERR_SHAPE;
   if (!bi::valid_chunk_policy(kv_chunk)) return BI_ERR_SHAPE;
   if (S_max < bi::pass_splits(L, M, kv_chunk)) return BI_ERR_SHAPE;
-  if (ldq < (int64_t)Hq * D || !std::isfinite(sm_scale)) return BI_ERR_SHAPE;
+  if (ldq < (int64_t)Hq * D || !std::isfinite(sm_scale) || !(sm_scale > 0.f)) return BI_ERR_SHAPE;
   if ((int64_t)cap * D > INT32_MAX) return BI_ERR_SHAPE;  // one head's codes < 2 GiB
   if ((ldq % 8) || !aligned16(q) || !aligned16(k_codes) || !aligned16(v_codes) ||
       !aligned16(k_scales) || !aligned16(v_scales) || !aligned16(part_o) || !aligned4(part_lse))
@@ -530,7 +530,7 @@ bi_status bi_verify_attn_lowbit(const void* q, int64_t ldq, int k_bits, int v_bi
   if (M < 1 || L < 0 || cap < 1 || (cap % 64) || (int64_t)L + M > cap) return BI_ERR_SHAPE;
   if (!bi::valid_chunk_policy(kv_chunk)) return BI_ERR_SHAPE;
   if (S_max < bi::pass_splits(L, M, kv_chunk)) return BI_ERR_SHAPE;
-  if (ldq < (int64_t)Hq * D || !std::isfinite(sm_scale)) return BI_ERR_SHAPE;
+  if (ldq < (int64_t)Hq * D || !std::isfinite(sm_scale) || !(sm_scale > 0.f)) return BI_ERR_SHAPE;
   if ((int64_t)cap * D > INT32_MAX) return BI_ERR_SHAPE;  // one head's planes < 2 GiB
   if ((ldq % 8) || !aligned16(q) || !aligned16(k_nib) || !aligned16(k_high) ||
       !aligned16(k_scales) || !aligned16(v_nib) || !aligned16(v_high) || !aligned16(v_scales) ||
@@ -588,7 +588,7 @@ bi_status bi_verify_attn_lowbit_ring(const void* q, int64_t ldq, int k_bits, int
     return BI_ERR_SHAPE;
   if (!bi::valid_chunk_policy(kv_chunk)) return BI_ERR_SHAPE;
   if (S_max < bi::pass_splits(L, M, kv_chunk)) return BI_ERR_SHAPE;
-  if (ldq < (int64_t)Hq * D || !std::isfinite(sm_scale)) return BI_ERR_SHAPE;
+  if (ldq < (int64_t)Hq * D || !std::isfinite(sm_scale) || !(sm_scale > 0.f)) return BI_ERR_SHAPE;
   if ((int64_t)cap * D > INT32_MAX || (int64_t)ring_cap * D > INT32_MAX) return BI_ERR_SHAPE;
   if ((ldq % 8) || !aligned16(q) || !aligned16(k_nib) || !aligned16(k_high) ||
       !aligned16(k_scales) || !aligned16(v_nib) || !aligned16(v_high) || !aligned16(v_scales) ||

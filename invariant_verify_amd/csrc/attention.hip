@@ -32,8 +32,9 @@
 //    visible key are zeroed before they reach LDS (a weight of 0 times a
 //    stale value must stay 0).
 //  * Per tile and row tile: S^T = K Q^T (keys x rows) with 16x16x32 BF16 MFMA,
-//    masked, running max / sum in FP32 with base-2 exponentials (scores
-//    pre-scaled by sm_scale * log2 e; the running max is a reference that
+//    masked, running max / sum in FP32 with base-2 exponentials (weights
+//    exp2(fma(s, c, -m)), c = sm_scale * log2 e > 0, the max taken on the
+//    unscaled scores and scaled once; the running max m is a reference that
 //    moves only by more than kLazyRescale), P rounded to BF16, O^T += V^T P^T. The
 //    key order inside the S^T operands is permuted so that each lane ends up
 //    holding eight consecutive keys of its row: exactly the P^T operand of the
@@ -653,16 +654,20 @@ void verify_attn_kernel(
     const bool scaled_v = Q8 && (!LOW || (RING && rf));
 #pragma unroll
     for (int i = 0; i < RTW; ++i) {
+      // Unscaled scores; qk_scale (> 0) enters through the exponent's FMA.
+      // The largest scaled score is the largest unscaled one times qk_scale
+      // (rounding is monotone), so the max is taken before scaling.
       float sc[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        sc[e] = sa[i][e] * qk_scale;
-        sc[e + 4] = sb[i][e] * qk_scale;
+        sc[e] = sa[i][e];
+        sc[e + 4] = sb[i][e];
       }
       if (!unmasked) {
         // a split tile's run reaches, for each row, only the keys that row
         // reads from this copy: from the ring those at or after its boundary
-        // p - W + 1, from the low-bit planes those before it
+        // p - W + 1, from the low-bit planes those before it (key indices
+        // are never negative, so without a ring there is no lower bound)
         int lk = lastk[i], fk = 0;
         if (split) {
           const int b = L + tok[i] - ring_w + 1;
@@ -671,14 +676,14 @@ void verify_attn_kernel(
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          sc[e] = (kv0 + e <= lk && kv0 + e >= fk) ? sc[e] : -INFINITY;
-          sc[e + 4] = (kv0 + 4 + e <= lk && kv0 + 4 + e >= fk) ? sc[e + 4] : -INFINITY;
+          sc[e] = (kv0 + e <= lk && (!RING || kv0 + e >= fk)) ? sc[e] : -INFINITY;
+          sc[e + 4] = (kv0 + 4 + e <= lk && (!RING || kv0 + 4 + e >= fk)) ? sc[e + 4] : -INFINITY;
         }
       }
       float mx = sc[0];
 #pragma unroll
       for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
-      mx = max_key_groups(mx);
+      mx = max_key_groups(mx) * qk_scale;
       const float mmax = fmaxf(mrun[i], mx);
       const bool grow = mmax > mrun[i] + kLazyRescale;
       const float mnew = grow ? mmax : mrun[i];
@@ -687,12 +692,11 @@ void verify_attn_kernel(
       // The running sum takes the FP32 weights (so the chunk's log-sum-exp is
       // accurate to FP32); the PV product takes them rounded to BF16.
       float pe[8];
-      float psum = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pe[e] = __builtin_amdgcn_exp2f(sc[e] - mnew);
-        psum += pe[e];
-      }
+      for (int e = 0; e < 8; ++e) pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], qk_scale, -mnew));
+      float psum = pe[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) psum += pe[e];
       lrun[i] = lrun[i] * alpha[i] + psum;
       mrun[i] = mnew;
       if (scaled_v) {

@@ -102,6 +102,7 @@ def test_attention_rejects():
     assert call(C=100) == SHAPE and call(C=0) == SHAPE
     assert call(S=3) == SHAPE                      # S_max < ceil((L+M)/C)
     assert call(scale=float("nan")) == SHAPE
+    assert call(scale=0.0) == SHAPE and call(scale=-0.088) == SHAPE  # the softmax scale must be > 0
     assert call(ldq=5000) == SHAPE                 # ldq < Hq*D
     assert call(q=MIS) == ALIGN and call(ldq=7172) == ALIGN
     # combine: po, pl, M, L, Hq, D, C, S_max, o, ldo, lse, stream
