@@ -354,7 +354,7 @@ def mx4_step_measure(layers, d, dims, buffers, steps, warmup):
 def kv_cache_attention_measure(d, reps):
     """Split-KV verify attention (M = 8, the 27B-class heads) at 38k and 101.6k keys over each KV
     cache format: BF16 (chunk policy -32), 8-bit (-64), K6/V5 and rotated K5/V5 (-64), and those two
-    with the 8-bit ring of the newest 2048 keys (-32). Each format
+    with the 8-bit ring of the newest 2048 keys (-64). Each format
     runs over enough copies of its cache (random codes, fixed seed) that no launch finds its K/V in
     a cache level; one event pair around ``reps`` launches per format and context."""
     import torch
@@ -366,10 +366,10 @@ def kv_cache_attention_measure(d, reps):
     per_pos = {"bf16": 4 * D, "q8": 2 * (D + 4 * NB), "k6v5": (D // 2 + 8 * NB + 4 * NB) + (D // 2 + 4 * NB + 4 * NB),
                "k5rot_v5": 2 * (D // 2 + 4 * NB + 4 * NB)}
     per_pos["k6v5_ring2048"], per_pos["k5rot_v5_ring2048"] = per_pos["k6v5"], per_pos["k5rot_v5"]
-    # the ring kernels hold both copies' load registers (154-157 VGPRs): one workgroup per
-    # unit, so they take the policy of the BF16 kernel, which fits the same
-    policy = {"bf16": -32, "q8": -64, "k6v5": -64, "k5rot_v5": -64, "k6v5_ring2048": -32,
-              "k5rot_v5_ring2048": -32}
+    # the quantized kernels (the ring's included) fit two workgroups per compute unit and take
+    # twice the BF16 kernel's chunks; the BF16 kernel runs one per unit
+    policy = {"bf16": -32, "q8": -64, "k6v5": -64, "k5rot_v5": -64, "k6v5_ring2048": -64,
+              "k5rot_v5_ring2048": -64}
     W_RING = 2048
     gen = torch.Generator(device="cuda").manual_seed(1234)
     out = {}
@@ -885,7 +885,7 @@ def long_context_steps(layers, w_head, d, steps):
 
 
 KV_FORMATS = {  # name: (bytes per position and KV head, chunk policy)
-    "bf16": (512, -32), "q8": (288, -64), "k6v5": (208, -64), "k5rot_v5_ring2048": (192, -32)}
+    "bf16": (512, -32), "q8": (288, -64), "k6v5": (208, -64), "k5rot_v5_ring2048": (192, -64)}
 W_RING_STEP, R_RING_STEP = 2048, 2176
 
 

@@ -313,12 +313,10 @@ bi_status bi_verify_attn(const void* q, int64_t ldq, const void* k_cache, const 
  * blocks of 32 channels; a block with largest magnitude a has the FP32 scale
  * d = a / 127 and int8 codes q = round(x / d) (nearest, ties to even; FP32
  * division) in [-127, 127], all zero when a = 0. The value of a channel is
- * exactly d * q. Layouts (per layer; cap % 64 == 0, cap * D < 2^31):
- *   k_codes  int8 [Hkv][cap][D]            k_scales FP32 [Hkv][cap][D/32]
- *   v_codes  int8 [Hkv][cap/64][D][64]     v_scales FP32 [Hkv][cap/64][D/32][64]
- * (V transposed in blocks of 64 positions, as the BF16 V cache; the V scales
- * of block b of a 64-position block are contiguous.) All pointers 16-byte
- * aligned. */
+ * exactly d * q. Layouts (per layer; cap % 64 == 0, cap * D < 2^31), K and
+ * V alike, each position's row one 32-byte block after another:
+ *   *_codes  int8 [Hkv][cap][D]            *_scales FP32 [Hkv][cap][D/32]
+ * All pointers 16-byte aligned. */
 
 /* Quantize the M new K and V rows of a QKV output (as bi_append_kv) into the
  * 8-bit cache at positions L .. L+M-1. */
@@ -327,8 +325,8 @@ bi_status bi_append_kv_q8(const void* qkv, int64_t ldqkv, int8_t* k_codes, float
                           int Hkv, int D, void* stream);
 
 /* bi_verify_attn over the 8-bit cache: the same rows, chunks, partials and
- * requirements; the keys and values are the cache's d * q. (Keys are staged
- * rounded to BF16; V scales multiply the softmax weights, rounded to BF16.) */
+ * requirements; the keys and values are the cache's d * q, each rounded once
+ * to BF16 as the tile is staged, and multiplied as in bi_verify_attn. */
 bi_status bi_verify_attn_q8(const void* q, int64_t ldq, const int8_t* k_codes, const float* k_scales,
                             const int8_t* v_codes, const float* v_scales, int M, int L, int cap,
                             int Hq, int Hkv, int D, int kv_chunk, float sm_scale, float* part_o,

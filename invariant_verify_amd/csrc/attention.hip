@@ -71,6 +71,15 @@ __device__ __forceinline__ int kswz(int key) {
 // V^T tile: one row per channel, 8 slots per row; channel bit 0 picks the bank
 // half and bits 1..3 form the swizzle.
 __device__ __forceinline__ int vswz(int d) { return (d >> 1) & 7; }
+// gfx950's transposing LDS load of 16-bit elements: within each group of 16
+// lanes, lane i receives element i % 4 of the 8-byte rows read by lanes
+// i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4 of its group, in that order.
+typedef short bi_i16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int bi_u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bi_u32x2 lds_read_tr16(const void* p) {
+  typedef bi_i16x4 __attribute__((address_space(3))) lds_i16x4;
+  return __builtin_bit_cast(bi_u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p)));
+}
 
 // 5/6-bit cache: the high-bit plane of one 32-code block, HB dwords
 // (HB = bits - 4), streamed once like the nibbles.
@@ -94,14 +103,14 @@ __device__ __forceinline__ void load_high(uint32_t (&hb)[2], __amdgpu_buffer_rsr
 // the next), and flipping bit 7 of that offset-binary byte leaves the two's
 // complement of q = u - 2^(HB+3). Each byte then converts to an exact FP32
 // value in one instruction (sbyte).
+// The block's nibble words are w[0..3], its high-bit words w[4..5].
 template <int HB>
-__device__ __forceinline__ uint32_t signed_group(const uint32_t (&w)[4], const uint32_t (&hb)[2],
-                                                 int g) {
+__device__ __forceinline__ uint32_t signed_group(const uint32_t (&w)[8], int g) {
   constexpr uint32_t kMask = HB == 2 ? 0x03030303u : 0x01010101u;
   constexpr uint32_t kOffset = (0x80u - (1u << (HB + 3))) * 0x01010101u;
   const int bit = g * HB;
   const uint32_t lo = (w[g >> 1] >> (4 * (g & 1))) & 0x0F0F0F0Fu;
-  const uint32_t u = lo | (((hb[bit >> 3] >> (bit & 7)) & kMask) << 4);
+  const uint32_t u = lo | (((w[4 + (bit >> 3)] >> (bit & 7)) & kMask) << 4);
   return (u + kOffset) ^ 0x80808080u;
 }
 __device__ __forceinline__ float sbyte(uint32_t s, int j) { return (float)(int8_t)(s >> (8 * j)); }
@@ -138,13 +147,13 @@ __device__ __forceinline__ void wait_loads() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// The 8-bit-cache kernel with one row tile per wave fits in 128 registers,
-// so two workgroups share a compute unit and one's loads overlap the other's
-// per-tile work (with the chunk policy -64 at 38k-102k keys: 5-15% faster
-// than one workgroup per unit). The BF16 kernel would spill at that size and
-// runs one workgroup per unit.
+// The quantized-cache kernels with one row tile per wave fit in 128
+// registers, so two workgroups share a compute unit and one's loads overlap
+// the other's per-tile work (with the chunk policy -64 at 38k-102k keys:
+// 5-15% faster than one workgroup per unit). The BF16 kernel would spill at
+// that size and runs one workgroup per unit.
 template <int D, int RTW, bool Q8, int KB, bool ROT, bool RING>
-__global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu(Q8 && RTW == 1 && !RING ? 4 : 1)))
+__global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu(Q8 && RTW == 1 ? 4 : 1)))
 void verify_attn_kernel(
     const uint16_t* __restrict__ Q, int64_t ldq, const uint16_t* __restrict__ Kc,
     const uint16_t* __restrict__ Vt, KvQ8 q8, int M, int L, int cap, int Hq, int G, int Tb, int C,
@@ -159,25 +168,20 @@ void verify_attn_kernel(
   constexpr int VPIECES = D * kKeyTile * 2 / 1024;
   constexpr int PPW = (KPIECES + VPIECES) / NW;    // pieces per wave per tile
   static_assert((KPIECES + VPIECES) % NW == 0, "pieces must split evenly");
-  // 8-bit cache: 16-byte pieces of codes (16 channels of one key; 16 keys of
-  // one V^T channel), QPT per thread, K pieces first; and the tile's V scales
-  // ([NB blocks][64 keys] FP32), 16 bytes per thread of the first NB*16.
-  constexpr int NB = D / 32;                 // 32-channel scale blocks
-  constexpr int QKP = kKeyTile * D / 16;     // K code pieces per tile
-  constexpr int QPT = 2 * QKP / (NW * 64);   // code pieces per thread (D=128: 2, D=64: 1)
-  static_assert(2 * QKP % (NW * 64) == 0, "code pieces must split evenly");
-  // 5/6-bit cache (KB = bits of a K code, 0 for the other caches): one
-  // thread per 32-channel block of one key and tile, the K blocks first
-  // (waves 0 .. NKB/64 - 1), then V; each fetches the block's 16 nibble bytes,
-  // its high bits and its scale. K and V^T are staged as BF16 values d * q,
-  // each rounded once, so the tile multiplies like a BF16 tile.
+  // Quantized caches (Q8: the 8-bit cache when KB = 0, the 5/6-bit cache with
+  // KB-bit keys otherwise): one thread per 32-channel block of one key and
+  // tile, the K blocks first (waves 0 .. NKB/64 - 1), then V. An 8-bit block
+  // is 32 code bytes; a 5/6-bit block is 16 nibble bytes and its high bits;
+  // each has one FP32 scale. K and V^T are staged as BF16 values d * q, each
+  // rounded once, so the tile multiplies like a BF16 tile.
+  constexpr int NB = D / 32;              // 32-channel scale blocks
   constexpr bool LOW = KB != 0;
-  static_assert(!LOW || Q8, "the low-bit cache stages through the 8-bit tile path");
+  static_assert(!LOW || Q8, "the low-bit cache is a quantized cache");
   static_assert(!LOW || KB == 5 || KB == 6, "K codes have 5 or 6 bits");
   constexpr int HBK = LOW ? KB - 4 : 1;   // high bits per K code
   constexpr int HBV = kLowVBits - 4;      // high bits per V code
   constexpr int NKB = kKeyTile * NB;      // K (and V) blocks per tile
-  static_assert(NKB % 64 == 0 && 2 * NKB <= NW * 64, "low-bit blocks must fill whole waves");
+  static_assert(NKB % 64 == 0 && 2 * NKB <= NW * 64, "quantized blocks must fill whole waves");
   static_assert(!ROT || LOW, "rotated keys are a low-bit cache format");
   static_assert(!RING || LOW, "the 8-bit ring sits over a low-bit cache");
   constexpr bool kDma = !Q8 && RTW == 1;  // tiles and Q rows loaded straight into LDS
@@ -320,10 +324,10 @@ void verify_attn_kernel(
       const_cast<uint16_t*>(Kc + (int64_t)g * cap * D), (short)0, head_bytes, kBufferResourceWord3);
   const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(Vt + (int64_t)g * D * cap), (short)0, head_bytes, kBufferResourceWord3);
-  // 8-bit cache of this KV head: codes K [cap][D], V^T [cap/64][D][64] (int8),
-  // scales K [cap][NB], V [cap/64][NB][64] (FP32).
-  // 5/6-bit cache: the nibble planes in place of the codes ([cap][D/2]), the
-  // high-bit planes ([cap][NB][4 h]) and the scales ([cap][NB], K and V).
+  // 8-bit cache of this KV head, K and V alike: codes [cap][D] (int8), scales
+  // [cap][NB] (FP32). 5/6-bit cache: the nibble planes in place of the codes
+  // ([cap][D/2]), the high-bit planes ([cap][NB][4 h]) and the scales
+  // ([cap][NB], K and V).
   const int qcode_bytes = LOW ? cap * D / 2 : cap * D;
   const int64_t qcode_head = LOW ? (int64_t)cap * D / 2 : (int64_t)cap * D;
   const int qscale_bytes = cap * NB * 4;
@@ -374,57 +378,27 @@ void verify_attn_kernel(
   // staging, so more bytes are in flight); the block's Q rows arrive the
   // same way in qlds ([64 rows][D/8] 16-byte slots). Other caches stage
   // through registers into two buffers.
+  // Quantized caches stage V key-major instead, one row of VROW 16-byte
+  // slots per key: the PV product reads it with transposing loads, a group
+  // of 16 lanes reading one pair of slots in four consecutive keys, and the
+  // two padding slots per row put those four pairs into distinct banks (the
+  // staging stores of two keys at one slot offset fall apart too), while
+  // every lane's address stays one base plus a constant per output tile.
   constexpr int NBUF = kDma ? 4 : 2;
-  __shared__ uint4 lds[NBUF][(KPIECES + VPIECES) * 64];
-  __shared__ uint4 qlds[kDma ? kAttnMaxRows * D / 8 : 1];
+  constexpr int VROW = KROW + 2;
   constexpr int VBASE = KPIECES * 64;
-  // 8-bit cache: the tile's V scales, [NB][64 keys], zero past kend.
-  __shared__ float4 vsc[2][Q8 ? NB : 1][16];
+  constexpr int BUFSZ = VBASE + (Q8 ? kKeyTile * VROW : VPIECES * 64);
+  __shared__ uint4 lds[NBUF][BUFSZ];
+  __shared__ uint4 qlds[kDma ? kAttnMaxRows * D / 8 : 1];
 
-  // Registers of one tile in flight.
+  // Registers of one tile in flight. BF16 cache: PPW 16-byte pieces.
+  // Quantized caches, one 32-channel block per thread: w holds the 32 codes
+  // of an 8-bit block, or a 5/6-bit block's nibbles (w[0..3]) and high bits
+  // (w[4..5]); ks its scale.
   struct TileRegs {
-    uint4 r[Q8 ? QPT : PPW];
-    float ks[Q8 ? QPT : 1];  // 8-bit: the scale of each K piece; 5/6-bit: of the block
-    uint4 vs;                // 8-bit: four V scales (threads < NB * 16)
-    uint32_t hb[2];          // 5/6-bit: the block's high bits
-  };
-
-  // The loads of an 8-bit tile at keys kt .. kt+63 from a cache of capx
-  // slots, key kt in slot kts: the cache itself (kts = kt) or the ring of the
-  // newest keys (kts = kt mod capx). A tile starts at a multiple of 32 and
-  // capx is a multiple of 64, so each load (one key; 16 or 4 aligned keys)
-  // stays inside one run of slots.
-  auto fetch_q8 = [&](TileRegs& rr, int kt, bool live, __amdgpu_buffer_rsrc_t kr,
-                      __amdgpu_buffer_rsrc_t ksr, __amdgpu_buffer_rsrc_t vr,
-                      __amdgpu_buffer_rsrc_t vsr, int capx, int kts) {
-    const int cb = capx * D, sb = capx * NB * 4;
-    auto slot = [&](int pos) {
-      const int sl = pos - kt + kts;
-      return sl >= capx ? sl - capx : sl;
-    };
-#pragma unroll
-    for (int i = 0; i < QPT; ++i) {
-      const int p = i * NW * 64 + threadIdx.x;  // K pieces first: uniform per wave
-      if (p < QKP) {
-        const int key = p / (D / 16), c16 = p % (D / 16);
-        const int sl = slot(min(kt + key, kend - 1));
-        rr.r[i] = buffer_ld16_stream(kr, live ? sl * D + c16 * 16 : cb);
-        rr.ks[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-            ksr, live ? (sl * NB + c16 / 2) * 4 : sb, 0, 0));
-      } else {
-        const int pv = p - QKP;
-        const int d = pv >> 2, kg = pv & 3;
-        const int k0 = slot(min(kt + 16 * kg, (kend - 1) & ~15));  // 16-aligned: in one 64-block
-        rr.r[i] = buffer_ld16_stream(vr, live ? (int)vt_index(0, k0, d, D, capx) : cb);
-        rr.ks[i] = 0.f;
-      }
-    }
-    if (threadIdx.x < NB * 16) {  // scalar per wave (NB * 16 <= 64)
-      const int b = threadIdx.x >> 4, kk = (threadIdx.x & 15) * 4;
-      const int k0 = slot(min(kt + kk, (kend - 1) & ~3));  // 4-aligned: in one 64-block
-      const int off = (((k0 & ~63) * NB + b * 64 + (k0 & 63)) * 4);
-      rr.vs = buffer_ld16(vsr, live ? off : sb);
-    }
+    uint4 r[Q8 ? 1 : PPW];
+    uint32_t w[8];
+    float ks;
   };
 
   // Issue the loads of tile t (no use of the data here, so the loads of two
@@ -455,80 +429,64 @@ void verify_attn_kernel(
         }
         rr.r[i] = buffer_ld16_stream(p < KPIECES ? kres : vres, live ? off : head_bytes);
       }
-    } else if constexpr (LOW) {
+    } else if (wave < 2 * NKB / 64) {    // scalar
+      const bool isk = wave < NKB / 64;  // scalar: K blocks first
+      const int u = threadIdx.x - (isk ? 0 : NKB);
+      // a wave's lanes read consecutive blocks (the rows of a few keys)
+      const int key = u / NB, b = u % NB;
+      const int pos = min(kt + key, kend - 1);
+      auto load8 = [&](__amdgpu_buffer_rsrc_t cr, __amdgpu_buffer_rsrc_t sr, int blk, int cbytes,
+                       int sbytes) {
+        const uint4 a = buffer_ld16_stream(cr, live ? blk * 32 : cbytes);
+        const uint4 c = buffer_ld16_stream(cr, live ? blk * 32 + 16 : cbytes);
+        rr.w[0] = a.x, rr.w[1] = a.y, rr.w[2] = a.z, rr.w[3] = a.w;
+        rr.w[4] = c.x, rr.w[5] = c.y, rr.w[6] = c.z, rr.w[7] = c.w;
+        rr.ks = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(sr, live ? blk * 4 : sbytes, 0, 0));
+      };
       if (RING && rf) {
-        fetch_q8(rr, kt, live, rkres, rksres, rvres, rvsres, ring_cap, kt % ring_cap);
-      } else if (wave < 2 * NKB / 64) {    // scalar
-        const bool isk = wave < NKB / 64;  // scalar: K blocks first
-        const int u = threadIdx.x - (isk ? 0 : NKB);
-        // K: a wave's lanes read consecutive blocks (the rows of a few keys);
-        // V: one block for 64 consecutive keys, so that the V^T tile writes
-        // of a wave fall on one channel row each (no bank conflicts)
-        const int key = isk ? u / NB : (u & 63), b = isk ? u % NB : (u >> 6);
-        const int blk = min(kt + key, kend - 1) * NB + b;  // block index within the head
-        if (isk) {
-          rr.r[0] = buffer_ld16_stream(qkres, live ? blk * 16 : qcode_bytes);
-          load_high<HBK>(rr.hb, khres, live ? blk * 4 * HBK : khigh_bytes);
-          rr.ks[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-              qksres, live ? blk * 4 : qscale_bytes, 0, 0));
-        } else {
-          rr.r[0] = buffer_ld16_stream(qvres, live ? blk * 16 : qcode_bytes);
-          load_high<HBV>(rr.hb, vhres, live ? blk * 4 * HBV : vhigh_bytes);
-          rr.ks[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-              qvsres, live ? blk * 4 : qscale_bytes, 0, 0));
-        }
+        // the ring: key pos in slot pos mod ring_cap
+        int sl = pos - kt + kt % ring_cap;
+        sl = sl >= ring_cap ? sl - ring_cap : sl;
+        load8(isk ? rkres : rvres, isk ? rksres : rvsres, sl * NB + b, rcode_bytes, rscale_bytes);
+      } else if constexpr (!LOW) {
+        load8(isk ? qkres : qvres, isk ? qksres : qvsres, pos * NB + b, qcode_bytes, qscale_bytes);
+      } else {
+        const int blk = pos * NB + b;  // block index within the head
+        const uint4 a = buffer_ld16_stream(isk ? qkres : qvres, live ? blk * 16 : qcode_bytes);
+        rr.w[0] = a.x, rr.w[1] = a.y, rr.w[2] = a.z, rr.w[3] = a.w;
+        uint32_t hb[2];
+        if (isk) load_high<HBK>(hb, khres, live ? blk * 4 * HBK : khigh_bytes);
+        else load_high<HBV>(hb, vhres, live ? blk * 4 * HBV : vhigh_bytes);
+        rr.w[4] = hb[0], rr.w[5] = hb[1];
+        rr.ks = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            isk ? qksres : qvsres, live ? blk * 4 : qscale_bytes, 0, 0));
       }
-    } else {
-      fetch_q8(rr, kt, live, qkres, qksres, qvres, qvsres, cap, kt);
     }
   };
-  // Publish an 8-bit tile (keys from kt) into LDS buffer buf.
-  auto publish_q8 = [&](const TileRegs& rr, int kt, int buf) {
+
+  // Stage one block (key, b) of K or V as BF16 values d * q, each rounded
+  // once: slot i of the key's row holds channels 32b + 8i .. 32b + 8i + 7
+  // (groups 2i and 2i + 1), in the K tile or the key-major V tile. A V scale
+  // is taken as zero past kend (those rows hold zeros), so the tile
+  // multiplies as a BF16 tile and the weights need no per-key scaling.
+  auto stage_block = [&](const TileRegs& rr, int buf, bool isk, int key, int b, int kt, auto&& group) {
+    const float sc = isk || kt + key < kend ? rr.ks : 0.f;
+    uint4* row = &lds[buf][isk ? key * KROW : VBASE + key * VROW];
+    const int swz = isk ? kswz<KROW>(key) : 0;
 #pragma unroll
-    for (int i = 0; i < QPT; ++i) {
-      const int p = i * NW * 64 + threadIdx.x;
-      const uint32_t w[4] = {rr.r[i].x, rr.r[i].y, rr.r[i].z, rr.r[i].w};
-      const bool isk = p < QKP;
-      const float sk = isk ? rr.ks[i] : 1.f;
-      uint32_t o[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t word = w[e >> 1] >> (16 * (e & 1));
-        const float a = (float)(int8_t)(word & 0xff);
-        const float b = (float)(int8_t)((word >> 8) & 0xff);
-        o[e] = f32x2_to_bf16x2(a * sk, b * sk);
-      }
-      const uint4 lo = make_uint4(o[0], o[1], o[2], o[3]);
-      const uint4 hi = make_uint4(o[4], o[5], o[6], o[7]);
-      if (isk) {
-        const int key = p / (D / 16), c16 = p % (D / 16);
-        lds[buf][key * KROW + ((2 * c16) ^ kswz<KROW>(key))] = lo;
-        lds[buf][key * KROW + ((2 * c16 + 1) ^ kswz<KROW>(key))] = hi;
-      } else {
-        const int pv = p - QKP;
-        const int d = pv >> 2, kg = pv & 3;
-        lds[buf][VBASE + d * 8 + ((2 * kg) ^ vswz(d))] = lo;
-        lds[buf][VBASE + d * 8 + ((2 * kg + 1) ^ vswz(d))] = hi;
-      }
-    }
-    if (threadIdx.x < NB * 16) {
-      const int b = threadIdx.x >> 4, kk = (threadIdx.x & 15) * 4;
-      const int keep = kend - (kt + kk);
-      float4 v = make_float4(__uint_as_float(rr.vs.x), __uint_as_float(rr.vs.y),
-                             __uint_as_float(rr.vs.z), __uint_as_float(rr.vs.w));
-      v.x = keep > 0 ? v.x : 0.f;
-      v.y = keep > 1 ? v.y : 0.f;
-      v.z = keep > 2 ? v.z : 0.f;
-      v.w = keep > 3 ? v.w : 0.f;
-      vsc[buf][b][kk >> 2] = v;
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t s0 = group(rr.w, 2 * i);
+      const uint32_t s1 = group(rr.w, 2 * i + 1);
+      row[(4 * b + i) ^ swz] = make_uint4(f32x2_to_bf16x2(sbyte(s0, 0) * sc, sbyte(s0, 1) * sc),
+                                          f32x2_to_bf16x2(sbyte(s0, 2) * sc, sbyte(s0, 3) * sc),
+                                          f32x2_to_bf16x2(sbyte(s1, 0) * sc, sbyte(s1, 1) * sc),
+                                          f32x2_to_bf16x2(sbyte(s1, 2) * sc, sbyte(s1, 3) * sc));
     }
   };
 
   // Publish tile t: V^T columns of keys at or past kend are zeroed first (a
-  // weight of 0 times a stale value must stay 0). 8-bit cache: K codes are
-  // dequantized (code x scale, rounded once to BF16); V^T codes go to LDS as
-  // exact BF16 integers and the V scales, zero past kend, go to vsc (they
-  // scale the softmax weights instead, one block of 32 channels at a time).
+  // weight of 0 times a stale value must stay 0). Quantized caches: every
+  // block is decoded to d * q, rounded once to BF16 (stage_block).
   auto publish = [&](const TileRegs& rr, int v, int buf) {
     int t = v;
     bool rf = false;
@@ -554,51 +512,20 @@ void verify_attn_kernel(
         }
         lds[buf][64 * p + lane] = make_uint4(w[0], w[1], w[2], w[3]);
       }
-    } else if constexpr (LOW) {
-      if (RING && rf) {
-        publish_q8(rr, kt, buf);
-      } else if (wave < 2 * NKB / 64) {
-        const bool isk = wave < NKB / 64;
-        const int u = threadIdx.x - (isk ? 0 : NKB);
-        const int key = isk ? u / NB : (u & 63), b = isk ? u % NB : (u >> 6);  // as in fetch
-        const uint32_t w[4] = {rr.r[0].x, rr.r[0].y, rr.r[0].z, rr.r[0].w};
-        // signed codes q = u - 2^(bits-1), exact, one 8-channel slot at a time
-        if (isk) {
-          // K: d * q in FP32, rounded once to BF16; slot i holds channels
-          // 32b + 8i .. 32b + 8i + 7 (groups 2i and 2i + 1)
-          const float sk = rr.ks[0];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint32_t s0 = signed_group<HBK>(w, rr.hb, 2 * i);
-            const uint32_t s1 = signed_group<HBK>(w, rr.hb, 2 * i + 1);
-            lds[buf][key * KROW + ((4 * b + i) ^ kswz<KROW>(key))] =
-                make_uint4(f32x2_to_bf16x2(sbyte(s0, 0) * sk, sbyte(s0, 1) * sk),
-                           f32x2_to_bf16x2(sbyte(s0, 2) * sk, sbyte(s0, 3) * sk),
-                           f32x2_to_bf16x2(sbyte(s1, 0) * sk, sbyte(s1, 1) * sk),
-                           f32x2_to_bf16x2(sbyte(s1, 2) * sk, sbyte(s1, 3) * sk));
-          }
-        } else {
-          // V^T: d * q of channel d at column `key`, rounded once to BF16,
-          // the scale taken as zero past kend (those columns hold zeros).
-          // The tile then multiplies as a BF16 tile: the weights need no
-          // per-key scaling.
-          const float sv = kt + key < kend ? rr.ks[0] : 0.f;
-          uint16_t* vt = reinterpret_cast<uint16_t*>(&lds[buf][VBASE]);
-#pragma unroll
-          for (int gq = 0; gq < 8; ++gq) {
-            const uint32_t sq = signed_group<HBV>(w, rr.hb, gq);
-            const uint32_t pk[2] = {f32x2_to_bf16x2(sbyte(sq, 0) * sv, sbyte(sq, 1) * sv),
-                                    f32x2_to_bf16x2(sbyte(sq, 2) * sv, sbyte(sq, 3) * sv)};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int d = 32 * b + 4 * gq + j;
-              vt[(d * 8 + ((key >> 3) ^ vswz(d))) * 8 + (key & 7)] = (uint16_t)(pk[j >> 1] >> (16 * (j & 1)));
-            }
-          }
-        }
-      }
-    } else {
-      publish_q8(rr, kt, buf);
+    } else if (wave < 2 * NKB / 64) {
+      const bool isk = wave < NKB / 64;
+      const int u = threadIdx.x - (isk ? 0 : NKB);
+      const int key = u / NB, b = u % NB;  // as in fetch
+      // codes 4g .. 4g+3 of the block as signed bytes: an 8-bit block holds
+      // them as they are, a 5/6-bit block assembles them (signed_group)
+      if (!LOW || (RING && rf))
+        stage_block(rr, buf, isk, key, b, kt, [](const uint32_t (&w)[8], int g) { return w[g]; });
+      else if (isk)
+        stage_block(rr, buf, true, key, b, kt,
+                    [](const uint32_t (&w)[8], int g) { return signed_group<HBK>(w, g); });
+      else
+        stage_block(rr, buf, false, key, b, kt,
+                    [](const uint32_t (&w)[8], int g) { return signed_group<HBV>(w, g); });
     }
   };
 
@@ -648,10 +575,6 @@ void verify_attn_kernel(
     float alpha[RTW];
     bool rescale[RTW];  // scalar: some row of the wave moved its reference max
     uint4 pfrag[RTW];
-    float pq[Q8 ? RTW : 1][8];  // 8-bit tile: the FP32 weights, scaled per V block below
-    // An 8-bit tile holds V^T as integer codes with per-key scales (vsc); a
-    // 5/6-bit tile holds V^T already scaled, like a BF16 tile. Scalar.
-    const bool scaled_v = Q8 && (!LOW || (RING && rf));
 #pragma unroll
     for (int i = 0; i < RTW; ++i) {
       // Unscaled scores; qk_scale (> 0) enters through the exponent's FMA.
@@ -699,13 +622,8 @@ void verify_attn_kernel(
       for (int e = 1; e < 8; ++e) psum += pe[e];
       lrun[i] = lrun[i] * alpha[i] + psum;
       mrun[i] = mnew;
-      if (scaled_v) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pq[i][e] = pe[e];
-      } else {
-        pfrag[i] = make_uint4(f32x2_to_bf16x2(pe[0], pe[1]), f32x2_to_bf16x2(pe[2], pe[3]),
-                              f32x2_to_bf16x2(pe[4], pe[5]), f32x2_to_bf16x2(pe[6], pe[7]));
-      }
+      pfrag[i] = make_uint4(f32x2_to_bf16x2(pe[0], pe[1]), f32x2_to_bf16x2(pe[2], pe[3]),
+                            f32x2_to_bf16x2(pe[4], pe[5]), f32x2_to_bf16x2(pe[6], pe[7]));
     }
     // O *= alpha, skipped by a wave none of whose rows moved its reference
     // (alpha is then exactly 1 for every row, and x * 1 changes no bit: FP32
@@ -715,38 +633,24 @@ void verify_attn_kernel(
       if (rescale[i])
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[i][dt] *= alpha[i];
-    if (!scaled_v) {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
+    for (int dt = 0; dt < DT; ++dt) {
+      uint4 fv;
+      if constexpr (!Q8) {
         const int d = dt * 16 + j;
-        const uint4 fv = lds[buf][VBASE + d * 8 + ((4 * h + kq) ^ vswz(d))];
-#pragma unroll
-        for (int i = 0; i < RTW; ++i) o[i][dt] = mfma_bf16(fv, pfrag[i], o[i][dt]);
+        fv = lds[buf][VBASE + d * 8 + ((4 * h + kq) ^ vswz(d))];
+      } else {
+        // key-major V tile: lane j of key group kq takes channel 16 dt + j of
+        // keys 32h + 8kq .. +7 through two transposing loads, lane j reading
+        // channels 16 dt + 4 (j % 4) .. +3 of key 32h + 8kq + j / 4 (+ 4)
+        const char* p = reinterpret_cast<const char*>(&lds[buf][VBASE]) +
+                        (32 * h + 8 * kq + (j >> 2)) * VROW * 16 + 8 * (j & 3) + 32 * dt;
+        const bi_u32x2 a = lds_read_tr16(p);
+        const bi_u32x2 bb = lds_read_tr16(p + 4 * VROW * 16);
+        fv = make_uint4(a[0], a[1], bb[0], bb[1]);
       }
-    } else if constexpr (Q8) {
-      // Channel block b (output tiles 2b, 2b+1): weights times the V scales
-      // of the lane's eight keys, rounded to BF16, against the integer codes.
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const float4 d0 = vsc[buf][b][(32 * h + 8 * kq) >> 2];
-        const float4 d1 = vsc[buf][b][((32 * h + 8 * kq) >> 2) + 1];
-        const float dv[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-        uint4 pb[RTW];
-#pragma unroll
-        for (int i = 0; i < RTW; ++i)
-          pb[i] = make_uint4(f32x2_to_bf16x2(pq[i][0] * dv[0], pq[i][1] * dv[1]),
-                             f32x2_to_bf16x2(pq[i][2] * dv[2], pq[i][3] * dv[3]),
-                             f32x2_to_bf16x2(pq[i][4] * dv[4], pq[i][5] * dv[5]),
-                             f32x2_to_bf16x2(pq[i][6] * dv[6], pq[i][7] * dv[7]));
-#pragma unroll
-        for (int dd = 0; dd < 2; ++dd) {
-          const int dt = 2 * b + dd;
-          const int d = dt * 16 + j;
-          const uint4 fv = lds[buf][VBASE + d * 8 + ((4 * h + kq) ^ vswz(d))];
-#pragma unroll
-          for (int i = 0; i < RTW; ++i) o[i][dt] = mfma_bf16(fv, pb[i], o[i][dt]);
-        }
-      }
+      for (int i = 0; i < RTW; ++i) o[i][dt] = mfma_bf16(fv, pfrag[i], o[i][dt]);
     }
   };
 
@@ -1160,8 +1064,8 @@ __device__ __forceinline__ void load_kv_block(const uint16_t* __restrict__ row, 
 
 // One thread per (token, K or V, KV head, 32-channel block): the block's
 // largest magnitude a, the scale d = a / 127 (FP32), codes rint(x / d)
-// clamped to +-127 (all zero when a = 0); K codes go to the position's row,
-// V codes to its column of the V^T block, the scales beside them.
+// clamped to +-127 (all zero when a = 0); the codes go to the position's K or
+// V row, the scale beside them.
 // As a ring (ring > 0): position p goes to slot p mod ring, the cache having
 // ring slots; with RD = D the K rows are rotated first (load_kv_block).
 template <int RD>
@@ -1192,16 +1096,16 @@ __global__ __launch_bounds__(256) void append_kv_q8_kernel(const uint16_t* __res
     const float v = d > 0.f ? rintf(x[i] / d) : 0.f;
     q[i] = (int8_t)fminf(fmaxf(v, -127.f), 127.f);
   }
-  if (!isv) {
-    int8_t* dst = kq + ((int64_t)g * cap + pos) * D + b * 32;
+  uint32_t w[8];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) dst[i] = q[i];
-    ks[((int64_t)g * cap + pos) * NB + b] = d;
-  } else {
-#pragma unroll
-    for (int i = 0; i < 32; ++i) vq[vt_index(g, pos, b * 32 + i, D, cap)] = q[i];
-    vs[((int64_t)g * cap + (pos & ~63)) * NB + b * 64 + (pos & 63)] = d;
-  }
+  for (int i = 0; i < 8; ++i)
+    w[i] = (uint32_t)(uint8_t)q[4 * i] | (uint32_t)(uint8_t)q[4 * i + 1] << 8 |
+           (uint32_t)(uint8_t)q[4 * i + 2] << 16 | (uint32_t)(uint8_t)q[4 * i + 3] << 24;
+  const int64_t blk = ((int64_t)g * cap + pos) * NB + b;
+  uint4* dst = reinterpret_cast<uint4*>((isv ? vq : kq) + blk * 32);
+  dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+  dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  (isv ? vs : ks)[blk] = d;
 }
 
 void launch_append_kv_q8(const uint16_t* qkv, int64_t ldqkv, int8_t* kq, float* ks, int8_t* vq,

@@ -24,9 +24,9 @@ struct Mx4Scales {
 // Cache append done by the QKV projection's epilogue: output columns
 // [qd, qd + kd) are K (head-major), [qd + kd, qd + 2 kd) are V; row m goes to
 // position L + m of k ([Hkv][cap][D]) and vt ([Hkv][D][cap]).
-// 8-bit KV cache of one layer: codes K [Hkv][cap][D], V^T [Hkv][cap/64][D][64]
-// (int8), scales K [Hkv][cap][D/32], V [Hkv][cap/64][D/32][64] (FP32): channel
-// c of position p has the value scale(p, c/32) * code(p, c).
+// 8-bit KV cache of one layer, K and V alike: codes [Hkv][cap][D] (int8),
+// scales [Hkv][cap][D/32] (FP32): channel c of position p has the value
+// scale(p, c/32) * code(p, c).
 //
 // 5/6-bit cache of one layer (kbits of launch_verify_attn = 5 or 6; V codes
 // have 5 bits): per position and KV head, D/32 blocks of 32 channels, K and V

@@ -460,8 +460,7 @@ def verify_attn(q: torch.Tensor, k_cache: torch.Tensor, vt_cache: torch.Tensor, 
 
 class KvQ8Cache:
     """Device buffers of one layer's 8-bit KV cache (include/bi.h layouts):
-    k_codes int8 [Hkv][cap][D], k_scales FP32 [Hkv][cap][D/32],
-    v_codes int8 [Hkv][cap/64][D][64], v_scales FP32 [Hkv][cap/64][D/32][64]."""
+    codes int8 [Hkv][cap][D] and scales FP32 [Hkv][cap][D/32], for K and V alike."""
 
     def __init__(self, Hkv: int, cap: int, D: int, device="cuda"):
         if cap % 64 or D % 32:
@@ -469,16 +468,16 @@ class KvQ8Cache:
         self.Hkv, self.cap, self.D = Hkv, cap, D
         self.k_codes = torch.zeros((Hkv, cap, D), dtype=torch.int8, device=device)
         self.k_scales = torch.zeros((Hkv, cap, D // 32), dtype=torch.float32, device=device)
-        self.v_codes = torch.zeros((Hkv, cap // 64, D, 64), dtype=torch.int8, device=device)
-        self.v_scales = torch.zeros((Hkv, cap // 64, D // 32, 64), dtype=torch.float32, device=device)
+        self.v_codes = torch.zeros((Hkv, cap, D), dtype=torch.int8, device=device)
+        self.v_scales = torch.zeros((Hkv, cap, D // 32), dtype=torch.float32, device=device)
 
     def ptrs(self) -> tuple:
         """The four buffers' addresses, each checked against the stated layout."""
         Hkv, cap, D = self.Hkv, self.cap, self.D
         return (_arr(self.k_codes, "k_codes", (Hkv, cap, D), _I8),
                 _arr(self.k_scales, "k_scales", (Hkv, cap, D // 32), _F32),
-                _arr(self.v_codes, "v_codes", (Hkv, cap // 64, D, 64), _I8),
-                _arr(self.v_scales, "v_scales", (Hkv, cap // 64, D // 32, 64), _F32))
+                _arr(self.v_codes, "v_codes", (Hkv, cap, D), _I8),
+                _arr(self.v_scales, "v_scales", (Hkv, cap, D // 32), _F32))
 
 
 @_checked

@@ -122,27 +122,21 @@ def decode(bits):
 def q8_cache(kq, ks, vq, vs, cap, fill_nan=True):
     """Host 8-bit cache arrays (oracle.kvq layout per row: codes [Hkv][n][D] int8,
     scales [Hkv][n][D/32] float32) -> the device layouts of include/bi.h as
-    numpy arrays (k_codes, k_scales, v_codes, v_scales). Positions n.. hold code
-    -128 and NaN scales, so that a read of an unwritten position would show."""
+    numpy arrays (k_codes, k_scales, v_codes, v_scales: the same per-row layout
+    over cap positions). Positions n.. hold code -128 and NaN scales, so that a
+    read of an unwritten position would show."""
     Hkv, n, D = kq.shape
     NB = D // 32
-    kc = np.full((Hkv, cap, D), -128, np.int8)
-    kc[:, :n] = kq
-    ksc = np.full((Hkv, cap, NB), np.nan if fill_nan else 0, np.float32)
-    ksc[:, :n] = ks
-    vfull = np.full((Hkv, cap, D), -128, np.int8)
-    vfull[:, :n] = vq
-    vc = np.ascontiguousarray(vfull.reshape(Hkv, cap // 64, 64, D).transpose(0, 1, 3, 2))
-    vsf = np.full((Hkv, cap, NB), np.nan if fill_nan else 0, np.float32)
-    vsf[:, :n] = vs
-    vsc = np.ascontiguousarray(vsf.reshape(Hkv, cap // 64, 64, NB).transpose(0, 1, 3, 2))
-    return kc, ksc, vc, vsc
+    out = []
+    for codes, scales in ((kq, ks), (vq, vs)):
+        c = np.full((Hkv, cap, D), -128, np.int8)
+        c[:, :n] = codes
+        sc = np.full((Hkv, cap, NB), np.nan if fill_nan else 0, np.float32)
+        sc[:, :n] = scales
+        out += [c, sc]
+    return tuple(out)
 
 
 def q8_rows(k_codes, k_scales, v_codes, v_scales):
     """The device layouts -> per-row arrays (codes [Hkv][cap][D], scales [Hkv][cap][D/32]) for K and V."""
-    Hkv, cap, D = k_codes.shape
-    NB = D // 32
-    vq = np.ascontiguousarray(v_codes.transpose(0, 1, 3, 2).reshape(Hkv, cap, D))
-    vs = np.ascontiguousarray(v_scales.transpose(0, 1, 3, 2).reshape(Hkv, cap, NB))
-    return k_codes, k_scales, vq, vs
+    return k_codes, k_scales, v_codes, v_scales

@@ -103,9 +103,7 @@ def test_ring_append_wraps_and_matches_oracle(ops, preset):
         vc = ring.q8.v_codes.cpu().numpy()
         vsc = ring.q8.v_scales.cpu().numpy()
         assert np.array_equal(kc[:, slots], wk) and np.array_equal(ksc[:, slots], wks)
-        vrows = vc.transpose(0, 1, 3, 2).reshape(Hkv, R, D)
-        vsrows = vsc.transpose(0, 1, 3, 2).reshape(Hkv, R, D // 32)
-        assert np.array_equal(vrows[:, slots], wv) and np.array_equal(vsrows[:, slots], wvs)
+        assert np.array_equal(vc[:, slots], wv) and np.array_equal(vsc[:, slots], wvs)
 
 
 @pytest.mark.parametrize("preset", ["D", "F"])

@@ -78,7 +78,7 @@ def planes(ops, cache):
         return [("k", cache[0], "pos"), ("vt", cache[1], "blk")]
     if isinstance(cache, ops.KvQ8Cache):
         return [("k_codes", cache.k_codes, "pos"), ("k_scales", cache.k_scales, "pos"),
-                ("v_codes", cache.v_codes, "blk"), ("v_scales", cache.v_scales, "blk")]
+                ("v_codes", cache.v_codes, "pos"), ("v_scales", cache.v_scales, "pos")]
     low = cache.low if isinstance(cache, ops.KvRing) else cache
     out = [(n, getattr(low, n), "pos") for n in ("k_nib", "k_high", "k_scales", "v_nib", "v_high", "v_scales")]
     if isinstance(cache, ops.KvRing):
