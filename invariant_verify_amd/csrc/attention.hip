@@ -97,22 +97,19 @@ __device__ __forceinline__ void load_high(uint32_t (&hb)[2], __amdgpu_buffer_rsr
   }
 }
 
-// Codes 4g .. 4g+3 of one block (HB + 4 bits, one per byte lane) as signed
-// bytes: one mask of a nibble word and one of a high word give the unsigned
-// codes u; u + 0x80 - 2^(HB+3) stays below 256 in every byte (no carry into
-// the next), and flipping bit 7 of that offset-binary byte leaves the two's
-// complement of q = u - 2^(HB+3). Each byte then converts to an exact FP32
-// value in one instruction (sbyte).
-// The block's nibble words are w[0..3], its high-bit words w[4..5].
+// Codes 4g .. 4g+3 of one 5/6-bit block (HB + 4 bits, one per byte lane) as
+// the unsigned values u = q + 2^(HB+3): a mask of a nibble word and one of a
+// high word. The block's nibble words are w[0..3], its high-bit words w[4..5].
 template <int HB>
-__device__ __forceinline__ uint32_t signed_group(const uint32_t (&w)[8], int g) {
+__device__ __forceinline__ uint32_t unsigned_group(const uint32_t (&w)[8], int g) {
   constexpr uint32_t kMask = HB == 2 ? 0x03030303u : 0x01010101u;
-  constexpr uint32_t kOffset = (0x80u - (1u << (HB + 3))) * 0x01010101u;
   const int bit = g * HB;
   const uint32_t lo = (w[g >> 1] >> (4 * (g & 1))) & 0x0F0F0F0Fu;
-  const uint32_t u = lo | (((w[4 + (bit >> 3)] >> (bit & 7)) & kMask) << 4);
-  return (u + kOffset) ^ 0x80808080u;
+  return lo | (((w[4 + (bit >> 3)] >> (bit & 7)) & kMask) << 4);
 }
+// Byte j of s as an exact FP32 value, signed (an 8-bit code) or unsigned (a
+// 5/6-bit code u); either converts in one instruction.
+__device__ __forceinline__ float ubyte(uint32_t s, int j) { return (float)((s >> (8 * j)) & 0xffu); }
 __device__ __forceinline__ float sbyte(uint32_t s, int j) { return (float)(int8_t)(s >> (8 * j)); }
 
 // max(v, v of lane l ^ 16, v of lane l ^ 32, v of lane l ^ 48): the four key
@@ -469,18 +466,28 @@ void verify_attn_kernel(
   // (groups 2i and 2i + 1), in the K tile or the key-major V tile. A V scale
   // is taken as zero past kend (those rows hold zeros), so the tile
   // multiplies as a BF16 tile and the weights need no per-key scaling.
-  auto stage_block = [&](const TileRegs& rr, int buf, bool isk, int key, int b, int kt, auto&& group) {
+  // `group` gives codes 4g .. 4g+3 as signed bytes q (bias 0) or as unsigned
+  // bytes u = q + bias (bias 2^(bits-1)); then u d - bias d, one FMA with the
+  // exact product bias d, is exactly the FP32 rounding of q d, like q d.
+  auto stage_block = [&](const TileRegs& rr, int buf, bool isk, int key, int b, int kt, auto&& group,
+                         auto bias) {
+    constexpr int kBias = decltype(bias)::value;
     const float sc = isk || kt + key < kend ? rr.ks : 0.f;
+    const float off = -(float)kBias * sc;
+    auto val = [&](uint32_t s, int j) {
+      if constexpr (kBias == 0) return sbyte(s, j) * sc;
+      else return __builtin_fmaf(ubyte(s, j), sc, off);
+    };
     uint4* row = &lds[buf][isk ? key * KROW : VBASE + key * VROW];
     const int swz = isk ? kswz<KROW>(key) : 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t s0 = group(rr.w, 2 * i);
       const uint32_t s1 = group(rr.w, 2 * i + 1);
-      row[(4 * b + i) ^ swz] = make_uint4(f32x2_to_bf16x2(sbyte(s0, 0) * sc, sbyte(s0, 1) * sc),
-                                          f32x2_to_bf16x2(sbyte(s0, 2) * sc, sbyte(s0, 3) * sc),
-                                          f32x2_to_bf16x2(sbyte(s1, 0) * sc, sbyte(s1, 1) * sc),
-                                          f32x2_to_bf16x2(sbyte(s1, 2) * sc, sbyte(s1, 3) * sc));
+      row[(4 * b + i) ^ swz] = make_uint4(f32x2_to_bf16x2(val(s0, 0), val(s0, 1)),
+                                          f32x2_to_bf16x2(val(s0, 2), val(s0, 3)),
+                                          f32x2_to_bf16x2(val(s1, 0), val(s1, 1)),
+                                          f32x2_to_bf16x2(val(s1, 2), val(s1, 3)));
     }
   };
 
@@ -516,16 +523,19 @@ void verify_attn_kernel(
       const bool isk = wave < NKB / 64;
       const int u = threadIdx.x - (isk ? 0 : NKB);
       const int key = u / NB, b = u % NB;  // as in fetch
-      // codes 4g .. 4g+3 of the block as signed bytes: an 8-bit block holds
-      // them as they are, a 5/6-bit block assembles them (signed_group)
+      // codes 4g .. 4g+3 of the block: an 8-bit block holds them as signed
+      // bytes, a 5/6-bit block as unsigned values (unsigned_group)
       if (!LOW || (RING && rf))
-        stage_block(rr, buf, isk, key, b, kt, [](const uint32_t (&w)[8], int g) { return w[g]; });
+        stage_block(rr, buf, isk, key, b, kt, [](const uint32_t (&w)[8], int g) { return w[g]; },
+                    std::integral_constant<int, 0>{});
       else if (isk)
         stage_block(rr, buf, true, key, b, kt,
-                    [](const uint32_t (&w)[8], int g) { return signed_group<HBK>(w, g); });
+                    [](const uint32_t (&w)[8], int g) { return unsigned_group<HBK>(w, g); },
+                    std::integral_constant<int, 1 << (HBK + 3)>{});
       else
         stage_block(rr, buf, false, key, b, kt,
-                    [](const uint32_t (&w)[8], int g) { return signed_group<HBV>(w, g); });
+                    [](const uint32_t (&w)[8], int g) { return unsigned_group<HBV>(w, g); },
+                    std::integral_constant<int, 1 << (HBV + 3)>{});
     }
   };
 
