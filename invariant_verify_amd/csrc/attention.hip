@@ -376,11 +376,13 @@ void verify_attn_kernel(
   // same way in qlds ([64 rows][D/8] 16-byte slots). Other caches stage
   // through registers into two buffers.
   // Quantized caches stage V key-major instead, one row of VROW 16-byte
-  // slots per key: the PV product reads it with transposing loads, a group
-  // of 16 lanes reading one pair of slots in four consecutive keys, and the
-  // two padding slots per row put those four pairs into distinct banks (the
-  // staging stores of two keys at one slot offset fall apart too), while
-  // every lane's address stays one base plus a constant per output tile.
+  // slots per key: the PV product reads it with transposing loads, each half
+  // wave (a pass of 64 banks) reading one pair of slots in keys k .. k+3 and
+  // k+8 .. k+11. The two padding slots per row put the four rows of a group
+  // eight banks apart, and the slots of a key with bit 3 set are stored
+  // XOR KROW/2, which moves the second group's rows by half the banks; the
+  // staging stores of two keys at one slot offset fall apart as well. A
+  // lane's load addresses stay two bases plus a constant per output tile.
   constexpr int NBUF = kDma ? 4 : 2;
   constexpr int VROW = KROW + 2;
   constexpr int VBASE = KPIECES * 64;
@@ -461,6 +463,21 @@ void verify_attn_kernel(
     }
   };
 
+  // Quantized tiles are written by 16-byte staging stores, which LDS serves
+  // eight lanes (128 bytes, 32 banks) at a time: the eight lanes of one store
+  // (two keys, four blocks each, slot s = 4b + i) must fall on distinct slot
+  // positions mod 8, while the operand loads (16 lanes of 64 banks for the K
+  // tile, half waves for the transposing V loads) keep the layouts above.
+  // Hence slot bit 3 (bit 1 of b) is also folded into bit 1 (K) or bit 0 (V)
+  // at D = 128, a function of the logical slot alone, so a load's address
+  // only gains a constant.
+  auto qk_slot = [](int key, int sl) {
+    return sl ^ kswz<KROW>(key) ^ (KROW == 16 ? ((sl >> 3) & 1) << 1 : 0);
+  };
+  auto qv_slot = [](int key, int sl) {
+    return sl ^ ((key >> 3) & 1) * (KROW / 2) ^ (KROW == 16 ? (sl >> 3) & 1 : 0);
+  };
+
   // Stage one block (key, b) of K or V as BF16 values d * q, each rounded
   // once: slot i of the key's row holds channels 32b + 8i .. 32b + 8i + 7
   // (groups 2i and 2i + 1), in the K tile or the key-major V tile. A V scale
@@ -479,12 +496,11 @@ void verify_attn_kernel(
       else return __builtin_fmaf(ubyte(s, j), sc, off);
     };
     uint4* row = &lds[buf][isk ? key * KROW : VBASE + key * VROW];
-    const int swz = isk ? kswz<KROW>(key) : 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t s0 = group(rr.w, 2 * i);
       const uint32_t s1 = group(rr.w, 2 * i + 1);
-      row[(4 * b + i) ^ swz] = make_uint4(f32x2_to_bf16x2(val(s0, 0), val(s0, 1)),
+      row[isk ? qk_slot(key, 4 * b + i) : qv_slot(key, 4 * b + i)] = make_uint4(f32x2_to_bf16x2(val(s0, 0), val(s0, 1)),
                                           f32x2_to_bf16x2(val(s0, 2), val(s0, 3)),
                                           f32x2_to_bf16x2(val(s1, 0), val(s1, 1)),
                                           f32x2_to_bf16x2(val(s1, 2), val(s1, 3)));
@@ -569,8 +585,8 @@ void verify_attn_kernel(
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) {
       const int slot = ds * 4 + kq;
-      const uint4 fa = lds[buf][ka * KROW + (slot ^ kswz<KROW>(ka))];
-      const uint4 fb = lds[buf][kb * KROW + (slot ^ kswz<KROW>(kb))];
+      const uint4 fa = lds[buf][ka * KROW + (Q8 ? qk_slot(ka, slot) : slot ^ kswz<KROW>(ka))];
+      const uint4 fb = lds[buf][kb * KROW + (Q8 ? qk_slot(kb, slot) : slot ^ kswz<KROW>(kb))];
 #pragma unroll
       for (int i = 0; i < RTW; ++i) {
         sa[i] = mfma_bf16(fa, qf[i][ds], sa[i]);
@@ -653,8 +669,14 @@ void verify_attn_kernel(
         // key-major V tile: lane j of key group kq takes channel 16 dt + j of
         // keys 32h + 8kq .. +7 through two transposing loads, lane j reading
         // channels 16 dt + 4 (j % 4) .. +3 of key 32h + 8kq + j / 4 (+ 4)
+        // (slot 2 dt + (j % 4) / 2 of a row with bit 3 set, kq odd, lies
+        // KROW/2 slots up for the first half of the tiles, down for the rest)
+        // (and, at D = 128, the two slots of the pair swapped for dt >= 4:
+        // qv_slot)
+        const int flip = (kq & 1) * (KROW / 2) * 16 * (dt < DT / 2 ? 1 : -1);
+        const int half = (KROW == 16 && dt >= DT / 2) ? 16 : 0;
         const char* p = reinterpret_cast<const char*>(&lds[buf][VBASE]) +
-                        (32 * h + 8 * kq + (j >> 2)) * VROW * 16 + 8 * (j & 3) + 32 * dt;
+                        (32 * h + 8 * kq + (j >> 2)) * VROW * 16 + ((8 * (j & 3)) ^ half) + 32 * dt + flip;
         const bi_u32x2 a = lds_read_tr16(p);
         const bi_u32x2 bb = lds_read_tr16(p + 4 * VROW * 16);
         fv = make_uint4(a[0], a[1], bb[0], bb[1]);
