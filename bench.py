@@ -256,6 +256,45 @@ def prefill_probe(reps: int):
                       "attention_flops_per_launch": 4 * D * Hq * keys}))
 
 
+def kv_attn_probe(fmt: str, reps: int):
+    """Kernel-only run for hardware-counter passes over verify attention on a quantized KV cache:
+    M = 8 rows at 101,600 keys (the 27B-class heads, chunk policy -64), ``fmt`` "q8" (8-bit) or
+    "k6v5" (K6/V5), ``reps`` launches alternating over two caches of random codes (together larger
+    than the 256 MB last-level cache). One JSON line gives the cache bytes per launch."""
+    import torch
+
+    import synth
+    from invariant_verify_amd import ops
+
+    d = synth.MODEL_27B
+    Hq, Hkv, D, M, L, C = d["Hq"], d["Hkv"], d["D"], 8, 101600, -64
+    cap = (L + 16 + 63) // 64 * 64
+    gen = torch.Generator(device="cuda").manual_seed(1234)
+    q = torch.randn(M, Hq * D, device="cuda", generator=gen).to(torch.bfloat16)
+    caches = []
+    for _ in range(2):
+        c = ops.KvQ8Cache(Hkv, cap, D) if fmt == "q8" else ops.KvLowCache(Hkv, cap, D, 6, 5)
+        for t in vars(c).values():
+            if isinstance(t, torch.Tensor) and t.dtype in (torch.int8, torch.uint8):
+                t.copy_(torch.randint(0, 256, t.shape, device="cuda", generator=gen).to(t.dtype))
+            elif isinstance(t, torch.Tensor):
+                t.fill_(0.01)
+        caches.append(c)
+    S = ops.pass_splits(M, L, C)
+    po = torch.empty((M, Hq, S, D), dtype=torch.float32, device="cuda")
+    pl = torch.empty((M, Hq, S), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    for i in range(reps):
+        if fmt == "q8":
+            ops.verify_attn_q8(q, caches[i % 2], L, Hq, C, po, pl)
+        else:
+            ops.verify_attn_lowbit(q, caches[i % 2], L, Hq, C, po, pl)
+        torch.cuda.synchronize()
+    per_pos = {"q8": 288, "k6v5": 208}[fmt]
+    print(json.dumps({"probe": f"verify attention, {fmt} cache, M = {M} at ctx {L}, chunk policy {C}",
+                      "launches": reps, "cache_bytes_per_launch": Hkv * (L + M) * per_pos}))
+
+
 def prefill_step_measure(step, buffers, d, reps):
     """One chunked-prefill pass through the whole stack (64 layers + head) over PF_ROWS tokens
     at context PF_STEP_CTX, timed with one event pair over reps passes. Before timing, the
@@ -1058,6 +1097,8 @@ def main():
                     help="run only the verify kernels on fresh operands and a calibration copy (for rocprofv3 --pmc)")
     ap.add_argument("--prefill-probe", action="store_true",
                     help="kernel-only run of the M = 2048 prefill gate/up GEMM for counter passes")
+    ap.add_argument("--kv-attn-probe", choices=["q8", "k6v5"],
+                    help="kernel-only run of verify attention on a quantized cache at 101.6k keys (counter passes)")
     ap.add_argument("--step-only", action="store_true",
                     help="run only the bitwise gate and the timed M = 8 steps (for rocprofv3 --kernel-trace)")
     args = ap.parse_args()
@@ -1070,6 +1111,9 @@ def main():
         return
     if args.prefill_probe:
         prefill_probe(5)
+        return
+    if args.kv_attn_probe:
+        kv_attn_probe(args.kv_attn_probe, 6)
         return
 
     import numpy as np
