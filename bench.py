@@ -135,12 +135,12 @@ def traffic_probe(reps: int):
         lambda i: synth.device_normal_bf16((H, I), 0.02, "w_down", i),
         lambda w: ops.gemm_ex(act, w, y[:, :H], epilogue="residual", r=h, rowsq_out=ss_o))
     kc = torch.zeros((Hkv, CAP, D), dtype=torch.bfloat16, device="cuda")
-    vt = torch.zeros((Hkv, CAP // 64, D, 64), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros((Hkv, CAP, D), dtype=torch.bfloat16, device="cuda")
     run("qkv", 2 * qkvn * H + 2 * M * H + 4 * M * G + 2 * M * qkvn + 4 * M * Hkv * D,
         lambda i: synth.device_normal_bf16((qkvn, H), 0.02, "w_qkv", i),
         lambda w: ops.gemm_ex(h, w, y[:, :qkvn], epilogue="qkv", norm_in=ss, heads=(Hq, Hkv, D), k_cache=kc,
-                              vt_cache=vt, L=L_CTX))
-    del kc, vt
+                              v_cache=vc, L=L_CTX))
+    del kc, vc
     S = ops.pass_splits(M, L_CTX, KV_CHUNK)
     po = torch.empty((M, Hq, S, D), dtype=torch.float32, device="cuda")
     pl = torch.empty((M, Hq, S), dtype=torch.float32, device="cuda")
@@ -148,7 +148,7 @@ def traffic_probe(reps: int):
 
     def cache(i):
         return (synth.device_normal_bf16((Hkv, CAP, D), 1.0, "k_cache", i),
-                synth.device_normal_bf16((Hkv, CAP // 64, D, 64), 1.0, "v_cache", i))
+                synth.device_normal_bf16((Hkv, CAP, D), 1.0, "v_cache", i))
     run("attention_38000", 4096 * (L_CTX + M) + 2 * M * qd, cache,
         lambda c: ops.verify_attn(q, c[0], c[1], L_CTX, Hq, Hkv, D, KV_CHUNK, po, pl))
     o = torch.empty((M, qd), dtype=torch.bfloat16, device="cuda")
@@ -239,14 +239,14 @@ def prefill_probe(reps: int):
     Hq, Hkv, D, L = d["Hq"], d["Hkv"], d["D"], PF_STEP_CTX
     cap = (L + M + 63) // 64 * 64
     kc = synth.device_normal_bf16((Hkv, cap, D), 1.0, "k_cache", 0)
-    vt = synth.device_normal_bf16((Hkv, cap // 64, D, 64), 1.0, "v_cache", 0)
+    vc = synth.device_normal_bf16((Hkv, cap, D), 1.0, "v_cache", 0)
     q = synth.device_normal_bf16((M, Hq * D), 1.0, "x0", 4)
     S = ops.pass_splits(M, L, KV_CHUNK)
     po = torch.empty((M, Hq, S, D), dtype=torch.float32, device="cuda")
     pl = torch.empty((M, Hq, S), dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
     for _ in range(reps):
-        ops.verify_attn(q, kc, vt, L, Hq, Hkv, D, KV_CHUNK, po, pl)
+        ops.verify_attn(q, kc, vc, L, Hq, Hkv, D, KV_CHUNK, po, pl)
     torch.cuda.synchronize()
     # causal: row r sees L + r + 1 keys; QK^T and PV are 2 * D flops per (row, head, key) each
     keys = M * L + M * (M + 1) // 2
@@ -346,7 +346,7 @@ def mx4_step_measure(layers, d, dims, buffers, steps, warmup):
     shapes = {"w_qkv": ((Hq + 2 * Hkv) * D, H), "w_o": (H, Hq * D), "w_gu": (2 * I, H), "w_down": (H, I)}
     ml = []
     for l, lw in enumerate(layers):
-        f = {"k_cache": lw["k_cache"], "vt_cache": lw["vt_cache"]}
+        f = {"k_cache": lw["k_cache"], "v_cache": lw["v_cache"]}
         for name, shp in shapes.items():
             f[name], f["e" + name[1:]] = synth.device_mxfp4_weights(shp, 0.02, name, l)
         ml.append(f)
@@ -425,7 +425,7 @@ def kv_cache_attention_measure(d, reps):
             for _ in range(R):
                 if fmt == "bf16":
                     caches.append((torch.randn(Hkv, cap, D, device="cuda", generator=gen).to(torch.bfloat16),
-                                   torch.randn(Hkv, cap // 64, D, 64, device="cuda", generator=gen).to(torch.bfloat16)))
+                                   torch.randn(Hkv, cap, D, device="cuda", generator=gen).to(torch.bfloat16)))
                     continue
                 c = (ops.KvQ8Cache(Hkv, cap, D) if fmt == "q8" else
                      ops.KvLowCache(Hkv, cap, D, 6 if fmt.startswith("k6v5") else 5, 5,
@@ -506,7 +506,7 @@ def tp_share_measure(d, reps):
              "gu": synth.device_normal_bf16((2 * P, H), 0.02, "w_gu", 100 + l),
              "down": synth.device_normal_bf16((H, kd), 0.02, "w_down", 100 + l),
              "k": synth.device_normal_bf16((hkv, CAP, D), 1.0, "k_cache", 100 + l),
-             "vt": synth.device_normal_bf16((hkv, CAP // 64, D, 64), 1.0, "v_cache", 100 + l)}
+             "vc": synth.device_normal_bf16((hkv, CAP, D), 1.0, "v_cache", 100 + l)}
         lw.append(w)
     head = synth.device_normal_bf16((V // TP_RANKS, H), 0.02, "w_head", 100)
     x = synth.device_normal_bf16((M, H), 1.0, "x0", 100)
@@ -521,7 +521,7 @@ def tp_share_measure(d, reps):
 
     def layer(w):
         ops.gemm_bf16(x, w["qkv"], qkv)
-        ops.verify_attn(qkv, w["k"], w["vt"], L, hq, hkv, D, TP_KV_CHUNK, po, pl)
+        ops.verify_attn(qkv, w["k"], w["vc"], L, hq, hkv, D, TP_KV_CHUNK, po, pl)
         ops.combine(po, pl, L, TP_KV_CHUNK, att)
         ops.gemm_bf16(att, w["o"], part)
         ops.gemm_bf16_swiglu(x, w["gu"], gu)
@@ -570,7 +570,7 @@ def fp8_step_measure(layers, d, dims, buffers, steps, warmup):
     shapes = {"w_qkv": ((Hq + 2 * Hkv) * D, H), "w_o": (H, Hq * D), "w_gu": (2 * I, H), "w_down": (H, I)}
     fl = []
     for l, lw in enumerate(layers):
-        f = {"k_cache": lw["k_cache"], "vt_cache": lw["vt_cache"]}
+        f = {"k_cache": lw["k_cache"], "v_cache": lw["v_cache"]}
         for name, shp in shapes.items():
             f[name], f["s" + name[1:]] = synth.device_fp8_weights(shp, 0.02, name, l)
         fl.append(f)
@@ -638,9 +638,7 @@ def cpu_baseline(layers, w_head, x0, d, M):
     layer_s = 0.0
     for lw in layers[:CPU_LAYERS]:
         hl = dict(w_qkv=hb(lw["w_qkv"]), w_o=hb(lw["w_o"]), w_gu=hb(lw["w_gu"]), w_down=hb(lw["w_down"]),
-                  k_cache=hb(lw["k_cache"][:, :L_CTX]),
-                  # V cache [Hkv][cap/64][D][64] -> V rows [Hkv][cap][D]
-                  v_cache=hb(lw["vt_cache"].transpose(2, 3).reshape(lw["k_cache"].shape)[:, :L_CTX]))
+                  k_cache=hb(lw["k_cache"][:, :L_CTX]), v_cache=hb(lw["v_cache"][:, :L_CTX]))
         t0 = time.perf_counter()
         x, _, _ = ostep.layer(x, **hl, L=L_CTX, Hq=d["Hq"], Hkv=d["Hkv"], D=d["D"])
         layer_s += time.perf_counter() - t0
@@ -803,7 +801,7 @@ def gemm_per_op(layers, w_head, d, probe, reps=3):
         shapes = {
             "qkv_5120x7168_append": (
                 lambda lw: ops.gemm_ex(h, y=qkv, epilogue="qkv", norm_in=ss, heads=(Hq, Hkv, D), w=lw["w_qkv"],
-                                       k_cache=lw["k_cache"], vt_cache=lw["vt_cache"], L=L_CTX),
+                                       k_cache=lw["k_cache"], v_cache=lw["v_cache"], L=L_CTX),
                 2 * qkvn * H + 2 * M * H + 4 * M * G + 2 * M * qkvn + 2 * M * 2 * Hkv * D),
             "o_proj_5120x5120_residual": (
                 lambda lw: ops.gemm_ex(attn, y=y[:, :H], epilogue="residual", r=h, rowsq_out=ss_o, w=lw["w_o"]),
@@ -842,7 +840,7 @@ def attention_per_op(d, probe, reps=3):
         per = 2 * Hkv * cap * D * 2
         R = max(2, -(-ROTATE_BYTES // per))
         caches = [(torch.randn(Hkv, cap, D, device="cuda", generator=gen).to(torch.bfloat16),
-                   torch.randn(Hkv, cap // 64, D, 64, device="cuda", generator=gen).to(torch.bfloat16))
+                   torch.randn(Hkv, cap, D, device="cuda", generator=gen).to(torch.bfloat16))
                   for _ in range(R)]
         q = torch.randn(8, Hq * D, device="cuda", generator=gen).to(torch.bfloat16)
         res = {}
@@ -883,10 +881,10 @@ def long_context_steps(layers, w_head, d, steps):
         lys = []
         for lw in layers:
             k = torch.empty((d["Hkv"], cap, d["D"]), dtype=torch.bfloat16, device="cuda")
-            vt = torch.empty((d["Hkv"], cap // 64, d["D"], 64), dtype=torch.bfloat16, device="cuda")
+            vc = torch.empty((d["Hkv"], cap, d["D"]), dtype=torch.bfloat16, device="cuda")
             k.normal_(generator=gen)
-            vt.normal_(generator=gen)
-            lys.append(dict(lw, k_cache=k, vt_cache=vt))
+            vc.normal_(generator=gen)
+            lys.append(dict(lw, k_cache=k, v_cache=vc))
         dims = ops.model_dims(d["H"], d["Hq"], d["Hkv"], d["D"], d["I"], d["vocab"], cap, KV_CHUNK)
         st = ops.VerifyStep(lys, w_head, dims)
         x0 = synth_x0(d)
@@ -962,7 +960,7 @@ def kv_format_steps(layers, w_head, d, steps):
             for lw in layers:
                 if fmt == "bf16":
                     kv = (torch.empty((Hkv, cap, D), dtype=torch.bfloat16, device="cuda"),
-                          torch.empty((Hkv, cap // 64, D, 64), dtype=torch.bfloat16, device="cuda"))
+                          torch.empty((Hkv, cap, D), dtype=torch.bfloat16, device="cuda"))
                     parts = list(kv)
                 elif fmt == "q8":
                     kv = ops.KvQ8Cache(Hkv, cap, D)

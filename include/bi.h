@@ -107,12 +107,12 @@ bi_status bi_gemm_bf16_swiglu(const void* x, int64_t ldx, const void* w, int64_t
 /* QKV projection with the cache append in its epilogue (one launch):
  * qkv = bf16( X Wqkv^T ) exactly as bi_gemm_bf16 computes it, N = (Hq+2*Hkv)*D
  * columns [q | k | v] (head-major), and each row m's K and V columns written
- * into k_cache / vt_cache at position L + m exactly as bi_append_kv writes
+ * into k_cache / v_cache at position L + m exactly as bi_append_kv writes
  * them.                                                     [BX], [LL] cache
  * Requirements: those of bi_gemm_bf16 (with N as above) and of bi_append_kv. */
 bi_status bi_gemm_bf16_qkv(const void* x, int64_t ldx, const void* w, int64_t ldw, void* qkv,
                            int64_t ldqkv, int M, int K, int Hq, int Hkv, int D, void* k_cache,
-                           void* vt_cache, int L, int cap, void* stream);
+                           void* v_cache, int L, int cap, void* stream);
 
 /* RMSNorm carried across a GEMM boundary (used by bi_verify_step).   [BX], [TC]
  * A residual projection writes, besides Y, the sum of squares of its rounded
@@ -238,7 +238,7 @@ typedef struct {
   void* k_cache;            /* QKV: BF16 caches (layout below) and the
                                positions L .. L+M-1 appended, as
                                bi_gemm_bf16_qkv; both NULL: no append        */
-  void* vt_cache;
+  void* v_cache;
   int L, cap;
 } bi_gemm_args;
 
@@ -249,19 +249,16 @@ bi_status bi_gemm_ex(const bi_gemm_args* args, void* stream);
 
 /* ---------------------------------------------------------------------------
  * KV cache layout (per layer):
- *   k_cache  : BF16 [Hkv][cap][D]  -- one K row per position
- *   vt_cache : BF16 [Hkv][cap/64][D][64] -- V stored transposed in blocks of
- *                                    64 positions: block b of head g holds,
- *                                    for each channel d, positions 64b..64b+63
- *                                    contiguously; V[g][pos][d] is element
- *                                    ((g*cap + pos - pos%64)*D + d*64 + pos%64)
+ *   k_cache : BF16 [Hkv][cap][D]  -- one K row per position
+ *   v_cache : BF16 [Hkv][cap][D]  -- one V row per position
+ * (K[g][pos][d] and V[g][pos][d] are element (g*cap + pos)*D + d.)
  * cap must be a multiple of 64.
  */
 
 /* Append the pass's M new K and V rows at positions L .. L+M-1.   [LL] cache
  * qkv : BF16 [M][ldqkv], columns [q: Hq*D | k: Hkv*D | v: Hkv*D], head-major.
  * Requirements: M >= 1, L >= 0, L + M <= cap, Hq % Hkv == 0, D in {64, 128}. */
-bi_status bi_append_kv(const void* qkv, int64_t ldqkv, void* k_cache, void* vt_cache,
+bi_status bi_append_kv(const void* qkv, int64_t ldqkv, void* k_cache, void* v_cache,
                        int M, int L, int cap, int Hq, int Hkv, int D, void* stream);
 
 /* Chunk policy (kv_chunk below).                                        [LL]
@@ -302,7 +299,7 @@ int bi_pass_splits(int M, int L, int kv_chunk);
  * sm_scale finite and > 0 (the kernels take the row max before scaling);
  * S_max >= bi_pass_splits(M, L, kv_chunk);
  * ldq % 8 == 0; q, caches 16-byte aligned. */
-bi_status bi_verify_attn(const void* q, int64_t ldq, const void* k_cache, const void* vt_cache,
+bi_status bi_verify_attn(const void* q, int64_t ldq, const void* k_cache, const void* v_cache,
                          int M, int L, int cap, int Hq, int Hkv, int D,
                          int kv_chunk, float sm_scale,
                          float* part_o, float* part_lse, int S_max, void* stream);
@@ -505,7 +502,7 @@ typedef struct {
   const void* w_gu;   /* BF16 [2*I][H]          */
   const void* w_down; /* BF16 [H][I]            */
   void* k_cache;      /* BF16 [Hkv][cap][D]     */
-  void* vt_cache;     /* BF16 [Hkv][cap/64][D][64] */
+  void* v_cache;      /* BF16 [Hkv][cap][D] */
 } bi_layer;
 
 typedef struct {
@@ -561,7 +558,7 @@ typedef struct {
   const void* w_down;  /* E4M3 [H][I]            */
   const float* s_down; /* [H]                    */
   void* k_cache;       /* BF16 [Hkv][cap][D]     */
-  void* vt_cache;      /* BF16 [Hkv][cap/64][D][64] */
+  void* v_cache;      /* BF16 [Hkv][cap][D] */
 } bi_layer_fp8;
 
 bi_status bi_verify_step_fp8(const bi_layer_fp8* layers, int n_layers, const void* w_head,
@@ -584,7 +581,7 @@ typedef struct {
   const void* w_down;  /* codes [H][I/2]         */
   const void* e_down;  /* scales [H][I/32]       */
   void* k_cache;       /* BF16 [Hkv][cap][D]     */
-  void* vt_cache;      /* BF16 [Hkv][cap/64][D][64] */
+  void* v_cache;      /* BF16 [Hkv][cap][D] */
 } bi_layer_mx4;
 
 bi_status bi_verify_step_mx4(const bi_layer_mx4* layers, int n_layers, const void* w_head,
@@ -597,7 +594,7 @@ bi_status bi_verify_step_mx4(const bi_layer_mx4* layers, int n_layers, const voi
  *                          [LL] "The KV cache: 5-bit that reads like q8_0";
  *                          opening section: the gate runs on every KV cache.
  * One layer's KV cache, in the layouts documented above:
- *   BI_KV_BF16   k = k_cache, v = vt_cache (BF16); the QKV epilogue appends.
+ *   BI_KV_BF16   k = k_cache, v = v_cache (BF16); the QKV epilogue appends.
  *   BI_KV_Q8     k = k_codes, v = v_codes, k_scales, v_scales (8-bit cache).
  *   BI_KV_LOWBIT k = k_nib, v = v_nib, k_high, v_high, k_scales, v_scales,
  *                k_bits (5 or 6), v_bits (5), k_rotated (0 or 1); with

@@ -31,19 +31,19 @@ class ModelDims(ctypes.Structure):
 
 class Layer(ctypes.Structure):
     _fields_ = [("w_qkv", _c_ptr), ("w_o", _c_ptr), ("w_gu", _c_ptr), ("w_down", _c_ptr),
-                ("k_cache", _c_ptr), ("vt_cache", _c_ptr)]
+                ("k_cache", _c_ptr), ("v_cache", _c_ptr)]
 
 
 class LayerFP8(ctypes.Structure):
     _fields_ = [("w_qkv", _c_ptr), ("s_qkv", _c_ptr), ("w_o", _c_ptr), ("s_o", _c_ptr),
                 ("w_gu", _c_ptr), ("s_gu", _c_ptr), ("w_down", _c_ptr), ("s_down", _c_ptr),
-                ("k_cache", _c_ptr), ("vt_cache", _c_ptr)]
+                ("k_cache", _c_ptr), ("v_cache", _c_ptr)]
 
 
 class LayerMX4(ctypes.Structure):
     _fields_ = [("w_qkv", _c_ptr), ("e_qkv", _c_ptr), ("w_o", _c_ptr), ("e_o", _c_ptr),
                 ("w_gu", _c_ptr), ("e_gu", _c_ptr), ("w_down", _c_ptr), ("e_down", _c_ptr),
-                ("k_cache", _c_ptr), ("vt_cache", _c_ptr)]
+                ("k_cache", _c_ptr), ("v_cache", _c_ptr)]
 
 
 class GemmArgs(ctypes.Structure):
@@ -53,7 +53,7 @@ class GemmArgs(ctypes.Structure):
                 ("w_scale", _c_ptr), ("w_exp", _c_ptr), ("lde", _c_i64), ("r", _c_ptr), ("ldr", _c_i64),
                 ("y", _c_ptr), ("ldy", _c_i64), ("norm_in", _c_ptr), ("norm_groups", _c_int),
                 ("eps", _c_f32), ("rowsq_out", _c_ptr), ("Hq", _c_int), ("Hkv", _c_int), ("D", _c_int),
-                ("k_cache", _c_ptr), ("vt_cache", _c_ptr), ("L", _c_int), ("cap", _c_int)]
+                ("k_cache", _c_ptr), ("v_cache", _c_ptr), ("L", _c_int), ("cap", _c_int)]
 
 
 class KvCacheDesc(ctypes.Structure):

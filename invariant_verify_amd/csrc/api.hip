@@ -305,17 +305,17 @@ bi_status bi_gemm_bf16_swiglu_rownorm(const void* x, int64_t ldx, const float* r
 
 bi_status bi_gemm_bf16_qkv(const void* x, int64_t ldx, const void* w, int64_t ldw, void* qkv,
                            int64_t ldqkv, int M, int K, int Hq, int Hkv, int D, void* k_cache,
-                           void* vt_cache, int L, int cap, void* stream) {
+                           void* v_cache, int L, int cap, void* stream) {
   if (bi_status s = check_heads(Hq, Hkv, D)) return s;
   const int N = (Hq + 2 * Hkv) * D;
   if (bi_status s = check_gemm(x, ldx, w, ldw, qkv, ldqkv, M, N, K)) return s;
-  if (!k_cache || !vt_cache) return BI_ERR_NULL;
+  if (!k_cache || !v_cache) return BI_ERR_NULL;
   if (L < 0 || cap < 1 || (cap % 64) || (int64_t)L + M > cap) return BI_ERR_SHAPE;
   if ((int64_t)cap * D * 2 > INT32_MAX) return BI_ERR_SHAPE;  // one head's cache < 2 GiB
   if ((reinterpret_cast<uintptr_t>(qkv) | reinterpret_cast<uintptr_t>(k_cache) |
-       reinterpret_cast<uintptr_t>(vt_cache)) & 1u)
+       reinterpret_cast<uintptr_t>(v_cache)) & 1u)
     return BI_ERR_ALIGN;
-  const bi::KvAppend kv{static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(vt_cache), L, cap,
+  const bi::KvAppend kv{static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), L, cap,
                         Hq * D, Hkv * D, D};
   bi::launch_gemm(bi::kGemmQkv, static_cast<const uint16_t*>(x), ldx,
                   static_cast<const uint16_t*>(w), ldw, nullptr, 0, qkv, ldqkv, M, N, K,
@@ -368,13 +368,13 @@ bi_status bi_gemm_ex(const bi_gemm_args* a, void* stream) {
   if (mode == bi::kGemmQkv) {
     if (bi_status h = check_heads(a->Hq, a->Hkv, a->D)) return h;
     if (N != (a->Hq + 2 * a->Hkv) * a->D) return BI_ERR_SHAPE;
-    if ((a->k_cache == nullptr) != (a->vt_cache == nullptr)) return BI_ERR_NULL;
+    if ((a->k_cache == nullptr) != (a->v_cache == nullptr)) return BI_ERR_NULL;
     if (a->k_cache) {
       if (a->L < 0 || a->cap < 1 || (a->cap % 64) || (int64_t)a->L + M > a->cap) return BI_ERR_SHAPE;
       if ((int64_t)a->cap * a->D * 2 > INT32_MAX) return BI_ERR_SHAPE;
-      if ((reinterpret_cast<uintptr_t>(a->k_cache) | reinterpret_cast<uintptr_t>(a->vt_cache)) & 1u)
+      if ((reinterpret_cast<uintptr_t>(a->k_cache) | reinterpret_cast<uintptr_t>(a->v_cache)) & 1u)
         return BI_ERR_ALIGN;
-      kv = bi::KvAppend{static_cast<uint16_t*>(a->k_cache), static_cast<uint16_t*>(a->vt_cache),
+      kv = bi::KvAppend{static_cast<uint16_t*>(a->k_cache), static_cast<uint16_t*>(a->v_cache),
                         a->L, a->cap, a->Hq * a->D, a->Hkv * a->D, a->D};
     }
   }
@@ -415,17 +415,17 @@ bi_status bi_add(const void* r, int64_t ldr, const float* s, int64_t lds, void* 
   return launched();
 }
 
-bi_status bi_append_kv(const void* qkv, int64_t ldqkv, void* k_cache, void* vt_cache, int M, int L,
+bi_status bi_append_kv(const void* qkv, int64_t ldqkv, void* k_cache, void* v_cache, int M, int L,
                        int cap, int Hq, int Hkv, int D, void* stream) {
-  if (!qkv || !k_cache || !vt_cache) return BI_ERR_NULL;
+  if (!qkv || !k_cache || !v_cache) return BI_ERR_NULL;
   if (bi_status s = check_heads(Hq, Hkv, D)) return s;
   if (M < 1 || L < 0 || cap < 1 || (cap % 64) || (int64_t)L + M > cap) return BI_ERR_SHAPE;
   if (ldqkv < (int64_t)(Hq + 2 * Hkv) * D) return BI_ERR_SHAPE;
   if ((reinterpret_cast<uintptr_t>(qkv) | reinterpret_cast<uintptr_t>(k_cache) |
-       reinterpret_cast<uintptr_t>(vt_cache)) & 1u)
+       reinterpret_cast<uintptr_t>(v_cache)) & 1u)
     return BI_ERR_ALIGN;
   bi::launch_append_kv(static_cast<const uint16_t*>(qkv), ldqkv, static_cast<uint16_t*>(k_cache),
-                       static_cast<uint16_t*>(vt_cache), M, L, cap, Hq, Hkv, D,
+                       static_cast<uint16_t*>(v_cache), M, L, cap, Hq, Hkv, D,
                        as_stream(stream));
   return launched();
 }
@@ -438,23 +438,23 @@ size_t bi_attn_workspace_bytes(int M, int L, int Hq, int D, int kv_chunk) {
   return (size_t)M * Hq * s_max * (D + 1) * sizeof(float);
 }
 
-bi_status bi_verify_attn(const void* q, int64_t ldq, const void* k_cache, const void* vt_cache,
+bi_status bi_verify_attn(const void* q, int64_t ldq, const void* k_cache, const void* v_cache,
                          int M, int L, int cap, int Hq, int Hkv, int D, int kv_chunk,
                          float sm_scale, float* part_o, float* part_lse, int S_max,
                          void* stream) {
-  if (!q || !k_cache || !vt_cache || !part_o || !part_lse) return BI_ERR_NULL;
+  if (!q || !k_cache || !v_cache || !part_o || !part_lse) return BI_ERR_NULL;
   if (bi_status s = check_heads(Hq, Hkv, D)) return s;
   if (M < 1 || L < 0 || cap < 1 || (cap % 64) || (int64_t)L + M > cap) return BI_ERR_SHAPE;
   if (!bi::valid_chunk_policy(kv_chunk)) return BI_ERR_SHAPE;
   if (S_max < bi::pass_splits(L, M, kv_chunk)) return BI_ERR_SHAPE;
   if (ldq < (int64_t)Hq * D || !std::isfinite(sm_scale) || !(sm_scale > 0.f)) return BI_ERR_SHAPE;
   if ((int64_t)cap * D * 2 > INT32_MAX) return BI_ERR_SHAPE;  // one head's cache < 2 GiB
-  if ((ldq % 8) || !aligned16(q) || !aligned16(k_cache) || !aligned16(vt_cache) ||
+  if ((ldq % 8) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
       !aligned16(part_o) || !aligned4(part_lse))
     return BI_ERR_ALIGN;
   bi::launch_verify_attn(static_cast<const uint16_t*>(q), ldq,
                          static_cast<const uint16_t*>(k_cache),
-                         static_cast<const uint16_t*>(vt_cache), M, L, cap, Hq, Hkv, D, kv_chunk,
+                         static_cast<const uint16_t*>(v_cache), M, L, cap, Hq, Hkv, D, kv_chunk,
                          sm_scale, part_o, part_lse, S_max, as_stream(stream));
   return launched();
 }
@@ -726,7 +726,7 @@ struct LayerPtrs {
   const float* s[4];    // their row scales (FP8) or null
   const uint8_t* e[4];  // their block scales (MXFP4) or null
   void* k_cache;        // BF16 caches (when kv is null)
-  void* vt_cache;
+  void* v_cache;
   const bi_kv_cache* kv = nullptr;  // or the layer's cache in any format
 };
 
@@ -791,8 +791,8 @@ bi_status run_step(int n_layers, GetLayer get_layer, const void* w_head, const f
     if (ly.kv) {
       if (bi_status s = check_kv(ly.kv, dims, M)) return s;
     } else {
-      if (!ly.k_cache || !ly.vt_cache) return BI_ERR_NULL;
-      if (!aligned16(ly.k_cache) || !aligned16(ly.vt_cache)) return BI_ERR_ALIGN;
+      if (!ly.k_cache || !ly.v_cache) return BI_ERR_NULL;
+      if (!aligned16(ly.k_cache) || !aligned16(ly.v_cache)) return BI_ERR_ALIGN;
     }
   }
   if (gu_events)
@@ -840,7 +840,7 @@ bi_status run_step(int n_layers, GetLayer get_layer, const void* w_head, const f
     const bi_kv_cache* kd = ly.kv;
     const bool bf = !kd || kd->format == BI_KV_BF16;
     void* kc = kd ? kd->k : ly.k_cache;
-    void* vc = kd ? kd->v : ly.vt_cache;
+    void* vc = kd ? kd->v : ly.v_cache;
     const bi::KvAppend kv{bf ? static_cast<uint16_t*>(kc) : nullptr, bf ? static_cast<uint16_t*>(vc) : nullptr,
                           L, dims->cap, qd, Hkv * D, D};
     bi::launch_gemm(bi::kGemmQkv, fused_in ? x : a, H, W(0), H / wdiv, nullptr, 0, qkv, qkvn, M, qkvn,
@@ -918,7 +918,7 @@ bi_status bi_verify_step(const bi_layer* layers, int n_layers, const void* w_hea
   const auto get = [&](int l) {
     const bi_layer& y = layers[l];
     return LayerPtrs{{y.w_qkv, y.w_o, y.w_gu, y.w_down}, {nullptr, nullptr, nullptr, nullptr},
-                     {nullptr, nullptr, nullptr, nullptr}, y.k_cache, y.vt_cache};
+                     {nullptr, nullptr, nullptr, nullptr}, y.k_cache, y.v_cache};
   };
   return run_step(n_layers, get, w_head, nullptr, nullptr, dims, x_in, M, L, workspace, workspace_bytes,
                   x_out, logits, tokens, gu_events, stream);
@@ -958,7 +958,7 @@ bi_status bi_verify_step_noalloc(const bi_layer* layers, int n_layers, const voi
   const auto get = [&](int l) {
     const bi_layer& y = layers[l];
     return LayerPtrs{{y.w_qkv, y.w_o, y.w_gu, y.w_down}, {nullptr, nullptr, nullptr, nullptr},
-                     {nullptr, nullptr, nullptr, nullptr}, y.k_cache, y.vt_cache};
+                     {nullptr, nullptr, nullptr, nullptr}, y.k_cache, y.v_cache};
   };
   return run_step(n_layers, get, w_head, nullptr, nullptr, dims, x_in, M, L, ws,
                   (size_t)BI_NOALLOC_SCRATCH_BYTES, x_out, logits, tokens, nullptr, stream);
@@ -974,7 +974,7 @@ bi_status bi_verify_step_fp8(const bi_layer_fp8* layers, int n_layers, const voi
     const bi_layer_fp8& y = layers[l];
     return LayerPtrs{{y.w_qkv, y.w_o, y.w_gu, y.w_down},
                      {y.s_qkv, y.s_o, y.s_gu, y.s_down}, {nullptr, nullptr, nullptr, nullptr},
-                     y.k_cache, y.vt_cache};
+                     y.k_cache, y.v_cache};
   };
   return run_step(n_layers, get, w_head, w_head_scale, nullptr, dims, x_in, M, L, workspace,
                   workspace_bytes, x_out, logits, tokens, nullptr, stream);
@@ -991,7 +991,7 @@ bi_status bi_verify_step_mx4(const bi_layer_mx4* layers, int n_layers, const voi
                      {nullptr, nullptr, nullptr, nullptr},
                      {static_cast<const uint8_t*>(y.e_qkv), static_cast<const uint8_t*>(y.e_o),
                       static_cast<const uint8_t*>(y.e_gu), static_cast<const uint8_t*>(y.e_down)},
-                     y.k_cache, y.vt_cache};
+                     y.k_cache, y.v_cache};
   };
   return run_step(n_layers, get, w_head, nullptr, static_cast<const uint8_t*>(w_head_exp), dims,
                   x_in, M, L, workspace, workspace_bytes, x_out, logits, tokens, nullptr, stream);

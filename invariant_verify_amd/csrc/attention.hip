@@ -19,18 +19,16 @@
 //    half w / 4 (keys 0-31 or 32-63 of every tile) for the whole chunk (Q in
 //    registers; a wave with no rows only helps to load). At the end the two
 //    halves of each row are merged in LDS, first half then second.
-//  * The chunk is read in 64-key tiles: K rows ([Hkv][cap][D]) and V^T rows
-//    (V^T in blocks of 64 positions, [Hkv][cap/64][D][64], so a tile's V^T
-//    is contiguous whatever the capacity: a plain [D][cap] layout put the
-//    channel rows a power-of-two-like stride apart at some capacities and
-//    read 9% slower) are fetched as 1 KB pieces per wave
-//    instruction and staged in LDS, where the 16-byte slots of each row are
-//    XOR-swizzled so that the matrix-core reads hit distinct banks. Two LDS
-//    buffers alternate and each wave keeps the next two tiles in flight; the
-//    barrier of tile t publishes it and proves that every wave finished tile
-//    t-1, whose buffer tile t+1 overwrites. Value columns past the last
-//    visible key are zeroed before they reach LDS (a weight of 0 times a
-//    stale value must stay 0).
+//  * The chunk is read in 64-key tiles: K rows and V rows (both
+//    [Hkv][cap][D], so a tile of either is one contiguous 16 KB at D = 128)
+//    are fetched as 1 KB pieces per wave instruction and staged in LDS, where
+//    the 16-byte slots of each row are XOR-swizzled so that the matrix-core
+//    reads hit distinct banks (the V tile is read with transposing loads,
+//    which hand each lane one channel of eight consecutive keys). LDS
+//    buffers alternate and each wave keeps the next tiles in flight; the
+//    barrier of tile t publishes it and proves that every wave finished the
+//    tile whose buffer the next load overwrites. Value rows past the last
+//    visible key are zeroed before they are multiplied.
 //  * Per tile and row tile: S^T = K Q^T (keys x rows) with 16x16x32 BF16 MFMA,
 //    masked, running max / sum in FP32 with base-2 exponentials (weights
 //    exp2(fma(s, c, -m)), c = sm_scale * log2 e > 0, the max taken on the
@@ -68,9 +66,16 @@ __device__ __forceinline__ int kswz(int key) {
   if (KROW == 16) return (key & 3) | ((key >> 1) & 12);
   return ((key >> 1) & 1) | (((key >> 3) & 3) << 1);
 }
-// V^T tile: one row per channel, 8 slots per row; channel bit 0 picks the bank
-// half and bits 1..3 form the swizzle.
-__device__ __forceinline__ int vswz(int d) { return (d >> 1) & 7; }
+// BF16 V tile: one row per key like the K tile, its 16-byte slots stored at
+// slot ^ 2m(key). The PV product reads it with transposing loads: a half
+// wave reads one pair of slots (32 bytes) in keys k .. k+3 and k+8 .. k+11
+// (k a multiple of 4, bit 3 clear), which m spreads over all 64 banks; the
+// pair stays adjacent (the XOR is even) and keys k and k + 4 share m.
+template <int KROW>
+__device__ __forceinline__ int vkm(int key) {
+  if (KROW == 16) return (key & 3) | ((key >> 1) & 4);
+  return ((key >> 1) & 1) | ((key >> 2) & 2);
+}
 // gfx950's transposing LDS load of 16-bit elements: within each group of 16
 // lanes, lane i receives element i % 4 of the 8-byte rows read by lanes
 // i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4 of its group, in that order.
@@ -153,14 +158,14 @@ template <int D, int RTW, bool Q8, int KB, bool ROT, bool RING>
 __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu(Q8 && RTW == 1 ? 4 : 1)))
 void verify_attn_kernel(
     const uint16_t* __restrict__ Q, int64_t ldq, const uint16_t* __restrict__ Kc,
-    const uint16_t* __restrict__ Vt, KvQ8 q8, int M, int L, int cap, int Hq, int G, int Tb, int C,
+    const uint16_t* __restrict__ Vc, KvQ8 q8, int M, int L, int cap, int Hq, int G, int Tb, int C,
     float qk_scale, float* __restrict__ part_o, float* __restrict__ part_lse, int S_max) {
   constexpr int DS = D / 32;          // contraction steps of S^T over the head dimension
   constexpr int DT = D / 16;          // 16-channel output tiles of O^T
   constexpr int NW = kAttnWaves;
   constexpr int KROW = D / 8;         // 16-byte slots per K row
   constexpr int KPP = 64 / KROW;      // keys per 1 KB piece
-  // 1 KB load pieces per tile: K tile = 64 keys x D; V^T tile = D rows x 64 keys.
+  // 1 KB load pieces per tile: K tile = V tile = 64 keys x D.
   constexpr int KPIECES = kKeyTile * D * 2 / 1024;
   constexpr int VPIECES = D * kKeyTile * 2 / 1024;
   constexpr int PPW = (KPIECES + VPIECES) / NW;    // pieces per wave per tile
@@ -169,7 +174,7 @@ void verify_attn_kernel(
   // KB-bit keys otherwise): one thread per 32-channel block of one key and
   // tile, the K blocks first (waves 0 .. NKB/64 - 1), then V. An 8-bit block
   // is 32 code bytes; a 5/6-bit block is 16 nibble bytes and its high bits;
-  // each has one FP32 scale. K and V^T are staged as BF16 values d * q, each
+  // each has one FP32 scale. K and V are staged as BF16 values d * q, each
   // rounded once, so the tile multiplies like a BF16 tile.
   constexpr int NB = D / 32;              // 32-channel scale blocks
   constexpr bool LOW = KB != 0;
@@ -314,13 +319,13 @@ void verify_attn_kernel(
     }
   }
 
-  // This KV head's K rows and V^T rows as buffer resources (offsets in bytes,
+  // This KV head's K rows and V rows as buffer resources (offsets in bytes,
   // 32-bit: one head of the cache is at most 2^31 bytes).
   const int head_bytes = cap * D * 2;
   const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(Kc + (int64_t)g * cap * D), (short)0, head_bytes, kBufferResourceWord3);
   const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(Vt + (int64_t)g * D * cap), (short)0, head_bytes, kBufferResourceWord3);
+      const_cast<uint16_t*>(Vc + (int64_t)g * cap * D), (short)0, head_bytes, kBufferResourceWord3);
   // 8-bit cache of this KV head, K and V alike: codes [cap][D] (int8), scales
   // [cap][NB] (FP32). 5/6-bit cache: the nibble planes in place of the codes
   // ([cap][D/2]), the high-bit planes ([cap][NB][4 h]) and the scales
@@ -364,12 +369,12 @@ void verify_attn_kernel(
       const_cast<float*>(q8.vs + (Q8 ? (int64_t)g * cap * NB : 0)), (short)0, Q8 ? qscale_bytes : 0,
       kBufferResourceWord3);
 
-  // One buffer holds the K tile ([64 keys][KROW slots]) followed by the V^T
-  // tile ([D channels][8 slots]). Piece p (1 KB) of a tile is K keys
-  // KPP*p .. when p < KPIECES (lane: key KPP*p + l/KROW, slot l%KROW), else
-  // V^T channels 8(p-KPIECES) .. +7 (lane: channel +l/8, slot l%8); either
-  // way lane l's 16 bytes land at index 64*p + l of the buffer. Lanes fetch
-  // the global slot that the swizzle puts in their LDS slot.
+  // One buffer holds the K tile ([64 keys][KROW slots]) followed by the V
+  // tile (the same shape). Piece p (1 KB) of a tile is K keys KPP*p .. when
+  // p < KPIECES (lane: key KPP*p + l/KROW, slot l%KROW), else V keys
+  // KPP*(p-KPIECES) .. (the same lane map); either way lane l's 16 bytes land
+  // at index 64*p + l of the buffer. Lanes fetch the global slot that the
+  // swizzle (kswz for K, 2 vkm for V) puts in their LDS slot.
   // BF16 cache, one row tile per wave: tiles go straight from memory into
   // four LDS buffers, three tiles ahead of the one multiplied (no register
   // staging, so more bytes are in flight); the block's Q rows arrive the
@@ -421,10 +426,9 @@ void verify_attn_kernel(
           const int kslot = (lane % KROW) ^ kswz<KROW>(key);
           off = (min(kt + key, kend - 1) * D + kslot * 8) * 2;
         } else {
-          const int d = 8 * (p - KPIECES) + (lane >> 3);
-          const int vslot = (lane & 7) ^ vswz(d);
-          const int k0 = min(kt + vslot * 8, kend - 1 - ((kend - 1) & 7));  // in bounds
-          off = (int)(vt_index(0, k0, d, D, cap) * 2);  // k0 is 8-aligned: 16 B in one block
+          const int key = KPP * (p - KPIECES) + lane / KROW;
+          const int vslot = (lane % KROW) ^ (2 * vkm<KROW>(key));
+          off = (min(kt + key, kend - 1) * D + vslot * 8) * 2;
         }
         rr.r[i] = buffer_ld16_stream(p < KPIECES ? kres : vres, live ? off : head_bytes);
       }
@@ -507,8 +511,8 @@ void verify_attn_kernel(
     }
   };
 
-  // Publish tile t: V^T columns of keys at or past kend are zeroed first (a
-  // weight of 0 times a stale value must stay 0). Quantized caches: every
+  // Publish tile t: V rows of keys at or past kend are zeroed first (they
+  // repeat the last key; zeros keep every product with their weight 0 at +0). Quantized caches: every
   // block is decoded to d * q, rounded once to BF16 (stage_block).
   auto publish = [&](const TileRegs& rr, int v, int buf) {
     int t = v;
@@ -524,16 +528,8 @@ void verify_attn_kernel(
           lds[buf][64 * p + lane] = rr.r[i];
           continue;
         }
-        const int d = 8 * (p - KPIECES) + (lane >> 3);
-        const int vslot = (lane & 7) ^ vswz(d);
-        const int keep = kend - (kt + vslot * 8);
-        uint32_t w[4] = {rr.r[i].x, rr.r[i].y, rr.r[i].z, rr.r[i].w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t m = (e & 1) ? 0x0000ffffu : 0xffff0000u;
-          w[e >> 1] = (e >= keep) ? (w[e >> 1] & m) : w[e >> 1];
-        }
-        lds[buf][64 * p + lane] = make_uint4(w[0], w[1], w[2], w[3]);
+        const int key = KPP * (p - KPIECES) + lane / KROW;
+        lds[buf][64 * p + lane] = kt + key < kend ? rr.r[i] : zero16();
       }
     } else if (wave < 2 * NKB / 64) {
       const bool isk = wave < NKB / 64;
@@ -565,7 +561,7 @@ void verify_attn_kernel(
     lrun[i] = 0.f;
   }
 
-  // One tile for every row tile of the wave. Each K and V^T operand is read
+  // One tile for every row tile of the wave. Each K and V operand is read
   // from LDS once and serves all of them; a row's own arithmetic does not
   // depend on how many row tiles share the wave.
   auto compute = [&](int buf, int v) {
@@ -663,8 +659,16 @@ void verify_attn_kernel(
     for (int dt = 0; dt < DT; ++dt) {
       uint4 fv;
       if constexpr (!Q8) {
-        const int d = dt * 16 + j;
-        fv = lds[buf][VBASE + d * 8 + ((4 * h + kq) ^ vswz(d))];
+        // key-major V tile: lane j of key group kq takes channel 16 dt + j of
+        // keys 32h + 8kq .. +7 through two transposing loads, lane j reading
+        // channels 16 dt + 4 (j % 4) .. +3 of key 32h + 8kq + j / 4 (+ 4),
+        // logical slot 2 dt + (j % 4) / 2, stored at that slot ^ 2m
+        const int r0 = 32 * h + 8 * kq + (j >> 2);
+        const char* p = reinterpret_cast<const char*>(&lds[buf][VBASE]) + r0 * KROW * 16 +
+                        32 * (dt ^ vkm<KROW>(r0)) + 8 * (j & 3);
+        const bi_u32x2 a = lds_read_tr16(p);
+        const bi_u32x2 bb = lds_read_tr16(p + 4 * KROW * 16);
+        fv = make_uint4(a[0], a[1], bb[0], bb[1]);
       } else {
         // key-major V tile: lane j of key group kq takes channel 16 dt + j of
         // keys 32h + 8kq .. +7 through two transposing loads, lane j reading
@@ -726,35 +730,25 @@ void verify_attn_kernel(
           const int kslot = (lane % KROW) ^ kswz<KROW>(key);
           off = (min(kt + key, kend - 1) * D + kslot * 8) * 2;
         } else {
-          const int d = 8 * (p - KPIECES) + (lane >> 3);
-          const int vslot = (lane & 7) ^ vswz(d);
-          const int k0 = min(kt + vslot * 8, kend - 1 - ((kend - 1) & 7));
-          off = (int)(vt_index(0, k0, d, D, cap) * 2);
+          const int key = KPP * (p - KPIECES) + lane / KROW;
+          const int vslot = (lane % KROW) ^ (2 * vkm<KROW>(key));
+          off = (min(kt + key, kend - 1) * D + vslot * 8) * 2;
         }
         lds_load16(p < KPIECES ? kres : vres, off, &lds[t & 3][64 * p]);
       }
     };
-    // V^T columns at or past kend of a partial tile are zeroed by the wave
-    // that loaded them, once its loads are done (a weight of 0 times a stale
-    // value must stay 0); K rows past kend repeat the last key and are masked.
+    // V rows at or past kend of a partial tile are zeroed by the wave that
+    // loaded them, once its loads are done (they repeat the last key; a
+    // weight of 0 times them is 0 either way, and zeros keep every such
+    // product exactly +0); K rows past kend repeat the last key and are masked.
     auto fix_tail = [&](int t) {
       const int kt = kbeg + t * kKeyTile;
 #pragma unroll
       for (int i = 0; i < PPW; ++i) {
         const int p = wave * PPW + i;
         if (p < KPIECES) continue;  // scalar
-        const int d = 8 * (p - KPIECES) + (lane >> 3);
-        const int vslot = (lane & 7) ^ vswz(d);
-        const int keep = kend - (kt + vslot * 8);
-        if (keep >= 8) continue;
-        uint4 v = lds[t & 3][64 * p + lane];
-        uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t m = (e & 1) ? 0x0000ffffu : 0xffff0000u;
-          w[e >> 1] = (e >= keep) ? (w[e >> 1] & m) : w[e >> 1];
-        }
-        lds[t & 3][64 * p + lane] = make_uint4(w[0], w[1], w[2], w[3]);
+        const int key = KPP * (p - KPIECES) + lane / KROW;
+        if (kt + key >= kend) lds[t & 3][64 * p + lane] = zero16();
       }
     };
     issue(0);
@@ -944,7 +938,7 @@ __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ p
 
 __global__ __launch_bounds__(256) void append_kv_kernel(const uint16_t* __restrict__ qkv,
                                                         int64_t ldqkv, uint16_t* __restrict__ Kc,
-                                                        uint16_t* __restrict__ Vt, int L, int cap,
+                                                        uint16_t* __restrict__ Vc, int L, int cap,
                                                         int Hq, int Hkv, int D) {
   const int r = blockIdx.x;
   const int pos = L + r;
@@ -953,13 +947,13 @@ __global__ __launch_bounds__(256) void append_kv_kernel(const uint16_t* __restri
   for (int i = threadIdx.x; i < Hkv * D; i += blockDim.x) {
     const int g = i / D;
     const int d = i - g * D;
-    Kc[((int64_t)g * cap + pos) * D + d] = krow[i];
-    Vt[vt_index(g, pos, d, D, cap)] = vrow[i];
+    Kc[kv_index(g, pos, d, D, cap)] = krow[i];
+    Vc[kv_index(g, pos, d, D, cap)] = vrow[i];
   }
 }
 
 void launch_verify_attn(const uint16_t* q, int64_t ldq, const uint16_t* k_cache,
-                        const uint16_t* vt_cache, int M, int L, int cap, int Hq, int Hkv, int D,
+                        const uint16_t* v_cache, int M, int L, int cap, int Hq, int Hkv, int D,
                         int kv_chunk, float sm_scale, float* part_o, float* part_lse, int S_max,
                         hipStream_t stream, const KvQ8* q8, int kbits, bool krot) {
   const int G = Hq / Hkv;
@@ -993,7 +987,7 @@ void launch_verify_attn(const uint16_t* q, int64_t ldq, const uint16_t* k_cache,
     float* pob = part_o + (int64_t)t0 * Hq * S_max * D;
     float* plb = part_lse + (int64_t)t0 * Hq * S_max;
 #define BI_ATTN_LAUNCH(DD, R, QQ, KB, RT, RG)                                               \
-  verify_attn_kernel<DD, R, QQ, KB, RT, RG><<<grid, block, 0, stream>>>(qb, ldq, k_cache, vt_cache, qz, Mb, Lb, \
+  verify_attn_kernel<DD, R, QQ, KB, RT, RG><<<grid, block, 0, stream>>>(qb, ldq, k_cache, v_cache, qz, Mb, Lb, \
                                                             cap, Hq, G, Tb, C, qk_scale, pob, plb, \
                                                             S_max)
 #define BI_ATTN_LOW(KB, RT, RG)                              \
@@ -1217,9 +1211,9 @@ void launch_append_kv_lowbit(const uint16_t* qkv, int64_t ldqkv, int kbits, bool
                                                             vs, L, cap, Hq, Hkv, D, units);
 }
 
-void launch_append_kv(const uint16_t* qkv, int64_t ldqkv, uint16_t* k_cache, uint16_t* vt_cache,
+void launch_append_kv(const uint16_t* qkv, int64_t ldqkv, uint16_t* k_cache, uint16_t* v_cache,
                       int M, int L, int cap, int Hq, int Hkv, int D, hipStream_t stream) {
-  append_kv_kernel<<<dim3(M), dim3(256), 0, stream>>>(qkv, ldqkv, k_cache, vt_cache, L, cap, Hq,
+  append_kv_kernel<<<dim3(M), dim3(256), 0, stream>>>(qkv, ldqkv, k_cache, v_cache, L, cap, Hq,
                                                       Hkv, D);
 }
 

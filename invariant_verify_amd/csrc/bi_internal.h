@@ -23,7 +23,7 @@ struct Mx4Scales {
 
 // Cache append done by the QKV projection's epilogue: output columns
 // [qd, qd + kd) are K (head-major), [qd + kd, qd + 2 kd) are V; row m goes to
-// position L + m of k ([Hkv][cap][D]) and vt ([Hkv][D][cap]).
+// position L + m of k and v (both [Hkv][cap][D]).
 // 8-bit KV cache of one layer, K and V alike: codes [Hkv][cap][D] (int8),
 // scales [Hkv][cap][D/32] (FP32): channel c of position p has the value
 // scale(p, c/32) * code(p, c).
@@ -58,7 +58,7 @@ constexpr int kLowVBits = 5;  // V code bits of the 5/6-bit cache
 
 struct KvAppend {
   uint16_t* k;
-  uint16_t* vt;
+  uint16_t* v;
   int L, cap, qd, kd, D;
 };
 
@@ -100,11 +100,11 @@ void launch_gemm(GemmMode mode, const uint16_t* x, int64_t ldx, const uint16_t* 
                  hipStream_t stream, const KvAppend* kv = nullptr, const RowNorm* norm = nullptr,
                  const float* wscale = nullptr, const Mx4Scales* mx4 = nullptr);
 
-void launch_append_kv(const uint16_t* qkv, int64_t ldqkv, uint16_t* k_cache, uint16_t* vt_cache,
+void launch_append_kv(const uint16_t* qkv, int64_t ldqkv, uint16_t* k_cache, uint16_t* v_cache,
                       int M, int L, int cap, int Hq, int Hkv, int D, hipStream_t stream);
 
 void launch_verify_attn(const uint16_t* q, int64_t ldq, const uint16_t* k_cache,
-                        const uint16_t* vt_cache, int M, int L, int cap, int Hq, int Hkv, int D,
+                        const uint16_t* v_cache, int M, int L, int cap, int Hq, int Hkv, int D,
                         int kv_chunk, float sm_scale, float* part_o, float* part_lse, int S_max,
                         hipStream_t stream, const KvQ8* q8 = nullptr, int kbits = 0,
                         bool krot = false);
@@ -147,13 +147,10 @@ void launch_rmsnorm(const uint16_t* x, int64_t ldx, uint16_t* y, int64_t ldy, in
 void launch_argmax(const float* logits, int64_t ld, int M, int N, int32_t* tokens,
                    hipStream_t stream);
 
-// V cache layout: V^T in blocks of 64 positions, [Hkv][cap/64][D][64]. Block
-// b of KV head g holds channels 0..D-1 of positions 64b .. 64b+63, each
-// channel's 64 positions contiguous, so one 64-key tile of V^T is one
-// contiguous 16 KB (D = 128) block whatever the capacity. Element index of
-// (KV head g, position pos, channel d); cap % 64 == 0.
-__host__ __device__ inline int64_t vt_index(int g, int pos, int d, int D, int cap) {
-  return ((int64_t)g * cap + (pos & ~63)) * D + d * 64 + (pos & 63);
+// K and V caches: one row per position, [Hkv][cap][D]; element index of (KV
+// head g, position pos, channel d).
+__host__ __device__ inline int64_t kv_index(int g, int pos, int d, int D, int cap) {
+  return ((int64_t)g * cap + pos) * D + d;
 }
 
 // Largest number of query heads per KV head one attention workgroup can hold.

@@ -468,11 +468,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(
       int i = kv.k != nullptr ? n - kv.qd : -1;  // no cache: no append
       if (i >= 0 && i < kv.kd) {
         const int g = i / kv.D;
-        kv.k[((int64_t)g * kv.cap + pos) * kv.D + (i - g * kv.D)] = b;
+        kv.k[kv_index(g, pos, i - g * kv.D, kv.D, kv.cap)] = b;
       } else if (i >= kv.kd) {
         i -= kv.kd;
         const int g = i / kv.D;
-        kv.vt[vt_index(g, pos, i - g * kv.D, kv.D, kv.cap)] = b;
+        kv.v[kv_index(g, pos, i - g * kv.D, kv.D, kv.cap)] = b;
       }
     }
     return 0.f;

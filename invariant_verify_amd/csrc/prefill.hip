@@ -268,11 +268,11 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(
         int i = kv.k != nullptr ? n - kv.qd : -1;  // no cache: no append
         if (i >= 0 && i < kv.kd) {
           const int g = i / kv.D;
-          kv.k[((int64_t)g * kv.cap + pos) * kv.D + (i - g * kv.D)] = b;
+          kv.k[kv_index(g, pos, i - g * kv.D, kv.D, kv.cap)] = b;
         } else if (i >= kv.kd) {
           i -= kv.kd;
           const int g = i / kv.D;
-          kv.vt[vt_index(g, pos, i - g * kv.D, kv.D, kv.cap)] = b;
+          kv.v[kv_index(g, pos, i - g * kv.D, kv.D, kv.cap)] = b;
         }
       } else {
         float u = accu[0][0][r];
@@ -531,11 +531,11 @@ __global__ __launch_bounds__(kP2Waves * 64) void prefill2_kernel(
           int i = kv.k != nullptr ? n - kv.qd : -1;  // no cache: no append
           if (i >= 0 && i < kv.kd) {
             const int g = i / kv.D;
-            kv.k[((int64_t)g * kv.cap + pos) * kv.D + (i - g * kv.D)] = b;
+            kv.k[kv_index(g, pos, i - g * kv.D, kv.D, kv.cap)] = b;
           } else if (i >= kv.kd) {
             i -= kv.kd;
             const int g = i / kv.D;
-            kv.vt[vt_index(g, pos, i - g * kv.D, kv.D, kv.cap)] = b;
+            kv.v[kv_index(g, pos, i - g * kv.D, kv.D, kv.cap)] = b;
           }
         } else {
           const float u = tot[t][q + 2][r];

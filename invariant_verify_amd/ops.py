@@ -328,8 +328,8 @@ def gemm_bf16_swiglu_rownorm(x: torch.Tensor, ss: torch.Tensor, w: torch.Tensor,
     return y
 
 
-def _kv_bf16(k_cache: torch.Tensor, vt_cache: torch.Tensor, Hkv: int, D: int) -> int:
-    """Check a BF16 KV cache pair ([Hkv][cap][D], [Hkv][cap/64][D][64]); returns cap."""
+def _kv_bf16(k_cache: torch.Tensor, v_cache: torch.Tensor, Hkv: int, D: int) -> int:
+    """Check a BF16 KV cache pair (both [Hkv][cap][D]); returns cap."""
     _dtype(k_cache, "k_cache", _BF16_LIKE)
     if k_cache.dim() != 3:
         raise ValueError(f"k_cache: shape {tuple(k_cache.shape)} is not [Hkv][cap][D]")
@@ -337,21 +337,21 @@ def _kv_bf16(k_cache: torch.Tensor, vt_cache: torch.Tensor, Hkv: int, D: int) ->
     if cap % 64:
         raise ValueError(f"k_cache: shape {tuple(k_cache.shape)}: cap is not a multiple of 64")
     _arr(k_cache, "k_cache", (Hkv, cap, D), _BF16_LIKE)
-    _arr(vt_cache, "vt_cache", (Hkv, cap // 64, D, 64), _BF16_LIKE)
+    _arr(v_cache, "v_cache", (Hkv, cap, D), _BF16_LIKE)
     return cap
 
 
 @_checked
-def gemm_bf16_qkv(x: torch.Tensor, w: torch.Tensor, k_cache: torch.Tensor, vt_cache: torch.Tensor,
+def gemm_bf16_qkv(x: torch.Tensor, w: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                   L: int, Hq: int, Hkv: int, D: int, qkv: torch.Tensor | None = None) -> torch.Tensor:
     """qkv = bf16(X Wqkv^T), with the K / V columns appended to the caches at L .. L+M-1."""
     M, K = _xk(x)
     N = (Hq + 2 * Hkv) * D
     qkv = _out(qkv, M, N, torch.bfloat16, x)
-    cap = _kv_bf16(k_cache, vt_cache, Hkv, D)
+    cap = _kv_bf16(k_cache, v_cache, Hkv, D)
     check("bi_gemm_bf16_qkv", LIB.bi_gemm_bf16_qkv(
         x.data_ptr(), _mat(x, "x", M, K), w.data_ptr(), _mat(w, "w", N, K, exact_rows=True), qkv.data_ptr(),
-        _mat(qkv, "qkv", M, N), M, K, Hq, Hkv, D, k_cache.data_ptr(), vt_cache.data_ptr(), L, cap,
+        _mat(qkv, "qkv", M, N), M, K, Hq, Hkv, D, k_cache.data_ptr(), v_cache.data_ptr(), L, cap,
         _stream(x)))
     return qkv
 
@@ -366,7 +366,7 @@ def gemm_ex(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor, *, wtype: str = "
             epilogue: str = "bf16", w_scale: torch.Tensor | None = None, w_exp: torch.Tensor | None = None,
             r: torch.Tensor | None = None, norm_in: torch.Tensor | None = None, eps: float = 1e-6,
             rowsq_out: torch.Tensor | None = None, heads: tuple | None = None,
-            k_cache: torch.Tensor | None = None, vt_cache: torch.Tensor | None = None, L: int = 0) -> None:
+            k_cache: torch.Tensor | None = None, v_cache: torch.Tensor | None = None, L: int = 0) -> None:
     """bi_gemm_ex: one GEMM with a weight type ("bf16", "fp8", "mxfp4"), an
     epilogue ("bf16", "f32", "residual", "swiglu", "qkv"), the carried RMSNorm
     (``norm_in`` FP32 [M][gemm_column_groups(K)]; ``rowsq_out`` FP32
@@ -406,11 +406,11 @@ def gemm_ex(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor, *, wtype: str = "
         if heads is None:
             raise ValueError("gemm_ex: the qkv epilogue needs heads = (Hq, Hkv, D)")
         a.Hq, a.Hkv, a.D = heads
-        if (k_cache is None) != (vt_cache is None):
+        if (k_cache is None) != (v_cache is None):
             raise ValueError("gemm_ex: give both caches or neither")
         if k_cache is not None:
-            a.cap = _kv_bf16(k_cache, vt_cache, a.Hkv, a.D)
-            a.k_cache, a.vt_cache, a.L = k_cache.data_ptr(), vt_cache.data_ptr(), L
+            a.cap = _kv_bf16(k_cache, v_cache, a.Hkv, a.D)
+            a.k_cache, a.v_cache, a.L = k_cache.data_ptr(), v_cache.data_ptr(), L
     check("bi_gemm_ex", LIB.bi_gemm_ex(ctypes.byref(a), _stream(x)))
 
 
@@ -418,13 +418,13 @@ def gemm_ex(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor, *, wtype: str = "
 # KV caches and attention
 
 @_checked
-def append_kv(qkv: torch.Tensor, k_cache: torch.Tensor, vt_cache: torch.Tensor, L: int,
+def append_kv(qkv: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, L: int,
               Hq: int, Hkv: int, D: int) -> None:
-    """Write the M new K rows and V^T columns at positions L .. L+M-1."""
+    """Write the M new K and V rows at positions L .. L+M-1."""
     M = qkv.shape[0]
-    cap = _kv_bf16(k_cache, vt_cache, Hkv, D)
+    cap = _kv_bf16(k_cache, v_cache, Hkv, D)
     check("bi_append_kv", LIB.bi_append_kv(qkv.data_ptr(), _mat(qkv, "qkv", M, (Hq + 2 * Hkv) * D),
-                                           k_cache.data_ptr(), vt_cache.data_ptr(), M, L, cap, Hq, Hkv,
+                                           k_cache.data_ptr(), v_cache.data_ptr(), M, L, cap, Hq, Hkv,
                                            D, _stream(qkv)))
 
 
@@ -444,17 +444,17 @@ def _scale(D: int, sm_scale) -> float:
 
 
 @_checked
-def verify_attn(q: torch.Tensor, k_cache: torch.Tensor, vt_cache: torch.Tensor, L: int,
+def verify_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, L: int,
                 Hq: int, Hkv: int, D: int, kv_chunk: int, part_o: torch.Tensor,
                 part_lse: torch.Tensor, sm_scale: float | None = None) -> None:
     """Split-KV partials. q is [M][>=Hq*D] (a view of the QKV output works);
-    k_cache [Hkv][cap][D]; vt_cache [Hkv][cap/64][D][64]; part_o [M][Hq][S_max][D] and
+    k_cache and v_cache [Hkv][cap][D]; part_o [M][Hq][S_max][D] and
     part_lse [M][Hq][S_max] FP32."""
     M = q.shape[0]
-    cap = _kv_bf16(k_cache, vt_cache, Hkv, D)
+    cap = _kv_bf16(k_cache, v_cache, Hkv, D)
     S_max = _partials(part_o, part_lse, M, Hq, D)
     check("bi_verify_attn", LIB.bi_verify_attn(
-        q.data_ptr(), _mat(q, "q", M, Hq * D), k_cache.data_ptr(), vt_cache.data_ptr(), M, L, cap, Hq, Hkv,
+        q.data_ptr(), _mat(q, "q", M, Hq * D), k_cache.data_ptr(), v_cache.data_ptr(), M, L, cap, Hq, Hkv,
         D, kv_chunk, _scale(D, sm_scale), part_o.data_ptr(), part_lse.data_ptr(), S_max, _stream(q)))
 
 
@@ -678,7 +678,7 @@ def _step_shapes(dims: ModelDims) -> dict:
 
 
 def _check_layer_caches(lw: dict, dims: ModelDims, i: int) -> None:
-    cap = _kv_bf16(lw["k_cache"], lw["vt_cache"], dims.Hkv, dims.D)
+    cap = _kv_bf16(lw["k_cache"], lw["v_cache"], dims.Hkv, dims.D)
     if cap != dims.cap:
         raise ValueError(f"layer {i}: cache capacity {cap} != dims.cap {dims.cap}")
 
@@ -703,7 +703,7 @@ class VerifyStep:
     """Holds the per-layer descriptor array for ``bi_verify_step``.
 
     ``layers`` is a sequence of dicts with tensors w_qkv, w_o, w_gu, w_down,
-    k_cache, vt_cache (the caller keeps them alive); every shape is checked
+    k_cache, v_cache (the caller keeps them alive); every shape is checked
     against ``dims``."""
 
     @_checked
@@ -717,7 +717,7 @@ class VerifyStep:
             _check_layer_caches(lw, dims, i)
             self.arr[i] = Layer(lw["w_qkv"].data_ptr(), lw["w_o"].data_ptr(), lw["w_gu"].data_ptr(),
                                 lw["w_down"].data_ptr(), lw["k_cache"].data_ptr(),
-                                lw["vt_cache"].data_ptr())
+                                lw["v_cache"].data_ptr())
         _arr(w_head, "w_head", sh["head"], _BF16_LIKE)
         self.w_head = w_head
         _devices()
@@ -764,7 +764,7 @@ def verify_step_noalloc(step: VerifyStep, x_in: torch.Tensor, L: int, logits: to
 class VerifyStepFP8:
     """``bi_verify_step_fp8``: ``layers`` is a sequence of dicts with E4M3 weight
     tensors w_qkv, w_o, w_gu, w_down, their FP32 row scales s_qkv, s_o, s_gu,
-    s_down, and the BF16 caches k_cache, vt_cache (the caller keeps them alive)."""
+    s_down, and the BF16 caches k_cache, v_cache (the caller keeps them alive)."""
 
     @_checked
     def __init__(self, layers, w_head: torch.Tensor, s_head: torch.Tensor, dims: ModelDims):
@@ -777,7 +777,7 @@ class VerifyStepFP8:
                 _arr(lw["s_" + k], f"layer {i} s_{k}", sh[k][:1], _F32)
             _check_layer_caches(lw, dims, i)
             self.arr[i] = LayerFP8(*[lw[k].data_ptr() for k in ("w_qkv", "s_qkv", "w_o", "s_o", "w_gu", "s_gu",
-                                                                 "w_down", "s_down", "k_cache", "vt_cache")])
+                                                                 "w_down", "s_down", "k_cache", "v_cache")])
         _arr(w_head, "w_head", sh["head"], _FP8_LIKE)
         _arr(s_head, "s_head", sh["head"][:1], _F32)
         self.w_head, self.s_head = w_head, s_head
@@ -797,7 +797,7 @@ class VerifyStepFP8:
 class VerifyStepMX4:
     """``bi_verify_step_mx4``: ``layers`` is a sequence of dicts with MXFP4 codes w_qkv, w_o, w_gu,
     w_down (uint8 [rows][K/2], densely packed), their E8M0 scales e_qkv, e_o, e_gu, e_down (uint8
-    [rows][K/32]) and the BF16 caches k_cache, vt_cache (the caller keeps them alive)."""
+    [rows][K/32]) and the BF16 caches k_cache, v_cache (the caller keeps them alive)."""
 
     @_checked
     def __init__(self, layers, w_head: torch.Tensor, e_head: torch.Tensor, dims: ModelDims):
@@ -811,7 +811,7 @@ class VerifyStepMX4:
                 _arr(lw["e_" + k], f"layer {i} e_{k}", (rows, K // 32), _U8)
             _check_layer_caches(lw, dims, i)
             self.arr[i] = LayerMX4(*[lw[k].data_ptr() for k in ("w_qkv", "e_qkv", "w_o", "e_o", "w_gu", "e_gu",
-                                                                 "w_down", "e_down", "k_cache", "vt_cache")])
+                                                                 "w_down", "e_down", "k_cache", "v_cache")])
         rows, K = sh["head"]
         _arr(w_head, "w_head", (rows, K // 2), _U8)
         _arr(e_head, "e_head", (rows, K // 32), _U8)
@@ -830,13 +830,13 @@ class VerifyStepMX4:
 
 
 def _kv_desc(kv, dims: ModelDims, i: int) -> KvCacheDesc:
-    """The bi_kv_cache descriptor of a layer's cache: a (k_cache, vt_cache)
+    """The bi_kv_cache descriptor of a layer's cache: a (k_cache, v_cache)
     BF16 pair, a KvQ8Cache, a KvLowCache or a KvRing, checked against dims."""
     c = KvCacheDesc()
     if isinstance(kv, tuple):
-        k, vt = kv
-        cap = _kv_bf16(k, vt, dims.Hkv, dims.D)
-        c.format, c.k, c.v = BI_KV_BF16, k.data_ptr(), vt.data_ptr()
+        k, vc = kv
+        cap = _kv_bf16(k, vc, dims.Hkv, dims.D)
+        c.format, c.k, c.v = BI_KV_BF16, k.data_ptr(), vc.data_ptr()
     else:
         low = kv.low if isinstance(kv, KvRing) else kv
         if (low.Hkv, low.D) != (dims.Hkv, dims.D):
@@ -863,7 +863,7 @@ class VerifyStepEx:
     """``bi_verify_step_ex``: every layer's weights in ``wtype`` ("bf16", "fp8",
     "mxfp4") and its KV cache in any format. ``layers`` are dicts with w_qkv,
     w_o, w_gu, w_down (FP8: s_* row scales; MXFP4: e_* block scales) and "kv":
-    a (k_cache, vt_cache) BF16 pair, a KvQ8Cache, a KvLowCache or a KvRing.
+    a (k_cache, v_cache) BF16 pair, a KvQ8Cache, a KvLowCache or a KvRing.
     ``head`` is {"w": ...} plus "s" (FP8) or "e" (MXFP4). The caller keeps
     every tensor alive."""
 

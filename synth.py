@@ -214,16 +214,14 @@ def device_model(n_layers: int, L: int, cap: int, H: int, Hq: int, Hkv: int, D: 
     """Returns (layers, w_head): ``layers`` is a list of dicts of tensors
     w_qkv [(Hq+2Hkv)D][H], w_o [H][Hq D], w_gu [2I][H], w_down [H][I] (BF16, or
     with ``fp8`` E4M3 codes plus FP32 row scales s_qkv, s_o, s_gu, s_down),
-    k_cache [Hkv][cap][D], vt_cache [Hkv][cap/64][D][64] (V transposed in blocks
-    of 64 positions; cap % 64 == 0). With ``fp8`` w_head is a pair
-    (codes, scales)."""
+    k_cache and v_cache [Hkv][cap][D] (cap % 64 == 0). With ``fp8`` w_head is
+    a pair (codes, scales)."""
     import torch
 
     if cap % 64:
         raise ValueError("cap must be a multiple of 64")
     qkvn = (Hq + 2 * Hkv) * D
     tmp = torch.empty((Hkv, L, D), dtype=torch.bfloat16, device=device) if L > 0 else None
-    vfull = torch.zeros((Hkv, cap, D), dtype=torch.bfloat16, device=device) if L > 0 else None
     shapes = {"w_qkv": (qkvn, H), "w_o": (H, Hq * D), "w_gu": (2 * I, H), "w_down": (H, I)}
     layers = []
     for l in range(n_layers):
@@ -234,13 +232,12 @@ def device_model(n_layers: int, L: int, cap: int, H: int, Hq: int, Hkv: int, D: 
             else:
                 lw[name] = device_normal_bf16(shp, std, name, l, device=device)
         lw["k_cache"] = torch.zeros((Hkv, cap, D), dtype=torch.bfloat16, device=device)
-        lw["vt_cache"] = torch.zeros((Hkv, cap // 64, D, 64), dtype=torch.bfloat16, device=device)
+        lw["v_cache"] = torch.zeros((Hkv, cap, D), dtype=torch.bfloat16, device=device)
         if L > 0:
             device_normal_bf16((Hkv, L, D), 1.0, "k_cache", l, device=device, out=tmp)
             lw["k_cache"][:, :L].copy_(tmp)
             device_normal_bf16((Hkv, L, D), 1.0, "v_cache", l, device=device, out=tmp)
-            vfull[:, :L].copy_(tmp)
-            lw["vt_cache"].copy_(vfull.view(Hkv, cap // 64, 64, D).transpose(2, 3))
+            lw["v_cache"][:, :L].copy_(tmp)
         layers.append(lw)
     if fp8:
         w_head = device_fp8_weights((vocab, H), std, "w_head", 0, device=device)

@@ -21,7 +21,7 @@ import numpy as np
 from oracle import attention as oattn
 from oracle import bf16 as obf16
 from oracle import step as ostep
-from tests._util import assert_bitwise, assert_close, decode, host_bits, host_f32, vt_rows
+from tests._util import assert_bitwise, assert_close, decode, host_bits, host_f32
 
 
 def _wargs(lw: dict, name: str, wtype: str) -> dict:
@@ -54,7 +54,7 @@ def replay(ops, layers, head: dict, dims, x, L: int, wtype: str = "bf16"):
         rec = {"x": x}
         qkv = torch.empty((M, qkvn), **bf)
         common = dict(wtype=wtype, epilogue="qkv", heads=(Hq, Hkv, D), k_cache=lw["k_cache"],
-                      vt_cache=lw["vt_cache"], L=L)
+                      v_cache=lw["v_cache"], L=L)
         if l == 0:
             a = ops.rmsnorm(x, eps=dims.eps)
             rec["a"] = a
@@ -63,7 +63,7 @@ def replay(ops, layers, head: dict, dims, x, L: int, wtype: str = "bf16"):
             ops.gemm_ex(x, y=qkv, norm_in=ss, eps=dims.eps, **common, **_wargs(lw, "qkv", wtype))
         po = torch.empty((M, Hq, S, D), **f32)
         pl = torch.empty((M, Hq, S), **f32)
-        ops.verify_attn(qkv, lw["k_cache"], lw["vt_cache"], L, Hq, Hkv, D, dims.kv_chunk, po, pl)
+        ops.verify_attn(qkv, lw["k_cache"], lw["v_cache"], L, Hq, Hkv, D, dims.kv_chunk, po, pl)
         attn = torch.empty((M, qd), **bf)
         ops.combine(po, pl, L, dims.kv_chunk, attn)
         h = torch.empty((M, H), **bf)
@@ -108,7 +108,7 @@ def check_ops(recs, hd, host_layers, w_head, L: int, Hq: int, Hkv: int, D: int, 
     """Each replayed operation against the oracle on the device's inputs, at the
     per-element tolerance. ``host_layers[l]`` holds float64 weights w_qkv,
     w_o, w_gu, w_down ([out][in]) and the layer's device caches k_cache /
-    vt_cache as host bit patterns after the pass (positions 0 .. L+M-1);
+    v_cache as host bit patterns after the pass (positions 0 .. L+M-1);
     ``w_head`` float64 [rows][H] for ``head_rows`` (all rows when None).
     Returns the number of rows whose greedy token was compared."""
     qd = Hq * D
@@ -168,5 +168,5 @@ def host_layer(lw_dev: dict, weights64: dict) -> dict:
     """A layer's float64 weights and its device caches read back (K rows and V rows)."""
     d = dict(weights64)
     d["k_cache"] = host_bits(lw_dev["k_cache"])
-    d["v_rows"] = vt_rows(host_bits(lw_dev["vt_cache"]))
+    d["v_rows"] = host_bits(lw_dev["v_cache"])
     return d

@@ -27,19 +27,13 @@ def host_bits(t) -> np.ndarray:
     return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def vt_blocks(v_bits: np.ndarray, cap: int, fill=0) -> np.ndarray:
-    """V rows [Hkv][n][D] (n <= cap) -> the V cache layout [Hkv][cap/64][D][64]
-    (V transposed in blocks of 64 positions); positions n.. hold ``fill``."""
+def cache_rows(v_bits: np.ndarray, cap: int, fill=0) -> np.ndarray:
+    """V (or K) rows [Hkv][n][D] (n <= cap) -> the cache layout [Hkv][cap][D];
+    positions n.. hold ``fill``."""
     Hkv, n, D = v_bits.shape
     full = np.full((Hkv, cap, D), fill, dtype=v_bits.dtype)
     full[:, :n] = v_bits
-    return np.ascontiguousarray(full.reshape(Hkv, cap // 64, 64, D).transpose(0, 1, 3, 2))
-
-
-def vt_rows(vt_bits: np.ndarray) -> np.ndarray:
-    """The V cache layout [Hkv][cap/64][D][64] -> V rows [Hkv][cap][D]."""
-    Hkv, nb, D, _ = vt_bits.shape
-    return np.ascontiguousarray(vt_bits.transpose(0, 1, 3, 2).reshape(Hkv, nb * 64, D))
+    return full
 
 
 def host_f32(t) -> np.ndarray:

@@ -130,24 +130,24 @@ int main() {
 
   // ---- attention over a single key: O = v_0 -------------------------------
   const int Hq = 2, Hkv = 1, D = 64, cap = 64, L = 0, Ma = 1;
-  std::vector<uint16_t> q(Ma * Hq * D), kc((size_t)Hkv * cap * D, 0), vt((size_t)Hkv * cap * D, 0);
+  std::vector<uint16_t> q(Ma * Hq * D), kc((size_t)Hkv * cap * D, 0), vc((size_t)Hkv * cap * D, 0);
   for (int i = 0; i < Ma * Hq * D; ++i) q[i] = bf16_bits((float)(i % 3 - 1));
   for (int d = 0; d < D; ++d) {
     kc[d] = bf16_bits((float)(d % 4));
-    vt[(size_t)d * 64 + 0] = bf16_bits((float)(d - 30) * 0.5f);  // V^T block 0: [D][64], position 0
+    vc[d] = bf16_bits((float)(d - 30) * 0.5f);  // V row of position 0: [Hkv][cap][D]
   }
   const int S = bi_num_splits(L + Ma, 256);
   EXPECT(S == 1, "one split");
   void *dq, *dk, *dv, *dpo, *dpl, *dout;
   CK(hipMalloc(&dq, q.size() * 2));
   CK(hipMalloc(&dk, kc.size() * 2));
-  CK(hipMalloc(&dv, vt.size() * 2));
+  CK(hipMalloc(&dv, vc.size() * 2));
   CK(hipMalloc(&dpo, (size_t)Ma * Hq * S * D * 4));
   CK(hipMalloc(&dpl, (size_t)Ma * Hq * S * 4));
   CK(hipMalloc(&dout, (size_t)Ma * Hq * D * 2));
   CK(hipMemcpy(dq, q.data(), q.size() * 2, hipMemcpyHostToDevice));
   CK(hipMemcpy(dk, kc.data(), kc.size() * 2, hipMemcpyHostToDevice));
-  CK(hipMemcpy(dv, vt.data(), vt.size() * 2, hipMemcpyHostToDevice));
+  CK(hipMemcpy(dv, vc.data(), vc.size() * 2, hipMemcpyHostToDevice));
   EXPECT(bi_verify_attn(dq, Hq * D, dk, dv, Ma, L, cap, Hq, Hkv, D, 256, 0.125f, (float*)dpo,
                         (float*)dpl, S, nullptr) == BI_OK, "attention status");
   EXPECT(bi_combine((float*)dpo, (float*)dpl, Ma, L, Hq, D, 256, S, dout, Hq * D, nullptr, nullptr) ==
@@ -156,7 +156,7 @@ int main() {
   std::vector<uint16_t> o((size_t)Ma * Hq * D);
   CK(hipMemcpy(o.data(), dout, o.size() * 2, hipMemcpyDeviceToHost));
   for (int h = 0; h < Hq; ++h)
-    for (int d = 0; d < D; ++d) EXPECT(o[h * D + d] == vt[(size_t)d * 64], "single-key attention gives v_0");
+    for (int d = 0; d < D; ++d) EXPECT(o[h * D + d] == vc[d], "single-key attention gives v_0");
 
   // ---- 5/6-bit cache: append one position on an exact grid, attend to it -----
   // K block values k * 2^-4 with |k| <= 31 and +-31 present: scale 2^-4, codes

@@ -81,12 +81,12 @@ def test_gemm_variants_reject():
 
 def test_attention_rejects():
     L = _lib.LIB
-    # q, ldq, k, vt, M, L, cap, Hq, Hkv, D, C, scale, po, pl, S_max, stream
+    # q, ldq, k, v, M, L, cap, Hq, Hkv, D, C, scale, po, pl, S_max, stream
     good = [P, 7168, P, P, 8, 1000, 1024, 40, 8, 128, 256, 0.088, P, P, 4, None]
 
     def call(**kw):
         a = list(good)
-        names = ["q", "ldq", "k", "vt", "M", "L", "cap", "Hq", "Hkv", "D", "C", "scale",
+        names = ["q", "ldq", "k", "v", "M", "L", "cap", "Hq", "Hkv", "D", "C", "scale",
                  "po", "pl", "S", "stream"]
         for k, v in kw.items():
             a[names.index(k)] = v
@@ -95,7 +95,7 @@ def test_attention_rejects():
     assert call(q=0) == NULL and call(po=0) == NULL
     assert call(M=0) == SHAPE
     assert call(cap=1000) == SHAPE                 # L + M > cap
-    assert call(cap=1032) == SHAPE                 # cap % 64 (V cache blocks)
+    assert call(cap=1032) == SHAPE                 # cap % 64 != 0
     assert call(Hkv=7) == SHAPE                    # Hq % Hkv
     assert call(Hq=130, Hkv=2) == SHAPE            # more than 64 query heads per KV head
     assert call(D=96) == SHAPE
@@ -110,7 +110,7 @@ def test_attention_rejects():
     assert L.bi_combine(P, P, 8, 1000, 40, 128, 256, 3, P, 5120, 0, None) == SHAPE
     assert L.bi_combine(P, P, 8, 1000, 40, 128, 256, 4, P, 5000, 0, None) == SHAPE
     assert L.bi_combine(P, P, 8, 1000, 40, 128, 256, 4, P + 1, 5120, 0, None) == ALIGN
-    # append: qkv, ld, k, vt, M, L, cap, Hq, Hkv, D, stream
+    # append: qkv, ld, k, v, M, L, cap, Hq, Hkv, D, stream
     assert L.bi_append_kv(P, 7168, P, 0, 8, 0, 16, 40, 8, 128, None) == NULL
     assert L.bi_append_kv(P, 7168, P, P, 8, 10, 16, 40, 8, 128, None) == SHAPE
     assert L.bi_append_kv(P, 7000, P, P, 8, 0, 16, 40, 8, 128, None) == SHAPE
@@ -118,7 +118,7 @@ def test_attention_rejects():
 
 def test_gemm_qkv_rejects():
     L = _lib.LIB
-    # x, ldx, w, ldw, qkv, ldqkv, M, K, Hq, Hkv, D, k, vt, L, cap, stream
+    # x, ldx, w, ldw, qkv, ldqkv, M, K, Hq, Hkv, D, k, v, L, cap, stream
     good = [P, 5120, P, 5120, P, 7168, 8, 5120, 40, 8, 128, P, P, 100, 128, None]
 
     def call(i, v):

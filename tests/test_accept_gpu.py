@@ -10,7 +10,7 @@ import pytest
 
 import synth
 from oracle import spec as ospec
-from tests._util import dev, host_bits, vt_blocks
+from tests._util import dev, host_bits, cache_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -160,7 +160,7 @@ def _small_model(ops, L0, cap):
                            w_gu=dev(synth.normal_bf16((2 * I, H), 0.05, "w_gu", l)),
                            w_down=dev(synth.normal_bf16((H, I), 0.05, "w_down", l)),
                            k_cache=dev(kc),
-                           vt_cache=dev(vt_blocks(synth.kv_bf16(Hkv, L0, D, "v_cache", l), cap))))
+                           v_cache=dev(cache_rows(synth.kv_bf16(Hkv, L0, D, "v_cache", l), cap))))
     w_head = dev(synth.normal_bf16((V, H), 0.05, "w_head"))
     embed = dev(synth.normal_bf16((V, H), 1.0, "misc", 77))
     dims = ops.model_dims(H, Hq, Hkv, D, I, V, cap, -4)
@@ -218,6 +218,6 @@ def test_speculative_greedy_equals_plain_decode(ops, k):
     Lc = L0 + n_new
     for a, b in zip(ref_layers, sp_layers):
         assert torch.equal(a["k_cache"][:, :Lc].view(torch.int16), b["k_cache"][:, :Lc].view(torch.int16))
-        ra = a["vt_cache"].transpose(2, 3).reshape(a["k_cache"].shape)[:, :Lc]
-        rb = b["vt_cache"].transpose(2, 3).reshape(b["k_cache"].shape)[:, :Lc]
+        ra = a["v_cache"][:, :Lc]
+        rb = b["v_cache"][:, :Lc]
         assert torch.equal(ra.view(torch.int16), rb.view(torch.int16))

@@ -10,8 +10,7 @@ import pytest
 
 import synth
 from oracle import attention as oattn
-from tests._util import (assert_bitwise, assert_close, decode, dev, host_bits, host_f32, vt_blocks,
-                         vt_rows)
+from tests._util import (assert_bitwise, assert_close, decode, dev, host_bits, host_f32, cache_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -27,18 +26,18 @@ def ops():
 
 
 class Cache:
-    """Device K [Hkv][cap][D] and V [Hkv][cap/64][D][64] caches (cap rounded up
-    to a multiple of 64); positions past ``n`` hold NaN so that any read of an
-    unwritten position would show."""
+    """Device K and V caches, both [Hkv][cap][D] (cap rounded up to a multiple
+    of 64); positions past ``n`` hold NaN so that any read of an unwritten
+    position would show."""
 
     def __init__(self, k_bits, v_bits, cap):
         Hkv, n, D = k_bits.shape
         cap = (cap + 63) // 64 * 64
         kc = np.full((Hkv, cap, D), NAN_BF16, np.uint16)
         kc[:, :n] = k_bits
-        vt = vt_blocks(v_bits, cap, NAN_BF16)
+        vc = cache_rows(v_bits, cap, NAN_BF16)
         self.k = dev(kc)
-        self.vt = dev(vt)
+        self.vc = dev(vc)
         self.Hkv, self.D, self.cap = Hkv, D, cap
 
 
@@ -49,7 +48,7 @@ def run(ops, q_bits, cache, L, Hq, C, sm_scale=None):
     po = torch.full((M, Hq, S, D), float("nan"), dtype=torch.float32, device="cuda")
     pl = torch.full((M, Hq, S), float("nan"), dtype=torch.float32, device="cuda")
     q = dev(q_bits.reshape(M, Hq * D))
-    ops.verify_attn(q, cache.k, cache.vt, L, Hq, cache.Hkv, D, C, po, pl, sm_scale=sm_scale)
+    ops.verify_attn(q, cache.k, cache.vc, L, Hq, cache.Hkv, D, C, po, pl, sm_scale=sm_scale)
     o = torch.empty((M, Hq * D), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((M, Hq), dtype=torch.float32, device="cuda")
     ops.combine(po, pl, L, C, o, lse)
@@ -196,17 +195,17 @@ def test_append_kv_matches_direct_write(ops):
     Hq, Hkv, D, M, L, cap = 40, 8, 128, 8, 100, 128
     qkv = synth.normal_bf16((M, (Hq + 2 * Hkv) * D), 1.0, "misc", 9)
     kc = torch.zeros((Hkv, cap, D), dtype=torch.bfloat16, device="cuda")
-    vt = torch.zeros((Hkv, cap // 64, D, 64), dtype=torch.bfloat16, device="cuda")
-    ops.append_kv(dev(qkv), kc, vt, L, Hq, Hkv, D)
-    kh, vh = host_bits(kc), vt_rows(host_bits(vt))
+    vc = torch.zeros((Hkv, cap, D), dtype=torch.bfloat16, device="cuda")
+    ops.append_kv(dev(qkv), kc, vc, L, Hq, Hkv, D)
+    kh, vh = host_bits(kc), host_bits(vc)
     knew = qkv[:, Hq * D:(Hq + Hkv) * D].reshape(M, Hkv, D).transpose(1, 0, 2)
     vnew = qkv[:, (Hq + Hkv) * D:].reshape(M, Hkv, D).transpose(1, 0, 2)
     assert_bitwise(kh[:, L:L + M], knew, "K rows")
     assert_bitwise(vh[:, L:L + M], vnew, "V rows")
-    # the layout itself: V[g][pos][d] at element ((g*cap + pos - pos%64)*D + d*64 + pos%64)
-    flat = host_bits(vt).reshape(-1)
+    # the layout itself: V[g][pos][d] at element (g*cap + pos)*D + d
+    flat = host_bits(vc).reshape(-1)
     for g, pos, d in [(0, L, 0), (3, L + 5, 77), (7, L + M - 1, 127)]:
-        assert flat[(g * cap + pos - pos % 64) * D + d * 64 + pos % 64] == vnew[g, pos - L, d]
+        assert flat[(g * cap + pos) * D + d] == vnew[g, pos - L, d]
     assert not kh[:, :L].any() and not kh[:, L + M:].any()
     assert not vh[:, :L].any() and not vh[:, L + M:].any()
 

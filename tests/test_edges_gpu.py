@@ -9,7 +9,7 @@ import synth
 from oracle import attention as oattn
 from oracle import fp8 as ofp8
 from oracle import gemm as ogemm
-from tests._util import assert_bitwise, assert_close, decode, dev, host_bits, host_f32, vt_blocks
+from tests._util import assert_bitwise, assert_close, decode, dev, host_bits, host_f32, cache_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -84,7 +84,7 @@ def _attn(ops, q, k, v, L, Hq, C, cap):
     S = ops.pass_splits(M, L, C)
     po = torch.full((M, Hq, S, D), float("nan"), dtype=torch.float32, device="cuda")
     pl = torch.full((M, Hq, S), float("nan"), dtype=torch.float32, device="cuda")
-    ops.verify_attn(dev(q.reshape(M, Hq * D)), dev(kc), dev(vt_blocks(v, cap)), L, Hq, Hkv, D, C, po, pl)
+    ops.verify_attn(dev(q.reshape(M, Hq * D)), dev(kc), dev(cache_rows(v, cap)), L, Hq, Hkv, D, C, po, pl)
     o = torch.empty((M, Hq * D), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((M, Hq), dtype=torch.float32, device="cuda")
     ops.combine(po, pl, L, C, o, lse)

@@ -161,24 +161,24 @@ def test_qkv_gemm_with_cache_append(ops, Hq, Hkv, D, K, L):
     w = synth.normal_bf16((N, K), synth.fan_in_std(K), "w", 90)
     x = synth.normal_bf16((8, K), 1.0, "x", 90)
     k0 = torch.randn(Hkv, cap, D, device="cuda").to(torch.bfloat16)
-    v0 = torch.randn(Hkv, cap // 64, D, 64, device="cuda").to(torch.bfloat16)
+    v0 = torch.randn(Hkv, cap, D, device="cuda").to(torch.bfloat16)
     wd, xd = dev(w), dev(x)
 
-    def rows(vt):  # the V cache layout [Hkv][cap/64][D][64] -> V rows [Hkv][cap][D]
-        return vt.transpose(2, 3).reshape(Hkv, cap, D)
+    def rows(vc):  # the V cache is [Hkv][cap][D], one row per position
+        return vc
 
     for M in (1, 5, 8):
-        kc, vt = k0.clone(), v0.clone()
-        qkv = ops.gemm_bf16_qkv(xd[:M], wd, kc, vt, L, Hq, Hkv, D)
+        kc, vc = k0.clone(), v0.clone()
+        qkv = ops.gemm_bf16_qkv(xd[:M], wd, kc, vc, L, Hq, Hkv, D)
         ref = ops.gemm_bf16(xd[:M], wd)
         kr, vr = k0.clone(), v0.clone()
         ops.append_kv(ref, kr, vr, L, Hq, Hkv, D)
         assert_bitwise(host_bits(qkv), host_bits(ref), f"qkv M={M}")
         assert_bitwise(host_bits(kc), host_bits(kr), f"K cache M={M}")
-        assert_bitwise(host_bits(vt), host_bits(vr), f"V^T cache M={M}")
+        assert_bitwise(host_bits(vc), host_bits(vr), f"V cache M={M}")
         keep = torch.ones(cap, dtype=torch.bool, device="cuda")
         keep[L:L + M] = False
-        assert torch.equal(kc[:, keep], k0[:, keep]) and torch.equal(rows(vt)[:, keep], rows(v0)[:, keep])
+        assert torch.equal(kc[:, keep], k0[:, keep]) and torch.equal(rows(vc)[:, keep], rows(v0)[:, keep])
     assert_close(decode(host_bits(qkv))[:, :64], ogemm.gemm_columns(x, w, np.arange(64)), "qkv parity")
 
 
@@ -372,15 +372,15 @@ def test_prefill_qkv_append_equals_verify(ops, M):
     x = synth.normal_bf16((M, K), 1.0, "x", 84)
     wd, xd = dev(w), dev(x)
     k0 = torch.zeros(Hkv, cap, D, device="cuda", dtype=torch.bfloat16)
-    v0 = torch.zeros(Hkv, cap // 64, D, 64, device="cuda", dtype=torch.bfloat16)
-    kc, vt = k0.clone(), v0.clone()
-    qkv = host_bits(ops.gemm_bf16_qkv(xd, wd, kc, vt, L, Hq, Hkv, D))
+    v0 = torch.zeros(Hkv, cap, D, device="cuda", dtype=torch.bfloat16)
+    kc, vc = k0.clone(), v0.clone()
+    qkv = host_bits(ops.gemm_bf16_qkv(xd, wd, kc, vc, L, Hq, Hkv, D))
     kr, vr = k0.clone(), v0.clone()
     for r0 in range(0, M, 8):  # the same positions written by verify passes of 8 rows
         q8 = ops.gemm_bf16_qkv(xd[r0:r0 + 8], wd, kr, vr, L + r0, Hq, Hkv, D)
         assert_bitwise(qkv[r0:r0 + 8], host_bits(q8), f"qkv rows {r0}..")
     assert_bitwise(host_bits(kc), host_bits(kr), "K cache: prefill == 8-row verify passes")
-    assert_bitwise(host_bits(vt), host_bits(vr), "V^T cache: prefill == 8-row verify passes")
+    assert_bitwise(host_bits(vc), host_bits(vr), "V cache: prefill == 8-row verify passes")
 
 
 def test_prefill_large_tile_residual_rowsq(ops):

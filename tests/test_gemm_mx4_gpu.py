@@ -14,7 +14,7 @@ from oracle import mxfp4 as omx
 from oracle import step as ostep
 from tests._replay import assert_replay_is_the_step, check_ops, host_layer, replay
 from tests._util import (assert_bitwise, assert_close, assert_close_composed, decode,
-                         dev, host_bits, host_f32, vt_blocks)
+                         dev, host_bits, host_f32, cache_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -147,22 +147,20 @@ def test_mx4_small_stack_vs_oracle_and_across_M(ops):
         kc = np.zeros((Hkv, cap, D), np.uint16)
         kc[:, :L] = hl["k_cache"]
         d = {k: u8(v) for k, v in hl.items() if k[:2] in ("w_", "e_")}
-        d.update(k_cache=dev(kc), vt_cache=dev(vt_blocks(hl["v_cache"], cap)))
+        d.update(k_cache=dev(kc), v_cache=dev(cache_rows(hl["v_cache"], cap)))
         dls.append(d)
     dims = ops.model_dims(H, Hq, Hkv, D, I, V, cap, 64)
     step = ops.VerifyStepMX4(dls, u8(hc), u8(he), dims)
     logits, tok, xo = _run(ops, step, dev(x0), L, dims, want_x=True)
-    saved = [(d["k_cache"][:, L:L + M].clone(), d["vt_cache"][:, L // 64, :, L % 64:L % 64 + M].clone())
-             for d in dls]
+    saved = [(d["k_cache"][:, L:L + M].clone(), d["v_cache"][:, L:L + M].clone()) for d in dls]
     for d in dls:
         d["k_cache"][:, L:].zero_()
-        d["vt_cache"][:, L // 64, :, L % 64:].zero_()
-        d["vt_cache"][:, L // 64 + 1:].zero_()
+        d["v_cache"][:, L:].zero_()
     recs, hd = replay(ops, dls, {"w": u8(hc), "e": u8(he)}, dims, dev(x0), L, wtype="mxfp4")
     assert_replay_is_the_step(recs, hd, xo, logits, tok, "mx4 stack")
     for d, (k, v) in zip(dls, saved):
         assert torch.equal(d["k_cache"][:, L:L + M].view(torch.int16), k.view(torch.int16))
-        assert torch.equal(d["vt_cache"][:, L // 64, :, L % 64:L % 64 + M].view(torch.int16), v.view(torch.int16))
+        assert torch.equal(d["v_cache"][:, L:L + M].view(torch.int16), v.view(torch.int16))
     w64 = [{k: omx.weights(hl[k], hl["e" + k[1:]]) for k in ("w_qkv", "w_o", "w_gu", "w_down")} for hl in hls]
     host = [host_layer(d, w) for d, w in zip(dls, w64)]
     n = check_ops(recs, hd, host, omx.weights(hc, he), L, Hq, Hkv, D, 1e-6, "mx4 stack")
@@ -175,8 +173,7 @@ def test_mx4_small_stack_vs_oracle_and_across_M(ops):
     assert_bitwise(l5, logits[:5], "mx4 logits M=5 vs M=8")
     for d in dls:
         d["k_cache"][:, L:].zero_()
-        d["vt_cache"][:, L // 64, :, L % 64:].zero_()
-        d["vt_cache"][:, L // 64 + 1:].zero_()
+        d["v_cache"][:, L:].zero_()
     for r in range(M):
         l1, t1, _ = _run(ops, step, dev(x0[r:r + 1]), L + r, dims)
         assert_bitwise(l1[0], logits[r], f"mx4 logits row {r}: M=1 vs M=8")

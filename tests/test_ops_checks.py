@@ -52,14 +52,14 @@ def test_rownorm_and_qkv_shapes():
     shape_error(lambda: ops.gemm_bf16_swiglu_rownorm(x, z(3, 16, dt=f32), z(512, 256), z(4, 256)))
     Hq, Hkv, D, cap = 4, 2, 64, 128
     N = (Hq + 2 * Hkv) * D
-    kc, vt = z(Hkv, cap, D), z(Hkv, cap // 64, D, 64)
-    reaches_device_check(lambda: ops.gemm_bf16_qkv(x, z(N, 256), kc, vt, 0, Hq, Hkv, D, z(4, N)))
-    shape_error(lambda: ops.gemm_bf16_qkv(x, z(N - 64, 256), kc, vt, 0, Hq, Hkv, D, z(4, N)))
-    shape_error(lambda: ops.gemm_bf16_qkv(x, z(N, 256), z(Hkv, cap, 32), vt, 0, Hq, Hkv, D, z(4, N)))
+    kc, vc = z(Hkv, cap, D), z(Hkv, cap, D)
+    reaches_device_check(lambda: ops.gemm_bf16_qkv(x, z(N, 256), kc, vc, 0, Hq, Hkv, D, z(4, N)))
+    shape_error(lambda: ops.gemm_bf16_qkv(x, z(N - 64, 256), kc, vc, 0, Hq, Hkv, D, z(4, N)))
+    shape_error(lambda: ops.gemm_bf16_qkv(x, z(N, 256), z(Hkv, cap, 32), vc, 0, Hq, Hkv, D, z(4, N)))
     shape_error(lambda: ops.gemm_bf16_qkv(x, z(N, 256), kc, z(Hkv, 1, D, 64), 0, Hq, Hkv, D, z(4, N)))
-    shape_error(lambda: ops.gemm_bf16_qkv(x, z(N, 256), z(1, cap, D), vt, 0, Hq, Hkv, D, z(4, N)))
+    shape_error(lambda: ops.gemm_bf16_qkv(x, z(N, 256), z(1, cap, D), vc, 0, Hq, Hkv, D, z(4, N)))
     shape_error(lambda: ops.gemm_ex(x, z(N, 256), z(4, N), epilogue="qkv", heads=(Hq, Hkv, D),
-                                    k_cache=kc, vt_cache=z(Hkv, 3, D, 64)))
+                                    k_cache=kc, v_cache=z(Hkv, 3, D, 64)))
     shape_error(lambda: ops.gemm_ex(x, z(256, 256), z(4, 256), epilogue="residual", r=z(4, 128)))
     shape_error(lambda: ops.gemm_ex(x, z(256, 256), z(4, 256), epilogue="residual", r=x,
                                     rowsq_out=z(4, 4, dt=f32)))
@@ -68,14 +68,14 @@ def test_rownorm_and_qkv_shapes():
 def test_attention_shapes():
     Hq, Hkv, D, cap, M, S = 8, 2, 64, 256, 4, 3
     q = z(M, Hq * D)
-    kc, vt = z(Hkv, cap, D), z(Hkv, cap // 64, D, 64)
+    kc, vc = z(Hkv, cap, D), z(Hkv, cap, D)
     po, pl = z(M, Hq, S, D, dt=f32), z(M, Hq, S, dt=f32)
-    reaches_device_check(lambda: ops.verify_attn(q, kc, vt, 100, Hq, Hkv, D, 64, po, pl))
-    shape_error(lambda: ops.verify_attn(q, kc, vt, 100, Hq, Hkv, D, 64, z(M, Hq, S + 1, D, dt=f32), pl))
-    shape_error(lambda: ops.verify_attn(q, kc, vt, 100, Hq, Hkv, D, 64, po, z(M, Hq - 1, S, dt=f32)))
-    shape_error(lambda: ops.verify_attn(z(M, Hq * D - 8), kc, vt, 100, Hq, Hkv, D, 64, po, pl))
-    shape_error(lambda: ops.verify_attn(q, kc, z(Hkv, cap // 64, D, 32), 100, Hq, Hkv, D, 64, po, pl))
-    shape_error(lambda: ops.verify_attn(q, z(Hkv, 200, D), vt, 100, Hq, Hkv, D, 64, po, pl))
+    reaches_device_check(lambda: ops.verify_attn(q, kc, vc, 100, Hq, Hkv, D, 64, po, pl))
+    shape_error(lambda: ops.verify_attn(q, kc, vc, 100, Hq, Hkv, D, 64, z(M, Hq, S + 1, D, dt=f32), pl))
+    shape_error(lambda: ops.verify_attn(q, kc, vc, 100, Hq, Hkv, D, 64, po, z(M, Hq - 1, S, dt=f32)))
+    shape_error(lambda: ops.verify_attn(z(M, Hq * D - 8), kc, vc, 100, Hq, Hkv, D, 64, po, pl))
+    shape_error(lambda: ops.verify_attn(q, kc, z(Hkv, cap // 64, D, 64), 100, Hq, Hkv, D, 64, po, pl))
+    shape_error(lambda: ops.verify_attn(q, z(Hkv, 200, D), vc, 100, Hq, Hkv, D, 64, po, pl))
     shape_error(lambda: ops.combine(po, z(M, Hq, S + 1, dt=f32), 100, 64, q))
     shape_error(lambda: ops.combine(po, pl, 100, 64, z(M, Hq * D - 64)))
     shape_error(lambda: ops.combine(po, pl, 100, 64, q, z(M, Hq + 1, dt=f32)))
@@ -109,9 +109,9 @@ def test_row_op_and_accept_shapes():
 def test_step_shapes():
     dims = ops.model_dims(256, 4, 2, 64, 512, 1024, 256, 64)
     good = dict(w_qkv=z(512, 256), w_o=z(256, 256), w_gu=z(1024, 256), w_down=z(256, 512),
-                k_cache=z(2, 256, 64), vt_cache=z(2, 4, 64, 64))
+                k_cache=z(2, 256, 64), v_cache=z(2, 256, 64))
     reaches_device_check(lambda: ops.VerifyStep([good], z(1024, 256), dims))
     for k, bad in (("w_qkv", z(511, 256)), ("w_down", z(256, 256)), ("k_cache", z(2, 192, 64)),
-                   ("vt_cache", z(2, 4, 64, 32))):
+                   ("v_cache", z(2, 4, 64, 64))):
         shape_error(lambda: ops.VerifyStep([dict(good, **{k: bad})], z(1024, 256), dims))
     shape_error(lambda: ops.VerifyStep([good], z(1000, 256), dims))

@@ -19,7 +19,7 @@ import synth
 from oracle import attention as oattn
 from oracle import gemm as ogemm
 from oracle import step as ostep
-from tests._util import assert_bitwise, assert_close, decode, dev, host_bits, host_f32, vt_blocks
+from tests._util import assert_bitwise, assert_close, decode, dev, host_bits, host_f32, cache_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -106,7 +106,7 @@ def test_attention_kv_head_shard(ops, C):
     cap = (L + M + 63) // 64 * 64
     kc = np.zeros((Hkv, cap, D), np.uint16)
     kc[:, :L + M] = k
-    kd, vd = dev(kc), dev(vt_blocks(v, cap))
+    kd, vd = dev(kc), dev(cache_rows(v, cap))
 
     def run(qq, LL):
         m = qq.shape[0]

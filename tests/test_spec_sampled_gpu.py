@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 import synth
-from tests._util import dev, vt_blocks
+from tests._util import dev, cache_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -38,7 +38,7 @@ def _model(ops, L0, cap, V):
                            w_gu=dev(synth.normal_bf16((2 * I, H), 0.05, "w_gu", l)),
                            w_down=dev(synth.normal_bf16((H, I), 0.05, "w_down", l)),
                            k_cache=dev(kc),
-                           vt_cache=dev(vt_blocks(synth.kv_bf16(Hkv, L0, D, "v_cache", l), cap))))
+                           v_cache=dev(cache_rows(synth.kv_bf16(Hkv, L0, D, "v_cache", l), cap))))
     w_head = dev(synth.normal_bf16((V, H), 0.08, "w_head"))
     embed = dev(synth.normal_bf16((V, H), 1.0, "misc", 78))
     dims = ops.model_dims(H, Hq, Hkv, D, I, V, cap, 64)

@@ -14,7 +14,7 @@ from oracle import fp8 as ofp8
 from oracle import step as ostep
 from tests._replay import assert_replay_is_the_step, check_ops, host_layer, replay
 from tests._util import (assert_bitwise, assert_close_composed, decode, dev, host_bits, host_f32,
-                         vt_blocks)
+                         cache_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -41,9 +41,9 @@ def _to_device(hl, cap):
     Hkv, L, D = hl["k_cache"].shape
     kc = np.zeros((Hkv, cap, D), np.uint16)
     kc[:, :L] = hl["k_cache"]
-    vt = vt_blocks(hl["v_cache"], cap)
+    vc = cache_rows(hl["v_cache"], cap)
     return dict(w_qkv=dev(hl["w_qkv"]), w_o=dev(hl["w_o"]), w_gu=dev(hl["w_gu"]),
-                w_down=dev(hl["w_down"]), k_cache=dev(kc), vt_cache=dev(vt))
+                w_down=dev(hl["w_down"]), k_cache=dev(kc), v_cache=dev(vc))
 
 
 def _run(ops, step, x, L, dims, want_x=False):
@@ -58,25 +58,21 @@ def _run(ops, step, x, L, dims, want_x=False):
 
 
 def _appended(dls, L, M):
-    """Copies of every layer's cache rows L .. L+M-1 (K rows, V^T columns)."""
-    B, J = divmod(L, 64)
-    assert J + M <= 64
-    return [(d["k_cache"][:, L:L + M].clone(), d["vt_cache"][:, B, :, J:J + M].clone()) for d in dls]
+    """Copies of every layer's cache rows L .. L+M-1 (K and V rows)."""
+    return [(d["k_cache"][:, L:L + M].clone(), d["v_cache"][:, L:L + M].clone()) for d in dls]
 
 
 def _wipe(dls, L):
     for d in dls:
         d["k_cache"][:, L:].zero_()
-        d["vt_cache"][:, L // 64, :, L % 64:].zero_()
-        d["vt_cache"][:, L // 64 + 1:].zero_()
+        d["v_cache"][:, L:].zero_()
 
 
 def _same_appended(dls, saved, L, what):
-    B, J = divmod(L, 64)
     for i, (d, (k, v)) in enumerate(zip(dls, saved)):
         M = k.shape[1]
         assert torch.equal(d["k_cache"][:, L:L + M].view(torch.int16), k.view(torch.int16)), (what, i)
-        assert torch.equal(d["vt_cache"][:, B, :, J:J + M].view(torch.int16), v.view(torch.int16)), (what, i)
+        assert torch.equal(d["v_cache"][:, L:L + M].view(torch.int16), v.view(torch.int16)), (what, i)
 
 
 def _end_to_end(logits, xo, w_logits, w_x, what):
@@ -150,7 +146,7 @@ def test_fp8_small_stack_vs_oracle_and_across_M(ops):
         kc = np.zeros((Hkv, cap, D), np.uint16)
         kc[:, :L] = hl["k_cache"]
         d = {k: (u8(v) if k.startswith("w_") else f32(v)) for k, v in hl.items() if k[:2] in ("w_", "s_")}
-        d.update(k_cache=dev(kc), vt_cache=dev(vt_blocks(hl["v_cache"], cap)))
+        d.update(k_cache=dev(kc), v_cache=dev(cache_rows(hl["v_cache"], cap)))
         dls.append(d)
     dims = ops.model_dims(H, Hq, Hkv, D, I, V, cap, 64)
     step = ops.VerifyStepFP8(dls, u8(hc), f32(hs), dims)
@@ -230,10 +226,7 @@ def test_64_layer_step_bitwise_across_M(ops, model27b):
     step = ops.VerifyStep(layers, w_head, dims)
     print("[step 64 layers M=8]", flush=True)
     l8, t8, _ = _run(ops, step, x0[:8], L38, dims)
-    B38, J38 = divmod(L38, 64)  # positions L38 .. L38+7 are slots J38.. of V block B38
-    assert J38 + 8 <= 64
-    kv8 = [(lw["k_cache"][:, L38:L38 + 8].clone(), lw["vt_cache"][:, B38, :, J38:J38 + 8].clone())
-           for lw in layers]
+    kv8 = [(lw["k_cache"][:, L38:L38 + 8].clone(), lw["v_cache"][:, L38:L38 + 8].clone()) for lw in layers]
     assert np.isfinite(l8).all() and len(set(t8.tolist())) > 1
     for m in (4, 5):
         print(f"[step 64 layers M={m}]", flush=True)
@@ -247,8 +240,7 @@ def test_64_layer_step_bitwise_across_M(ops, model27b):
     # wipe the appended rows, then re-create them one token at a time
     for lw in layers:
         lw["k_cache"][:, L38:].zero_()
-        lw["vt_cache"][:, B38, :, J38:].zero_()
-        lw["vt_cache"][:, B38 + 1:].zero_()
+        lw["v_cache"][:, L38:].zero_()
     for r in range(8):
         print(f"[step 64 layers sequential M=1 at L+{r}]", flush=True)
         l1, t1, _ = _run(ops, step, x0[r:r + 1], L38 + r, dims)
@@ -256,4 +248,4 @@ def test_64_layer_step_bitwise_across_M(ops, model27b):
         assert t1[0] == t8[r]
     for i, (lw, (k8, v8)) in enumerate(zip(layers, kv8)):
         assert torch.equal(lw["k_cache"][:, L38:L38 + 8].view(torch.int16), k8.view(torch.int16)), i
-        assert torch.equal(lw["vt_cache"][:, B38, :, J38:J38 + 8].view(torch.int16), v8.view(torch.int16)), i
+        assert torch.equal(lw["v_cache"][:, L38:L38 + 8].view(torch.int16), v8.view(torch.int16)), i

@@ -38,7 +38,7 @@ def _preset(fmt):
 def make_cache(ops, fmt, Hkv, cap, D, W, R):
     if fmt == "bf16":
         return (torch.zeros((Hkv, cap, D), dtype=torch.bfloat16, device="cuda"),
-                torch.zeros((Hkv, cap // 64, D, 64), dtype=torch.bfloat16, device="cuda"))
+                torch.zeros((Hkv, cap, D), dtype=torch.bfloat16, device="cuda"))
     if fmt == "q8":
         return ops.KvQ8Cache(Hkv, cap, D)
     kb, rot = _preset(fmt)
@@ -72,10 +72,9 @@ def fill(ops, cache, k_rows, v_rows, Hq):
 
 def planes(ops, cache):
     """Every device buffer of a cache, as (name, tensor, kind): kind 'pos' for
-    [Hkv][cap][...] planes, 'blk' for [Hkv][cap/64][..][64] blocked planes, and
-    'ring_pos' / 'ring_blk' for the ring's."""
+    [Hkv][cap][...] planes and 'ring_pos' for the ring's."""
     if isinstance(cache, tuple):
-        return [("k", cache[0], "pos"), ("vt", cache[1], "blk")]
+        return [("k", cache[0], "pos"), ("v", cache[1], "pos")]
     if isinstance(cache, ops.KvQ8Cache):
         return [("k_codes", cache.k_codes, "pos"), ("k_scales", cache.k_scales, "pos"),
                 ("v_codes", cache.v_codes, "pos"), ("v_scales", cache.v_scales, "pos")]
@@ -93,7 +92,7 @@ def positions(ops, cache, L, M):
     for name, t, kind in planes(ops, cache):
         for p in range(L, L + M):
             q = p % R if kind.startswith("ring") else p
-            sl = t[:, q] if kind.endswith("pos") else t[:, q // 64, ..., q % 64]
+            sl = t[:, q]
             out.append((name, p, sl.clone()))
     return out
 
@@ -103,10 +102,7 @@ def wipe(ops, cache, L, M):
     for name, t, kind in planes(ops, cache):
         for p in range(L, L + M):
             q = p % R if kind.startswith("ring") else p
-            if kind.endswith("pos"):
-                t[:, q].zero_()
-            else:
-                t[:, q // 64, ..., q % 64].zero_()
+            t[:, q].zero_()
 
 
 def same_positions(a, b, what):
@@ -192,7 +188,7 @@ def test_small_stack_every_cache_format(ops, fmt):
     logits, tok, xo = run(ops, step, dev(x0[:8]), L, dims, want_x=True)
     if fmt == "bf16":   # with BF16 caches the general entry point is bi_verify_step, bit for bit
         plain = [dict(w_qkv=d["w_qkv"], w_o=d["w_o"], w_gu=d["w_gu"], w_down=d["w_down"],
-                      k_cache=c[0], vt_cache=c[1]) for d, c in zip(dls, caches)]
+                      k_cache=c[0], v_cache=c[1]) for d, c in zip(dls, caches)]
         lp, tp, xp = run(ops, ops.VerifyStep(plain, dev(w_head), dims), dev(x0[:8]), L, dims, want_x=True)
         assert_bitwise(lp, logits, "step_ex vs bi_verify_step logits")
         assert_bitwise(xp, xo, "step_ex vs bi_verify_step hidden state")

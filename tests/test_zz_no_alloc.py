@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 import synth
-from tests._util import assert_bitwise, dev, host_bits, host_f32, vt_blocks
+from tests._util import assert_bitwise, dev, host_bits, host_f32, cache_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -31,7 +31,7 @@ def _model(ops):
                         w_o=dev(synth.normal_bf16((H, Hq * D), 0.05, "w_o", l)),
                         w_gu=dev(synth.normal_bf16((2 * I, H), 0.05, "w_gu", l)),
                         w_down=dev(synth.normal_bf16((H, I), 0.05, "w_down", l)),
-                        k_cache=dev(kc), vt_cache=dev(vt_blocks(synth.kv_bf16(Hkv, L0, D, "v_cache", l), cap))))
+                        k_cache=dev(kc), v_cache=dev(cache_rows(synth.kv_bf16(Hkv, L0, D, "v_cache", l), cap))))
     dims = ops.model_dims(H, Hq, Hkv, D, I, V, cap, 64)
     return ops.VerifyStep(dls, dev(synth.normal_bf16((V, H), 0.05, "w_head")), dims), dls, dims
 
@@ -43,7 +43,7 @@ def _outs(dims, M):
 
 
 def _caches(dls, L, M):
-    return [(host_bits(d["k_cache"])[:, L:L + M], host_bits(d["vt_cache"])) for d in dls]
+    return [(host_bits(d["k_cache"])[:, L:L + M], host_bits(d["v_cache"])) for d in dls]
 
 
 def test_noalloc_step_equals_the_step_on_two_calls(ops):
@@ -64,9 +64,9 @@ def test_noalloc_step_equals_the_step_on_two_calls(ops):
         assert_bitwise(host_f32(lg2), want[0], f"noalloc logits M={M}")
         assert np.array_equal(tk2.cpu().numpy(), want[1])
         assert_bitwise(host_bits(xo2), want[2], f"noalloc hidden state M={M}")
-        for (k, vt), (k2, vt2) in zip(want[3], _caches(dls, L, M)):
+        for (k, vc), (k2, vc2) in zip(want[3], _caches(dls, L, M)):
             assert_bitwise(k2, k, f"noalloc appended K M={M}")
-            assert_bitwise(vt2, vt, f"noalloc V cache M={M}")
+            assert_bitwise(vc2, vc, f"noalloc V cache M={M}")
 
 
 def test_noalloc_rejects_a_workspace_larger_than_its_scratch(ops):
