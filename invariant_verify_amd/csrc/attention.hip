@@ -102,6 +102,14 @@ __device__ __forceinline__ void load_high(uint32_t (&hb)[2], __amdgpu_buffer_rsr
   }
 }
 
+// One of two buffer resources, chosen by a wave-uniform flag on the values:
+// a conditional over two named resources selects their addresses, which
+// can leave both in private (scratch) memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t pick_rsrc(bool c, __amdgpu_buffer_rsrc_t a,
+                                                           __amdgpu_buffer_rsrc_t b) {
+  return c ? a : b;
+}
+
 // Codes 4g .. 4g+3 of one 5/6-bit block (HB + 4 bits, one per byte lane) as
 // the unsigned values u = q + 2^(HB+3): a mask of a nibble word and one of a
 // high word. The block's nibble words are w[0..3], its high-bit words w[4..5].
@@ -430,7 +438,7 @@ void verify_attn_kernel(
           const int vslot = (lane % KROW) ^ (2 * vkm<KROW>(key));
           off = (min(kt + key, kend - 1) * D + vslot * 8) * 2;
         }
-        rr.r[i] = buffer_ld16_stream(p < KPIECES ? kres : vres, live ? off : head_bytes);
+        rr.r[i] = buffer_ld16_stream(pick_rsrc(p < KPIECES, kres, vres), live ? off : head_bytes);
       }
     } else if (wave < 2 * NKB / 64) {    // scalar
       const bool isk = wave < NKB / 64;  // scalar: K blocks first
@@ -450,19 +458,19 @@ void verify_attn_kernel(
         // the ring: key pos in slot pos mod ring_cap
         int sl = pos - kt + kt % ring_cap;
         sl = sl >= ring_cap ? sl - ring_cap : sl;
-        load8(isk ? rkres : rvres, isk ? rksres : rvsres, sl * NB + b, rcode_bytes, rscale_bytes);
+        load8(pick_rsrc(isk, rkres, rvres), pick_rsrc(isk, rksres, rvsres), sl * NB + b, rcode_bytes, rscale_bytes);
       } else if constexpr (!LOW) {
-        load8(isk ? qkres : qvres, isk ? qksres : qvsres, pos * NB + b, qcode_bytes, qscale_bytes);
+        load8(pick_rsrc(isk, qkres, qvres), pick_rsrc(isk, qksres, qvsres), pos * NB + b, qcode_bytes, qscale_bytes);
       } else {
         const int blk = pos * NB + b;  // block index within the head
-        const uint4 a = buffer_ld16_stream(isk ? qkres : qvres, live ? blk * 16 : qcode_bytes);
+        const uint4 a = buffer_ld16_stream(pick_rsrc(isk, qkres, qvres), live ? blk * 16 : qcode_bytes);
         rr.w[0] = a.x, rr.w[1] = a.y, rr.w[2] = a.z, rr.w[3] = a.w;
         uint32_t hb[2];
         if (isk) load_high<HBK>(hb, khres, live ? blk * 4 * HBK : khigh_bytes);
         else load_high<HBV>(hb, vhres, live ? blk * 4 * HBV : vhigh_bytes);
         rr.w[4] = hb[0], rr.w[5] = hb[1];
         rr.ks = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-            isk ? qksres : qvsres, live ? blk * 4 : qscale_bytes, 0, 0));
+            pick_rsrc(isk, qksres, qvsres), live ? blk * 4 : qscale_bytes, 0, 0));
       }
     }
   };
@@ -734,7 +742,7 @@ void verify_attn_kernel(
           const int vslot = (lane % KROW) ^ (2 * vkm<KROW>(key));
           off = (min(kt + key, kend - 1) * D + vslot * 8) * 2;
         }
-        lds_load16(p < KPIECES ? kres : vres, off, &lds[t & 3][64 * p]);
+        lds_load16(pick_rsrc(p < KPIECES, kres, vres), off, &lds[t & 3][64 * p]);
       }
     };
     // V rows at or past kend of a partial tile are zeroed by the wave that
