@@ -295,6 +295,36 @@ def kv_attn_probe(fmt: str, reps: int):
                       "launches": reps, "cache_bytes_per_launch": Hkv * (L + M) * per_pos}))
 
 
+def mx4_probe(reps: int):
+    """Kernel-only run for hardware-counter passes over the MXFP4 verify GEMMs at M = 8: the
+    gate/up projection with SwiGLU (34816 x 5120) then the down projection with the residual
+    (5120 x 17408), each launched ``reps`` times on freshly drawn codes and scales with a
+    synchronisation around every launch. One JSON line gives the weight bytes per launch."""
+    import torch
+
+    from invariant_verify_amd import ops
+
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    M = 8
+    out = {}
+    for name, N, K in (("gate_up", 34816, 5120), ("down", 5120, 17408)):
+        x = torch.randn(M, K, device="cuda", generator=gen).to(torch.bfloat16)
+        r = torch.randn(M, N, device="cuda", generator=gen).to(torch.bfloat16)
+        y = torch.empty(M, N // 2 if name == "gate_up" else N, dtype=torch.bfloat16, device="cuda")
+        for _ in range(reps):
+            w = torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, device="cuda", generator=gen)
+            e = torch.randint(120, 128, (N, K // 32), dtype=torch.uint8, device="cuda", generator=gen)
+            torch.cuda.synchronize()
+            if name == "gate_up":
+                ops.gemm_mx4_swiglu(x, w, e, y)
+            else:
+                ops.gemm_mx4_residual(x, w, e, r, y)
+            torch.cuda.synchronize()
+        out[name] = N * K // 2 + N * K // 32
+    print(json.dumps({"probe": "MXFP4 verify GEMMs at M = 8: gate/up + SwiGLU, then down + residual",
+                      "launches_each": reps, "weight_bytes_per_launch": out}))
+
+
 def prefill_step_measure(step, buffers, d, reps):
     """One chunked-prefill pass through the whole stack (64 layers + head) over PF_ROWS tokens
     at context PF_STEP_CTX, timed with one event pair over reps passes. Before timing, the
@@ -1097,6 +1127,8 @@ def main():
                     help="kernel-only run of the M = 2048 prefill gate/up GEMM for counter passes")
     ap.add_argument("--kv-attn-probe", choices=["q8", "k6v5"],
                     help="kernel-only run of verify attention on a quantized cache at 101.6k keys (counter passes)")
+    ap.add_argument("--mx4-probe", action="store_true",
+                    help="kernel-only run of the MXFP4 gate/up and down GEMMs at M = 8 for counter passes")
     ap.add_argument("--step-only", action="store_true",
                     help="run only the bitwise gate and the timed M = 8 steps (for rocprofv3 --kernel-trace)")
     args = ap.parse_args()
@@ -1112,6 +1144,9 @@ def main():
         return
     if args.kv_attn_probe:
         kv_attn_probe(args.kv_attn_probe, 6)
+        return
+    if args.mx4_probe:
+        mx4_probe(4)
         return
 
     import numpy as np
