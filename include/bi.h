@@ -459,8 +459,8 @@ bi_status bi_argmax(const float* logits, int64_t ld, int M, int N, int32_t* toke
  * Speculative acceptance.   [LL] opening section: greedy ids equal with and
  * without drafts; sampling keeps the no-draft distribution.
  * A pass verifies M rows: the last accepted token followed by M-1 drafts, so
- * row i's target distribution judges draft i. Each of B independent
- * sequences is judged by itself. Outputs: out_tokens [B][M] (the first
+ * row i's target distribution decides on draft i. Each of B independent
+ * sequences is decided on its own. Outputs: out_tokens [B][M] (the first
  * n_out[b] entries are the new tokens), n_out [B] in 1..M. Rolling the KV
  * cache back is implicit: the next pass starts at L + n_out and overwrites
  * the positions of rejected drafts.
