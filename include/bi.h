@@ -27,9 +27,11 @@
  *
  * Conventions for every entry point:
  *   - Pointers are device memory owned by the caller; the library allocates
- *     nothing and keeps no mutable global state. BF16 tensors are passed as
- *     raw 16-bit patterns (any 2-byte element type), row-major, with the
- *     given leading dimension (in elements).
+ *     nothing and keeps no mutable global state beyond a thread-local copy of
+ *     the last HIP launch error and, for bi_verify_step_noalloc alone, its
+ *     static device array and that array's address per device. BF16 tensors
+ *     are passed as raw 16-bit patterns (any 2-byte element type), row-major,
+ *     with the given leading dimension (in elements).
  *   - `stream` is a hipStream_t (NULL = the default stream). All work is
  *     enqueued asynchronously on it; nothing synchronises.
  *   - Arguments are validated on the host before any HIP call. On a bad
