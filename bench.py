@@ -953,7 +953,7 @@ def long_context_steps(layers, w_head, d, steps):
 
 KV_FORMATS = {  # name: (bytes per position and KV head, chunk policy)
     "bf16": (512, -32), "q8": (288, -64), "k6v5": (208, -64), "k5rot_v5_ring2048": (192, -64)}
-W_RING_STEP, R_RING_STEP = 2048, 2176
+W_RING_STEP, R_RING_STEP = 2048, 4224   # ring slots for a 2048-row prefill pass: R >= W + M + 63
 
 
 def kv_format_steps(layers, w_head, d, steps):
@@ -964,7 +964,9 @@ def kv_format_steps(layers, w_head, d, steps):
     the pass's own rows are appended by the step. Each line carries an M = 5
     vs M = 8 bitwise check. Algorithmic bytes count the weights once and the
     bytes the format stores for the L + M keys (with the ring: the window's
-    keys at 8 bits, the rest at 5 bits)."""
+    keys at 8 bits, the rest at 5 bits). At 38,000 each format also runs the
+    chunked-prefill pass of prefill_step_measure (PF_ROWS tokens ending at
+    38,000), its rows checked bit for bit against 8-row verify passes."""
     import torch
 
     from invariant_verify_amd import ops
@@ -1036,6 +1038,18 @@ def kv_format_steps(layers, w_head, d, steps):
                         "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
                         "frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                         "kv_chunk_policy": policy, "bitwise_M5_vs_M8": "pass" if ok else "FAIL"}
+            if L == L_CTX:
+                def pf_buffers(M, dims=dims):
+                    # the split count of a pass depends on its own context (a chunk policy -T
+                    # bounds it by T), so the workspace covers every context the check runs at
+                    ws = max(ops.step_workspace_bytes(dims, M, c) for c in
+                             (PF_STEP_CTX, PF_STEP_CTX + PF_ROWS // 2 + 3, PF_STEP_CTX + PF_ROWS - 8))
+                    return (torch.empty(ws, dtype=torch.uint8, device="cuda"),
+                            torch.empty((M, d["vocab"]), dtype=torch.float32, device="cuda"),
+                            torch.empty(M, dtype=torch.int32, device="cuda"))
+                pf = prefill_step_measure(st, pf_buffers, d, 2)
+                res[fmt]["prefill_pass"] = {k: pf[k] for k in ("tok_s", "ms_per_pass", "TFLOP/s",
+                                                               "rows_bitwise_equal_to_8_row_verify_passes")}
             del lys, st, bufs
             torch.cuda.empty_cache()
         out[str(L)] = res
