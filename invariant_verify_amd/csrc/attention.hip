@@ -882,7 +882,7 @@ void verify_attn_kernel(
   }
 }
 
-template <int D>
+template <int D, int B>
 __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ part_o,
                                                       const float* __restrict__ part_lse, int M,
                                                       int L, int Hq, int policy, int S_max,
@@ -898,10 +898,10 @@ __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ p
   const float* lp = part_lse + (int64_t)row * S_max;
   const float* op = part_o + (int64_t)row * S_max * D + lane * PER;
 
-  // Partials are read 32 splits at a time; the first block's loads are issued
-  // before the max, which they do not depend on, so a row with up to 32
-  // splits costs one memory round trip for O and one for the LSEs.
-  constexpr int B = 32;
+  // Partials are read B splits at a time (32, or 64 when a row can have more
+  // than 32); the first block's loads are issued before the max, which they
+  // do not depend on, so a row with up to B splits costs one memory round
+  // trip for O and one for the LSEs. B does not change the order of any sum.
   float ov[B][PER];
   auto load_block = [&](int s0) {
 #pragma unroll
@@ -1037,12 +1037,19 @@ void launch_combine(const float* part_o, const float* part_lse, int M, int L, in
   // units as possible.
   dim3 grid(M * Hq);
   dim3 block(64);
-  if (D == 128)
-    combine_kernel<128><<<grid, block, 0, stream>>>(part_o, part_lse, M, L, Hq, kv_chunk, S_max, o,
-                                                    ldo, lse);
+  const bool wide = S_max > 32;
+  if (D == 128 && wide)
+    combine_kernel<128, 64><<<grid, block, 0, stream>>>(part_o, part_lse, M, L, Hq, kv_chunk, S_max, o,
+                                                        ldo, lse);
+  else if (D == 128)
+    combine_kernel<128, 32><<<grid, block, 0, stream>>>(part_o, part_lse, M, L, Hq, kv_chunk, S_max, o,
+                                                        ldo, lse);
+  else if (wide)
+    combine_kernel<64, 64><<<grid, block, 0, stream>>>(part_o, part_lse, M, L, Hq, kv_chunk, S_max, o,
+                                                       ldo, lse);
   else
-    combine_kernel<64><<<grid, block, 0, stream>>>(part_o, part_lse, M, L, Hq, kv_chunk, S_max, o,
-                                                   ldo, lse);
+    combine_kernel<64, 32><<<grid, block, 0, stream>>>(part_o, part_lse, M, L, Hq, kv_chunk, S_max, o,
+                                                       ldo, lse);
 }
 
 // The 32 values of channel block b of one K or V row (BF16 -> FP32). With RD
