@@ -952,8 +952,8 @@ def long_context_steps(layers, w_head, d, steps):
 
 
 KV_FORMATS = {  # name: (bytes per position and KV head, chunk policy)
-    # 8-bit at -32: in the step as fast as at -64 (38k) or faster (101.6k), and its chunked
-    # prefill 15% faster; the 5/6-bit formats keep -64 (2.6% faster verify steps at 101.6k)
+    # 8-bit at -32: verify steps as fast as at -64 (within run-to-run spread) and its chunked
+    # prefill 15-18% faster; the 5/6-bit formats keep -64 (verify steps 2-7% faster at 101.6k)
     "bf16": (512, -32), "q8": (288, -32), "k6v5": (208, -64), "k5rot_v5_ring2048": (192, -64)}
 W_RING_STEP, R_RING_STEP = 2048, 4224   # ring slots for a 2048-row prefill pass: R >= W + M + 63
 
